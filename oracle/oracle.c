@@ -1,0 +1,276 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for the batch-1 MoE verify hot path.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the bench's
+ * CPU-baseline leg load this library; the GPU library never does. Every
+ * function is the plain definition of what the step computes, written from
+ * the LMSYS post "Chasing the batch-1 floor: Ling-3.0-flash speculative
+ * decode on Blackwell": double-precision sums in ascending index order, no
+ * blocking, no fusion. OpenMP only splits independent outputs between
+ * threads; it never changes the order of any sum.
+ *
+ * Readings of points the post leaves open (each is listed with its reason
+ * in the design notes):
+ *   - scoring is a softmax over the router logits, k = 8 in the model, and
+ *     the k weights are renormalised over the selected set;
+ *   - the optional router bias is added to the logits before both the
+ *     selection and the softmax;
+ *   - selection and argmax are decided on fp32-rounded logits (the post runs
+ *     fp32 logits), ties to the lower index;
+ *   - silu(z) = z / (1 + exp(-z)), applied to the gate projection and
+ *     multiplied by the up projection (section "Two fusions and a retune");
+ *   - the combine sums the k slots in slot order (same section).
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+double oracle_bf16_value(uint16_t bits)
+{
+    /* bf16 is the upper 16 bits of a binary32 value. */
+    uint32_t wide = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &wide, sizeof f);
+    return (double)f;
+}
+
+/* Dot product of two bf16 rows of length n, in double, ascending index. */
+static double dot_bf16(const uint16_t *a, const uint16_t *b, int64_t n)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        s += oracle_bf16_value(a[i]) * oracle_bf16_value(b[i]);
+    return s;
+}
+
+/* Dot product of a bf16 row with a double vector, ascending index. */
+static double dot_bf16_f64(const uint16_t *a, const double *b, int64_t n)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        s += oracle_bf16_value(a[i]) * b[i];
+    return s;
+}
+
+static int all_finite_bf16(const uint16_t *a, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        if ((a[i] & 0x7F80u) == 0x7F80u) /* exponent all ones: inf or nan */
+            return 0;
+    return 1;
+}
+
+static int cmp_desc(const void *pa, const void *pb)
+{
+    double a = *(const double *)pa, b = *(const double *)pb;
+    return (a < b) - (a > b);
+}
+
+/* Largest minus second-largest gap information over n values. */
+static void sorted_gaps(const double *v, int32_t n, int32_t k,
+                        double *gap_sel, double *gap_order)
+{
+    double *s = (double *)malloc(sizeof(double) * (size_t)n);
+    memcpy(s, v, sizeof(double) * (size_t)n);
+    qsort(s, (size_t)n, sizeof(double), cmp_desc);
+    *gap_sel = (k < n) ? s[k - 1] - s[k] : INFINITY;
+    double g = INFINITY;
+    for (int32_t j = 0; j + 1 < k; ++j)
+        if (s[j] - s[j + 1] < g)
+            g = s[j] - s[j + 1];
+    *gap_order = g;
+    free(s);
+}
+
+int oracle_route(const uint16_t *x, const uint16_t *wg, const float *bias,
+                 int32_t M, int32_t H, int32_t E, int32_t k,
+                 double *logits, int32_t *idx, double *w, double *w_full,
+                 double *gap_sel, double *gap_order)
+{
+    if (!x || !wg || !logits || !idx || !w || !w_full || !gap_sel || !gap_order)
+        return -1;
+    if (M < 1 || H < 1 || E < 1 || k < 1 || k > E)
+        return -2;
+    if (!all_finite_bf16(x, (int64_t)M * H) || !all_finite_bf16(wg, (int64_t)E * H))
+        return -4;
+    if (bias)
+        for (int32_t e = 0; e < E; ++e)
+            if (!isfinite(bias[e]))
+                return -4;
+
+    char *taken = (char *)malloc((size_t)E);
+    double *p = (double *)malloc(sizeof(double) * (size_t)E);
+
+    for (int32_t t = 0; t < M; ++t) {
+        double *l = logits + (int64_t)t * E;
+
+        /* Gate matvec (router chain, Fig. 7), plus the optional bias. */
+        for (int32_t e = 0; e < E; ++e) {
+            l[e] = dot_bf16(x + (int64_t)t * H, wg + (int64_t)e * H, H);
+            if (bias)
+                l[e] += (double)bias[e];
+        }
+
+        /* Top-k: k rounds, each picking the largest fp32-rounded logit not
+         * yet taken; a strict comparison keeps the lower id on ties. */
+        memset(taken, 0, (size_t)E);
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t best = -1;
+            float best_v = 0.0f;
+            for (int32_t e = 0; e < E; ++e) {
+                if (taken[e])
+                    continue;
+                float v = (float)l[e];
+                if (best < 0 || v > best_v) {
+                    best = e;
+                    best_v = v;
+                }
+            }
+            taken[best] = 1;
+            idx[(int64_t)t * k + j] = best;
+        }
+
+        /* Softmax restricted to the selected set, shifted by its largest
+         * member for range safety (the shift cancels in the ratio). */
+        double m = l[idx[(int64_t)t * k]];
+        double den = 0.0;
+        for (int32_t j = 0; j < k; ++j)
+            den += exp(l[idx[(int64_t)t * k + j]] - m);
+        for (int32_t j = 0; j < k; ++j)
+            w[(int64_t)t * k + j] = exp(l[idx[(int64_t)t * k + j]] - m) / den;
+
+        /* Same weights the long way: softmax over all E experts, then
+         * renormalised over the selected set. */
+        double mx = l[0];
+        for (int32_t e = 1; e < E; ++e)
+            if (l[e] > mx)
+                mx = l[e];
+        double z = 0.0;
+        for (int32_t e = 0; e < E; ++e) {
+            p[e] = exp(l[e] - mx);
+            z += p[e];
+        }
+        for (int32_t e = 0; e < E; ++e)
+            p[e] /= z;
+        double ps = 0.0;
+        for (int32_t j = 0; j < k; ++j)
+            ps += p[idx[(int64_t)t * k + j]];
+        for (int32_t j = 0; j < k; ++j)
+            w_full[(int64_t)t * k + j] = p[idx[(int64_t)t * k + j]] / ps;
+
+        sorted_gaps(l, E, k, &gap_sel[t], &gap_order[t]);
+    }
+    free(taken);
+    free(p);
+    return 0;
+}
+
+int oracle_expert_ffn(const uint16_t *x, const int32_t *idx, const double *w,
+                      const uint16_t *wgate, const uint16_t *wup,
+                      const uint16_t *wdown,
+                      int32_t M, int32_t H, int32_t I, int32_t E, int32_t k,
+                      double *out, double *act)
+{
+    if (!x || !idx || !w || !wgate || !wup || !wdown || !out)
+        return -1;
+    if (M < 1 || H < 1 || I < 1 || E < 1 || k < 1)
+        return -2;
+    const int64_t NP = (int64_t)M * k;
+    for (int64_t p = 0; p < NP; ++p)
+        if (idx[p] < 0 || idx[p] >= E)
+            return -3;
+    if (!all_finite_bf16(x, (int64_t)M * H))
+        return -4;
+    for (int64_t p = 0; p < NP; ++p) {
+        int64_t e = idx[p];
+        if (!isfinite(w[p]) ||
+            !all_finite_bf16(wgate + e * I * H, (int64_t)I * H) ||
+            !all_finite_bf16(wup + e * I * H, (int64_t)I * H) ||
+            !all_finite_bf16(wdown + e * H * I, (int64_t)H * I))
+            return -4;
+    }
+
+    double *a = (double *)malloc(sizeof(double) * (size_t)(NP * I));
+    double *y = (double *)malloc(sizeof(double) * (size_t)(NP * H));
+
+    /* Up projection and SwiGLU for every (token, slot) pair: gate and up are
+     * separate dot products, silu is taken on the gate, and the product is
+     * kept in double (section "Two fusions and a retune"). */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t p = 0; p < NP; ++p)
+        for (int32_t i = 0; i < I; ++i) {
+            int32_t t = (int32_t)(p / k);
+            int64_t e = idx[p];
+            const uint16_t *xt = x + (int64_t)t * H;
+            double g = dot_bf16(wgate + (e * I + i) * H, xt, H);
+            double u = dot_bf16(wup + (e * I + i) * H, xt, H);
+            double s = g / (1.0 + exp(-g));
+            a[p * I + i] = s * u;
+        }
+
+    /* Down projection of every pair. */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t p = 0; p < NP; ++p)
+        for (int32_t r = 0; r < H; ++r) {
+            int64_t e = idx[p];
+            y[p * H + r] = dot_bf16_f64(wdown + (e * H + r) * I, a + p * I, I);
+        }
+
+    /* Weighted combine, slots in order. */
+    for (int32_t t = 0; t < M; ++t)
+        for (int32_t r = 0; r < H; ++r) {
+            double s = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                int64_t p = (int64_t)t * k + j;
+                s += w[p] * y[p * H + r];
+            }
+            out[(int64_t)t * H + r] = s;
+        }
+
+    if (act)
+        memcpy(act, a, sizeof(double) * (size_t)(NP * I));
+    free(a);
+    free(y);
+    return 0;
+}
+
+int oracle_lmhead(const uint16_t *h, const uint16_t *wlm,
+                  int32_t M, int32_t H, int32_t V,
+                  int32_t *tok, double *zmax, double *gap)
+{
+    if (!h || !wlm || !tok || !zmax || !gap)
+        return -1;
+    if (M < 1 || H < 1 || V < 1)
+        return -2;
+    if (!all_finite_bf16(h, (int64_t)M * H) ||
+        !all_finite_bf16(wlm, (int64_t)V * H))
+        return -4;
+
+    double *z = (double *)malloc(sizeof(double) * (size_t)V);
+    for (int32_t t = 0; t < M; ++t) {
+        /* Logits of token t over the whole vocabulary. */
+#pragma omp parallel for schedule(static)
+        for (int32_t v = 0; v < V; ++v)
+            z[v] = dot_bf16(h + (int64_t)t * H, wlm + (int64_t)v * H, H);
+
+        /* Greedy token: first v holding the largest fp32-rounded logit. */
+        int32_t best = 0;
+        float best_v = (float)z[0];
+        for (int32_t v = 1; v < V; ++v) {
+            float zv = (float)z[v];
+            if (zv > best_v) {
+                best = v;
+                best_v = zv;
+            }
+        }
+        tok[t] = best;
+        zmax[t] = z[best];
+
+        double unused;
+        sorted_gaps(z, V, 1, &gap[t], &unused);
+    }
+    free(z);
+    return 0;
+}

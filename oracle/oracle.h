@@ -1,0 +1,98 @@
+/*
+ * oracle.h -- plain fp64 CPU reference for the batch-1 MoE verify hot path.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the bench's
+ * CPU-baseline leg load this library. The GPU library shares no code, header,
+ * table or constant with it, and neither side includes or links the other.
+ *
+ * Source of the method: the LMSYS post "Chasing the batch-1 floor:
+ * Ling-3.0-flash speculative decode on Blackwell" (2026-08-21):
+ *   - section "PDL: the latency floor of stacked small kernels", Fig. 7:
+ *     router chain (gate matvec -> top-k) and MoE chain
+ *     (up-GEMM -> activation -> down-GEMM -> combine);
+ *   - section "Two fusions and a retune": SwiGLU silu(gate)*up computed in
+ *     float; combine is an fp32 sum times the routing scale;
+ *   - section "bf16 router gate and lm_head": both weights are bf16 and are
+ *     pure bandwidth; the lm_head result feeds a greedy (argmax) verdict.
+ *
+ * Conventions shared by every function here:
+ *   - bf16 tensors are raw uint16 bit patterns, row-major, reduction axis
+ *     contiguous;
+ *   - every sum is taken in double, over the reduction index in ascending
+ *     order, with no blocking or reordering;
+ *   - a selection (top-k, argmax) is decided on the logits rounded to fp32,
+ *     the precision the post runs those logits in, lowest index first among
+ *     equal fp32 values;
+ *   - the functions return 0 on success and a negative code on bad
+ *     arguments: -1 null pointer, -2 bad size, -3 index out of range,
+ *     -4 non-finite input.
+ */
+#ifndef MOE_VERIFY_ORACLE_H
+#define MOE_VERIFY_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exact value of one bf16 bit pattern (bf16 is the top half of an IEEE
+ * binary32, so widening is exact). */
+double oracle_bf16_value(uint16_t bits);
+
+/* Router: logits, softmax top-k, renormalised weights.
+ *   x      [M,H] bf16    token activations
+ *   wg     [E,H] bf16    router gate weight
+ *   bias   [E]   float   added to every token's logits, or NULL
+ * outputs (all caller-owned):
+ *   logits [M,E] double  l[t,e] = sum_h x[t,h]*wg[e,h] + bias[e]
+ *   idx    [M,k] int32   k largest fp32-rounded logits, descending,
+ *                        ties to the lower expert id
+ *   w      [M,k] double  softmax restricted to the selected set
+ *   w_full [M,k] double  softmax over all E experts, then renormalised
+ *                        over the selected set (must equal w)
+ *   gap_sel   [M] double l_(k) - l_(k+1) over the sorted fp64 logits
+ *                        (+inf when k == E): a small gap means the set
+ *                        boundary is a near-tie
+ *   gap_order [M] double min_{j<k-1} l_(j) - l_(j+1): a small gap means the
+ *                        order inside the set is a near-tie (+inf if k == 1)
+ */
+int oracle_route(const uint16_t *x, const uint16_t *wg, const float *bias,
+                 int32_t M, int32_t H, int32_t E, int32_t k,
+                 double *logits, int32_t *idx, double *w, double *w_full,
+                 double *gap_sel, double *gap_order);
+
+/* Selected experts' SwiGLU FFN and weighted combine.
+ *   x      [M,H]    bf16
+ *   idx    [M,k]    int32 expert ids (may repeat across tokens)
+ *   w      [M,k]    double routing weights
+ *   wgate  [E,I,H]  bf16, wup [E,I,H] bf16, wdown [E,H,I] bf16
+ * output:
+ *   out    [M,H] double
+ *     out[t,r] = sum_j w[t,j] * sum_i wdown[e,r,i] * silu(g_i) * u_i,
+ *     e = idx[t,j], g_i = wgate[e,i,:].x[t,:], u_i = wup[e,i,:].x[t,:],
+ *     silu(z) = z / (1 + exp(-z)); slots summed in order j = 0..k-1.
+ *   act    [M,k,I] double, optional (NULL skips): silu(g)*u per pair.
+ */
+int oracle_expert_ffn(const uint16_t *x, const int32_t *idx, const double *w,
+                      const uint16_t *wgate, const uint16_t *wup,
+                      const uint16_t *wdown,
+                      int32_t M, int32_t H, int32_t I, int32_t E, int32_t k,
+                      double *out, double *act);
+
+/* lm_head projection and greedy argmax.
+ *   h [M,H] bf16, wlm [V,H] bf16
+ * outputs:
+ *   tok  [M] int32  first v with the largest fp32-rounded z[t,v]
+ *   zmax [M] double z[t,tok[t]] in fp64
+ *   gap  [M] double z_(1) - z_(2) over the fp64 logits (+inf when V == 1)
+ */
+int oracle_lmhead(const uint16_t *h, const uint16_t *wlm,
+                  int32_t M, int32_t H, int32_t V,
+                  int32_t *tok, double *zmax, double *gap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

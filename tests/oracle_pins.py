@@ -1,0 +1,317 @@
+"""Pins for the CPU oracle: facts that hold independently of the oracle's code.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with something fixed outside it: a library routine (numpy
+matmul, stable argsort, argmax, scipy's logistic function), a closed form on
+planted inputs, or an invariant of the mathematics. The mutation test runs
+every pin against copies of the oracle with planted mistakes to show that each
+mistake is caught.
+
+The method is the one in the LMSYS post "Chasing the batch-1 floor:
+Ling-3.0-flash speculative decode on Blackwell".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import expit
+
+import synth
+
+F = synth.bf16_to_f32
+
+
+def _bits(values) -> np.ndarray:
+    """bf16 bits of values that are exactly representable in bf16."""
+    v = np.asarray(values, dtype=np.float32)
+    b = synth.bf16_bits(v)
+    assert np.array_equal(F(b), v), "planted value is not exact in bf16"
+    return b
+
+
+def _silu(z):
+    return z * expit(z)
+
+
+# --------------------------------------------------------------------- bf16
+
+def pin_bf16_decode(o):
+    """bf16 is the top half of binary32: a few patterns with known values."""
+    cases = {0x3F80: 1.0, 0xBF80: -1.0, 0x4049: 3.140625, 0x0000: 0.0,
+             0x0001: 2.0 ** -133, 0x0080: 2.0 ** -126,
+             0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127, 0xC2F7: -123.5}
+    for bits, val in cases.items():
+        assert o.bf16_value(bits) == val, hex(bits)
+
+
+# ------------------------------------------------------------------- router
+
+def pin_route_logits_match_matmul(o):
+    """Logits equal numpy's fp64 x @ Wg^T + bias on a non-square case."""
+    M, H, E, k = 3, 40, 24, 5
+    x = synth.normal_bf16((M, H), 1.0, 11, 1)
+    wg = synth.normal_bf16((E, H), 0.02, 11, 2)
+    bias = synth.rng(11, 3).normal(size=E).astype(np.float32) * 0.05
+    r = o.route(x, wg, bias, k)
+    ref = F(x).astype(np.float64) @ F(wg).astype(np.float64).T + bias.astype(np.float64)
+    assert np.allclose(r["logits"], ref, rtol=0, atol=1e-12)
+
+
+def pin_route_topk_matches_stable_argsort(o):
+    """Selection equals numpy's stable argsort of the fp32 logits, with
+    planted exact ties (duplicated router rows) resolved to the lower id."""
+    M, H, E, k = 4, 32, 16, 4
+    x = synth.normal_bf16((M, H), 1.0, 12, 1)
+    wg = synth.normal_bf16((E, H), 0.02, 12, 2)
+    wg[9] = wg[3]          # exact tie between experts 3 and 9
+    wg[14] = wg[2]         # and between 2 and 14
+    r = o.route(x, wg, None, k)
+    with np.errstate(over="ignore"):
+        l32 = r["logits"].astype(np.float32)
+    for t in range(M):
+        ref = np.argsort(-l32[t], kind="stable")[:k]
+        assert np.array_equal(r["idx"][t], ref), (t, r["idx"][t], ref)
+        sel = set(r["idx"][t].tolist())
+        lo = min(l32[t, list(sel)])
+        hi = max([l32[t, e] for e in range(E) if e not in sel])
+        assert lo >= hi
+    # planting the tie at the top: both copies of the largest row selected,
+    # lower id first
+    x1 = synth.normal_bf16((1, H), 1.0, 13, 1)
+    wg1 = synth.normal_bf16((E, H), 0.02, 13, 2)
+    top = int(np.argmax(F(x1)[0] @ F(wg1).T))
+    wg1[0] = wg1[top]
+    r1 = o.route(x1, wg1, None, 2)
+    assert r1["idx"][0].tolist() == sorted([0, top])
+
+
+def pin_route_planted_closed_form(o):
+    """One-hot token against planted router rows: logits are the planted
+    values and the weights are a softmax of them, in closed form."""
+    H, E, k = 8, 6, 3
+    vals = [0.5, -1.0, 2.0, 2.0, 0.0, -3.0]
+    x = _bits([[1.0] + [0.0] * (H - 1)])
+    wg = np.zeros((E, H), np.uint16)
+    for e, v in enumerate(vals):
+        wg[e, 0] = _bits([v])[0]
+    r = o.route(x, wg, None, k)
+    assert r["idx"][0].tolist() == [2, 3, 0]
+    den = 2 * math.exp(2.0) + math.exp(0.5)
+    exp_w = [math.exp(2.0) / den, math.exp(2.0) / den, math.exp(0.5) / den]
+    assert np.allclose(r["w"][0], exp_w, rtol=1e-14, atol=0)
+    assert r["gap_order"][0] == 0.0          # experts 2 and 3 tie exactly
+    assert r["gap_sel"][0] == 0.5            # 3rd (0.5) minus 4th (0.0)
+
+
+def pin_route_zero_input(o):
+    """x = 0 and no bias: all logits are 0, ids 0..k-1, weights exactly 1/k."""
+    M, H, E, k = 2, 16, 12, 4
+    x = np.zeros((M, H), np.uint16)
+    wg = synth.normal_bf16((E, H), 0.02, 14, 2)
+    r = o.route(x, wg, None, k)
+    assert np.all(r["logits"] == 0.0)
+    assert np.array_equal(r["idx"], np.tile(np.arange(k, dtype=np.int32), (M, 1)))
+    assert np.all(r["w"] == 1.0 / k)
+
+
+def pin_route_bias_semantics(o):
+    """A constant bias changes no selection or weight (softmax is shift
+    invariant); a large bias on one expert puts it first."""
+    M, H, E, k = 3, 24, 16, 4
+    x = synth.normal_bf16((M, H), 1.0, 15, 1)
+    wg = synth.normal_bf16((E, H), 0.02, 15, 2)
+    r0 = o.route(x, wg, None, k)
+    r1 = o.route(x, wg, np.full(E, 0.25, np.float32), k)
+    assert np.array_equal(r0["idx"], r1["idx"])
+    assert np.allclose(r0["w"], r1["w"], rtol=1e-12, atol=0)
+    b = np.zeros(E, np.float32)
+    b[7] = 50.0
+    r2 = o.route(x, wg, b, k)
+    assert np.all(r2["idx"][:, 0] == 7)
+    assert np.all(r2["w"][:, 0] > 0.999)
+
+
+def pin_route_weight_identities(o):
+    """Weights sum to one, do not increase along the slots, and equal the
+    full-softmax-then-renormalise route (the full denominator cancels)."""
+    M, H, E, k = 5, 64, 32, 8
+    x = synth.normal_bf16((M, H), 1.0, 16, 1)
+    wg = synth.normal_bf16((E, H), 0.05, 16, 2)
+    r = o.route(x, wg, synth.zipf_bias(E, 1.0), k)
+    assert np.allclose(r["w"].sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    assert np.all(np.diff(r["w"], axis=1) <= 1e-15)
+    assert np.allclose(r["w"], r["w_full"], rtol=1e-12, atol=0)
+    # weights are the softmax of the selected logits: ratio of two weights
+    # is exp of the logit difference
+    for t in range(M):
+        l = r["logits"][t, r["idx"][t]]
+        assert np.allclose(r["w"][t] / r["w"][t, 0], np.exp(l - l[0]), rtol=1e-12)
+
+
+def pin_route_gaps(o):
+    """Near-tie gaps equal the differences of numpy's sorted logits."""
+    M, H, E, k = 3, 32, 20, 6
+    x = synth.normal_bf16((M, H), 1.0, 17, 1)
+    wg = synth.normal_bf16((E, H), 0.02, 17, 2)
+    r = o.route(x, wg, None, k)
+    s = -np.sort(-r["logits"], axis=1)
+    assert np.array_equal(r["gap_sel"], s[:, k - 1] - s[:, k])
+    assert np.array_equal(r["gap_order"], np.min(s[:, :k - 1] - s[:, 1:k], axis=1))
+
+
+# ------------------------------------------------------------------ experts
+
+def pin_ffn_single_expert_is_dense_swiglu(o):
+    """k = 1, weight 1: the layer is one dense SwiGLU MLP,
+    Wd (silu(Wg x) * (Wu x)), here with numpy matmuls and scipy's logistic."""
+    M, H, I, E = 3, 40, 24, 4
+    x = synth.normal_bf16((M, H), 1.0, 21, 1)
+    wgt = synth.layer_weights(H, E, I, seed=21)
+    # N(0, 0.02) weights give |g| ~ 0.1; rescale so silu's curvature matters
+    for key in ("gate", "up", "down"):
+        wgt[key] = synth.bf16_bits(F(wgt[key]) * 8)
+    idx = np.array([[2], [0], [3]], np.int32)
+    w = np.ones((M, 1))
+    out = o.expert_ffn(x, idx, w, wgt["gate"], wgt["up"], wgt["down"])
+    xf = F(x).astype(np.float64)
+    for t in range(M):
+        e = idx[t, 0]
+        g = F(wgt["gate"][e]).astype(np.float64) @ xf[t]
+        u = F(wgt["up"][e]).astype(np.float64) @ xf[t]
+        ref = F(wgt["down"][e]).astype(np.float64) @ (_silu(g) * u)
+        assert np.allclose(out[t], ref, rtol=1e-11, atol=1e-13), t
+
+
+def pin_ffn_silu_closed_forms(o):
+    """Planted one-hot weights make g = (z, -z) and u = (1, 1), so the down
+    rows read silu(z) - silu(-z) = z and silu(z) + silu(-z) = z tanh(z/2)."""
+    H, I, E = 4, 2, 1
+    for z in (0.0, 0.75, -2.5, 6.0, 0.015625):
+        x = _bits([[z, 1.0, 0.0, 0.0]])
+        wg = np.zeros((E, I, H), np.uint16)
+        wu = np.zeros((E, I, H), np.uint16)
+        wd = np.zeros((E, H, I), np.uint16)
+        wg[0, 0, 0] = _bits([1.0])[0]
+        wg[0, 1, 0] = _bits([-1.0])[0]
+        wu[0, 0, 1] = wu[0, 1, 1] = _bits([1.0])[0]
+        wd[0, 0] = _bits([1.0, -1.0])
+        wd[0, 1] = _bits([1.0, 1.0])
+        wd[0, 2] = _bits([1.0, 0.0])
+        out, act = o.expert_ffn(x, np.zeros((1, 1), np.int32), np.ones((1, 1)),
+                                wg, wu, wd, want_act=True)
+        assert math.isclose(out[0, 0], z, rel_tol=1e-14, abs_tol=1e-15), z
+        assert math.isclose(out[0, 1], z * math.tanh(z / 2), rel_tol=1e-13, abs_tol=1e-15), z
+        assert math.isclose(out[0, 2], float(_silu(z)), rel_tol=1e-14, abs_tol=1e-15), z
+        assert out[0, 3] == 0.0
+        assert math.isclose(act[0, 0, 0], float(_silu(z)), rel_tol=1e-14, abs_tol=1e-15)
+    # silu(0) is exactly 0
+    x = _bits([[0.0, 1.0, 0.0, 0.0]])
+    out = o.expert_ffn(x, np.zeros((1, 1), np.int32), np.ones((1, 1)), wg, wu, wd)
+    assert np.all(out == 0.0)
+
+
+def pin_ffn_dense_soft_moe(o):
+    """k = E with the router's own weights: the layer is the dense soft MoE
+    sum_e softmax_e(l) * SwiGLU_e(x), computed here with numpy."""
+    M, H, I, E = 2, 32, 16, 6
+    x = synth.normal_bf16((M, H), 1.0, 22, 1)
+    wgt = synth.layer_weights(H, E, I, seed=22)
+    for key in ("gate", "up", "down"):
+        wgt[key] = synth.bf16_bits(F(wgt[key]) * 8)
+    r = o.route(x, wgt["router"], None, E)
+    out = o.expert_ffn(x, r["idx"], r["w"], wgt["gate"], wgt["up"], wgt["down"])
+    xf = F(x).astype(np.float64)
+    logits = xf @ F(wgt["router"]).astype(np.float64).T
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    for t in range(M):
+        ref = np.zeros(H)
+        for e in range(E):
+            g = F(wgt["gate"][e]).astype(np.float64) @ xf[t]
+            u = F(wgt["up"][e]).astype(np.float64) @ xf[t]
+            ref += p[t, e] * (F(wgt["down"][e]).astype(np.float64) @ (_silu(g) * u))
+        assert np.allclose(out[t], ref, rtol=1e-10, atol=1e-13)
+
+
+def pin_ffn_linearity_and_relabeling(o):
+    """Doubling W_down doubles the output exactly; the output is linear in the
+    routing weights; relabeling experts (moving their slabs and ids together)
+    leaves it bitwise unchanged."""
+    M, H, I, E, k = 2, 24, 16, 6, 3
+    x = synth.normal_bf16((M, H), 1.0, 23, 1)
+    wgt = synth.layer_weights(H, E, I, seed=23)
+    idx = np.array([[4, 1, 5], [1, 0, 2]], np.int32)
+    w = np.array([[0.5, 0.3, 0.2], [0.6, 0.25, 0.15]])
+    out = o.expert_ffn(x, idx, w, wgt["gate"], wgt["up"], wgt["down"])
+    wd2 = synth.bf16_bits(F(wgt["down"]) * 2)
+    out2 = o.expert_ffn(x, idx, w, wgt["gate"], wgt["up"], wd2)
+    assert np.array_equal(out2, 2 * out)
+    # linear in w: one-hot weights per slot sum back to the full result
+    parts = []
+    for j in range(k):
+        wj = np.zeros_like(w)
+        wj[:, j] = w[:, j]
+        parts.append(o.expert_ffn(x, idx, wj, wgt["gate"], wgt["up"], wgt["down"]))
+    assert np.allclose(sum(parts), out, rtol=1e-13, atol=1e-16)
+    # slot j alone with weight 1 is that expert's own output; every slot
+    # contributes (a dropped slot would leave its part at zero)
+    for j in range(k):
+        assert np.any(parts[j] != 0.0)
+    perm = np.array([3, 5, 0, 4, 2, 1])        # new id of old expert e
+    inv = np.argsort(perm)
+    out_p = o.expert_ffn(x, perm[idx].astype(np.int32), w, wgt["gate"][inv],
+                         wgt["up"][inv], wgt["down"][inv])
+    assert np.array_equal(out_p, out)
+
+
+def pin_ffn_rejects_bad_ids(o):
+    x = np.zeros((1, 8), np.uint16)
+    wg = np.zeros((2, 4, 8), np.uint16)
+    wd = np.zeros((2, 8, 4), np.uint16)
+    for bad in (-1, 2):
+        try:
+            o.expert_ffn(x, np.array([[bad]], np.int32), np.ones((1, 1)), wg, wg, wd)
+        except ValueError:
+            continue
+        raise AssertionError("out-of-range expert id accepted")
+
+
+# ------------------------------------------------------------------ lm_head
+
+def pin_lmhead_matches_numpy_argmax(o):
+    """Greedy token equals numpy's first-occurrence argmax of the fp32-rounded
+    logits; zmax and gap match numpy's fp64 logits."""
+    M, H, V = 3, 64, 300
+    h = synth.normal_bf16((M, H), 1.0, 31, 1)
+    wl = synth.normal_bf16((V, H), 0.02, 31, 2)
+    wl[200] = wl[57]                         # duplicated rows: an exact tie
+    r = o.lmhead(h, wl)
+    z = F(h).astype(np.float64) @ F(wl).astype(np.float64).T
+    tok = np.argmax(z.astype(np.float32), axis=1)
+    assert np.array_equal(r["tok"], tok)
+    assert np.array_equal(r["zmax"], z[np.arange(M), tok])
+    s = -np.sort(-z, axis=1)
+    assert np.array_equal(r["gap"], s[:, 0] - s[:, 1])
+
+
+def pin_lmhead_planted(o):
+    """A row equal to the hidden state wins (also at the first and last row);
+    duplicated winners resolve to the lower id; a zero hidden state gives
+    token 0."""
+    M, H, V = 4, 32, 64
+    h = synth.normal_bf16((M, H), 1.0, 32, 1)
+    wl = synth.normal_bf16((V, H), 0.02, 32, 2)
+    wl[41] = h[0]
+    wl[13] = h[1]
+    wl[50] = h[1]
+    wl[V - 1] = h[2]
+    wl[0] = h[3]
+    r = o.lmhead(h, wl)
+    assert r["tok"].tolist() == [41, 13, V - 1, 0]
+    assert r["gap"][1] == 0.0
+    r0 = o.lmhead(np.zeros((1, H), np.uint16), wl)
+    assert r0["tok"].tolist() == [0]
+
+
+ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]
