@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Cold-weight bench of the batch-1 MoE verify hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of M verify tokens:
+  moe_layer     router gate GEMV + softmax top-k, then the selected experts'
+                SwiGLU FFN with weighted combine (one MoE layer verify step)
+  lmhead_argmax lm_head GEMV fused with the greedy argmax
+Weights are seeded synthetic bf16 ~N(0, 0.02) generated on the device: 16
+distinct MoE layers (8.06 GB each) rotated step by step and two lm_head
+copies (805 MB each) alternated, so every weight byte comes from HBM (the
+gap between two visits of the same bytes is far beyond the 256 MB of
+Infinity Cache plus L2).
+
+Prints ONE JSON line. `value` is algorithmic bytes per step / step time in
+GB/s, where algorithmic bytes = every distinct selected expert's weights once,
+the router gate, the lm_head, and the activations and outputs.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--M", type=int, default=6)
+    ap.add_argument("--layers", type=int, default=16, help="distinct MoE layers rotated")
+    ap.add_argument("--lm-copies", type=int, default=2)
+    ap.add_argument("--router-copies", type=int, default=128,
+                    help="distinct router gates rotated in the gate-only timing")
+    ap.add_argument("--zipf-alpha", type=float, default=None,
+                    help="add a Zipf(1.1)-shaped router bias of this strength")
+    ap.add_argument("--cpu-sample-steps", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="only run this many steps (for rocprofv3), print nothing else")
+    return ap.parse_args()
+
+
+def src_digest(*names: str) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "moe_speculative_verify_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, digest: str):
+    """HBM bytes per dispatch from committed rocprofv3 counter runs, or None
+    when they are missing or were taken on different kernel source."""
+    path = os.path.join(PROFILES, f"{kernel}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("source_digest") != digest:
+        return None
+    return c.get("hbm_bytes_per_dispatch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_speculative_verify_amd as mv
+    import synth
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = mv.lib()
+
+    cfg = synth.WORKLOADS["layer_m6"]
+    H, E, I, k = cfg["H"], cfg["E"], cfg["I"], cfg["k"]
+    V = synth.WORKLOADS["lmhead"]["V"]
+    M = args.M
+
+    # ------------------------------------------------------------ inputs
+    t0 = time.time()
+    K_ = synth.KIND
+    layers = []
+    for l in range(args.layers):
+        layers.append(dict(
+            router=synth.device_normal_bf16((E, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, l, K_["router"]),
+            gate=synth.device_normal_bf16((E, I, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, l, K_["gate"]),
+            up=synth.device_normal_bf16((E, I, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, l, K_["up"]),
+            down=synth.device_normal_bf16((E, H, I), synth.WEIGHT_STD, synth.WEIGHT_SEED, l, K_["down"]),
+        ))
+        log(f"layer {l} weights generated ({time.time() - t0:.1f} s)")
+    lms = [synth.device_normal_bf16((V, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 100 + c,
+                                    K_["lm_head"]) for c in range(args.lm_copies)]
+    routers = [synth.device_normal_bf16((E, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 200 + c,
+                                        K_["router"]) for c in range(args.router_copies)]
+    log(f"weights ready: {torch.cuda.memory_allocated() / 1e9:.1f} GB ({time.time() - t0:.1f} s)")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x = up(synth.activations(M, H))
+    h = up(synth.activations(M, H, tag=1))
+    bias = None
+    if args.zipf_alpha is not None:
+        bias = torch.from_numpy(synth.zipf_bias(E, args.zipf_alpha)).to(dev)
+    idx = torch.empty((M, k), dtype=torch.int32, device=dev)
+    tw = torch.empty((M, k), dtype=torch.float32, device=dev)
+    out = torch.empty((M, H), dtype=torch.float32, device=dev)
+    am = torch.empty(M, dtype=torch.int32, device=dev)
+    ws_layer = torch.zeros(L.moe_layer_workspace_bytes(M, H, I, E, k), dtype=torch.uint8, device=dev)
+    ws_lm = torch.zeros(L.lmhead_argmax_workspace_bytes(M, V), dtype=torch.uint8, device=dev)
+    ws_route = torch.zeros(L.moe_route_workspace_bytes(M, E), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    # raw C-ABI argument tuples, built once so the timed loop only enqueues
+    layer_args = [(x.data_ptr(), Lw["router"].data_ptr(), bias.data_ptr() if bias is not None else None,
+                   Lw["gate"].data_ptr(), Lw["up"].data_ptr(), Lw["down"].data_ptr(),
+                   M, H, I, E, k, idx.data_ptr(), tw.data_ptr(), out.data_ptr(),
+                   ws_layer.data_ptr(), ws_layer.numel(), stream) for Lw in layers]
+    lm_args = [(h.data_ptr(), w.data_ptr(), M, H, V, am.data_ptr(), None, ws_lm.data_ptr(),
+                ws_lm.numel(), stream) for w in lms]
+    route_args = [(x.data_ptr(), r.data_ptr(), bias.data_ptr() if bias is not None else None,
+                   M, H, E, k, idx.data_ptr(), tw.data_ptr(), None, ws_route.data_ptr(),
+                   ws_route.numel(), stream) for r in routers]
+
+    def check(fn, st):
+        if st != 0:
+            raise RuntimeError(f"{fn}: {mv.status_str(st)}")
+
+    def step(s):
+        check("moe_layer", L.moe_layer(*layer_args[s % len(layer_args)]))
+        check("lmhead_argmax", L.lmhead_argmax(*lm_args[s % len(lm_args)]))
+
+    if args.profile_steps:
+        for s in range(args.profile_steps):
+            step(s)
+            check("moe_route", L.moe_route(*route_args[s % len(route_args)]))
+        torch.cuda.synchronize()
+        log(f"profile run: {args.profile_steps} steps done")
+        return
+
+    # --------------------------------------------- algorithmic bytes per step
+    D = []
+    for l in range(len(layers)):
+        check("moe_layer", L.moe_layer(*layer_args[l]))
+        torch.cuda.synchronize()
+        D.append(len(np.unique(idx.cpu().numpy())))
+    per_expert = 3 * I * H * 2
+    io_layer = M * H * 2 + M * k * 8 + M * H * 4 + (E * 4 if bias is not None else 0)
+    layer_bytes = [E * H * 2 + d * per_expert + io_layer for d in D]
+    lm_bytes = V * H * 2 + M * H * 2 + M * 4
+    route_bytes = E * H * 2 + M * H * 2 + M * k * 8 + (E * 4 if bias is not None else 0)
+    nl = len(layers)
+    K = args.steps
+    step_bytes_mean = (sum(layer_bytes[s % nl] for s in range(args.warmup, args.warmup + K)) / K
+                       + lm_bytes)
+
+    # --------------------------------------------------------- timed steps
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t_start = time.perf_counter()
+    ev0.record()
+    for s in range(args.warmup, args.warmup + K):
+        step(s)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_start) * 1e3 / K
+    gpu_ms = ev0.elapsed_time(ev1) / K
+    log(f"{K} steps: {wall_ms * 1e3:.1f} us/step wall, {gpu_ms * 1e3:.1f} us/step events")
+
+    # ------------------ per-call durations, HIP events on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for s in range(K):
+        evs[s][0].record()
+        check("moe_layer", L.moe_layer(*layer_args[s % nl]))
+        evs[s][1].record()
+        check("lmhead_argmax", L.lmhead_argmax(*lm_args[s % len(lm_args)]))
+        evs[s][2].record()
+    torch.cuda.synchronize()
+    layer_us = [evs[s][0].elapsed_time(evs[s][1]) * 1e3 for s in range(K)]
+    lm_us = [evs[s][1].elapsed_time(evs[s][2]) * 1e3 for s in range(K)]
+    layer_us_mean = sum(layer_us) / K
+    lm_us_mean = sum(lm_us) / K
+    layer_bytes_mean = sum(layer_bytes[s % nl] for s in range(K)) / K
+
+    # gate only: router GEMV + top-k over rotating router copies
+    R = len(route_args)
+    for s in range(min(R, 16)):
+        check("moe_route", L.moe_route(*route_args[s]))
+    torch.cuda.synchronize()
+    re0 = torch.cuda.Event(enable_timing=True)
+    re1 = torch.cuda.Event(enable_timing=True)
+    re0.record()
+    for s in range(R):
+        check("moe_route", L.moe_route(*route_args[s]))
+    re1.record()
+    torch.cuda.synchronize()
+    route_us = re0.elapsed_time(re1) * 1e3 / R
+
+    lm_gbps = lm_bytes / (lm_us_mean * 1e-6) / 1e9
+    layer_gbps = layer_bytes_mean / (layer_us_mean * 1e-6) / 1e9
+    traffic = load_traffic("lmhead_argmax", src_digest("lmhead.hip", "common.h"))
+
+    # ------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline and args.cpu_sample_steps > 0:
+        import oracle
+
+        def host_bits(t):
+            return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+        n = args.cpu_sample_steps
+        xb, hb = host_bits(x), host_bits(h)
+        bias_np = None if bias is None else bias.cpu().numpy()
+        samples = []
+        for s in range(n):
+            Lw = layers[s % nl]
+            wr = host_bits(Lw["router"])
+            # routing first (untimed) to know which experts to read back
+            r = oracle.route(xb, wr, bias_np, k)
+            uniq, inv = np.unique(r["idx"], return_inverse=True)
+            sel = torch.as_tensor(uniq, dtype=torch.long, device=dev)
+            sub = {key: host_bits(Lw[key].index_select(0, sel)) for key in ("gate", "up", "down")}
+            wl = host_bits(lms[s % len(lms)])
+            t1 = time.perf_counter()
+            r = oracle.route(xb, wr, bias_np, k)
+            oracle.expert_ffn(xb, inv.reshape(r["idx"].shape).astype(np.int32), r["w"],
+                              sub["gate"], sub["up"], sub["down"])
+            oracle.lmhead(hb, wl)
+            samples.append(time.perf_counter() - t1)
+            del wl, sub
+        cpu_s = sum(samples) / n
+        cpu_bytes = sum(layer_bytes[s % nl] for s in range(n)) / n + lm_bytes
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count()))
+        cpu = {"value": round(cpu_bytes / cpu_s / 1e9, 3), "unit": "GB/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"{n} full steps (M={M} MoE layer route+experts+combine and "
+                         f"lm_head argmax) in fp64, {cpu_s * 1e3:.0f} ms per step"}
+        log(f"cpu oracle: {cpu_s * 1e3:.0f} ms/step on {cores} threads")
+
+    res = {
+        "metric": "cold-weight HBM GB/s (% of peak) + us per MoE-layer verify step, M=6",
+        "value": round(step_bytes_mean / (wall_ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"moe_layer_verify_step_M{M}+lm_head_argmax",
+                   "M": M, "hidden": H, "experts": E, "intermediate": I, "top_k": k,
+                   "vocab": V, "layers_rotated": nl, "lm_head_copies": len(lms),
+                   "zipf_alpha": args.zipf_alpha, "seeds": [synth.WEIGHT_SEED, synth.ACT_SEED]},
+        "frac_of_hbm_peak": round(step_bytes_mean / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "gpu_ms_per_step_events": round(gpu_ms, 4),
+        "moe_layer": {"us": round(layer_us_mean, 2), "GBps": round(layer_gbps, 1),
+                      "frac": round(layer_gbps / HBM_PEAK_GBPS, 4),
+                      "bytes": int(layer_bytes_mean), "distinct_experts_mean": sum(D) / len(D)},
+        "lm_head": {"us": round(lm_us_mean, 2), "GBps": round(lm_gbps, 1),
+                    "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "bytes": lm_bytes},
+        "router_gate_cold": {"us": round(route_us, 2),
+                             "GBps": round(route_bytes / (route_us * 1e-6) / 1e9, 1),
+                             "copies": R},
+        "roofline": {"kernel": "lmhead_argmax", "bound": "hbm",
+                     "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * moe_verify.h -- C ABI of the MI355X (gfx950) batch-1 MoE verify hot path.
+ *
+ * The path is the weight-bandwidth-bound part of one speculative-decode
+ * verify step of a 512-expert MoE model, as the LMSYS post "Chasing the
+ * batch-1 floor: Ling-3.0-flash speculative decode on Blackwell" describes
+ * it:
+ *   - router chain: gate matvec then top-k (section "PDL: the latency floor
+ *     of stacked small kernels", Fig. 7), gate weight in bf16 (section
+ *     "bf16 router gate and lm_head");
+ *   - MoE chain: expert grouping, up projection with SwiGLU folded into it,
+ *     down projection and an fp32 weighted combine (section "Two fusions and
+ *     a retune");
+ *   - lm_head projection in bf16 feeding the greedy verdict (section "bf16
+ *     router gate and lm_head"; the verdict itself, section "The shape of a
+ *     single-request step", Fig. 3).
+ *
+ * Conventions (every entry point):
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The
+ *     library never allocates, frees, copies to the host or synchronises.
+ *   - bf16 tensors are raw uint16 bit patterns; every matrix is row-major
+ *     with the reduction axis contiguous.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = legacy default
+ *     stream) and runs asynchronously. A device fault surfaces at the
+ *     caller's next synchronisation.
+ *   - Device values (expert ids, routing weights) are never read on the
+ *     host: one call can consume what the previous call on the same stream
+ *     produced.
+ *   - The status is MOE_OK when the work was enqueued. Errors come from
+ *     host-side argument checks (nothing is launched then) or from the
+ *     launch itself (MOE_ERR_LAUNCH).
+ *   - Pointers to bf16/fp32 tensors must be 16-byte aligned (128-bit
+ *     loads). Shape limits: 1 <= M <= 16, 1 <= k <= min(E, 16),
+ *     1 <= E <= 1024, H and I multiples of 8 and at most 16384,
+ *     1 <= V < 2^31.
+ *   - Workspaces: size from the matching *_workspace_bytes query,
+ *     16-byte aligned, ZERO-FILLED before their first use (one
+ *     moe_workspace_clear call, or any zero fill). Every call leaves the
+ *     counters it uses at zero again, so a workspace is reused without
+ *     clearing. Two calls that may run concurrently must not share a
+ *     workspace.
+ *   - Results are deterministic: no floating-point atomics; rerunning a
+ *     call on the same inputs gives bitwise-equal outputs, and a token's
+ *     results do not depend on the other tokens in the call.
+ */
+#ifndef MOE_VERIFY_H
+#define MOE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status_t;
+
+enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL */
+    MOE_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+    MOE_ERR_UNSUPPORTED = 3, /* a size this library does not handle */
+    MOE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+    MOE_ERR_WORKSPACE = 5,   /* workspace smaller than its query */
+    MOE_ERR_LAUNCH = 6       /* the kernel launch failed */
+};
+
+/* ABI version; bumps on any signature or semantic change. */
+int32_t moe_abi_version(void);
+
+/* Static string naming a status (never NULL). */
+const char *moe_status_str(moe_status_t status);
+
+/* Zero-fill a workspace on `stream` with a fill kernel (capturable in a
+ * graph). bytes must be a multiple of 16. */
+moe_status_t moe_workspace_clear(void *workspace, size_t bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_route -- router gate GEMV, softmax top-k, renormalised weights.
+ * (router chain: gate matvec -> top-k; section "PDL: the latency floor of
+ *  stacked small kernels", Fig. 7; bf16 gate, section "bf16 router gate
+ *  and lm_head")
+ *
+ *   x         [M,H] bf16   token activations
+ *   w_router  [E,H] bf16   gate weight
+ *   bias      [E]   fp32   added to every logit before selection and
+ *                          softmax, or NULL for none
+ *   topk_idx  [M,k] int32  out: the k experts with the largest fp32 logits,
+ *                          in descending logit order, ties to the lower id
+ *   topk_w    [M,k] fp32   out: softmax of the selected logits (equal to a
+ *                          softmax over all E renormalised over the set)
+ *   logits    [M,E] fp32   optional out (NULL skips): l = x.w_router^T + bias
+ *   workspace              moe_route_workspace_bytes(M, E) bytes
+ * ---------------------------------------------------------------------- */
+size_t moe_route_workspace_bytes(int32_t M, int32_t E);
+moe_status_t moe_route(const uint16_t *x, const uint16_t *w_router,
+                       const float *bias, int32_t M, int32_t H, int32_t E,
+                       int32_t k, int32_t *topk_idx, float *topk_w,
+                       float *logits, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_expert_ffn -- selected experts' SwiGLU FFN with weighted combine.
+ * (MoE chain: grouping -> up-GEMM with SwiGLU epilogue -> down-GEMM ->
+ *  combine; section "Two fusions and a retune")
+ *
+ *   x         [M,H]   bf16   token activations
+ *   topk_idx  [M,k]   int32  expert of each (token, slot) pair; ids may
+ *                            repeat across tokens; an id outside [0,E)
+ *                            makes the pair contribute nothing
+ *   topk_w    [M,k]   fp32   routing weight of each pair
+ *   w_gate    [E,I,H] bf16   gate projection rows
+ *   w_up      [E,I,H] bf16   up projection rows
+ *   w_down    [E,H,I] bf16   down projection rows
+ *   out       [M,H]   fp32   out (overwritten):
+ *       out[t,:] = sum_{j<k} topk_w[t,j] * W_down[e] (silu(W_gate[e] x_t)
+ *                  * (W_up[e] x_t)),  e = topk_idx[t,j],
+ *       silu(z) = z / (1 + exp(-z)) in fp32, the SwiGLU product rounded once
+ *       to bf16 before the down projection, slots summed in order in fp32.
+ *   workspace                moe_expert_ffn_workspace_bytes(M,H,I,E,k) bytes
+ *
+ * Every distinct selected expert's weights are read from HBM exactly once
+ * per call, however many tokens chose it.
+ * ---------------------------------------------------------------------- */
+size_t moe_expert_ffn_workspace_bytes(int32_t M, int32_t H, int32_t I,
+                                      int32_t E, int32_t k);
+moe_status_t moe_expert_ffn(const uint16_t *x, const int32_t *topk_idx,
+                            const float *topk_w, const uint16_t *w_gate,
+                            const uint16_t *w_up, const uint16_t *w_down,
+                            int32_t M, int32_t H, int32_t I, int32_t E,
+                            int32_t k, float *out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_layer -- one MoE layer verify step: moe_route then moe_expert_ffn,
+ * enqueued back to back on `stream` (same arguments and results as the two
+ * calls; topk_idx/topk_w are written and then consumed on the device).
+ *   workspace  moe_layer_workspace_bytes(M,H,I,E,k) bytes
+ * ---------------------------------------------------------------------- */
+size_t moe_layer_workspace_bytes(int32_t M, int32_t H, int32_t I, int32_t E,
+                                 int32_t k);
+moe_status_t moe_layer(const uint16_t *x, const uint16_t *w_router,
+                       const float *bias, const uint16_t *w_gate,
+                       const uint16_t *w_up, const uint16_t *w_down,
+                       int32_t M, int32_t H, int32_t I, int32_t E, int32_t k,
+                       int32_t *topk_idx, float *topk_w, float *out,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * lmhead_argmax -- lm_head GEMV fused with the greedy argmax.
+ * (bf16 lm_head, section "bf16 router gate and lm_head"; greedy decoding,
+ *  section "The shape of a single-request step")
+ *
+ *   h          [M,H] bf16   final hidden states
+ *   w_lm       [V,H] bf16   lm_head rows
+ *   argmax     [M]   int32  out: first v with the largest fp32 logit
+ *                           z[t,v] = h[t,:].w_lm[v,:] (lowest id on ties)
+ *   max_logit  [M]   fp32   optional out (NULL skips): z[t, argmax[t]]
+ *   workspace               lmhead_argmax_workspace_bytes(M, V) bytes
+ *
+ * The [M,V] logits are never written to memory.
+ * ---------------------------------------------------------------------- */
+size_t lmhead_argmax_workspace_bytes(int32_t M, int32_t V);
+moe_status_t lmhead_argmax(const uint16_t *h, const uint16_t *w_lm,
+                           int32_t M, int32_t H, int32_t V, int32_t *argmax,
+                           float *max_logit, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

@@ -1,0 +1,256 @@
+"""Python binding of libmoeverify.so, the gfx950 MoE verify hot path.
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream; nothing here computes.
+The names match the C entry points declared in include/moe_verify.h.
+
+bf16 tensors may be torch.bfloat16, torch.int16 or torch.uint16 (raw bits).
+If the library is not built, importing works but every call raises
+RuntimeError: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoeverify.so")
+
+MOE_OK = 0
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPPORTED",
+          4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_LAUNCH"}
+
+#: every symbol the header declares
+EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_clear",
+           "moe_route_workspace_bytes", "moe_route",
+           "moe_expert_ffn_workspace_bytes", "moe_expert_ffn",
+           "moe_layer_workspace_bytes", "moe_layer",
+           "lmhead_argmax_workspace_bytes", "lmhead_argmax")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({status_str(status)})")
+        self.status = status
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_S = ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (RuntimeError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                               "(run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_abi_version.restype = ctypes.c_int32
+        L.moe_abi_version.argtypes = []
+        L.moe_status_str.restype = ctypes.c_char_p
+        L.moe_status_str.argtypes = [ctypes.c_int32]
+        L.moe_workspace_clear.restype = ctypes.c_int32
+        L.moe_workspace_clear.argtypes = [_P, _S, _P]
+        L.moe_route_workspace_bytes.restype = _S
+        L.moe_route_workspace_bytes.argtypes = [_I, _I]
+        L.moe_route.restype = ctypes.c_int32
+        L.moe_route.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _S, _P]
+        L.moe_expert_ffn_workspace_bytes.restype = _S
+        L.moe_expert_ffn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+        L.moe_expert_ffn.restype = ctypes.c_int32
+        L.moe_expert_ffn.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                     _P, _P, _S, _P]
+        L.moe_layer_workspace_bytes.restype = _S
+        L.moe_layer_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+        L.moe_layer.restype = ctypes.c_int32
+        L.moe_layer.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                _P, _P, _P, _P, _S, _P]
+        L.lmhead_argmax_workspace_bytes.restype = _S
+        L.lmhead_argmax_workspace_bytes.argtypes = [_I, _I]
+        L.lmhead_argmax.restype = ctypes.c_int32
+        L.lmhead_argmax.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _S, _P]
+        _lib = L
+    return _lib
+
+
+def moe_abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def status_str(status: int) -> str:
+    return lib().moe_status_str(int(status)).decode()
+
+
+moe_status_str = status_str
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+# ----------------------------------------------------------- marshalling
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _ptr(t: torch.Tensor | None, name: str, dtypes=None, shape=None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+class Workspace:
+    """A zero-filled device workspace, grown on demand, one per key.
+
+    The library leaves every counter it uses at zero, so a workspace is
+    reused across calls on the same stream without clearing.
+    """
+
+    _pool: dict = {}
+
+    @classmethod
+    def get(cls, kind: str, nbytes: int, device, stream_handle: int) -> torch.Tensor:
+        key = (kind, torch.device(device).index, stream_handle)
+        ws = cls._pool.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            cls._pool[key] = ws
+        return ws
+
+
+def moe_workspace_clear(ws: torch.Tensor, stream=None) -> None:
+    _check("moe_workspace_clear",
+           lib().moe_workspace_clear(_ptr(ws, "workspace"), ws.numel() * ws.element_size(),
+                                     _stream(stream)))
+
+
+def moe_route_workspace_bytes(M: int, E: int) -> int:
+    return lib().moe_route_workspace_bytes(M, E)
+
+
+def moe_expert_ffn_workspace_bytes(M: int, H: int, I: int, E: int, k: int) -> int:
+    return lib().moe_expert_ffn_workspace_bytes(M, H, I, E, k)
+
+
+def moe_layer_workspace_bytes(M: int, H: int, I: int, E: int, k: int) -> int:
+    return lib().moe_layer_workspace_bytes(M, H, I, E, k)
+
+
+def lmhead_argmax_workspace_bytes(M: int, V: int) -> int:
+    return lib().lmhead_argmax_workspace_bytes(M, V)
+
+
+def moe_route(x, w_router, k: int, bias=None, *, want_logits=False, out=None,
+              workspace=None, stream=None):
+    """Router gate GEMV + softmax top-k. Returns (topk_idx, topk_w[, logits])."""
+    M, H = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    idx, w, logits = out if out is not None else (None, None, None)
+    if idx is None:
+        idx = torch.empty((M, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((M, k), dtype=torch.float32, device=dev)
+    if want_logits and logits is None:
+        logits = torch.empty((M, E), dtype=torch.float32, device=dev)
+    st = _stream(stream)
+    nbytes = moe_route_workspace_bytes(M, E)
+    ws = workspace if workspace is not None else Workspace.get("route", nbytes, dev, st)
+    _check("moe_route", lib().moe_route(
+        _ptr(x, "x", _BF16), _ptr(w_router, "w_router", _BF16, (E, H)),
+        _ptr(bias, "bias", (torch.float32,), (E,)), M, H, E, k,
+        _ptr(idx, "topk_idx", (torch.int32,), (M, k)),
+        _ptr(w, "topk_w", (torch.float32,), (M, k)),
+        _ptr(logits, "logits", (torch.float32,), (M, E)) if want_logits else None,
+        _ptr(ws, "workspace"), ws.numel(), st))
+    return (idx, w, logits) if want_logits else (idx, w)
+
+
+def moe_expert_ffn(x, topk_idx, topk_w, w_gate, w_up, w_down, *, out=None,
+                   workspace=None, stream=None):
+    """Selected experts' SwiGLU FFN + weighted combine. Returns out [M,H] fp32."""
+    M, H = x.shape
+    E, I, _ = w_gate.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.float32, device=dev)
+    st = _stream(stream)
+    nbytes = moe_expert_ffn_workspace_bytes(M, H, I, E, k)
+    ws = workspace if workspace is not None else Workspace.get("ffn", nbytes, dev, st)
+    _check("moe_expert_ffn", lib().moe_expert_ffn(
+        _ptr(x, "x", _BF16), _ptr(topk_idx, "topk_idx", (torch.int32,), (M, k)),
+        _ptr(topk_w, "topk_w", (torch.float32,), (M, k)),
+        _ptr(w_gate, "w_gate", _BF16, (E, I, H)), _ptr(w_up, "w_up", _BF16, (E, I, H)),
+        _ptr(w_down, "w_down", _BF16, (E, H, I)), M, H, I, E, k,
+        _ptr(out, "out", (torch.float32,), (M, H)), _ptr(ws, "workspace"), ws.numel(), st))
+    return out
+
+
+def moe_layer(x, w_router, w_gate, w_up, w_down, k: int, bias=None, *, out=None,
+              workspace=None, stream=None):
+    """Route + expert FFN in one call. Returns (topk_idx, topk_w, out)."""
+    M, H = x.shape
+    E, I, _ = w_gate.shape
+    dev = x.device
+    idx, w, o = out if out is not None else (None, None, None)
+    if idx is None:
+        idx = torch.empty((M, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((M, k), dtype=torch.float32, device=dev)
+    if o is None:
+        o = torch.empty((M, H), dtype=torch.float32, device=dev)
+    st = _stream(stream)
+    nbytes = moe_layer_workspace_bytes(M, H, I, E, k)
+    ws = workspace if workspace is not None else Workspace.get("layer", nbytes, dev, st)
+    _check("moe_layer", lib().moe_layer(
+        _ptr(x, "x", _BF16), _ptr(w_router, "w_router", _BF16, (E, H)),
+        _ptr(bias, "bias", (torch.float32,), (E,)),
+        _ptr(w_gate, "w_gate", _BF16, (E, I, H)), _ptr(w_up, "w_up", _BF16, (E, I, H)),
+        _ptr(w_down, "w_down", _BF16, (E, H, I)), M, H, I, E, k,
+        _ptr(idx, "topk_idx", (torch.int32,), (M, k)),
+        _ptr(w, "topk_w", (torch.float32,), (M, k)),
+        _ptr(o, "out", (torch.float32,), (M, H)), _ptr(ws, "workspace"), ws.numel(), st))
+    return idx, w, o
+
+
+def lmhead_argmax(h, w_lm, *, want_max=False, out=None, workspace=None, stream=None):
+    """lm_head GEMV + greedy argmax. Returns argmax [M] int32 (, max_logit)."""
+    M, H = h.shape
+    V = w_lm.shape[0]
+    dev = h.device
+    am, ml = out if out is not None else (None, None)
+    if am is None:
+        am = torch.empty(M, dtype=torch.int32, device=dev)
+    if want_max and ml is None:
+        ml = torch.empty(M, dtype=torch.float32, device=dev)
+    st = _stream(stream)
+    nbytes = lmhead_argmax_workspace_bytes(M, V)
+    ws = workspace if workspace is not None else Workspace.get("lmhead", nbytes, dev, st)
+    _check("lmhead_argmax", lib().lmhead_argmax(
+        _ptr(h, "h", _BF16), _ptr(w_lm, "w_lm", _BF16, (V, H)), M, H, V,
+        _ptr(am, "argmax", (torch.int32,), (M,)),
+        _ptr(ml, "max_logit", (torch.float32,), (M,)) if want_max else None,
+        _ptr(ws, "workspace"), ws.numel(), st))
+    return (am, ml) if want_max else am

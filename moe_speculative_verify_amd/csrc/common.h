@@ -1,0 +1,170 @@
+// common.h -- device helpers and host-side argument checks shared by the
+// gfx950 kernels of the MoE verify hot path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_verify.h"
+
+namespace mv {
+
+// 16-byte vector of four 32-bit words: one 128-bit global or LDS access.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kMaxM = 16;          // verify tokens per call
+constexpr int kMaxK = 16;          // experts per token
+constexpr int kMaxNP = kMaxM * kMaxK;
+constexpr int kMaxE = 1024;
+constexpr int kMaxDim = 8192;      // largest H or I
+
+// ------------------------------------------------------------------ device
+
+// a.lo*b.lo + a.hi*b.hi + c on two bf16 pairs, fp32 accumulate
+// (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c,
+                                           false);
+}
+
+// Eight bf16 products of two 16-byte chunks added to acc.
+__device__ __forceinline__ float dot8_bf16(u32x4 w, u32x4 x, float acc)
+{
+    acc = dot2_bf16(w.x, x.x, acc);
+    acc = dot2_bf16(w.y, x.y, acc);
+    acc = dot2_bf16(w.z, x.z, acc);
+    acc = dot2_bf16(w.w, x.w, acc);
+    return acc;
+}
+
+// Weight streams are read once per call: non-temporal 128-bit loads keep
+// them from displacing the small reused tensors in the caches.
+__device__ __forceinline__ u32x4 load_stream(const u32x4 *p)
+{
+    return __builtin_nontemporal_load(p);
+}
+
+// Sum over the 64 lanes of a wavefront; every lane gets the total. The
+// butterfly order is fixed, so the result does not depend on timing.
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v += __shfl_xor(v, m);
+    return v;
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7F800000u) == 0x7F800000u)
+        return (u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Expert grouping of the (token, slot) pairs, built in LDS by every
+// workgroup that needs it. This is the pair-axis form of the grouping the
+// post describes in section "Two fusions and a retune": each pair compares
+// itself with every other pair to find its rank inside its expert's bucket
+// and whether it heads the bucket; nothing scales with the expert count.
+// Buckets are ordered by expert id, pairs inside a bucket by pair index.
+struct Groups {
+    int D;                       // distinct valid experts
+    int nvalid;                  // pairs with a valid expert id
+    int e[kMaxNP];               // expert of pair p, -1 if out of range
+    int head[kMaxNP];            // 1 if p is the first pair of its expert
+    int below[kMaxNP];           // valid pairs with a smaller expert id
+    int sorted[kMaxNP];          // pair ids, bucket by bucket
+    int dexp[kMaxNP];            // expert id of bucket d
+    int doff[kMaxNP + 1];        // bucket d = sorted[doff[d] .. doff[d+1])
+};
+
+__device__ inline void build_groups(const int *__restrict__ topk_idx, int NP,
+                                    int E, Groups &g)
+{
+    const int tid = threadIdx.x, nt = blockDim.x;
+    for (int p = tid; p < NP; p += nt) {
+        int e = topk_idx[p];
+        g.e[p] = (e >= 0 && e < E) ? e : -1;
+    }
+    __syncthreads();
+    // each pair against every other: rank in (expert, pair) order, whether
+    // it heads its bucket, and how many pairs sit in lower buckets
+    for (int p = tid; p < NP; p += nt) {
+        const int ep = g.e[p];
+        int below = 0, rank = 0, head = 1;
+        for (int q = 0; q < NP; ++q) {
+            const int eq = g.e[q];
+            if (eq < 0)
+                continue;
+            below += eq < ep;
+            rank += (eq < ep) || (eq == ep && q < p);
+            head &= !(eq == ep && q < p);
+        }
+        g.head[p] = (ep >= 0) ? head : 0;
+        g.below[p] = below;
+        if (ep >= 0)
+            g.sorted[rank] = p;
+    }
+    __syncthreads();
+    // bucket index of each head = heads with a smaller expert id
+    for (int p = tid; p < NP; p += nt) {
+        if (!g.head[p])
+            continue;
+        const int ep = g.e[p];
+        int d = 0;
+        for (int q = 0; q < NP; ++q)
+            d += g.head[q] && g.e[q] < ep;
+        g.dexp[d] = ep;
+        g.doff[d] = g.below[p];
+    }
+    if (tid == 0) {
+        int D = 0, nv = 0;
+        for (int p = 0; p < NP; ++p) {
+            D += g.head[p];
+            nv += g.e[p] >= 0;
+        }
+        g.D = D;
+        g.nvalid = nv;
+        g.doff[D] = nv;
+    }
+    __syncthreads();
+}
+
+// -------------------------------------------------------------------- host
+
+// Every workspace layout starts with the same 256-byte header whose first
+// word is the arrival ticket of the last-workgroup pattern; the ticket is zero
+// when a call starts and when it ends, so one workspace can serve every entry
+// point and shape in turn.
+constexpr size_t kWsHeader = 256;
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+inline size_t align_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+
+inline moe_status_t check_launch()
+{
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+// Shape gates shared by the MoE entry points.
+inline moe_status_t check_moe_shape(int32_t M, int32_t H, int32_t E, int32_t k)
+{
+    if (M < 1 || H < 1 || E < 1 || k < 1)
+        return MOE_ERR_SHAPE;
+    if (M > kMaxM || k > kMaxK || k > E || E > kMaxE)
+        return MOE_ERR_UNSUPPORTED;
+    if (H % 8 != 0 || H > kMaxDim)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+} // namespace mv

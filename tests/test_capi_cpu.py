@@ -1,0 +1,147 @@
+"""The C ABI on the CPU: the library loads, exports what include/moe_verify.h
+declares, and every host-side argument check returns its status without
+launching anything (no call here passes validation, so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_speculative_verify_amd as mv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_verify.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+
+# fake, never-dereferenced device addresses
+A = 1 << 20          # 16-byte aligned
+B = (1 << 20) + 4096
+MIS = (1 << 20) + 8  # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mv.LIB_PATH):
+        from moe_speculative_verify_amd import build
+        build.build()
+    return mv.lib()
+
+
+def test_exports_match_header(L):
+    decl = declared_functions()
+    assert decl == sorted(mv.EXPORTS)
+    for name in decl:
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(L, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(L):
+    assert mv.moe_abi_version() == 1
+    for s in range(7):
+        assert mv.status_str(s) and mv.status_str(s) != "unknown status"
+    assert mv.status_str(99) == "unknown status"
+
+
+def test_workspace_queries(L):
+    assert L.moe_route_workspace_bytes(6, 512) >= 6 * 512 * 4 + 4
+    assert L.moe_route_workspace_bytes(17, 512) == 0
+    assert L.moe_expert_ffn_workspace_bytes(6, 2560, 1024, 512, 8) >= 48 * 1024 * 2
+    assert L.moe_expert_ffn_workspace_bytes(6, 2560, 1000 + 4, 512, 8) == 0
+    assert L.moe_layer_workspace_bytes(6, 2560, 1024, 512, 8) >= max(
+        L.moe_route_workspace_bytes(6, 512), L.moe_expert_ffn_workspace_bytes(6, 2560, 1024, 512, 8))
+    assert L.lmhead_argmax_workspace_bytes(6, 157184) > 0
+    assert L.lmhead_argmax_workspace_bytes(0, 157184) == 0
+
+
+def route(L, x=A, w=A, bias=None, M=6, H=2560, E=512, k=8, idx=A, tw=A, lg=None,
+          ws=B, wsb=1 << 20):
+    return L.moe_route(x, w, bias, M, H, E, k, idx, tw, lg, ws, wsb, None)
+
+
+def test_route_checks(L):
+    assert route(L, x=None) == NULL
+    assert route(L, w=None) == NULL
+    assert route(L, idx=None) == NULL
+    assert route(L, ws=None) == NULL
+    assert route(L, M=0) == SHAPE
+    assert route(L, k=0) == SHAPE
+    assert route(L, M=17) == UNSUP
+    assert route(L, k=17) == UNSUP
+    assert route(L, E=4, k=8) == UNSUP
+    assert route(L, E=1025) == UNSUP
+    assert route(L, H=2561) == UNSUP
+    assert route(L, x=MIS) == ALIGN
+    assert route(L, w=MIS) == ALIGN
+    assert route(L, idx=A + 2) == ALIGN
+    assert route(L, ws=MIS) == ALIGN
+    assert route(L, wsb=100) == WS
+
+
+def ffn(L, x=A, idx=A, tw=A, wg=A, wu=A, wd=A, M=6, H=2560, I=1024, E=512, k=8,
+        out=A, ws=B, wsb=1 << 20):
+    return L.moe_expert_ffn(x, idx, tw, wg, wu, wd, M, H, I, E, k, out, ws, wsb, None)
+
+
+def test_expert_ffn_checks(L):
+    for kw in ("x", "idx", "tw", "wg", "wu", "wd", "out", "ws"):
+        assert ffn(L, **{kw: None}) == NULL, kw
+    assert ffn(L, I=0) == SHAPE
+    assert ffn(L, I=1020) == UNSUP
+    assert ffn(L, I=16384) == UNSUP
+    assert ffn(L, H=8200) == UNSUP
+    assert ffn(L, M=16, k=16, E=8) == UNSUP
+    for kw in ("x", "wg", "wu", "wd", "ws"):
+        assert ffn(L, **{kw: MIS}) == ALIGN, kw
+    assert ffn(L, out=A + 1) == ALIGN
+    assert ffn(L, wsb=48 * 1024 * 2 - 1) == WS
+
+
+def test_layer_checks(L):
+    def layer(**kw):
+        a = dict(x=A, w=A, bias=None, wg=A, wu=A, wd=A, M=6, H=2560, I=1024, E=512,
+                 k=8, idx=A, tw=A, out=A, ws=B, wsb=1 << 20)
+        a.update(kw)
+        return L.moe_layer(a["x"], a["w"], a["bias"], a["wg"], a["wu"], a["wd"], a["M"],
+                           a["H"], a["I"], a["E"], a["k"], a["idx"], a["tw"], a["out"],
+                           a["ws"], a["wsb"], None)
+    assert layer(w=None) == NULL
+    assert layer(out=None) == NULL
+    assert layer(E=1025) == UNSUP
+    assert layer(bias=A + 2) == ALIGN
+    assert layer(wsb=L.moe_layer_workspace_bytes(6, 2560, 1024, 512, 8) - 1) == WS
+
+
+def test_lmhead_checks(L):
+    def lm(h=A, w=A, M=6, H=2560, V=157184, am=A, ml=None, ws=B, wsb=1 << 20):
+        return L.lmhead_argmax(h, w, M, H, V, am, ml, ws, wsb, None)
+    assert lm(h=None) == NULL
+    assert lm(am=None) == NULL
+    assert lm(ws=None) == NULL
+    assert lm(V=0) == SHAPE
+    assert lm(M=17) == UNSUP
+    assert lm(H=12) == UNSUP
+    assert lm(w=MIS) == ALIGN
+    assert lm(ml=A + 2) == ALIGN
+    assert lm(wsb=16) == WS
+
+
+def test_workspace_clear_checks(L):
+    assert L.moe_workspace_clear(None, 256, None) == NULL
+    assert L.moe_workspace_clear(MIS, 256, None) == ALIGN
+    assert L.moe_workspace_clear(A, 250, None) == SHAPE
+    assert L.moe_workspace_clear(A, 0, None) == OK
+
+
+def test_binding_refuses_host_tensors(L):
+    import torch
+    x = torch.zeros((1, 256), dtype=torch.bfloat16)
+    w = torch.zeros((16, 256), dtype=torch.bfloat16)
+    with pytest.raises((ValueError, RuntimeError, AssertionError)):
+        mv.moe_route(x, w, 2)

@@ -1,0 +1,330 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Every case prints its name and shape before it touches the GPU. Indices must
+be bit-exact except where the oracle flags a near-tie (fp64 gap < 1e-3),
+where the GPU's choice must still be a valid top-k / argmax; fp32 outputs must
+satisfy max|gpu - ref| <= 1e-2 * max|ref| per tensor.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_speculative_verify_amd as mv
+import oracle
+import synth
+from gpu_util import (REL_TOL, TIE_BAND, assert_close, check_selection, compare_route,
+                      device_layer, oracle_ffn_from_device, to_dev, to_host_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    mv.lib()   # fails loudly when the HIP library is missing
+    yield
+    torch.cuda.synchronize()
+
+
+def say(*a):
+    print("CASE", *a, flush=True)
+
+
+def host_case(M, H, E, I, seed, bias_alpha=None):
+    x = synth.activations(M, H, seed=seed)
+    w = synth.layer_weights(H, E, I, seed=synth.WEIGHT_SEED + seed) if I else dict(
+        router=synth.normal_bf16((E, H), synth.WEIGHT_STD, synth.WEIGHT_SEED + seed, 0, 0))
+    bias = None if bias_alpha is None else synth.zipf_bias(E, bias_alpha)
+    return x, w, bias
+
+
+def run_route(x, wr, bias, k, want_logits=True):
+    b = None if bias is None else torch.from_numpy(bias).cuda()
+    idx, w, lg = mv.moe_route(to_dev(x) if isinstance(x, np.ndarray) else x,
+                              to_dev(wr) if isinstance(wr, np.ndarray) else wr, k, b,
+                              want_logits=True)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy()
+
+
+# ----------------------------------------------------------------- router
+
+ROUTE_CASES = [
+    # M, H, E, k, bias alpha
+    (1, 256, 16, 2, None),       # tiny layer's router
+    (3, 264, 20, 4, 1.0),        # ragged: 33 chunks per row, E not a multiple of 64
+    (16, 256, 16, 16, None),     # k = E
+    (1, 8, 1, 1, None),          # smallest shape
+    (6, 2560, 512, 8, None),     # router gate, verify width 6
+    (6, 2560, 512, 8, 1.0),      # with Zipf bias
+    (16, 2560, 512, 8, 1.0),     # block-16 verify
+    (5, 4096, 1024, 16, 0.5),    # largest E and k
+]
+
+
+@pytest.mark.parametrize("M,H,E,k,alpha", ROUTE_CASES)
+def test_route_matches_oracle(M, H, E, k, alpha):
+    say("route", M, H, E, k, alpha)
+    x, w, bias = host_case(M, H, E, None, seed=100 + M + E, bias_alpha=alpha)
+    gi, gw, gl = run_route(x, w["router"], bias, k)
+    ref = oracle.route(x, w["router"], bias, k)
+    compare_route(gi, gw, gl, ref, k)
+
+
+def test_route_zero_input_and_planted_ties():
+    say("route special cases")
+    M, H, E, k = 2, 256, 16, 4
+    wr = synth.normal_bf16((E, H), 0.02, 7, 1)
+    gi, gw, gl = run_route(np.zeros((M, H), np.uint16), wr, None, k)
+    assert np.array_equal(gi, np.tile(np.arange(k), (M, 1)))
+    assert np.all(gw == np.float32(1.0 / k)) and np.all(gl == 0.0)
+    # duplicated router rows tie exactly: the lower id must come first
+    x = synth.activations(M, H, seed=8)
+    ref = oracle.route(x, wr, None, k)
+    top = ref["idx"][:, 0]
+    wr2 = wr.copy()
+    wr2[0] = wr[top[0]]
+    wr2[15] = wr[top[1]]
+    gi, _, gl = run_route(x, wr2, None, k)
+    assert gi[0, 0] == min(0, top[0]) and top[0] in gi[0, :2] and 0 in gi[0, :2]
+    assert gl[0, 0] == gl[0, top[0]]
+    assert gi[1, 0] == top[1] and gi[1, 1] == 15
+    # exact doubling of x doubles the logits exactly and keeps the ids
+    x2 = synth.bf16_bits(synth.bf16_to_f32(x) * 2)
+    gi_a, _, gl_a = run_route(x, wr, None, k)
+    gi_b, _, gl_b = run_route(x2, wr, None, k)
+    assert np.array_equal(gi_a, gi_b) and np.array_equal(gl_b, 2 * gl_a)
+
+
+# ----------------------------------------------------------- expert FFN
+
+def _ffn_host(M, H, I, E, k, seed, skew=0.0):
+    x = synth.activations(M, H, seed=seed)
+    w = synth.layer_weights(H, E, I, seed=synth.WEIGHT_SEED + seed)
+    idx, tw = synth.random_routing(M, E, k, seed, skew)
+    return x, w, idx, tw
+
+
+FFN_CASES = [
+    # M, H, I, E, k
+    (1, 256, 128, 16, 2),        # tiny layer
+    (3, 264, 136, 20, 4),        # ragged chunk counts
+    (16, 256, 128, 16, 16),      # every token uses every expert
+    (2, 8, 8, 3, 2),             # smallest shape
+    (7, 512, 1032, 40, 3),       # I not a multiple of the 512-element lane stride
+]
+
+
+@pytest.mark.parametrize("M,H,I,E,k", FFN_CASES)
+def test_expert_ffn_matches_oracle(M, H, I, E, k):
+    say("expert_ffn", M, H, I, E, k)
+    x, w, idx, tw = _ffn_host(M, H, I, E, k, seed=200 + M + I)
+    dw = {key: to_dev(w[key]) for key in ("gate", "up", "down")}
+    out = mv.moe_expert_ffn(to_dev(x), torch.from_numpy(idx).cuda(),
+                            torch.from_numpy(tw).cuda(), dw["gate"], dw["up"], dw["down"])
+    got = out.cpu().numpy()
+    ref = oracle.expert_ffn(x, idx, tw.astype(np.float64), w["gate"], w["up"], w["down"])
+    assert_close(got, ref, "out")
+
+
+@pytest.fixture(scope="module")
+def full_layer():
+    say("generating full-size layer weights on the device")
+    return device_layer(2560, 512, 1024)
+
+
+@pytest.mark.parametrize("M,skew", [(1, 0.0), (6, 0.0), (16, 0.0), (16, 1.0)])
+def test_expert_ffn_full_size(full_layer, M, skew):
+    say("expert_ffn full size", M, skew)
+    k = 8
+    x = synth.activations(M, 2560, seed=300 + M)
+    idx, tw = synth.random_routing(M, 512, k, 300 + M, skew)
+    out = mv.moe_expert_ffn(to_dev(x), torch.from_numpy(idx).cuda(),
+                            torch.from_numpy(tw).cuda(), full_layer["gate"],
+                            full_layer["up"], full_layer["down"])
+    got = out.cpu().numpy()
+    ref = oracle_ffn_from_device(x, idx, tw.astype(np.float64), full_layer)
+    assert_close(got, ref, "out")
+
+
+def test_expert_ffn_identical_tokens_share_experts(full_layer):
+    """M identical tokens route identically: every row equals the M=1 row."""
+    say("expert_ffn identical tokens")
+    x1 = synth.activations(1, 2560, seed=41)
+    idx1, tw1 = synth.random_routing(1, 512, 8, 41)
+    M = 6
+    x = np.repeat(x1, M, axis=0)
+    idx = np.repeat(idx1, M, axis=0)
+    tw = np.repeat(tw1, M, axis=0)
+    a = mv.moe_expert_ffn(to_dev(x1), torch.from_numpy(idx1).cuda(), torch.from_numpy(tw1).cuda(),
+                          full_layer["gate"], full_layer["up"], full_layer["down"]).cpu().numpy()
+    b = mv.moe_expert_ffn(to_dev(x), torch.from_numpy(idx).cuda(), torch.from_numpy(tw).cuda(),
+                          full_layer["gate"], full_layer["up"], full_layer["down"]).cpu().numpy()
+    for t in range(M):
+        assert np.array_equal(b[t], a[0])
+
+
+def test_expert_ffn_invalid_ids_contribute_nothing():
+    say("expert_ffn invalid ids")
+    M, H, I, E, k = 3, 256, 128, 16, 4
+    x, w, idx, tw = _ffn_host(M, H, I, E, k, seed=51)
+    dw = {key: to_dev(w[key]) for key in ("gate", "up", "down")}
+    bad = idx.copy()
+    bad[0, 1] = -1
+    bad[2, 3] = E + 5
+    out = mv.moe_expert_ffn(to_dev(x), torch.from_numpy(bad).cuda(), torch.from_numpy(tw).cuda(),
+                            dw["gate"], dw["up"], dw["down"]).cpu().numpy()
+    tw0 = tw.astype(np.float64).copy()
+    tw0[0, 1] = 0.0
+    tw0[2, 3] = 0.0
+    fixed = np.where(bad < 0, 0, np.where(bad >= E, 0, bad)).astype(np.int32)
+    ref = oracle.expert_ffn(x, fixed, tw0, w["gate"], w["up"], w["down"])
+    assert_close(out, ref, "out")
+
+
+def test_expert_ffn_single_expert_scaling():
+    """k = 1, weight 1: doubling W_down (exact in bf16) doubles out exactly."""
+    say("expert_ffn scaling")
+    M, H, I, E = 4, 512, 256, 8
+    x, w, _, _ = _ffn_host(M, H, I, E, 1, seed=61)
+    idx = np.array([[3], [3], [5], [0]], np.int32)
+    tw = np.ones((M, 1), np.float32)
+    dw = {key: to_dev(w[key]) for key in ("gate", "up", "down")}
+    a = mv.moe_expert_ffn(to_dev(x), torch.from_numpy(idx).cuda(), torch.from_numpy(tw).cuda(),
+                          dw["gate"], dw["up"], dw["down"]).cpu().numpy()
+    d2 = to_dev(synth.bf16_bits(synth.bf16_to_f32(w["down"]) * 2))
+    b = mv.moe_expert_ffn(to_dev(x), torch.from_numpy(idx).cuda(), torch.from_numpy(tw).cuda(),
+                          dw["gate"], dw["up"], d2).cpu().numpy()
+    assert np.array_equal(b, 2 * a)
+    ref = oracle.expert_ffn(x, idx, tw.astype(np.float64), w["gate"], w["up"], w["down"])
+    assert_close(a, ref, "out")
+
+
+# ------------------------------------------------------------- full layer
+
+def _layer_gpu(x, w, bias, k):
+    b = None if bias is None else torch.from_numpy(bias).cuda()
+    idx, tw, out = mv.moe_layer(to_dev(x), w["router"], w["gate"], w["up"], w["down"], k, b)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), tw.cpu().numpy(), out.cpu().numpy()
+
+
+def test_layer_tiny():
+    say("layer tiny")
+    cfg = synth.WORKLOADS["tiny"]
+    x, w, _ = host_case(cfg["M"], cfg["H"], cfg["E"], cfg["I"], seed=0)
+    dw = {key: to_dev(v) for key, v in w.items()}
+    gi, gw, go = _layer_gpu(x, dw, None, cfg["k"])
+    ref = oracle.route(x, w["router"], None, cfg["k"])
+    same = compare_route(gi, gw, None, ref, cfg["k"])
+    out = oracle.expert_ffn(x, ref["idx"], ref["w"], w["gate"], w["up"], w["down"])
+    assert_close(go[same], out[same], "out")
+
+
+@pytest.mark.parametrize("M,alpha", [(1, None), (6, None), (6, 1.0), (16, 1.0), (16, 0.0)])
+def test_layer_full_size(full_layer, M, alpha):
+    say("layer full size", M, alpha)
+    k = 8
+    x = synth.activations(M, 2560, seed=400 + M)
+    bias = None if alpha is None else synth.zipf_bias(512, alpha)
+    gi, gw, go = _layer_gpu(x, full_layer, bias, k)
+    wr = to_host_bits(full_layer["router"])
+    ref = oracle.route(x, wr, bias, k)
+    same = compare_route(gi, gw, None, ref, k)
+    assert len(same) >= M - 1, "more than one near-tie in a handful of tokens"
+    out = oracle_ffn_from_device(x, ref["idx"], ref["w"], full_layer)
+    assert_close(go[same], out[same], "out")
+
+
+# ---------------------------------------------------------------- lm_head
+
+def _lm_gpu(h, wl):
+    am, ml = mv.lmhead_argmax(to_dev(h), wl if isinstance(wl, torch.Tensor) else to_dev(wl),
+                              want_max=True)
+    torch.cuda.synchronize()
+    return am.cpu().numpy(), ml.cpu().numpy()
+
+
+def _compare_lm(am, ml, h, wl_bits, ref):
+    M = h.shape[0]
+    for t in range(M):
+        if am[t] != ref["tok"][t]:
+            assert ref["gap"][t] < TIE_BAND, f"token {t}: {am[t]} != {ref['tok'][t]}"
+            zt = synth.bf16_to_f32(h[t]).astype(np.float64) @ \
+                synth.bf16_to_f32(wl_bits[am[t]]).astype(np.float64)
+            assert zt >= ref["zmax"][t] - TIE_BAND
+    assert_close(ml, ref["zmax"], "max_logit")
+
+
+@pytest.mark.parametrize("M,H,V", [(1, 256, 1000), (3, 264, 777), (16, 256, 4099),
+                                   (6, 2560, 65), (2, 8, 1)])
+def test_lmhead_matches_oracle(M, H, V):
+    say("lmhead", M, H, V)
+    h = synth.activations(M, H, seed=500 + V)
+    wl = synth.normal_bf16((V, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 9, V)
+    am, ml = _lm_gpu(h, wl)
+    _compare_lm(am, ml, h, wl, oracle.lmhead(h, wl))
+
+
+def test_lmhead_full_size():
+    say("lmhead full size 6 x 2560 x 157184")
+    M, H, V = 6, 2560, 157184
+    h = synth.activations(M, H, seed=601)
+    wl = synth.device_normal_bf16((V, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 0,
+                                  synth.KIND["lm_head"])
+    # planted winners: the last row for token 0, a row equal to h for token 1,
+    # and two equal copies for token 2 (lower id must win)
+    hd = to_dev(h)
+    wl[V - 1] = hd[0] * 4
+    wl[1234] = hd[1] * 4
+    wl[90000] = hd[2] * 4
+    wl[777] = hd[2] * 4
+    am, ml = _lm_gpu(h, wl)
+    assert am[0] == V - 1 and am[1] == 1234 and am[2] == 777
+    wl_bits = to_host_bits(wl)
+    _compare_lm(am, ml, h, wl_bits, oracle.lmhead(h, wl_bits))
+
+
+def test_lmhead_zero_hidden():
+    say("lmhead zero hidden")
+    wl = synth.normal_bf16((300, 64), 0.02, 3, 3)
+    am, ml = _lm_gpu(np.zeros((2, 64), np.uint16), wl)
+    assert am.tolist() == [0, 0] and np.all(ml == 0.0)
+
+
+# --------------------------------------------- determinism and invariance
+
+def test_determinism_and_batch_invariance(full_layer):
+    """Two runs are bitwise equal, and each token's results equal the same
+    token run alone (no float atomics; per-token order fixed)."""
+    say("determinism / batch invariance")
+    M, k = 6, 8
+    x = synth.activations(M, 2560, seed=701)
+    runs = [_layer_gpu(x, full_layer, None, k) for _ in range(2)]
+    for a, b in zip(runs[0], runs[1]):
+        assert np.array_equal(a, b)
+    gi, gw, go = runs[0]
+    for t in (0, 3, 5):
+        gi1, gw1, go1 = _layer_gpu(x[t:t + 1], full_layer, None, k)
+        assert np.array_equal(gi1[0], gi[t])
+        assert np.array_equal(gw1[0], gw[t])
+        assert np.array_equal(go1[0], go[t])
+    wl = synth.normal_bf16((5000, 2560), 0.02, 4, 4)
+    am, ml = _lm_gpu(x, wl)
+    for t in (1, 4):
+        am1, ml1 = _lm_gpu(x[t:t + 1], wl)
+        assert am1[0] == am[t] and ml1[0] == ml[t]
+
+
+def test_workspace_reuse_across_shapes():
+    """Counters left at zero: calls of different shapes reuse one workspace."""
+    say("workspace reuse")
+    for (M, H, E, k) in [(6, 2560, 512, 8), (1, 256, 16, 2), (16, 512, 64, 4), (6, 2560, 512, 8)]:
+        x, w, _ = host_case(M, H, E, None, seed=800 + M)
+        gi, gw, gl = run_route(x, w["router"], None, k)
+        compare_route(gi, gw, gl, oracle.route(x, w["router"], None, k), k)
+    for (M, V) in [(6, 20000), (1, 100), (6, 20000)]:
+        h = synth.activations(M, 256, seed=900 + M)
+        wl = synth.normal_bf16((V, 256), 0.02, 5, V)
+        am, ml = _lm_gpu(h, wl)
+        _compare_lm(am, ml, h, wl, oracle.lmhead(h, wl))
