@@ -13,6 +13,10 @@ namespace mv {
 // 16-byte vector of four 32-bit words: one 128-bit global or LDS access.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define MV_LDS __attribute__((address_space(3)))
 
 constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kMaxM = 16;          // verify tokens per call
@@ -49,14 +53,64 @@ __device__ __forceinline__ u32x4 load_stream(const u32x4 *p)
     return __builtin_nontemporal_load(p);
 }
 
-// Sum over the 64 lanes of a wavefront; every lane gets the total. The
-// butterfly order is fixed, so the result does not depend on timing.
+// One DPP move: lane i receives lane ctrl(i)'s v (same-row patterns only).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- 15-i within 16
+
+// Sum over the 64 lanes of a wavefront; every lane gets the same total.
+// DPP within each 16-lane row (every lane of a row ends with the identical
+// row sum, since each step adds a commuted pair), then the four row sums in
+// a fixed order. No LDS traffic; the order never depends on timing.
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v += __shfl_xor(v, m);
-    return v;
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppHalfMirror>(v);
+    v += dpp_f32<kDppMirror>(v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0)) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16)) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32)) +
+           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+}
+
+// D += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate. Lane l supplies
+// row (l % 16) of A and column (l % 16) of B over K elements
+// [8*(l/16), 8*(l/16)+8) of the 32-element step; it receives D rows
+// 4*(l/16) .. 4*(l/16)+3 of column l % 16.
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b),
+                                                   c, 0, 0, 0);
+}
+
+// Direct HBM -> LDS 128-bit load (global_load_lds_dwordx4), non-temporal:
+// lane i's 16 bytes land at lds_wave_base + 16*i. Completion is counted by
+// vmcnt; the caller waits with wait_vmcnt before reading the LDS.
+__device__ __forceinline__ void load_lds16(const void *g, void *lds_wave_base)
+{
+    __builtin_amdgcn_global_load_lds(g, (MV_LDS void *)lds_wave_base, 16, 0, 2);
+}
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left alone).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // fp32 -> bf16 bits, round to nearest, ties to even (NaN stays NaN).
@@ -75,15 +129,21 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
 // itself with every other pair to find its rank inside its expert's bucket
 // and whether it heads the bucket; nothing scales with the expert count.
 // Buckets are ordered by expert id, pairs inside a bucket by pair index.
+// A bucket is then cut into column blocks of at most 16 pairs (one MFMA B
+// operand); with distinct experts per token a bucket never exceeds M <= 16
+// pairs, so this only matters for repeated ids within a token.
 struct Groups {
     int D;                       // distinct valid experts
-    int nvalid;                  // pairs with a valid expert id
-    int e[kMaxNP];               // expert of pair p, -1 if out of range
-    int head[kMaxNP];            // 1 if p is the first pair of its expert
-    int below[kMaxNP];           // valid pairs with a smaller expert id
-    int sorted[kMaxNP];          // pair ids, bucket by bucket
-    int dexp[kMaxNP];            // expert id of bucket d
-    int doff[kMaxNP + 1];        // bucket d = sorted[doff[d] .. doff[d+1])
+    int DV;                      // column blocks
+    int16_t e[kMaxNP];           // expert of pair p, -1 if out of range
+    int16_t head[kMaxNP];        // 1 if p is the first pair of its expert
+    int16_t below[kMaxNP];       // valid pairs with a smaller expert id
+    int16_t sorted[kMaxNP];      // pair ids, bucket by bucket
+    int16_t dexp[kMaxNP];        // expert id of bucket d
+    int16_t doff[kMaxNP + 1];    // bucket d = sorted[doff[d] .. doff[d+1])
+    int16_t vexp[kMaxNP];        // expert of column block v
+    int16_t vbeg[kMaxNP];        // first index into sorted of block v
+    int16_t vcnt[kMaxNP];        // pairs in block v (1..16)
 };
 
 __device__ inline void build_groups(const int *__restrict__ topk_idx, int NP,
@@ -91,8 +151,8 @@ __device__ inline void build_groups(const int *__restrict__ topk_idx, int NP,
 {
     const int tid = threadIdx.x, nt = blockDim.x;
     for (int p = tid; p < NP; p += nt) {
-        int e = topk_idx[p];
-        g.e[p] = (e >= 0 && e < E) ? e : -1;
+        const int e = topk_idx[p];
+        g.e[p] = (int16_t)((e >= 0 && e < E) ? e : -1);
     }
     __syncthreads();
     // each pair against every other: rank in (expert, pair) order, whether
@@ -108,10 +168,10 @@ __device__ inline void build_groups(const int *__restrict__ topk_idx, int NP,
             rank += (eq < ep) || (eq == ep && q < p);
             head &= !(eq == ep && q < p);
         }
-        g.head[p] = (ep >= 0) ? head : 0;
-        g.below[p] = below;
+        g.head[p] = (int16_t)((ep >= 0) ? head : 0);
+        g.below[p] = (int16_t)below;
         if (ep >= 0)
-            g.sorted[rank] = p;
+            g.sorted[rank] = (int16_t)p;
     }
     __syncthreads();
     // bucket index of each head = heads with a smaller expert id
@@ -122,9 +182,10 @@ __device__ inline void build_groups(const int *__restrict__ topk_idx, int NP,
         int d = 0;
         for (int q = 0; q < NP; ++q)
             d += g.head[q] && g.e[q] < ep;
-        g.dexp[d] = ep;
+        g.dexp[d] = (int16_t)ep;
         g.doff[d] = g.below[p];
     }
+    __syncthreads();
     if (tid == 0) {
         int D = 0, nv = 0;
         for (int p = 0; p < NP; ++p) {
@@ -132,8 +193,18 @@ __device__ inline void build_groups(const int *__restrict__ topk_idx, int NP,
             nv += g.e[p] >= 0;
         }
         g.D = D;
-        g.nvalid = nv;
-        g.doff[D] = nv;
+        g.doff[D] = (int16_t)nv;
+        int DV = 0;
+        for (int d = 0; d < D; ++d) {
+            const int n = g.doff[d + 1] - g.doff[d];
+            for (int o = 0; o < n; o += 16) {
+                g.vexp[DV] = g.dexp[d];
+                g.vbeg[DV] = (int16_t)(g.doff[d] + o);
+                g.vcnt[DV] = (int16_t)(n - o < 16 ? n - o : 16);
+                ++DV;
+            }
+        }
+        g.DV = DV;
     }
     __syncthreads();
 }
@@ -146,9 +217,13 @@ __device__ inline void build_groups(const int *__restrict__ topk_idx, int NP,
 // point and shape in turn.
 constexpr size_t kWsHeader = 256;
 
+// Dynamic LDS a kernel may request: 160 KB per CU on gfx950, less a margin
+// for the kernels' small static arrays.
+constexpr int kLdsDynMax = 159 * 1024;
+
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
-inline size_t align_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+__host__ __device__ inline size_t align_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
 
 inline moe_status_t check_launch()
 {

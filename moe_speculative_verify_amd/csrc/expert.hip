@@ -6,268 +6,360 @@
 // stacked small kernels" (grouping -> up-GEMM -> activation -> down-GEMM ->
 // combine) with the two changes of section "Two fusions and a retune": the
 // SwiGLU product is computed in fp32 inside the up projection and rounded
-// once, and the combine is a single fp32 weighted sum.
+// once, and the combine is a single fp32 weighted sum per output.
 //
-// At batch 1 every selected expert serves one to sixteen tokens, so each
-// projection is a GEMV bound by the cold weight read. Two kernels:
-//   up    every workgroup rebuilds the pair grouping in LDS from topk_idx
-//         (cheaper than a launch), then streams an equal share of the
-//         D * I (gate row, up row) pairs of the D distinct experts with
-//         128-bit loads; each wavefront keeps RB row pairs in flight,
-//         reduces one fp32 dot per token and row, and writes
-//         a = bf16(silu(g) * u) per (pair, i).
-//   down  workgroup b owns rows [r0, r1) of the output for every expert:
-//         its wavefronts stream those rows of W_down for the distinct
-//         experts, dot them with the activations of each pair, and the
-//         workgroup then forms out[t, r] = sum_j w[t,j] y[(t,j), r] in slot
-//         order. No float atomics: results are bitwise reproducible and a
-//         token's result does not depend on the other tokens.
+// Work is cut into units = (column block v of <= 16 pairs sharing one
+// expert, 16-row tile of the weight matrix). Workgroup b owns a contiguous
+// run of units; its four wavefronts split the reduction axis K of every
+// unit, each streaming its K range of the tile's 16 rows straight from HBM
+// into a private LDS double buffer (non-temporal 128-bit direct-to-LDS
+// loads, 1 KB per instruction, the next block always in flight, across unit
+// boundaries too). The dot products run on the matrix cores
+// (v_mfma_f32_16x16x32_bf16: A = 16 weight rows, B = the block's <= 16
+// activation columns). The four partial tiles are summed through LDS in a
+// fixed order, so results are bitwise reproducible and every pair's result
+// depends only on its own token.
+//
+//   up       A = W_gate and W_up rows (two MFMAs share each B fragment),
+//            B = x of the pairs' tokens (staged once per workgroup in LDS);
+//            epilogue a = bf16(silu(g) * u) in fp32, one rounding.
+//   down     A = W_down rows, B = the pairs' activations a (L2-resident,
+//            fetched with the same direct-to-LDS loads);
+//            epilogue y[pair, rows] = W_down a in fp32.
+//   combine  out[t, r] = sum_j w[t,j] * y[(t,j), r], slots in order, fp32.
+// Every workgroup rebuilds the pair grouping in LDS from topk_idx, which
+// costs less than a separate launch.
 #include "common.h"
+
+#include <mutex>
 
 namespace mv {
 
-constexpr int kUpThreads = 256;
-constexpr int kDownThreads = 256;
+constexpr int kXWaves = 4;                          // wavefronts split K
+constexpr int kXKB = 128;                           // K elements per block
+constexpr int kXRowBytes = kXKB * 2;                // 256 B of a row per block
+constexpr int kXRowsPerLd = 1024 / kXRowBytes;      // 4 rows per load instruction
+constexpr int kXLoads = 16 / kXRowsPerLd;           // 4 loads per 16-row block
+constexpr int kXLdStride = 1024 + 16;               // LDS bytes per load (padded)
+constexpr int kXBuf = kXLoads * kXLdStride;         // one block of one matrix
+constexpr int kXSteps = kXKB / 32;                  // MFMA steps per block
+constexpr int kXThreads = kXWaves * kWave;
+constexpr int kXGrid = 256;                         // one workgroup per CU
+// static LDS (grouping + small arrays) stays below this margin
+constexpr int kXLdsDynMax = 160 * 1024 - 8 * 1024;
 
-// ------------------------------------------------------------------ up
-template <int NC, int RB>  // NC chunks per lane of H; RB row pairs in flight
-__global__ __launch_bounds__(kUpThreads) void expert_up_kernel(
+static_assert(sizeof(Groups) + 64 <= 8 * 1024, "static LDS margin");
+
+struct UnitRange {
+    int u0, u1;       // this workgroup's units
+    int kb0, kb1;     // this wavefront's K blocks
+};
+
+__device__ inline UnitRange unit_range(int nunits, int nkb)
+{
+    UnitRange r;
+    const int per = (nunits + gridDim.x - 1) / gridDim.x;
+    r.u0 = min(nunits, (int)blockIdx.x * per);
+    r.u1 = min(nunits, r.u0 + per);
+    const int wave = threadIdx.x / kWave;
+    const int kper = (nkb + kXWaves - 1) / kXWaves;
+    r.kb0 = min(nkb, wave * kper);
+    r.kb1 = min(nkb, r.kb0 + kper);
+    return r;
+}
+
+// Slot of this lane in a 16-row block load: row lrow of the four rows an
+// instruction covers, 16-byte chunk lcol of that row's 256-byte run.
+struct LdSlot {
+    int lrow, lcol;
+};
+__device__ __forceinline__ LdSlot ld_slot(int lane)
+{
+    return LdSlot{lane / (kWave / kXRowsPerLd), lane % (kWave / kXRowsPerLd)};
+}
+// LDS byte offset of the A fragment of lane (row j, K group g) in a block
+__device__ __forceinline__ int a_frag_off(int j, int g)
+{
+    return (j / kXRowsPerLd) * kXLdStride + (j % kXRowsPerLd) * kXRowBytes + g * 16;
+}
+
+// Issue the direct-to-LDS loads of one 16-row block of a [rows, K] matrix:
+// rows row0 .. row0+15 (clamped to nrows-1), K block kb (chunks clamped to
+// the row). Four instructions, 1 KB each.
+__device__ __forceinline__ void issue_block(const u32x4 *__restrict__ base, int row0,
+                                            int nrows, int nch, int kb, LdSlot sl,
+                                            unsigned char *buf)
+{
+    int c = kb * (kXKB / 8) + sl.lcol;
+    c = c < nch ? c : nch - 1;
+#pragma unroll
+    for (int q = 0; q < kXLoads; ++q) {
+        int row = row0 + q * kXRowsPerLd + sl.lrow;
+        row = row < nrows ? row : nrows - 1;
+        load_lds16(base + (size_t)row * nch + c, buf + q * kXLdStride);
+    }
+}
+
+// ------------------------------------------------------------------- up
+__global__ __launch_bounds__(kXThreads) void expert_up_kernel(
     const u32x4 *__restrict__ x, const int *__restrict__ topk_idx,
     const u32x4 *__restrict__ wg, const u32x4 *__restrict__ wu, int M, int H,
     int I, int E, int k, uint16_t *__restrict__ act)
 {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ Groups g;
-    build_groups(topk_idx, M * k, E, g);
-
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int nwave = blockDim.x / kWave;
-    const int nchunk = H / 8;
+    const int nch = H / 8;
+    const int nkb = (H + kXKB - 1) / kXKB;
+    const int xs = nkb * (kXKB / 8) + 1;                 // padded x row, chunks
+    const size_t xbytes = align_up((size_t)M * xs * 16, 256);
+    u32x4 *s_x = (u32x4 *)smem;
+    unsigned char *wbuf = smem + xbytes + wave * 4 * kXBuf;   // [2 bufs][gate, up]
+    float *red = (float *)(smem + xbytes + kXWaves * 4 * kXBuf); // [3][64][8]
 
-    // equal shares of the D*I row pairs, in whole groups of RB (RB divides I,
-    // so a group never straddles two experts)
-    const long ngroups = (long)g.D * (I / RB);
-    const long per_wg = (ngroups + gridDim.x - 1) / gridDim.x;
-    const long b0 = (long)blockIdx.x * per_wg;
-    const long b1 = min(ngroups, b0 + per_wg);
-    const long per_w = (b1 - b0 + nwave - 1) / nwave;
-    const long w0 = b0 + (long)wave * per_w;
-    const long w1 = min(b1, w0 + per_w);
+    for (int i = threadIdx.x; i < M * xs; i += blockDim.x) {
+        const int t = i / xs, c = i % xs;
+        s_x[i] = (c < nch) ? x[(size_t)t * nch + c] : u32x4{0, 0, 0, 0};
+    }
+    build_groups(topk_idx, M * k, E, g);                 // ends with a barrier
 
-    for (long grp = w0; grp < w1; ++grp) {
-        const long q = grp * RB;                 // first row pair
-        const int d = (int)(q / I);
-        const int i0 = (int)(q % I);
-        const int e = g.dexp[d];
-        const size_t row0 = ((size_t)e * I + i0) * nchunk;
+    const int TI = (I + 15) / 16;
+    const UnitRange ur = unit_range(g.DV * TI, nkb);
+    const LdSlot sl = ld_slot(lane);
+    const int j = lane & 15, gq = lane >> 4;
+    const int aoff = a_frag_off(j, gq);
 
-        u32x4 G[RB][NC], U[RB][NC];
-#pragma unroll
-        for (int b = 0; b < RB; ++b)
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const int ci = lane + kWave * c;
-                if (ci < nchunk) {
-                    G[b][c] = load_stream(wg + row0 + (size_t)b * nchunk + ci);
-                    U[b][c] = load_stream(wu + row0 + (size_t)b * nchunk + ci);
-                } else {
-                    G[b][c] = U[b][c] = u32x4{0, 0, 0, 0};
-                }
+    auto issue = [&](int u, int kb, int b) {
+        const int v = u / TI, tile = u % TI;
+        const size_t eoff = (size_t)g.vexp[v] * I;
+        unsigned char *bb = wbuf + b * 2 * kXBuf;
+        issue_block(wg + eoff * nch, tile * 16, I, nch, kb, sl, bb);
+        issue_block(wu + eoff * nch, tile * 16, I, nch, kb, sl, bb + kXBuf);
+    };
+
+    int b = 0;
+    const bool has_k = ur.kb0 < ur.kb1;
+    if (has_k && ur.u0 < ur.u1)
+        issue(ur.u0, ur.kb0, 0);
+    for (int u = ur.u0; u < ur.u1; ++u) {
+        const int v = u / TI, tile = u % TI;
+        const int npair = g.vcnt[v];
+        const bool col_ok = j < npair;
+        const int p = col_ok ? g.sorted[g.vbeg[v] + j] : 0;
+        const u32x4 *xrow = s_x + (p / k) * xs + gq;
+        f32x4 ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = ag;
+        for (int kb = ur.kb0; kb < ur.kb1; ++kb) {
+            // prefetch the next block of this wavefront's sequence
+            const bool last_kb = kb + 1 == ur.kb1;
+            const int nu = last_kb ? u + 1 : u;
+            const int nkbi = last_kb ? ur.kb0 : kb + 1;
+            if (nu < ur.u1) {
+                issue(nu, nkbi, b ^ 1);
+                wait_vmcnt<2 * kXLoads>();
+            } else {
+                wait_vmcnt<0>();
             }
-
-        for (int s = g.doff[d]; s < g.doff[d + 1]; ++s) {
-            const int p = g.sorted[s];
-            const int t = p / k;
-            u32x4 xv[NC];
+            const unsigned char *bg = wbuf + b * 2 * kXBuf + aoff;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const int ci = lane + kWave * c;
-                xv[c] = (ci < nchunk) ? x[(size_t)t * nchunk + ci] : u32x4{0, 0, 0, 0};
+            for (int s = 0; s < kXSteps; ++s) {
+                u32x4 xv = xrow[kb * (kXKB / 8) + 4 * s];
+                if (!col_ok)
+                    xv = u32x4{0, 0, 0, 0};
+                ag = mfma_bf16(*(const MV_LDS u32x4 *)(bg + s * 64), xv, ag);
+                au = mfma_bf16(*(const MV_LDS u32x4 *)(bg + kXBuf + s * 64), xv, au);
             }
-            float ag[RB], au[RB];
+            b ^= 1;
+        }
+        // sum the four K partials in wavefront order, then SwiGLU
+        if (wave > 0) {
+            float *rp = red + ((wave - 1) * kWave + lane) * 8;
 #pragma unroll
-            for (int b = 0; b < RB; ++b) {
-                float sg = 0.0f, su = 0.0f;
-#pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    sg = dot8_bf16(G[b][c], xv[c], sg);
-                    su = dot8_bf16(U[b][c], xv[c], su);
-                }
-                ag[b] = wave_sum(sg);
-                au[b] = wave_sum(su);
-            }
-            if (lane < RB) {
-                // SwiGLU in fp32, one rounding of the product to bf16
-                float gv = ag[0], uv = au[0];
-#pragma unroll
-                for (int b = 1; b < RB; ++b)
-                    if (lane == b) {
-                        gv = ag[b];
-                        uv = au[b];
-                    }
-                const float a = gv / (1.0f + expf(-gv)) * uv;
-                act[(size_t)p * I + i0 + lane] = (uint16_t)f32_to_bf16_rne(a);
+            for (int r = 0; r < 4; ++r) {
+                rp[r] = ag[r];
+                rp[4 + r] = au[r];
             }
         }
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int w = 1; w < kXWaves; ++w) {
+                const float *rp = red + ((w - 1) * kWave + lane) * 8;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    ag[r] += rp[r];
+                    au[r] += rp[4 + r];
+                }
+            }
+            if (col_ok) {
+                // rows 4gq .. 4gq+3 of the tile for pair p
+                const int row0 = tile * 16 + 4 * gq;
+                uint32_t h[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float gv = ag[r];
+                    const float a = gv / (1.0f + expf(-gv)) * au[r];
+                    h[r] = f32_to_bf16_rne(a);
+                }
+                uint16_t *dst = act + (size_t)p * I + row0;
+                if (row0 + 3 < I && (I % 4) == 0) {
+                    *(uint2 *)dst = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                } else {
+                    for (int r = 0; r < 4; ++r)
+                        if (row0 + r < I)
+                            dst[r] = (uint16_t)h[r];
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 
-// ---------------------------------------------------------------- down
-template <int NC, int RB>  // NC chunks per lane of I; RB rows in flight
-__global__ __launch_bounds__(kDownThreads) void expert_down_kernel(
-    const u32x4 *__restrict__ act, const int *__restrict__ topk_idx,
-    const float *__restrict__ topk_w, const u32x4 *__restrict__ wd, int M,
-    int H, int I, int E, int k, int rows_per_wg, float *__restrict__ out)
-{
-    __shared__ Groups g;
-    extern __shared__ float s_y[];               // [NP][rows_per_wg]
-    build_groups(topk_idx, M * k, E, g);
+// ----------------------------------------------------------------- down
+constexpr int kXBBuf = kXSteps * 1024;              // B fragments of one block
 
+__global__ __launch_bounds__(kXThreads) void expert_down_kernel(
+    const u32x4 *__restrict__ act, const int *__restrict__ topk_idx,
+    const u32x4 *__restrict__ wd, int M, int H, int I, int E, int k,
+    float *__restrict__ y)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ Groups g;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int nwave = blockDim.x / kWave;
-    const int nchunk = I / 8;
-    const int r0 = blockIdx.x * rows_per_wg;
-    const int r1 = min(H, r0 + rows_per_wg);
-    const int nr = r1 - r0;
-    if (nr <= 0)
-        return;
+    const int nch = I / 8;                               // K = I here
+    const int nkb = (I + kXKB - 1) / kXKB;
+    unsigned char *wbuf = smem + wave * 2 * kXBuf;                    // A blocks
+    unsigned char *bbuf = smem + kXWaves * 2 * kXBuf + wave * 2 * kXBBuf;  // B blocks
+    float *red = (float *)(smem + kXWaves * 2 * (kXBuf + kXBBuf));    // [3][64][4]
 
-    for (int d = wave; d < g.D; d += nwave) {
-        const int e = g.dexp[d];
-        for (int r = r0; r < r1; r += RB) {
-            u32x4 W[RB][NC];
+    build_groups(topk_idx, M * k, E, g);
+
+    const int TH = (H + 15) / 16;
+    const UnitRange ur = unit_range(g.DV * TH, nkb);
+    const LdSlot sl = ld_slot(lane);
+    const int j = lane & 15, gq = lane >> 4;
+    const int aoff = a_frag_off(j, gq);
+
+    // A: 16 rows of W_down[e]; B: lane (j, gq) fetches the activation chunks
+    // of pair j for its K group, one 1 KB load per MFMA step, landing in lane
+    // order so that each lane later reads back exactly its own fragment
+    auto issue = [&](int u, int kb, int b) {
+        const int v = u / TH, tile = u % TH;
+        issue_block(wd + (size_t)g.vexp[v] * H * nch, tile * 16, H, nch, kb, sl,
+                    wbuf + b * kXBuf);
+        const int p = j < g.vcnt[v] ? g.sorted[g.vbeg[v] + j] : 0;
 #pragma unroll
-            for (int b = 0; b < RB; ++b)
+        for (int s = 0; s < kXSteps; ++s) {
+            int c = kb * (kXKB / 8) + 4 * s + gq;
+            c = c < nch ? c : nch - 1;
+            load_lds16(act + (size_t)p * nch + c, bbuf + b * kXBBuf + s * 1024);
+        }
+    };
+
+    int b = 0;
+    const bool has_k = ur.kb0 < ur.kb1;
+    if (has_k && ur.u0 < ur.u1)
+        issue(ur.u0, ur.kb0, 0);
+    for (int u = ur.u0; u < ur.u1; ++u) {
+        const int v = u / TH, tile = u % TH;
+        const bool col_ok = j < g.vcnt[v];
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int kb = ur.kb0; kb < ur.kb1; ++kb) {
+            const bool last_kb = kb + 1 == ur.kb1;
+            const int nu = last_kb ? u + 1 : u;
+            const int nkbi = last_kb ? ur.kb0 : kb + 1;
+            if (nu < ur.u1) {
+                issue(nu, nkbi, b ^ 1);
+                wait_vmcnt<kXLoads + kXSteps>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            const unsigned char *ba = wbuf + b * kXBuf + aoff;
+            const unsigned char *bb = bbuf + b * kXBBuf + lane * 16;
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    const int ci = lane + kWave * c;
-                    W[b][c] = (r + b < r1 && ci < nchunk)
-                                  ? load_stream(wd + ((size_t)e * H + r + b) * nchunk + ci)
-                                  : u32x4{0, 0, 0, 0};
-                }
-            for (int s = g.doff[d]; s < g.doff[d + 1]; ++s) {
-                const int p = g.sorted[s];
-                u32x4 av[NC];
+            for (int s = 0; s < kXSteps; ++s) {
+                u32x4 bv = *(const MV_LDS u32x4 *)(bb + s * 1024);
+                if (!col_ok || kb * (kXKB / 8) + 4 * s + gq >= nch)
+                    bv = u32x4{0, 0, 0, 0};
+                acc = mfma_bf16(*(const MV_LDS u32x4 *)(ba + s * 64), bv, acc);
+            }
+            b ^= 1;
+        }
+        if (wave > 0) {
+            float *rp = red + ((wave - 1) * kWave + lane) * 4;
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    const int ci = lane + kWave * c;
-                    av[c] = (ci < nchunk) ? act[(size_t)p * nchunk + ci] : u32x4{0, 0, 0, 0};
-                }
+            for (int r = 0; r < 4; ++r)
+                rp[r] = acc[r];
+        }
+        __syncthreads();
+        if (wave == 0) {
 #pragma unroll
-                for (int b = 0; b < RB; ++b) {
-                    float acc = 0.0f;
+            for (int w = 1; w < kXWaves; ++w) {
+                const float *rp = red + ((w - 1) * kWave + lane) * 4;
 #pragma unroll
-                    for (int c = 0; c < NC; ++c)
-                        acc = dot8_bf16(W[b][c], av[c], acc);
-                    acc = wave_sum(acc);
-                    if (lane == 0 && r + b < r1)
-                        s_y[p * rows_per_wg + (r + b - r0)] = acc;
+                for (int r = 0; r < 4; ++r)
+                    acc[r] += rp[r];
+            }
+            if (col_ok) {
+                const int p = g.sorted[g.vbeg[v] + j];
+                const int row0 = tile * 16 + 4 * gq;
+                float *dst = y + (size_t)p * H + row0;
+                if (row0 + 3 < H && (H % 4) == 0) {
+                    *(float4 *)dst = make_float4(acc[0], acc[1], acc[2], acc[3]);
+                } else {
+                    for (int r = 0; r < 4; ++r)
+                        if (row0 + r < H)
+                            dst[r] = acc[r];
                 }
             }
         }
+        __syncthreads();
     }
-    __syncthreads();
+}
 
-    // weighted combine, slots in order, fp32
-    for (int i = threadIdx.x; i < M * nr; i += blockDim.x) {
-        const int t = i / nr, rr = i % nr;
-        float sum = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            const int p = t * k + j;
-            if (g.e[p] >= 0)
-                sum = fmaf(topk_w[p], s_y[p * rows_per_wg + rr], sum);
-        }
-        out[(size_t)t * H + r0 + rr] = sum;
+// -------------------------------------------------------------- combine
+__global__ __launch_bounds__(256) void expert_combine_kernel(
+    const float *__restrict__ y, const int *__restrict__ topk_idx,
+    const float *__restrict__ topk_w, int M, int H, int E, int k,
+    float *__restrict__ out)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= M * H)
+        return;
+    const int t = i / H, r = i % H;
+    float s = 0.0f;
+    for (int jj = 0; jj < k; ++jj) {
+        const int p = t * k + jj;
+        const int e = topk_idx[p];
+        if (e >= 0 && e < E)
+            s = fmaf(topk_w[p], y[(size_t)p * H + r], s);
     }
+    out[i] = s;
 }
 
 // ------------------------------------------------------------------ host
 
-static int chunks_per_lane(int n) { return (n / 8 + kWave - 1) / kWave; }
-
-// Grid sizes: the up share is split evenly on the device once D is known;
-// the down rows are split over a fixed number of workgroups.
-constexpr int kUpGrid = 512;
-constexpr int kDownGrid = 256;
-
-template <int NC>
-static void launch_up_nc(const uint16_t *x, const int *idx, const uint16_t *wg,
-                         const uint16_t *wu, int M, int H, int I, int E, int k,
-                         uint16_t *act, hipStream_t st)
+static size_t up_lds_bytes(int M, int H)
 {
-    if (NC <= 8 && I % 2 == 0)
-        hipLaunchKernelGGL((expert_up_kernel<NC, (NC <= 8 ? 2 : 1)>), dim3(kUpGrid),
-                           dim3(kUpThreads), 0, st, (const u32x4 *)x, idx,
-                           (const u32x4 *)wg, (const u32x4 *)wu, M, H, I, E, k, act);
-    else
-        hipLaunchKernelGGL((expert_up_kernel<NC, 1>), dim3(kUpGrid), dim3(kUpThreads),
-                           0, st, (const u32x4 *)x, idx, (const u32x4 *)wg,
-                           (const u32x4 *)wu, M, H, I, E, k, act);
+    const int nkb = (H + kXKB - 1) / kXKB;
+    return align_up((size_t)M * (nkb * (kXKB / 8) + 1) * 16, 256) +
+           (size_t)kXWaves * 4 * kXBuf + (size_t)(kXWaves - 1) * kWave * 8 * 4;
+}
+static size_t down_lds_bytes()
+{
+    return (size_t)kXWaves * 2 * (kXBuf + kXBBuf) + (size_t)(kXWaves - 1) * kWave * 4 * 4;
 }
 
-static void launch_up(const uint16_t *x, const int *idx, const uint16_t *wg,
-                      const uint16_t *wu, int M, int H, int I, int E, int k,
-                      uint16_t *act, hipStream_t st)
+// Workspace: the header, the [M*k, I] bf16 activations, the [M*k, H] fp32
+// per-pair down projections.
+static size_t ffn_act_bytes(int32_t M, int32_t I, int32_t k)
 {
-    const int need = chunks_per_lane(H);
-    if (need <= 1)
-        launch_up_nc<1>(x, idx, wg, wu, M, H, I, E, k, act, st);
-    else if (need <= 2)
-        launch_up_nc<2>(x, idx, wg, wu, M, H, I, E, k, act, st);
-    else if (need <= 4)
-        launch_up_nc<4>(x, idx, wg, wu, M, H, I, E, k, act, st);
-    else if (need <= 5)
-        launch_up_nc<5>(x, idx, wg, wu, M, H, I, E, k, act, st);
-    else if (need <= 8)
-        launch_up_nc<8>(x, idx, wg, wu, M, H, I, E, k, act, st);
-    else
-        launch_up_nc<16>(x, idx, wg, wu, M, H, I, E, k, act, st);
+    return align_up((size_t)M * k * I * sizeof(uint16_t), 256);
 }
-
-template <int NC>
-static void launch_down_nc(const uint16_t *act, const int *idx, const float *tw,
-                           const uint16_t *wd, int M, int H, int I, int E, int k,
-                           float *out, hipStream_t st)
+static size_t ffn_ws_bytes(int32_t M, int32_t H, int32_t I, int32_t k)
 {
-    const int rows = (H + kDownGrid - 1) / kDownGrid;
-    const int grid = (H + rows - 1) / rows;
-    const size_t lds = (size_t)M * k * rows * sizeof(float);
-    if (rows % 5 == 0)
-        hipLaunchKernelGGL((expert_down_kernel<NC, 5>), dim3(grid), dim3(kDownThreads),
-                           lds, st, (const u32x4 *)act, idx, tw, (const u32x4 *)wd,
-                           M, H, I, E, k, rows, out);
-    else if (rows % 4 == 0)
-        hipLaunchKernelGGL((expert_down_kernel<NC, 4>), dim3(grid), dim3(kDownThreads),
-                           lds, st, (const u32x4 *)act, idx, tw, (const u32x4 *)wd,
-                           M, H, I, E, k, rows, out);
-    else
-        hipLaunchKernelGGL((expert_down_kernel<NC, 2>), dim3(grid), dim3(kDownThreads),
-                           lds, st, (const u32x4 *)act, idx, tw, (const u32x4 *)wd,
-                           M, H, I, E, k, rows, out);
-}
-
-static void launch_down(const uint16_t *act, const int *idx, const float *tw,
-                        const uint16_t *wd, int M, int H, int I, int E, int k,
-                        float *out, hipStream_t st)
-{
-    const int need = chunks_per_lane(I);
-    if (need <= 1)
-        launch_down_nc<1>(act, idx, tw, wd, M, H, I, E, k, out, st);
-    else if (need <= 2)
-        launch_down_nc<2>(act, idx, tw, wd, M, H, I, E, k, out, st);
-    else if (need <= 4)
-        launch_down_nc<4>(act, idx, tw, wd, M, H, I, E, k, out, st);
-    else if (need <= 8)
-        launch_down_nc<8>(act, idx, tw, wd, M, H, I, E, k, out, st);
-    else
-        launch_down_nc<16>(act, idx, tw, wd, M, H, I, E, k, out, st);
-}
-
-// Workspace: the header, then the [M*k, I] bf16 SwiGLU activations.
-static size_t ffn_ws_bytes(int32_t M, int32_t I, int32_t k)
-{
-    return kWsHeader + align_up((size_t)M * k * I * sizeof(uint16_t), 256);
+    return kWsHeader + ffn_act_bytes(M, I, k) + align_up((size_t)M * k * H * sizeof(float), 256);
 }
 
 static moe_status_t ffn_check(const uint16_t *x, const int32_t *topk_idx,
@@ -283,7 +375,7 @@ static moe_status_t ffn_check(const uint16_t *x, const int32_t *topk_idx,
         return s;
     if (I < 1)
         return MOE_ERR_SHAPE;
-    if (I % 8 != 0 || I > kMaxDim)
+    if (I % 8 != 0 || I > kMaxDim || up_lds_bytes(M, H) > (size_t)kXLdsDynMax)
         return MOE_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) ||
         !aligned16(w_down) || !aligned4(topk_idx) || !aligned4(topk_w) ||
@@ -298,12 +390,31 @@ static moe_status_t ffn_enqueue(const uint16_t *x, const int32_t *topk_idx,
                                 int32_t M, int32_t H, int32_t I, int32_t E,
                                 int32_t k, float *out, void *ws, hipStream_t st)
 {
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+        attr = hipFuncSetAttribute((const void *)expert_up_kernel,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, kXLdsDynMax);
+    });
+    if (attr != hipSuccess)
+        return MOE_ERR_LAUNCH;
     uint16_t *act = (uint16_t *)((char *)ws + kWsHeader);
-    launch_up(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st);
+    float *y = (float *)((char *)ws + kWsHeader + ffn_act_bytes(M, I, k));
+    hipLaunchKernelGGL(expert_up_kernel, dim3(kXGrid), dim3(kXThreads),
+                       up_lds_bytes(M, H), st, (const u32x4 *)x, topk_idx,
+                       (const u32x4 *)w_gate, (const u32x4 *)w_up, M, H, I, E, k, act);
     moe_status_t s = check_launch();
     if (s != MOE_OK)
         return s;
-    launch_down(act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st);
+    hipLaunchKernelGGL(expert_down_kernel, dim3(kXGrid), dim3(kXThreads), down_lds_bytes(),
+                       st, (const u32x4 *)act, topk_idx, (const u32x4 *)w_down, M, H, I,
+                       E, k, y);
+    s = check_launch();
+    if (s != MOE_OK)
+        return s;
+    const int n = M * H;
+    hipLaunchKernelGGL(expert_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, st, y,
+                       topk_idx, topk_w, M, H, E, k, out);
     return check_launch();
 }
 
@@ -326,7 +437,7 @@ extern "C" size_t moe_expert_ffn_workspace_bytes(int32_t M, int32_t H, int32_t I
 {
     if (check_moe_shape(M, H, E, k) != MOE_OK || I < 8 || I % 8 || I > kMaxDim)
         return 0;
-    return ffn_ws_bytes(M, I, k);
+    return ffn_ws_bytes(M, H, I, k);
 }
 
 extern "C" moe_status_t moe_expert_ffn(const uint16_t *x, const int32_t *topk_idx,

@@ -6,198 +6,216 @@
 // the greedy verdict inside the verify step (section "The shape of a
 // single-request step", Fig. 3).
 //
-// Workgroup b owns a contiguous slice of vocabulary rows; each wavefront
-// streams RB rows at a time with 128-bit loads, reduces one fp32 dot per
-// token and row, and keeps a running (max, first index) per token. The
-// workgroup's best per token goes to a slot of the workspace; the last
-// workgroup to finish (atomic ticket, no spinning) reduces the slots in
-// ascending workgroup order. Logits never reach memory, and the result is
-// the same whatever the finishing order.
+// Design (gfx950):
+//   - The vocabulary is cut into 16-row tiles; workgroup b owns a contiguous
+//     run of tiles and its four wavefronts take every fourth tile.
+//   - A wavefront streams its tile K-block by K-block (KB elements of each of
+//     the 16 rows) straight from HBM into its own LDS double buffer with
+//     non-temporal 128-bit direct-to-LDS loads: every load instruction reads
+//     1 KB made of two 512-byte row runs, the access pattern that reaches the
+//     HBM roofline, and the next block is in flight while the current one is
+//     consumed.
+//   - The dot products run on the matrix cores: v_mfma_f32_16x16x32_bf16
+//     with A = 16 weight rows (from LDS) and B = the M <= 16 hidden states
+//     (staged once per workgroup in LDS, zero columns beyond M). One MFMA
+//     covers 1 KB of weights; no cross-lane reductions are needed.
+//   - Each lane keeps a running (max, first index) for its token; the
+//     workgroup's best per token is folded into a 64-bit key
+//     (order-preserving value bits << 32 | ~index) with a device-scope
+//     atomic max, so the largest value and then the lowest index win
+//     whatever the order. The last workgroup to take a ticket (device-scope
+//     atomic, no spinning, no cache flush) decodes the keys and resets them.
 #include "common.h"
+
+#include <mutex>
 
 namespace mv {
 
-constexpr int kLmThreads = 256;
-constexpr int kLmMaxGrid = 2048;
+constexpr int kLmWaves = 4;
+constexpr int kLmKB = 256;                        // K elements per block
+constexpr int kLmRowBytes = kLmKB * 2;            // 512 B of a row per block
+constexpr int kLmRowsPerLd = 1024 / kLmRowBytes;  // rows per load instruction
+constexpr int kLmLoads = 16 / kLmRowsPerLd;       // load instructions per block
+constexpr int kLmLdStride = 1024 + 16;            // LDS bytes per load (padded)
+constexpr int kLmBuf = kLmLoads * kLmLdStride;    // one block of a tile
+constexpr int kLmSteps = kLmKB / 32;              // MFMA steps per block
 
-template <int NC, int RB, int MT>  // MT >= M: tokens held in registers
-__global__ __launch_bounds__(kLmThreads) void lmhead_kernel(
+__host__ __device__ static size_t lm_x_bytes(int M, int H)
+{
+    const int nkb = (H + kLmKB - 1) / kLmKB;
+    return align_up((size_t)M * (nkb * (kLmKB / 8) + 1) * 16, 256);
+}
+static size_t lm_lds_bytes(int M, int H)
+{
+    return lm_x_bytes(M, H) + (size_t)kLmWaves * 2 * kLmBuf;
+}
+
+// order-preserving map of fp32 to uint32 (-0 and +0 both map to +0's code)
+__device__ __forceinline__ uint32_t f32_order(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u)
+        u = 0;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f32_unorder(uint32_t u)
+{
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+__global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     const u32x4 *__restrict__ h, const u32x4 *__restrict__ wl, int M, int H,
-    int V, int rows_per_wg, float *__restrict__ part_v, int *__restrict__ part_i,
+    int V, int tiles_per_wg, unsigned long long *__restrict__ keys,
     unsigned *__restrict__ ticket, int *__restrict__ argmax,
     float *__restrict__ max_logit)
 {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int nwave = blockDim.x / kWave;
-    const int nchunk = H / 8;
+    const int nch = H / 8;                               // 16-byte chunks per row
+    const int nkb = (H + kLmKB - 1) / kLmKB;
+    const int xs = nkb * (kLmKB / 8) + 1;                // padded x row, chunks
+    u32x4 *s_x = (u32x4 *)smem;
+    unsigned char *wbuf = smem + lm_x_bytes(M, H) + wave * 2 * kLmBuf;
 
-    const int v0 = blockIdx.x * rows_per_wg;
-    const int v1 = min(V, v0 + rows_per_wg);
-    const int per_w = ((v1 - v0 + nwave - 1) / nwave + RB - 1) / RB * RB;
-    const int a0 = v0 + wave * per_w;
-    const int a1 = min(v1, a0 + per_w);
-
-    float bv[MT];
-    int bi[MT];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-        bv[t] = -INFINITY;
-        bi[t] = 0x7FFFFFFF;
+    // hidden states into LDS, zero beyond H
+    for (int i = threadIdx.x; i < M * xs; i += blockDim.x) {
+        const int t = i / xs, c = i % xs;
+        s_x[i] = (c < nch) ? h[(size_t)t * nch + c] : u32x4{0, 0, 0, 0};
     }
+    __syncthreads();
 
-    for (int v = a0; v < a1; v += RB) {
-        u32x4 W[RB][NC];
+    const int j = lane & 15;        // A row in the tile / B column = token
+    const int g = lane >> 4;        // K group of 8 elements in an MFMA step
+    const bool tok_ok = j < M;
+    const u32x4 *xrow = s_x + (tok_ok ? j : 0) * xs + g;
+    // this lane's slot in a load instruction: row lrow of the group of
+    // rows the instruction covers, chunk lcol of that row's block
+    const int lrow = lane / (kWave / kLmRowsPerLd);
+    const int lcol = lane % (kWave / kLmRowsPerLd);
+    const int a_off = (j / kLmRowsPerLd) * kLmLdStride + (j % kLmRowsPerLd) * kLmRowBytes + g * 16;
+
+    const int ntiles = (V + 15) / 16;
+    const int t0 = blockIdx.x * tiles_per_wg;
+    const int t1 = min(ntiles, t0 + tiles_per_wg);
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+
+    for (int tile = t0 + wave; tile < t1; tile += kLmWaves) {
+        const u32x4 *rp[kLmLoads];
 #pragma unroll
-        for (int b = 0; b < RB; ++b)
+        for (int q = 0; q < kLmLoads; ++q) {
+            int row = tile * 16 + q * kLmRowsPerLd + lrow;
+            row = row < V ? row : V - 1;                 // tail rows: valid memory, ignored
+            rp[q] = wl + (size_t)row * nch;
+        }
+        auto issue = [&](int kb, int b) {
+            int c = kb * (kLmKB / 8) + lcol;
+            c = c < nch ? c : nch - 1;                   // K tail: valid memory, x is zero there
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const int ci = lane + kWave * c;
-                W[b][c] = (v + b < a1 && ci < nchunk)
-                              ? load_stream(wl + (size_t)(v + b) * nchunk + ci)
-                              : u32x4{0, 0, 0, 0};
+            for (int q = 0; q < kLmLoads; ++q)
+                load_lds16(rp[q] + c, wbuf + b * kLmBuf + q * kLmLdStride);
+        };
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        issue(0, 0);
+        for (int kb = 0; kb < nkb; ++kb) {
+            const int b = kb & 1;
+            if (kb + 1 < nkb) {
+                issue(kb + 1, b ^ 1);
+                wait_vmcnt<kLmLoads>();                  // block kb has landed
+            } else {
+                wait_vmcnt<0>();
             }
+            const unsigned char *ab = wbuf + b * kLmBuf + a_off;
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            if (t < M) {
-                u32x4 xv[NC];
+            for (int s = 0; s < kLmSteps; ++s) {
+                const u32x4 a = *(const MV_LDS u32x4 *)(ab + s * 64);
+                u32x4 x = xrow[kb * (kLmKB / 8) + 4 * s];
+                if (!tok_ok)
+                    x = u32x4{0, 0, 0, 0};
+                acc = mfma_bf16(a, x, acc);
+            }
+        }
+        // rows 4g..4g+3 of the tile for token j; ascending rows, so a strict
+        // comparison keeps the first of equal values
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    const int ci = lane + kWave * c;
-                    xv[c] = (ci < nchunk) ? h[(size_t)t * nchunk + ci] : u32x4{0, 0, 0, 0};
-                }
-#pragma unroll
-                for (int b = 0; b < RB; ++b) {
-                    float acc = 0.0f;
-#pragma unroll
-                    for (int c = 0; c < NC; ++c)
-                        acc = dot8_bf16(W[b][c], xv[c], acc);
-                    acc = wave_sum(acc);
-                    // rows ascend, so a strict comparison keeps the first
-                    if (v + b < a1 && acc > bv[t]) {
-                        bv[t] = acc;
-                        bi[t] = v + b;
-                    }
-                }
+        for (int r = 0; r < 4; ++r) {
+            const int row = tile * 16 + 4 * g + r;
+            if (row < V && acc[r] > bv) {
+                bv = acc[r];
+                bi = row;
             }
         }
     }
 
-    // workgroup best per token: wavefronts in ascending row order
-    __shared__ float s_v[kLmThreads / kWave][MT];
-    __shared__ int s_i[kLmThreads / kWave][MT];
-    if (lane == 0)
+    // the four lanes of token j (one per K group) hold interleaved rows
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            s_v[wave][t] = bv[t];
-            s_i[wave][t] = bi[t];
+    for (int m = 16; m <= 32; m <<= 1) {
+        const float ov = __shfl_xor(bv, m);
+        const int oi = __shfl_xor(bi, m);
+        if (ov > bv || (ov == bv && oi < bi)) {
+            bv = ov;
+            bi = oi;
         }
+    }
+    __shared__ float s_v[kLmWaves][16];
+    __shared__ int s_i[kLmWaves][16];
+    __shared__ int s_last;
+    if (g == 0) {
+        s_v[wave][j] = bv;
+        s_i[wave][j] = bi;
+    }
     __syncthreads();
     if (threadIdx.x < M) {
         const int t = threadIdx.x;
         float best = s_v[0][t];
         int besti = s_i[0][t];
-        for (int w = 1; w < nwave; ++w)
+        for (int w = 1; w < kLmWaves; ++w)
             if (s_v[w][t] > best || (s_v[w][t] == best && s_i[w][t] < besti)) {
                 best = s_v[w][t];
                 besti = s_i[w][t];
             }
-        part_v[(size_t)blockIdx.x * M + t] = best;
-        part_i[(size_t)blockIdx.x * M + t] = besti;
+        const unsigned long long key =
+            ((unsigned long long)f32_order(best) << 32) | (uint32_t)(~(uint32_t)besti);
+        // returning form: the max has been performed when the value is back
+        const unsigned long long old = __hip_atomic_fetch_max(
+            keys + t, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == ~0ull)                                // never true: keeps old live
+            s_i[0][t] = 0;
     }
-
-    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        const unsigned prev = atomicAdd(ticket, 1u);
-        s_last = (prev == gridDim.x - 1);
-    }
+    if (threadIdx.x == 0)
+        s_last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
     __syncthreads();
     if (!s_last)
         return;
-    __threadfence();
-    if (threadIdx.x == 0)
-        *ticket = 0u;
-
-    // one wavefront per token over all workgroup slots
-    for (int t = wave; t < M; t += nwave) {
-        float best = -INFINITY;
-        int besti = 0x7FFFFFFF;
-        for (int b = lane; b < (int)gridDim.x; b += kWave) {
-            const float pv = part_v[(size_t)b * M + t];
-            const int pi = part_i[(size_t)b * M + t];
-            if (pv > best || (pv == best && pi < besti)) {
-                best = pv;
-                besti = pi;
-            }
-        }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            const float ov = __shfl_xor(best, m);
-            const int oi = __shfl_xor(besti, m);
-            if (ov > best || (ov == best && oi < besti)) {
-                best = ov;
-                besti = oi;
-            }
-        }
-        if (lane == 0) {
-            argmax[t] = besti;
-            if (max_logit)
-                max_logit[t] = best;
-        }
+    if (threadIdx.x < M) {
+        const int t = threadIdx.x;
+        const unsigned long long key = __hip_atomic_exchange(
+            keys + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        argmax[t] = (int)(~(uint32_t)key);
+        if (max_logit)
+            max_logit[t] = f32_unorder((uint32_t)(key >> 32));
     }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-static int lm_grid(int V) { return V < kLmMaxGrid ? V : kLmMaxGrid; }
-
-template <int NC, int MT>
-static void launch_lm(const uint16_t *h, const uint16_t *w, int M, int H, int V,
-                      float *pv, int *pi, unsigned *ticket, int *am, float *ml,
-                      hipStream_t st)
-{
-    // 512 workgroups cover the 256 CUs twice; small vocabularies get fewer
-    int grid = (V + 63) / 64;
-    if (grid > 512)
-        grid = 512;
-    const int rows = (V + grid - 1) / grid;
-    grid = (V + rows - 1) / rows;
-    // rows in flight per wavefront: fewer for wide rows to stay in registers
-    constexpr int RB = NC <= 5 ? 4 : (NC <= 8 ? 2 : 1);
-    hipLaunchKernelGGL((lmhead_kernel<NC, RB, MT>), dim3(grid), dim3(kLmThreads), 0,
-                       st, (const u32x4 *)h, (const u32x4 *)w, M, H, V, rows, pv,
-                       pi, ticket, am, ml);
-}
-
-template <int NC>
-static void launch_lm_m(const uint16_t *h, const uint16_t *w, int M, int H, int V,
-                        float *pv, int *pi, unsigned *ticket, int *am, float *ml,
-                        hipStream_t st)
-{
-    if (M <= 1)
-        launch_lm<NC, 1>(h, w, M, H, V, pv, pi, ticket, am, ml, st);
-    else if (M <= 2)
-        launch_lm<NC, 2>(h, w, M, H, V, pv, pi, ticket, am, ml, st);
-    else if (M <= 4)
-        launch_lm<NC, 4>(h, w, M, H, V, pv, pi, ticket, am, ml, st);
-    else if (M <= 8)
-        launch_lm<NC, 8>(h, w, M, H, V, pv, pi, ticket, am, ml, st);
-    else
-        launch_lm<NC, 16>(h, w, M, H, V, pv, pi, ticket, am, ml, st);
-}
+// one workgroup per CU: the LDS footprint allows no more
+constexpr int kLmGridTarget = 256;
 
 } // namespace mv
 
 using namespace mv;
 
-// Workspace: the header (ticket), [grid][M] fp32 best values, [grid][M]
-// int32 best rows.
+// Workspace: the header (ticket), then M 64-bit keys.
 extern "C" size_t lmhead_argmax_workspace_bytes(int32_t M, int32_t V)
 {
     if (M < 1 || M > kMaxM || V < 1)
         return 0;
-    const size_t slots = (size_t)lm_grid(V) * (size_t)M;
-    return kWsHeader + 2 * align_up(slots * 4, 256);
+    return kWsHeader + align_up((size_t)M * 8, 256);
 }
 
 extern "C" moe_status_t lmhead_argmax(const uint16_t *h, const uint16_t *w_lm,
@@ -210,30 +228,29 @@ extern "C" moe_status_t lmhead_argmax(const uint16_t *h, const uint16_t *w_lm,
         return MOE_ERR_NULL;
     if (M < 1 || H < 1 || V < 1)
         return MOE_ERR_SHAPE;
-    if (M > kMaxM || H % 8 != 0 || H > kMaxDim)
+    if (M > kMaxM || H % 8 != 0 || H > kMaxDim || lm_lds_bytes(M, H) > (size_t)kLdsDynMax)
         return MOE_ERR_UNSUPPORTED;
     if (!aligned16(h) || !aligned16(w_lm) || !aligned4(argmax) ||
         (max_logit && !aligned4(max_logit)) || !aligned16(workspace))
         return MOE_ERR_ALIGN;
     if (workspace_bytes < lmhead_argmax_workspace_bytes(M, V))
         return MOE_ERR_WORKSPACE;
-    const size_t slots = (size_t)lm_grid(V) * (size_t)M;
     unsigned *ticket = (unsigned *)workspace;
-    float *pv = (float *)((char *)workspace + kWsHeader);
-    int *pi = (int *)((char *)workspace + kWsHeader + align_up(slots * 4, 256));
-    hipStream_t st = (hipStream_t)stream;
-    const int need = (H / 8 + kWave - 1) / kWave;
-    if (need <= 1)
-        launch_lm_m<1>(h, w_lm, M, H, V, pv, pi, ticket, argmax, max_logit, st);
-    else if (need <= 2)
-        launch_lm_m<2>(h, w_lm, M, H, V, pv, pi, ticket, argmax, max_logit, st);
-    else if (need <= 4)
-        launch_lm_m<4>(h, w_lm, M, H, V, pv, pi, ticket, argmax, max_logit, st);
-    else if (need <= 5)
-        launch_lm_m<5>(h, w_lm, M, H, V, pv, pi, ticket, argmax, max_logit, st);
-    else if (need <= 8)
-        launch_lm_m<8>(h, w_lm, M, H, V, pv, pi, ticket, argmax, max_logit, st);
-    else
-        launch_lm_m<16>(h, w_lm, M, H, V, pv, pi, ticket, argmax, max_logit, st);
+    unsigned long long *keys = (unsigned long long *)((char *)workspace + kWsHeader);
+    const int ntiles = (V + 15) / 16;
+    const int tpw = (ntiles + kLmGridTarget - 1) / kLmGridTarget;
+    const int grid = (ntiles + tpw - 1) / tpw;
+    const size_t lds = lm_lds_bytes(M, H);
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+        attr = hipFuncSetAttribute((const void *)lmhead_kernel,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, kLdsDynMax);
+    });
+    if (attr != hipSuccess)
+        return MOE_ERR_LAUNCH;
+    hipLaunchKernelGGL(lmhead_kernel, dim3(grid), dim3(kLmWaves * kWave), lds,
+                       (hipStream_t)stream, (const u32x4 *)h, (const u32x4 *)w_lm,
+                       M, H, V, tpw, keys, ticket, argmax, max_logit);
     return check_launch();
 }

@@ -5,20 +5,36 @@
 // stacked small kernels", Fig. 7: gate matvec, then top-k. The gate weight
 // is bf16 (section "bf16 router gate and lm_head").
 //
-// One launch does both steps. Every wavefront owns router rows: it issues
-// its row's 128-bit weight loads first, then reads the (cached) token rows
-// and reduces one fp32 dot product per token. The last workgroup to finish
-// (an atomic ticket, no spinning) runs the top-k: one wavefront per token,
-// k rounds of a wave-wide argmax with lower-id tie-break, then the softmax
-// of the selected logits.
+// The post hides the gate's 2.6 MB cold read behind its producer with a
+// programmatic dependent launch. Here the chain is one launch whose latency
+// is a single HBM round trip plus the selection:
+//   - every wavefront owns one router row: it issues the row's 128-bit
+//     loads (1 KB contiguous per instruction) before anything else, then
+//     reduces one fp32 dot product per token with DPP (no LDS traffic);
+//   - the logits are published with device-scope stores, and the last
+//     workgroup to take a ticket (device-scope atomic; no spinning, no cache
+//     flush) selects: one wavefront per token, k rounds of a wave-wide
+//     (value, id) argmax with the lower id winning ties, then the softmax of
+//     the selected logits in fp32.
 #include "common.h"
 
 namespace mv {
 
-constexpr int kRouteThreads = 128;   // two wavefronts per workgroup
+constexpr int kRouteWaves = 8;
 
-template <int NC>  // NC = 16-byte chunks per lane per row (H <= 512 * NC)
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+// lexicographic (larger value, then smaller id) maximum with a DPP partner
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float &v, int &i)
+{
+    const float ov = dpp_f32<CTRL>(v);
+    const int oi = dpp_i32<CTRL>(i);
+    const bool take = ov > v || (ov == v && oi < i);
+    v = take ? ov : v;
+    i = take ? oi : i;
+}
+
+template <int NC, int KJ>  // NC: 16-byte chunks per lane per row; KJ: logits per lane
+__global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ wr,
     const float *__restrict__ bias, int M, int H, int E, int k,
     float *__restrict__ logits, int *__restrict__ topk_idx,
@@ -26,102 +42,101 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int nwave = blockDim.x / kWave;
-    const int nchunk = H / 8;
+    const int nch = H / 8;
 
     // ---- gate GEMV: l[t,e] = x[t,:] . wr[e,:] + bias[e]
-    for (int e = blockIdx.x * nwave + wave; e < E; e += gridDim.x * nwave) {
+    for (int e = blockIdx.x * kRouteWaves + wave; e < E; e += gridDim.x * kRouteWaves) {
         u32x4 w[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            const int i = lane + kWave * c;
-            w[c] = (i < nchunk) ? load_stream(wr + (size_t)e * nchunk + i)
-                                : u32x4{0, 0, 0, 0};
+            const int ci = lane + kWave * c;
+            w[c] = (ci < nch) ? load_stream(wr + (size_t)e * nch + ci) : u32x4{0, 0, 0, 0};
         }
         const float b = bias ? bias[e] : 0.0f;
         for (int t = 0; t < M; ++t) {
             float acc = 0.0f;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const int i = lane + kWave * c;
-                if (i < nchunk)
-                    acc = dot8_bf16(w[c], x[(size_t)t * nchunk + i], acc);
+                const int ci = lane + kWave * c;
+                if (ci < nch)
+                    acc = dot8_bf16(w[c], x[(size_t)t * nch + ci], acc);
             }
             acc = wave_sum(acc);
             if (lane == 0)
-                logits[(size_t)t * E + e] = acc + b;
+                __hip_atomic_store(logits + (size_t)t * E + e, acc + b, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
     // ---- the last workgroup to arrive selects
     __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0);               // this thread's logits are out
     __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();                         // publish this block's logits
-        const unsigned prev = atomicAdd(ticket, 1u);
-        s_last = (prev == gridDim.x - 1);
-    }
+    if (threadIdx.x == 0)
+        s_last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
     __syncthreads();
     if (!s_last)
         return;
-    __threadfence();                             // see every block's logits
     if (threadIdx.x == 0)
-        *ticket = 0u;                            // ready for the next call
+        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    constexpr int kJ = kMaxE / kWave;            // logits held per lane
-
-    for (int t = wave; t < M; t += nwave) {
-        float v[kJ];
+    for (int t = wave; t < M; t += kRouteWaves) {
+        float v[KJ];
         uint32_t taken = 0;
 #pragma unroll
-        for (int j = 0; j < kJ; ++j) {
-            const int e = lane + kWave * j;
+        for (int jj = 0; jj < KJ; ++jj) {
+            const int e = lane + kWave * jj;
             float l = -INFINITY;
             if (e < E) {
-                l = logits[(size_t)t * E + e];
+                l = __hip_atomic_load(logits + (size_t)t * E + e, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
                 if (l != l)
                     l = -INFINITY;               // NaN never outranks a number
             } else {
-                taken |= 1u << j;
+                taken |= 1u << jj;
             }
-            v[j] = l;
+            v[jj] = l;
         }
-        // lane s keeps the s-th selection
-        int my_e = 0;
+        int my_e = 0;                            // lane s keeps selection s
         float my_v = -INFINITY;
         for (int s = 0; s < k; ++s) {
-            // this lane's best untaken logit; j ascending = id ascending,
-            // so a strict comparison keeps the lower id on ties
+            // this lane's best free logit; jj ascending = id ascending
             float bv = -INFINITY;
             int be = 0x7FFFFFFF;
 #pragma unroll
-            for (int j = 0; j < kJ; ++j) {
-                const int e = lane + kWave * j;
-                const bool free = !((taken >> j) & 1u);
-                if (free && (v[j] > bv || (v[j] == bv && e < be))) {
-                    bv = v[j];
+            for (int jj = 0; jj < KJ; ++jj) {
+                const int e = lane + kWave * jj;
+                if (!((taken >> jj) & 1u) && (v[jj] > bv || (v[jj] == bv && e < be))) {
+                    bv = v[jj];
                     be = e;
                 }
             }
-            // wave-wide argmax, lower id on ties
+            argmax_dpp<kDppXor1>(bv, be);
+            argmax_dpp<kDppXor2>(bv, be);
+            argmax_dpp<kDppHalfMirror>(bv, be);
+            argmax_dpp<kDppMirror>(bv, be);
+            // the four row winners, in a fixed order
+            float wv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 0));
+            int wi = __builtin_amdgcn_readlane(be, 0);
 #pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) {
-                const float ov = __shfl_xor(bv, m);
-                const int oe = __shfl_xor(be, m);
-                if (ov > bv || (ov == bv && oe < be)) {
-                    bv = ov;
-                    be = oe;
+            for (int r = 1; r < 4; ++r) {
+                const float cv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 16 * r));
+                const int ci = __builtin_amdgcn_readlane(be, 16 * r);
+                if (cv > wv || (cv == wv && ci < wi)) {
+                    wv = cv;
+                    wi = ci;
                 }
             }
-            if ((be & (kWave - 1)) == lane)
-                taken |= 1u << (be / kWave);
+            if ((wi & (kWave - 1)) == lane)
+                taken |= 1u << (wi / kWave);
             if (lane == s) {
-                my_e = be;
-                my_v = bv;
+                my_e = wi;
+                my_v = wv;
             }
         }
         // softmax over the selected logits, shifted by the largest
-        const float top = __shfl(my_v, 0);
+        const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
         const float ex = (lane < k) ? expf(my_v - top) : 0.0f;
         const float den = wave_sum(ex);
         if (lane < k) {
@@ -131,16 +146,32 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
 }
 
+template <int NC, int KJ>
+static void launch_route2(const uint16_t *x, const uint16_t *w, const float *bias,
+                          int M, int H, int E, int k, float *logits, int *idx,
+                          float *tw, unsigned *ticket, hipStream_t st)
+{
+    const int grid = (E + kRouteWaves - 1) / kRouteWaves;
+    hipLaunchKernelGGL((route_kernel<NC, KJ>), dim3(grid), dim3(kRouteWaves * kWave), 0,
+                       st, (const u32x4 *)x, (const u32x4 *)w, bias, M, H, E, k,
+                       logits, idx, tw, ticket);
+}
+
 template <int NC>
 static void launch_route(const uint16_t *x, const uint16_t *w, const float *bias,
                          int M, int H, int E, int k, float *logits, int *idx,
                          float *tw, unsigned *ticket, hipStream_t st)
 {
-    const int nwave = kRouteThreads / kWave;
-    const int grid = (E + nwave - 1) / nwave;
-    hipLaunchKernelGGL(route_kernel<NC>, dim3(grid), dim3(kRouteThreads), 0, st,
-                       (const u32x4 *)x, (const u32x4 *)w, bias, M, H, E, k,
-                       logits, idx, tw, ticket);
+    if (E <= 64)
+        launch_route2<NC, 1>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
+    else if (E <= 128)
+        launch_route2<NC, 2>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
+    else if (E <= 256)
+        launch_route2<NC, 4>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
+    else if (E <= 512)
+        launch_route2<NC, 8>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
+    else
+        launch_route2<NC, 16>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
 }
 
 // Workspace: the header (ticket), then [M,E] fp32 logits scratch.
@@ -161,8 +192,6 @@ moe_status_t route_enqueue(const uint16_t *x, const uint16_t *w_router,
         launch_route<1>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
     else if (need <= 2)
         launch_route<2>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
-    else if (need <= 4)
-        launch_route<4>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
     else if (need <= 5)
         launch_route<5>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
     else if (need <= 8)
