@@ -123,6 +123,19 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
     return u >> 16;
 }
 
+// Workgroup barrier for LDS data written with ds_write/LDS atomics only:
+// waits for this wavefront's LDS operations (lgkmcnt) and keeps the compiler
+// from moving memory accesses across it, but leaves global loads -- and
+// direct-to-LDS loads into OTHER LDS regions -- in flight. Data that arrives
+// by direct-to-LDS loads needs wait_vmcnt and __syncthreads instead.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);                 // lgkmcnt(0) only
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Expert grouping of the (token, slot) pairs, built in LDS by every
 // workgroup that needs it. This is the pair-axis form of the grouping the
 // post describes in section "Two fusions and a retune": each pair compares
@@ -135,78 +148,133 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
 struct Groups {
     int D;                       // distinct valid experts
     int DV;                      // column blocks
+    int nvalid;                  // pairs with a valid expert id
+    int wheads[16];              // per-wavefront counts of bucket heads
+    int wvalid[16];              // per-wavefront counts of valid pairs
     int16_t e[kMaxNP];           // expert of pair p, -1 if out of range
-    int16_t head[kMaxNP];        // 1 if p is the first pair of its expert
     int16_t below[kMaxNP];       // valid pairs with a smaller expert id
+    int16_t same[kMaxNP];        // valid pairs with the same expert id
     int16_t sorted[kMaxNP];      // pair ids, bucket by bucket
     int16_t dexp[kMaxNP];        // expert id of bucket d
-    int16_t doff[kMaxNP + 1];    // bucket d = sorted[doff[d] .. doff[d+1])
+    int16_t doff[kMaxNP];        // bucket d starts at sorted[doff[d]]
+    int16_t dcnt[kMaxNP];        // pairs in bucket d
     int16_t vexp[kMaxNP];        // expert of column block v
     int16_t vbeg[kMaxNP];        // first index into sorted of block v
     int16_t vcnt[kMaxNP];        // pairs in block v (1..16)
 };
 
-__device__ inline void build_groups(const int *__restrict__ topk_idx, int NP,
-                                    int E, Groups &g)
+// Every phase is parallel over pairs or buckets (the workgroup has at least
+// NP <= 256 threads). Two steps, so that other prologue loads can be issued
+// in between: groups_set_pairs records this thread's pair (idx =
+// topk_idx[threadIdx.x], loaded by the caller), groups_finish builds the
+// buckets (it starts with a barrier).
+__device__ inline void groups_set_pairs(int idx, int NP, int E, Groups &g)
 {
-    const int tid = threadIdx.x, nt = blockDim.x;
-    for (int p = tid; p < NP; p += nt) {
-        const int e = topk_idx[p];
-        g.e[p] = (int16_t)((e >= 0 && e < E) ? e : -1);
-    }
-    __syncthreads();
-    // each pair against every other: rank in (expert, pair) order, whether
-    // it heads its bucket, and how many pairs sit in lower buckets
-    for (int p = tid; p < NP; p += nt) {
+    const int p = threadIdx.x;
+    if (p < NP)
+        g.e[p] = (int16_t)((idx >= 0 && idx < E) ? idx : -1);
+}
+
+__device__ inline void groups_finish(int NP, Groups &g)
+{
+    const int p = threadIdx.x;
+    lds_barrier();
+    // each pair against every other: its rank in (expert, pair) order, the
+    // pairs below its bucket and in it, and whether it heads the bucket
+    int head = 0;
+    if (p < NP && g.e[p] >= 0) {
         const int ep = g.e[p];
-        int below = 0, rank = 0, head = 1;
+        int below = 0, rank = 0, same = 0;
+        head = 1;
         for (int q = 0; q < NP; ++q) {
             const int eq = g.e[q];
             if (eq < 0)
                 continue;
             below += eq < ep;
+            same += eq == ep;
             rank += (eq < ep) || (eq == ep && q < p);
             head &= !(eq == ep && q < p);
         }
-        g.head[p] = (int16_t)((ep >= 0) ? head : 0);
         g.below[p] = (int16_t)below;
-        if (ep >= 0)
-            g.sorted[rank] = (int16_t)p;
+        g.same[p] = (int16_t)same;
+        g.sorted[rank] = (int16_t)p;
     }
-    __syncthreads();
+    // counts without atomics: a ballot per wavefront, summed after the barrier
+    {
+        const bool valid = p < NP && g.e[p] >= 0;
+        const unsigned long long hb = __ballot(head);
+        const unsigned long long vb = __ballot(valid);
+        if ((threadIdx.x & (kWave - 1)) == 0) {
+            g.wheads[threadIdx.x / kWave] = __popcll(hb);
+            g.wvalid[threadIdx.x / kWave] = __popcll(vb);
+        }
+    }
+    lds_barrier();
+    int D = 0, nvalid = 0;
+    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
+        D += g.wheads[w];
+        nvalid += g.wvalid[w];
+    }
     // bucket index of each head = heads with a smaller expert id
-    for (int p = tid; p < NP; p += nt) {
-        if (!g.head[p])
-            continue;
+    if (head) {
         const int ep = g.e[p];
         int d = 0;
         for (int q = 0; q < NP; ++q)
-            d += g.head[q] && g.e[q] < ep;
+            d += g.e[q] >= 0 && g.e[q] < ep && g.sorted[g.below[q]] == q;  // q heads its bucket
         g.dexp[d] = (int16_t)ep;
         g.doff[d] = g.below[p];
+        g.dcnt[d] = g.same[p];
     }
-    __syncthreads();
-    if (tid == 0) {
-        int D = 0, nv = 0;
-        for (int p = 0; p < NP; ++p) {
-            D += g.head[p];
-            nv += g.e[p] >= 0;
-        }
+    lds_barrier();
+    if (p == 0) {
         g.D = D;
-        g.doff[D] = (int16_t)nv;
-        int DV = 0;
-        for (int d = 0; d < D; ++d) {
-            const int n = g.doff[d + 1] - g.doff[d];
-            for (int o = 0; o < n; o += 16) {
-                g.vexp[DV] = g.dexp[d];
-                g.vbeg[DV] = (int16_t)(g.doff[d] + o);
-                g.vcnt[DV] = (int16_t)(n - o < 16 ? n - o : 16);
-                ++DV;
-            }
-        }
-        g.DV = DV;
+        g.nvalid = nvalid;
     }
-    __syncthreads();
+    // column blocks of <= 16 pairs: bucket d's blocks start after the
+    // blocks of the buckets below it
+    if (p < D) {
+        int vstart = 0;
+        for (int q = 0; q < p; ++q)
+            vstart += (g.dcnt[q] + 15) / 16;
+        const int n = g.dcnt[p];
+        for (int o = 0; o < n; o += 16) {
+            const int v = vstart + o / 16;
+            g.vexp[v] = g.dexp[p];
+            g.vbeg[v] = (int16_t)(g.doff[p] + o);
+            g.vcnt[v] = (int16_t)(n - o < 16 ? n - o : 16);
+        }
+        if (p == D - 1)
+            g.DV = vstart + (n + 15) / 16;
+    }
+    if (p == 0 && D == 0)
+        g.DV = 0;
+    lds_barrier();
+}
+
+__device__ inline void build_groups(const int *__restrict__ topk_idx, int NP, int E, Groups &g)
+{
+    const int idx = (int)threadIdx.x < NP ? topk_idx[threadIdx.x] : -1;
+    groups_set_pairs(idx, NP, E, g);
+    groups_finish(NP, g);
+}
+
+// Direct-to-LDS staging of nrows rows of nch 16-byte chunks (row-major,
+// contiguous) into LDS rows of pitch xs chunks: one 1 KB load per run of 64
+// chunks, spread over the workgroup's wavefronts, lanes past the row end
+// idle. Nothing waits here: the caller waits (vmcnt) and then synchronises.
+__device__ inline void stage_rows_lds(const u32x4 *__restrict__ src, int nrows, int nch,
+                                      u32x4 *dst, int xs)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nwave = blockDim.x / kWave;
+    const int runs = (nch + kWave - 1) / kWave;
+    for (int i = wave; i < nrows * runs; i += nwave) {
+        const int t = i / runs, r = i % runs;
+        const int c = r * kWave + lane;
+        if (c < nch)
+            load_lds16(src + (size_t)t * nch + c, dst + (size_t)t * xs + r * kWave);
+    }
 }
 
 // -------------------------------------------------------------------- host

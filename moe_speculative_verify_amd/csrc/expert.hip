@@ -35,72 +35,35 @@
 
 namespace mv {
 
-constexpr int kXWaves = 4;                          // wavefronts split K
-constexpr int kXKB = 128;                           // K elements per block
-constexpr int kXRowBytes = kXKB * 2;                // 256 B of a row per block
-constexpr int kXRowsPerLd = 1024 / kXRowBytes;      // 4 rows per load instruction
-constexpr int kXLoads = 16 / kXRowsPerLd;           // 4 loads per 16-row block
-constexpr int kXLdStride = 1024 + 16;               // LDS bytes per load (padded)
-constexpr int kXBuf = kXLoads * kXLdStride;         // one block of one matrix
-constexpr int kXSteps = kXKB / 32;                  // MFMA steps per block
+constexpr int kXWaves = 4;
 constexpr int kXThreads = kXWaves * kWave;
+constexpr int kXKB = 512;                           // K elements per block
+constexpr int kXRowPitch = kXKB * 2 + 16;           // LDS bytes per row (padded)
+constexpr int kXSteps = kXKB / 32;                  // MFMA steps per block
 constexpr int kXGrid = 256;                         // one workgroup per CU
-// static LDS (grouping + small arrays) stays below this margin
-constexpr int kXLdsDynMax = 160 * 1024 - 8 * 1024;
+constexpr int kXLdsDynMax = 160 * 1024 - 8 * 1024;  // static LDS stays below 8 KB
 
 static_assert(sizeof(Groups) + 64 <= 8 * 1024, "static LDS margin");
 
-struct UnitRange {
-    int u0, u1;       // this workgroup's units
-    int kb0, kb1;     // this wavefront's K blocks
-};
+// A value read from LDS that is the same in every lane, moved to a scalar
+// register so that control flow and addresses built from it stay scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-__device__ inline UnitRange unit_range(int nunits, int nkb)
-{
-    UnitRange r;
-    const int per = (nunits + gridDim.x - 1) / gridDim.x;
-    r.u0 = min(nunits, (int)blockIdx.x * per);
-    r.u1 = min(nunits, r.u0 + per);
-    const int wave = threadIdx.x / kWave;
-    const int kper = (nkb + kXWaves - 1) / kXWaves;
-    r.kb0 = min(nkb, wave * kper);
-    r.kb1 = min(nkb, r.kb0 + kper);
-    return r;
-}
-
-// Slot of this lane in a 16-row block load: row lrow of the four rows an
-// instruction covers, 16-byte chunk lcol of that row's 256-byte run.
-struct LdSlot {
-    int lrow, lcol;
-};
-__device__ __forceinline__ LdSlot ld_slot(int lane)
-{
-    return LdSlot{lane / (kWave / kXRowsPerLd), lane % (kWave / kXRowsPerLd)};
-}
-// LDS byte offset of the A fragment of lane (row j, K group g) in a block
-__device__ __forceinline__ int a_frag_off(int j, int g)
-{
-    return (j / kXRowsPerLd) * kXLdStride + (j % kXRowsPerLd) * kXRowBytes + g * 16;
-}
-
-// Issue the direct-to-LDS loads of one 16-row block of a [rows, K] matrix:
-// rows row0 .. row0+15 (clamped to nrows-1), K block kb (chunks clamped to
-// the row). Four instructions, 1 KB each.
-__device__ __forceinline__ void issue_block(const u32x4 *__restrict__ base, int row0,
-                                            int nrows, int nch, int kb, LdSlot sl,
-                                            unsigned char *buf)
-{
-    int c = kb * (kXKB / 8) + sl.lcol;
-    c = c < nch ? c : nch - 1;
-#pragma unroll
-    for (int q = 0; q < kXLoads; ++q) {
-        int row = row0 + q * kXRowsPerLd + sl.lrow;
-        row = row < nrows ? row : nrows - 1;
-        load_lds16(base + (size_t)row * nch + c, buf + q * kXLdStride);
-    }
-}
 
 // ------------------------------------------------------------------- up
+// Units = (column block v, 16-row tile of the expert's I rows). Unit u runs
+// on workgroup u % G, wavefront (u / G) % 4, so every CU gets work even at
+// M = 1. A wavefront streams each of its units over the full K = H in
+// blocks of KB = 128 (16 gate rows and 16 up rows, 256 B each: 8 loads of
+// 4 rows x 256 B) through an NB-deep ring; x is staged once per workgroup.
+constexpr int kUpKB = 128;
+constexpr int kUpPitch = kUpKB * 2 + 16;             // LDS bytes per row (padded)
+constexpr int kUpMat = 16 * kUpPitch;                // one matrix, 16 rows
+constexpr int kUpBlk = 2 * kUpMat;                   // gate + up
+constexpr int kUpLd = 8;                             // loads per block
+constexpr int kUpSteps = kUpKB / 32;
+
+template <int NB>
 __global__ __launch_bounds__(kXThreads) void expert_up_kernel(
     const u32x4 *__restrict__ x, const int *__restrict__ topk_idx,
     const u32x4 *__restrict__ wg, const u32x4 *__restrict__ wu, int M, int H,
@@ -109,100 +72,99 @@ __global__ __launch_bounds__(kXThreads) void expert_up_kernel(
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ Groups g;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = uniform(threadIdx.x / kWave);
     const int nch = H / 8;
-    const int nkb = (H + kXKB - 1) / kXKB;
-    const int xs = nkb * (kXKB / 8) + 1;                 // padded x row, chunks
+    const int nkb = (H + kUpKB - 1) / kUpKB;
+    const int xs = nkb * (kUpKB / 8) + 1;                // padded x row, chunks
     const size_t xbytes = align_up((size_t)M * xs * 16, 256);
     u32x4 *s_x = (u32x4 *)smem;
-    unsigned char *wbuf = smem + xbytes + wave * 4 * kXBuf;   // [2 bufs][gate, up]
-    float *red = (float *)(smem + xbytes + kXWaves * 4 * kXBuf); // [3][64][8]
+    unsigned char *ring = smem + xbytes + wave * NB * kUpBlk;
+    const int NP = M * k;
 
-    for (int i = threadIdx.x; i < M * xs; i += blockDim.x) {
-        const int t = i / xs, c = i % xs;
-        s_x[i] = (c < nch) ? x[(size_t)t * nch + c] : u32x4{0, 0, 0, 0};
+    // prologue: pair ids first (their load retires before the staging
+    // loads are issued), then x into LDS while the buckets are built
+    groups_set_pairs((int)threadIdx.x < NP ? topk_idx[threadIdx.x] : -1, NP, E, g);
+    wait_vmcnt<0>();                                     // only the pair id is in flight
+    for (int i = threadIdx.x; i < M * (xs - nch); i += blockDim.x) {
+        const int t = i / (xs - nch), c = nch + i % (xs - nch);
+        s_x[t * xs + c] = u32x4{0, 0, 0, 0};             // K padding reads as zero
     }
-    build_groups(topk_idx, M * k, E, g);                 // ends with a barrier
+    stage_rows_lds(x, M, nch, s_x, xs);
+    groups_finish(NP, g);
+    wait_vmcnt<0>();
+    __syncthreads();
 
     const int TI = (I + 15) / 16;
-    const UnitRange ur = unit_range(g.DV * TI, nkb);
-    const LdSlot sl = ld_slot(lane);
-    const int j = lane & 15, gq = lane >> 4;
-    const int aoff = a_frag_off(j, gq);
+    const int nunits = uniform(g.DV) * TI;
+    const int G = gridDim.x;
+    const int first = (int)blockIdx.x + G * wave;        // unit of local index 0
+    const int nmine = nunits > first ? (nunits - 1 - first) / (kXWaves * G) + 1 : 0;
+    const int nblk = nmine * nkb;
+    if (nblk == 0)
+        return;
+    auto unit_of = [&](int i) { return first + kXWaves * G * i; };
 
-    auto issue = [&](int u, int kb, int b) {
-        const int v = u / TI, tile = u % TI;
-        const size_t eoff = (size_t)g.vexp[v] * I;
-        unsigned char *bb = wbuf + b * 2 * kXBuf;
-        issue_block(wg + eoff * nch, tile * 16, I, nch, kb, sl, bb);
-        issue_block(wu + eoff * nch, tile * 16, I, nch, kb, sl, bb + kXBuf);
+    const int j = lane & 15, gq = lane >> 4;
+    const int lrow = lane >> 4, lcol = lane & 15;        // 4 rows x 16 chunks per load
+    // Past the end of the sequence the same number of loads reads a cached
+    // dummy into a slot nobody reads, so every iteration waits on one
+    // constant count.
+    const u32x4 *dummy = x + min(lane, M * nch - 1);
+    auto issue = [&](int X) {
+        const bool real = X < nblk;
+        const int Xr = real ? X : 0;
+        const int u = unit_of(Xr / nkb), kb = Xr % nkb;
+        const int v = u / TI, i0 = (u % TI) * 16;
+        unsigned char *slot = ring + (X % NB) * kUpBlk;
+        const size_t ebase = (size_t)uniform(g.vexp[v]) * I;
+        int c = kb * (kUpKB / 8) + lcol;
+        c = c < nch ? c : nch - 1;                       // K tail: x is zero there
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = min(i0 + 4 * q + lrow, I - 1);   // tail rows: unused
+            load_lds16(real ? wg + (ebase + row) * nch + c : dummy, slot + q * 4 * kUpPitch);
+            load_lds16(real ? wu + (ebase + row) * nch + c : dummy,
+                       slot + kUpMat + q * 4 * kUpPitch);
+        }
     };
 
-    int b = 0;
-    const bool has_k = ur.kb0 < ur.kb1;
-    if (has_k && ur.u0 < ur.u1)
-        issue(ur.u0, ur.kb0, 0);
-    for (int u = ur.u0; u < ur.u1; ++u) {
-        const int v = u / TI, tile = u % TI;
-        const int npair = g.vcnt[v];
+#pragma unroll
+    for (int q = 0; q < NB - 1; ++q)
+        issue(q);
+    f32x4 ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = ag;
+    for (int X = 0; X < nblk; ++X) {
+        issue(X + NB - 1);
+        wait_vmcnt<(NB - 1) * kUpLd>();                  // block X has landed
+        const int u = unit_of(X / nkb), kb = X % nkb;
+        const int v = u / TI;
+        const int npair = uniform(g.vcnt[v]);
         const bool col_ok = j < npair;
-        const int p = col_ok ? g.sorted[g.vbeg[v] + j] : 0;
-        const u32x4 *xrow = s_x + (p / k) * xs + gq;
-        f32x4 ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = ag;
-        for (int kb = ur.kb0; kb < ur.kb1; ++kb) {
-            // prefetch the next block of this wavefront's sequence
-            const bool last_kb = kb + 1 == ur.kb1;
-            const int nu = last_kb ? u + 1 : u;
-            const int nkbi = last_kb ? ur.kb0 : kb + 1;
-            if (nu < ur.u1) {
-                issue(nu, nkbi, b ^ 1);
-                wait_vmcnt<2 * kXLoads>();
-            } else {
-                wait_vmcnt<0>();
-            }
-            const unsigned char *bg = wbuf + b * 2 * kXBuf + aoff;
+        const int p = col_ok ? g.sorted[uniform(g.vbeg[v]) + j] : 0;
+        const u32x4 *xrow = s_x + (p / k) * xs + kb * (kUpKB / 8) + gq;
+        // A row j of the tile sits in load j / 4 at position j % 4
+        const unsigned char *sa = ring + (X % NB) * kUpBlk + (j >> 2) * 4 * kUpPitch +
+                                  (j & 3) * (kUpKB * 2) + gq * 16;
 #pragma unroll
-            for (int s = 0; s < kXSteps; ++s) {
-                u32x4 xv = xrow[kb * (kXKB / 8) + 4 * s];
-                if (!col_ok)
-                    xv = u32x4{0, 0, 0, 0};
-                ag = mfma_bf16(*(const MV_LDS u32x4 *)(bg + s * 64), xv, ag);
-                au = mfma_bf16(*(const MV_LDS u32x4 *)(bg + kXBuf + s * 64), xv, au);
-            }
-            b ^= 1;
+        for (int s = 0; s < kUpSteps; ++s) {
+            u32x4 xv = xrow[4 * s];
+            if (!col_ok)
+                xv = u32x4{0, 0, 0, 0};
+            ag = mfma_bf16(*(const MV_LDS u32x4 *)(sa + s * 64), xv, ag);
+            au = mfma_bf16(*(const MV_LDS u32x4 *)(sa + kUpMat + s * 64), xv, au);
         }
-        // sum the four K partials in wavefront order, then SwiGLU
-        if (wave > 0) {
-            float *rp = red + ((wave - 1) * kWave + lane) * 8;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                rp[r] = ag[r];
-                rp[4 + r] = au[r];
-            }
-        }
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll
-            for (int w = 1; w < kXWaves; ++w) {
-                const float *rp = red + ((w - 1) * kWave + lane) * 8;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    ag[r] += rp[r];
-                    au[r] += rp[4 + r];
-                }
-            }
+        if (kb == nkb - 1) {
+            // lane (j, gq) holds rows 4gq .. 4gq+3 of the tile for column j:
+            // SwiGLU in fp32, one rounding to bf16
             if (col_ok) {
-                // rows 4gq .. 4gq+3 of the tile for pair p
-                const int row0 = tile * 16 + 4 * gq;
+                const int row0 = (u % TI) * 16 + 4 * gq;
                 uint32_t h[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float gv = ag[r];
-                    const float a = gv / (1.0f + expf(-gv)) * au[r];
-                    h[r] = f32_to_bf16_rne(a);
+                    h[r] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * au[r]);
                 }
                 uint16_t *dst = act + (size_t)p * I + row0;
-                if (row0 + 3 < I && (I % 4) == 0) {
+                if (row0 + 3 < I) {
                     *(uint2 *)dst = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
                 } else {
                     for (int r = 0; r < 4; ++r)
@@ -210,156 +172,169 @@ __global__ __launch_bounds__(kXThreads) void expert_up_kernel(
                             dst[r] = (uint16_t)h[r];
                 }
             }
+            ag = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            au = ag;
         }
-        __syncthreads();
     }
+    wait_vmcnt<0>();                                     // dummy loads have landed
 }
 
 // ----------------------------------------------------------------- down
-constexpr int kXBBuf = kXSteps * 1024;              // B fragments of one block
-
+// Workgroup b owns R output rows r0 .. r0+R-1 for every expert; its
+// wavefronts split the column blocks (v = wave, wave+4, ...) and stream
+// the R rows of W_down[e] (1 KB per row per block, NB-deep ring). The B
+// fragments (the pairs' activations, L2-resident) are loaded at the start
+// of their block, ahead of the next weight block. Per-pair results y land in LDS and the
+// workgroup finishes with the weighted combine over slots in order, so no
+// other kernel and no cross-workgroup traffic is needed.
+template <int R, int NB>
 __global__ __launch_bounds__(kXThreads) void expert_down_kernel(
     const u32x4 *__restrict__ act, const int *__restrict__ topk_idx,
-    const u32x4 *__restrict__ wd, int M, int H, int I, int E, int k,
-    float *__restrict__ y)
+    const float *__restrict__ topk_w, const u32x4 *__restrict__ wd, int M, int H,
+    int I, int E, int k, float *__restrict__ out)
 {
+    constexpr int kBlk = R * kXRowPitch;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ Groups g;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = uniform(threadIdx.x / kWave);
     const int nch = I / 8;                               // K = I here
     const int nkb = (I + kXKB - 1) / kXKB;
-    unsigned char *wbuf = smem + wave * 2 * kXBuf;                    // A blocks
-    unsigned char *bbuf = smem + kXWaves * 2 * kXBuf + wave * 2 * kXBBuf;  // B blocks
-    float *red = (float *)(smem + kXWaves * 2 * (kXBuf + kXBBuf));    // [3][64][4]
+    const int r0 = blockIdx.x * R;
+    const int nr = min(R, H - r0);
+    unsigned char *ring = smem + wave * NB * kBlk;
+    float *y_s = (float *)(smem + kXWaves * NB * kBlk);  // [NP][R]
 
     build_groups(topk_idx, M * k, E, g);
 
-    const int TH = (H + 15) / 16;
-    const UnitRange ur = unit_range(g.DV * TH, nkb);
-    const LdSlot sl = ld_slot(lane);
+    const int DV = uniform(g.DV);
+    const int nv = DV > wave ? (DV - wave + kXWaves - 1) / kXWaves : 0;
+    const int nblk = nv * nkb;                           // this wavefront's blocks
     const int j = lane & 15, gq = lane >> 4;
-    const int aoff = a_frag_off(j, gq);
+    const bool row_ok = j < nr;
 
-    // A: 16 rows of W_down[e]; B: lane (j, gq) fetches the activation chunks
-    // of pair j for its K group, one 1 KB load per MFMA step, landing in lane
-    // order so that each lane later reads back exactly its own fragment
-    auto issue = [&](int u, int kb, int b) {
-        const int v = u / TH, tile = u % TH;
-        issue_block(wd + (size_t)g.vexp[v] * H * nch, tile * 16, H, nch, kb, sl,
-                    wbuf + b * kXBuf);
-        const int p = j < g.vcnt[v] ? g.sorted[g.vbeg[v] + j] : 0;
+    // Block X = (column block v, K block kb): R rows of W_down[e], 1 KB per
+    // row, into ring slot X % NB, issued NB-1 blocks ahead. Past the end of
+    // the sequence the same number of loads reads a cached dummy (act,
+    // clamped) into a slot nobody reads: every iteration then has the same
+    // loads in flight and waits on one constant count.
+    const int NP = M * k;
+    const u32x4 *dummy = act + min(lane, NP * nch - 1);
+    auto issue = [&](int X) {
+        const bool real = X < nblk;
+        const int Xr = real ? X : 0;
+        const int v = wave + kXWaves * (Xr / nkb), kb = Xr % nkb;
+        unsigned char *slot = ring + (X % NB) * kBlk;
+        const u32x4 *base = wd + (size_t)uniform(g.vexp[min(v, kMaxNP - 1)]) * H * nch;
+        int c = kb * (kXKB / 8) + lane;
+        c = c < nch ? c : nch - 1;
 #pragma unroll
-        for (int s = 0; s < kXSteps; ++s) {
-            int c = kb * (kXKB / 8) + 4 * s + gq;
-            c = c < nch ? c : nch - 1;
-            load_lds16(act + (size_t)p * nch + c, bbuf + b * kXBBuf + s * 1024);
+        for (int r = 0; r < R; ++r) {
+            const int row = min(r0 + r, H - 1);          // rows past H: unused
+            load_lds16(real ? base + (size_t)row * nch + c : dummy, slot + r * kXRowPitch);
         }
     };
 
-    int b = 0;
-    const bool has_k = ur.kb0 < ur.kb1;
-    if (has_k && ur.u0 < ur.u1)
-        issue(ur.u0, ur.kb0, 0);
-    for (int u = ur.u0; u < ur.u1; ++u) {
-        const int v = u / TH, tile = u % TH;
-        const bool col_ok = j < g.vcnt[v];
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int kb = ur.kb0; kb < ur.kb1; ++kb) {
-            const bool last_kb = kb + 1 == ur.kb1;
-            const int nu = last_kb ? u + 1 : u;
-            const int nkbi = last_kb ? ur.kb0 : kb + 1;
-            if (nu < ur.u1) {
-                issue(nu, nkbi, b ^ 1);
-                wait_vmcnt<kXLoads + kXSteps>();
-            } else {
-                wait_vmcnt<0>();
-            }
-            const unsigned char *ba = wbuf + b * kXBuf + aoff;
-            const unsigned char *bb = bbuf + b * kXBBuf + lane * 16;
 #pragma unroll
-            for (int s = 0; s < kXSteps; ++s) {
-                u32x4 bv = *(const MV_LDS u32x4 *)(bb + s * 1024);
-                if (!col_ok || kb * (kXKB / 8) + 4 * s + gq >= nch)
-                    bv = u32x4{0, 0, 0, 0};
-                acc = mfma_bf16(*(const MV_LDS u32x4 *)(ba + s * 64), bv, acc);
-            }
-            b ^= 1;
+    for (int q = 0; q < NB - 1; ++q)
+        issue(q);
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int X = 0; X < nblk; ++X) {
+        const int v = wave + kXWaves * (X / nkb), kb = X % nkb;
+        const int npair = uniform(g.vcnt[v]);
+        const bool col_ok = j < npair;
+        // B fragments of block X (pair j's activation chunks for K group
+        // gq, L2-resident), issued before the next weight block so that one
+        // wait covers both them and block X's weights (loads retire in order)
+        const int p = g.sorted[uniform(g.vbeg[v]) + (col_ok ? j : 0)];
+        u32x4 bf[kXSteps];
+#pragma unroll
+        for (int s = 0; s < kXSteps; ++s) {
+            const int c = min(kb * (kXKB / 8) + 4 * s + gq, nch - 1);
+            bf[s] = act[(size_t)p * nch + c];
         }
-        if (wave > 0) {
-            float *rp = red + ((wave - 1) * kWave + lane) * 4;
+        issue(X + NB - 1);
+        // block X's B loads (and everything older, block X's weights among
+        // them) have landed; the newest weight block stays in flight
+        wait_vmcnt<R>();
+        const unsigned char *slot = ring + (X % NB) * kBlk + (row_ok ? j : 0) * kXRowPitch + gq * 16;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                rp[r] = acc[r];
+        for (int s = 0; s < kXSteps; ++s) {
+            u32x4 a = *(const MV_LDS u32x4 *)(slot + s * 64);
+            if (!row_ok)
+                a = u32x4{0, 0, 0, 0};
+            u32x4 bv = bf[s];
+            if (!col_ok || kb * (kXKB / 8) + 4 * s + gq >= nch)
+                bv = u32x4{0, 0, 0, 0};
+            acc = mfma_bf16(a, bv, acc);
         }
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll
-            for (int w = 1; w < kXWaves; ++w) {
-                const float *rp = red + ((w - 1) * kWave + lane) * 4;
+        if (kb == nkb - 1) {
+            if (col_ok) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    acc[r] += rp[r];
+                    if (4 * gq + r < nr)
+                        y_s[p * R + 4 * gq + r] = acc[r];
             }
-            if (col_ok) {
-                const int p = g.sorted[g.vbeg[v] + j];
-                const int row0 = tile * 16 + 4 * gq;
-                float *dst = y + (size_t)p * H + row0;
-                if (row0 + 3 < H && (H % 4) == 0) {
-                    *(float4 *)dst = make_float4(acc[0], acc[1], acc[2], acc[3]);
-                } else {
-                    for (int r = 0; r < 4; ++r)
-                        if (row0 + r < H)
-                            dst[r] = acc[r];
-                }
-            }
+            acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
-        __syncthreads();
     }
-}
+    wait_vmcnt<0>();                                     // dummy loads have landed
+    __syncthreads();
 
-// -------------------------------------------------------------- combine
-__global__ __launch_bounds__(256) void expert_combine_kernel(
-    const float *__restrict__ y, const int *__restrict__ topk_idx,
-    const float *__restrict__ topk_w, int M, int H, int E, int k,
-    float *__restrict__ out)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= M * H)
-        return;
-    const int t = i / H, r = i % H;
-    float s = 0.0f;
-    for (int jj = 0; jj < k; ++jj) {
-        const int p = t * k + jj;
-        const int e = topk_idx[p];
-        if (e >= 0 && e < E)
-            s = fmaf(topk_w[p], y[(size_t)p * H + r], s);
+    // weighted combine, slots in order, fp32
+    for (int i = threadIdx.x; i < M * nr; i += blockDim.x) {
+        const int t = i / nr, rr = i % nr;
+        float sum = 0.0f;
+        for (int jj = 0; jj < k; ++jj) {
+            const int p = t * k + jj;
+            if (g.e[p] >= 0)
+                sum = fmaf(topk_w[p], y_s[p * R + rr], sum);
+        }
+        out[(size_t)t * H + r0 + rr] = sum;
     }
-    out[i] = s;
 }
 
 // ------------------------------------------------------------------ host
 
-static size_t up_lds_bytes(int M, int H)
+static size_t up_lds_bytes(int M, int H, int nb)
 {
-    const int nkb = (H + kXKB - 1) / kXKB;
-    return align_up((size_t)M * (nkb * (kXKB / 8) + 1) * 16, 256) +
-           (size_t)kXWaves * 4 * kXBuf + (size_t)(kXWaves - 1) * kWave * 8 * 4;
+    const int nkb = (H + kUpKB - 1) / kUpKB;
+    return align_up((size_t)M * (nkb * (kUpKB / 8) + 1) * 16, 256) +
+           (size_t)kXWaves * nb * kUpBlk;
 }
-static size_t down_lds_bytes()
+static int up_nb(int M, int H)
 {
-    return (size_t)kXWaves * 2 * (kXBuf + kXBBuf) + (size_t)(kXWaves - 1) * kWave * 4 * 4;
+    for (int nb = 3; nb >= 2; --nb)
+        if (up_lds_bytes(M, H, nb) <= (size_t)kXLdsDynMax)
+            return nb;
+    return 0;                                            // does not fit
+}
+// rows per down workgroup: at least ceil(H / 256), from the instantiated set
+static int down_rows(int H)
+{
+    const int need = (H + kXGrid - 1) / kXGrid;
+    const int opts[] = {4, 8, 10, 12, 16};
+    for (int r : opts)
+        if (r >= need)
+            return r;
+    return 0;
+}
+static size_t down_lds_bytes(int R, int NB, int M, int k)
+{
+    return (size_t)kXWaves * NB * R * kXRowPitch + (size_t)M * k * R * sizeof(float);
+}
+static int down_nb(int R, int M, int k)
+{
+    for (int nb = 3; nb >= 2; --nb)
+        if (down_lds_bytes(R, nb, M, k) <= (size_t)kXLdsDynMax)
+            return nb;
+    return 0;
 }
 
-// Workspace: the header, the [M*k, I] bf16 activations, the [M*k, H] fp32
-// per-pair down projections.
-static size_t ffn_act_bytes(int32_t M, int32_t I, int32_t k)
+// Workspace: the header, then the [M*k, I] bf16 activations.
+static size_t ffn_ws_bytes(int32_t M, int32_t I, int32_t k)
 {
-    return align_up((size_t)M * k * I * sizeof(uint16_t), 256);
-}
-static size_t ffn_ws_bytes(int32_t M, int32_t H, int32_t I, int32_t k)
-{
-    return kWsHeader + ffn_act_bytes(M, I, k) + align_up((size_t)M * k * H * sizeof(float), 256);
+    return kWsHeader + align_up((size_t)M * k * I * sizeof(uint16_t), 256);
 }
 
 static moe_status_t ffn_check(const uint16_t *x, const int32_t *topk_idx,
@@ -375,13 +350,48 @@ static moe_status_t ffn_check(const uint16_t *x, const int32_t *topk_idx,
         return s;
     if (I < 1)
         return MOE_ERR_SHAPE;
-    if (I % 8 != 0 || I > kMaxDim || up_lds_bytes(M, H) > (size_t)kXLdsDynMax)
+    if (I % 8 != 0 || I > kMaxDim || up_nb(M, H) == 0 || down_rows(H) == 0 ||
+        down_nb(down_rows(H), M, k) == 0)
         return MOE_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) ||
         !aligned16(w_down) || !aligned4(topk_idx) || !aligned4(topk_w) ||
         !aligned4(out))
         return MOE_ERR_ALIGN;
     return MOE_OK;
+}
+
+template <typename K>
+static hipError_t allow_lds(K kernel)
+{
+    return hipFuncSetAttribute((const void *)kernel,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, kXLdsDynMax);
+}
+
+static hipError_t set_lds_attributes()
+{
+    hipError_t e = hipSuccess;
+    auto chk = [&](hipError_t r) { if (r != hipSuccess) e = r; };
+    chk(allow_lds(expert_up_kernel<2>));
+    chk(allow_lds(expert_up_kernel<3>));
+#define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, 2>)); chk(allow_lds(expert_down_kernel<R, 3>));
+    MV_DOWN_ATTR(4) MV_DOWN_ATTR(8) MV_DOWN_ATTR(10) MV_DOWN_ATTR(12) MV_DOWN_ATTR(16)
+#undef MV_DOWN_ATTR
+    return e;
+}
+
+template <int R>
+static void launch_down_r(int nb, const uint16_t *act, const int *idx, const float *tw,
+                          const uint16_t *wd, int M, int H, int I, int E, int k, float *out,
+                          hipStream_t st)
+{
+    const int grid = (H + R - 1) / R;
+    const size_t lds = down_lds_bytes(R, nb, M, k);
+    if (nb == 3)
+        hipLaunchKernelGGL((expert_down_kernel<R, 3>), dim3(grid), dim3(kXThreads), lds, st,
+                           (const u32x4 *)act, idx, tw, (const u32x4 *)wd, M, H, I, E, k, out);
+    else
+        hipLaunchKernelGGL((expert_down_kernel<R, 2>), dim3(grid), dim3(kXThreads), lds, st,
+                           (const u32x4 *)act, idx, tw, (const u32x4 *)wd, M, H, I, E, k, out);
 }
 
 static moe_status_t ffn_enqueue(const uint16_t *x, const int32_t *topk_idx,
@@ -392,29 +402,34 @@ static moe_status_t ffn_enqueue(const uint16_t *x, const int32_t *topk_idx,
 {
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
-    std::call_once(once, [] {
-        attr = hipFuncSetAttribute((const void *)expert_up_kernel,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, kXLdsDynMax);
-    });
+    std::call_once(once, [] { attr = set_lds_attributes(); });
     if (attr != hipSuccess)
         return MOE_ERR_LAUNCH;
     uint16_t *act = (uint16_t *)((char *)ws + kWsHeader);
-    float *y = (float *)((char *)ws + kWsHeader + ffn_act_bytes(M, I, k));
-    hipLaunchKernelGGL(expert_up_kernel, dim3(kXGrid), dim3(kXThreads),
-                       up_lds_bytes(M, H), st, (const u32x4 *)x, topk_idx,
-                       (const u32x4 *)w_gate, (const u32x4 *)w_up, M, H, I, E, k, act);
+
+    const int nbu = up_nb(M, H);
+    const size_t ulds = up_lds_bytes(M, H, nbu);
+    if (nbu == 3)
+        hipLaunchKernelGGL(expert_up_kernel<3>, dim3(kXGrid), dim3(kXThreads), ulds, st,
+                           (const u32x4 *)x, topk_idx, (const u32x4 *)w_gate,
+                           (const u32x4 *)w_up, M, H, I, E, k, act);
+    else
+        hipLaunchKernelGGL(expert_up_kernel<2>, dim3(kXGrid), dim3(kXThreads), ulds, st,
+                           (const u32x4 *)x, topk_idx, (const u32x4 *)w_gate,
+                           (const u32x4 *)w_up, M, H, I, E, k, act);
     moe_status_t s = check_launch();
     if (s != MOE_OK)
         return s;
-    hipLaunchKernelGGL(expert_down_kernel, dim3(kXGrid), dim3(kXThreads), down_lds_bytes(),
-                       st, (const u32x4 *)act, topk_idx, (const u32x4 *)w_down, M, H, I,
-                       E, k, y);
-    s = check_launch();
-    if (s != MOE_OK)
-        return s;
-    const int n = M * H;
-    hipLaunchKernelGGL(expert_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, st, y,
-                       topk_idx, topk_w, M, H, E, k, out);
+
+    const int R = down_rows(H);
+    const int nbd = down_nb(R, M, k);
+    switch (R) {
+    case 4: launch_down_r<4>(nbd, act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
+    case 8: launch_down_r<8>(nbd, act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
+    case 10: launch_down_r<10>(nbd, act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
+    case 12: launch_down_r<12>(nbd, act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
+    default: launch_down_r<16>(nbd, act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
+    }
     return check_launch();
 }
 
@@ -437,7 +452,7 @@ extern "C" size_t moe_expert_ffn_workspace_bytes(int32_t M, int32_t H, int32_t I
 {
     if (check_moe_shape(M, H, E, k) != MOE_OK || I < 8 || I % 8 || I > kMaxDim)
         return 0;
-    return ffn_ws_bytes(M, H, I, k);
+    return ffn_ws_bytes(M, I, k);
 }
 
 extern "C" moe_status_t moe_expert_ffn(const uint16_t *x, const int32_t *topk_idx,

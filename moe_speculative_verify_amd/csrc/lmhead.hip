@@ -78,11 +78,14 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     u32x4 *s_x = (u32x4 *)smem;
     unsigned char *wbuf = smem + lm_x_bytes(M, H) + wave * 2 * kLmBuf;
 
-    // hidden states into LDS, zero beyond H
-    for (int i = threadIdx.x; i < M * xs; i += blockDim.x) {
-        const int t = i / xs, c = i % xs;
-        s_x[i] = (c < nch) ? h[(size_t)t * nch + c] : u32x4{0, 0, 0, 0};
+    // hidden states into LDS with direct-to-LDS loads (all in flight at
+    // once), K padding zeroed
+    for (int i = threadIdx.x; i < M * (xs - nch); i += blockDim.x) {
+        const int t = i / (xs - nch), c = nch + i % (xs - nch);
+        s_x[t * xs + c] = u32x4{0, 0, 0, 0};
     }
+    stage_rows_lds(h, M, nch, s_x, xs);
+    wait_vmcnt<0>();
     __syncthreads();
 
     const int j = lane & 15;        // A row in the tile / B column = token
