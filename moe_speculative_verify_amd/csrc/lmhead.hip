@@ -50,19 +50,6 @@ static size_t lm_lds_bytes(int M, int H)
     return lm_x_bytes(M, H) + (size_t)kLmWaves * 2 * kLmBuf;
 }
 
-// order-preserving map of fp32 to uint32 (-0 and +0 both map to +0's code)
-__device__ __forceinline__ uint32_t f32_order(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u)
-        u = 0;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float f32_unorder(uint32_t u)
-{
-    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
-}
-
 __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     const u32x4 *__restrict__ h, const u32x4 *__restrict__ wl, int M, int H,
     int V, int tiles_per_wg, unsigned long long *__restrict__ keys,

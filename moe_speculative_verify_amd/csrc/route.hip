@@ -8,68 +8,205 @@
 // The post hides the gate's 2.6 MB cold read behind its producer with a
 // programmatic dependent launch. Here the chain is one launch whose latency
 // is a single HBM round trip plus the selection:
-//   - every wavefront owns one router row: it issues the row's 128-bit
-//     loads (1 KB contiguous per instruction) before anything else, then
-//     reduces one fp32 dot product per token with DPP (no LDS traffic);
-//   - the logits are published with device-scope stores, and the last
-//     workgroup to take a ticket (device-scope atomic; no spinning, no cache
-//     flush) selects: one wavefront per token, k rounds of a wave-wide
-//     (value, id) argmax with the lower id winning ties, then the softmax of
-//     the selected logits in fp32.
+//   - a workgroup owns RT router rows (one MFMA tile of 16 rows, or 8 rows
+//     with the upper half of the tile repeating the lower) and its eight
+//     wavefronts split the hidden dimension. Every wavefront issues all of
+//     its weight loads and hidden-state loads (the latter hit in L2) at
+//     once, so the whole gate matrix is in flight across the grid, then runs
+//     one v_mfma_f32_16x16x32_bf16 per 32 columns. The eight partial tiles
+//     are added in LDS in a fixed order, the bias added, and the logits
+//     published with device-scope stores;
+//   - the last workgroup to take a ticket (device-scope atomic; no spinning,
+//     no cache flush) selects, one wavefront per token: every lane sorts its
+//     logits by (value descending, id ascending) once; then each of the k
+//     rounds takes the wave-wide maximum of the lane heads (DPP on the
+//     32-bit order code), breaks an equal-value tie by the lowest id, and
+//     advances the winning lane's list. All loads are unpredicated and every
+//     step is branch-free apart from uniform tie checks. The softmax of the
+//     selected logits is taken in fp32.
 #include "common.h"
+
+#include <utility>
 
 namespace mv {
 
-constexpr int kRouteWaves = 8;
+constexpr int kRouteWaves = 8;              // wavefronts per workgroup
 
-// lexicographic (larger value, then smaller id) maximum with a DPP partner
-template <int CTRL>
-__device__ __forceinline__ void argmax_dpp(float &v, int &i)
+// ---- per-lane sorted lists of 64-bit selection keys (order code of the
+// logit << 32 | ~id: a larger key is a larger logit, or an equal logit with
+// a smaller id; keys of distinct ids never tie). Written with compile-time
+// indices only, so every element stays in its own registers.
+
+template <int KJ, int A, int B, bool DESC>
+__device__ __forceinline__ void sel_cex(uint64_t (&key)[KJ])
 {
-    const float ov = dpp_f32<CTRL>(v);
-    const int oi = dpp_i32<CTRL>(i);
-    const bool take = ov > v || (ov == v && oi < i);
-    v = take ? ov : v;
-    i = take ? oi : i;
+    const uint64_t ka = key[A], kb = key[B];
+    const bool sw = DESC ? ka < kb : ka > kb;
+    key[A] = sw ? kb : ka;
+    key[B] = sw ? ka : kb;
 }
 
-template <int NC, int KJ>  // NC: 16-byte chunks per lane per row; KJ: logits per lane
+// one bitonic stage: compare-exchange every pair (a, a ^ STRIDE)
+template <int KJ, int SIZE, int STRIDE, int A>
+__device__ __forceinline__ void sel_stage(uint64_t (&key)[KJ])
+{
+    if constexpr (A < KJ) {
+        constexpr int B = A ^ STRIDE;
+        if constexpr (B > A)
+            sel_cex<KJ, A, B, (A & SIZE) == 0>(key);
+        sel_stage<KJ, SIZE, STRIDE, A + 1>(key);
+    }
+}
+template <int KJ, int SIZE, int STRIDE>
+__device__ __forceinline__ void sel_merge(uint64_t (&key)[KJ])
+{
+    if constexpr (STRIDE > 0) {
+        sel_stage<KJ, SIZE, STRIDE, 0>(key);
+        sel_merge<KJ, SIZE, STRIDE / 2>(key);
+    }
+}
+// bitonic sort, largest key first (KJ a power of two)
+template <int KJ, int SIZE = 2>
+__device__ __forceinline__ void sel_sort(uint64_t (&key)[KJ])
+{
+    if constexpr (SIZE <= KJ) {
+        sel_merge<KJ, SIZE, SIZE / 2>(key);
+        sel_sort<KJ, SIZE * 2>(key);
+    }
+}
+// drop the head of the list where adv is set (key 0 enters at the end)
+template <int KJ, int J = 0>
+__device__ __forceinline__ void sel_pop(uint64_t (&key)[KJ], bool adv)
+{
+    if constexpr (J + 1 < KJ) {
+        key[J] = adv ? key[J + 1] : key[J];
+        sel_pop<KJ, J + 1>(key, adv);
+    } else {
+        key[J] = adv ? 0ull : key[J];
+    }
+}
+
+// one DPP step of a wave-wide 64-bit maximum; rows a broadcast leaves out
+// receive 0, the identity
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t key_dpp_step(uint64_t v)
+{
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWMASK, 0xF, false);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWMASK, 0xF, false);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    return o > v ? o : v;
+}
+// largest key over the wavefront, uniform: DPP steps inside each 16-lane
+// row, the rows combined with row_bcast:15 (into rows 1 and 3) and
+// row_bcast:31 (into rows 2 and 3), then lane 63, which has seen every lane
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
+{
+    v = key_dpp_step<0xB1, 0xF>(v);
+    v = key_dpp_step<0x4E, 0xF>(v);
+    v = key_dpp_step<0x141, 0xF>(v);
+    v = key_dpp_step<0x140, 0xF>(v);
+    v = key_dpp_step<0x142, 0xA>(v);
+    v = key_dpp_step<0x143, 0xC>(v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// S: MFMA steps per wavefront; KJ: logits per lane in the selection (a
+// power of two, KJ * 64 >= E); RT: router rows per workgroup; P: column
+// blocks per MFMA. With P = 2 (RT = 8 rows, at most 8 tokens) one MFMA takes
+// two 32-column blocks at once, block-diagonally: tile rows 0-7 and tokens
+// 0-7 carry block X, tile rows 8-15 and tokens 8-15 carry block Y (the same
+// router rows and tokens), so D[r][t] + D[8+r][8+t] is the dot product over
+// 64 columns and every lane loads distinct data.
+template <int S, int KJ, int RT, int P>
 __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ wr,
     const float *__restrict__ bias, int M, int H, int E, int k,
     float *__restrict__ logits, int *__restrict__ topk_idx,
     float *__restrict__ topk_w, unsigned *__restrict__ ticket)
 {
+    static_assert(RT == 8 || RT == 16, "tile rows");
+    static_assert(P == 1 || (P == 2 && RT == 8), "block-diagonal packing needs 8-row tiles");
+    __shared__ f32x4 s_part[kRouteWaves][kWave];
+    __shared__ int s_last;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int nch = H / 8;
+    const int nch = H / 8;                       // 16-byte chunks per row
+    const int j = lane & 15;                     // A row in the tile / B column
+    const int g = lane >> 4;                     // chunk within a 32-column block
+    const int blk = P == 2 ? j >> 3 : 0;         // column block of this lane
+    const int e0 = blockIdx.x * RT;
 
-    // ---- gate GEMV: l[t,e] = x[t,:] . wr[e,:] + bias[e]
-    for (int e = blockIdx.x * kRouteWaves + wave; e < E; e += gridDim.x * kRouteWaves) {
-        u32x4 w[NC];
+    // ---- every load first, unpredicated: rows past E, tokens past M and
+    // chunks past the row end read valid memory (zeroed or unused below)
+    int arow = e0 + (P == 2 ? (j & 7) : (j % RT));
+    arow = arow < E ? arow : E - 1;
+    int tok = P == 2 ? (j & 7) : j;
+    tok = tok < M ? tok : M - 1;
+    const u32x4 *ap = wr + (size_t)arow * nch;
+    const u32x4 *bp = x + (size_t)tok * nch;
+    const int cbase = wave * (4 * P * S) + 4 * blk + g;
+    float bv[4];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int ci = lane + kWave * c;
-            w[c] = (ci < nch) ? load_stream(wr + (size_t)e * nch + ci) : u32x4{0, 0, 0, 0};
+    for (int r = 0; r < 4; ++r) {
+        const int e = e0 + 4 * g + r;
+        bv[r] = bias ? bias[e < E ? e : E - 1] : 0.0f;
+    }
+    // at most 16 steps of operands in registers at a time
+    constexpr int SPH = S < 16 ? S : 16;
+    static_assert(S % SPH == 0, "steps per phase");
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ph = 0; ph < S; ph += SPH) {
+        u32x4 a[SPH], b[SPH];
+#pragma unroll
+        for (int s = 0; s < SPH; ++s) {
+            const int c = cbase + 4 * P * (ph + s);
+            a[s] = load_stream(ap + (c < nch ? c : nch - 1));
         }
-        const float b = bias ? bias[e] : 0.0f;
-        for (int t = 0; t < M; ++t) {
-            float acc = 0.0f;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const int ci = lane + kWave * c;
-                if (ci < nch)
-                    acc = dot8_bf16(w[c], x[(size_t)t * nch + ci], acc);
-            }
-            acc = wave_sum(acc);
-            if (lane == 0)
-                __hip_atomic_store(logits + (size_t)t * E + e, acc + b, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        for (int s = 0; s < SPH; ++s) {
+            const int c = cbase + 4 * P * (ph + s);
+            b[s] = bp[c < nch ? c : nch - 1];
+        }
+        wait_vmcnt<0>();
+        // partial tile over this wavefront's columns
+#pragma unroll
+        for (int s = 0; s < SPH; ++s) {
+            const bool ok = cbase + 4 * P * (ph + s) < nch;
+            acc = mfma_bf16(ok ? a[s] : u32x4{0, 0, 0, 0}, ok ? b[s] : u32x4{0, 0, 0, 0}, acc);
+        }
+    }
+    s_part[wave][lane] = acc;
+    __syncthreads();
+
+    // ---- the partial tiles in a fixed order; lane (j, g) holds rows
+    // 4g .. 4g+3 of the tile for column j (with P = 2 the Y block of the
+    // same rows and token sits 40 lanes up)
+    if (wave == 0) {
+        f32x4 sum = s_part[0][lane];
+#pragma unroll
+        for (int w = 1; w < kRouteWaves; ++w)
+            sum += s_part[w][lane];
+        if (P == 2) {
+            const int ly = (lane + 40) & (kWave - 1);
+            f32x4 sy = s_part[0][ly];
+#pragma unroll
+            for (int w = 1; w < kRouteWaves; ++w)
+                sy += s_part[w][ly];
+            sum += sy;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 4 * g + r, e = e0 + row;
+            if (row < RT && e < E && j < M && (P == 1 || j < 8))
+                __hip_atomic_store(logits + (size_t)j * E + e, sum[r] + bv[r],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
     // ---- the last workgroup to arrive selects
-    __shared__ int s_last;
     __builtin_amdgcn_s_waitcnt(0);               // this thread's logits are out
     __syncthreads();
     if (threadIdx.x == 0)
@@ -82,96 +219,82 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
         __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     for (int t = wave; t < M; t += kRouteWaves) {
-        float v[KJ];
-        uint32_t taken = 0;
+        // this lane's logits e = lane + 64*q as (order code, id); ids past E
+        // get code 0, below every number (k <= E keeps them unselected)
+        uint64_t key[KJ];
+        float lv[KJ];
 #pragma unroll
-        for (int jj = 0; jj < KJ; ++jj) {
-            const int e = lane + kWave * jj;
-            float l = -INFINITY;
-            if (e < E) {
-                l = __hip_atomic_load(logits + (size_t)t * E + e, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-                if (l != l)
-                    l = -INFINITY;               // NaN never outranks a number
-            } else {
-                taken |= 1u << jj;
-            }
-            v[jj] = l;
+        for (int q = 0; q < KJ; ++q) {           // all loads in flight together
+            const int e = lane + kWave * q;
+            lv[q] = __hip_atomic_load(logits + (size_t)t * E + (e < E ? e : E - 1),
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        int my_e = 0;                            // lane s keeps selection s
-        float my_v = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < KJ; ++q) {
+            const int e = lane + kWave * q;
+            // NaN never outranks a number; -0 and +0 share a code
+            uint32_t u = __float_as_uint(lv[q] != lv[q] ? -INFINITY : lv[q]);
+            u = u == 0x80000000u ? 0u : u;
+            const uint32_t code = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+            key[q] = e < E ? ((uint64_t)code << 32) | (uint32_t)~(uint32_t)e : 0ull;
+        }
+        sel_sort<KJ>(key);
+        uint64_t sel = 0;                        // lane s keeps selection s
         for (int s = 0; s < k; ++s) {
-            // this lane's best free logit; jj ascending = id ascending
-            float bv = -INFINITY;
-            int be = 0x7FFFFFFF;
-#pragma unroll
-            for (int jj = 0; jj < KJ; ++jj) {
-                const int e = lane + kWave * jj;
-                if (!((taken >> jj) & 1u) && (v[jj] > bv || (v[jj] == bv && e < be))) {
-                    bv = v[jj];
-                    be = e;
-                }
-            }
-            argmax_dpp<kDppXor1>(bv, be);
-            argmax_dpp<kDppXor2>(bv, be);
-            argmax_dpp<kDppHalfMirror>(bv, be);
-            argmax_dpp<kDppMirror>(bv, be);
-            // the four row winners, in a fixed order
-            float wv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 0));
-            int wi = __builtin_amdgcn_readlane(be, 0);
-#pragma unroll
-            for (int r = 1; r < 4; ++r) {
-                const float cv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 16 * r));
-                const int ci = __builtin_amdgcn_readlane(be, 16 * r);
-                if (cv > wv || (cv == wv && ci < wi)) {
-                    wv = cv;
-                    wi = ci;
-                }
-            }
-            if ((wi & (kWave - 1)) == lane)
-                taken |= 1u << (wi / kWave);
-            if (lane == s) {
-                my_e = wi;
-                my_v = wv;
-            }
+            const uint64_t W = wave_max_key(key[0]);
+            sel = lane == s ? W : sel;
+            sel_pop<KJ>(key, key[0] == W);       // the winner's next logit moves up
         }
+        const int sel_i = (int)~(uint32_t)sel;
+        const uint32_t sel_h = (uint32_t)(sel >> 32);
         // softmax over the selected logits, shifted by the largest
+        const float my_v = f32_unorder(sel_h);
         const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
         const float ex = (lane < k) ? expf(my_v - top) : 0.0f;
         const float den = wave_sum(ex);
         if (lane < k) {
-            topk_idx[(size_t)t * k + lane] = my_e;
+            topk_idx[(size_t)t * k + lane] = sel_i;
             topk_w[(size_t)t * k + lane] = ex / den;
         }
     }
 }
 
-template <int NC, int KJ>
-static void launch_route2(const uint16_t *x, const uint16_t *w, const float *bias,
-                          int M, int H, int E, int k, float *logits, int *idx,
-                          float *tw, unsigned *ticket, hipStream_t st)
+template <int S, int KJ, int P>
+static moe_status_t launch_route3(const uint16_t *x, const uint16_t *w, const float *bias,
+                                  int M, int H, int E, int k, float *logits, int *idx,
+                                  float *tw, unsigned *ticket, hipStream_t st)
 {
-    const int grid = (E + kRouteWaves - 1) / kRouteWaves;
-    hipLaunchKernelGGL((route_kernel<NC, KJ>), dim3(grid), dim3(kRouteWaves * kWave), 0,
-                       st, (const u32x4 *)x, (const u32x4 *)w, bias, M, H, E, k,
-                       logits, idx, tw, ticket);
+    constexpr int RT = 8;
+    const int grid = (E + RT - 1) / RT;
+    hipLaunchKernelGGL((route_kernel<S, KJ, RT, P>), dim3(grid), dim3(kRouteWaves * kWave), 0,
+                       st, (const u32x4 *)x, (const u32x4 *)w, bias, M, H, E, k, logits,
+                       idx, tw, ticket);
+    return check_launch();
 }
 
-template <int NC>
-static void launch_route(const uint16_t *x, const uint16_t *w, const float *bias,
-                         int M, int H, int E, int k, float *logits, int *idx,
-                         float *tw, unsigned *ticket, hipStream_t st)
+// S counts MFMA steps of 32 columns; packed, each step takes 64
+template <int S, int KJ>
+static moe_status_t launch_route2(const uint16_t *x, const uint16_t *w, const float *bias,
+                                  int M, int H, int E, int k, float *logits, int *idx,
+                                  float *tw, unsigned *ticket, hipStream_t st)
 {
-    if (E <= 64)
-        launch_route2<NC, 1>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
-    else if (E <= 128)
-        launch_route2<NC, 2>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
-    else if (E <= 256)
-        launch_route2<NC, 4>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
-    else if (E <= 512)
-        launch_route2<NC, 8>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
-    else
-        launch_route2<NC, 16>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
+    if (M <= 8)
+        return launch_route3<(S + 1) / 2, KJ, 2>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
+    return launch_route3<S, KJ, 1>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
+}
+
+template <int S>
+static moe_status_t launch_route(const uint16_t *x, const uint16_t *w, const float *bias,
+                                 int M, int H, int E, int k, float *logits, int *idx,
+                                 float *tw, unsigned *ticket, hipStream_t st)
+{
+    if (E <= 128)
+        return launch_route2<S, 2>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
+    if (E <= 256)
+        return launch_route2<S, 4>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
+    if (E <= 512)
+        return launch_route2<S, 8>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
+    return launch_route2<S, 16>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
 }
 
 // Workspace: the header (ticket), then [M,E] fp32 logits scratch.
@@ -187,18 +310,17 @@ moe_status_t route_enqueue(const uint16_t *x, const uint16_t *w_router,
 {
     unsigned *ticket = (unsigned *)ws;
     float *lg = logits ? logits : (float *)((char *)ws + kWsHeader);
-    const int need = (H / 8 + kWave - 1) / kWave;
-    if (need <= 1)
-        launch_route<1>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
-    else if (need <= 2)
-        launch_route<2>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
-    else if (need <= 5)
-        launch_route<5>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
-    else if (need <= 8)
-        launch_route<8>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
-    else
-        launch_route<16>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
-    return check_launch();
+    // MFMA steps per wavefront: eight wavefronts of 32-column steps
+    const int need = (H / 8 + 4 * kRouteWaves - 1) / (4 * kRouteWaves);
+    if (need <= 2)
+        return launch_route<2>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
+    if (need <= 4)
+        return launch_route<4>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
+    if (need <= 10)
+        return launch_route<10>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
+    if (need <= 16)
+        return launch_route<16>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
+    return launch_route<32>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
 }
 
 moe_status_t route_check(const uint16_t *x, const uint16_t *w_router,

@@ -59,6 +59,8 @@ ROUTE_CASES = [
     (6, 2560, 512, 8, 1.0),      # with Zipf bias
     (16, 2560, 512, 8, 1.0),     # block-16 verify
     (5, 4096, 1024, 16, 0.5),    # largest E and k
+    (8, 8192, 256, 8, None),     # widest hidden state staged in LDS
+    (16, 8192, 1024, 16, 0.5),   # hidden states too large for LDS: read from the caches
 ]
 
 
@@ -94,6 +96,26 @@ def test_route_zero_input_and_planted_ties():
     gi_a, _, gl_a = run_route(x, wr, None, k)
     gi_b, _, gl_b = run_route(x2, wr, None, k)
     assert np.array_equal(gi_a, gi_b) and np.array_equal(gl_b, 2 * gl_a)
+
+
+@pytest.mark.parametrize("E,k", [(512, 8), (1024, 16), (200, 8)])
+def test_route_planted_ties_full_width(E, k):
+    """Zero hidden states make the logits equal to the bias exactly; a bias
+    with few distinct values plants ties inside a lane (ids e and e + 64) and
+    across lanes. Order is value descending, then id ascending."""
+    say("route planted ties", E, k)
+    M, H = 3, 2560
+    wr = synth.normal_bf16((E, H), 0.02, 9, E)
+    bias = np.stack([((np.arange(E) * (31 + 6 * t)) % (5 + t)).astype(np.float32)
+                     for t in range(M)])
+    for t in range(M):
+        gi, gw, gl = run_route(np.zeros((1, H), np.uint16), wr, bias[t].copy(), k)
+        order = np.lexsort((np.arange(E), -bias[t].astype(np.float64)))[:k]
+        assert np.array_equal(gi[0], order), (t, gi[0], order)
+        assert np.array_equal(gl[0], bias[t])
+        ref = oracle.route(np.zeros((1, H), np.uint16), wr, bias[t].copy(), k)
+        assert np.array_equal(gi[0], ref["idx"][0])
+        assert_close(gw[0], ref["w"][0], "topk_w")
 
 
 # ----------------------------------------------------------- expert FFN
