@@ -105,7 +105,13 @@ __device__ __forceinline__ void load_lds16(const void *g, void *lds_wave_base)
     __builtin_amdgcn_global_load_lds(g, (MV_LDS void *)lds_wave_base, 16, 0, 2);
 }
 
-// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left alone).
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left alone). Direct-to-LDS loads
+// have side effects and keep their program order, so a count over them is
+// exact. Plain loads from read-only kernel arguments may be moved by the
+// compiler (it also inserts the waits their register uses need), so with
+// those in flight a nonzero count is only a scheduling hint: data that other
+// wavefronts read from LDS is waited for with N = 0 unless only
+// direct-to-LDS loads can follow it.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
 {
@@ -187,94 +193,114 @@ __device__ __forceinline__ void lds_barrier()
 struct Groups {
     int D;                       // distinct valid experts
     int DV;                      // column blocks
-    int nvalid;                  // pairs with a valid expert id
     int wheads[16];              // per-wavefront counts of bucket heads
-    int wvalid[16];              // per-wavefront counts of valid pairs
-    int16_t e[kMaxNP];           // expert of pair p, -1 if out of range
-    int16_t below[kMaxNP];       // valid pairs with a smaller expert id
-    int16_t same[kMaxNP];        // valid pairs with the same expert id
-    int16_t sorted[kMaxNP];      // pair ids, bucket by bucket
-    int16_t dexp[kMaxNP];        // expert id of bucket d
-    int16_t doff[kMaxNP];        // bucket d starts at sorted[doff[d]]
-    int16_t dcnt[kMaxNP];        // pairs in bucket d
-    int16_t vexp[kMaxNP];        // expert of column block v
-    int16_t vbeg[kMaxNP];        // first index into sorted of block v
-    int16_t vcnt[kMaxNP];        // pairs in block v (1..16)
+    int pad_[14];
+    // int16 arrays, 16-byte aligned and padded to a multiple of 8 entries
+    // so that eight entries are read with one 128-bit LDS load
+    alignas(16) int16_t e[kMaxNP];      // expert of pair p, -1 if out of range
+    alignas(16) int16_t hd[kMaxNP];     // expert of pair p if it heads its bucket, else -1
+    alignas(16) int16_t sorted[kMaxNP]; // pair ids, bucket by bucket
+    alignas(16) int16_t dexp[kMaxNP];   // expert id of bucket d
+    alignas(16) int16_t doff[kMaxNP];   // bucket d starts at sorted[doff[d]]
+    alignas(16) int16_t dcnt[kMaxNP];   // pairs in bucket d
+    alignas(16) int16_t vexp[kMaxNP];   // expert of column block v
+    alignas(16) int16_t vbeg[kMaxNP];   // first index into sorted of block v
+    alignas(16) int16_t vcnt[kMaxNP];   // pairs in block v (1..16)
 };
 
+// Eight consecutive int16 entries of an LDS array (index a multiple of 8).
+__device__ __forceinline__ void lds_load8(const int16_t *arr, int q0, int (&v)[8])
+{
+    const u32x4 w = *(const u32x4 *)(arr + q0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = (int)(int16_t)(w[i] & 0xFFFFu);
+        v[2 * i + 1] = (int)w[i] >> 16;
+    }
+}
+
 // Every phase is parallel over pairs or buckets (the workgroup has at least
-// NP <= 256 threads). Two steps, so that other prologue loads can be issued
-// in between: groups_set_pairs records this thread's pair (idx =
-// topk_idx[threadIdx.x], loaded by the caller), groups_finish builds the
-// buckets (it starts with a barrier).
+// NP <= 256 threads) and reads the shared arrays eight entries at a time,
+// with no dependent LDS reads. Two steps, so that other prologue loads can
+// be issued in between: groups_set_pairs records this thread's pair (idx =
+// topk_idx[threadIdx.x], loaded by the caller; threads past NP pad the array
+// with -1), groups_finish builds the buckets (it starts with a barrier).
 __device__ inline void groups_set_pairs(int idx, int NP, int E, Groups &g)
 {
     const int p = threadIdx.x;
-    if (p < NP)
-        g.e[p] = (int16_t)((idx >= 0 && idx < E) ? idx : -1);
+    if (p < ((NP + 7) & ~7))
+        g.e[p] = (int16_t)((p < NP && idx >= 0 && idx < E) ? idx : -1);
 }
 
 __device__ inline void groups_finish(int NP, Groups &g)
 {
     const int p = threadIdx.x;
+    const int NP8 = (NP + 7) & ~7;
     lds_barrier();
     // each pair against every other: its rank in (expert, pair) order, the
     // pairs below its bucket and in it, and whether it heads the bucket
-    int head = 0;
-    if (p < NP && g.e[p] >= 0) {
-        const int ep = g.e[p];
-        int below = 0, rank = 0, same = 0;
+    const int ep = p < NP ? g.e[p] : -1;
+    int below = 0, same = 0, rank = 0, head = 0;
+    if (ep >= 0) {
         head = 1;
-        for (int q = 0; q < NP; ++q) {
-            const int eq = g.e[q];
-            if (eq < 0)
-                continue;
-            below += eq < ep;
-            same += eq == ep;
-            rank += (eq < ep) || (eq == ep && q < p);
-            head &= !(eq == ep && q < p);
+        for (int q0 = 0; q0 < NP8; q0 += 8) {
+            int eq[8];
+            lds_load8(g.e, q0, eq);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = q0 + i;
+                const bool ok = eq[i] >= 0;
+                const bool lt = ok && eq[i] < ep;
+                const bool eqe = ok && eq[i] == ep;
+                below += lt;
+                same += eqe;
+                rank += lt || (eqe && q < p);
+                head &= !(eqe && q < p);
+            }
         }
-        g.below[p] = (int16_t)below;
-        g.same[p] = (int16_t)same;
         g.sorted[rank] = (int16_t)p;
     }
-    // counts without atomics: a ballot per wavefront, summed after the barrier
+    if (p < NP8)
+        g.hd[p] = (int16_t)(head ? ep : -1);
+    // bucket count without atomics: a ballot per wavefront, summed after
+    // the barrier
     {
-        const bool valid = p < NP && g.e[p] >= 0;
         const unsigned long long hb = __ballot(head);
-        const unsigned long long vb = __ballot(valid);
-        if ((threadIdx.x & (kWave - 1)) == 0) {
+        if ((threadIdx.x & (kWave - 1)) == 0)
             g.wheads[threadIdx.x / kWave] = __popcll(hb);
-            g.wvalid[threadIdx.x / kWave] = __popcll(vb);
-        }
     }
     lds_barrier();
-    int D = 0, nvalid = 0;
-    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) {
+    int D = 0;
+    for (int w = 0; w < (int)(blockDim.x / kWave); ++w)
         D += g.wheads[w];
-        nvalid += g.wvalid[w];
-    }
     // bucket index of each head = heads with a smaller expert id
     if (head) {
-        const int ep = g.e[p];
         int d = 0;
-        for (int q = 0; q < NP; ++q)
-            d += g.e[q] >= 0 && g.e[q] < ep && g.sorted[g.below[q]] == q;  // q heads its bucket
+        for (int q0 = 0; q0 < NP8; q0 += 8) {
+            int hq[8];
+            lds_load8(g.hd, q0, hq);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                d += hq[i] >= 0 && hq[i] < ep;
+        }
         g.dexp[d] = (int16_t)ep;
-        g.doff[d] = g.below[p];
-        g.dcnt[d] = g.same[p];
+        g.doff[d] = (int16_t)below;
+        g.dcnt[d] = (int16_t)same;
     }
     lds_barrier();
-    if (p == 0) {
+    if (p == 0)
         g.D = D;
-        g.nvalid = nvalid;
-    }
     // column blocks of <= 16 pairs: bucket d's blocks start after the
     // blocks of the buckets below it
     if (p < D) {
         int vstart = 0;
-        for (int q = 0; q < p; ++q)
-            vstart += (g.dcnt[q] + 15) / 16;
+        for (int q0 = 0; q0 < p; q0 += 8) {
+            int cq[8];
+            lds_load8(g.dcnt, q0, cq);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                vstart += q0 + i < p ? (cq[i] + 15) / 16 : 0;
+        }
         const int n = g.dcnt[p];
         for (int o = 0; o < n; o += 16) {
             const int v = vstart + o / 16;

@@ -294,6 +294,168 @@ __global__ __launch_bounds__(kXThreads) void expert_down_kernel(
     }
 }
 
+// ---------------------------------------------------------- down (GEMV)
+// The down projection at verify widths is a set of matrix-vector products:
+// with distinct experts per token a column block holds about one pair. The
+// weights therefore stream straight into registers -- one 1 KB load per row
+// per K block (lane i takes 16-byte chunk i), an NB-deep register ring, so
+// (NB - 1) blocks of every wavefront are in flight while one is consumed --
+// and every pair's activation row sits in LDS, staged once per workgroup with
+// direct-to-LDS loads. Nothing but the weights is read inside the loop, so
+// the loop waits on one constant count. Per (pair, K block) every lane forms
+// R eight-element dot products (v_dot2_f32_bf16) and each row is summed over
+// the wavefront in a fixed DPP tree; the block sums are added over K blocks
+// in order in the combine. Workgroup b owns rows r0 .. r0+R-1 of every
+// expert; its wavefronts split the column blocks (v = wave, wave+4, ...).
+constexpr int kDnKB = 512;                       // K elements per block
+constexpr int kDnCh = kDnKB / 8;                 // 16-byte chunks per row per block
+
+// Sum over the wavefront in a fixed order, returned uniform: the 16-lane row
+// butterfly, then row 1 += row 0 and row 3 += row 2 (row_bcast:15), then
+// row 3 += row 1 (row_bcast:31); lane 63 holds (r3 + r2) + (r1 + r0).
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float add_dpp_step(float v)
+{
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                   0, __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xF, false));
+}
+__device__ __forceinline__ float wave_total(float v)
+{
+    v = add_dpp_step<0xB1, 0xF>(v);
+    v = add_dpp_step<0x4E, 0xF>(v);
+    v = add_dpp_step<0x141, 0xF>(v);
+    v = add_dpp_step<0x140, 0xF>(v);
+    v = add_dpp_step<0x142, 0xA>(v);
+    v = add_dpp_step<0x143, 0xC>(v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+__host__ __device__ inline size_t down_gemv_act_bytes(int NP, int I)
+{
+    const int nkb = (I / 8 + kDnCh - 1) / kDnCh;
+    return align_up((size_t)NP * nkb * kDnCh * 16, 256);
+}
+__host__ __device__ inline size_t down_gemv_lds_bytes(int R, int NP, int I)
+{
+    const int nkb = (I / 8 + kDnCh - 1) / kDnCh;
+    return down_gemv_act_bytes(NP, I) + (size_t)NP * nkb * R * sizeof(float);
+}
+
+template <int R, int NB>
+__global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
+    const u32x4 *__restrict__ act, const int *__restrict__ topk_idx,
+    const float *__restrict__ topk_w, const u32x4 *__restrict__ wd, int M, int H,
+    int I, int E, int k, float *__restrict__ out)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ Groups g;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int nch = I / 8;                               // K = I here
+    const int nkb = (nch + kDnCh - 1) / kDnCh;
+    const int xs = nkb * kDnCh;                          // LDS activation row, chunks
+    const int NP = M * k;
+    const int r0 = blockIdx.x * R;
+    const int nr = min(R, H - r0);
+    u32x4 *s_act = (u32x4 *)smem;                        // [NP][xs]
+    float *s_y = (float *)(smem + down_gemv_act_bytes(NP, I));  // [NP][nkb][R]
+
+    // prologue: pair ids and buckets; then the ring's first weight blocks
+    // and every pair's activation row into LDS (direct-to-LDS), so the
+    // weights lead the memory queue
+    groups_set_pairs((int)threadIdx.x < NP ? topk_idx[threadIdx.x] : -1, NP, E, g);
+    wait_vmcnt<0>();                                     // only the pair id is in flight
+    for (int i = threadIdx.x; i < NP * (xs - nch); i += blockDim.x) {
+        const int p = i / (xs - nch), c = nch + i % (xs - nch);
+        s_act[p * xs + c] = u32x4{0, 0, 0, 0};           // K padding reads as zero
+    }
+    groups_finish(NP, g);
+
+    const int DV = uniform(g.DV);
+    const int nv = DV > wave ? (DV - wave + kXWaves - 1) / kXWaves : 0;
+    const int nblk = nv * nkb;                           // this wavefront's blocks
+
+    // Block X = (column block v, K block kb): lane i loads chunk i of the
+    // block for each of the R rows. Past the end of the sequence the same
+    // number of loads rereads the first kilobyte of W_down (cached), so every
+    // wait is one constant; the choice is an index select, one base pointer.
+    auto issue = [&](int X, u32x4 (&dst)[R]) {
+        const bool real = X < nblk;
+        const int Xr = real ? X : 0;
+        const int v = wave + kXWaves * (Xr / nkb), kb = Xr % nkb;
+        const size_t eoff = (size_t)uniform(g.vexp[min(v, kMaxNP - 1)]) * H * nch;
+        const u32x4 *bp = wd + (real ? eoff : 0);        // uniform
+        int c = kb * kDnCh + lane;
+        c = c < nch ? c : nch - 1;                       // K tail: zeroed before use
+        const int cd = min(lane, nch - 1);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = min(r0 + r, H - 1);          // rows past H: unused
+            int off = real ? row * nch + c : cd;
+            asm volatile("" : "+v"(off));                // one load on one path: no branch
+            dst[r] = load_stream(bp + off);
+        }
+    };
+    auto consume = [&](int X, u32x4 (&wr)[R]) {
+        const int v = wave + kXWaves * (X / nkb), kb = X % nkb;
+        const int npair = uniform(g.vcnt[v]);
+        const int pb = uniform(g.vbeg[v]);
+        if (kb * kDnCh + kDnCh > nch) {                  // uniform: the K tail block
+            const bool ok = kb * kDnCh + lane < nch;
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                wr[r] = ok ? wr[r] : u32x4{0, 0, 0, 0};
+        }
+        for (int jj = 0; jj < npair; ++jj) {
+            const int p = uniform(g.sorted[pb + jj]);
+            const u32x4 a = s_act[p * xs + kb * kDnCh + lane];
+            float yv = 0.0f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float t = wave_total(dot8_bf16(wr[r], a, 0.0f));
+                yv = lane == r ? t : yv;
+            }
+            if (lane < nr)
+                s_y[(p * nkb + kb) * R + lane] = yv;
+        }
+    };
+
+    u32x4 w[NB][R];
+#pragma unroll
+    for (int q = 0; q < NB - 1; ++q)
+        issue(q, w[q]);
+    stage_rows_lds(act, NP, nch, s_act, xs);
+    wait_vmcnt<0>();                                     // this wave's staging has landed
+    lds_barrier();                                       // ... and every other wave's staging
+    for (int X0 = 0; X0 < nblk; X0 += NB) {
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            issue(X0 + q + NB - 1, w[(q + NB - 1) % NB]);
+            wait_vmcnt<(NB - 1) * R>();                  // block X0 + q has landed
+            if (X0 + q < nblk)
+                consume(X0 + q, w[q]);
+        }
+    }
+    wait_vmcnt<0>();                                     // dummy loads have landed
+    __syncthreads();
+
+    // weighted combine, slots in order, fp32; each pair's K blocks in order
+    for (int i = threadIdx.x; i < M * nr; i += blockDim.x) {
+        const int t = i / nr, rr = i % nr;
+        float sum = 0.0f;
+        for (int jj = 0; jj < k; ++jj) {
+            const int p = t * k + jj;
+            if (g.e[p] >= 0) {
+                float y = 0.0f;
+                for (int kb = 0; kb < nkb; ++kb)
+                    y += s_y[(p * nkb + kb) * R + rr];
+                sum = fmaf(topk_w[p], y, sum);
+            }
+        }
+        out[(size_t)t * H + r0 + rr] = sum;
+    }
+}
+
 // ------------------------------------------------------------------ host
 
 static size_t up_lds_bytes(int M, int H, int nb)
@@ -318,6 +480,13 @@ static int down_rows(int H)
         if (r >= need)
             return r;
     return 0;
+}
+// register ring depth of the GEMV down kernel: R * NB 16-byte loads per lane
+constexpr int down_gemv_nb(int R) { return R <= 10 ? 4 : (R <= 12 ? 3 : 2); }
+// the GEMV down kernel runs when every pair's activation row fits in LDS
+static bool down_gemv_fits(int R, int M, int k, int I)
+{
+    return down_gemv_lds_bytes(R, M * k, I) <= (size_t)kXLdsDynMax;
 }
 static size_t down_lds_bytes(int R, int NB, int M, int k)
 {
@@ -373,10 +542,23 @@ static hipError_t set_lds_attributes()
     auto chk = [&](hipError_t r) { if (r != hipSuccess) e = r; };
     chk(allow_lds(expert_up_kernel<2>));
     chk(allow_lds(expert_up_kernel<3>));
-#define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, 2>)); chk(allow_lds(expert_down_kernel<R, 3>));
+#define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, 2>)); chk(allow_lds(expert_down_kernel<R, 3>)); \
+    chk(allow_lds(expert_down_gemv_kernel<R, down_gemv_nb(R)>));
     MV_DOWN_ATTR(4) MV_DOWN_ATTR(8) MV_DOWN_ATTR(10) MV_DOWN_ATTR(12) MV_DOWN_ATTR(16)
 #undef MV_DOWN_ATTR
     return e;
+}
+
+template <int R>
+static void launch_down_gemv(const uint16_t *act, const int *idx, const float *tw,
+                             const uint16_t *wd, int M, int H, int I, int E, int k,
+                             float *out, hipStream_t st)
+{
+    const int grid = (H + R - 1) / R;
+    const size_t lds = down_gemv_lds_bytes(R, M * k, I);
+    hipLaunchKernelGGL((expert_down_gemv_kernel<R, down_gemv_nb(R)>), dim3(grid),
+                       dim3(kXThreads), lds, st, (const u32x4 *)act, idx, tw,
+                       (const u32x4 *)wd, M, H, I, E, k, out);
 }
 
 template <int R>
@@ -422,6 +604,16 @@ static moe_status_t ffn_enqueue(const uint16_t *x, const int32_t *topk_idx,
         return s;
 
     const int R = down_rows(H);
+    if (down_gemv_fits(R, M, k, I)) {
+        switch (R) {
+        case 4: launch_down_gemv<4>(act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
+        case 8: launch_down_gemv<8>(act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
+        case 10: launch_down_gemv<10>(act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
+        case 12: launch_down_gemv<12>(act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
+        default: launch_down_gemv<16>(act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
+        }
+        return check_launch();
+    }
     const int nbd = down_nb(R, M, k);
     switch (R) {
     case 4: launch_down_r<4>(nbd, act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
