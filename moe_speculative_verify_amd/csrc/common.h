@@ -182,137 +182,109 @@ __device__ __forceinline__ void lds_barrier()
 }
 
 // Expert grouping of the (token, slot) pairs, built in LDS by every
-// workgroup that needs it. This is the pair-axis form of the grouping the
-// post describes in section "Two fusions and a retune": each pair compares
-// itself with every other pair to find its rank inside its expert's bucket
-// and whether it heads the bucket; nothing scales with the expert count.
-// Buckets are ordered by expert id, pairs inside a bucket by pair index.
-// A bucket is then cut into column blocks of at most 16 pairs (one MFMA B
-// operand); with distinct experts per token a bucket never exceeds M <= 16
-// pairs, so this only matters for repeated ids within a token.
+// workgroup that needs it (the grouping step of the post's MoE chain,
+// section "PDL: the latency floor of stacked small kernels"): a histogram of
+// the pairs over the experts (LDS atomics), one packed prefix scan over the
+// experts that yields each bucket's offset, index and first column block
+// at once, and a scatter of the pair ids. Buckets are ordered by expert id;
+// the order of pairs inside a bucket is whatever the atomics produced,
+// which no result depends on (every pair's arithmetic is its own). A bucket
+// is cut into column blocks of at most 16 pairs (one MFMA B operand); with
+// distinct experts per token a bucket never exceeds M <= 16 pairs.
+constexpr int kGroupThreads = 256;               // workgroup size of every user
+constexpr int kBinsPerThread = kMaxE / kGroupThreads;
+
 struct Groups {
     int D;                       // distinct valid experts
     int DV;                      // column blocks
-    int wheads[16];              // per-wavefront counts of bucket heads
-    int pad_[14];
-    // int16 arrays, 16-byte aligned and padded to a multiple of 8 entries
-    // so that eight entries are read with one 128-bit LDS load
-    alignas(16) int16_t e[kMaxNP];      // expert of pair p, -1 if out of range
-    alignas(16) int16_t hd[kMaxNP];     // expert of pair p if it heads its bucket, else -1
-    alignas(16) int16_t sorted[kMaxNP]; // pair ids, bucket by bucket
-    alignas(16) int16_t dexp[kMaxNP];   // expert id of bucket d
-    alignas(16) int16_t doff[kMaxNP];   // bucket d starts at sorted[doff[d]]
-    alignas(16) int16_t dcnt[kMaxNP];   // pairs in bucket d
-    alignas(16) int16_t vexp[kMaxNP];   // expert of column block v
-    alignas(16) int16_t vbeg[kMaxNP];   // first index into sorted of block v
-    alignas(16) int16_t vcnt[kMaxNP];   // pairs in block v (1..16)
+    int wsum[kGroupThreads / kWave];   // per-wavefront totals of the scan
+    int bins[kMaxE];             // pairs per expert, then bucket offsets
+    int16_t e[kMaxNP];           // expert of pair p, -1 if out of range
+    int16_t slot[kMaxNP];        // position of pair p inside its bucket
+    int16_t sorted[kMaxNP];      // pair ids, bucket by bucket
+    int16_t vexp[kMaxNP];        // expert of column block v
+    int16_t vbeg[kMaxNP];        // first index into sorted of block v
+    int16_t vcnt[kMaxNP];        // pairs in block v (1..16)
 };
 
-// Eight consecutive int16 entries of an LDS array (index a multiple of 8).
-__device__ __forceinline__ void lds_load8(const int16_t *arr, int q0, int (&v)[8])
+// One step of an inclusive wavefront scan: add the value of lane
+// (lane - shift) in the same 16-lane row (row_shr), or the last lane of the
+// previous row(s) (row_bcast); lanes without a source add 0.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int scan_step(int v)
 {
-    const u32x4 w = *(const u32x4 *)(arr + q0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = (int)(int16_t)(w[i] & 0xFFFFu);
-        v[2 * i + 1] = (int)w[i] >> 16;
-    }
+    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xF, false);
 }
 
-// Every phase is parallel over pairs or buckets (the workgroup has at least
-// NP <= 256 threads) and reads the shared arrays eight entries at a time,
-// with no dependent LDS reads. Two steps, so that other prologue loads can
-// be issued in between: groups_set_pairs records this thread's pair (idx =
-// topk_idx[threadIdx.x], loaded by the caller; threads past NP pad the array
-// with -1), groups_finish builds the buckets (it starts with a barrier).
+// Two steps, so that other prologue loads can be issued in between:
+// groups_set_pairs records this thread's pair (idx = topk_idx[threadIdx.x],
+// loaded by the caller) and clears the histogram, groups_finish builds the
+// buckets (it starts with a barrier). Needs blockDim.x == kGroupThreads.
 __device__ inline void groups_set_pairs(int idx, int NP, int E, Groups &g)
 {
     const int p = threadIdx.x;
-    if (p < ((NP + 7) & ~7))
-        g.e[p] = (int16_t)((p < NP && idx >= 0 && idx < E) ? idx : -1);
+    if (p < NP)
+        g.e[p] = (int16_t)((idx >= 0 && idx < E) ? idx : -1);
+#pragma unroll
+    for (int i = 0; i < kBinsPerThread; ++i)
+        g.bins[i * kGroupThreads + p] = 0;
 }
 
 __device__ inline void groups_finish(int NP, Groups &g)
 {
     const int p = threadIdx.x;
-    const int NP8 = (NP + 7) & ~7;
+    const int lane = p & (kWave - 1), wave = p / kWave;
     lds_barrier();
-    // each pair against every other: its rank in (expert, pair) order, the
-    // pairs below its bucket and in it, and whether it heads the bucket
+    // histogram: each valid pair takes the next position in its bucket
     const int ep = p < NP ? g.e[p] : -1;
-    int below = 0, same = 0, rank = 0, head = 0;
-    if (ep >= 0) {
-        head = 1;
-        for (int q0 = 0; q0 < NP8; q0 += 8) {
-            int eq[8];
-            lds_load8(g.e, q0, eq);
+    if (ep >= 0)
+        g.slot[p] = (int16_t)atomicAdd(&g.bins[ep], 1);
+    lds_barrier();
+    // packed per-expert fields, summed by one exclusive scan over experts:
+    // bits 0-9 pairs (bucket offset), 10-19 non-empty buckets (bucket
+    // index), 20-29 column blocks (first block); every total is <= 256
+    int cnt[kBinsPerThread], pk[kBinsPerThread];
+    int tsum = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int q = q0 + i;
-                const bool ok = eq[i] >= 0;
-                const bool lt = ok && eq[i] < ep;
-                const bool eqe = ok && eq[i] == ep;
-                below += lt;
-                same += eqe;
-                rank += lt || (eqe && q < p);
-                head &= !(eqe && q < p);
-            }
-        }
-        g.sorted[rank] = (int16_t)p;
+    for (int i = 0; i < kBinsPerThread; ++i) {
+        cnt[i] = g.bins[p * kBinsPerThread + i];
+        pk[i] = cnt[i] | ((cnt[i] > 0) << 10) | (((cnt[i] + 15) >> 4) << 20);
+        tsum += pk[i];
     }
-    if (p < NP8)
-        g.hd[p] = (int16_t)(head ? ep : -1);
-    // bucket count without atomics: a ballot per wavefront, summed after
-    // the barrier
-    {
-        const unsigned long long hb = __ballot(head);
-        if ((threadIdx.x & (kWave - 1)) == 0)
-            g.wheads[threadIdx.x / kWave] = __popcll(hb);
+    int incl = tsum;
+    incl = scan_step<0x111, 0xF>(incl);          // row_shr:1
+    incl = scan_step<0x112, 0xF>(incl);          // row_shr:2
+    incl = scan_step<0x114, 0xF>(incl);          // row_shr:4
+    incl = scan_step<0x118, 0xF>(incl);          // row_shr:8
+    incl = scan_step<0x142, 0xA>(incl);          // row_bcast:15
+    incl = scan_step<0x143, 0xC>(incl);          // row_bcast:31
+    if (lane == kWave - 1)
+        g.wsum[wave] = incl;
+    lds_barrier();
+    int run = incl - tsum;
+    for (int w = 0; w < wave; ++w)
+        run += g.wsum[w];
+    if (p == kGroupThreads - 1) {
+        const int tot = run + tsum;
+        g.D = (tot >> 10) & 1023;
+        g.DV = tot >> 20;
+    }
+#pragma unroll
+    for (int i = 0; i < kBinsPerThread; ++i) {
+        const int off = run & 1023, v0 = run >> 20;
+        const int expert = p * kBinsPerThread + i;
+        g.bins[expert] = off;                     // bucket offset for the scatter
+        for (int o = 0; o < cnt[i]; o += 16) {
+            const int v = v0 + o / 16;
+            g.vexp[v] = (int16_t)expert;
+            g.vbeg[v] = (int16_t)(off + o);
+            g.vcnt[v] = (int16_t)(cnt[i] - o < 16 ? cnt[i] - o : 16);
+        }
+        run += pk[i];
     }
     lds_barrier();
-    int D = 0;
-    for (int w = 0; w < (int)(blockDim.x / kWave); ++w)
-        D += g.wheads[w];
-    // bucket index of each head = heads with a smaller expert id
-    if (head) {
-        int d = 0;
-        for (int q0 = 0; q0 < NP8; q0 += 8) {
-            int hq[8];
-            lds_load8(g.hd, q0, hq);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                d += hq[i] >= 0 && hq[i] < ep;
-        }
-        g.dexp[d] = (int16_t)ep;
-        g.doff[d] = (int16_t)below;
-        g.dcnt[d] = (int16_t)same;
-    }
-    lds_barrier();
-    if (p == 0)
-        g.D = D;
-    // column blocks of <= 16 pairs: bucket d's blocks start after the
-    // blocks of the buckets below it
-    if (p < D) {
-        int vstart = 0;
-        for (int q0 = 0; q0 < p; q0 += 8) {
-            int cq[8];
-            lds_load8(g.dcnt, q0, cq);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                vstart += q0 + i < p ? (cq[i] + 15) / 16 : 0;
-        }
-        const int n = g.dcnt[p];
-        for (int o = 0; o < n; o += 16) {
-            const int v = vstart + o / 16;
-            g.vexp[v] = g.dexp[p];
-            g.vbeg[v] = (int16_t)(g.doff[p] + o);
-            g.vcnt[v] = (int16_t)(n - o < 16 ? n - o : 16);
-        }
-        if (p == D - 1)
-            g.DV = vstart + (n + 15) / 16;
-    }
-    if (p == 0 && D == 0)
-        g.DV = 0;
+    if (ep >= 0)
+        g.sorted[g.bins[ep] + g.slot[p]] = (int16_t)p;
     lds_barrier();
 }
 

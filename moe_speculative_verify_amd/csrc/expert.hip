@@ -44,6 +44,7 @@ constexpr int kXGrid = 256;                         // one workgroup per CU
 constexpr int kXLdsDynMax = 160 * 1024 - 8 * 1024;  // static LDS stays below 8 KB
 
 static_assert(sizeof(Groups) + 64 <= 8 * 1024, "static LDS margin");
+static_assert(kXThreads == kGroupThreads, "grouping needs one thread per histogram slice");
 
 // A value read from LDS that is the same in every lane, moved to a scalar
 // register so that control flow and addresses built from it stay scalar.
@@ -81,18 +82,17 @@ __global__ __launch_bounds__(kXThreads) void expert_up_kernel(
     unsigned char *ring = smem + xbytes + wave * NB * kUpBlk;
     const int NP = M * k;
 
-    // prologue: pair ids first (their load retires before the staging
-    // loads are issued), then x into LDS while the buckets are built
+    // prologue: pair ids and buckets (nothing else in flight, so the LDS
+    // atomics need no wait), then x into LDS and the ring's first weight
+    // blocks, all direct-to-LDS and therefore retiring in program order
     groups_set_pairs((int)threadIdx.x < NP ? topk_idx[threadIdx.x] : -1, NP, E, g);
     wait_vmcnt<0>();                                     // only the pair id is in flight
     for (int i = threadIdx.x; i < M * (xs - nch); i += blockDim.x) {
         const int t = i / (xs - nch), c = nch + i % (xs - nch);
         s_x[t * xs + c] = u32x4{0, 0, 0, 0};             // K padding reads as zero
     }
-    stage_rows_lds(x, M, nch, s_x, xs);
     groups_finish(NP, g);
-    wait_vmcnt<0>();
-    __syncthreads();
+    stage_rows_lds(x, M, nch, s_x, xs);
 
     const int TI = (I + 15) / 16;
     const int nunits = uniform(g.DV) * TI;
@@ -100,8 +100,6 @@ __global__ __launch_bounds__(kXThreads) void expert_up_kernel(
     const int first = (int)blockIdx.x + G * wave;        // unit of local index 0
     const int nmine = nunits > first ? (nunits - 1 - first) / (kXWaves * G) + 1 : 0;
     const int nblk = nmine * nkb;
-    if (nblk == 0)
-        return;
     auto unit_of = [&](int i) { return first + kXWaves * G * i; };
 
     const int j = lane & 15, gq = lane >> 4;
@@ -116,7 +114,8 @@ __global__ __launch_bounds__(kXThreads) void expert_up_kernel(
         const int u = unit_of(Xr / nkb), kb = Xr % nkb;
         const int v = u / TI, i0 = (u % TI) * 16;
         unsigned char *slot = ring + (X % NB) * kUpBlk;
-        const size_t ebase = (size_t)uniform(g.vexp[v]) * I;
+        // a wavefront without units issues dummies only; v stays in range
+        const size_t ebase = (size_t)uniform(g.vexp[min(v, kMaxNP - 1)]) * I;
         int c = kb * (kUpKB / 8) + lcol;
         c = c < nch ? c : nch - 1;                       // K tail: x is zero there
 #pragma unroll
@@ -131,6 +130,8 @@ __global__ __launch_bounds__(kXThreads) void expert_up_kernel(
 #pragma unroll
     for (int q = 0; q < NB - 1; ++q)
         issue(q);
+    wait_vmcnt<(NB - 1) * kUpLd>();                      // this wave's share of x has landed
+    lds_barrier();                                       // ... and every other wave's
     f32x4 ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = ag;
     for (int X = 0; X < nblk; ++X) {
         issue(X + NB - 1);
