@@ -52,6 +52,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many steps (for rocprofv3), print nothing else")
+    ap.add_argument("--calib-mib", type=int, default=1024,
+                    help="profile mode: size of the int32 bitwise_not calibration kernel "
+                         "(reads and writes this many MiB)")
+    ap.add_argument("--write-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files "
+                         "(FETCH_SIZE run, WRITE_SIZE run) of the profile mode into "
+                         "profiles/lmhead_argmax_counters.json")
     return ap.parse_args()
 
 
@@ -61,6 +68,62 @@ def src_digest(*names: str) -> str:
         with open(os.path.join(ROOT, "moe_speculative_verify_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+CALIB_KERNEL = "bitwise_not"     # substring of the calibration kernel's name
+LM_KERNEL = "lmhead_kernel"
+
+
+def counter_means(path: str, counter: str) -> dict:
+    """Mean per-dispatch value of `counter` for the lm_head kernel and the
+    calibration kernel in one rocprofv3 counter_collection.csv."""
+    import csv
+    vals = {LM_KERNEL: [], CALIB_KERNEL: []}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            for key in vals:
+                if key in row.get("Kernel_Name", ""):
+                    vals[key].append(float(row["Counter_Value"]))
+    for key, v in vals.items():
+        if not v:
+            raise SystemExit(f"{path}: no {counter} rows for a kernel named *{key}*")
+    return {key: sum(v) / len(v) for key, v in vals.items()} | {
+        "dispatches": {key: len(v) for key, v in vals.items()}}
+
+
+def write_counters(fetch_csv: str, write_csv: str, calib_mib: int) -> None:
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of lmhead_argmax, each
+    scaled by what the same counter reads for the calibration kernel, which
+    reads and writes calib_mib MiB: HBM bytes = KiB * 1024 / factor."""
+    fe = counter_means(fetch_csv, "FETCH_SIZE")
+    wr = counter_means(write_csv, "WRITE_SIZE")
+    calib_bytes = calib_mib * 2**20
+    f_fac = fe[CALIB_KERNEL] * 1024 / calib_bytes
+    w_fac = wr[CALIB_KERNEL] * 1024 / calib_bytes
+    lm_read = fe[LM_KERNEL] * 1024 / f_fac
+    lm_write = wr[LM_KERNEL] * 1024 / w_fac
+    out = {
+        "kernel": "lmhead_argmax (lmhead_kernel), 157184x2560 bf16, M=6",
+        "source_digest": src_digest("lmhead.hip", "common.h"),
+        "fetch_kib_per_dispatch": round(fe[LM_KERNEL], 1),
+        "write_kib_per_dispatch": round(wr[LM_KERNEL], 3),
+        "calibration": {"kernel": f"torch int32 {CALIB_KERNEL}, {calib_mib} MiB in and out",
+                        "fetch_kib": round(fe[CALIB_KERNEL], 1),
+                        "write_kib": round(wr[CALIB_KERNEL], 1),
+                        "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4)},
+        "hbm_read_bytes_per_dispatch": int(lm_read),
+        "hbm_write_bytes_per_dispatch": int(lm_write),
+        "hbm_bytes_per_dispatch": int(lm_read + lm_write),
+        "dispatches": {"fetch_run": fe["dispatches"], "write_run": wr["dispatches"]},
+    }
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, "lmhead_argmax_counters.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def load_traffic(kernel: str, digest: str):
@@ -78,6 +141,9 @@ def load_traffic(kernel: str, digest: str):
 
 def main():
     args = parse()
+    if args.write_counters:
+        write_counters(args.write_counters[0], args.write_counters[1], args.calib_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is a design note, not built)", file=sys.stderr)
@@ -154,6 +220,17 @@ def main():
         check("lmhead_argmax", L.lmhead_argmax(*lm_args[s % len(lm_args)]))
 
     if args.profile_steps:
+        # calibration kernel of known traffic for the HBM counters: an int32
+        # bitwise_not that reads and writes calib_mib MiB, run cold twice
+        n = args.calib_mib * 2**20 // 4
+        src = torch.ones(n, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        flush = torch.empty(n, dtype=torch.int32, device=dev)
+        for _ in range(2):
+            flush.fill_(0)
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst, flush
         for s in range(args.profile_steps):
             step(s)
             check("moe_route", L.moe_route(*route_args[s % len(route_args)]))
@@ -178,35 +255,28 @@ def main():
                        + lm_bytes)
 
     # --------------------------------------------------------- timed steps
+    # HIP events on the launch stream bracket every call inside the timed
+    # region: per-call durations for the roofline come from the same run
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     t_start = time.perf_counter()
-    ev0.record()
-    for s in range(args.warmup, args.warmup + K):
-        step(s)
-    ev1.record()
+    for i, s in enumerate(range(args.warmup, args.warmup + K)):
+        evs[i][0].record()
+        check("moe_layer", L.moe_layer(*layer_args[s % nl]))
+        evs[i][1].record()
+        check("lmhead_argmax", L.lmhead_argmax(*lm_args[s % len(lm_args)]))
+        evs[i][2].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_start) * 1e3 / K
-    gpu_ms = ev0.elapsed_time(ev1) / K
+    gpu_ms = evs[0][0].elapsed_time(evs[K - 1][2]) / K
     log(f"{K} steps: {wall_ms * 1e3:.1f} us/step wall, {gpu_ms * 1e3:.1f} us/step events")
-
-    # ------------------ per-call durations, HIP events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    for s in range(K):
-        evs[s][0].record()
-        check("moe_layer", L.moe_layer(*layer_args[s % nl]))
-        evs[s][1].record()
-        check("lmhead_argmax", L.lmhead_argmax(*lm_args[s % len(lm_args)]))
-        evs[s][2].record()
-    torch.cuda.synchronize()
-    layer_us = [evs[s][0].elapsed_time(evs[s][1]) * 1e3 for s in range(K)]
-    lm_us = [evs[s][1].elapsed_time(evs[s][2]) * 1e3 for s in range(K)]
+    layer_us = [evs[i][0].elapsed_time(evs[i][1]) * 1e3 for i in range(K)]
+    lm_us = [evs[i][1].elapsed_time(evs[i][2]) * 1e3 for i in range(K)]
     layer_us_mean = sum(layer_us) / K
     lm_us_mean = sum(lm_us) / K
-    layer_bytes_mean = sum(layer_bytes[s % nl] for s in range(K)) / K
+    layer_bytes_mean = sum(layer_bytes[s % nl] for s in range(args.warmup, args.warmup + K)) / K
 
     # gate only: router GEMV + top-k over rotating router copies
     R = len(route_args)
@@ -264,7 +334,7 @@ def main():
         log(f"cpu oracle: {cpu_s * 1e3:.0f} ms/step on {cores} threads")
 
     res = {
-        "metric": "cold-weight HBM GB/s (% of peak) + us per MoE-layer verify step, M=6",
+        "metric": "cold-weight HBM GB/s (% of peak) + \u00b5s per MoE-layer verify step, M=6",
         "value": round(step_bytes_mean / (wall_ms * 1e-3) / 1e9, 1),
         "unit": "GB/s",
         "n_gpus": 1,
