@@ -31,14 +31,15 @@
  *     launch itself (MOE_ERR_LAUNCH).
  *   - Pointers to bf16/fp32 tensors must be 16-byte aligned (128-bit
  *     loads). Shape limits: 1 <= M <= 16, 1 <= k <= min(E, 16),
- *     1 <= E <= 1024, H and I multiples of 8 and at most 16384,
+ *     1 <= E <= 1024, H and I multiples of 8 and at most 8192,
  *     1 <= V < 2^31.
  *   - Workspaces: size from the matching *_workspace_bytes query,
  *     16-byte aligned, ZERO-FILLED before their first use (one
- *     moe_workspace_clear call, or any zero fill). Every call leaves the
- *     counters it uses at zero again, so a workspace is reused without
- *     clearing. Two calls that may run concurrently must not share a
- *     workspace.
+ *     moe_workspace_clear call, or any zero fill). The first 256 bytes of
+ *     every workspace are a header whose counters (an arrival ticket) sit
+ *     at fixed offsets; every call leaves them at zero again, so one
+ *     workspace is reused by every entry point and shape without clearing.
+ *     Two calls that may run concurrently must not share a workspace.
  *   - Results are deterministic: no floating-point atomics; rerunning a
  *     call on the same inputs gives bitwise-equal outputs, and a token's
  *     results do not depend on the other tokens in the call.

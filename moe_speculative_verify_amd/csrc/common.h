@@ -133,31 +133,6 @@ __device__ __forceinline__ float f32_unorder(uint32_t u)
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
-// Maximum / minimum of a uint32 over the wavefront, returned uniform: DPP
-// steps inside each 16-lane row, the rows combined with row broadcasts
-// (row_bcast:15 into rows 1 and 3, then row_bcast:31 into rows 2 and 3), and
-// lane 63, which has seen every lane, read back. Rows a broadcast leaves out
-// receive the operation's identity, so they keep their own value (and the
-// move folds into a DPP max/min). Branch-free.
-template <int CTRL, int ROWMASK, bool MAX>
-__device__ __forceinline__ uint32_t u32_dpp_step(uint32_t v)
-{
-    const int ident = MAX ? 0 : -1;
-    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(ident, (int)v, CTRL, ROWMASK, 0xF, false);
-    return MAX ? (o > v ? o : v) : (o < v ? o : v);
-}
-template <bool MAX>
-__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v)
-{
-    v = u32_dpp_step<0xB1, 0xF, MAX>(v);    // quad_perm [1,0,3,2]
-    v = u32_dpp_step<0x4E, 0xF, MAX>(v);    // quad_perm [2,3,0,1]
-    v = u32_dpp_step<0x141, 0xF, MAX>(v);   // row_half_mirror
-    v = u32_dpp_step<0x140, 0xF, MAX>(v);   // row_mirror: row extreme everywhere
-    v = u32_dpp_step<0x142, 0xA, MAX>(v);   // row_bcast:15
-    v = u32_dpp_step<0x143, 0xC, MAX>(v);   // row_bcast:31
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
 // fp32 -> bf16 bits, round to nearest, ties to even (NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
 {
@@ -318,8 +293,8 @@ __device__ inline void stage_rows_lds(const u32x4 *__restrict__ src, int nrows, 
 
 // Every workspace layout starts with the same 256-byte header whose first
 // word is the arrival ticket of the last-workgroup pattern; the ticket is zero
-// when a call starts and when it ends, so one workspace can serve every entry
-// point and shape in turn.
+// when a call starts and when it ends, and it sits at the same offset for
+// every entry point and shape, so one workspace serves them all in turn.
 constexpr size_t kWsHeader = 256;
 
 // Dynamic LDS a kernel may request: 160 KB per CU on gfx950, less a margin

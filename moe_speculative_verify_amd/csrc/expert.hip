@@ -457,6 +457,146 @@ __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
     }
 }
 
+// ------------------------------------------------------------ up (GEMV)
+// The up projection at verify widths is a set of matrix-vector products as
+// well: a selected expert serves about one pair. Units are (column block v,
+// row i of I): the unit's gate row and up row, KC chunks of 16 bytes per
+// lane each (lane l takes chunks l, l+64, ...: 1 KB contiguous per load),
+// stream straight into registers through an NB-deep register ring; x sits in
+// LDS, staged once per workgroup. For every pair of the column block each
+// lane forms its gate and up partial dot products (v_dot2_f32_bf16), two
+// fixed DPP trees sum them over the wavefront, and the SwiGLU product is
+// taken in fp32 and rounded once to bf16. With more than KC * 64 chunks per
+// row a unit spans several K blocks; the per-block sums of each pair are
+// added in LDS in block order.
+template <int KC, int NB>
+__global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
+    const u32x4 *__restrict__ x, const int *__restrict__ topk_idx,
+    const u32x4 *__restrict__ wg, const u32x4 *__restrict__ wu, int M, int H,
+    int I, int E, int k, uint16_t *__restrict__ act)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ Groups g;
+    __shared__ float s_acc[kXWaves][16][2];      // per-pair running sums
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int nch = H / 8;                               // 16-byte chunks per row
+    const int nbu = (nch + KC * kWave - 1) / (KC * kWave);   // K blocks per unit
+    const int xs = nbu * KC * kWave;                     // LDS x row, chunks
+    const int NP = M * k;
+    u32x4 *s_x = (u32x4 *)smem;                          // [M][xs]
+
+    groups_set_pairs((int)threadIdx.x < NP ? topk_idx[threadIdx.x] : -1, NP, E, g);
+    wait_vmcnt<0>();                                     // only the pair id is in flight
+    for (int i = threadIdx.x; i < M * (xs - nch); i += blockDim.x) {
+        const int t = i / (xs - nch), c = nch + i % (xs - nch);
+        s_x[t * xs + c] = u32x4{0, 0, 0, 0};             // K padding reads as zero
+    }
+    groups_finish(NP, g);
+
+    // ---- unit u runs on wavefront u mod (4 * gridDim.x), so every
+    // wavefront sees every column block and a heavily shared expert's cost
+    // spreads evenly; block X of this wavefront carries the tag
+    // unit * 16 + kb, or -1 past its last block
+    const int nunits = uniform(g.DV) * I;
+    const int GW = gridDim.x * kXWaves;
+    const int gw = blockIdx.x * kXWaves + wave;
+    const int nmine = nunits > gw ? (nunits - 1 - gw) / GW + 1 : 0;
+    const int nblk = nmine * nbu;
+    auto tag_of = [&](int X) {
+        return X < nblk ? (gw + GW * (X / nbu)) * 16 + X % nbu : -1;
+    };
+
+    // Block of a tag: KC loads of the gate row, KC of the up row. A -1 tag
+    // rereads the first kilobyte of W_gate instead, so every wait is one
+    // constant.
+    auto issue = [&](int tag, u32x4 (&dg)[KC], u32x4 (&du)[KC]) {
+        const bool real = tag >= 0;
+        const int u = real ? tag >> 4 : 0, kb = real ? tag & 15 : 0;
+        const int v = min(u / I, kMaxNP - 1), i = u % I;
+        const size_t roff = ((size_t)uniform(g.vexp[v]) * I + i) * nch;
+        const u32x4 *bg = wg + (real ? roff : 0);        // uniform
+        const u32x4 *bu = wu + (real ? roff : 0);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            int ch = (kb * KC + c) * kWave + lane;
+            ch = ch < nch ? ch : nch - 1;                // K tail: zeroed before use
+            int off = real ? ch : min(lane, nch - 1);
+            asm volatile("" : "+v"(off));                // one load on one path: no branch
+            dg[c] = load_stream(bg + off);
+            du[c] = load_stream(bu + off);
+        }
+    };
+    auto consume = [&](int tag, u32x4 (&dg)[KC], u32x4 (&du)[KC]) {
+        const int u = tag >> 4, kb = tag & 15;
+        const int v = u / I, i = u % I;
+        const int npair = uniform(g.vcnt[v]);
+        const int pb = uniform(g.vbeg[v]);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            if ((kb * KC + c) * kWave + kWave > nch) {   // uniform: the K tail
+                const bool ok = (kb * KC + c) * kWave + lane < nch;
+                dg[c] = ok ? dg[c] : u32x4{0, 0, 0, 0};
+                du[c] = ok ? du[c] : u32x4{0, 0, 0, 0};
+            }
+        }
+        for (int jj = 0; jj < npair; ++jj) {
+            const int p = uniform(g.sorted[pb + jj]);
+            const u32x4 *xr = s_x + (p / k) * xs + kb * KC * kWave + lane;
+            float ga = 0.0f, ua = 0.0f;
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                const u32x4 xv = xr[c * kWave];
+                ga = dot8_bf16(dg[c], xv, ga);
+                ua = dot8_bf16(du[c], xv, ua);
+            }
+            float gt = wave_total(ga), ut = wave_total(ua);
+            if (nbu > 1) {                               // uniform
+                if (kb > 0) {
+                    gt = s_acc[wave][jj][0] + gt;
+                    ut = s_acc[wave][jj][1] + ut;
+                }
+                if (kb < nbu - 1) {
+                    if (lane == 0) {
+                        s_acc[wave][jj][0] = gt;
+                        s_acc[wave][jj][1] = ut;
+                    }
+                    continue;
+                }
+            }
+            // SwiGLU in fp32, one rounding to bf16
+            if (lane == 0)
+                act[(size_t)p * I + i] = (uint16_t)f32_to_bf16_rne(gt / (1.0f + expf(-gt)) * ut);
+        }
+    };
+
+    u32x4 wgr[NB][KC], wur[NB][KC];
+#pragma unroll
+    for (int q = 0; q < NB - 1; ++q)
+        issue(tag_of(q), wgr[q], wur[q]);
+    stage_rows_lds(x, M, nch, s_x, xs);
+    wait_vmcnt<0>();                                     // this wave's share of x has landed
+    lds_barrier();                                       // ... and every other wave's
+    for (int X0 = 0; X0 < nblk; X0 += NB) {
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const int nq = (q + NB - 1) % NB;
+            issue(tag_of(X0 + q + NB - 1), wgr[nq], wur[nq]);
+            wait_vmcnt<(NB - 1) * 2 * KC>();             // block X0 + q has landed
+            if (X0 + q < nblk)
+                consume(tag_of(X0 + q), wgr[q], wur[q]);
+        }
+    }
+    wait_vmcnt<0>();                                     // dummy loads have landed
+}
+
+__host__ __device__ inline size_t up_gemv_lds_bytes(int M, int H, int KC)
+{
+    const int nch = H / 8;
+    const int nbu = (nch + KC * kWave - 1) / (KC * kWave);
+    return align_up((size_t)M * nbu * KC * kWave * 16, 256);
+}
+
 // ------------------------------------------------------------------ host
 
 static size_t up_lds_bytes(int M, int H, int nb)
@@ -465,6 +605,29 @@ static size_t up_lds_bytes(int M, int H, int nb)
     return align_up((size_t)M * (nkb * (kUpKB / 8) + 1) * 16, 256) +
            (size_t)kXWaves * nb * kUpBlk;
 }
+// GEMV up kernel: KC 16-byte chunks per lane per row and block (a unit is
+// one block when a row has at most 5 * 64 chunks), a 4-deep register ring
+constexpr int kUpGemvNB = 4;
+static int up_gemv_kc(int H)
+{
+    const int need = (H / 8 + kWave - 1) / kWave;
+    return need <= 5 ? need : 4;
+}
+static bool up_gemv_fits(int M, int H)
+{
+    return up_gemv_lds_bytes(M, H, up_gemv_kc(H)) <= (size_t)kXLdsDynMax;
+}
+
+template <int KC>
+static void launch_up_gemv(const uint16_t *x, const int *idx, const uint16_t *wg,
+                           const uint16_t *wu, int M, int H, int I, int E, int k,
+                           uint16_t *act, hipStream_t st)
+{
+    hipLaunchKernelGGL((expert_up_gemv_kernel<KC, kUpGemvNB>), dim3(kXGrid), dim3(kXThreads),
+                       up_gemv_lds_bytes(M, H, KC), st, (const u32x4 *)x, idx,
+                       (const u32x4 *)wg, (const u32x4 *)wu, M, H, I, E, k, act);
+}
+
 static int up_nb(int M, int H)
 {
     for (int nb = 3; nb >= 2; --nb)
@@ -543,6 +706,11 @@ static hipError_t set_lds_attributes()
     auto chk = [&](hipError_t r) { if (r != hipSuccess) e = r; };
     chk(allow_lds(expert_up_kernel<2>));
     chk(allow_lds(expert_up_kernel<3>));
+    chk(allow_lds(expert_up_gemv_kernel<1, kUpGemvNB>));
+    chk(allow_lds(expert_up_gemv_kernel<2, kUpGemvNB>));
+    chk(allow_lds(expert_up_gemv_kernel<3, kUpGemvNB>));
+    chk(allow_lds(expert_up_gemv_kernel<4, kUpGemvNB>));
+    chk(allow_lds(expert_up_gemv_kernel<5, kUpGemvNB>));
 #define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, 2>)); chk(allow_lds(expert_down_kernel<R, 3>)); \
     chk(allow_lds(expert_down_gemv_kernel<R, down_gemv_nb(R)>));
     MV_DOWN_ATTR(4) MV_DOWN_ATTR(8) MV_DOWN_ATTR(10) MV_DOWN_ATTR(12) MV_DOWN_ATTR(16)
@@ -581,18 +749,28 @@ static moe_status_t ffn_enqueue(const uint16_t *x, const int32_t *topk_idx,
                                 const float *topk_w, const uint16_t *w_gate,
                                 const uint16_t *w_up, const uint16_t *w_down,
                                 int32_t M, int32_t H, int32_t I, int32_t E,
-                                int32_t k, float *out, void *ws, hipStream_t st)
+                                int32_t k, float *out, void *data, hipStream_t st)
 {
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] { attr = set_lds_attributes(); });
     if (attr != hipSuccess)
         return MOE_ERR_LAUNCH;
-    uint16_t *act = (uint16_t *)((char *)ws + kWsHeader);
+    // the activations live in the data part, wherever the caller's layout
+    // puts it
+    uint16_t *act = (uint16_t *)data;
 
     const int nbu = up_nb(M, H);
     const size_t ulds = up_lds_bytes(M, H, nbu);
-    if (nbu == 3)
+    if (up_gemv_fits(M, H)) {
+        switch (up_gemv_kc(H)) {
+        case 1: launch_up_gemv<1>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
+        case 2: launch_up_gemv<2>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
+        case 3: launch_up_gemv<3>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
+        case 4: launch_up_gemv<4>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
+        default: launch_up_gemv<5>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
+        }
+    } else if (nbu == 3)
         hipLaunchKernelGGL(expert_up_kernel<3>, dim3(kXGrid), dim3(kXThreads), ulds, st,
                            (const u32x4 *)x, topk_idx, (const u32x4 *)w_gate,
                            (const u32x4 *)w_up, M, H, I, E, k, act);
@@ -666,7 +844,7 @@ extern "C" moe_status_t moe_expert_ffn(const uint16_t *x, const int32_t *topk_id
     if (workspace_bytes < moe_expert_ffn_workspace_bytes(M, H, I, E, k))
         return MOE_ERR_WORKSPACE;
     return ffn_enqueue(x, topk_idx, topk_w, w_gate, w_up, w_down, M, H, I, E, k,
-                       out, workspace, (hipStream_t)stream);
+                       out, (char *)workspace + kWsHeader, (hipStream_t)stream);
 }
 
 extern "C" size_t moe_layer_workspace_bytes(int32_t M, int32_t H, int32_t I,
@@ -701,8 +879,8 @@ extern "C" moe_status_t moe_layer(const uint16_t *x, const uint16_t *w_router,
         return MOE_ERR_ALIGN;
     if (workspace_bytes < moe_layer_workspace_bytes(M, H, I, E, k))
         return MOE_ERR_WORKSPACE;
-    // the FFN's data part starts where the route's ends; its header slot
-    // overlaps the route's logits, which the FFN never reads
+    // the FFN's data part starts where the route's ends; both share the
+    // header at the start of the workspace
     const size_t r = moe_route_workspace_bytes(M, E);
     hipStream_t st = (hipStream_t)stream;
     s = route_enqueue(x, w_router, bias, M, H, E, k, topk_idx, topk_w, nullptr,
@@ -710,5 +888,5 @@ extern "C" moe_status_t moe_layer(const uint16_t *x, const uint16_t *w_router,
     if (s != MOE_OK)
         return s;
     return ffn_enqueue(x, topk_idx, topk_w, w_gate, w_up, w_down, M, H, I, E, k,
-                       out, (char *)workspace + r - kWsHeader, st);
+                       out, (char *)workspace + r, st);
 }

@@ -350,3 +350,30 @@ def test_workspace_reuse_across_shapes():
         wl = synth.normal_bf16((V, 256), 0.02, 5, V)
         am, ml = _lm_gpu(h, wl)
         _compare_lm(am, ml, h, wl, oracle.lmhead(h, wl))
+
+
+def test_layer_workspace_shared_across_M(full_layer):
+    """One workspace serves moe_layer at M = 6, 1, 16, 6 in turn, with
+    moe_expert_ffn calls in between: every result equals the same call on a
+    fresh zero-filled workspace, and the 256-byte header of counters is
+    zero after every call (the header sits at fixed offsets for every
+    shape)."""
+    say("workspace shared across M")
+    k, H, I, E = 8, 2560, 1024, 512
+    nbytes = max(mv.moe_layer_workspace_bytes(M, H, I, E, k) for M in (1, 6, 16))
+    shared = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    fw = full_layer
+    for i, M in enumerate((6, 1, 16, 6)):
+        x = to_dev(synth.activations(M, H, seed=1000 + i))
+        fresh = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        a = mv.moe_layer(x, fw["router"], fw["gate"], fw["up"], fw["down"], k, workspace=fresh)
+        b = mv.moe_layer(x, fw["router"], fw["gate"], fw["up"], fw["down"], k, workspace=shared)
+        torch.cuda.synchronize()
+        for ta, tb in zip(a, b):
+            assert torch.equal(ta, tb), (M, "layer")
+        assert int(shared[:256].count_nonzero()) == 0, (M, "header after moe_layer")
+        # the FFN alone on the same workspace, routed by the layer's ids
+        c = mv.moe_expert_ffn(x, a[0], a[1], fw["gate"], fw["up"], fw["down"], workspace=shared)
+        torch.cuda.synchronize()
+        assert torch.equal(c, a[2]), (M, "ffn")
+        assert int(shared[:256].count_nonzero()) == 0, (M, "header after moe_expert_ffn")
