@@ -8,27 +8,29 @@
 // SwiGLU product is computed in fp32 inside the up projection and rounded
 // once, and the combine is a single fp32 weighted sum per output.
 //
-// Work is cut into units = (column block v of <= 16 pairs sharing one
-// expert, 16-row tile of the weight matrix). Workgroup b owns a contiguous
-// run of units; its four wavefronts split the reduction axis K of every
-// unit, each streaming its K range of the tile's 16 rows straight from HBM
-// into a private LDS double buffer (non-temporal 128-bit direct-to-LDS
-// loads, 1 KB per instruction, the next block always in flight, across unit
-// boundaries too). The dot products run on the matrix cores
-// (v_mfma_f32_16x16x32_bf16: A = 16 weight rows, B = the block's <= 16
-// activation columns). The four partial tiles are summed through LDS in a
-// fixed order, so results are bitwise reproducible and every pair's result
-// depends only on its own token.
+// At verify widths (M <= 16 tokens, top-k of 512 experts) a selected expert
+// serves about one (token, slot) pair, so both projections are streamed as
+// matrix-vector products: the weights go straight from HBM into registers
+// (128-bit non-temporal loads, 1 KB contiguous per instruction, a register
+// ring of several blocks in flight per wavefront), the tokens' vectors sit
+// in LDS, and every lane forms eight-element dot products
+// (v_dot2_f32_bf16) that fixed DPP trees sum over the wavefront. No
+// floating-point atomics: results are bitwise reproducible and every pair's
+// result depends only on its own token.
 //
-//   up       A = W_gate and W_up rows (two MFMAs share each B fragment),
-//            B = x of the pairs' tokens (staged once per workgroup in LDS);
+//   up       unit = (expert, row i of I): gate row and up row of the unit;
 //            epilogue a = bf16(silu(g) * u) in fp32, one rounding.
-//   down     A = W_down rows, B = the pairs' activations a (L2-resident,
-//            fetched with the same direct-to-LDS loads);
-//            epilogue y[pair, rows] = W_down a in fp32.
-//   combine  out[t, r] = sum_j w[t,j] * y[(t,j), r], slots in order, fp32.
-// Every workgroup rebuilds the pair grouping in LDS from topk_idx, which
-// costs less than a separate launch.
+//   down     workgroup b owns R rows of W_down of every selected expert;
+//            block sums y[pair, rows] in LDS.
+//   combine  out[t, r] = sum_j w[t,j] * y[(t,j), r], slots in order, fp32,
+//            at the end of the down kernel.
+// When the pairs' activations do not fit in LDS (M*k*I*2 bytes beyond about
+// 150 KB, i.e. M >= 10 at I = 1024, k = 8) the down projection runs as the
+// MFMA kernel below instead: v_mfma_f32_16x16x32_bf16 with A = 16 rows of
+// W_down from a direct-to-LDS ring and B = the pairs' activations read from
+// L2; its summation order differs, so batch invariance holds within each of
+// the two regimes. Every workgroup rebuilds the pair grouping in LDS from
+// topk_idx, which costs less than a separate launch.
 #include "common.h"
 
 #include <mutex>
@@ -50,135 +52,6 @@ static_assert(kXThreads == kGroupThreads, "grouping needs one thread per histogr
 // register so that control flow and addresses built from it stay scalar.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-
-// ------------------------------------------------------------------- up
-// Units = (column block v, 16-row tile of the expert's I rows). Unit u runs
-// on workgroup u % G, wavefront (u / G) % 4, so every CU gets work even at
-// M = 1. A wavefront streams each of its units over the full K = H in
-// blocks of KB = 128 (16 gate rows and 16 up rows, 256 B each: 8 loads of
-// 4 rows x 256 B) through an NB-deep ring; x is staged once per workgroup.
-constexpr int kUpKB = 128;
-constexpr int kUpPitch = kUpKB * 2 + 16;             // LDS bytes per row (padded)
-constexpr int kUpMat = 16 * kUpPitch;                // one matrix, 16 rows
-constexpr int kUpBlk = 2 * kUpMat;                   // gate + up
-constexpr int kUpLd = 8;                             // loads per block
-constexpr int kUpSteps = kUpKB / 32;
-
-template <int NB>
-__global__ __launch_bounds__(kXThreads) void expert_up_kernel(
-    const u32x4 *__restrict__ x, const int *__restrict__ topk_idx,
-    const u32x4 *__restrict__ wg, const u32x4 *__restrict__ wu, int M, int H,
-    int I, int E, int k, uint16_t *__restrict__ act)
-{
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    __shared__ Groups g;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = uniform(threadIdx.x / kWave);
-    const int nch = H / 8;
-    const int nkb = (H + kUpKB - 1) / kUpKB;
-    const int xs = nkb * (kUpKB / 8) + 1;                // padded x row, chunks
-    const size_t xbytes = align_up((size_t)M * xs * 16, 256);
-    u32x4 *s_x = (u32x4 *)smem;
-    unsigned char *ring = smem + xbytes + wave * NB * kUpBlk;
-    const int NP = M * k;
-
-    // prologue: pair ids and buckets (nothing else in flight, so the LDS
-    // atomics need no wait), then x into LDS and the ring's first weight
-    // blocks, all direct-to-LDS and therefore retiring in program order
-    groups_set_pairs((int)threadIdx.x < NP ? topk_idx[threadIdx.x] : -1, NP, E, g);
-    wait_vmcnt<0>();                                     // only the pair id is in flight
-    for (int i = threadIdx.x; i < M * (xs - nch); i += blockDim.x) {
-        const int t = i / (xs - nch), c = nch + i % (xs - nch);
-        s_x[t * xs + c] = u32x4{0, 0, 0, 0};             // K padding reads as zero
-    }
-    groups_finish(NP, g);
-    stage_rows_lds(x, M, nch, s_x, xs);
-
-    const int TI = (I + 15) / 16;
-    const int nunits = uniform(g.DV) * TI;
-    const int G = gridDim.x;
-    const int first = (int)blockIdx.x + G * wave;        // unit of local index 0
-    const int nmine = nunits > first ? (nunits - 1 - first) / (kXWaves * G) + 1 : 0;
-    const int nblk = nmine * nkb;
-    auto unit_of = [&](int i) { return first + kXWaves * G * i; };
-
-    const int j = lane & 15, gq = lane >> 4;
-    const int lrow = lane >> 4, lcol = lane & 15;        // 4 rows x 16 chunks per load
-    // Past the end of the sequence the same number of loads reads a cached
-    // dummy into a slot nobody reads, so every iteration waits on one
-    // constant count.
-    const u32x4 *dummy = x + min(lane, M * nch - 1);
-    auto issue = [&](int X) {
-        const bool real = X < nblk;
-        const int Xr = real ? X : 0;
-        const int u = unit_of(Xr / nkb), kb = Xr % nkb;
-        const int v = u / TI, i0 = (u % TI) * 16;
-        unsigned char *slot = ring + (X % NB) * kUpBlk;
-        // a wavefront without units issues dummies only; v stays in range
-        const size_t ebase = (size_t)uniform(g.vexp[min(v, kMaxNP - 1)]) * I;
-        int c = kb * (kUpKB / 8) + lcol;
-        c = c < nch ? c : nch - 1;                       // K tail: x is zero there
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int row = min(i0 + 4 * q + lrow, I - 1);   // tail rows: unused
-            load_lds16(real ? wg + (ebase + row) * nch + c : dummy, slot + q * 4 * kUpPitch);
-            load_lds16(real ? wu + (ebase + row) * nch + c : dummy,
-                       slot + kUpMat + q * 4 * kUpPitch);
-        }
-    };
-
-#pragma unroll
-    for (int q = 0; q < NB - 1; ++q)
-        issue(q);
-    wait_vmcnt<(NB - 1) * kUpLd>();                      // this wave's share of x has landed
-    lds_barrier();                                       // ... and every other wave's
-    f32x4 ag = {0.0f, 0.0f, 0.0f, 0.0f}, au = ag;
-    for (int X = 0; X < nblk; ++X) {
-        issue(X + NB - 1);
-        wait_vmcnt<(NB - 1) * kUpLd>();                  // block X has landed
-        const int u = unit_of(X / nkb), kb = X % nkb;
-        const int v = u / TI;
-        const int npair = uniform(g.vcnt[v]);
-        const bool col_ok = j < npair;
-        const int p = col_ok ? g.sorted[uniform(g.vbeg[v]) + j] : 0;
-        const u32x4 *xrow = s_x + (p / k) * xs + kb * (kUpKB / 8) + gq;
-        // A row j of the tile sits in load j / 4 at position j % 4
-        const unsigned char *sa = ring + (X % NB) * kUpBlk + (j >> 2) * 4 * kUpPitch +
-                                  (j & 3) * (kUpKB * 2) + gq * 16;
-#pragma unroll
-        for (int s = 0; s < kUpSteps; ++s) {
-            u32x4 xv = xrow[4 * s];
-            if (!col_ok)
-                xv = u32x4{0, 0, 0, 0};
-            ag = mfma_bf16(*(const MV_LDS u32x4 *)(sa + s * 64), xv, ag);
-            au = mfma_bf16(*(const MV_LDS u32x4 *)(sa + kUpMat + s * 64), xv, au);
-        }
-        if (kb == nkb - 1) {
-            // lane (j, gq) holds rows 4gq .. 4gq+3 of the tile for column j:
-            // SwiGLU in fp32, one rounding to bf16
-            if (col_ok) {
-                const int row0 = (u % TI) * 16 + 4 * gq;
-                uint32_t h[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float gv = ag[r];
-                    h[r] = f32_to_bf16_rne(gv / (1.0f + expf(-gv)) * au[r]);
-                }
-                uint16_t *dst = act + (size_t)p * I + row0;
-                if (row0 + 3 < I) {
-                    *(uint2 *)dst = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-                } else {
-                    for (int r = 0; r < 4; ++r)
-                        if (row0 + r < I)
-                            dst[r] = (uint16_t)h[r];
-                }
-            }
-            ag = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            au = ag;
-        }
-    }
-    wait_vmcnt<0>();                                     // dummy loads have landed
-}
 
 // ----------------------------------------------------------------- down
 // Workgroup b owns R output rows r0 .. r0+R-1 for every expert; its
@@ -599,12 +472,6 @@ __host__ __device__ inline size_t up_gemv_lds_bytes(int M, int H, int KC)
 
 // ------------------------------------------------------------------ host
 
-static size_t up_lds_bytes(int M, int H, int nb)
-{
-    const int nkb = (H + kUpKB - 1) / kUpKB;
-    return align_up((size_t)M * (nkb * (kUpKB / 8) + 1) * 16, 256) +
-           (size_t)kXWaves * nb * kUpBlk;
-}
 // GEMV up kernel: KC 16-byte chunks per lane per row and block (a unit is
 // one block when a row has at most 5 * 64 chunks), a 4-deep register ring
 constexpr int kUpGemvNB = 4;
@@ -628,13 +495,6 @@ static void launch_up_gemv(const uint16_t *x, const int *idx, const uint16_t *wg
                        (const u32x4 *)wg, (const u32x4 *)wu, M, H, I, E, k, act);
 }
 
-static int up_nb(int M, int H)
-{
-    for (int nb = 3; nb >= 2; --nb)
-        if (up_lds_bytes(M, H, nb) <= (size_t)kXLdsDynMax)
-            return nb;
-    return 0;                                            // does not fit
-}
 // rows per down workgroup: at least ceil(H / 256), from the instantiated set
 static int down_rows(int H)
 {
@@ -683,7 +543,7 @@ static moe_status_t ffn_check(const uint16_t *x, const int32_t *topk_idx,
         return s;
     if (I < 1)
         return MOE_ERR_SHAPE;
-    if (I % 8 != 0 || I > kMaxDim || up_nb(M, H) == 0 || down_rows(H) == 0 ||
+    if (I % 8 != 0 || I > kMaxDim || !up_gemv_fits(M, H) || down_rows(H) == 0 ||
         down_nb(down_rows(H), M, k) == 0)
         return MOE_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) ||
@@ -704,8 +564,6 @@ static hipError_t set_lds_attributes()
 {
     hipError_t e = hipSuccess;
     auto chk = [&](hipError_t r) { if (r != hipSuccess) e = r; };
-    chk(allow_lds(expert_up_kernel<2>));
-    chk(allow_lds(expert_up_kernel<3>));
     chk(allow_lds(expert_up_gemv_kernel<1, kUpGemvNB>));
     chk(allow_lds(expert_up_gemv_kernel<2, kUpGemvNB>));
     chk(allow_lds(expert_up_gemv_kernel<3, kUpGemvNB>));
@@ -760,24 +618,13 @@ static moe_status_t ffn_enqueue(const uint16_t *x, const int32_t *topk_idx,
     // puts it
     uint16_t *act = (uint16_t *)data;
 
-    const int nbu = up_nb(M, H);
-    const size_t ulds = up_lds_bytes(M, H, nbu);
-    if (up_gemv_fits(M, H)) {
-        switch (up_gemv_kc(H)) {
-        case 1: launch_up_gemv<1>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
-        case 2: launch_up_gemv<2>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
-        case 3: launch_up_gemv<3>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
-        case 4: launch_up_gemv<4>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
-        default: launch_up_gemv<5>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
-        }
-    } else if (nbu == 3)
-        hipLaunchKernelGGL(expert_up_kernel<3>, dim3(kXGrid), dim3(kXThreads), ulds, st,
-                           (const u32x4 *)x, topk_idx, (const u32x4 *)w_gate,
-                           (const u32x4 *)w_up, M, H, I, E, k, act);
-    else
-        hipLaunchKernelGGL(expert_up_kernel<2>, dim3(kXGrid), dim3(kXThreads), ulds, st,
-                           (const u32x4 *)x, topk_idx, (const u32x4 *)w_gate,
-                           (const u32x4 *)w_up, M, H, I, E, k, act);
+    switch (up_gemv_kc(H)) {
+    case 1: launch_up_gemv<1>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
+    case 2: launch_up_gemv<2>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
+    case 3: launch_up_gemv<3>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
+    case 4: launch_up_gemv<4>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
+    default: launch_up_gemv<5>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
+    }
     moe_status_t s = check_launch();
     if (s != MOE_OK)
         return s;
