@@ -292,6 +292,61 @@ def main():
     torch.cuda.synchronize()
     route_us = re0.elapsed_time(re1) * 1e3 / R
 
+    # gate coldness: the same calls cycling over fewer distinct copies (the
+    # time rises to a plateau once the copies no longer fit the caches)
+    gate_sweep = {}
+    for n in (8, 32, R):
+        for s in range(n):
+            check("moe_route", L.moe_route(*route_args[s]))
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for s in range(2 * R):
+            check("moe_route", L.moe_route(*route_args[s % n]))
+        g1.record()
+        torch.cuda.synchronize()
+        gate_sweep[str(n)] = round(g0.elapsed_time(g1) * 1e3 / (2 * R), 2)
+
+    # layer step at the other verify widths of the workload, uniform and
+    # Zipf-biased routing (same 16 rotating layers, cold)
+    def layer_at(Ms, alpha, steps=32, warm=8):
+        xs = up(synth.activations(Ms, H, seed=synth.ACT_SEED, tag=10 + Ms))
+        bs = None if alpha is None else torch.from_numpy(synth.zipf_bias(E, alpha)).to(dev)
+        ids = torch.empty((Ms, k), dtype=torch.int32, device=dev)
+        tws = torch.empty((Ms, k), dtype=torch.float32, device=dev)
+        outs = torch.empty((Ms, H), dtype=torch.float32, device=dev)
+        ws = torch.zeros(L.moe_layer_workspace_bytes(Ms, H, I, E, k), dtype=torch.uint8, device=dev)
+        a = [(xs.data_ptr(), Lw["router"].data_ptr(), bs.data_ptr() if bs is not None else None,
+              Lw["gate"].data_ptr(), Lw["up"].data_ptr(), Lw["down"].data_ptr(),
+              Ms, H, I, E, k, ids.data_ptr(), tws.data_ptr(), outs.data_ptr(),
+              ws.data_ptr(), ws.numel(), stream) for Lw in layers]
+        Ds = []
+        for l in range(nl):
+            check("moe_layer", L.moe_layer(*a[l]))
+            torch.cuda.synchronize()
+            Ds.append(len(np.unique(ids.cpu().numpy())))
+        io = Ms * H * 2 + Ms * k * 8 + Ms * H * 4 + (E * 4 if bs is not None else 0)
+        for s in range(warm):
+            check("moe_layer", L.moe_layer(*a[s % nl]))
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        for i in range(steps):
+            ev[i].record()
+            check("moe_layer", L.moe_layer(*a[(warm + i) % nl]))
+        ev[steps].record()
+        torch.cuda.synchronize()
+        us = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) * 1e3 / steps
+        byts = sum(E * H * 2 + Ds[(warm + i) % nl] * per_expert + io for i in range(steps)) / steps
+        gbps = byts / (us * 1e-6) / 1e9
+        return {"M": Ms, "zipf_alpha": alpha, "us": round(us, 2), "GBps": round(gbps, 1),
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes": int(byts),
+                "distinct_experts_mean": sum(Ds) / len(Ds)}
+
+    layer_sweep = [layer_at(m, a) for m, a in ((1, None), (1, 1.0), (16, None), (16, 1.0))]
+    log("layer sweep: " + ", ".join(f"M={r['M']} alpha={r['zipf_alpha']}: {r['us']} us "
+                                    f"({r['frac']:.1%})" for r in layer_sweep))
+
     lm_gbps = lm_bytes / (lm_us_mean * 1e-6) / 1e9
     layer_gbps = layer_bytes_mean / (layer_us_mean * 1e-6) / 1e9
     traffic = load_traffic("lmhead_argmax", src_digest("lmhead.hip", "common.h"))
@@ -359,7 +414,8 @@ def main():
                     "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "bytes": lm_bytes},
         "router_gate_cold": {"us": round(route_us, 2),
                              "GBps": round(route_bytes / (route_us * 1e-6) / 1e9, 1),
-                             "copies": R},
+                             "copies": R, "us_by_distinct_copies": gate_sweep},
+        "moe_layer_other_widths": layer_sweep,
         "roofline": {"kernel": "lmhead_argmax", "bound": "hbm",
                      "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},

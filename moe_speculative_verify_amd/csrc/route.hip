@@ -86,30 +86,35 @@ __device__ __forceinline__ void sel_pop(uint64_t (&key)[KJ], bool adv)
     }
 }
 
-// one DPP step of a wave-wide 64-bit maximum; rows a broadcast leaves out
-// receive 0, the identity
+// one fused DPP step of a wave-wide uint32 maximum; rows a broadcast leaves
+// out receive 0, the identity, so the move folds into v_max_u32_dpp
 template <int CTRL, int ROWMASK>
-__device__ __forceinline__ uint64_t key_dpp_step(uint64_t v)
+__device__ __forceinline__ uint32_t max_u32_dpp(uint32_t v)
 {
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWMASK, 0xF, false);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWMASK, 0xF, false);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWMASK, 0xF, false);
     return o > v ? o : v;
 }
-// largest key over the wavefront, uniform: DPP steps inside each 16-lane
-// row, the rows combined with row_bcast:15 (into rows 1 and 3) and
-// row_bcast:31 (into rows 2 and 3), then lane 63, which has seen every lane
+// maximum over the wavefront, uniform: DPP steps inside each 16-lane row,
+// the rows combined with row_bcast:15 (into rows 1 and 3) and row_bcast:31
+// (into rows 2 and 3), then lane 63, which has seen every lane
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max_u32_dpp<0xB1, 0xF>(v);
+    v = max_u32_dpp<0x4E, 0xF>(v);
+    v = max_u32_dpp<0x141, 0xF>(v);
+    v = max_u32_dpp<0x140, 0xF>(v);
+    v = max_u32_dpp<0x142, 0xA>(v);
+    v = max_u32_dpp<0x143, 0xC>(v);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+// largest 64-bit key over the wavefront, uniform: the largest high word,
+// then the largest low word among the lanes holding it (branch-free)
 __device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
 {
-    v = key_dpp_step<0xB1, 0xF>(v);
-    v = key_dpp_step<0x4E, 0xF>(v);
-    v = key_dpp_step<0x141, 0xF>(v);
-    v = key_dpp_step<0x140, 0xF>(v);
-    v = key_dpp_step<0x142, 0xA>(v);
-    v = key_dpp_step<0x143, 0xC>(v);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
-    return ((uint64_t)hi << 32) | lo;
+    const uint32_t hi = (uint32_t)(v >> 32);
+    const uint32_t whi = wave_max_u32(hi);
+    const uint32_t wlo = wave_max_u32(hi == whi ? (uint32_t)v : 0u);
+    return ((uint64_t)whi << 32) | wlo;
 }
 
 // S: MFMA steps per wavefront; KJ: logits per lane in the selection (a
