@@ -55,6 +55,8 @@ class Oracle:
         lib.oracle_expert_ffn.restype = ctypes.c_int
         lib.oracle_lmhead.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P]
         lib.oracle_lmhead.restype = ctypes.c_int
+        lib.oracle_greedy_verdict.argtypes = [_P, _P, _I, _P]
+        lib.oracle_greedy_verdict.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -128,6 +130,19 @@ class Oracle:
         self._check(rc, "oracle_lmhead")
         return dict(tok=tok, zmax=zmax, gap=gap)
 
+    def greedy_verdict(self, tokens, tok) -> tuple[int, int]:
+        """tokens [M] (root, drafted candidates), tok [M] (target argmax)
+        -> (accept length n + 1, bonus token tok[n])."""
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+        tok = np.ascontiguousarray(tok, dtype=np.int32)
+        if tokens.shape != tok.shape or tokens.ndim != 1:
+            raise ValueError("tokens and tok must be two [M] vectors")
+        acc = np.empty(2, np.int32)
+        rc = self.lib.oracle_greedy_verdict(tokens.ctypes.data, tok.ctypes.data,
+                                            tokens.shape[0], acc.ctypes.data)
+        self._check(rc, "oracle_greedy_verdict")
+        return int(acc[0]), int(acc[1])
+
 
 _default: Oracle | None = None
 
@@ -152,3 +167,7 @@ def expert_ffn(x, idx, w, wgate, wup, wdown, want_act=False):
 
 def lmhead(h, wlm):
     return load().lmhead(h, wlm)
+
+
+def greedy_verdict(tokens, tok):
+    return load().greedy_verdict(tokens, tok)

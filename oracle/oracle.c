@@ -19,7 +19,12 @@
  *     fp32 logits), ties to the lower index;
  *   - silu(z) = z / (1 + exp(-z)), applied to the gate projection and
  *     multiplied by the up projection (section "Two fusions and a retune");
- *   - the combine sums the k slots in slot order (same section).
+ *   - the combine sums the k slots in slot order (same section);
+ *   - the verify chain is scored greedily: a drafted candidate is accepted
+ *     while it equals the target's argmax at the position before it, and
+ *     the target's argmax after the last accepted position is the bonus
+ *     token (section "The shape of a single-request step", greedy decoding
+ *     throughout).
  */
 #include "oracle.h"
 
@@ -272,5 +277,26 @@ int oracle_lmhead(const uint16_t *h, const uint16_t *wlm,
         sorted_gaps(z, V, 1, &gap[t], &unused);
     }
     free(z);
+    return 0;
+}
+
+int oracle_greedy_verdict(const int32_t *tokens, const int32_t *tok, int32_t M,
+                          int32_t *accept)
+{
+    if (!tokens || !tok || !accept)
+        return -1;
+    if (M < 1)
+        return -2;
+    /* Walk the chain from the first drafted candidate: position i is
+     * accepted when its token is what the target predicted after position
+     * i - 1; the first rejection ends the accepted prefix. */
+    int32_t n = 0;
+    for (int32_t i = 1; i < M; ++i) {
+        if (tokens[i] != tok[i - 1])
+            break;
+        n = i;
+    }
+    accept[0] = n + 1;
+    accept[1] = tok[n];
     return 0;
 }

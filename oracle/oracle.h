@@ -91,6 +91,25 @@ int oracle_lmhead(const uint16_t *h, const uint16_t *wlm,
                   int32_t M, int32_t H, int32_t V,
                   int32_t *tok, double *zmax, double *gap);
 
+/* Greedy verdict of one verify step over a drafted chain (section "The
+ * shape of a single-request step": the target scores the whole chain in one
+ * forward and the verdict is taken inside the verify step).
+ *   tokens [M] int32  the chain the target scored: tokens[0] is the root
+ *                     (committed by the previous step), tokens[1..M-1] the
+ *                     drafted candidates in chain order
+ *   tok    [M] int32  the target's greedy token after each chain position
+ *                     (tok of oracle_lmhead)
+ * output:
+ *   accept [2] int32  accept[0] = n + 1, n = the number of leading drafted
+ *                     candidates equal to the target's token at the position
+ *                     before them (tokens[i] == tok[i-1], i = 1..n; the
+ *                     first mismatch ends the prefix); accept[1] = tok[n],
+ *                     the bonus token and next root.
+ * The step commits tok[0..n]: the n accepted candidates and the bonus token.
+ */
+int oracle_greedy_verdict(const int32_t *tokens, const int32_t *tok, int32_t M,
+                          int32_t *accept);
+
 #ifdef __cplusplus
 }
 #endif

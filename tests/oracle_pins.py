@@ -314,4 +314,46 @@ def pin_lmhead_planted(o):
     assert r0["tok"].tolist() == [0]
 
 
+# ----------------------------------------------------------- greedy verdict
+
+def pin_verdict_planted_chains(o):
+    """Chains built from the target's tokens: a chain that follows every
+    prediction is accepted whole (M tokens committed, bonus tok[M-1]); a
+    candidate changed at position j ends the prefix there (j tokens, bonus
+    tok[j-1]) whatever follows it; the root never matters; a one-position
+    chain commits just the bonus token."""
+    rng = np.random.default_rng(5)
+    for M in (1, 2, 6, 16):
+        tok = rng.integers(0, 157184, size=M).astype(np.int32)
+        chain = np.concatenate([[rng.integers(0, 157184)], tok[:-1]]).astype(np.int32)
+        assert o.greedy_verdict(chain, tok) == (M, int(tok[M - 1]))
+        for j in range(1, M):
+            bad = chain.copy()
+            bad[j] = tok[j - 1] + 1          # rejected; every later one still matches
+            assert o.greedy_verdict(bad, tok) == (j, int(tok[j - 1]))
+        root = chain.copy()
+        root[0] = -7
+        assert o.greedy_verdict(root, tok) == (M, int(tok[M - 1]))
+
+
+def pin_verdict_brute_force(o):
+    """Every chain over a two-token vocabulary at M = 5 against the target's
+    tokens: the accept length is one plus the length of the run of pairwise
+    equal (candidate, previous prediction) pairs from the start, and the
+    committed tokens tok[0..n] are the accepted candidates followed by the
+    bonus token."""
+    import itertools
+    M = 5
+    for tok_bits in itertools.product((0, 1), repeat=M):
+        tok = np.array(tok_bits, np.int32)
+        for cand in itertools.product((0, 1), repeat=M - 1):
+            chain = np.array((3,) + cand, np.int32)
+            run = len(list(itertools.takewhile(lambda ab: ab[0] == ab[1],
+                                               zip(chain[1:], tok[:-1]))))
+            acc, bonus = o.greedy_verdict(chain, tok)
+            assert acc == run + 1 and bonus == tok[run]
+            committed = list(chain[1:acc]) + [bonus]
+            assert committed == list(tok[:acc])
+
+
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

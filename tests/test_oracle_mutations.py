@@ -40,6 +40,10 @@ MUTATIONS = {
     "argmax_tie_to_higher": ("if (zv > best_v) {", "if (zv >= best_v) {"),
     "argmax_skips_last": ("for (int32_t v = 1; v < V; ++v) {", "for (int32_t v = 1; v + 1 < V; ++v) {"),
     "lmhead_row_stride": ("wlm + (int64_t)v * H, H);", "wlm + (int64_t)v, H);"),
+    "verdict_same_position": ("if (tokens[i] != tok[i - 1])", "if (tokens[i] != tok[i])"),
+    "verdict_no_stop": ("            break;\n        n = i;", "            continue;\n        n = i;"),
+    "verdict_bonus_from_chain": ("accept[1] = tok[n];", "accept[1] = tokens[n];"),
+    "verdict_no_bonus": ("accept[0] = n + 1;", "accept[0] = n;"),
     "gap_wrong_rank": ("*gap_sel = (k < n) ? s[k - 1] - s[k] : INFINITY;",
                        "*gap_sel = (k < n) ? s[0] - s[k] : INFINITY;"),
 }
