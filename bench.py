@@ -4,7 +4,9 @@
 One step = one pass of the whole path over one batch of M verify tokens:
   moe_layer     router gate GEMV + softmax top-k, then the selected experts'
                 SwiGLU FFN with weighted combine (one MoE layer verify step)
-  lmhead_argmax lm_head GEMV fused with the greedy argmax
+  lmhead_greedy_verify
+                lm_head GEMV fused with the greedy argmax and the greedy
+                verdict of the verify chain (accept length, bonus token)
 Weights are seeded synthetic bf16 ~N(0, 0.02) generated on the device: 16
 distinct MoE layers (8.06 GB each) rotated step by step and two lm_head
 copies (805 MB each) alternated, so every weight byte comes from HBM (the
@@ -105,7 +107,7 @@ def write_counters(fetch_csv: str, write_csv: str, calib_mib: int) -> None:
     lm_read = fe[LM_KERNEL] * 1024 / f_fac
     lm_write = wr[LM_KERNEL] * 1024 / w_fac
     out = {
-        "kernel": "lmhead_argmax (lmhead_kernel), 157184x2560 bf16, M=6",
+        "kernel": "lmhead_greedy_verify (lmhead_kernel), 157184x2560 bf16, M=6",
         "source_digest": src_digest("lmhead.hip", "common.h"),
         "fetch_kib_per_dispatch": round(fe[LM_KERNEL], 1),
         "write_kib_per_dispatch": round(wr[LM_KERNEL], 3),
@@ -195,6 +197,10 @@ def main():
     tw = torch.empty((M, k), dtype=torch.float32, device=dev)
     out = torch.empty((M, H), dtype=torch.float32, device=dev)
     am = torch.empty(M, dtype=torch.int32, device=dev)
+    # the verify chain (root, then M - 1 drafted candidates): seeded tokens;
+    # the verdict's cost does not depend on how many are accepted
+    chain = torch.from_numpy(np.random.default_rng(3).integers(0, V, size=M).astype(np.int32)).to(dev)
+    acc = torch.empty(2, dtype=torch.int32, device=dev)
     ws_layer = torch.zeros(L.moe_layer_workspace_bytes(M, H, I, E, k), dtype=torch.uint8, device=dev)
     ws_lm = torch.zeros(L.lmhead_argmax_workspace_bytes(M, V), dtype=torch.uint8, device=dev)
     ws_route = torch.zeros(L.moe_route_workspace_bytes(M, E), dtype=torch.uint8, device=dev)
@@ -205,8 +211,8 @@ def main():
                    Lw["gate"].data_ptr(), Lw["up"].data_ptr(), Lw["down"].data_ptr(),
                    M, H, I, E, k, idx.data_ptr(), tw.data_ptr(), out.data_ptr(),
                    ws_layer.data_ptr(), ws_layer.numel(), stream) for Lw in layers]
-    lm_args = [(h.data_ptr(), w.data_ptr(), M, H, V, am.data_ptr(), None, ws_lm.data_ptr(),
-                ws_lm.numel(), stream) for w in lms]
+    lm_args = [(h.data_ptr(), w.data_ptr(), chain.data_ptr(), M, H, V, am.data_ptr(), None,
+                acc.data_ptr(), ws_lm.data_ptr(), ws_lm.numel(), stream) for w in lms]
     route_args = [(x.data_ptr(), r.data_ptr(), bias.data_ptr() if bias is not None else None,
                    M, H, E, k, idx.data_ptr(), tw.data_ptr(), None, ws_route.data_ptr(),
                    ws_route.numel(), stream) for r in routers]
@@ -217,7 +223,7 @@ def main():
 
     def step(s):
         check("moe_layer", L.moe_layer(*layer_args[s % len(layer_args)]))
-        check("lmhead_argmax", L.lmhead_argmax(*lm_args[s % len(lm_args)]))
+        check("lmhead_greedy_verify", L.lmhead_greedy_verify(*lm_args[s % len(lm_args)]))
 
     if args.profile_steps:
         # calibration kernel of known traffic for the HBM counters: an int32
@@ -247,7 +253,7 @@ def main():
     per_expert = 3 * I * H * 2
     io_layer = M * H * 2 + M * k * 8 + M * H * 4 + (E * 4 if bias is not None else 0)
     layer_bytes = [E * H * 2 + d * per_expert + io_layer for d in D]
-    lm_bytes = V * H * 2 + M * H * 2 + M * 4
+    lm_bytes = V * H * 2 + M * H * 2 + M * 4 + M * 4 + 8
     route_bytes = E * H * 2 + M * H * 2 + M * k * 8 + (E * 4 if bias is not None else 0)
     nl = len(layers)
     K = args.steps
@@ -266,7 +272,7 @@ def main():
         evs[i][0].record()
         check("moe_layer", L.moe_layer(*layer_args[s % nl]))
         evs[i][1].record()
-        check("lmhead_argmax", L.lmhead_argmax(*lm_args[s % len(lm_args)]))
+        check("lmhead_greedy_verify", L.lmhead_greedy_verify(*lm_args[s % len(lm_args)]))
         evs[i][2].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_start) * 1e3 / K
@@ -416,7 +422,7 @@ def main():
                              "GBps": round(route_bytes / (route_us * 1e-6) / 1e9, 1),
                              "copies": R, "us_by_distinct_copies": gate_sweep},
         "moe_layer_other_widths": layer_sweep,
-        "roofline": {"kernel": "lmhead_argmax", "bound": "hbm",
+        "roofline": {"kernel": "lmhead_kernel (lmhead_greedy_verify)", "bound": "hbm",
                      "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},
         "cpu_baseline": cpu,

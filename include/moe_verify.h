@@ -167,6 +167,35 @@ moe_status_t lmhead_argmax(const uint16_t *h, const uint16_t *w_lm,
                            float *max_logit, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * lmhead_greedy_verify -- lmhead_argmax and, in the same launch, the greedy
+ * verdict of the verify chain. (Section "The shape of a single-request
+ * step": the target scores the drafted chain in one forward and the verdict
+ * is taken inside the verify step, on the device; greedy decoding.)
+ *
+ *   h, w_lm, M, H, V, argmax, max_logit, workspace: as lmhead_argmax; row t
+ *              of h is the target's hidden state at chain position t
+ *   tokens     [M] int32  the chain the target scored: tokens[0] the root
+ *                         (committed by the previous step), tokens[1..M-1]
+ *                         the drafted candidates in chain order
+ *   accept     [2] int32  out: accept[0] = n + 1, where n counts the leading
+ *                         candidates with tokens[i] == argmax[i-1]
+ *                         (i = 1..n; the first mismatch ends the prefix);
+ *                         accept[1] = argmax[n], the bonus token and the
+ *                         next step's root
+ *
+ * The step commits argmax[0..n] (n accepted candidates, then the bonus
+ * token). tokens is read on the device only; any int32 value is allowed.
+ * Errors: as lmhead_argmax; MOE_ERR_NULL if tokens or accept is NULL,
+ * MOE_ERR_ALIGN unless both are 4-byte aligned. Uses the same workspace
+ * size as lmhead_argmax.
+ * ---------------------------------------------------------------------- */
+moe_status_t lmhead_greedy_verify(const uint16_t *h, const uint16_t *w_lm,
+                                  const int32_t *tokens, int32_t M, int32_t H,
+                                  int32_t V, int32_t *argmax, float *max_logit,
+                                  int32_t *accept, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

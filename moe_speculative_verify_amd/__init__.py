@@ -27,7 +27,7 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_clear",
            "moe_route_workspace_bytes", "moe_route",
            "moe_expert_ffn_workspace_bytes", "moe_expert_ffn",
            "moe_layer_workspace_bytes", "moe_layer",
-           "lmhead_argmax_workspace_bytes", "lmhead_argmax")
+           "lmhead_argmax_workspace_bytes", "lmhead_argmax", "lmhead_greedy_verify")
 
 
 class MoeError(RuntimeError):
@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.lmhead_argmax_workspace_bytes.argtypes = [_I, _I]
         L.lmhead_argmax.restype = ctypes.c_int32
         L.lmhead_argmax.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _S, _P]
+        L.lmhead_greedy_verify.restype = ctypes.c_int32
+        L.lmhead_greedy_verify.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _S, _P]
         _lib = L
     return _lib
 
@@ -254,3 +256,31 @@ def lmhead_argmax(h, w_lm, *, want_max=False, out=None, workspace=None, stream=N
         _ptr(ml, "max_logit", (torch.float32,), (M,)) if want_max else None,
         _ptr(ws, "workspace"), ws.numel(), st))
     return (am, ml) if want_max else am
+
+
+def lmhead_greedy_verify(h, w_lm, tokens, *, want_max=False, out=None, workspace=None,
+                         stream=None):
+    """lm_head GEMV + greedy argmax + greedy verdict of the chain `tokens`
+    ([M] int32: root, then the drafted candidates). Returns (argmax [M] int32,
+    accept [2] int32 = (accept length, bonus token)) (, max_logit)."""
+    M, H = h.shape
+    V = w_lm.shape[0]
+    dev = h.device
+    am, acc, ml = out if out is not None else (None, None, None)
+    if am is None:
+        am = torch.empty(M, dtype=torch.int32, device=dev)
+    if acc is None:
+        acc = torch.empty(2, dtype=torch.int32, device=dev)
+    if want_max and ml is None:
+        ml = torch.empty(M, dtype=torch.float32, device=dev)
+    st = _stream(stream)
+    nbytes = lmhead_argmax_workspace_bytes(M, V)
+    ws = workspace if workspace is not None else Workspace.get("lmhead", nbytes, dev, st)
+    _check("lmhead_greedy_verify", lib().lmhead_greedy_verify(
+        _ptr(h, "h", _BF16), _ptr(w_lm, "w_lm", _BF16, (V, H)),
+        _ptr(tokens, "tokens", (torch.int32,), (M,)), M, H, V,
+        _ptr(am, "argmax", (torch.int32,), (M,)),
+        _ptr(ml, "max_logit", (torch.float32,), (M,)) if want_max else None,
+        _ptr(acc, "accept", (torch.int32,), (2,)),
+        _ptr(ws, "workspace"), ws.numel(), st))
+    return (am, acc, ml) if want_max else (am, acc)

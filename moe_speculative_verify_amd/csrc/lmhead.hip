@@ -25,6 +25,10 @@
 //     atomic max, so the largest value and then the lowest index win
 //     whatever the order. The last workgroup to take a ticket (device-scope
 //     atomic, no spinning, no cache flush) decodes the keys and resets them.
+//   - lmhead_greedy_verify: the same launch, and the same last workgroup
+//     then takes the greedy verdict of the verify chain from the decoded
+//     tokens (section "The shape of a single-request step": the verdict is
+//     part of the verify step and stays on the device).
 #include "common.h"
 
 #include <mutex>
@@ -54,7 +58,8 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     const u32x4 *__restrict__ h, const u32x4 *__restrict__ wl, int M, int H,
     int V, int tiles_per_wg, unsigned long long *__restrict__ keys,
     unsigned *__restrict__ ticket, int *__restrict__ argmax,
-    float *__restrict__ max_logit)
+    float *__restrict__ max_logit, const int *__restrict__ tokens,
+    int *__restrict__ accept)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int lane = threadIdx.x & (kWave - 1);
@@ -151,6 +156,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     __shared__ float s_v[kLmWaves][16];
     __shared__ int s_i[kLmWaves][16];
     __shared__ int s_last;
+    __shared__ int s_tok[kMaxM];
     if (g == 0) {
         s_v[wave][j] = bv;
         s_i[wave][j] = bi;
@@ -185,12 +191,27 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
         const int t = threadIdx.x;
         const unsigned long long key = __hip_atomic_exchange(
             keys + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        argmax[t] = (int)(~(uint32_t)key);
+        const int tok = (int)(~(uint32_t)key);
+        argmax[t] = tok;
+        s_tok[t] = tok;
         if (max_logit)
             max_logit[t] = f32_unorder((uint32_t)(key >> 32));
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tokens == nullptr)                               // uniform
+        return;
+    // Greedy verdict: drafted candidate i (chain position i >= 1) is
+    // accepted while it equals the target's token after position i - 1;
+    // the first rejection ends the prefix. accept = {n + 1, bonus token}.
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int n = 0;
+        while (n + 1 < M && tokens[n + 1] == s_tok[n])
+            ++n;
+        accept[0] = n + 1;
+        accept[1] = s_tok[n];
+    }
 }
 
 // one workgroup per CU: the LDS footprint allows no more
@@ -208,11 +229,11 @@ extern "C" size_t lmhead_argmax_workspace_bytes(int32_t M, int32_t V)
     return kWsHeader + align_up((size_t)M * 8, 256);
 }
 
-extern "C" moe_status_t lmhead_argmax(const uint16_t *h, const uint16_t *w_lm,
-                                      int32_t M, int32_t H, int32_t V,
-                                      int32_t *argmax, float *max_logit,
-                                      void *workspace, size_t workspace_bytes,
-                                      void *stream)
+static moe_status_t lmhead_enqueue(const uint16_t *h, const uint16_t *w_lm,
+                                   int32_t M, int32_t H, int32_t V, int32_t *argmax,
+                                   float *max_logit, const int32_t *tokens,
+                                   int32_t *accept, void *workspace,
+                                   size_t workspace_bytes, void *stream)
 {
     if (!h || !w_lm || !argmax || !workspace)
         return MOE_ERR_NULL;
@@ -221,7 +242,8 @@ extern "C" moe_status_t lmhead_argmax(const uint16_t *h, const uint16_t *w_lm,
     if (M > kMaxM || H % 8 != 0 || H > kMaxDim || lm_lds_bytes(M, H) > (size_t)kLdsDynMax)
         return MOE_ERR_UNSUPPORTED;
     if (!aligned16(h) || !aligned16(w_lm) || !aligned4(argmax) ||
-        (max_logit && !aligned4(max_logit)) || !aligned16(workspace))
+        (max_logit && !aligned4(max_logit)) || !aligned16(workspace) ||
+        (tokens && (!aligned4(tokens) || !aligned4(accept))))
         return MOE_ERR_ALIGN;
     if (workspace_bytes < lmhead_argmax_workspace_bytes(M, V))
         return MOE_ERR_WORKSPACE;
@@ -241,6 +263,29 @@ extern "C" moe_status_t lmhead_argmax(const uint16_t *h, const uint16_t *w_lm,
         return MOE_ERR_LAUNCH;
     hipLaunchKernelGGL(lmhead_kernel, dim3(grid), dim3(kLmWaves * kWave), lds,
                        (hipStream_t)stream, (const u32x4 *)h, (const u32x4 *)w_lm,
-                       M, H, V, tpw, keys, ticket, argmax, max_logit);
+                       M, H, V, tpw, keys, ticket, argmax, max_logit, tokens, accept);
     return check_launch();
+}
+
+extern "C" moe_status_t lmhead_argmax(const uint16_t *h, const uint16_t *w_lm,
+                                      int32_t M, int32_t H, int32_t V,
+                                      int32_t *argmax, float *max_logit,
+                                      void *workspace, size_t workspace_bytes,
+                                      void *stream)
+{
+    return lmhead_enqueue(h, w_lm, M, H, V, argmax, max_logit, nullptr, nullptr,
+                          workspace, workspace_bytes, stream);
+}
+
+extern "C" moe_status_t lmhead_greedy_verify(const uint16_t *h, const uint16_t *w_lm,
+                                             const int32_t *tokens, int32_t M,
+                                             int32_t H, int32_t V, int32_t *argmax,
+                                             float *max_logit, int32_t *accept,
+                                             void *workspace, size_t workspace_bytes,
+                                             void *stream)
+{
+    if (!tokens || !accept)
+        return MOE_ERR_NULL;
+    return lmhead_enqueue(h, w_lm, M, H, V, argmax, max_logit, tokens, accept,
+                          workspace, workspace_bytes, stream);
 }

@@ -132,6 +132,19 @@ def test_lmhead_checks(L):
     assert lm(wsb=16) == WS
 
 
+def test_greedy_verify_checks(L):
+    def gv(h=A, w=A, tok=A, M=6, H=2560, V=157184, am=A, ml=None, acc=B, ws=B, wsb=1 << 20):
+        return L.lmhead_greedy_verify(h, w, tok, M, H, V, am, ml, acc, ws, wsb, None)
+    assert gv(tok=None) == NULL
+    assert gv(acc=None) == NULL
+    assert gv(h=None) == NULL
+    assert gv(M=0) == SHAPE
+    assert gv(M=17) == UNSUP
+    assert gv(tok=A + 2) == ALIGN
+    assert gv(acc=B + 1) == ALIGN
+    assert gv(wsb=16) == WS
+
+
 def test_workspace_clear_checks(L):
     assert L.moe_workspace_clear(None, 256, None) == NULL
     assert L.moe_workspace_clear(MIS, 256, None) == ALIGN

@@ -314,6 +314,76 @@ def test_lmhead_zero_hidden():
     assert am.tolist() == [0, 0] and np.all(ml == 0.0)
 
 
+# --------------------------------------------------- greedy verify verdict
+
+def _verify_gpu(h, wl, chain):
+    am, acc, ml = mv.lmhead_greedy_verify(
+        to_dev(h), wl if isinstance(wl, torch.Tensor) else to_dev(wl),
+        torch.from_numpy(np.ascontiguousarray(chain, np.int32)).to("cuda"), want_max=True)
+    torch.cuda.synchronize()
+    return am.cpu().numpy(), acc.cpu().numpy(), ml.cpu().numpy()
+
+
+def _chains(tok, V, rng):
+    """Chains against the target tokens tok: followed throughout, rejected at
+    each position j (later candidates still follow), and one random chain."""
+    M = tok.shape[0]
+    full = np.concatenate([[rng.integers(0, V)], tok[:-1]]).astype(np.int32)
+    out = [full]
+    for j in range(1, M):
+        c = full.copy()
+        c[j] = (tok[j - 1] + 1) % max(V, 2)
+        out.append(c)
+    out.append(rng.integers(0, V, size=M).astype(np.int32))
+    return out
+
+
+@pytest.mark.parametrize("M,H,V", [(6, 2560, 4099), (1, 256, 1000), (16, 256, 4099),
+                                   (5, 264, 777), (2, 8, 1)])
+def test_greedy_verify_matches_oracle(M, H, V):
+    say("greedy verify", M, H, V)
+    h = synth.activations(M, H, seed=1500 + V)
+    wl = synth.normal_bf16((V, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 19, V)
+    ref = oracle.lmhead(h, wl)
+    am0, ml0 = _lm_gpu(h, wl)
+    rng = np.random.default_rng(M * 1000 + V)
+    for chain in _chains(ref["tok"], V, rng):
+        am, acc, ml = _verify_gpu(h, wl, chain)
+        # the argmax is lmhead_argmax's, bit for bit, and matches the oracle
+        assert np.array_equal(am, am0) and np.array_equal(ml, ml0)
+        _compare_lm(am, ml, h, wl, ref)
+        # the verdict is exact given the kernel's tokens, and equals the
+        # oracle's verdict on the oracle's tokens whenever those agree
+        assert tuple(acc) == oracle.greedy_verdict(chain, am)
+        if np.array_equal(am, ref["tok"]):
+            assert tuple(acc) == oracle.greedy_verdict(chain, ref["tok"])
+
+
+def test_greedy_verify_full_size():
+    """Full lm_head (157184 x 2560, M = 6) with planted winners, so every
+    target token is known exactly: the chain is accepted up to a planted
+    rejection at position 3."""
+    say("greedy verify full size 6 x 2560 x 157184")
+    M, H, V = 6, 2560, 157184
+    h = synth.activations(M, H, seed=1601)
+    wl = synth.device_normal_bf16((V, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 0,
+                                  synth.KIND["lm_head"])
+    hd = to_dev(h)
+    rows = [V - 1, 1234, 777, 90001, 5, 150000]
+    for t, r in enumerate(rows):
+        wl[r] = hd[t] * 4
+    chain = np.array([42, rows[0], rows[1], rows[2] + 1, rows[3], rows[4]], np.int32)
+    am, acc, ml = _verify_gpu(h, wl, chain)
+    assert am.tolist() == rows
+    assert acc.tolist() == [3, rows[2]]
+    wl_bits = to_host_bits(wl)
+    _compare_lm(am, ml, h, wl_bits, oracle.lmhead(h, wl_bits))
+    assert tuple(acc) == oracle.greedy_verdict(chain, np.array(rows, np.int32))
+    chain_all = np.array([42] + rows[:5], np.int32)
+    _, acc2, _ = _verify_gpu(h, wl, chain_all)
+    assert acc2.tolist() == [6, rows[5]]
+
+
 # --------------------------------------------- determinism and invariance
 
 def test_determinism_and_batch_invariance(full_layer):
