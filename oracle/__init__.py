@@ -55,6 +55,8 @@ class Oracle:
         lib.oracle_expert_ffn.restype = ctypes.c_int
         lib.oracle_lmhead.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P]
         lib.oracle_lmhead.restype = ctypes.c_int
+        lib.oracle_rmsnorm.argtypes = [_P, _P, ctypes.c_double, _I, _I, _P, _P]
+        lib.oracle_rmsnorm.restype = ctypes.c_int
         lib.oracle_greedy_verdict.argtypes = [_P, _P, _I, _P]
         lib.oracle_greedy_verdict.restype = ctypes.c_int
         self.lib = lib
@@ -130,6 +132,20 @@ class Oracle:
         self._check(rc, "oracle_lmhead")
         return dict(tok=tok, zmax=zmax, gap=gap)
 
+    def rmsnorm(self, h, gamma, eps: float, want_exact=False):
+        """h [M,H] u16, gamma [H] u16 -> xn [M,H] u16 (bf16 bits) (, fp64 values)."""
+        h = np.ascontiguousarray(h, dtype=np.uint16)
+        gamma = np.ascontiguousarray(gamma, dtype=np.uint16)
+        M, H = h.shape
+        if gamma.shape != (H,):
+            raise ValueError("gamma must be [H]")
+        xn = np.empty((M, H), np.uint16)
+        ex = np.empty((M, H), np.float64) if want_exact else None
+        rc = self.lib.oracle_rmsnorm(h.ctypes.data, gamma.ctypes.data, float(eps), M, H,
+                                     xn.ctypes.data, None if ex is None else ex.ctypes.data)
+        self._check(rc, "oracle_rmsnorm")
+        return (xn, ex) if want_exact else xn
+
     def greedy_verdict(self, tokens, tok) -> tuple[int, int]:
         """tokens [M] (root, drafted candidates), tok [M] (target argmax)
         -> (accept length n + 1, bonus token tok[n])."""
@@ -171,3 +187,7 @@ def lmhead(h, wlm):
 
 def greedy_verdict(tokens, tok):
     return load().greedy_verdict(tokens, tok)
+
+
+def rmsnorm(h, gamma, eps, want_exact=False):
+    return load().rmsnorm(h, gamma, eps, want_exact)

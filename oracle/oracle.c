@@ -20,6 +20,8 @@
  *   - silu(z) = z / (1 + exp(-z)), applied to the gate projection and
  *     multiplied by the up projection (section "Two fusions and a retune");
  *   - the combine sums the k slots in slot order (same section);
+ *   - the router chain's norm is RMSNorm with a per-column gain, rounded
+ *     once to bf16 (the value both the gate and the experts read);
  *   - the verify chain is scored greedily: a drafted candidate is accepted
  *     while it equals the target's argmax at the position before it, and
  *     the target's argmax after the last accepted position is the bonus
@@ -298,5 +300,55 @@ int oracle_greedy_verdict(const int32_t *tokens, const int32_t *tok, int32_t M,
     }
     accept[0] = n + 1;
     accept[1] = tok[n];
+    return 0;
+}
+
+/* Nearest bf16 value to v, ties to an even significand, as a bit pattern:
+ * 8 significant bits in every binade, a fixed spacing of 2^-133 below the
+ * smallest normal. nearbyint rounds to nearest even in the default mode. */
+static uint16_t bf16_nearest(double v)
+{
+    if (v == 0.0)
+        return signbit(v) ? 0x8000 : 0;
+    int e;
+    (void)frexp(v, &e);                 /* |v| = m * 2^e, 0.5 <= m < 1 */
+    int q = e - 8;                      /* spacing of the binade holding v */
+    if (q < -133)
+        q = -133;
+    double r = ldexp(nearbyint(ldexp(v, -q)), q);
+    float f = (float)r;                 /* exact: at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+int oracle_rmsnorm(const uint16_t *h, const uint16_t *gamma, double eps,
+                   int32_t M, int32_t H, uint16_t *xn, double *xn_exact)
+{
+    if (!h || !gamma || !xn)
+        return -1;
+    if (M < 1 || H < 1 || !(eps >= 0.0))
+        return -2;
+    if (!all_finite_bf16(h, (int64_t)M * H) || !all_finite_bf16(gamma, H))
+        return -4;
+    for (int32_t t = 0; t < M; ++t) {
+        const uint16_t *row = h + (int64_t)t * H;
+        /* mean square of the row, plus eps */
+        double ss = 0.0;
+        for (int32_t i = 0; i < H; ++i) {
+            double v = oracle_bf16_value(row[i]);
+            ss += v * v;
+        }
+        double ms = ss / (double)H + eps;
+        if (ms == 0.0)
+            return -4;
+        double inv = 1.0 / sqrt(ms);
+        for (int32_t i = 0; i < H; ++i) {
+            double y = oracle_bf16_value(row[i]) * oracle_bf16_value(gamma[i]) * inv;
+            xn[(int64_t)t * H + i] = bf16_nearest(y);
+            if (xn_exact)
+                xn_exact[(int64_t)t * H + i] = y;
+        }
+    }
     return 0;
 }

@@ -91,6 +91,22 @@ int oracle_lmhead(const uint16_t *h, const uint16_t *wlm,
                   int32_t M, int32_t H, int32_t V,
                   int32_t *tok, double *zmax, double *gap);
 
+/* The norm at the head of the router chain (section "PDL: the latency floor
+ * of stacked small kernels", Fig. 7: norm -> gate matvec -> top-k), read as
+ * RMSNorm with a per-column gain and one rounding to bf16.
+ *   h     [M,H] bf16  hidden states
+ *   gamma [H]   bf16  gain
+ *   eps         >= 0  added to the mean square
+ * outputs:
+ *   xn       [M,H] bf16 bits  the bf16 value nearest (ties to an even
+ *                             significand) to
+ *                             h[t,i] * gamma[i] / sqrt(mean_i h[t,i]^2 + eps)
+ *   xn_exact [M,H] double     optional (NULL skips): that value in fp64
+ * Returns -4 when a row's mean square plus eps is zero.
+ */
+int oracle_rmsnorm(const uint16_t *h, const uint16_t *gamma, double eps,
+                   int32_t M, int32_t H, uint16_t *xn, double *xn_exact);
+
 /* Greedy verdict of one verify step over a drafted chain (section "The
  * shape of a single-request step": the target scores the whole chain in one
  * forward and the verdict is taken inside the verify step).

@@ -314,6 +314,67 @@ def pin_lmhead_planted(o):
     assert r0["tok"].tolist() == [0]
 
 
+# ------------------------------------------------------------------ RMSNorm
+
+def pin_rmsnorm_hand_examples(o):
+    """Worked by hand. h = [3, 4], gain 1, eps 0: mean square 12.5, so the
+    values are 3/sqrt(12.5) = 0.848528... = 1.697056 * 2^-1 (fraction
+    0.697056 * 128 = 89.22 -> 89: bits 126 << 7 | 89 = 0x3F59) and
+    4/sqrt(12.5) = 1.131371 (fraction 16.82 -> 17: 127 << 7 | 17 = 0x3F91).
+    h = [0.5, 0.5], eps 1: mean square 0.25 + 1 = 1.25, 0.5/sqrt(1.25) =
+    0.447214 = 1.788854 * 2^-2 (fraction 100.97 -> 101: 125 << 7 | 101 =
+    0x3EE5). h = [1.5, 0, 0, 0], gain [1 + 3/128, 1, 1, 1], eps 0.4375: mean
+    square 0.5625 + 0.4375 = 1 exactly, value 1.5 * 1.0234375 = 1.53515625,
+    a tie between fractions 68 and 69 -> the even 68 (0x3FC4)."""
+    one = 0x3F80
+    xn = o.rmsnorm(_bits([[3.0, 4.0]]), np.array([one, one], np.uint16), 0.0)
+    assert xn.tolist() == [[0x3F59, 0x3F91]]
+    xn = o.rmsnorm(_bits([[0.5, 0.5]]), np.array([one, one], np.uint16), 1.0)
+    assert xn.tolist() == [[0x3EE5, 0x3EE5]]
+    xn = o.rmsnorm(_bits([[1.5, 0.0, 0.0, 0.0]]), _bits([1.0234375, 1.0, 1.0, 1.0]), 0.4375)
+    assert xn.tolist() == [[0x3FC4, 0, 0, 0]]
+
+
+def pin_rmsnorm_closed_forms(o):
+    """eps = 0, gain 1: a constant row normalises to +-1 exactly; scaling a
+    row by a power of two leaves the result bitwise unchanged; doubling the
+    gain doubles every value exactly; the fp64 values have unit mean square;
+    permuting the columns (with the gain) permutes the result."""
+    H = 64
+    rng = np.random.default_rng(11)
+    one = np.full(H, 0x3F80, np.uint16)
+    xn = o.rmsnorm(_bits([[-2.5] * H, [0.375] * H]), one, 0.0)
+    assert np.all(xn[0] == 0xBF80) and np.all(xn[1] == 0x3F80)
+    h = synth.normal_bf16((3, H), 1.0, 41, 1)
+    g = synth.normal_bf16((H,), 1.0, 41, 2)
+    base, ex = o.rmsnorm(h, g, 0.0, want_exact=True)
+    assert np.array_equal(o.rmsnorm(_bits(F(h) * 8.0), g, 0.0), base)
+    two = o.rmsnorm(h, _bits(F(g) * 2.0), 0.0)
+    assert np.array_equal(F(two), F(base) * 2.0)
+    _, ex1 = o.rmsnorm(h, one, 0.0, want_exact=True)
+    assert np.allclose(np.mean(ex1 ** 2, axis=1), 1.0, rtol=0, atol=1e-14)
+    perm = rng.permutation(H)
+    assert np.array_equal(o.rmsnorm(h[:, perm], g[perm], 0.0), base[:, perm])
+
+
+def pin_rmsnorm_rounds_to_nearest(o):
+    """Every output is the bf16 value nearest to the fp64 value (neither
+    neighbour is closer; an exact tie takes the even significand), on random
+    rows with eps > 0."""
+    h = synth.normal_bf16((4, 256), 3.0, 43, 1)
+    g = synth.normal_bf16((256,), 1.0, 43, 2)
+    xn, ex = o.rmsnorm(h, g, 1e-6, want_exact=True)
+    b = xn.astype(np.int64)
+    val = F(xn).astype(np.float64)
+    up = F(((b + 1) & 0xFFFF).astype(np.uint16)).astype(np.float64)
+    dn = F(((b - 1) & 0xFFFF).astype(np.uint16)).astype(np.float64)
+    d = np.abs(ex - val)
+    assert np.all(d <= np.abs(ex - up)) and np.all(d <= np.abs(ex - dn))
+    tie = (d == np.abs(ex - up)) | (d == np.abs(ex - dn))
+    assert np.all((b[tie] & 1) == 0)
+    assert np.all(np.sign(val[ex != 0]) == np.sign(ex[ex != 0]))
+
+
 # ----------------------------------------------------------- greedy verdict
 
 def pin_verdict_planted_chains(o):

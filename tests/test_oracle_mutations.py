@@ -40,6 +40,16 @@ MUTATIONS = {
     "argmax_tie_to_higher": ("if (zv > best_v) {", "if (zv >= best_v) {"),
     "argmax_skips_last": ("for (int32_t v = 1; v < V; ++v) {", "for (int32_t v = 1; v + 1 < V; ++v) {"),
     "lmhead_row_stride": ("wlm + (int64_t)v * H, H);", "wlm + (int64_t)v, H);"),
+    "rms_mean_over_h_minus_1": ("double ms = ss / (double)H + eps;", "double ms = ss / (double)(H - 1) + eps;"),
+    "rms_eps_dropped": ("double ms = ss / (double)H + eps;", "double ms = ss / (double)H;"),
+    "rms_no_sqrt": ("double inv = 1.0 / sqrt(ms);", "double inv = 1.0 / ms;"),
+    "rms_gain_dropped": ("oracle_bf16_value(row[i]) * oracle_bf16_value(gamma[i]) * inv;",
+                         "oracle_bf16_value(row[i]) * inv;"),
+    "rms_truncating_round": ("double r = ldexp(nearbyint(ldexp(v, -q)), q);",
+                             "double r = ldexp(trunc(ldexp(v, -q)), q);"),
+    "rms_ties_away": ("double r = ldexp(nearbyint(ldexp(v, -q)), q);",
+                      "double r = ldexp(round(ldexp(v, -q)), q);"),
+    "rms_wrong_binade": ("    int q = e - 8;", "    int q = e - 9;"),
     "verdict_same_position": ("if (tokens[i] != tok[i - 1])", "if (tokens[i] != tok[i])"),
     "verdict_no_stop": ("            break;\n        n = i;", "            continue;\n        n = i;"),
     "verdict_bonus_from_chain": ("accept[1] = tok[n];", "accept[1] = tokens[n];"),
