@@ -217,6 +217,17 @@ def main():
                    M, H, E, k, idx.data_ptr(), tw.data_ptr(), None, ws_route.data_ptr(),
                    ws_route.numel(), stream) for r in routers]
 
+    # the router chain with its norm in front (moe_route_rmsnorm): the same
+    # rotating router copies, hidden states before the norm and a gain
+    hn = up(synth.hidden_states(M, H))
+    gain = up(synth.norm_gain(H))
+    xnorm = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    eps = ctypes.c_float(1e-6)
+    rn_args = [(hn.data_ptr(), gain.data_ptr(), eps, r.data_ptr(),
+                bias.data_ptr() if bias is not None else None, M, H, E, k, xnorm.data_ptr(),
+                idx.data_ptr(), tw.data_ptr(), None, ws_route.data_ptr(), ws_route.numel(),
+                stream) for r in routers]
+
     def check(fn, st):
         if st != 0:
             raise RuntimeError(f"{fn}: {mv.status_str(st)}")
@@ -240,6 +251,7 @@ def main():
         for s in range(args.profile_steps):
             step(s)
             check("moe_route", L.moe_route(*route_args[s % len(route_args)]))
+            check("moe_route_rmsnorm", L.moe_route_rmsnorm(*rn_args[s % len(rn_args)]))
         torch.cuda.synchronize()
         log(f"profile run: {args.profile_steps} steps done")
         return
@@ -314,42 +326,70 @@ def main():
         torch.cuda.synchronize()
         gate_sweep[str(n)] = round(g0.elapsed_time(g1) * 1e3 / (2 * R), 2)
 
+    for s in range(min(R, 16)):
+        check("moe_route_rmsnorm", L.moe_route_rmsnorm(*rn_args[s]))
+    torch.cuda.synchronize()
+    re0.record()
+    for s in range(R):
+        check("moe_route_rmsnorm", L.moe_route_rmsnorm(*rn_args[s]))
+    re1.record()
+    torch.cuda.synchronize()
+    route_norm_us = re0.elapsed_time(re1) * 1e3 / R
+
     # layer step at the other verify widths of the workload, uniform and
-    # Zipf-biased routing (same 16 rotating layers, cold)
-    def layer_at(Ms, alpha, steps=32, warm=8):
+    # Zipf-biased routing (same 16 rotating layers, cold); with norm=True the
+    # router chain's norm runs in front (moe_layer_rmsnorm)
+    def layer_at(Ms, alpha, steps=32, warm=8, norm=False):
         xs = up(synth.activations(Ms, H, seed=synth.ACT_SEED, tag=10 + Ms))
         bs = None if alpha is None else torch.from_numpy(synth.zipf_bias(E, alpha)).to(dev)
         ids = torch.empty((Ms, k), dtype=torch.int32, device=dev)
         tws = torch.empty((Ms, k), dtype=torch.float32, device=dev)
         outs = torch.empty((Ms, H), dtype=torch.float32, device=dev)
         ws = torch.zeros(L.moe_layer_workspace_bytes(Ms, H, I, E, k), dtype=torch.uint8, device=dev)
-        a = [(xs.data_ptr(), Lw["router"].data_ptr(), bs.data_ptr() if bs is not None else None,
-              Lw["gate"].data_ptr(), Lw["up"].data_ptr(), Lw["down"].data_ptr(),
-              Ms, H, I, E, k, ids.data_ptr(), tws.data_ptr(), outs.data_ptr(),
-              ws.data_ptr(), ws.numel(), stream) for Lw in layers]
+        if norm:
+            hs = up(synth.hidden_states(Ms, H, tag=10 + Ms))
+            xns = torch.empty((Ms, H), dtype=torch.bfloat16, device=dev)
+            a = [(hs.data_ptr(), gain.data_ptr(), eps, Lw["router"].data_ptr(),
+                  bs.data_ptr() if bs is not None else None,
+                  Lw["gate"].data_ptr(), Lw["up"].data_ptr(), Lw["down"].data_ptr(),
+                  Ms, H, I, E, k, xns.data_ptr(), ids.data_ptr(), tws.data_ptr(),
+                  outs.data_ptr(), ws.data_ptr(), ws.numel(), stream) for Lw in layers]
+            fn = L.moe_layer_rmsnorm
+        else:
+            a = [(xs.data_ptr(), Lw["router"].data_ptr(), bs.data_ptr() if bs is not None else None,
+                  Lw["gate"].data_ptr(), Lw["up"].data_ptr(), Lw["down"].data_ptr(),
+                  Ms, H, I, E, k, ids.data_ptr(), tws.data_ptr(), outs.data_ptr(),
+                  ws.data_ptr(), ws.numel(), stream) for Lw in layers]
+            fn = L.moe_layer
         Ds = []
         for l in range(nl):
-            check("moe_layer", L.moe_layer(*a[l]))
+            check("moe_layer", fn(*a[l]))
             torch.cuda.synchronize()
             Ds.append(len(np.unique(ids.cpu().numpy())))
-        io = Ms * H * 2 + Ms * k * 8 + Ms * H * 4 + (E * 4 if bs is not None else 0)
+        # with the norm: the pre-norm rows and the gain in, the normalised rows out
+        io = (Ms * H * 2 + Ms * k * 8 + Ms * H * 4 + (E * 4 if bs is not None else 0)
+              + (H * 2 + Ms * H * 2 if norm else 0))
         for s in range(warm):
-            check("moe_layer", L.moe_layer(*a[s % nl]))
+            check("moe_layer", fn(*a[s % nl]))
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         for i in range(steps):
             ev[i].record()
-            check("moe_layer", L.moe_layer(*a[(warm + i) % nl]))
+            check("moe_layer", fn(*a[(warm + i) % nl]))
         ev[steps].record()
         torch.cuda.synchronize()
         us = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) * 1e3 / steps
         byts = sum(E * H * 2 + Ds[(warm + i) % nl] * per_expert + io for i in range(steps)) / steps
         gbps = byts / (us * 1e-6) / 1e9
-        return {"M": Ms, "zipf_alpha": alpha, "us": round(us, 2), "GBps": round(gbps, 1),
+        return {"M": Ms, "zipf_alpha": alpha, "rmsnorm": norm, "us": round(us, 2),
+                "GBps": round(gbps, 1),
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes": int(byts),
                 "distinct_experts_mean": sum(Ds) / len(Ds)}
 
     layer_sweep = [layer_at(m, a) for m, a in ((1, None), (1, 1.0), (16, None), (16, 1.0))]
+    layer_norm = layer_at(M, args.zipf_alpha, norm=True)
+    log(f"router chain with norm: gate {route_norm_us:.2f} us (without {route_us:.2f}); "
+        f"layer M={M} {layer_norm['us']} us")
     log("layer sweep: " + ", ".join(f"M={r['M']} alpha={r['zipf_alpha']}: {r['us']} us "
                                     f"({r['frac']:.1%})" for r in layer_sweep))
 
@@ -422,6 +462,8 @@ def main():
                              "GBps": round(route_bytes / (route_us * 1e-6) / 1e9, 1),
                              "copies": R, "us_by_distinct_copies": gate_sweep},
         "moe_layer_other_widths": layer_sweep,
+        "router_chain_rmsnorm": {"gate_us": round(route_norm_us, 2),
+                                 "moe_layer_rmsnorm": layer_norm},
         "roofline": {"kernel": "lmhead_kernel (lmhead_greedy_verify)", "bound": "hbm",
                      "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},

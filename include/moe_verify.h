@@ -101,6 +101,35 @@ moe_status_t moe_route(const uint16_t *x, const uint16_t *w_router,
                        void *stream);
 
 /* ------------------------------------------------------------------------
+ * moe_route_rmsnorm -- the router chain with its norm in front: RMSNorm,
+ * then moe_route on the normalised rows, in one launch. (Router chain
+ * norm -> gate matvec -> top-k, section "PDL: the latency floor of stacked
+ * small kernels", Fig. 7; the norm is read as RMSNorm with a per-column
+ * gain, rounded once to bf16.)
+ *
+ *   h         [M,H] bf16   hidden states before the norm
+ *   gamma     [H]   bf16   gain (16-byte aligned)
+ *   eps              fp32  added to each row's mean square (>= 0, finite)
+ *   x_norm    [M,H] bf16   out: the bf16 value nearest to
+ *                          h[t,i] * gamma[i] / sqrt(mean_i h[t,i]^2 + eps)
+ *                          (ties to even); the gate reads exactly these
+ *                          values, and moe_expert_ffn should too
+ *   w_router, bias, M, H, E, k, topk_idx, topk_w, logits, workspace:
+ *                          as moe_route (same workspace size)
+ *
+ * Errors: as moe_route; MOE_ERR_NULL for a NULL gamma or x_norm,
+ * MOE_ERR_SHAPE for a negative, NaN or infinite eps, MOE_ERR_ALIGN unless
+ * gamma and x_norm are 16-byte aligned, MOE_ERR_UNSUPPORTED when M > 8 and
+ * H > 4096 (every hidden-state chunk of a lane must fit in registers).
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_route_rmsnorm(const uint16_t *h, const uint16_t *gamma, float eps,
+                               const uint16_t *w_router, const float *bias,
+                               int32_t M, int32_t H, int32_t E, int32_t k,
+                               uint16_t *x_norm, int32_t *topk_idx, float *topk_w,
+                               float *logits, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * moe_expert_ffn -- selected experts' SwiGLU FFN with weighted combine.
  * (MoE chain: grouping -> up-GEMM with SwiGLU epilogue -> down-GEMM ->
  *  combine; section "Two fusions and a retune")
@@ -146,6 +175,25 @@ moe_status_t moe_layer(const uint16_t *x, const uint16_t *w_router,
                        int32_t M, int32_t H, int32_t I, int32_t E, int32_t k,
                        int32_t *topk_idx, float *topk_w, float *out,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_layer_rmsnorm -- moe_route_rmsnorm then moe_expert_ffn on the
+ * normalised rows it wrote (x_norm), on one stream: the whole router chain
+ * (norm -> gate -> top-k) and MoE chain of the section "PDL: the latency
+ * floor of stacked small kernels", Fig. 7.
+ *
+ *   h, gamma, eps, x_norm:  as moe_route_rmsnorm
+ *   the rest:               as moe_layer (same workspace size)
+ * Errors: those of moe_route_rmsnorm and moe_expert_ffn.
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_layer_rmsnorm(const uint16_t *h, const uint16_t *gamma, float eps,
+                               const uint16_t *w_router, const float *bias,
+                               const uint16_t *w_gate, const uint16_t *w_up,
+                               const uint16_t *w_down, int32_t M, int32_t H,
+                               int32_t I, int32_t E, int32_t k, uint16_t *x_norm,
+                               int32_t *topk_idx, float *topk_w, float *out,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
 
 /* ------------------------------------------------------------------------
  * lmhead_argmax -- lm_head GEMV fused with the greedy argmax.

@@ -24,9 +24,9 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPP
 
 #: every symbol the header declares
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_clear",
-           "moe_route_workspace_bytes", "moe_route",
+           "moe_route_workspace_bytes", "moe_route", "moe_route_rmsnorm",
            "moe_expert_ffn_workspace_bytes", "moe_expert_ffn",
-           "moe_layer_workspace_bytes", "moe_layer",
+           "moe_layer_workspace_bytes", "moe_layer", "moe_layer_rmsnorm",
            "lmhead_argmax_workspace_bytes", "lmhead_argmax", "lmhead_greedy_verify")
 
 
@@ -61,6 +61,12 @@ def lib() -> ctypes.CDLL:
         L.moe_route_workspace_bytes.argtypes = [_I, _I]
         L.moe_route.restype = ctypes.c_int32
         L.moe_route.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _S, _P]
+        L.moe_route_rmsnorm.restype = ctypes.c_int32
+        L.moe_route_rmsnorm.argtypes = [_P, _P, ctypes.c_float, _P, _P, _I, _I, _I, _I,
+                                        _P, _P, _P, _P, _P, _S, _P]
+        L.moe_layer_rmsnorm.restype = ctypes.c_int32
+        L.moe_layer_rmsnorm.argtypes = [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P,
+                                        _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _S, _P]
         L.moe_expert_ffn_workspace_bytes.restype = _S
         L.moe_expert_ffn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
         L.moe_expert_ffn.restype = ctypes.c_int32
@@ -284,3 +290,66 @@ def lmhead_greedy_verify(h, w_lm, tokens, *, want_max=False, out=None, workspace
         _ptr(acc, "accept", (torch.int32,), (2,)),
         _ptr(ws, "workspace"), ws.numel(), st))
     return (am, acc, ml) if want_max else (am, acc)
+
+
+def moe_route_rmsnorm(h, gamma, eps: float, w_router, k: int, bias=None, *, want_logits=False,
+                      out=None, workspace=None, stream=None):
+    """RMSNorm + router gate GEMV + softmax top-k in one launch.
+    Returns (x_norm, topk_idx, topk_w[, logits])."""
+    M, H = h.shape
+    E = w_router.shape[0]
+    dev = h.device
+    xn, idx, w, logits = out if out is not None else (None, None, None, None)
+    if xn is None:
+        xn = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    if idx is None:
+        idx = torch.empty((M, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((M, k), dtype=torch.float32, device=dev)
+    if want_logits and logits is None:
+        logits = torch.empty((M, E), dtype=torch.float32, device=dev)
+    st = _stream(stream)
+    nbytes = moe_route_workspace_bytes(M, E)
+    ws = workspace if workspace is not None else Workspace.get("route", nbytes, dev, st)
+    _check("moe_route_rmsnorm", lib().moe_route_rmsnorm(
+        _ptr(h, "h", _BF16), _ptr(gamma, "gamma", _BF16, (H,)), float(eps),
+        _ptr(w_router, "w_router", _BF16, (E, H)),
+        _ptr(bias, "bias", (torch.float32,), (E,)), M, H, E, k,
+        _ptr(xn, "x_norm", _BF16, (M, H)),
+        _ptr(idx, "topk_idx", (torch.int32,), (M, k)),
+        _ptr(w, "topk_w", (torch.float32,), (M, k)),
+        _ptr(logits, "logits", (torch.float32,), (M, E)) if want_logits else None,
+        _ptr(ws, "workspace"), ws.numel(), st))
+    return (xn, idx, w, logits) if want_logits else (xn, idx, w)
+
+
+def moe_layer_rmsnorm(h, gamma, eps: float, w_router, w_gate, w_up, w_down, k: int, bias=None,
+                      *, out=None, workspace=None, stream=None):
+    """RMSNorm + route + expert FFN on the normalised rows.
+    Returns (x_norm, topk_idx, topk_w, out)."""
+    M, H = h.shape
+    E, I, _ = w_gate.shape
+    dev = h.device
+    xn, idx, w, o = out if out is not None else (None, None, None, None)
+    if xn is None:
+        xn = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    if idx is None:
+        idx = torch.empty((M, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((M, k), dtype=torch.float32, device=dev)
+    if o is None:
+        o = torch.empty((M, H), dtype=torch.float32, device=dev)
+    st = _stream(stream)
+    nbytes = moe_layer_workspace_bytes(M, H, I, E, k)
+    ws = workspace if workspace is not None else Workspace.get("layer", nbytes, dev, st)
+    _check("moe_layer_rmsnorm", lib().moe_layer_rmsnorm(
+        _ptr(h, "h", _BF16), _ptr(gamma, "gamma", _BF16, (H,)), float(eps),
+        _ptr(w_router, "w_router", _BF16, (E, H)),
+        _ptr(bias, "bias", (torch.float32,), (E,)),
+        _ptr(w_gate, "w_gate", _BF16, (E, I, H)), _ptr(w_up, "w_up", _BF16, (E, I, H)),
+        _ptr(w_down, "w_down", _BF16, (E, H, I)), M, H, I, E, k,
+        _ptr(xn, "x_norm", _BF16, (M, H)),
+        _ptr(idx, "topk_idx", (torch.int32,), (M, k)),
+        _ptr(w, "topk_w", (torch.float32,), (M, k)),
+        _ptr(o, "out", (torch.float32,), (M, H)), _ptr(ws, "workspace"), ws.numel(), st))
+    return xn, idx, w, o

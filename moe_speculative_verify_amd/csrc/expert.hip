@@ -659,7 +659,10 @@ moe_status_t route_check(const uint16_t *x, const uint16_t *w_router,
 moe_status_t route_enqueue(const uint16_t *x, const uint16_t *w_router,
                            const float *bias, int32_t M, int32_t H, int32_t E,
                            int32_t k, int32_t *topk_idx, float *topk_w,
-                           float *logits, void *ws, hipStream_t st);
+                           float *logits, void *ws, hipStream_t st,
+                           const uint16_t *gamma, float eps, uint16_t *x_norm);
+moe_status_t norm_check(const uint16_t *gamma, float eps, const uint16_t *x_norm,
+                        int32_t M, int32_t H);
 
 } // namespace mv
 
@@ -731,9 +734,46 @@ extern "C" moe_status_t moe_layer(const uint16_t *x, const uint16_t *w_router,
     const size_t r = moe_route_workspace_bytes(M, E);
     hipStream_t st = (hipStream_t)stream;
     s = route_enqueue(x, w_router, bias, M, H, E, k, topk_idx, topk_w, nullptr,
-                      workspace, st);
+                      workspace, st, nullptr, 0.0f, nullptr);
     if (s != MOE_OK)
         return s;
     return ffn_enqueue(x, topk_idx, topk_w, w_gate, w_up, w_down, M, H, I, E, k,
+                       out, (char *)workspace + r, st);
+}
+
+extern "C" moe_status_t moe_layer_rmsnorm(const uint16_t *h, const uint16_t *gamma,
+                                          float eps, const uint16_t *w_router,
+                                          const float *bias, const uint16_t *w_gate,
+                                          const uint16_t *w_up, const uint16_t *w_down,
+                                          int32_t M, int32_t H, int32_t I, int32_t E,
+                                          int32_t k, uint16_t *x_norm, int32_t *topk_idx,
+                                          float *topk_w, float *out, void *workspace,
+                                          size_t workspace_bytes, void *stream)
+{
+    moe_status_t s = route_check(h, w_router, bias, M, H, E, k, topk_idx, topk_w,
+                                 nullptr);
+    if (s != MOE_OK)
+        return s;
+    s = norm_check(gamma, eps, x_norm, M, H);
+    if (s != MOE_OK)
+        return s;
+    s = ffn_check(x_norm, topk_idx, topk_w, w_gate, w_up, w_down, M, H, I, E, k, out);
+    if (s != MOE_OK)
+        return s;
+    if (!workspace)
+        return MOE_ERR_NULL;
+    if (!aligned16(workspace))
+        return MOE_ERR_ALIGN;
+    if (workspace_bytes < moe_layer_workspace_bytes(M, H, I, E, k))
+        return MOE_ERR_WORKSPACE;
+    // the route kernel writes the normalised rows; the expert kernels read
+    // them after the kernel boundary
+    const size_t r = moe_route_workspace_bytes(M, E);
+    hipStream_t st = (hipStream_t)stream;
+    s = route_enqueue(h, w_router, bias, M, H, E, k, topk_idx, topk_w, nullptr,
+                      workspace, st, gamma, eps, x_norm);
+    if (s != MOE_OK)
+        return s;
+    return ffn_enqueue(x_norm, topk_idx, topk_w, w_gate, w_up, w_down, M, H, I, E, k,
                        out, (char *)workspace + r, st);
 }

@@ -24,6 +24,14 @@
 //     advances the winning lane's list. All loads are unpredicated and every
 //     step is branch-free apart from uniform tie checks. The softmax of the
 //     selected logits is taken in fp32.
+//   - moe_route_rmsnorm puts the chain's norm in front (Fig. 7: norm -> gate
+//     matvec -> top-k), read as RMSNorm with a per-column gain: every
+//     workgroup already holds each (token, column) of the hidden states in
+//     exactly one lane, so the sum of squares is taken from those registers
+//     (per lane in step order, then over the lanes of a token in a fixed
+//     order through LDS), each lane scales its chunks and rounds them once to
+//     bf16 before the MFMAs, and workgroup 0 writes the normalised rows for
+//     the expert kernels. Every workgroup computes the same bits.
 #include "common.h"
 
 #include <utility>
@@ -31,6 +39,7 @@
 namespace mv {
 
 constexpr int kRouteWaves = 8;              // wavefronts per workgroup
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // ---- per-lane sorted lists of 64-bit selection keys (order code of the
 // logit << 32 | ~id: a larger key is a larger logit, or an equal logit with
@@ -124,16 +133,37 @@ __device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
 // 0-7 carry block X, tile rows 8-15 and tokens 8-15 carry block Y (the same
 // router rows and tokens), so D[r][t] + D[8+r][8+t] is the dot product over
 // 64 columns and every lane loads distinct data.
-template <int S, int KJ, int RT, int P>
+// bf16(x * gain * inv) for eight elements: x * gain is exact in fp32 (two
+// 8-bit significands), then one product and one rounding to bf16
+// (v_cvt_pk_bf16_f32: nearest, ties to even, in the default mode)
+__device__ __forceinline__ u32x4 rmsnorm8_bf16(u32x4 v, u32x4 g, float inv)
+{
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float xl = __builtin_bit_cast(float, v[i] << 16);
+        const float xh = __builtin_bit_cast(float, v[i] & 0xFFFF0000u);
+        const float gl = __builtin_bit_cast(float, g[i] << 16);
+        const float gh = __builtin_bit_cast(float, g[i] & 0xFFFF0000u);
+        const f32x2 y = {(xl * gl) * inv, (xh * gh) * inv};
+        r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(y, bf16x2));
+    }
+    return r;
+}
+
+template <int S, int KJ, int RT, int P, bool NORM>
 __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ wr,
     const float *__restrict__ bias, int M, int H, int E, int k,
     float *__restrict__ logits, int *__restrict__ topk_idx,
-    float *__restrict__ topk_w, unsigned *__restrict__ ticket)
+    float *__restrict__ topk_w, unsigned *__restrict__ ticket,
+    const u32x4 *__restrict__ gamma, float eps, u32x4 *__restrict__ xn_out)
 {
     static_assert(RT == 8 || RT == 16, "tile rows");
     static_assert(P == 1 || (P == 2 && RT == 8), "block-diagonal packing needs 8-row tiles");
+    static_assert(!NORM || S <= 16, "the norm needs every hidden-state chunk in registers at once");
     __shared__ f32x4 s_part[kRouteWaves][kWave];
+    __shared__ float s_ss[NORM ? kRouteWaves : 1][kWave];
     __shared__ int s_last;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -162,9 +192,10 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     constexpr int SPH = S < 16 ? S : 16;
     static_assert(S % SPH == 0, "steps per phase");
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    u32x4 xn_keep[NORM ? SPH : 1];               // the normalised chunks, stored late
 #pragma unroll
     for (int ph = 0; ph < S; ph += SPH) {
-        u32x4 a[SPH], b[SPH];
+        u32x4 a[SPH], b[SPH], gm[NORM ? SPH : 1];
 #pragma unroll
         for (int s = 0; s < SPH; ++s) {
             const int c = cbase + 4 * P * (ph + s);
@@ -174,8 +205,39 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
         for (int s = 0; s < SPH; ++s) {
             const int c = cbase + 4 * P * (ph + s);
             b[s] = bp[c < nch ? c : nch - 1];
+            if constexpr (NORM)
+                gm[s] = gamma[c < nch ? c : nch - 1];
         }
         wait_vmcnt<0>();
+        if constexpr (NORM) {
+            // this lane's squares in step order; then, in every wavefront,
+            // each lane adds the eight wavefronts' values of its own lane
+            // slot, and an xor butterfly over the lanes that hold the same
+            // token (j = t and, packed, t + 8; every g) completes the row:
+            // one fixed order, the same in every lane and workgroup
+            float ss = 0.0f;
+#pragma unroll
+            for (int s = 0; s < SPH; ++s) {
+                const float q = dot8_bf16(b[s], b[s], 0.0f);   // v_dot2_f32_bf16
+                ss += cbase + 4 * P * (ph + s) < nch ? q : 0.0f;
+            }
+            s_ss[wave][lane] = ss;
+            __syncthreads();
+            float tot = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kRouteWaves; ++w)
+                tot += s_ss[w][lane];
+            if (P == 2)
+                tot += __shfl_xor(tot, 8);
+            tot += __shfl_xor(tot, 16);
+            tot += __shfl_xor(tot, 32);
+            const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+#pragma unroll
+            for (int s = 0; s < SPH; ++s) {
+                b[s] = rmsnorm8_bf16(b[s], gm[s], inv);
+                xn_keep[s] = b[s];
+            }
+        }
         // partial tile over this wavefront's columns
 #pragma unroll
         for (int s = 0; s < SPH; ++s) {
@@ -218,6 +280,19 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
         s_last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
     __syncthreads();
+    if constexpr (NORM) {
+        // workgroup 0 writes the normalised rows for the expert kernels only
+        // now: they must land by the end of the kernel, not before the
+        // ticket, so their latency overlaps the selection
+        if (blockIdx.x == 0 && (P == 2 ? (j & 7) : j) < M) {
+#pragma unroll
+            for (int s = 0; s < SPH; ++s) {
+                const int c = cbase + 4 * P * s;
+                if (c < nch)
+                    xn_out[(size_t)tok * nch + c] = xn_keep[s];
+            }
+        }
+    }
     if (!s_last)
         return;
     if (threadIdx.x == 0)
@@ -264,16 +339,35 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     }
 }
 
+// the optional norm: gain [H] bf16, eps, normalised rows out [M,H] bf16
+struct RouteNorm {
+    const uint16_t *gamma;
+    float eps;
+    uint16_t *xn;
+};
+
 template <int S, int KJ, int P>
 static moe_status_t launch_route3(const uint16_t *x, const uint16_t *w, const float *bias,
                                   int M, int H, int E, int k, float *logits, int *idx,
-                                  float *tw, unsigned *ticket, hipStream_t st)
+                                  float *tw, unsigned *ticket, const RouteNorm &nm,
+                                  hipStream_t st)
 {
     constexpr int RT = 8;
     const int grid = (E + RT - 1) / RT;
-    hipLaunchKernelGGL((route_kernel<S, KJ, RT, P>), dim3(grid), dim3(kRouteWaves * kWave), 0,
-                       st, (const u32x4 *)x, (const u32x4 *)w, bias, M, H, E, k, logits,
-                       idx, tw, ticket);
+    if (nm.gamma) {
+        if constexpr (S <= 16)
+            hipLaunchKernelGGL((route_kernel<S, KJ, RT, P, true>), dim3(grid),
+                               dim3(kRouteWaves * kWave), 0, st, (const u32x4 *)x,
+                               (const u32x4 *)w, bias, M, H, E, k, logits, idx, tw, ticket,
+                               (const u32x4 *)nm.gamma, nm.eps, (u32x4 *)nm.xn);
+        else
+            return MOE_ERR_UNSUPPORTED;
+    } else {
+        hipLaunchKernelGGL((route_kernel<S, KJ, RT, P, false>), dim3(grid),
+                           dim3(kRouteWaves * kWave), 0, st, (const u32x4 *)x,
+                           (const u32x4 *)w, bias, M, H, E, k, logits, idx, tw, ticket,
+                           nullptr, 0.0f, nullptr);
+    }
     return check_launch();
 }
 
@@ -281,25 +375,28 @@ static moe_status_t launch_route3(const uint16_t *x, const uint16_t *w, const fl
 template <int S, int KJ>
 static moe_status_t launch_route2(const uint16_t *x, const uint16_t *w, const float *bias,
                                   int M, int H, int E, int k, float *logits, int *idx,
-                                  float *tw, unsigned *ticket, hipStream_t st)
+                                  float *tw, unsigned *ticket, const RouteNorm &nm,
+                                  hipStream_t st)
 {
     if (M <= 8)
-        return launch_route3<(S + 1) / 2, KJ, 2>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
-    return launch_route3<S, KJ, 1>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
+        return launch_route3<(S + 1) / 2, KJ, 2>(x, w, bias, M, H, E, k, logits, idx, tw,
+                                                 ticket, nm, st);
+    return launch_route3<S, KJ, 1>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, nm, st);
 }
 
 template <int S>
 static moe_status_t launch_route(const uint16_t *x, const uint16_t *w, const float *bias,
                                  int M, int H, int E, int k, float *logits, int *idx,
-                                 float *tw, unsigned *ticket, hipStream_t st)
+                                 float *tw, unsigned *ticket, const RouteNorm &nm,
+                                 hipStream_t st)
 {
     if (E <= 128)
-        return launch_route2<S, 2>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
+        return launch_route2<S, 2>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, nm, st);
     if (E <= 256)
-        return launch_route2<S, 4>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
+        return launch_route2<S, 4>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, nm, st);
     if (E <= 512)
-        return launch_route2<S, 8>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
-    return launch_route2<S, 16>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, st);
+        return launch_route2<S, 8>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, nm, st);
+    return launch_route2<S, 16>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, nm, st);
 }
 
 // Workspace: the header (ticket), then [M,E] fp32 logits scratch.
@@ -308,24 +405,52 @@ static size_t route_ws_logits(int32_t M, int32_t E)
     return align_up((size_t)M * (size_t)E * sizeof(float), 256);
 }
 
+// MFMA steps per wavefront: eight wavefronts of 32-column steps
+static int route_need(int H)
+{
+    return (H / 8 + 4 * kRouteWaves - 1) / (4 * kRouteWaves);
+}
+
+// the norm needs every chunk of a lane in registers at once: at most 16
+// MFMA steps per lane (always true when two blocks pack, M <= 8)
+bool route_norm_supported(int32_t M, int32_t H)
+{
+    return M <= 8 || route_need(H) <= 16;
+}
+
 moe_status_t route_enqueue(const uint16_t *x, const uint16_t *w_router,
                            const float *bias, int32_t M, int32_t H, int32_t E,
                            int32_t k, int32_t *topk_idx, float *topk_w,
-                           float *logits, void *ws, hipStream_t st)
+                           float *logits, void *ws, hipStream_t st,
+                           const uint16_t *gamma, float eps, uint16_t *x_norm)
 {
     unsigned *ticket = (unsigned *)ws;
     float *lg = logits ? logits : (float *)((char *)ws + kWsHeader);
-    // MFMA steps per wavefront: eight wavefronts of 32-column steps
-    const int need = (H / 8 + 4 * kRouteWaves - 1) / (4 * kRouteWaves);
+    const RouteNorm nm{gamma, eps, x_norm};
+    const int need = route_need(H);
     if (need <= 2)
-        return launch_route<2>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
+        return launch_route<2>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, nm, st);
     if (need <= 4)
-        return launch_route<4>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
+        return launch_route<4>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, nm, st);
     if (need <= 10)
-        return launch_route<10>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
+        return launch_route<10>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, nm, st);
     if (need <= 16)
-        return launch_route<16>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
-    return launch_route<32>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, st);
+        return launch_route<16>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, nm, st);
+    return launch_route<32>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, nm, st);
+}
+
+moe_status_t norm_check(const uint16_t *gamma, float eps, const uint16_t *x_norm,
+                        int32_t M, int32_t H)
+{
+    if (!gamma || !x_norm)
+        return MOE_ERR_NULL;
+    if (!(eps >= 0.0f) || eps == INFINITY)
+        return MOE_ERR_SHAPE;
+    if (!aligned16(gamma) || !aligned16(x_norm))
+        return MOE_ERR_ALIGN;
+    if (!route_norm_supported(M, H))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
 }
 
 moe_status_t route_check(const uint16_t *x, const uint16_t *w_router,
@@ -372,5 +497,29 @@ extern "C" moe_status_t moe_route(const uint16_t *x, const uint16_t *w_router,
     if (workspace_bytes < moe_route_workspace_bytes(M, E))
         return MOE_ERR_WORKSPACE;
     return route_enqueue(x, w_router, bias, M, H, E, k, topk_idx, topk_w, logits,
-                         workspace, (hipStream_t)stream);
+                         workspace, (hipStream_t)stream, nullptr, 0.0f, nullptr);
+}
+
+extern "C" moe_status_t moe_route_rmsnorm(const uint16_t *h, const uint16_t *gamma,
+                                          float eps, const uint16_t *w_router,
+                                          const float *bias, int32_t M, int32_t H,
+                                          int32_t E, int32_t k, uint16_t *x_norm,
+                                          int32_t *topk_idx, float *topk_w, float *logits,
+                                          void *workspace, size_t workspace_bytes,
+                                          void *stream)
+{
+    moe_status_t s = route_check(h, w_router, bias, M, H, E, k, topk_idx, topk_w, logits);
+    if (s != MOE_OK)
+        return s;
+    s = norm_check(gamma, eps, x_norm, M, H);
+    if (s != MOE_OK)
+        return s;
+    if (!workspace)
+        return MOE_ERR_NULL;
+    if (!aligned16(workspace))
+        return MOE_ERR_ALIGN;
+    if (workspace_bytes < moe_route_workspace_bytes(M, E))
+        return MOE_ERR_WORKSPACE;
+    return route_enqueue(h, w_router, bias, M, H, E, k, topk_idx, topk_w, logits,
+                         workspace, (hipStream_t)stream, gamma, eps, x_norm);
 }

@@ -75,6 +75,20 @@ def activations(M: int, H: int, seed: int = ACT_SEED, tag: int = 0) -> np.ndarra
     return normal_bf16((M, H), ACT_STD, seed, 1000 + tag, M, H)
 
 
+def hidden_states(M: int, H: int, seed: int = ACT_SEED, tag: int = 0,
+                  std: float = 3.0) -> np.ndarray:
+    """Hidden states before the router chain's norm [M,H]: N(0, std^2) in
+    bf16 (a residual stream whose scale the norm removes)."""
+    return normal_bf16((M, H), std, seed, 2000 + tag, M, H)
+
+
+def norm_gain(H: int, seed: int = WEIGHT_SEED, layer: int = 0) -> np.ndarray:
+    """Per-column gain of the norm [H]: 1 + N(0, 0.1^2), in bf16."""
+    g = rng(seed, layer, 97, H)
+    v = np.float32(1.0) + g.standard_normal(size=H, dtype=np.float32) * np.float32(0.1)
+    return bf16_bits(v)
+
+
 def zipf_bias(E: int, alpha: float, seed: int = ZIPF_SEED, s: float = ZIPF_S) -> np.ndarray:
     """Router bias whose exponential follows a Zipf(s) popularity.
 

@@ -158,3 +158,32 @@ def test_binding_refuses_host_tensors(L):
     w = torch.zeros((16, 256), dtype=torch.bfloat16)
     with pytest.raises((ValueError, RuntimeError, AssertionError)):
         mv.moe_route(x, w, 2)
+
+
+def test_rmsnorm_checks(L):
+    import ctypes as C
+    def rn(h=A, g=A, eps=1e-6, w=A, bias=None, M=6, H=2560, E=512, k=8, xn=B, idx=A, tw=A,
+           lg=None, ws=B, wsb=1 << 20):
+        return L.moe_route_rmsnorm(h, g, C.c_float(eps), w, bias, M, H, E, k, xn, idx, tw, lg,
+                                   ws, wsb, None)
+    assert rn(g=None) == NULL
+    assert rn(xn=None) == NULL
+    assert rn(h=None) == NULL
+    assert rn(eps=-1.0) == SHAPE
+    assert rn(eps=float("nan")) == SHAPE
+    assert rn(eps=float("inf")) == SHAPE
+    assert rn(g=A + 8) == ALIGN
+    assert rn(xn=B + 4) == ALIGN
+    assert rn(M=9, H=8192) == UNSUP
+    assert rn(wsb=16) == WS
+
+    def ln(h=A, g=A, eps=1e-6, xn=B, M=6, H=2560, I=1024, E=512, k=8, ws=B, wsb=1 << 30):
+        return L.moe_layer_rmsnorm(h, g, C.c_float(eps), A, None, A, A, A, M, H, I, E, k, xn,
+                                   A, A, A, ws, wsb, None)
+    assert ln(g=None) == NULL
+    assert ln(xn=None) == NULL
+    assert ln(eps=-0.5) == SHAPE
+    assert ln(g=A + 4) == ALIGN
+    assert ln(M=9, H=8192) == UNSUP
+    assert ln(I=1004) == UNSUP
+    assert ln(wsb=16) == WS
