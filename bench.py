@@ -177,6 +177,10 @@ def main():
             gate=synth.device_normal_bf16((E, I, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, l, K_["gate"]),
             up=synth.device_normal_bf16((E, I, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, l, K_["up"]),
             down=synth.device_normal_bf16((E, H, I), synth.WEIGHT_STD, synth.WEIGHT_SEED, l, K_["down"]),
+            # one shared expert per layer (the shared-expert variant's extra bucket)
+            s_gate=synth.device_normal_bf16((I, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, l, 50 + K_["gate"]),
+            s_up=synth.device_normal_bf16((I, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, l, 50 + K_["up"]),
+            s_down=synth.device_normal_bf16((H, I), synth.WEIGHT_STD, synth.WEIGHT_SEED, l, 50 + K_["down"]),
         ))
         log(f"layer {l} weights generated ({time.time() - t0:.1f} s)")
     lms = [synth.device_normal_bf16((V, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 100 + c,
@@ -339,7 +343,7 @@ def main():
     # layer step at the other verify widths of the workload, uniform and
     # Zipf-biased routing (same 16 rotating layers, cold); with norm=True the
     # router chain's norm runs in front (moe_layer_rmsnorm)
-    def layer_at(Ms, alpha, steps=32, warm=8, norm=False):
+    def layer_at(Ms, alpha, steps=32, warm=8, norm=False, shared=False):
         xs = up(synth.activations(Ms, H, seed=synth.ACT_SEED, tag=10 + Ms))
         bs = None if alpha is None else torch.from_numpy(synth.zipf_bias(E, alpha)).to(dev)
         ids = torch.empty((Ms, k), dtype=torch.int32, device=dev)
@@ -355,6 +359,13 @@ def main():
                   Ms, H, I, E, k, xns.data_ptr(), ids.data_ptr(), tws.data_ptr(),
                   outs.data_ptr(), ws.data_ptr(), ws.numel(), stream) for Lw in layers]
             fn = L.moe_layer_rmsnorm
+        elif shared:
+            a = [(xs.data_ptr(), Lw["router"].data_ptr(), bs.data_ptr() if bs is not None else None,
+                  Lw["gate"].data_ptr(), Lw["up"].data_ptr(), Lw["down"].data_ptr(),
+                  Lw["s_gate"].data_ptr(), Lw["s_up"].data_ptr(), Lw["s_down"].data_ptr(),
+                  Ms, H, I, E, k, ids.data_ptr(), tws.data_ptr(), outs.data_ptr(),
+                  ws.data_ptr(), ws.numel(), stream) for Lw in layers]
+            fn = L.moe_layer_shared
         else:
             a = [(xs.data_ptr(), Lw["router"].data_ptr(), bs.data_ptr() if bs is not None else None,
                   Lw["gate"].data_ptr(), Lw["up"].data_ptr(), Lw["down"].data_ptr(),
@@ -379,15 +390,20 @@ def main():
         ev[steps].record()
         torch.cuda.synchronize()
         us = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) * 1e3 / steps
-        byts = sum(E * H * 2 + Ds[(warm + i) % nl] * per_expert + io for i in range(steps)) / steps
+        byts = sum(E * H * 2 + (Ds[(warm + i) % nl] + (1 if shared else 0)) * per_expert + io
+                   for i in range(steps)) / steps
         gbps = byts / (us * 1e-6) / 1e9
-        return {"M": Ms, "zipf_alpha": alpha, "rmsnorm": norm, "us": round(us, 2),
+        return {"M": Ms, "zipf_alpha": alpha, "rmsnorm": norm, "shared_expert": shared,
+                "us": round(us, 2),
                 "GBps": round(gbps, 1),
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes": int(byts),
                 "distinct_experts_mean": sum(Ds) / len(Ds)}
 
     layer_sweep = [layer_at(m, a) for m, a in ((1, None), (1, 1.0), (16, None), (16, 1.0))]
     layer_norm = layer_at(M, args.zipf_alpha, norm=True)
+    layer_shared = [layer_at(m, args.zipf_alpha, shared=True) for m in (1, M, 16)]
+    log("layer with a shared expert: " + ", ".join(f"M={r['M']}: {r['us']} us ({r['frac']:.1%})"
+                                                  for r in layer_shared))
     log(f"router chain with norm: gate {route_norm_us:.2f} us (without {route_us:.2f}); "
         f"layer M={M} {layer_norm['us']} us")
     log("layer sweep: " + ", ".join(f"M={r['M']} alpha={r['zipf_alpha']}: {r['us']} us "
@@ -464,6 +480,7 @@ def main():
         "moe_layer_other_widths": layer_sweep,
         "router_chain_rmsnorm": {"gate_us": round(route_norm_us, 2),
                                  "moe_layer_rmsnorm": layer_norm},
+        "moe_layer_shared_expert": layer_shared,
         "roofline": {"kernel": "lmhead_kernel (lmhead_greedy_verify)", "bound": "hbm",
                      "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},

@@ -162,6 +162,35 @@ moe_status_t moe_expert_ffn(const uint16_t *x, const int32_t *topk_idx,
                             size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * moe_expert_ffn_shared -- moe_expert_ffn plus one shared expert that every
+ * token uses with weight 1, streamed in the same launches as one more bucket
+ * of the grouping (the "513-expert" MoE decode of section "Two fusions and a
+ * retune": 512 routed experts and one more). The shared expert's form is a
+ * reading: a SwiGLU FFN of the routed experts' shape, no gate on its output.
+ *
+ *   x, topk_idx, topk_w, w_gate, w_up, w_down, M, H, I, E, k, workspace:
+ *                           as moe_expert_ffn (same workspace size)
+ *   w_gate_shared [I,H] bf16, w_up_shared [I,H] bf16, w_down_shared [H,I]
+ *                           bf16: the shared expert (16-byte aligned)
+ *   out      [M,H]   fp32   out (overwritten): moe_expert_ffn's sum over the
+ *                           k slots in order, then + the shared expert's
+ *                           W_down_s (silu(W_gate_s x_t) * (W_up_s x_t)),
+ *                           same rounding rules
+ * Errors: as moe_expert_ffn; MOE_ERR_NULL for a NULL shared tensor,
+ * MOE_ERR_ALIGN for a misaligned one, MOE_ERR_UNSUPPORTED when
+ * M * (k + 1) > 256 or E > 1023.
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_expert_ffn_shared(const uint16_t *x, const int32_t *topk_idx,
+                                   const float *topk_w, const uint16_t *w_gate,
+                                   const uint16_t *w_up, const uint16_t *w_down,
+                                   const uint16_t *w_gate_shared,
+                                   const uint16_t *w_up_shared,
+                                   const uint16_t *w_down_shared, int32_t M,
+                                   int32_t H, int32_t I, int32_t E, int32_t k,
+                                   float *out, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
  * moe_layer -- one MoE layer verify step: moe_route then moe_expert_ffn,
  * enqueued back to back on `stream` (same arguments and results as the two
  * calls; topk_idx/topk_w are written and then consumed on the device).
@@ -175,6 +204,21 @@ moe_status_t moe_layer(const uint16_t *x, const uint16_t *w_router,
                        int32_t M, int32_t H, int32_t I, int32_t E, int32_t k,
                        int32_t *topk_idx, float *topk_w, float *out,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_layer_shared -- moe_route then moe_expert_ffn_shared on one stream.
+ *   Arguments as moe_layer, plus the shared expert's three tensors as in
+ *   moe_expert_ffn_shared. Workspace: moe_layer_workspace_bytes.
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_layer_shared(const uint16_t *x, const uint16_t *w_router,
+                              const float *bias, const uint16_t *w_gate,
+                              const uint16_t *w_up, const uint16_t *w_down,
+                              const uint16_t *w_gate_shared,
+                              const uint16_t *w_up_shared,
+                              const uint16_t *w_down_shared, int32_t M, int32_t H,
+                              int32_t I, int32_t E, int32_t k, int32_t *topk_idx,
+                              float *topk_w, float *out, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * moe_layer_rmsnorm -- moe_route_rmsnorm then moe_expert_ffn on the

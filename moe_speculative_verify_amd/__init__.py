@@ -25,8 +25,9 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPP
 #: every symbol the header declares
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_clear",
            "moe_route_workspace_bytes", "moe_route", "moe_route_rmsnorm",
-           "moe_expert_ffn_workspace_bytes", "moe_expert_ffn",
+           "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_expert_ffn_shared",
            "moe_layer_workspace_bytes", "moe_layer", "moe_layer_rmsnorm",
+           "moe_layer_shared",
            "lmhead_argmax_workspace_bytes", "lmhead_argmax", "lmhead_greedy_verify")
 
 
@@ -67,6 +68,10 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_rmsnorm.restype = ctypes.c_int32
         L.moe_layer_rmsnorm.argtypes = [_P, _P, ctypes.c_float, _P, _P, _P, _P, _P,
                                         _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _S, _P]
+        L.moe_expert_ffn_shared.restype = ctypes.c_int32
+        L.moe_expert_ffn_shared.argtypes = [_P] * 9 + [_I] * 5 + [_P, _P, _S, _P]
+        L.moe_layer_shared.restype = ctypes.c_int32
+        L.moe_layer_shared.argtypes = [_P] * 9 + [_I] * 5 + [_P, _P, _P, _P, _S, _P]
         L.moe_expert_ffn_workspace_bytes.restype = _S
         L.moe_expert_ffn_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
         L.moe_expert_ffn.restype = ctypes.c_int32
@@ -353,3 +358,57 @@ def moe_layer_rmsnorm(h, gamma, eps: float, w_router, w_gate, w_up, w_down, k: i
         _ptr(w, "topk_w", (torch.float32,), (M, k)),
         _ptr(o, "out", (torch.float32,), (M, H)), _ptr(ws, "workspace"), ws.numel(), st))
     return xn, idx, w, o
+
+
+def moe_expert_ffn_shared(x, topk_idx, topk_w, w_gate, w_up, w_down, w_gate_shared,
+                          w_up_shared, w_down_shared, *, out=None, workspace=None, stream=None):
+    """Selected experts' SwiGLU FFN + combine, plus one shared expert with
+    weight 1. Returns out [M,H] fp32."""
+    M, H = x.shape
+    _, k = topk_idx.shape
+    E, I, _ = w_gate.shape
+    dev = x.device
+    o = out if out is not None else torch.empty((M, H), dtype=torch.float32, device=dev)
+    st = _stream(stream)
+    nbytes = moe_expert_ffn_workspace_bytes(M, H, I, E, k)
+    ws = workspace if workspace is not None else Workspace.get("ffn", nbytes, dev, st)
+    _check("moe_expert_ffn_shared", lib().moe_expert_ffn_shared(
+        _ptr(x, "x", _BF16), _ptr(topk_idx, "topk_idx", (torch.int32,), (M, k)),
+        _ptr(topk_w, "topk_w", (torch.float32,), (M, k)),
+        _ptr(w_gate, "w_gate", _BF16, (E, I, H)), _ptr(w_up, "w_up", _BF16, (E, I, H)),
+        _ptr(w_down, "w_down", _BF16, (E, H, I)),
+        _ptr(w_gate_shared, "w_gate_shared", _BF16, (I, H)),
+        _ptr(w_up_shared, "w_up_shared", _BF16, (I, H)),
+        _ptr(w_down_shared, "w_down_shared", _BF16, (H, I)), M, H, I, E, k,
+        _ptr(o, "out", (torch.float32,), (M, H)), _ptr(ws, "workspace"), ws.numel(), st))
+    return o
+
+
+def moe_layer_shared(x, w_router, w_gate, w_up, w_down, w_gate_shared, w_up_shared,
+                     w_down_shared, k: int, bias=None, *, out=None, workspace=None, stream=None):
+    """Route + expert FFN with one shared expert. Returns (topk_idx, topk_w, out)."""
+    M, H = x.shape
+    E, I, _ = w_gate.shape
+    dev = x.device
+    idx, w, o = out if out is not None else (None, None, None)
+    if idx is None:
+        idx = torch.empty((M, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((M, k), dtype=torch.float32, device=dev)
+    if o is None:
+        o = torch.empty((M, H), dtype=torch.float32, device=dev)
+    st = _stream(stream)
+    nbytes = moe_layer_workspace_bytes(M, H, I, E, k)
+    ws = workspace if workspace is not None else Workspace.get("layer", nbytes, dev, st)
+    _check("moe_layer_shared", lib().moe_layer_shared(
+        _ptr(x, "x", _BF16), _ptr(w_router, "w_router", _BF16, (E, H)),
+        _ptr(bias, "bias", (torch.float32,), (E,)),
+        _ptr(w_gate, "w_gate", _BF16, (E, I, H)), _ptr(w_up, "w_up", _BF16, (E, I, H)),
+        _ptr(w_down, "w_down", _BF16, (E, H, I)),
+        _ptr(w_gate_shared, "w_gate_shared", _BF16, (I, H)),
+        _ptr(w_up_shared, "w_up_shared", _BF16, (I, H)),
+        _ptr(w_down_shared, "w_down_shared", _BF16, (H, I)), M, H, I, E, k,
+        _ptr(idx, "topk_idx", (torch.int32,), (M, k)),
+        _ptr(w, "topk_w", (torch.float32,), (M, k)),
+        _ptr(o, "out", (torch.float32,), (M, H)), _ptr(ws, "workspace"), ws.numel(), st))
+    return idx, w, o

@@ -31,6 +31,13 @@
 // L2; its summation order differs, so batch invariance holds within each of
 // the two regimes. Every workgroup rebuilds the pair grouping in LDS from
 // topk_idx, which costs less than a separate launch.
+//
+// The shared-expert entry points (moe_expert_ffn_shared, moe_layer_shared)
+// add one always-active expert per layer as one more bucket of the same
+// grouping: pair M*k + t is token t's pair with it (a virtual expert id E,
+// its own weight tensors, weight 1.0, added after the routed slots), so the
+// same up and down launches stream it with the routed experts (the post's
+// "513-expert" MoE decode, section "Two fusions and a retune").
 #include "common.h"
 
 #include <mutex>
@@ -52,6 +59,18 @@ static_assert(kXThreads == kGroupThreads, "grouping needs one thread per histogr
 // register so that control flow and addresses built from it stay scalar.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Pairs: p < NP = M*k are routed (token p / k, slot p % k); with a shared
+// expert (ns = 1) p = NP + t is token t's pair with it, expert id E.
+__device__ __forceinline__ int pair_token(int p, int NP, int k)
+{
+    return p < NP ? p / k : p - NP;
+}
+__device__ __forceinline__ int pair_expert(const int *__restrict__ topk_idx, int p, int NP,
+                                           int NPT, int E)
+{
+    return p < NP ? topk_idx[p] : (p < NPT ? E : -1);
+}
+
 
 // ----------------------------------------------------------------- down
 // Workgroup b owns R output rows r0 .. r0+R-1 for every expert; its
@@ -64,8 +83,9 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 template <int R, int NB>
 __global__ __launch_bounds__(kXThreads) void expert_down_kernel(
     const u32x4 *__restrict__ act, const int *__restrict__ topk_idx,
-    const float *__restrict__ topk_w, const u32x4 *__restrict__ wd, int M, int H,
-    int I, int E, int k, float *__restrict__ out)
+    const float *__restrict__ topk_w, const u32x4 *__restrict__ wd,
+    const u32x4 *__restrict__ wds, int M, int H, int I, int E, int k, int ns,
+    float *__restrict__ out)
 {
     constexpr int kBlk = R * kXRowPitch;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -77,9 +97,14 @@ __global__ __launch_bounds__(kXThreads) void expert_down_kernel(
     const int r0 = blockIdx.x * R;
     const int nr = min(R, H - r0);
     unsigned char *ring = smem + wave * NB * kBlk;
-    float *y_s = (float *)(smem + kXWaves * NB * kBlk);  // [NP][R]
+    float *y_s = (float *)(smem + kXWaves * NB * kBlk);  // [NPT][R]
+    const int NP = M * k, NPT = NP + ns * M;
 
-    build_groups(topk_idx, M * k, E, g);
+    {
+        const int id = pair_expert(topk_idx, threadIdx.x, NP, NPT, E);
+        groups_set_pairs(id, NPT, E + ns, g);
+        groups_finish(NPT, g);
+    }
 
     const int DV = uniform(g.DV);
     const int nv = DV > wave ? (DV - wave + kXWaves - 1) / kXWaves : 0;
@@ -92,14 +117,14 @@ __global__ __launch_bounds__(kXThreads) void expert_down_kernel(
     // the sequence the same number of loads reads a cached dummy (act,
     // clamped) into a slot nobody reads: every iteration then has the same
     // loads in flight and waits on one constant count.
-    const int NP = M * k;
-    const u32x4 *dummy = act + min(lane, NP * nch - 1);
+    const u32x4 *dummy = act + min(lane, NPT * nch - 1);
     auto issue = [&](int X) {
         const bool real = X < nblk;
         const int Xr = real ? X : 0;
         const int v = wave + kXWaves * (Xr / nkb), kb = Xr % nkb;
         unsigned char *slot = ring + (X % NB) * kBlk;
-        const u32x4 *base = wd + (size_t)uniform(g.vexp[min(v, kMaxNP - 1)]) * H * nch;
+        const int ev = uniform(g.vexp[min(v, kMaxNP - 1)]);
+        const u32x4 *base = ev >= E ? wds : wd + (size_t)ev * H * nch;
         int c = kb * (kXKB / 8) + lane;
         c = c < nch ? c : nch - 1;
 #pragma unroll
@@ -164,6 +189,8 @@ __global__ __launch_bounds__(kXThreads) void expert_down_kernel(
             if (g.e[p] >= 0)
                 sum = fmaf(topk_w[p], y_s[p * R + rr], sum);
         }
+        if (ns)                                          // the shared expert, weight 1
+            sum += y_s[(NP + t) * R + rr];
         out[(size_t)t * H + r0 + rr] = sum;
     }
 }
@@ -218,8 +245,9 @@ __host__ __device__ inline size_t down_gemv_lds_bytes(int R, int NP, int I)
 template <int R, int NB>
 __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
     const u32x4 *__restrict__ act, const int *__restrict__ topk_idx,
-    const float *__restrict__ topk_w, const u32x4 *__restrict__ wd, int M, int H,
-    int I, int E, int k, float *__restrict__ out)
+    const float *__restrict__ topk_w, const u32x4 *__restrict__ wd,
+    const u32x4 *__restrict__ wds, int M, int H, int I, int E, int k, int ns,
+    float *__restrict__ out)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ Groups g;
@@ -228,22 +256,22 @@ __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
     const int nch = I / 8;                               // K = I here
     const int nkb = (nch + kDnCh - 1) / kDnCh;
     const int xs = nkb * kDnCh;                          // LDS activation row, chunks
-    const int NP = M * k;
+    const int NP = M * k, NPT = NP + ns * M;
     const int r0 = blockIdx.x * R;
     const int nr = min(R, H - r0);
-    u32x4 *s_act = (u32x4 *)smem;                        // [NP][xs]
-    float *s_y = (float *)(smem + down_gemv_act_bytes(NP, I));  // [NP][nkb][R]
+    u32x4 *s_act = (u32x4 *)smem;                        // [NPT][xs]
+    float *s_y = (float *)(smem + down_gemv_act_bytes(NPT, I));  // [NPT][nkb][R]
 
     // prologue: pair ids and buckets; then the ring's first weight blocks
     // and every pair's activation row into LDS (direct-to-LDS), so the
     // weights lead the memory queue
-    groups_set_pairs((int)threadIdx.x < NP ? topk_idx[threadIdx.x] : -1, NP, E, g);
+    groups_set_pairs(pair_expert(topk_idx, threadIdx.x, NP, NPT, E), NPT, E + ns, g);
     wait_vmcnt<0>();                                     // only the pair id is in flight
-    for (int i = threadIdx.x; i < NP * (xs - nch); i += blockDim.x) {
+    for (int i = threadIdx.x; i < NPT * (xs - nch); i += blockDim.x) {
         const int p = i / (xs - nch), c = nch + i % (xs - nch);
         s_act[p * xs + c] = u32x4{0, 0, 0, 0};           // K padding reads as zero
     }
-    groups_finish(NP, g);
+    groups_finish(NPT, g);
 
     const int DV = uniform(g.DV);
     const int nv = DV > wave ? (DV - wave + kXWaves - 1) / kXWaves : 0;
@@ -257,8 +285,9 @@ __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
         const bool real = X < nblk;
         const int Xr = real ? X : 0;
         const int v = wave + kXWaves * (Xr / nkb), kb = Xr % nkb;
-        const size_t eoff = (size_t)uniform(g.vexp[min(v, kMaxNP - 1)]) * H * nch;
-        const u32x4 *bp = wd + (real ? eoff : 0);        // uniform
+        const int ev = uniform(g.vexp[min(v, kMaxNP - 1)]);
+        const bool sh = real && ev >= E;                 // the shared expert's slab
+        const u32x4 *bp = (sh ? wds : wd) + (real && !sh ? (size_t)ev * H * nch : 0);
         int c = kb * kDnCh + lane;
         c = c < nch ? c : nch - 1;                       // K tail: zeroed before use
         const int cd = min(lane, nch - 1);
@@ -298,7 +327,7 @@ __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
 #pragma unroll
     for (int q = 0; q < NB - 1; ++q)
         issue(q, w[q]);
-    stage_rows_lds(act, NP, nch, s_act, xs);
+    stage_rows_lds(act, NPT, nch, s_act, xs);
     wait_vmcnt<0>();                                     // this wave's staging has landed
     lds_barrier();                                       // ... and every other wave's staging
     for (int X0 = 0; X0 < nblk; X0 += NB) {
@@ -326,6 +355,13 @@ __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
                 sum = fmaf(topk_w[p], y, sum);
             }
         }
+        if (ns) {                                        // the shared expert, weight 1
+            const int p = NP + t;
+            float y = 0.0f;
+            for (int kb = 0; kb < nkb; ++kb)
+                y += s_y[(p * nkb + kb) * R + rr];
+            sum += y;
+        }
         out[(size_t)t * H + r0 + rr] = sum;
     }
 }
@@ -345,8 +381,9 @@ __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
 template <int KC, int NB>
 __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
     const u32x4 *__restrict__ x, const int *__restrict__ topk_idx,
-    const u32x4 *__restrict__ wg, const u32x4 *__restrict__ wu, int M, int H,
-    int I, int E, int k, uint16_t *__restrict__ act)
+    const u32x4 *__restrict__ wg, const u32x4 *__restrict__ wu,
+    const u32x4 *__restrict__ wgs, const u32x4 *__restrict__ wus, int M, int H,
+    int I, int E, int k, int ns, uint16_t *__restrict__ act)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ Groups g;
@@ -356,16 +393,16 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
     const int nch = H / 8;                               // 16-byte chunks per row
     const int nbu = (nch + KC * kWave - 1) / (KC * kWave);   // K blocks per unit
     const int xs = nbu * KC * kWave;                     // LDS x row, chunks
-    const int NP = M * k;
+    const int NP = M * k, NPT = NP + ns * M;
     u32x4 *s_x = (u32x4 *)smem;                          // [M][xs]
 
-    groups_set_pairs((int)threadIdx.x < NP ? topk_idx[threadIdx.x] : -1, NP, E, g);
+    groups_set_pairs(pair_expert(topk_idx, threadIdx.x, NP, NPT, E), NPT, E + ns, g);
     wait_vmcnt<0>();                                     // only the pair id is in flight
     for (int i = threadIdx.x; i < M * (xs - nch); i += blockDim.x) {
         const int t = i / (xs - nch), c = nch + i % (xs - nch);
         s_x[t * xs + c] = u32x4{0, 0, 0, 0};             // K padding reads as zero
     }
-    groups_finish(NP, g);
+    groups_finish(NPT, g);
 
     // ---- unit u runs on wavefront u mod (4 * gridDim.x), so every
     // wavefront sees every column block and a heavily shared expert's cost
@@ -387,9 +424,11 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
         const bool real = tag >= 0;
         const int u = real ? tag >> 4 : 0, kb = real ? tag & 15 : 0;
         const int v = min(u / I, kMaxNP - 1), i = u % I;
-        const size_t roff = ((size_t)uniform(g.vexp[v]) * I + i) * nch;
-        const u32x4 *bg = wg + (real ? roff : 0);        // uniform
-        const u32x4 *bu = wu + (real ? roff : 0);
+        const int ev = uniform(g.vexp[v]);
+        const bool sh = real && ev >= E;                 // the shared expert's slabs
+        const size_t roff = real ? ((size_t)(sh ? 0 : ev) * I + i) * nch : 0;
+        const u32x4 *bg = (sh ? wgs : wg) + roff;        // uniform
+        const u32x4 *bu = (sh ? wus : wu) + roff;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
             int ch = (kb * KC + c) * kWave + lane;
@@ -415,7 +454,7 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
         }
         for (int jj = 0; jj < npair; ++jj) {
             const int p = uniform(g.sorted[pb + jj]);
-            const u32x4 *xr = s_x + (p / k) * xs + kb * KC * kWave + lane;
+            const u32x4 *xr = s_x + pair_token(p, NP, k) * xs + kb * KC * kWave + lane;
             float ga = 0.0f, ua = 0.0f;
 #pragma unroll
             for (int c = 0; c < KC; ++c) {
@@ -485,14 +524,22 @@ static bool up_gemv_fits(int M, int H)
     return up_gemv_lds_bytes(M, H, up_gemv_kc(H)) <= (size_t)kXLdsDynMax;
 }
 
+// The experts of one call: routed weights and, when ns = 1, the shared
+// expert's (gate [I,H], up [I,H], down [H,I]).
+struct Experts {
+    const uint16_t *wg, *wu, *wd;
+    const uint16_t *wgs, *wus, *wds;
+    int ns;
+};
+
 template <int KC>
-static void launch_up_gemv(const uint16_t *x, const int *idx, const uint16_t *wg,
-                           const uint16_t *wu, int M, int H, int I, int E, int k,
-                           uint16_t *act, hipStream_t st)
+static void launch_up_gemv(const uint16_t *x, const int *idx, const Experts &ex, int M, int H,
+                           int I, int E, int k, uint16_t *act, hipStream_t st)
 {
     hipLaunchKernelGGL((expert_up_gemv_kernel<KC, kUpGemvNB>), dim3(kXGrid), dim3(kXThreads),
                        up_gemv_lds_bytes(M, H, KC), st, (const u32x4 *)x, idx,
-                       (const u32x4 *)wg, (const u32x4 *)wu, M, H, I, E, k, act);
+                       (const u32x4 *)ex.wg, (const u32x4 *)ex.wu, (const u32x4 *)ex.wgs,
+                       (const u32x4 *)ex.wus, M, H, I, E, k, ex.ns, act);
 }
 
 // rows per down workgroup: at least ceil(H / 256), from the instantiated set
@@ -508,26 +555,28 @@ static int down_rows(int H)
 // register ring depth of the GEMV down kernel: R * NB 16-byte loads per lane
 constexpr int down_gemv_nb(int R) { return R <= 10 ? 4 : (R <= 12 ? 3 : 2); }
 // the GEMV down kernel runs when every pair's activation row fits in LDS
-static bool down_gemv_fits(int R, int M, int k, int I)
+// (NPT pairs: M*k routed, plus M with a shared expert)
+static bool down_gemv_fits(int R, int NPT, int I)
 {
-    return down_gemv_lds_bytes(R, M * k, I) <= (size_t)kXLdsDynMax;
+    return down_gemv_lds_bytes(R, NPT, I) <= (size_t)kXLdsDynMax;
 }
-static size_t down_lds_bytes(int R, int NB, int M, int k)
+static size_t down_lds_bytes(int R, int NB, int NPT)
 {
-    return (size_t)kXWaves * NB * R * kXRowPitch + (size_t)M * k * R * sizeof(float);
+    return (size_t)kXWaves * NB * R * kXRowPitch + (size_t)NPT * R * sizeof(float);
 }
-static int down_nb(int R, int M, int k)
+static int down_nb(int R, int NPT)
 {
     for (int nb = 3; nb >= 2; --nb)
-        if (down_lds_bytes(R, nb, M, k) <= (size_t)kXLdsDynMax)
+        if (down_lds_bytes(R, nb, NPT) <= (size_t)kXLdsDynMax)
             return nb;
     return 0;
 }
 
-// Workspace: the header, then the [M*k, I] bf16 activations.
+// Workspace: the header, then the bf16 activations of M*(k+1) pairs (room
+// for the shared-expert pairs, so one size serves both kinds of call).
 static size_t ffn_ws_bytes(int32_t M, int32_t I, int32_t k)
 {
-    return kWsHeader + align_up((size_t)M * k * I * sizeof(uint16_t), 256);
+    return kWsHeader + align_up((size_t)M * (k + 1) * I * sizeof(uint16_t), 256);
 }
 
 static moe_status_t ffn_check(const uint16_t *x, const int32_t *topk_idx,
@@ -544,7 +593,7 @@ static moe_status_t ffn_check(const uint16_t *x, const int32_t *topk_idx,
     if (I < 1)
         return MOE_ERR_SHAPE;
     if (I % 8 != 0 || I > kMaxDim || !up_gemv_fits(M, H) || down_rows(H) == 0 ||
-        down_nb(down_rows(H), M, k) == 0)
+        down_nb(down_rows(H), M * k) == 0)
         return MOE_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) ||
         !aligned16(w_down) || !aligned4(topk_idx) || !aligned4(topk_w) ||
@@ -578,34 +627,35 @@ static hipError_t set_lds_attributes()
 
 template <int R>
 static void launch_down_gemv(const uint16_t *act, const int *idx, const float *tw,
-                             const uint16_t *wd, int M, int H, int I, int E, int k,
+                             const Experts &ex, int M, int H, int I, int E, int k,
                              float *out, hipStream_t st)
 {
     const int grid = (H + R - 1) / R;
-    const size_t lds = down_gemv_lds_bytes(R, M * k, I);
+    const size_t lds = down_gemv_lds_bytes(R, M * k + ex.ns * M, I);
     hipLaunchKernelGGL((expert_down_gemv_kernel<R, down_gemv_nb(R)>), dim3(grid),
                        dim3(kXThreads), lds, st, (const u32x4 *)act, idx, tw,
-                       (const u32x4 *)wd, M, H, I, E, k, out);
+                       (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, M, H, I, E, k, ex.ns, out);
 }
 
 template <int R>
 static void launch_down_r(int nb, const uint16_t *act, const int *idx, const float *tw,
-                          const uint16_t *wd, int M, int H, int I, int E, int k, float *out,
+                          const Experts &ex, int M, int H, int I, int E, int k, float *out,
                           hipStream_t st)
 {
     const int grid = (H + R - 1) / R;
-    const size_t lds = down_lds_bytes(R, nb, M, k);
+    const size_t lds = down_lds_bytes(R, nb, M * k + ex.ns * M);
     if (nb == 3)
         hipLaunchKernelGGL((expert_down_kernel<R, 3>), dim3(grid), dim3(kXThreads), lds, st,
-                           (const u32x4 *)act, idx, tw, (const u32x4 *)wd, M, H, I, E, k, out);
+                           (const u32x4 *)act, idx, tw, (const u32x4 *)ex.wd,
+                           (const u32x4 *)ex.wds, M, H, I, E, k, ex.ns, out);
     else
         hipLaunchKernelGGL((expert_down_kernel<R, 2>), dim3(grid), dim3(kXThreads), lds, st,
-                           (const u32x4 *)act, idx, tw, (const u32x4 *)wd, M, H, I, E, k, out);
+                           (const u32x4 *)act, idx, tw, (const u32x4 *)ex.wd,
+                           (const u32x4 *)ex.wds, M, H, I, E, k, ex.ns, out);
 }
 
 static moe_status_t ffn_enqueue(const uint16_t *x, const int32_t *topk_idx,
-                                const float *topk_w, const uint16_t *w_gate,
-                                const uint16_t *w_up, const uint16_t *w_down,
+                                const float *topk_w, const Experts &ex,
                                 int32_t M, int32_t H, int32_t I, int32_t E,
                                 int32_t k, float *out, void *data, hipStream_t st)
 {
@@ -619,36 +669,52 @@ static moe_status_t ffn_enqueue(const uint16_t *x, const int32_t *topk_idx,
     uint16_t *act = (uint16_t *)data;
 
     switch (up_gemv_kc(H)) {
-    case 1: launch_up_gemv<1>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
-    case 2: launch_up_gemv<2>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
-    case 3: launch_up_gemv<3>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
-    case 4: launch_up_gemv<4>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
-    default: launch_up_gemv<5>(x, topk_idx, w_gate, w_up, M, H, I, E, k, act, st); break;
+    case 1: launch_up_gemv<1>(x, topk_idx, ex, M, H, I, E, k, act, st); break;
+    case 2: launch_up_gemv<2>(x, topk_idx, ex, M, H, I, E, k, act, st); break;
+    case 3: launch_up_gemv<3>(x, topk_idx, ex, M, H, I, E, k, act, st); break;
+    case 4: launch_up_gemv<4>(x, topk_idx, ex, M, H, I, E, k, act, st); break;
+    default: launch_up_gemv<5>(x, topk_idx, ex, M, H, I, E, k, act, st); break;
     }
     moe_status_t s = check_launch();
     if (s != MOE_OK)
         return s;
 
     const int R = down_rows(H);
-    if (down_gemv_fits(R, M, k, I)) {
+    const int NPT = M * k + ex.ns * M;
+    if (down_gemv_fits(R, NPT, I)) {
         switch (R) {
-        case 4: launch_down_gemv<4>(act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
-        case 8: launch_down_gemv<8>(act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
-        case 10: launch_down_gemv<10>(act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
-        case 12: launch_down_gemv<12>(act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
-        default: launch_down_gemv<16>(act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
+        case 4: launch_down_gemv<4>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
+        case 8: launch_down_gemv<8>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
+        case 10: launch_down_gemv<10>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
+        case 12: launch_down_gemv<12>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
+        default: launch_down_gemv<16>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
         }
         return check_launch();
     }
-    const int nbd = down_nb(R, M, k);
+    const int nbd = down_nb(R, NPT);
     switch (R) {
-    case 4: launch_down_r<4>(nbd, act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
-    case 8: launch_down_r<8>(nbd, act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
-    case 10: launch_down_r<10>(nbd, act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
-    case 12: launch_down_r<12>(nbd, act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
-    default: launch_down_r<16>(nbd, act, topk_idx, topk_w, w_down, M, H, I, E, k, out, st); break;
+    case 4: launch_down_r<4>(nbd, act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
+    case 8: launch_down_r<8>(nbd, act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
+    case 10: launch_down_r<10>(nbd, act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
+    case 12: launch_down_r<12>(nbd, act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
+    default: launch_down_r<16>(nbd, act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
     }
     return check_launch();
+}
+
+// The shared expert's extra checks: its three tensors, 16-byte aligned,
+// M*(k+1) pairs within the grouping's capacity, id E inside the histogram.
+static moe_status_t shared_check(const uint16_t *wgs, const uint16_t *wus, const uint16_t *wds,
+                                 int32_t M, int32_t H, int32_t I, int32_t E, int32_t k)
+{
+    if (!wgs || !wus || !wds)
+        return MOE_ERR_NULL;
+    if (M * (k + 1) > kMaxNP || E + 1 > kMaxE ||
+        down_nb(down_rows(H), M * (k + 1)) == 0 || I > kMaxDim)
+        return MOE_ERR_UNSUPPORTED;
+    if (!aligned16(wgs) || !aligned16(wus) || !aligned16(wds))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
 }
 
 // route.hip
@@ -693,7 +759,33 @@ extern "C" moe_status_t moe_expert_ffn(const uint16_t *x, const int32_t *topk_id
         return MOE_ERR_ALIGN;
     if (workspace_bytes < moe_expert_ffn_workspace_bytes(M, H, I, E, k))
         return MOE_ERR_WORKSPACE;
-    return ffn_enqueue(x, topk_idx, topk_w, w_gate, w_up, w_down, M, H, I, E, k,
+    const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0};
+    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k,
+                       out, (char *)workspace + kWsHeader, (hipStream_t)stream);
+}
+
+extern "C" moe_status_t moe_expert_ffn_shared(
+    const uint16_t *x, const int32_t *topk_idx, const float *topk_w, const uint16_t *w_gate,
+    const uint16_t *w_up, const uint16_t *w_down, const uint16_t *w_gate_shared,
+    const uint16_t *w_up_shared, const uint16_t *w_down_shared, int32_t M, int32_t H,
+    int32_t I, int32_t E, int32_t k, float *out, void *workspace, size_t workspace_bytes,
+    void *stream)
+{
+    moe_status_t s = ffn_check(x, topk_idx, topk_w, w_gate, w_up, w_down, M, H, I,
+                               E, k, out);
+    if (s != MOE_OK)
+        return s;
+    s = shared_check(w_gate_shared, w_up_shared, w_down_shared, M, H, I, E, k);
+    if (s != MOE_OK)
+        return s;
+    if (!workspace)
+        return MOE_ERR_NULL;
+    if (!aligned16(workspace))
+        return MOE_ERR_ALIGN;
+    if (workspace_bytes < moe_expert_ffn_workspace_bytes(M, H, I, E, k))
+        return MOE_ERR_WORKSPACE;
+    const Experts ex{w_gate, w_up, w_down, w_gate_shared, w_up_shared, w_down_shared, 1};
+    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k,
                        out, (char *)workspace + kWsHeader, (hipStream_t)stream);
 }
 
@@ -737,7 +829,42 @@ extern "C" moe_status_t moe_layer(const uint16_t *x, const uint16_t *w_router,
                       workspace, st, nullptr, 0.0f, nullptr);
     if (s != MOE_OK)
         return s;
-    return ffn_enqueue(x, topk_idx, topk_w, w_gate, w_up, w_down, M, H, I, E, k,
+    const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0};
+    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k,
+                       out, (char *)workspace + r, st);
+}
+
+extern "C" moe_status_t moe_layer_shared(
+    const uint16_t *x, const uint16_t *w_router, const float *bias, const uint16_t *w_gate,
+    const uint16_t *w_up, const uint16_t *w_down, const uint16_t *w_gate_shared,
+    const uint16_t *w_up_shared, const uint16_t *w_down_shared, int32_t M, int32_t H,
+    int32_t I, int32_t E, int32_t k, int32_t *topk_idx, float *topk_w, float *out,
+    void *workspace, size_t workspace_bytes, void *stream)
+{
+    moe_status_t s = route_check(x, w_router, bias, M, H, E, k, topk_idx, topk_w,
+                                 nullptr);
+    if (s != MOE_OK)
+        return s;
+    s = ffn_check(x, topk_idx, topk_w, w_gate, w_up, w_down, M, H, I, E, k, out);
+    if (s != MOE_OK)
+        return s;
+    s = shared_check(w_gate_shared, w_up_shared, w_down_shared, M, H, I, E, k);
+    if (s != MOE_OK)
+        return s;
+    if (!workspace)
+        return MOE_ERR_NULL;
+    if (!aligned16(workspace))
+        return MOE_ERR_ALIGN;
+    if (workspace_bytes < moe_layer_workspace_bytes(M, H, I, E, k))
+        return MOE_ERR_WORKSPACE;
+    const size_t r = moe_route_workspace_bytes(M, E);
+    hipStream_t st = (hipStream_t)stream;
+    s = route_enqueue(x, w_router, bias, M, H, E, k, topk_idx, topk_w, nullptr,
+                      workspace, st, nullptr, 0.0f, nullptr);
+    if (s != MOE_OK)
+        return s;
+    const Experts ex{w_gate, w_up, w_down, w_gate_shared, w_up_shared, w_down_shared, 1};
+    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k,
                        out, (char *)workspace + r, st);
 }
 
@@ -774,6 +901,7 @@ extern "C" moe_status_t moe_layer_rmsnorm(const uint16_t *h, const uint16_t *gam
                       workspace, st, gamma, eps, x_norm);
     if (s != MOE_OK)
         return s;
-    return ffn_enqueue(x_norm, topk_idx, topk_w, w_gate, w_up, w_down, M, H, I, E, k,
+    const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0};
+    return ffn_enqueue(x_norm, topk_idx, topk_w, ex, M, H, I, E, k,
                        out, (char *)workspace + r, st);
 }

@@ -187,3 +187,23 @@ def test_rmsnorm_checks(L):
     assert ln(M=9, H=8192) == UNSUP
     assert ln(I=1004) == UNSUP
     assert ln(wsb=16) == WS
+
+
+def test_shared_expert_checks(L):
+    def sh(x=A, gs=A, us=A, ds=A, M=6, H=2560, I=1024, E=512, k=8, ws=B, wsb=1 << 30):
+        return L.moe_expert_ffn_shared(x, A, A, A, A, A, gs, us, ds, M, H, I, E, k, A,
+                                       ws, wsb, None)
+    assert sh(gs=None) == NULL
+    assert sh(ds=None) == NULL
+    assert sh(x=None) == NULL
+    assert sh(us=A + 8) == ALIGN
+    assert sh(M=16, k=16) == UNSUP          # 16 * 17 pairs > 256
+    assert sh(E=1024) == UNSUP              # the shared expert's id must fit the histogram
+    assert sh(wsb=16) == WS
+
+    def ls(gs=A, M=6, k=8, wsb=1 << 30):
+        return L.moe_layer_shared(A, A, None, A, A, A, gs, A, A, M, 2560, 1024, 512, k, A, A, A,
+                                  B, wsb, None)
+    assert ls(gs=None) == NULL
+    assert ls(M=16, k=16) == UNSUP
+    assert ls(wsb=16) == WS
