@@ -55,6 +55,12 @@ class Oracle:
         lib.oracle_expert_ffn.restype = ctypes.c_int
         lib.oracle_lmhead.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P]
         lib.oracle_lmhead.restype = ctypes.c_int
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_expert_ffn_fp8.argtypes = [_P] * 9 + [_I] * 5 + [_P]
+        lib.oracle_expert_ffn_fp8.restype = ctypes.c_int
+        lib.oracle_lmhead_fp8.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P]
+        lib.oracle_lmhead_fp8.restype = ctypes.c_int
         lib.oracle_rmsnorm.argtypes = [_P, _P, ctypes.c_double, _I, _I, _P, _P]
         lib.oracle_rmsnorm.restype = ctypes.c_int
         lib.oracle_greedy_verdict.argtypes = [_P, _P, _I, _P]
@@ -132,6 +138,48 @@ class Oracle:
         self._check(rc, "oracle_lmhead")
         return dict(tok=tok, zmax=zmax, gap=gap)
 
+    def e4m3_value(self, q: int) -> float:
+        return self.lib.oracle_e4m3_value(int(q) & 0xFF)
+
+    def expert_ffn_fp8(self, x, idx, w, qgate, sgate, qup, sup, qdown, sdown):
+        """fp8 expert weights (E4M3 codes [E,I,H]/[E,H,I] u8, per-row fp32
+        scales [E,I]/[E,H]) -> out [M,H] f64."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        w = np.ascontiguousarray(w, dtype=np.float64)
+        qg, qu, qd = (np.ascontiguousarray(a, dtype=np.uint8) for a in (qgate, qup, qdown))
+        sg, su, sd = (np.ascontiguousarray(a, dtype=np.float32) for a in (sgate, sup, sdown))
+        M, H = x.shape
+        _, k = idx.shape
+        E, I, H2 = qg.shape
+        if (H2 != H or qu.shape != qg.shape or qd.shape != (E, H, I) or sg.shape != (E, I)
+                or su.shape != (E, I) or sd.shape != (E, H)):
+            raise ValueError("fp8 expert shapes do not match")
+        out = np.empty((M, H), np.float64)
+        rc = self.lib.oracle_expert_ffn_fp8(
+            x.ctypes.data, idx.ctypes.data, w.ctypes.data, qg.ctypes.data, sg.ctypes.data,
+            qu.ctypes.data, su.ctypes.data, qd.ctypes.data, sd.ctypes.data, M, H, I, E, k,
+            out.ctypes.data)
+        self._check(rc, "oracle_expert_ffn_fp8")
+        return out
+
+    def lmhead_fp8(self, h, qlm, slm) -> dict:
+        """h [M,H] u16, qlm [V,H] u8 E4M3, slm [V] f32 -> dict(tok, zmax, gap)."""
+        h = np.ascontiguousarray(h, dtype=np.uint16)
+        q = np.ascontiguousarray(qlm, dtype=np.uint8)
+        sl = np.ascontiguousarray(slm, dtype=np.float32)
+        M, H = h.shape
+        V, H2 = q.shape
+        if H2 != H or sl.shape != (V,):
+            raise ValueError("fp8 lm_head shapes do not match")
+        tok = np.empty(M, np.int32)
+        zmax = np.empty(M, np.float64)
+        gap = np.empty(M, np.float64)
+        rc = self.lib.oracle_lmhead_fp8(h.ctypes.data, q.ctypes.data, sl.ctypes.data, M, H, V,
+                                        tok.ctypes.data, zmax.ctypes.data, gap.ctypes.data)
+        self._check(rc, "oracle_lmhead_fp8")
+        return dict(tok=tok, zmax=zmax, gap=gap)
+
     def rmsnorm(self, h, gamma, eps: float, want_exact=False):
         """h [M,H] u16, gamma [H] u16 -> xn [M,H] u16 (bf16 bits) (, fp64 values)."""
         h = np.ascontiguousarray(h, dtype=np.uint16)
@@ -191,3 +239,11 @@ def greedy_verdict(tokens, tok):
 
 def rmsnorm(h, gamma, eps, want_exact=False):
     return load().rmsnorm(h, gamma, eps, want_exact)
+
+
+def expert_ffn_fp8(x, idx, w, qgate, sgate, qup, sup, qdown, sdown):
+    return load().expert_ffn_fp8(x, idx, w, qgate, sgate, qup, sup, qdown, sdown)
+
+
+def lmhead_fp8(h, qlm, slm):
+    return load().lmhead_fp8(h, qlm, slm)

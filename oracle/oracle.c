@@ -20,6 +20,7 @@
  *   - silu(z) = z / (1 + exp(-z)), applied to the gate projection and
  *     multiplied by the up projection (section "Two fusions and a retune");
  *   - the combine sums the k slots in slot order (same section);
+ *   - fp8 weights are OCP E4M3 codes times one fp32 scale per output row;
  *   - the router chain's norm is RMSNorm with a per-column gain, rounded
  *     once to bf16 (the value both the gate and the experts read);
  *   - the verify chain is scored greedily: a drafted candidate is accepted
@@ -174,6 +175,14 @@ int oracle_route(const uint16_t *x, const uint16_t *wg, const float *bias,
     return 0;
 }
 
+/* SwiGLU of one row: silu on the gate projection, times the up projection
+ * (section "Two fusions and a retune"), in double. */
+static double swiglu(double g, double u)
+{
+    double s = g / (1.0 + exp(-g));
+    return s * u;
+}
+
 int oracle_expert_ffn(const uint16_t *x, const int32_t *idx, const double *w,
                       const uint16_t *wgate, const uint16_t *wup,
                       const uint16_t *wdown,
@@ -213,8 +222,7 @@ int oracle_expert_ffn(const uint16_t *x, const int32_t *idx, const double *w,
             const uint16_t *xt = x + (int64_t)t * H;
             double g = dot_bf16(wgate + (e * I + i) * H, xt, H);
             double u = dot_bf16(wup + (e * I + i) * H, xt, H);
-            double s = g / (1.0 + exp(-g));
-            a[p * I + i] = s * u;
+            a[p * I + i] = swiglu(g, u);
         }
 
     /* Down projection of every pair. */
@@ -243,6 +251,21 @@ int oracle_expert_ffn(const uint16_t *x, const int32_t *idx, const double *w,
     return 0;
 }
 
+/* Greedy token: the first v holding the largest fp32-rounded logit. */
+static int32_t first_argmax_f32(const double *z, int32_t V)
+{
+    int32_t best = 0;
+    float best_v = (float)z[0];
+    for (int32_t v = 1; v < V; ++v) {
+        float zv = (float)z[v];
+        if (zv > best_v) {
+            best = v;
+            best_v = zv;
+        }
+    }
+    return best;
+}
+
 int oracle_lmhead(const uint16_t *h, const uint16_t *wlm,
                   int32_t M, int32_t H, int32_t V,
                   int32_t *tok, double *zmax, double *gap)
@@ -262,16 +285,7 @@ int oracle_lmhead(const uint16_t *h, const uint16_t *wlm,
         for (int32_t v = 0; v < V; ++v)
             z[v] = dot_bf16(h + (int64_t)t * H, wlm + (int64_t)v * H, H);
 
-        /* Greedy token: first v holding the largest fp32-rounded logit. */
-        int32_t best = 0;
-        float best_v = (float)z[0];
-        for (int32_t v = 1; v < V; ++v) {
-            float zv = (float)z[v];
-            if (zv > best_v) {
-                best = v;
-                best_v = zv;
-            }
-        }
+        int32_t best = first_argmax_f32(z, V);
         tok[t] = best;
         zmax[t] = z[best];
 
@@ -350,5 +364,127 @@ int oracle_rmsnorm(const uint16_t *h, const uint16_t *gamma, double eps,
                 xn_exact[(int64_t)t * H + i] = y;
         }
     }
+    return 0;
+}
+
+double oracle_e4m3_value(uint8_t q)
+{
+    int sign = q >> 7, e = (q >> 3) & 15, m = q & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double mag = e == 0 ? ldexp((double)m / 8.0, -6)          /* subnormal */
+                        : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+static int all_finite_e4m3(const uint8_t *q, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        if ((q[i] & 0x7F) == 0x7F)
+            return 0;
+    return 1;
+}
+
+/* x (bf16) . one fp8 row times its scale, in double, ascending index:
+ * every element is dequantised (code value times the row's scale) first. */
+static double dot_e4m3(const uint8_t *q, double scale, const uint16_t *x, int64_t n)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        s += (oracle_e4m3_value(q[i]) * scale) * oracle_bf16_value(x[i]);
+    return s;
+}
+
+int oracle_expert_ffn_fp8(const uint16_t *x, const int32_t *idx, const double *w,
+                          const uint8_t *qgate, const float *sgate,
+                          const uint8_t *qup, const float *sup,
+                          const uint8_t *qdown, const float *sdown,
+                          int32_t M, int32_t H, int32_t I, int32_t E, int32_t k,
+                          double *out)
+{
+    if (!x || !idx || !w || !qgate || !sgate || !qup || !sup || !qdown || !sdown || !out)
+        return -1;
+    if (M < 1 || H < 1 || I < 1 || E < 1 || k < 1)
+        return -2;
+    const int64_t NP = (int64_t)M * k;
+    for (int64_t p = 0; p < NP; ++p)
+        if (idx[p] < 0 || idx[p] >= E)
+            return -3;
+    if (!all_finite_bf16(x, (int64_t)M * H))
+        return -4;
+    for (int64_t p = 0; p < NP; ++p) {
+        int64_t e = idx[p];
+        if (!isfinite(w[p]) ||
+            !all_finite_e4m3(qgate + e * I * H, (int64_t)I * H) ||
+            !all_finite_e4m3(qup + e * I * H, (int64_t)I * H) ||
+            !all_finite_e4m3(qdown + e * H * I, (int64_t)H * I))
+            return -4;
+        for (int32_t i = 0; i < I; ++i)
+            if (!isfinite(sgate[e * I + i]) || !isfinite(sup[e * I + i]))
+                return -4;
+        for (int32_t r = 0; r < H; ++r)
+            if (!isfinite(sdown[e * H + r]))
+                return -4;
+    }
+
+    double *a = (double *)malloc(sizeof(double) * (size_t)(NP * I));
+
+    /* Up projection and SwiGLU per pair, on the dequantised rows. */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t p = 0; p < NP; ++p)
+        for (int32_t i = 0; i < I; ++i) {
+            int32_t t = (int32_t)(p / k);
+            int64_t e = idx[p];
+            const uint16_t *xt = x + (int64_t)t * H;
+            double g = dot_e4m3(qgate + (e * I + i) * H, sgate[e * I + i], xt, H);
+            double u = dot_e4m3(qup + (e * I + i) * H, sup[e * I + i], xt, H);
+            a[p * I + i] = swiglu(g, u);
+        }
+
+    /* Down projection and the weighted combine, slots in order. */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int32_t t = 0; t < M; ++t)
+        for (int32_t r = 0; r < H; ++r) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                int64_t p = (int64_t)t * k + j;
+                int64_t e = idx[p];
+                const uint8_t *row = qdown + (e * H + r) * I;
+                double sd = sdown[e * H + r], y = 0.0;
+                for (int32_t i = 0; i < I; ++i)
+                    y += (oracle_e4m3_value(row[i]) * sd) * a[p * I + i];
+                acc += w[p] * y;
+            }
+            out[(int64_t)t * H + r] = acc;
+        }
+    free(a);
+    return 0;
+}
+
+int oracle_lmhead_fp8(const uint16_t *h, const uint8_t *qlm, const float *slm,
+                      int32_t M, int32_t H, int32_t V,
+                      int32_t *tok, double *zmax, double *gap)
+{
+    if (!h || !qlm || !slm || !tok || !zmax || !gap)
+        return -1;
+    if (M < 1 || H < 1 || V < 1)
+        return -2;
+    if (!all_finite_bf16(h, (int64_t)M * H) || !all_finite_e4m3(qlm, (int64_t)V * H))
+        return -4;
+    for (int32_t v = 0; v < V; ++v)
+        if (!isfinite(slm[v]))
+            return -4;
+    double *z = (double *)malloc(sizeof(double) * (size_t)V);
+    for (int32_t t = 0; t < M; ++t) {
+#pragma omp parallel for schedule(static)
+        for (int32_t v = 0; v < V; ++v)
+            z[v] = dot_e4m3(qlm + (int64_t)v * H, slm[v], h + (int64_t)t * H, H);
+        int32_t best = first_argmax_f32(z, V);
+        tok[t] = best;
+        zmax[t] = z[best];
+        double unused;
+        sorted_gaps(z, V, 1, &gap[t], &unused);
+    }
+    free(z);
     return 0;
 }

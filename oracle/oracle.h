@@ -107,6 +107,31 @@ int oracle_lmhead(const uint16_t *h, const uint16_t *wlm,
 int oracle_rmsnorm(const uint16_t *h, const uint16_t *gamma, double eps,
                    int32_t M, int32_t H, uint16_t *xn, double *xn_exact);
 
+/* fp8 weights (the post's next bandwidth lever, section "The economics of
+ * speculation at batch 1"), read as OCP E4M3 codes with one fp32 scale per
+ * output row: W[row, j] = e4m3(q[row, j]) * scale[row].
+ *
+ * Value of one E4M3 byte: sign bit, 4 exponent bits (bias 7), 3 mantissa
+ * bits; exponent 0 holds the subnormals m/8 * 2^-6; S.1111.111 is NaN;
+ * there are no infinities (largest finite 448). */
+double oracle_e4m3_value(uint8_t q);
+
+/* oracle_expert_ffn with fp8 expert weights:
+ *   qgate, qup [E,I,H] e4m3 with sgate, sup [E,I] fp32 (per row i),
+ *   qdown [E,H,I] e4m3 with sdown [E,H] fp32 (per row r);
+ * everything else as oracle_expert_ffn. NaN codes are rejected (-4). */
+int oracle_expert_ffn_fp8(const uint16_t *x, const int32_t *idx, const double *w,
+                          const uint8_t *qgate, const float *sgate,
+                          const uint8_t *qup, const float *sup,
+                          const uint8_t *qdown, const float *sdown,
+                          int32_t M, int32_t H, int32_t I, int32_t E, int32_t k,
+                          double *out);
+
+/* oracle_lmhead with an fp8 lm_head: qlm [V,H] e4m3, slm [V] fp32. */
+int oracle_lmhead_fp8(const uint16_t *h, const uint8_t *qlm, const float *slm,
+                      int32_t M, int32_t H, int32_t V,
+                      int32_t *tok, double *zmax, double *gap);
+
 /* Greedy verdict of one verify step over a drafted chain (section "The
  * shape of a single-request step": the target scores the whole chain in one
  * forward and the verdict is taken inside the verify step).

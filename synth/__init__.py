@@ -89,6 +89,44 @@ def norm_gain(H: int, seed: int = WEIGHT_SEED, layer: int = 0) -> np.ndarray:
     return bf16_bits(v)
 
 
+def fp8_rows(shape, std: float, seed: int, *ids: int):
+    """fp8 weights of N(0, std^2) rows: (E4M3 codes uint8 [..., K], fp32
+    scale per row [...]). Each row is scaled by its largest magnitude / 448
+    and converted with torch's own float8_e4m3fn conversion (nearest, no
+    saturation needed: every scaled value is within +-448)."""
+    import torch
+
+    g = rng(seed, *ids)
+    v = g.standard_normal(size=shape, dtype=np.float32) * np.float32(std)
+    amax = np.max(np.abs(v), axis=-1)
+    scale = (np.where(amax > 0, amax, 1.0) / 448.0).astype(np.float32)
+    t = torch.from_numpy(v / scale[..., None])
+    codes = t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scale
+
+
+def device_fp8_rows(shape, std: float, seed: int, *ids: int, device="cuda",
+                    chunk_rows: int = 1 << 16):
+    """fp8_rows drawn on the device (full-size tensors): (uint8 codes, fp32
+    scales) torch tensors; values are deterministic for (seed, ids, shape)."""
+    import torch
+
+    K = shape[-1]
+    rows = int(np.prod(shape[:-1]))
+    codes = torch.empty((rows, K), dtype=torch.uint8, device=device)
+    scales = torch.empty(rows, dtype=torch.float32, device=device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(np.random.SeedSequence([seed, *ids, 8]).generate_state(1)[0]))
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        v = torch.randn((r1 - r0, K), generator=gen, device=device, dtype=torch.float32) * std
+        amax = v.abs().amax(dim=1)
+        sc = torch.where(amax > 0, amax, torch.ones_like(amax)) / 448.0
+        codes[r0:r1] = (v / sc[:, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        scales[r0:r1] = sc
+    return codes.view(*shape), scales.view(*shape[:-1])
+
+
 def zipf_bias(E: int, alpha: float, seed: int = ZIPF_SEED, s: float = ZIPF_S) -> np.ndarray:
     """Router bias whose exponential follows a Zipf(s) popularity.
 

@@ -314,6 +314,97 @@ def pin_lmhead_planted(o):
     assert r0["tok"].tolist() == [0]
 
 
+# ---------------------------------------------------------------------- fp8
+
+def pin_e4m3_decode(o):
+    """Every E4M3 code against torch's float8_e4m3fn decode (NaN codes NaN),
+    and hand values: 0x01 = 2^-9, 0x07 = 7 * 2^-9, 0x08 = 2^-6 (smallest
+    normal), 0x38 = 1, 0x3C = 1.5, 0x7E = 448, 0xB8 = -1, 0x80 = -0."""
+    import torch
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    ref = ref.to(torch.float64).numpy()
+    got = np.array([o.e4m3_value(q) for q in range(256)])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    assert np.array_equal(got[~nan], ref[~nan])
+    hand = {0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x3C: 1.5,
+            0x7E: 448.0, 0xB8: -1.0}
+    assert all(o.e4m3_value(q) == v for q, v in hand.items())
+    z = o.e4m3_value(0x80)
+    assert z == 0.0 and math.copysign(1.0, z) < 0
+
+
+def _fp8_case(M, H, I, E, seed, pow2_scales):
+    rng = np.random.default_rng(seed)
+    def codes(shape):
+        q = rng.integers(0, 256, size=shape).astype(np.uint8)
+        q[(q & 0x7F) == 0x7F] = 0x3C                # no NaN codes
+        return q
+    def scales(shape):
+        if pow2_scales:
+            return np.ldexp(1.0, rng.integers(-12, -4, size=shape)).astype(np.float32)
+        return rng.uniform(0.001, 0.01, size=shape).astype(np.float32)
+    q = dict(gate=codes((E, I, H)), up=codes((E, I, H)), down=codes((E, H, I)))
+    sc = dict(gate=scales((E, I)), up=scales((E, I)), down=scales((E, H)))
+    return q, sc
+
+
+def _dequant_bf16(o, q, s):
+    """Exact bf16 bits of e4m3(q) * s for power-of-two scales."""
+    table = np.array([o.e4m3_value(c) for c in range(256)])
+    v = table[q] * s[..., None].astype(np.float64)
+    return _bits(v.astype(np.float32))
+
+
+def pin_expert_ffn_fp8_is_bf16_on_dequantised(o):
+    """With power-of-two scales every dequantised weight is exact in bf16, so
+    the fp8 FFN must equal the bf16 FFN on those values bit for bit; doubling
+    every down scale doubles the output exactly; an expert's weights only
+    matter through its own rows (a second expert's scales change nothing for
+    tokens that do not use it)."""
+    M, H, I, E, k = 3, 32, 16, 4, 2
+    q, sc = _fp8_case(M, H, I, E, 61, True)
+    x = synth.normal_bf16((M, H), 1.0, 61, 1)
+    idx = np.array([[0, 2], [2, 1], [3, 0]], np.int32)
+    w = np.array([[0.7, 0.3], [0.5, 0.5], [0.9, 0.1]])
+    out8 = o.expert_ffn_fp8(x, idx, w, q["gate"], sc["gate"], q["up"], sc["up"],
+                            q["down"], sc["down"])
+    ref = o.expert_ffn(x, idx, w, _dequant_bf16(o, q["gate"], sc["gate"]),
+                       _dequant_bf16(o, q["up"], sc["up"]), _dequant_bf16(o, q["down"], sc["down"]))
+    assert np.array_equal(out8, ref)
+    out2 = o.expert_ffn_fp8(x, idx, w, q["gate"], sc["gate"], q["up"], sc["up"],
+                            q["down"], sc["down"] * 2)
+    assert np.array_equal(out2, out8 * 2)
+    sg = sc["gate"].copy()
+    sg[1] *= 4                                    # expert 1: used by token 1 only
+    out3 = o.expert_ffn_fp8(x, idx, w, q["gate"], sg, q["up"], sc["up"], q["down"], sc["down"])
+    assert np.array_equal(out3[[0, 2]], out8[[0, 2]]) and not np.array_equal(out3[1], out8[1])
+
+
+def pin_lmhead_fp8(o):
+    """The fp8 lm_head equals the bf16 lm_head on the dequantised rows
+    (power-of-two scales); a row whose scale is raised far enough wins."""
+    M, H, V = 3, 32, 200
+    rng = np.random.default_rng(62)
+    q = rng.integers(0, 256, size=(V, H)).astype(np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x38
+    s = np.ldexp(1.0, rng.integers(-10, -6, size=V)).astype(np.float32)
+    h = synth.normal_bf16((M, H), 1.0, 62, 1)
+    r8 = o.lmhead_fp8(h, q, s)
+    table = np.array([o.e4m3_value(c) for c in range(256)])
+    wl = _bits((table[q] * s[:, None]).astype(np.float32))
+    r16 = o.lmhead(h, wl)
+    for key in ("tok", "zmax", "gap"):
+        assert np.array_equal(r8[key], r16[key]), key
+    z = (table[q] * s[:, None]) @ F(h).astype(np.float64).T        # [V, M]
+    v_pos = int(np.argmax(z[:, 0]))                                 # make another row win token 0
+    other = (v_pos + 7) % V
+    if z[other, 0] > 0:
+        s2 = s.copy()
+        s2[other] = s[other] * 2.0 ** 12
+        assert o.lmhead_fp8(h, q, s2)["tok"][0] == other
+
+
 # ------------------------------------------------------------------ RMSNorm
 
 def pin_rmsnorm_hand_examples(o):
