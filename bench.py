@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--M", type=int, default=6)
     ap.add_argument("--layers", type=int, default=16, help="distinct MoE layers rotated")
     ap.add_argument("--lm-copies", type=int, default=2)
+    ap.add_argument("--fp8-layers", type=int, default=8,
+                    help="distinct fp8 expert layers rotated for the fp8 lines (0 skips them)")
     ap.add_argument("--router-copies", type=int, default=128,
                     help="distinct router gates rotated in the gate-only timing")
     ap.add_argument("--zipf-alpha", type=float, default=None,
@@ -187,6 +189,17 @@ def main():
                                     K_["lm_head"]) for c in range(args.lm_copies)]
     routers = [synth.device_normal_bf16((E, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 200 + c,
                                         K_["router"]) for c in range(args.router_copies)]
+    # fp8 experts (E4M3 codes + fp32 row scales) for the fp8 lines; the router
+    # stays bf16 (each rotated layer's own); two fp8 lm_head copies
+    layers8 = []
+    for l in range(args.fp8_layers if not args.profile_steps else 0):
+        qg, sg = synth.device_fp8_rows((E, I, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 300 + l, K_["gate"])
+        qu, su = synth.device_fp8_rows((E, I, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 300 + l, K_["up"])
+        qd, sd = synth.device_fp8_rows((E, H, I), synth.WEIGHT_STD, synth.WEIGHT_SEED, 300 + l, K_["down"])
+        layers8.append(dict(router=layers[l % len(layers)]["router"], gate=qg, s_gate=sg, up=qu,
+                            s_up=su, down=qd, s_down=sd))
+    lms8 = [synth.device_fp8_rows((V, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 400 + c,
+                                  K_["lm_head"]) for c in range(2 if layers8 else 0)]
     log(f"weights ready: {torch.cuda.memory_allocated() / 1e9:.1f} GB ({time.time() - t0:.1f} s)")
 
     def up(bits):
@@ -267,6 +280,7 @@ def main():
         torch.cuda.synchronize()
         D.append(len(np.unique(idx.cpu().numpy())))
     per_expert = 3 * I * H * 2
+    per_expert8 = 3 * I * H + (2 * I + H) * 4          # fp8 codes + row scales
     io_layer = M * H * 2 + M * k * 8 + M * H * 4 + (E * 4 if bias is not None else 0)
     layer_bytes = [E * H * 2 + d * per_expert + io_layer for d in D]
     lm_bytes = V * H * 2 + M * H * 2 + M * 4 + M * 4 + 8
@@ -343,7 +357,7 @@ def main():
     # layer step at the other verify widths of the workload, uniform and
     # Zipf-biased routing (same 16 rotating layers, cold); with norm=True the
     # router chain's norm runs in front (moe_layer_rmsnorm)
-    def layer_at(Ms, alpha, steps=32, warm=8, norm=False, shared=False):
+    def layer_at(Ms, alpha, steps=32, warm=8, norm=False, shared=False, fp8=False):
         xs = up(synth.activations(Ms, H, seed=synth.ACT_SEED, tag=10 + Ms))
         bs = None if alpha is None else torch.from_numpy(synth.zipf_bias(E, alpha)).to(dev)
         ids = torch.empty((Ms, k), dtype=torch.int32, device=dev)
@@ -359,6 +373,13 @@ def main():
                   Ms, H, I, E, k, xns.data_ptr(), ids.data_ptr(), tws.data_ptr(),
                   outs.data_ptr(), ws.data_ptr(), ws.numel(), stream) for Lw in layers]
             fn = L.moe_layer_rmsnorm
+        elif fp8:
+            a = [(xs.data_ptr(), Lw["router"].data_ptr(), bs.data_ptr() if bs is not None else None,
+                  Lw["gate"].data_ptr(), Lw["s_gate"].data_ptr(), Lw["up"].data_ptr(),
+                  Lw["s_up"].data_ptr(), Lw["down"].data_ptr(), Lw["s_down"].data_ptr(),
+                  Ms, H, I, E, k, ids.data_ptr(), tws.data_ptr(), outs.data_ptr(),
+                  ws.data_ptr(), ws.numel(), stream) for Lw in layers8]
+            fn = L.moe_layer_fp8
         elif shared:
             a = [(xs.data_ptr(), Lw["router"].data_ptr(), bs.data_ptr() if bs is not None else None,
                   Lw["gate"].data_ptr(), Lw["up"].data_ptr(), Lw["down"].data_ptr(),
@@ -373,7 +394,8 @@ def main():
                   ws.data_ptr(), ws.numel(), stream) for Lw in layers]
             fn = L.moe_layer
         Ds = []
-        for l in range(nl):
+        nla = len(a)
+        for l in range(nla):
             check("moe_layer", fn(*a[l]))
             torch.cuda.synchronize()
             Ds.append(len(np.unique(ids.cpu().numpy())))
@@ -381,19 +403,21 @@ def main():
         io = (Ms * H * 2 + Ms * k * 8 + Ms * H * 4 + (E * 4 if bs is not None else 0)
               + (H * 2 + Ms * H * 2 if norm else 0))
         for s in range(warm):
-            check("moe_layer", fn(*a[s % nl]))
+            check("moe_layer", fn(*a[s % nla]))
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         for i in range(steps):
             ev[i].record()
-            check("moe_layer", fn(*a[(warm + i) % nl]))
+            check("moe_layer", fn(*a[(warm + i) % nla]))
         ev[steps].record()
         torch.cuda.synchronize()
         us = sum(ev[i].elapsed_time(ev[i + 1]) for i in range(steps)) * 1e3 / steps
-        byts = sum(E * H * 2 + (Ds[(warm + i) % nl] + (1 if shared else 0)) * per_expert + io
+        pe = per_expert8 if fp8 else per_expert
+        byts = sum(E * H * 2 + (Ds[(warm + i) % nla] + (1 if shared else 0)) * pe + io
                    for i in range(steps)) / steps
         gbps = byts / (us * 1e-6) / 1e9
         return {"M": Ms, "zipf_alpha": alpha, "rmsnorm": norm, "shared_expert": shared,
+                "fp8_experts": fp8,
                 "us": round(us, 2),
                 "GBps": round(gbps, 1),
                 "frac": round(gbps / HBM_PEAK_GBPS, 4), "bytes": int(byts),
@@ -402,6 +426,33 @@ def main():
     layer_sweep = [layer_at(m, a) for m, a in ((1, None), (1, 1.0), (16, None), (16, 1.0))]
     layer_norm = layer_at(M, args.zipf_alpha, norm=True)
     layer_shared = [layer_at(m, args.zipf_alpha, shared=True) for m in (1, M, 16)]
+    fp8 = None
+    if layers8:
+        # fp8 experts at M = 1 and the step's M (the activations of M*k pairs
+        # must fit in LDS: M <= 9 at I = 1024, k = 8), and the fp8 lm_head
+        # with the verdict, cold over two copies
+        l8 = [layer_at(m, args.zipf_alpha, fp8=True) for m in (1, M)]
+        lm8_args = [(h.data_ptr(), q.data_ptr(), sc.data_ptr(), chain.data_ptr(), M, H, V,
+                     am.data_ptr(), None, acc.data_ptr(), ws_lm.data_ptr(), ws_lm.numel(), stream)
+                    for q, sc in lms8]
+        for s in range(4):
+            check("lmhead_greedy_verify_fp8", L.lmhead_greedy_verify_fp8(*lm8_args[s % 2]))
+        torch.cuda.synchronize()
+        ev8 = [torch.cuda.Event(enable_timing=True) for _ in range(33)]
+        for i in range(32):
+            ev8[i].record()
+            check("lmhead_greedy_verify_fp8", L.lmhead_greedy_verify_fp8(*lm8_args[i % 2]))
+        ev8[32].record()
+        torch.cuda.synchronize()
+        lm8_us = sum(ev8[i].elapsed_time(ev8[i + 1]) for i in range(32)) * 1e3 / 32
+        lm8_bytes = V * H + V * 4 + M * H * 2 + M * 8 + 8
+        lm8_gbps = lm8_bytes / (lm8_us * 1e-6) / 1e9
+        fp8 = {"moe_layer": l8,
+               "lm_head": {"us": round(lm8_us, 2), "GBps": round(lm8_gbps, 1),
+                           "frac": round(lm8_gbps / HBM_PEAK_GBPS, 4), "bytes": lm8_bytes},
+               "step_us_M": round(l8[-1]["us"] + lm8_us, 2)}
+        log(f"fp8: layer M=1 {l8[0]['us']} us ({l8[0]['frac']:.1%}), M={M} {l8[1]['us']} us "
+            f"({l8[1]['frac']:.1%}); lm_head {lm8_us:.1f} us ({lm8_gbps / HBM_PEAK_GBPS:.1%})")
     log("layer with a shared expert: " + ", ".join(f"M={r['M']}: {r['us']} us ({r['frac']:.1%})"
                                                   for r in layer_shared))
     log(f"router chain with norm: gate {route_norm_us:.2f} us (without {route_us:.2f}); "
@@ -481,6 +532,7 @@ def main():
         "router_chain_rmsnorm": {"gate_us": round(route_norm_us, 2),
                                  "moe_layer_rmsnorm": layer_norm},
         "moe_layer_shared_expert": layer_shared,
+        "fp8_weights": fp8,
         "roofline": {"kernel": "lmhead_kernel (lmhead_greedy_verify)", "bound": "hbm",
                      "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},

@@ -191,6 +191,31 @@ moe_status_t moe_expert_ffn_shared(const uint16_t *x, const int32_t *topk_idx,
                                    size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * moe_expert_ffn_fp8 -- moe_expert_ffn with fp8 expert weights: the post's
+ * next bandwidth lever (section "The economics of speculation at batch 1"),
+ * read as OCP E4M3 codes with one fp32 scale per output row, which halves
+ * the bytes every selected expert streams.
+ *
+ *   w_gate, w_up [E,I,H] uint8   E4M3 codes (16-byte aligned)
+ *   s_gate, s_up [E,I]   fp32    row scales: W_gate[e,i,h] =
+ *                                s_gate[e,i] * e4m3(w_gate[e,i,h])
+ *   w_down       [E,H,I] uint8   E4M3 codes
+ *   s_down       [E,H]   fp32    row scales of W_down
+ *   the rest:                    as moe_expert_ffn (same workspace size)
+ * H and I must be multiples of 16. The activations of the M*k pairs must
+ * fit in LDS (M*k*I*2 bytes up to about 150 KB: M <= 9 at I = 1024, k = 8),
+ * else MOE_ERR_UNSUPPORTED. NaN codes are the caller's to avoid.
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_expert_ffn_fp8(const uint16_t *x, const int32_t *topk_idx,
+                                const float *topk_w, const uint8_t *w_gate,
+                                const float *s_gate, const uint8_t *w_up,
+                                const float *s_up, const uint8_t *w_down,
+                                const float *s_down, int32_t M, int32_t H,
+                                int32_t I, int32_t E, int32_t k, float *out,
+                                void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* ------------------------------------------------------------------------
  * moe_layer -- one MoE layer verify step: moe_route then moe_expert_ffn,
  * enqueued back to back on `stream` (same arguments and results as the two
  * calls; topk_idx/topk_w are written and then consumed on the device).
@@ -219,6 +244,20 @@ moe_status_t moe_layer_shared(const uint16_t *x, const uint16_t *w_router,
                               int32_t I, int32_t E, int32_t k, int32_t *topk_idx,
                               float *topk_w, float *out, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * moe_layer_fp8 -- moe_route (bf16 gate) then moe_expert_ffn_fp8, on one
+ * stream. Arguments as moe_layer with the fp8 expert tensors and scales of
+ * moe_expert_ffn_fp8. Workspace: moe_layer_workspace_bytes.
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_layer_fp8(const uint16_t *x, const uint16_t *w_router,
+                           const float *bias, const uint8_t *w_gate,
+                           const float *s_gate, const uint8_t *w_up,
+                           const float *s_up, const uint8_t *w_down,
+                           const float *s_down, int32_t M, int32_t H, int32_t I,
+                           int32_t E, int32_t k, int32_t *topk_idx, float *topk_w,
+                           float *out, void *workspace, size_t workspace_bytes,
+                           void *stream);
 
 /* ------------------------------------------------------------------------
  * moe_layer_rmsnorm -- moe_route_rmsnorm then moe_expert_ffn on the
@@ -287,6 +326,31 @@ moe_status_t lmhead_greedy_verify(const uint16_t *h, const uint16_t *w_lm,
                                   int32_t V, int32_t *argmax, float *max_logit,
                                   int32_t *accept, void *workspace,
                                   size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * lmhead_argmax_fp8, lmhead_greedy_verify_fp8 -- the same with an fp8
+ * lm_head: the post's next bandwidth lever ("once fp8 weights shrink the
+ * fixed base", section "The economics of speculation at batch 1"), read as
+ * OCP E4M3 codes with one fp32 scale per vocabulary row.
+ *
+ *   w_lm     [V,H] uint8  E4M3 codes (sign, 4 exponent bits with bias 7,
+ *                         3 mantissa bits; S.1111.111 is NaN), 16-byte aligned
+ *   w_scale  [V]   fp32   z[t,v] = w_scale[v] * sum_h h[t,h] * e4m3(w_lm[v,h])
+ *   the rest: as lmhead_argmax / lmhead_greedy_verify (same workspace size)
+ * H must be a multiple of 16. NaN codes are the caller's to avoid (the
+ * argmax over a NaN logit is unspecified).
+ * ---------------------------------------------------------------------- */
+moe_status_t lmhead_argmax_fp8(const uint16_t *h, const uint8_t *w_lm,
+                               const float *w_scale, int32_t M, int32_t H,
+                               int32_t V, int32_t *argmax, float *max_logit,
+                               void *workspace, size_t workspace_bytes,
+                               void *stream);
+moe_status_t lmhead_greedy_verify_fp8(const uint16_t *h, const uint8_t *w_lm,
+                                      const float *w_scale, const int32_t *tokens,
+                                      int32_t M, int32_t H, int32_t V,
+                                      int32_t *argmax, float *max_logit,
+                                      int32_t *accept, void *workspace,
+                                      size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -26,9 +26,11 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPP
 EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_clear",
            "moe_route_workspace_bytes", "moe_route", "moe_route_rmsnorm",
            "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_expert_ffn_shared",
+           "moe_expert_ffn_fp8", "moe_layer_fp8",
            "moe_layer_workspace_bytes", "moe_layer", "moe_layer_rmsnorm",
            "moe_layer_shared",
-           "lmhead_argmax_workspace_bytes", "lmhead_argmax", "lmhead_greedy_verify")
+           "lmhead_argmax_workspace_bytes", "lmhead_argmax", "lmhead_greedy_verify",
+           "lmhead_argmax_fp8", "lmhead_greedy_verify_fp8")
 
 
 class MoeError(RuntimeError):
@@ -70,6 +72,10 @@ def lib() -> ctypes.CDLL:
                                         _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _S, _P]
         L.moe_expert_ffn_shared.restype = ctypes.c_int32
         L.moe_expert_ffn_shared.argtypes = [_P] * 9 + [_I] * 5 + [_P, _P, _S, _P]
+        L.moe_expert_ffn_fp8.restype = ctypes.c_int32
+        L.moe_expert_ffn_fp8.argtypes = [_P] * 9 + [_I] * 5 + [_P, _P, _S, _P]
+        L.moe_layer_fp8.restype = ctypes.c_int32
+        L.moe_layer_fp8.argtypes = [_P] * 9 + [_I] * 5 + [_P, _P, _P, _P, _S, _P]
         L.moe_layer_shared.restype = ctypes.c_int32
         L.moe_layer_shared.argtypes = [_P] * 9 + [_I] * 5 + [_P, _P, _P, _P, _S, _P]
         L.moe_expert_ffn_workspace_bytes.restype = _S
@@ -86,6 +92,10 @@ def lib() -> ctypes.CDLL:
         L.lmhead_argmax_workspace_bytes.argtypes = [_I, _I]
         L.lmhead_argmax.restype = ctypes.c_int32
         L.lmhead_argmax.argtypes = [_P, _P, _I, _I, _I, _P, _P, _P, _S, _P]
+        L.lmhead_argmax_fp8.restype = ctypes.c_int32
+        L.lmhead_argmax_fp8.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _S, _P]
+        L.lmhead_greedy_verify_fp8.restype = ctypes.c_int32
+        L.lmhead_greedy_verify_fp8.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _S, _P]
         L.lmhead_greedy_verify.restype = ctypes.c_int32
         L.lmhead_greedy_verify.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _S, _P]
         _lib = L
@@ -409,6 +419,114 @@ def moe_layer_shared(x, w_router, w_gate, w_up, w_down, w_gate_shared, w_up_shar
         _ptr(w_up_shared, "w_up_shared", _BF16, (I, H)),
         _ptr(w_down_shared, "w_down_shared", _BF16, (H, I)), M, H, I, E, k,
         _ptr(idx, "topk_idx", (torch.int32,), (M, k)),
+        _ptr(w, "topk_w", (torch.float32,), (M, k)),
+        _ptr(o, "out", (torch.float32,), (M, H)), _ptr(ws, "workspace"), ws.numel(), st))
+    return idx, w, o
+
+
+_U8 = (torch.uint8,)
+
+
+def lmhead_argmax_fp8(h, w_lm, w_scale, *, want_max=False, out=None, workspace=None,
+                      stream=None):
+    """fp8 lm_head (E4M3 codes [V,H] uint8, fp32 scale per row [V]) + greedy
+    argmax. Returns argmax [M] int32 (, max_logit)."""
+    M, H = h.shape
+    V = w_lm.shape[0]
+    dev = h.device
+    am, ml = out if out is not None else (None, None)
+    if am is None:
+        am = torch.empty(M, dtype=torch.int32, device=dev)
+    if want_max and ml is None:
+        ml = torch.empty(M, dtype=torch.float32, device=dev)
+    st = _stream(stream)
+    nbytes = lmhead_argmax_workspace_bytes(M, V)
+    ws = workspace if workspace is not None else Workspace.get("lmhead", nbytes, dev, st)
+    _check("lmhead_argmax_fp8", lib().lmhead_argmax_fp8(
+        _ptr(h, "h", _BF16), _ptr(w_lm, "w_lm", _U8, (V, H)),
+        _ptr(w_scale, "w_scale", (torch.float32,), (V,)), M, H, V,
+        _ptr(am, "argmax", (torch.int32,), (M,)),
+        _ptr(ml, "max_logit", (torch.float32,), (M,)) if want_max else None,
+        _ptr(ws, "workspace"), ws.numel(), st))
+    return (am, ml) if want_max else am
+
+
+def lmhead_greedy_verify_fp8(h, w_lm, w_scale, tokens, *, want_max=False, out=None,
+                             workspace=None, stream=None):
+    """fp8 lm_head + greedy argmax + greedy verdict of the chain `tokens`.
+    Returns (argmax, accept) (, max_logit)."""
+    M, H = h.shape
+    V = w_lm.shape[0]
+    dev = h.device
+    am, acc, ml = out if out is not None else (None, None, None)
+    if am is None:
+        am = torch.empty(M, dtype=torch.int32, device=dev)
+    if acc is None:
+        acc = torch.empty(2, dtype=torch.int32, device=dev)
+    if want_max and ml is None:
+        ml = torch.empty(M, dtype=torch.float32, device=dev)
+    st = _stream(stream)
+    nbytes = lmhead_argmax_workspace_bytes(M, V)
+    ws = workspace if workspace is not None else Workspace.get("lmhead", nbytes, dev, st)
+    _check("lmhead_greedy_verify_fp8", lib().lmhead_greedy_verify_fp8(
+        _ptr(h, "h", _BF16), _ptr(w_lm, "w_lm", _U8, (V, H)),
+        _ptr(w_scale, "w_scale", (torch.float32,), (V,)),
+        _ptr(tokens, "tokens", (torch.int32,), (M,)), M, H, V,
+        _ptr(am, "argmax", (torch.int32,), (M,)),
+        _ptr(ml, "max_logit", (torch.float32,), (M,)) if want_max else None,
+        _ptr(acc, "accept", (torch.int32,), (2,)),
+        _ptr(ws, "workspace"), ws.numel(), st))
+    return (am, acc, ml) if want_max else (am, acc)
+
+
+def _fp8_expert_ptrs(E, I, H, w_gate, s_gate, w_up, s_up, w_down, s_down):
+    return (_ptr(w_gate, "w_gate", _U8, (E, I, H)), _ptr(s_gate, "s_gate", (torch.float32,), (E, I)),
+            _ptr(w_up, "w_up", _U8, (E, I, H)), _ptr(s_up, "s_up", (torch.float32,), (E, I)),
+            _ptr(w_down, "w_down", _U8, (E, H, I)), _ptr(s_down, "s_down", (torch.float32,), (E, H)))
+
+
+def moe_expert_ffn_fp8(x, topk_idx, topk_w, w_gate, s_gate, w_up, s_up, w_down, s_down, *,
+                       out=None, workspace=None, stream=None):
+    """Selected experts' SwiGLU FFN + combine with fp8 weights (E4M3 codes,
+    fp32 row scales). Returns out [M,H] fp32."""
+    M, H = x.shape
+    _, k = topk_idx.shape
+    E, I, _ = w_gate.shape
+    dev = x.device
+    o = out if out is not None else torch.empty((M, H), dtype=torch.float32, device=dev)
+    st = _stream(stream)
+    nbytes = moe_expert_ffn_workspace_bytes(M, H, I, E, k)
+    ws = workspace if workspace is not None else Workspace.get("ffn", nbytes, dev, st)
+    _check("moe_expert_ffn_fp8", lib().moe_expert_ffn_fp8(
+        _ptr(x, "x", _BF16), _ptr(topk_idx, "topk_idx", (torch.int32,), (M, k)),
+        _ptr(topk_w, "topk_w", (torch.float32,), (M, k)),
+        *_fp8_expert_ptrs(E, I, H, w_gate, s_gate, w_up, s_up, w_down, s_down),
+        M, H, I, E, k, _ptr(o, "out", (torch.float32,), (M, H)),
+        _ptr(ws, "workspace"), ws.numel(), st))
+    return o
+
+
+def moe_layer_fp8(x, w_router, w_gate, s_gate, w_up, s_up, w_down, s_down, k: int, bias=None,
+                  *, out=None, workspace=None, stream=None):
+    """Route (bf16 gate) + fp8 expert FFN. Returns (topk_idx, topk_w, out)."""
+    M, H = x.shape
+    E, I, _ = w_gate.shape
+    dev = x.device
+    idx, w, o = out if out is not None else (None, None, None)
+    if idx is None:
+        idx = torch.empty((M, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((M, k), dtype=torch.float32, device=dev)
+    if o is None:
+        o = torch.empty((M, H), dtype=torch.float32, device=dev)
+    st = _stream(stream)
+    nbytes = moe_layer_workspace_bytes(M, H, I, E, k)
+    ws = workspace if workspace is not None else Workspace.get("layer", nbytes, dev, st)
+    _check("moe_layer_fp8", lib().moe_layer_fp8(
+        _ptr(x, "x", _BF16), _ptr(w_router, "w_router", _BF16, (E, H)),
+        _ptr(bias, "bias", (torch.float32,), (E,)),
+        *_fp8_expert_ptrs(E, I, H, w_gate, s_gate, w_up, s_up, w_down, s_down),
+        M, H, I, E, k, _ptr(idx, "topk_idx", (torch.int32,), (M, k)),
         _ptr(w, "topk_w", (torch.float32,), (M, k)),
         _ptr(o, "out", (torch.float32,), (M, H)), _ptr(ws, "workspace"), ws.numel(), st))
     return idx, w, o

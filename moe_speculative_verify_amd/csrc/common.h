@@ -46,6 +46,23 @@ __device__ __forceinline__ float dot8_bf16(u32x4 w, u32x4 x, float acc)
     return acc;
 }
 
+// fp8 weights are OCP E4M3 codes with one fp32 scale per output row. Every
+// E4M3 value is exact in bf16, so the codes are widened to bf16 in registers
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1: two codes of one 16-bit half
+// per instruction, the lower byte into the lower half) and the bf16 dot
+// products and MFMAs run unchanged; the row scale multiplies the fp32 sum.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// eight codes (two words) -> eight bf16 (one 16-byte chunk), in order
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1)
+{
+    return u32x4{e4m3x2_to_bf16x2<false>(w0), e4m3x2_to_bf16x2<true>(w0),
+                 e4m3x2_to_bf16x2<false>(w1), e4m3x2_to_bf16x2<true>(w1)};
+}
+
 // Weight streams are read once per call: non-temporal 128-bit loads keep
 // them from displacing the small reused tensors in the caches.
 __device__ __forceinline__ u32x4 load_stream(const u32x4 *p)

@@ -231,36 +231,48 @@ __device__ __forceinline__ float wave_total(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
-__host__ __device__ inline size_t down_gemv_act_bytes(int NP, int I)
+// K blocks of a W_down row: kDnCh 16-byte chunks, 512 bf16 or 1024 fp8
+// columns; the activations sit in LDS as bf16 rows padded to whole blocks
+__host__ __device__ inline int down_gemv_nkb(int I, bool w8)
 {
-    const int nkb = (I / 8 + kDnCh - 1) / kDnCh;
-    return align_up((size_t)NP * nkb * kDnCh * 16, 256);
+    const int nwc = w8 ? I / 16 : I / 8;
+    return (nwc + kDnCh - 1) / kDnCh;
 }
-__host__ __device__ inline size_t down_gemv_lds_bytes(int R, int NP, int I)
+__host__ __device__ inline size_t down_gemv_act_bytes(int NP, int I, bool w8)
 {
-    const int nkb = (I / 8 + kDnCh - 1) / kDnCh;
-    return down_gemv_act_bytes(NP, I) + (size_t)NP * nkb * R * sizeof(float);
+    return align_up((size_t)NP * down_gemv_nkb(I, w8) * kDnCh * (w8 ? 2 : 1) * 16, 256);
+}
+__host__ __device__ inline size_t down_gemv_lds_bytes(int R, int NP, int I, bool w8)
+{
+    return down_gemv_act_bytes(NP, I, w8) +
+           (size_t)NP * down_gemv_nkb(I, w8) * R * sizeof(float);
 }
 
-template <int R, int NB>
+// W8: fp8 W_down (E4M3 codes, an fp32 scale per row in sd): a block is
+// 1024 columns, each chunk widened to two bf16 chunks that meet two
+// activation chunks; the row's scale is one more per-lane load of the block
+// and multiplies the reduced sum.
+template <int R, int NB, bool W8>
 __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
     const u32x4 *__restrict__ act, const int *__restrict__ topk_idx,
     const float *__restrict__ topk_w, const u32x4 *__restrict__ wd,
-    const u32x4 *__restrict__ wds, int M, int H, int I, int E, int k, int ns,
-    float *__restrict__ out)
+    const u32x4 *__restrict__ wds, const float *__restrict__ sd, int M, int H, int I,
+    int E, int k, int ns, float *__restrict__ out)
 {
+    constexpr int kLoads = R + (W8 ? 1 : 0);             // loads per block
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ Groups g;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
-    const int nch = I / 8;                               // K = I here
-    const int nkb = (nch + kDnCh - 1) / kDnCh;
-    const int xs = nkb * kDnCh;                          // LDS activation row, chunks
+    const int nch = I / 8;                               // bf16 activation chunks (K = I)
+    const int nwc = W8 ? I / 16 : nch;                   // weight chunks per row
+    const int nkb = down_gemv_nkb(I, W8);
+    const int xs = nkb * kDnCh * (W8 ? 2 : 1);           // LDS activation row, chunks
     const int NP = M * k, NPT = NP + ns * M;
     const int r0 = blockIdx.x * R;
     const int nr = min(R, H - r0);
     u32x4 *s_act = (u32x4 *)smem;                        // [NPT][xs]
-    float *s_y = (float *)(smem + down_gemv_act_bytes(NPT, I));  // [NPT][nkb][R]
+    float *s_y = (float *)(smem + down_gemv_act_bytes(NPT, I, W8));  // [NPT][nkb][R]
 
     // prologue: pair ids and buckets; then the ring's first weight blocks
     // and every pair's activation row into LDS (direct-to-LDS), so the
@@ -281,42 +293,64 @@ __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
     // block for each of the R rows. Past the end of the sequence the same
     // number of loads rereads the first kilobyte of W_down (cached), so every
     // wait is one constant; the choice is an index select, one base pointer.
-    auto issue = [&](int X, u32x4 (&dst)[R]) {
+    auto issue = [&](int X, u32x4 (&dst)[R], float &sdv) {
         const bool real = X < nblk;
         const int Xr = real ? X : 0;
         const int v = wave + kXWaves * (Xr / nkb), kb = Xr % nkb;
         const int ev = uniform(g.vexp[min(v, kMaxNP - 1)]);
         const bool sh = real && ev >= E;                 // the shared expert's slab
-        const u32x4 *bp = (sh ? wds : wd) + (real && !sh ? (size_t)ev * H * nch : 0);
+        const size_t ebase = real && !sh ? (size_t)ev * H : 0;   // first row of the slab
+        // the shared slab's rows are reached through off below; dummy blocks
+        // read wd itself (this form of the select also keeps the captured
+        // pointers out of scratch)
+        const u32x4 *bp = sh ? wds : wd + ebase * nwc;
         int c = kb * kDnCh + lane;
-        c = c < nch ? c : nch - 1;                       // K tail: zeroed before use
-        const int cd = min(lane, nch - 1);
+        c = c < nwc ? c : nwc - 1;                       // K tail: zeroed before use
+        const int cd = min(lane, nwc - 1);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int row = min(r0 + r, H - 1);          // rows past H: unused
-            int off = real ? row * nch + c : cd;
+            int off = real ? row * nwc + c : cd;
             asm volatile("" : "+v"(off));                // one load on one path: no branch
             dst[r] = load_stream(bp + off);
         }
+        if constexpr (W8) {                              // lane r < R: row r's scale
+            int si = real ? (int)min(r0 + min(lane, R - 1), H - 1) : 0;
+            asm volatile("" : "+v"(si));
+            sdv = sd[ebase + si];
+        }
     };
-    auto consume = [&](int X, u32x4 (&wr)[R]) {
+    auto consume = [&](int X, u32x4 (&wr)[R], float sdv) {
         const int v = wave + kXWaves * (X / nkb), kb = X % nkb;
         const int npair = uniform(g.vcnt[v]);
         const int pb = uniform(g.vbeg[v]);
-        if (kb * kDnCh + kDnCh > nch) {                  // uniform: the K tail block
-            const bool ok = kb * kDnCh + lane < nch;
+        if (kb * kDnCh + kDnCh > nwc) {                  // uniform: the K tail block
+            const bool ok = kb * kDnCh + lane < nwc;
 #pragma unroll
             for (int r = 0; r < R; ++r)
                 wr[r] = ok ? wr[r] : u32x4{0, 0, 0, 0};
         }
         for (int jj = 0; jj < npair; ++jj) {
             const int p = uniform(g.sorted[pb + jj]);
-            const u32x4 a = s_act[p * xs + kb * kDnCh + lane];
             float yv = 0.0f;
+            if constexpr (W8) {
+                const u32x4 *ar = s_act + p * xs + 2 * (kb * kDnCh + lane);
+                const u32x4 a0 = ar[0], a1 = ar[1];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const float t = wave_total(dot8_bf16(wr[r], a, 0.0f));
-                yv = lane == r ? t : yv;
+                for (int r = 0; r < R; ++r) {
+                    float d = dot8_bf16(e4m3x8_to_bf16(wr[r].x, wr[r].y), a0, 0.0f);
+                    d = dot8_bf16(e4m3x8_to_bf16(wr[r].z, wr[r].w), a1, d);
+                    const float t = wave_total(d);
+                    yv = lane == r ? t : yv;
+                }
+                yv *= sdv;                               // lane r: row r's scale
+            } else {
+                const u32x4 a = s_act[p * xs + kb * kDnCh + lane];
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const float t = wave_total(dot8_bf16(wr[r], a, 0.0f));
+                    yv = lane == r ? t : yv;
+                }
             }
             if (lane < nr)
                 s_y[(p * nkb + kb) * R + lane] = yv;
@@ -324,19 +358,20 @@ __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
     };
 
     u32x4 w[NB][R];
+    float sdr[NB] = {};                                  // fp8 row scales (unused for bf16)
 #pragma unroll
     for (int q = 0; q < NB - 1; ++q)
-        issue(q, w[q]);
+        issue(q, w[q], sdr[q]);
     stage_rows_lds(act, NPT, nch, s_act, xs);
     wait_vmcnt<0>();                                     // this wave's staging has landed
     lds_barrier();                                       // ... and every other wave's staging
     for (int X0 = 0; X0 < nblk; X0 += NB) {
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
-            issue(X0 + q + NB - 1, w[(q + NB - 1) % NB]);
-            wait_vmcnt<(NB - 1) * R>();                  // block X0 + q has landed
+            issue(X0 + q + NB - 1, w[(q + NB - 1) % NB], sdr[(q + NB - 1) % NB]);
+            wait_vmcnt<(NB - 1) * kLoads>();             // block X0 + q has landed
             if (X0 + q < nblk)
-                consume(X0 + q, w[q]);
+                consume(X0 + q, w[q], sdr[q]);
         }
     }
     wait_vmcnt<0>();                                     // dummy loads have landed
@@ -378,11 +413,15 @@ __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
 // taken in fp32 and rounded once to bf16. With more than KC * 64 chunks per
 // row a unit spans several K blocks; the per-block sums of each pair are
 // added in LDS in block order.
-template <int KC, int NB>
+// W8: fp8 weights (E4M3 codes, 16 per 16-byte chunk, an fp32 scale per
+// row in sg / su); each chunk is widened to two bf16 chunks that meet two x
+// chunks, and the row scales multiply the reduced sums before the SwiGLU.
+template <int KC, int NB, bool W8>
 __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
     const u32x4 *__restrict__ x, const int *__restrict__ topk_idx,
     const u32x4 *__restrict__ wg, const u32x4 *__restrict__ wu,
-    const u32x4 *__restrict__ wgs, const u32x4 *__restrict__ wus, int M, int H,
+    const u32x4 *__restrict__ wgs, const u32x4 *__restrict__ wus,
+    const float *__restrict__ sg, const float *__restrict__ su, int M, int H,
     int I, int E, int k, int ns, uint16_t *__restrict__ act)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -390,9 +429,10 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
     __shared__ float s_acc[kXWaves][16][2];      // per-pair running sums
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
-    const int nch = H / 8;                               // 16-byte chunks per row
-    const int nbu = (nch + KC * kWave - 1) / (KC * kWave);   // K blocks per unit
-    const int xs = nbu * KC * kWave;                     // LDS x row, chunks
+    const int nch = H / 8;                               // 16-byte x chunks per row
+    const int nwc = W8 ? H / 16 : nch;                   // 16-byte weight chunks per row
+    const int nbu = (nwc + KC * kWave - 1) / (KC * kWave);   // K blocks per unit
+    const int xs = nbu * KC * kWave * (W8 ? 2 : 1);      // LDS x row, chunks
     const int NP = M * k, NPT = NP + ns * M;
     u32x4 *s_x = (u32x4 *)smem;                          // [M][xs]
 
@@ -420,47 +460,65 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
     // Block of a tag: KC loads of the gate row, KC of the up row. A -1 tag
     // rereads the first kilobyte of W_gate instead, so every wait is one
     // constant.
-    auto issue = [&](int tag, u32x4 (&dg)[KC], u32x4 (&du)[KC]) {
+    auto issue = [&](int tag, u32x4 (&dg)[KC], u32x4 (&du)[KC], float &sgv, float &suv) {
         const bool real = tag >= 0;
         const int u = real ? tag >> 4 : 0, kb = real ? tag & 15 : 0;
         const int v = min(u / I, kMaxNP - 1), i = u % I;
         const int ev = uniform(g.vexp[v]);
         const bool sh = real && ev >= E;                 // the shared expert's slabs
-        const size_t roff = real ? ((size_t)(sh ? 0 : ev) * I + i) * nch : 0;
-        const u32x4 *bg = (sh ? wgs : wg) + roff;        // uniform
-        const u32x4 *bu = (sh ? wus : wu) + roff;
+        const size_t row = real ? (size_t)(sh ? 0 : ev) * I + i : 0;   // row in its tensor
+        const size_t roff = row * nwc;
+        const u32x4 *bg = sh ? wgs + roff : wg + roff;   // uniform
+        const u32x4 *bu = sh ? wus + roff : wu + roff;
+        if constexpr (W8) {                              // the rows' scales (uniform)
+            sgv = sg[row];
+            suv = su[row];
+        }
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
             int ch = (kb * KC + c) * kWave + lane;
-            ch = ch < nch ? ch : nch - 1;                // K tail: zeroed before use
-            int off = real ? ch : min(lane, nch - 1);
+            ch = ch < nwc ? ch : nwc - 1;                // K tail: zeroed before use
+            int off = real ? ch : min(lane, nwc - 1);
             asm volatile("" : "+v"(off));                // one load on one path: no branch
             dg[c] = load_stream(bg + off);
             du[c] = load_stream(bu + off);
         }
     };
-    auto consume = [&](int tag, u32x4 (&dg)[KC], u32x4 (&du)[KC]) {
+    auto consume = [&](int tag, u32x4 (&dg)[KC], u32x4 (&du)[KC], float sgv, float suv) {
         const int u = tag >> 4, kb = tag & 15;
         const int v = u / I, i = u % I;
         const int npair = uniform(g.vcnt[v]);
         const int pb = uniform(g.vbeg[v]);
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-            if ((kb * KC + c) * kWave + kWave > nch) {   // uniform: the K tail
-                const bool ok = (kb * KC + c) * kWave + lane < nch;
+            if ((kb * KC + c) * kWave + kWave > nwc) {   // uniform: the K tail
+                const bool ok = (kb * KC + c) * kWave + lane < nwc;
                 dg[c] = ok ? dg[c] : u32x4{0, 0, 0, 0};
                 du[c] = ok ? du[c] : u32x4{0, 0, 0, 0};
             }
         }
         for (int jj = 0; jj < npair; ++jj) {
             const int p = uniform(g.sorted[pb + jj]);
-            const u32x4 *xr = s_x + pair_token(p, NP, k) * xs + kb * KC * kWave + lane;
             float ga = 0.0f, ua = 0.0f;
+            if constexpr (W8) {
+                // chunk c holds columns 16 ch .. 16 ch + 15: x chunks 2 ch, 2 ch + 1
+                const u32x4 *xr = s_x + pair_token(p, NP, k) * xs + 2 * (kb * KC * kWave + lane);
 #pragma unroll
-            for (int c = 0; c < KC; ++c) {
-                const u32x4 xv = xr[c * kWave];
-                ga = dot8_bf16(dg[c], xv, ga);
-                ua = dot8_bf16(du[c], xv, ua);
+                for (int c = 0; c < KC; ++c) {
+                    const u32x4 x0 = xr[2 * c * kWave], x1 = xr[2 * c * kWave + 1];
+                    ga = dot8_bf16(e4m3x8_to_bf16(dg[c].x, dg[c].y), x0, ga);
+                    ga = dot8_bf16(e4m3x8_to_bf16(dg[c].z, dg[c].w), x1, ga);
+                    ua = dot8_bf16(e4m3x8_to_bf16(du[c].x, du[c].y), x0, ua);
+                    ua = dot8_bf16(e4m3x8_to_bf16(du[c].z, du[c].w), x1, ua);
+                }
+            } else {
+                const u32x4 *xr = s_x + pair_token(p, NP, k) * xs + kb * KC * kWave + lane;
+#pragma unroll
+                for (int c = 0; c < KC; ++c) {
+                    const u32x4 xv = xr[c * kWave];
+                    ga = dot8_bf16(dg[c], xv, ga);
+                    ua = dot8_bf16(du[c], xv, ua);
+                }
             }
             float gt = wave_total(ga), ut = wave_total(ua);
             if (nbu > 1) {                               // uniform
@@ -476,6 +534,10 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
                     continue;
                 }
             }
+            if constexpr (W8) {                          // the rows' scales
+                gt *= sgv;
+                ut *= suv;
+            }
             // SwiGLU in fp32, one rounding to bf16
             if (lane == 0)
                 act[(size_t)p * I + i] = (uint16_t)f32_to_bf16_rne(gt / (1.0f + expf(-gt)) * ut);
@@ -483,9 +545,10 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
     };
 
     u32x4 wgr[NB][KC], wur[NB][KC];
+    float sgr[NB] = {}, sur[NB] = {};                    // fp8 row scales (unused for bf16)
 #pragma unroll
     for (int q = 0; q < NB - 1; ++q)
-        issue(tag_of(q), wgr[q], wur[q]);
+        issue(tag_of(q), wgr[q], wur[q], sgr[q], sur[q]);
     stage_rows_lds(x, M, nch, s_x, xs);
     wait_vmcnt<0>();                                     // this wave's share of x has landed
     lds_barrier();                                       // ... and every other wave's
@@ -493,20 +556,20 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
             const int nq = (q + NB - 1) % NB;
-            issue(tag_of(X0 + q + NB - 1), wgr[nq], wur[nq]);
+            issue(tag_of(X0 + q + NB - 1), wgr[nq], wur[nq], sgr[nq], sur[nq]);
             wait_vmcnt<(NB - 1) * 2 * KC>();             // block X0 + q has landed
             if (X0 + q < nblk)
-                consume(tag_of(X0 + q), wgr[q], wur[q]);
+                consume(tag_of(X0 + q), wgr[q], wur[q], sgr[q], sur[q]);
         }
     }
     wait_vmcnt<0>();                                     // dummy loads have landed
 }
 
-__host__ __device__ inline size_t up_gemv_lds_bytes(int M, int H, int KC)
+__host__ __device__ inline size_t up_gemv_lds_bytes(int M, int H, int KC, bool w8)
 {
-    const int nch = H / 8;
-    const int nbu = (nch + KC * kWave - 1) / (KC * kWave);
-    return align_up((size_t)M * nbu * KC * kWave * 16, 256);
+    const int nwc = w8 ? H / 16 : H / 8;
+    const int nbu = (nwc + KC * kWave - 1) / (KC * kWave);
+    return align_up((size_t)M * nbu * KC * kWave * (w8 ? 2 : 1) * 16, 256);
 }
 
 // ------------------------------------------------------------------ host
@@ -514,32 +577,47 @@ __host__ __device__ inline size_t up_gemv_lds_bytes(int M, int H, int KC)
 // GEMV up kernel: KC 16-byte chunks per lane per row and block (a unit is
 // one block when a row has at most 5 * 64 chunks), a 4-deep register ring
 constexpr int kUpGemvNB = 4;
-static int up_gemv_kc(int H)
+static int up_gemv_kc(int H, bool w8)
 {
-    const int need = (H / 8 + kWave - 1) / kWave;
+    const int need = ((w8 ? H / 16 : H / 8) + kWave - 1) / kWave;
     return need <= 5 ? need : 4;
 }
-static bool up_gemv_fits(int M, int H)
+static bool up_gemv_fits(int M, int H, bool w8)
 {
-    return up_gemv_lds_bytes(M, H, up_gemv_kc(H)) <= (size_t)kXLdsDynMax;
+    return up_gemv_lds_bytes(M, H, up_gemv_kc(H, w8), w8) <= (size_t)kXLdsDynMax;
 }
 
 // The experts of one call: routed weights and, when ns = 1, the shared
 // expert's (gate [I,H], up [I,H], down [H,I]).
+// With w8 the routed tensors are fp8 codes with per-row scales sg, su, sd.
 struct Experts {
-    const uint16_t *wg, *wu, *wd;
+    const void *wg, *wu, *wd;
     const uint16_t *wgs, *wus, *wds;
     int ns;
+    bool w8;
+    const float *sg, *su, *sd;
 };
 
-template <int KC>
+template <int KC, bool W8>
 static void launch_up_gemv(const uint16_t *x, const int *idx, const Experts &ex, int M, int H,
                            int I, int E, int k, uint16_t *act, hipStream_t st)
 {
-    hipLaunchKernelGGL((expert_up_gemv_kernel<KC, kUpGemvNB>), dim3(kXGrid), dim3(kXThreads),
-                       up_gemv_lds_bytes(M, H, KC), st, (const u32x4 *)x, idx,
-                       (const u32x4 *)ex.wg, (const u32x4 *)ex.wu, (const u32x4 *)ex.wgs,
-                       (const u32x4 *)ex.wus, M, H, I, E, k, ex.ns, act);
+    hipLaunchKernelGGL((expert_up_gemv_kernel<KC, kUpGemvNB, W8>), dim3(kXGrid),
+                       dim3(kXThreads), up_gemv_lds_bytes(M, H, KC, W8), st, (const u32x4 *)x,
+                       idx, (const u32x4 *)ex.wg, (const u32x4 *)ex.wu, (const u32x4 *)ex.wgs,
+                       (const u32x4 *)ex.wus, ex.sg, ex.su, M, H, I, E, k, ex.ns, act);
+}
+template <bool W8>
+static void launch_up_gemv_kc(const uint16_t *x, const int *idx, const Experts &ex, int M,
+                              int H, int I, int E, int k, uint16_t *act, hipStream_t st)
+{
+    switch (up_gemv_kc(H, W8)) {
+    case 1: launch_up_gemv<1, W8>(x, idx, ex, M, H, I, E, k, act, st); break;
+    case 2: launch_up_gemv<2, W8>(x, idx, ex, M, H, I, E, k, act, st); break;
+    case 3: launch_up_gemv<3, W8>(x, idx, ex, M, H, I, E, k, act, st); break;
+    case 4: launch_up_gemv<4, W8>(x, idx, ex, M, H, I, E, k, act, st); break;
+    default: launch_up_gemv<5, W8>(x, idx, ex, M, H, I, E, k, act, st); break;
+    }
 }
 
 // rows per down workgroup: at least ceil(H / 256), from the instantiated set
@@ -556,9 +634,9 @@ static int down_rows(int H)
 constexpr int down_gemv_nb(int R) { return R <= 10 ? 4 : (R <= 12 ? 3 : 2); }
 // the GEMV down kernel runs when every pair's activation row fits in LDS
 // (NPT pairs: M*k routed, plus M with a shared expert)
-static bool down_gemv_fits(int R, int NPT, int I)
+static bool down_gemv_fits(int R, int NPT, int I, bool w8)
 {
-    return down_gemv_lds_bytes(R, NPT, I) <= (size_t)kXLdsDynMax;
+    return down_gemv_lds_bytes(R, NPT, I, w8) <= (size_t)kXLdsDynMax;
 }
 static size_t down_lds_bytes(int R, int NB, int NPT)
 {
@@ -592,7 +670,7 @@ static moe_status_t ffn_check(const uint16_t *x, const int32_t *topk_idx,
         return s;
     if (I < 1)
         return MOE_ERR_SHAPE;
-    if (I % 8 != 0 || I > kMaxDim || !up_gemv_fits(M, H) || down_rows(H) == 0 ||
+    if (I % 8 != 0 || I > kMaxDim || !up_gemv_fits(M, H, false) || down_rows(H) == 0 ||
         down_nb(down_rows(H), M * k) == 0)
         return MOE_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) ||
@@ -613,13 +691,13 @@ static hipError_t set_lds_attributes()
 {
     hipError_t e = hipSuccess;
     auto chk = [&](hipError_t r) { if (r != hipSuccess) e = r; };
-    chk(allow_lds(expert_up_gemv_kernel<1, kUpGemvNB>));
-    chk(allow_lds(expert_up_gemv_kernel<2, kUpGemvNB>));
-    chk(allow_lds(expert_up_gemv_kernel<3, kUpGemvNB>));
-    chk(allow_lds(expert_up_gemv_kernel<4, kUpGemvNB>));
-    chk(allow_lds(expert_up_gemv_kernel<5, kUpGemvNB>));
+#define MV_UP_ATTR(KC) chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, true>));
+    MV_UP_ATTR(1) MV_UP_ATTR(2) MV_UP_ATTR(3) MV_UP_ATTR(4) MV_UP_ATTR(5)
+#undef MV_UP_ATTR
 #define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, 2>)); chk(allow_lds(expert_down_kernel<R, 3>)); \
-    chk(allow_lds(expert_down_gemv_kernel<R, down_gemv_nb(R)>));
+    chk(allow_lds(expert_down_gemv_kernel<R, down_gemv_nb(R), false>)); \
+    chk(allow_lds(expert_down_gemv_kernel<R, down_gemv_nb(R), true>));
     MV_DOWN_ATTR(4) MV_DOWN_ATTR(8) MV_DOWN_ATTR(10) MV_DOWN_ATTR(12) MV_DOWN_ATTR(16)
 #undef MV_DOWN_ATTR
     return e;
@@ -631,10 +709,17 @@ static void launch_down_gemv(const uint16_t *act, const int *idx, const float *t
                              float *out, hipStream_t st)
 {
     const int grid = (H + R - 1) / R;
-    const size_t lds = down_gemv_lds_bytes(R, M * k + ex.ns * M, I);
-    hipLaunchKernelGGL((expert_down_gemv_kernel<R, down_gemv_nb(R)>), dim3(grid),
-                       dim3(kXThreads), lds, st, (const u32x4 *)act, idx, tw,
-                       (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, M, H, I, E, k, ex.ns, out);
+    const size_t lds = down_gemv_lds_bytes(R, M * k + ex.ns * M, I, ex.w8);
+    if (ex.w8)
+        hipLaunchKernelGGL((expert_down_gemv_kernel<R, down_gemv_nb(R), true>), dim3(grid),
+                           dim3(kXThreads), lds, st, (const u32x4 *)act, idx, tw,
+                           (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, ex.sd, M, H, I, E, k,
+                           ex.ns, out);
+    else
+        hipLaunchKernelGGL((expert_down_gemv_kernel<R, down_gemv_nb(R), false>), dim3(grid),
+                           dim3(kXThreads), lds, st, (const u32x4 *)act, idx, tw,
+                           (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, nullptr, M, H, I, E, k,
+                           ex.ns, out);
 }
 
 template <int R>
@@ -668,20 +753,17 @@ static moe_status_t ffn_enqueue(const uint16_t *x, const int32_t *topk_idx,
     // puts it
     uint16_t *act = (uint16_t *)data;
 
-    switch (up_gemv_kc(H)) {
-    case 1: launch_up_gemv<1>(x, topk_idx, ex, M, H, I, E, k, act, st); break;
-    case 2: launch_up_gemv<2>(x, topk_idx, ex, M, H, I, E, k, act, st); break;
-    case 3: launch_up_gemv<3>(x, topk_idx, ex, M, H, I, E, k, act, st); break;
-    case 4: launch_up_gemv<4>(x, topk_idx, ex, M, H, I, E, k, act, st); break;
-    default: launch_up_gemv<5>(x, topk_idx, ex, M, H, I, E, k, act, st); break;
-    }
+    if (ex.w8)
+        launch_up_gemv_kc<true>(x, topk_idx, ex, M, H, I, E, k, act, st);
+    else
+        launch_up_gemv_kc<false>(x, topk_idx, ex, M, H, I, E, k, act, st);
     moe_status_t s = check_launch();
     if (s != MOE_OK)
         return s;
 
     const int R = down_rows(H);
     const int NPT = M * k + ex.ns * M;
-    if (down_gemv_fits(R, NPT, I)) {
+    if (down_gemv_fits(R, NPT, I, ex.w8)) {
         switch (R) {
         case 4: launch_down_gemv<4>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
         case 8: launch_down_gemv<8>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
@@ -691,6 +773,8 @@ static moe_status_t ffn_enqueue(const uint16_t *x, const int32_t *topk_idx,
         }
         return check_launch();
     }
+    if (ex.w8)                       // fp8 runs the GEMV down kernel only (checked)
+        return MOE_ERR_UNSUPPORTED;
     const int nbd = down_nb(R, NPT);
     switch (R) {
     case 4: launch_down_r<4>(nbd, act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
@@ -759,7 +843,7 @@ extern "C" moe_status_t moe_expert_ffn(const uint16_t *x, const int32_t *topk_id
         return MOE_ERR_ALIGN;
     if (workspace_bytes < moe_expert_ffn_workspace_bytes(M, H, I, E, k))
         return MOE_ERR_WORKSPACE;
-    const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0};
+    const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0, false, nullptr, nullptr, nullptr};
     return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k,
                        out, (char *)workspace + kWsHeader, (hipStream_t)stream);
 }
@@ -784,7 +868,8 @@ extern "C" moe_status_t moe_expert_ffn_shared(
         return MOE_ERR_ALIGN;
     if (workspace_bytes < moe_expert_ffn_workspace_bytes(M, H, I, E, k))
         return MOE_ERR_WORKSPACE;
-    const Experts ex{w_gate, w_up, w_down, w_gate_shared, w_up_shared, w_down_shared, 1};
+    const Experts ex{w_gate, w_up, w_down, w_gate_shared, w_up_shared, w_down_shared, 1, false,
+                      nullptr, nullptr, nullptr};
     return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k,
                        out, (char *)workspace + kWsHeader, (hipStream_t)stream);
 }
@@ -829,7 +914,7 @@ extern "C" moe_status_t moe_layer(const uint16_t *x, const uint16_t *w_router,
                       workspace, st, nullptr, 0.0f, nullptr);
     if (s != MOE_OK)
         return s;
-    const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0};
+    const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0, false, nullptr, nullptr, nullptr};
     return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k,
                        out, (char *)workspace + r, st);
 }
@@ -863,7 +948,8 @@ extern "C" moe_status_t moe_layer_shared(
                       workspace, st, nullptr, 0.0f, nullptr);
     if (s != MOE_OK)
         return s;
-    const Experts ex{w_gate, w_up, w_down, w_gate_shared, w_up_shared, w_down_shared, 1};
+    const Experts ex{w_gate, w_up, w_down, w_gate_shared, w_up_shared, w_down_shared, 1, false,
+                      nullptr, nullptr, nullptr};
     return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k,
                        out, (char *)workspace + r, st);
 }
@@ -901,7 +987,86 @@ extern "C" moe_status_t moe_layer_rmsnorm(const uint16_t *h, const uint16_t *gam
                       workspace, st, gamma, eps, x_norm);
     if (s != MOE_OK)
         return s;
-    const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0};
+    const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0, false, nullptr, nullptr, nullptr};
     return ffn_enqueue(x_norm, topk_idx, topk_w, ex, M, H, I, E, k,
                        out, (char *)workspace + r, st);
+}
+
+// fp8 experts: E4M3 codes [E,I,H] / [E,H,I] with fp32 scales per row; H and
+// I multiples of 16; the down projection's activations must fit in LDS
+static moe_status_t ffn8_check(const uint16_t *x, const int32_t *topk_idx,
+                               const float *topk_w, const uint8_t *w_gate, const float *s_gate,
+                               const uint8_t *w_up, const float *s_up, const uint8_t *w_down,
+                               const float *s_down, int32_t M, int32_t H, int32_t I,
+                               int32_t E, int32_t k, const float *out)
+{
+    if (!x || !topk_idx || !topk_w || !w_gate || !w_up || !w_down || !s_gate || !s_up ||
+        !s_down || !out)
+        return MOE_ERR_NULL;
+    moe_status_t s = check_moe_shape(M, H, E, k);
+    if (s != MOE_OK)
+        return s;
+    if (I < 1)
+        return MOE_ERR_SHAPE;
+    if (H % 16 != 0 || I % 16 != 0 || I > kMaxDim || !up_gemv_fits(M, H, true) ||
+        down_rows(H) == 0 || !down_gemv_fits(down_rows(H), M * k, I, true))
+        return MOE_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
+        !aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down) || !aligned4(topk_idx) ||
+        !aligned4(topk_w) || !aligned4(out))
+        return MOE_ERR_ALIGN;
+    return MOE_OK;
+}
+
+extern "C" moe_status_t moe_expert_ffn_fp8(
+    const uint16_t *x, const int32_t *topk_idx, const float *topk_w, const uint8_t *w_gate,
+    const float *s_gate, const uint8_t *w_up, const float *s_up, const uint8_t *w_down,
+    const float *s_down, int32_t M, int32_t H, int32_t I, int32_t E, int32_t k, float *out,
+    void *workspace, size_t workspace_bytes, void *stream)
+{
+    moe_status_t s = ffn8_check(x, topk_idx, topk_w, w_gate, s_gate, w_up, s_up, w_down,
+                                s_down, M, H, I, E, k, out);
+    if (s != MOE_OK)
+        return s;
+    if (!workspace)
+        return MOE_ERR_NULL;
+    if (!aligned16(workspace))
+        return MOE_ERR_ALIGN;
+    if (workspace_bytes < moe_expert_ffn_workspace_bytes(M, H, I, E, k))
+        return MOE_ERR_WORKSPACE;
+    const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0, true,
+                     s_gate, s_up, s_down};
+    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k, out,
+                       (char *)workspace + kWsHeader, (hipStream_t)stream);
+}
+
+extern "C" moe_status_t moe_layer_fp8(
+    const uint16_t *x, const uint16_t *w_router, const float *bias, const uint8_t *w_gate,
+    const float *s_gate, const uint8_t *w_up, const float *s_up, const uint8_t *w_down,
+    const float *s_down, int32_t M, int32_t H, int32_t I, int32_t E, int32_t k,
+    int32_t *topk_idx, float *topk_w, float *out, void *workspace, size_t workspace_bytes,
+    void *stream)
+{
+    moe_status_t s = route_check(x, w_router, bias, M, H, E, k, topk_idx, topk_w, nullptr);
+    if (s != MOE_OK)
+        return s;
+    s = ffn8_check(x, topk_idx, topk_w, w_gate, s_gate, w_up, s_up, w_down, s_down, M, H, I,
+                   E, k, out);
+    if (s != MOE_OK)
+        return s;
+    if (!workspace)
+        return MOE_ERR_NULL;
+    if (!aligned16(workspace))
+        return MOE_ERR_ALIGN;
+    if (workspace_bytes < moe_layer_workspace_bytes(M, H, I, E, k))
+        return MOE_ERR_WORKSPACE;
+    const size_t r = moe_route_workspace_bytes(M, E);
+    hipStream_t st = (hipStream_t)stream;
+    s = route_enqueue(x, w_router, bias, M, H, E, k, topk_idx, topk_w, nullptr, workspace, st,
+                      nullptr, 0.0f, nullptr);
+    if (s != MOE_OK)
+        return s;
+    const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0, true,
+                     s_gate, s_up, s_down};
+    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k, out, (char *)workspace + r, st);
 }

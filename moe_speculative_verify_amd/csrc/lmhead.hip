@@ -25,6 +25,12 @@
 //     atomic max, so the largest value and then the lowest index win
 //     whatever the order. The last workgroup to take a ticket (device-scope
 //     atomic, no spinning, no cache flush) decodes the keys and resets them.
+//   - fp8 weights (lmhead_argmax_fp8, lmhead_greedy_verify_fp8): OCP E4M3
+//     codes with one fp32 scale per vocabulary row. A block is still 512
+//     bytes of each of the 16 rows (now 512 columns), staged the same way;
+//     each MFMA step reads the lane's eight codes from LDS, widens them to
+//     bf16 (exact), and the row scales multiply the fp32 tile before the
+//     argmax.
 //   - lmhead_greedy_verify: the same launch, and the same last workgroup
 //     then takes the greedy verdict of the verify chain from the decoded
 //     tokens (section "The shape of a single-request step": the verdict is
@@ -36,39 +42,46 @@
 namespace mv {
 
 constexpr int kLmWaves = 4;
-constexpr int kLmKB = 256;                        // K elements per block
-constexpr int kLmRowBytes = kLmKB * 2;            // 512 B of a row per block
+constexpr int kLmRowBytes = 512;                  // bytes of a row per block
 constexpr int kLmRowsPerLd = 1024 / kLmRowBytes;  // rows per load instruction
 constexpr int kLmLoads = 16 / kLmRowsPerLd;       // load instructions per block
 constexpr int kLmLdStride = 1024 + 16;            // LDS bytes per load (padded)
 constexpr int kLmBuf = kLmLoads * kLmLdStride;    // one block of a tile
-constexpr int kLmSteps = kLmKB / 32;              // MFMA steps per block
+constexpr int kLmRowCh = kLmRowBytes / 16;        // 16-byte chunks of a row per block
+// K elements per block: 256 bf16 or 512 fp8 columns
+constexpr int lm_kb(bool w8) { return w8 ? kLmRowBytes : kLmRowBytes / 2; }
 
-__host__ __device__ static size_t lm_x_bytes(int M, int H)
+__host__ __device__ static size_t lm_x_bytes(int M, int H, bool w8)
 {
-    const int nkb = (H + kLmKB - 1) / kLmKB;
-    return align_up((size_t)M * (nkb * (kLmKB / 8) + 1) * 16, 256);
+    const int KB = lm_kb(w8);
+    const int nkb = (H + KB - 1) / KB;
+    return align_up((size_t)M * (nkb * (KB / 8) + 1) * 16, 256);
 }
-static size_t lm_lds_bytes(int M, int H)
+static size_t lm_lds_bytes(int M, int H, bool w8)
 {
-    return lm_x_bytes(M, H) + (size_t)kLmWaves * 2 * kLmBuf;
+    return lm_x_bytes(M, H, w8) + (size_t)kLmWaves * 2 * kLmBuf;
 }
 
+template <bool W8>
 __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
-    const u32x4 *__restrict__ h, const u32x4 *__restrict__ wl, int M, int H,
+    const u32x4 *__restrict__ h, const u32x4 *__restrict__ wl,
+    const float *__restrict__ wscale, int M, int H,
     int V, int tiles_per_wg, unsigned long long *__restrict__ keys,
     unsigned *__restrict__ ticket, int *__restrict__ argmax,
     float *__restrict__ max_logit, const int *__restrict__ tokens,
     int *__restrict__ accept)
 {
+    constexpr int KB = lm_kb(W8);
+    constexpr int kLmSteps = KB / 32;                    // MFMA steps per block
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const int nch = H / 8;                               // 16-byte chunks per row
-    const int nkb = (H + kLmKB - 1) / kLmKB;
-    const int xs = nkb * (kLmKB / 8) + 1;                // padded x row, chunks
+    const int nch = H / 8;                               // bf16 chunks of an h row
+    const int nwch = W8 ? H / 16 : nch;                  // 16-byte chunks of a weight row
+    const int nkb = (H + KB - 1) / KB;
+    const int xs = nkb * (KB / 8) + 1;                   // padded x row, chunks
     u32x4 *s_x = (u32x4 *)smem;
-    unsigned char *wbuf = smem + lm_x_bytes(M, H) + wave * 2 * kLmBuf;
+    unsigned char *wbuf = smem + lm_x_bytes(M, H, W8) + wave * 2 * kLmBuf;
 
     // hidden states into LDS with direct-to-LDS loads (all in flight at
     // once), K padding zeroed
@@ -88,7 +101,10 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     // rows the instruction covers, chunk lcol of that row's block
     const int lrow = lane / (kWave / kLmRowsPerLd);
     const int lcol = lane % (kWave / kLmRowsPerLd);
-    const int a_off = (j / kLmRowsPerLd) * kLmLdStride + (j % kLmRowsPerLd) * kLmRowBytes + g * 16;
+    // lane (j, g) reads row j's columns [32 s + 8 g, +8) of step s: 16 bytes
+    // of bf16 or 8 bytes of fp8
+    const int a_off = (j / kLmRowsPerLd) * kLmLdStride + (j % kLmRowsPerLd) * kLmRowBytes +
+                      g * (W8 ? 8 : 16);
 
     const int ntiles = (V + 15) / 16;
     const int t0 = blockIdx.x * tiles_per_wg;
@@ -102,11 +118,18 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
         for (int q = 0; q < kLmLoads; ++q) {
             int row = tile * 16 + q * kLmRowsPerLd + lrow;
             row = row < V ? row : V - 1;                 // tail rows: valid memory, ignored
-            rp[q] = wl + (size_t)row * nch;
+            rp[q] = wl + (size_t)row * nwch;
+        }
+        // fp8: the scales of this lane's four tile rows, used after the K loop
+        float rs[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if constexpr (W8) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                rs[r] = wscale[min(tile * 16 + 4 * g + r, V - 1)];
         }
         auto issue = [&](int kb, int b) {
-            int c = kb * (kLmKB / 8) + lcol;
-            c = c < nch ? c : nch - 1;                   // K tail: valid memory, x is zero there
+            int c = kb * kLmRowCh + lcol;
+            c = c < nwch ? c : nwch - 1;                 // K tail: valid memory, x is zero there
 #pragma unroll
             for (int q = 0; q < kLmLoads; ++q)
                 load_lds16(rp[q] + c, wbuf + b * kLmBuf + q * kLmLdStride);
@@ -124,12 +147,24 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
             const unsigned char *ab = wbuf + b * kLmBuf + a_off;
 #pragma unroll
             for (int s = 0; s < kLmSteps; ++s) {
-                const u32x4 a = *(const MV_LDS u32x4 *)(ab + s * 64);
-                u32x4 x = xrow[kb * (kLmKB / 8) + 4 * s];
+                u32x4 a;
+                if constexpr (W8) {
+                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                    const u32x2 q8 = *(const MV_LDS u32x2 *)(ab + s * 32);
+                    a = e4m3x8_to_bf16(q8.x, q8.y);
+                } else {
+                    a = *(const MV_LDS u32x4 *)(ab + s * 64);
+                }
+                u32x4 x = xrow[kb * (KB / 8) + 4 * s];
                 if (!tok_ok)
                     x = u32x4{0, 0, 0, 0};
                 acc = mfma_bf16(a, x, acc);
             }
+        }
+        if constexpr (W8) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[r] *= rs[r];
         }
         // rows 4g..4g+3 of the tile for token j; ascending rows, so a strict
         // comparison keeps the first of equal values
@@ -229,18 +264,22 @@ extern "C" size_t lmhead_argmax_workspace_bytes(int32_t M, int32_t V)
     return kWsHeader + align_up((size_t)M * 8, 256);
 }
 
-static moe_status_t lmhead_enqueue(const uint16_t *h, const uint16_t *w_lm,
-                                   int32_t M, int32_t H, int32_t V, int32_t *argmax,
+// w_lm: bf16 rows, or fp8 codes when w_scale is given (one scale per row)
+static moe_status_t lmhead_enqueue(const uint16_t *h, const void *w_lm, const float *w_scale,
+                                   bool w8, int32_t M, int32_t H, int32_t V, int32_t *argmax,
                                    float *max_logit, const int32_t *tokens,
                                    int32_t *accept, void *workspace,
                                    size_t workspace_bytes, void *stream)
 {
-    if (!h || !w_lm || !argmax || !workspace)
+    if (!h || !w_lm || !argmax || !workspace || (w8 && !w_scale))
         return MOE_ERR_NULL;
     if (M < 1 || H < 1 || V < 1)
         return MOE_ERR_SHAPE;
-    if (M > kMaxM || H % 8 != 0 || H > kMaxDim || lm_lds_bytes(M, H) > (size_t)kLdsDynMax)
+    if (M > kMaxM || H % (w8 ? 16 : 8) != 0 || H > kMaxDim ||
+        lm_lds_bytes(M, H, w8) > (size_t)kLdsDynMax)
         return MOE_ERR_UNSUPPORTED;
+    if (w8 && !aligned4(w_scale))
+        return MOE_ERR_ALIGN;
     if (!aligned16(h) || !aligned16(w_lm) || !aligned4(argmax) ||
         (max_logit && !aligned4(max_logit)) || !aligned16(workspace) ||
         (tokens && (!aligned4(tokens) || !aligned4(accept))))
@@ -252,18 +291,26 @@ static moe_status_t lmhead_enqueue(const uint16_t *h, const uint16_t *w_lm,
     const int ntiles = (V + 15) / 16;
     const int tpw = (ntiles + kLmGridTarget - 1) / kLmGridTarget;
     const int grid = (ntiles + tpw - 1) / tpw;
-    const size_t lds = lm_lds_bytes(M, H);
+    const size_t lds = lm_lds_bytes(M, H, w8);
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
-        attr = hipFuncSetAttribute((const void *)lmhead_kernel,
+        attr = hipFuncSetAttribute((const void *)lmhead_kernel<false>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, kLdsDynMax);
+        if (attr == hipSuccess)
+            attr = hipFuncSetAttribute((const void *)lmhead_kernel<true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsDynMax);
     });
     if (attr != hipSuccess)
         return MOE_ERR_LAUNCH;
-    hipLaunchKernelGGL(lmhead_kernel, dim3(grid), dim3(kLmWaves * kWave), lds,
-                       (hipStream_t)stream, (const u32x4 *)h, (const u32x4 *)w_lm,
-                       M, H, V, tpw, keys, ticket, argmax, max_logit, tokens, accept);
+    if (w8)
+        hipLaunchKernelGGL(lmhead_kernel<true>, dim3(grid), dim3(kLmWaves * kWave), lds,
+                           (hipStream_t)stream, (const u32x4 *)h, (const u32x4 *)w_lm, w_scale,
+                           M, H, V, tpw, keys, ticket, argmax, max_logit, tokens, accept);
+    else
+        hipLaunchKernelGGL(lmhead_kernel<false>, dim3(grid), dim3(kLmWaves * kWave), lds,
+                           (hipStream_t)stream, (const u32x4 *)h, (const u32x4 *)w_lm, nullptr,
+                           M, H, V, tpw, keys, ticket, argmax, max_logit, tokens, accept);
     return check_launch();
 }
 
@@ -273,8 +320,18 @@ extern "C" moe_status_t lmhead_argmax(const uint16_t *h, const uint16_t *w_lm,
                                       void *workspace, size_t workspace_bytes,
                                       void *stream)
 {
-    return lmhead_enqueue(h, w_lm, M, H, V, argmax, max_logit, nullptr, nullptr,
-                          workspace, workspace_bytes, stream);
+    return lmhead_enqueue(h, w_lm, nullptr, false, M, H, V, argmax, max_logit, nullptr,
+                          nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" moe_status_t lmhead_argmax_fp8(const uint16_t *h, const uint8_t *w_lm,
+                                          const float *w_scale, int32_t M, int32_t H,
+                                          int32_t V, int32_t *argmax, float *max_logit,
+                                          void *workspace, size_t workspace_bytes,
+                                          void *stream)
+{
+    return lmhead_enqueue(h, w_lm, w_scale, true, M, H, V, argmax, max_logit, nullptr,
+                          nullptr, workspace, workspace_bytes, stream);
 }
 
 extern "C" moe_status_t lmhead_greedy_verify(const uint16_t *h, const uint16_t *w_lm,
@@ -286,6 +343,19 @@ extern "C" moe_status_t lmhead_greedy_verify(const uint16_t *h, const uint16_t *
 {
     if (!tokens || !accept)
         return MOE_ERR_NULL;
-    return lmhead_enqueue(h, w_lm, M, H, V, argmax, max_logit, tokens, accept,
-                          workspace, workspace_bytes, stream);
+    return lmhead_enqueue(h, w_lm, nullptr, false, M, H, V, argmax, max_logit, tokens,
+                          accept, workspace, workspace_bytes, stream);
+}
+
+extern "C" moe_status_t lmhead_greedy_verify_fp8(const uint16_t *h, const uint8_t *w_lm,
+                                                 const float *w_scale, const int32_t *tokens,
+                                                 int32_t M, int32_t H, int32_t V,
+                                                 int32_t *argmax, float *max_logit,
+                                                 int32_t *accept, void *workspace,
+                                                 size_t workspace_bytes, void *stream)
+{
+    if (!tokens || !accept)
+        return MOE_ERR_NULL;
+    return lmhead_enqueue(h, w_lm, w_scale, true, M, H, V, argmax, max_logit, tokens,
+                          accept, workspace, workspace_bytes, stream);
 }

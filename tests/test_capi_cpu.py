@@ -207,3 +207,25 @@ def test_shared_expert_checks(L):
     assert ls(gs=None) == NULL
     assert ls(M=16, k=16) == UNSUP
     assert ls(wsb=16) == WS
+
+
+def test_fp8_checks(L):
+    def ef(x=A, wg=A, sg=A, sd=A, M=6, H=2560, I=1024, E=512, k=8, ws=B, wsb=1 << 30):
+        return L.moe_expert_ffn_fp8(x, A, A, wg, sg, A, A, A, sd, M, H, I, E, k, A, ws, wsb, None)
+    assert ef(sg=None) == NULL
+    assert ef(sd=None) == NULL
+    assert ef(H=2568) == UNSUP             # H a multiple of 16
+    assert ef(I=1032) == UNSUP             # I a multiple of 16
+    assert ef(M=16) == UNSUP               # 128 activation rows beyond LDS
+    assert ef(wg=A + 8) == ALIGN
+    assert ef(sg=A + 2) == ALIGN
+    assert ef(wsb=16) == WS
+
+    def lf(h=A, w=A, s=A, M=6, H=2560, V=157184, am=A, ws=B, wsb=1 << 20):
+        return L.lmhead_argmax_fp8(h, w, s, M, H, V, am, None, ws, wsb, None)
+    assert lf(s=None) == NULL
+    assert lf(H=2568) == UNSUP
+    assert lf(s=A + 1) == ALIGN
+    assert lf(wsb=16) == WS
+    assert L.lmhead_greedy_verify_fp8(A, A, A, None, 6, 2560, 157184, A, None, A, B, 1 << 20,
+                                      None) == NULL
