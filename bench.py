@@ -75,14 +75,15 @@ def src_digest(*names: str) -> str:
 
 
 CALIB_KERNEL = "bitwise_not"     # substring of the calibration kernel's name
-LM_KERNEL = "lmhead_kernel"
+LM_KERNEL = "lmhead_kernel<false>"   # the bf16 lm_head (the roofline kernel)
+LM8_KERNEL = "lmhead_kernel<true>"   # the fp8 lm_head
 
 
 def counter_means(path: str, counter: str) -> dict:
     """Mean per-dispatch value of `counter` for the lm_head kernel and the
     calibration kernel in one rocprofv3 counter_collection.csv."""
     import csv
-    vals = {LM_KERNEL: [], CALIB_KERNEL: []}
+    vals = {LM_KERNEL: [], LM8_KERNEL: [], CALIB_KERNEL: []}
     with open(path, newline="") as f:
         for row in csv.DictReader(f):
             if row.get("Counter_Name") != counter:
@@ -90,9 +91,11 @@ def counter_means(path: str, counter: str) -> dict:
             for key in vals:
                 if key in row.get("Kernel_Name", ""):
                     vals[key].append(float(row["Counter_Value"]))
-    for key, v in vals.items():
-        if not v:
+    for key in (LM_KERNEL, CALIB_KERNEL):
+        if not vals[key]:
             raise SystemExit(f"{path}: no {counter} rows for a kernel named *{key}*")
+    if not vals[LM8_KERNEL]:
+        del vals[LM8_KERNEL]
     return {key: sum(v) / len(v) for key, v in vals.items()} | {
         "dispatches": {key: len(v) for key, v in vals.items()}}
 
@@ -122,6 +125,16 @@ def write_counters(fetch_csv: str, write_csv: str, calib_mib: int) -> None:
         "hbm_bytes_per_dispatch": int(lm_read + lm_write),
         "dispatches": {"fetch_run": fe["dispatches"], "write_run": wr["dispatches"]},
     }
+    if LM8_KERNEL in fe and LM8_KERNEL in wr:
+        # the fp8 lm_head of the same runs: algorithmic 157184*2560 codes +
+        # 157184 scales + h + outputs
+        r8, w8 = fe[LM8_KERNEL] * 1024 / f_fac, wr[LM8_KERNEL] * 1024 / w_fac
+        out["fp8"] = {"kernel": "lmhead_greedy_verify_fp8 (lmhead_kernel<true>), 157184x2560 e4m3, M=6",
+                      "fetch_kib_per_dispatch": round(fe[LM8_KERNEL], 1),
+                      "write_kib_per_dispatch": round(wr[LM8_KERNEL], 3),
+                      "hbm_read_bytes_per_dispatch": int(r8),
+                      "hbm_write_bytes_per_dispatch": int(w8),
+                      "hbm_bytes_per_dispatch": int(r8 + w8)}
     os.makedirs(PROFILES, exist_ok=True)
     path = os.path.join(PROFILES, "lmhead_argmax_counters.json")
     with open(path, "w") as f:
@@ -192,7 +205,7 @@ def main():
     # fp8 experts (E4M3 codes + fp32 row scales) for the fp8 lines; the router
     # stays bf16 (each rotated layer's own); two fp8 lm_head copies
     layers8 = []
-    for l in range(args.fp8_layers if not args.profile_steps else 0):
+    for l in range(args.fp8_layers if not args.profile_steps else min(2, args.fp8_layers)):
         qg, sg = synth.device_fp8_rows((E, I, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 300 + l, K_["gate"])
         qu, su = synth.device_fp8_rows((E, I, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 300 + l, K_["up"])
         qd, sd = synth.device_fp8_rows((E, H, I), synth.WEIGHT_STD, synth.WEIGHT_SEED, 300 + l, K_["down"])
@@ -265,10 +278,22 @@ def main():
             torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst, flush
+        p8 = [(x.data_ptr(), Lw["router"].data_ptr(), None, Lw["gate"].data_ptr(),
+               Lw["s_gate"].data_ptr(), Lw["up"].data_ptr(), Lw["s_up"].data_ptr(),
+               Lw["down"].data_ptr(), Lw["s_down"].data_ptr(), M, H, I, E, k, idx.data_ptr(),
+               tw.data_ptr(), out.data_ptr(), ws_layer.data_ptr(), ws_layer.numel(), stream)
+              for Lw in layers8]
+        pl8 = [(h.data_ptr(), q.data_ptr(), sc.data_ptr(), chain.data_ptr(), M, H, V,
+                am.data_ptr(), None, acc.data_ptr(), ws_lm.data_ptr(), ws_lm.numel(), stream)
+               for q, sc in lms8]
         for s in range(args.profile_steps):
             step(s)
             check("moe_route", L.moe_route(*route_args[s % len(route_args)]))
             check("moe_route_rmsnorm", L.moe_route_rmsnorm(*rn_args[s % len(rn_args)]))
+            if p8 and M <= 9:
+                check("moe_layer_fp8", L.moe_layer_fp8(*p8[s % len(p8)]))
+            if pl8:
+                check("lmhead_greedy_verify_fp8", L.lmhead_greedy_verify_fp8(*pl8[s % len(pl8)]))
         torch.cuda.synchronize()
         log(f"profile run: {args.profile_steps} steps done")
         return

@@ -577,6 +577,8 @@ __host__ __device__ inline size_t up_gemv_lds_bytes(int M, int H, int KC, bool w
 // GEMV up kernel: KC 16-byte chunks per lane per row and block (a unit is
 // one block when a row has at most 5 * 64 chunks), a 4-deep register ring
 constexpr int kUpGemvNB = 4;
+// fp8 rows are half the bytes: a deeper ring keeps as many bytes in flight
+constexpr int up_gemv_nb(bool w8) { return w8 ? 6 : kUpGemvNB; }
 static int up_gemv_kc(int H, bool w8)
 {
     const int need = ((w8 ? H / 16 : H / 8) + kWave - 1) / kWave;
@@ -598,12 +600,22 @@ struct Experts {
     const float *sg, *su, *sd;
 };
 
+// Two workgroups per CU when their LDS allows (x of M tokens plus the
+// grouping): eight wavefronts per CU hide each other's per-unit latency
+// (the group lookups, the reductions, the epilogue).
+static int up_gemv_grid(size_t lds, int M)
+{
+    // (a single token has only k units per 1024 rows: one per CU is enough)
+    return M > 1 && lds + 10 * 1024 <= 80 * 1024 ? 2 * kXGrid : kXGrid;
+}
+
 template <int KC, bool W8>
 static void launch_up_gemv(const uint16_t *x, const int *idx, const Experts &ex, int M, int H,
                            int I, int E, int k, uint16_t *act, hipStream_t st)
 {
-    hipLaunchKernelGGL((expert_up_gemv_kernel<KC, kUpGemvNB, W8>), dim3(kXGrid),
-                       dim3(kXThreads), up_gemv_lds_bytes(M, H, KC, W8), st, (const u32x4 *)x,
+    const size_t lds = up_gemv_lds_bytes(M, H, KC, W8);
+    hipLaunchKernelGGL((expert_up_gemv_kernel<KC, up_gemv_nb(W8), W8>), dim3(up_gemv_grid(lds, M)),
+                       dim3(kXThreads), lds, st, (const u32x4 *)x,
                        idx, (const u32x4 *)ex.wg, (const u32x4 *)ex.wu, (const u32x4 *)ex.wgs,
                        (const u32x4 *)ex.wus, ex.sg, ex.su, M, H, I, E, k, ex.ns, act);
 }
@@ -691,8 +703,8 @@ static hipError_t set_lds_attributes()
 {
     hipError_t e = hipSuccess;
     auto chk = [&](hipError_t r) { if (r != hipSuccess) e = r; };
-#define MV_UP_ATTR(KC) chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, true>));
+#define MV_UP_ATTR(KC) chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(false), false>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(true), true>));
     MV_UP_ATTR(1) MV_UP_ATTR(2) MV_UP_ATTR(3) MV_UP_ATTR(4) MV_UP_ATTR(5)
 #undef MV_UP_ATTR
 #define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, 2>)); chk(allow_lds(expert_down_kernel<R, 3>)); \
