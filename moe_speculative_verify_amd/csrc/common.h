@@ -173,120 +173,6 @@ __device__ __forceinline__ void lds_barrier()
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Expert grouping of the (token, slot) pairs, built in LDS by every
-// workgroup that needs it (the grouping step of the post's MoE chain,
-// section "PDL: the latency floor of stacked small kernels"): a histogram of
-// the pairs over the experts (LDS atomics), one packed prefix scan over the
-// experts that yields each bucket's offset, index and first column block
-// at once, and a scatter of the pair ids. Buckets are ordered by expert id;
-// the order of pairs inside a bucket is whatever the atomics produced,
-// which no result depends on (every pair's arithmetic is its own). A bucket
-// is cut into column blocks of at most 16 pairs (one MFMA B operand); with
-// distinct experts per token a bucket never exceeds M <= 16 pairs.
-constexpr int kGroupThreads = 256;               // workgroup size of every user
-constexpr int kBinsPerThread = kMaxE / kGroupThreads;
-
-struct Groups {
-    int D;                       // distinct valid experts
-    int DV;                      // column blocks
-    int wsum[kGroupThreads / kWave];   // per-wavefront totals of the scan
-    int bins[kMaxE];             // pairs per expert, then bucket offsets
-    int16_t e[kMaxNP];           // expert of pair p, -1 if out of range
-    int16_t slot[kMaxNP];        // position of pair p inside its bucket
-    int16_t sorted[kMaxNP];      // pair ids, bucket by bucket
-    int16_t vexp[kMaxNP];        // expert of column block v
-    int16_t vbeg[kMaxNP];        // first index into sorted of block v
-    int16_t vcnt[kMaxNP];        // pairs in block v (1..16)
-};
-
-// One step of an inclusive wavefront scan: add the value of lane
-// (lane - shift) in the same 16-lane row (row_shr), or the last lane of the
-// previous row(s) (row_bcast); lanes without a source add 0.
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ int scan_step(int v)
-{
-    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xF, false);
-}
-
-// Two steps, so that other prologue loads can be issued in between:
-// groups_set_pairs records this thread's pair (idx = topk_idx[threadIdx.x],
-// loaded by the caller) and clears the histogram, groups_finish builds the
-// buckets (it starts with a barrier). Needs blockDim.x == kGroupThreads.
-__device__ inline void groups_set_pairs(int idx, int NP, int E, Groups &g)
-{
-    const int p = threadIdx.x;
-    if (p < NP)
-        g.e[p] = (int16_t)((idx >= 0 && idx < E) ? idx : -1);
-#pragma unroll
-    for (int i = 0; i < kBinsPerThread; ++i)
-        g.bins[i * kGroupThreads + p] = 0;
-}
-
-__device__ inline void groups_finish(int NP, Groups &g)
-{
-    const int p = threadIdx.x;
-    const int lane = p & (kWave - 1), wave = p / kWave;
-    lds_barrier();
-    // histogram: each valid pair takes the next position in its bucket
-    const int ep = p < NP ? g.e[p] : -1;
-    if (ep >= 0)
-        g.slot[p] = (int16_t)atomicAdd(&g.bins[ep], 1);
-    lds_barrier();
-    // packed per-expert fields, summed by one exclusive scan over experts:
-    // bits 0-9 pairs (bucket offset), 10-19 non-empty buckets (bucket
-    // index), 20-29 column blocks (first block); every total is <= 256
-    int cnt[kBinsPerThread], pk[kBinsPerThread];
-    int tsum = 0;
-#pragma unroll
-    for (int i = 0; i < kBinsPerThread; ++i) {
-        cnt[i] = g.bins[p * kBinsPerThread + i];
-        pk[i] = cnt[i] | ((cnt[i] > 0) << 10) | (((cnt[i] + 15) >> 4) << 20);
-        tsum += pk[i];
-    }
-    int incl = tsum;
-    incl = scan_step<0x111, 0xF>(incl);          // row_shr:1
-    incl = scan_step<0x112, 0xF>(incl);          // row_shr:2
-    incl = scan_step<0x114, 0xF>(incl);          // row_shr:4
-    incl = scan_step<0x118, 0xF>(incl);          // row_shr:8
-    incl = scan_step<0x142, 0xA>(incl);          // row_bcast:15
-    incl = scan_step<0x143, 0xC>(incl);          // row_bcast:31
-    if (lane == kWave - 1)
-        g.wsum[wave] = incl;
-    lds_barrier();
-    int run = incl - tsum;
-    for (int w = 0; w < wave; ++w)
-        run += g.wsum[w];
-    if (p == kGroupThreads - 1) {
-        const int tot = run + tsum;
-        g.D = (tot >> 10) & 1023;
-        g.DV = tot >> 20;
-    }
-#pragma unroll
-    for (int i = 0; i < kBinsPerThread; ++i) {
-        const int off = run & 1023, v0 = run >> 20;
-        const int expert = p * kBinsPerThread + i;
-        g.bins[expert] = off;                     // bucket offset for the scatter
-        for (int o = 0; o < cnt[i]; o += 16) {
-            const int v = v0 + o / 16;
-            g.vexp[v] = (int16_t)expert;
-            g.vbeg[v] = (int16_t)(off + o);
-            g.vcnt[v] = (int16_t)(cnt[i] - o < 16 ? cnt[i] - o : 16);
-        }
-        run += pk[i];
-    }
-    lds_barrier();
-    if (ep >= 0)
-        g.sorted[g.bins[ep] + g.slot[p]] = (int16_t)p;
-    lds_barrier();
-}
-
-__device__ inline void build_groups(const int *__restrict__ topk_idx, int NP, int E, Groups &g)
-{
-    const int idx = (int)threadIdx.x < NP ? topk_idx[threadIdx.x] : -1;
-    groups_set_pairs(idx, NP, E, g);
-    groups_finish(NP, g);
-}
-
 // Direct-to-LDS staging of nrows rows of nch 16-byte chunks (row-major,
 // contiguous) into LDS rows of pitch xs chunks: one 1 KB load per run of 64
 // chunks, spread over the workgroup's wavefronts, lanes past the row end

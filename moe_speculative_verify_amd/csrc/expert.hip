@@ -52,12 +52,135 @@ constexpr int kXSteps = kXKB / 32;                  // MFMA steps per block
 constexpr int kXGrid = 256;                         // one workgroup per CU
 constexpr int kXLdsDynMax = 160 * 1024 - 8 * 1024;  // static LDS stays below 8 KB
 
-static_assert(sizeof(Groups) + 64 <= 8 * 1024, "static LDS margin");
-static_assert(kXThreads == kGroupThreads, "grouping needs one thread per histogram slice");
 
 // A value read from LDS that is the same in every lane, moved to a scalar
 // register so that control flow and addresses built from it stay scalar.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Expert grouping of the (token, slot) pairs, built in LDS by every
+// workgroup that needs it (the grouping step of the post's MoE chain,
+// section "PDL: the latency floor of stacked small kernels"): a histogram of
+// the pairs over the experts (LDS atomics), one packed prefix scan over the
+// experts that yields each bucket's offset, index and first column block
+// at once, and a scatter of the pair ids. Buckets are ordered by expert id;
+// the order of pairs inside a bucket is whatever the atomics produced,
+// which no result depends on (every pair's arithmetic is its own). A bucket
+// is cut into column blocks of at most 16 pairs (one MFMA B operand); with
+// distinct experts per token a bucket never exceeds M <= 16 pairs.
+constexpr int kGroupThreads = 256;               // threads that build it (the first 256)
+constexpr int kBinsPerThread = kMaxE / kGroupThreads;
+
+struct Groups {
+    int D;                       // distinct valid experts
+    int DV;                      // column blocks
+    int wsum[kGroupThreads / kWave];   // per-wavefront totals of the scan
+    int bins[kMaxE];             // pairs per expert, then bucket offsets
+    int16_t e[kMaxNP];           // expert of pair p, -1 if out of range
+    int16_t slot[kMaxNP];        // position of pair p inside its bucket
+    int16_t sorted[kMaxNP];      // pair ids, bucket by bucket
+    int16_t vexp[kMaxNP];        // expert of column block v
+    int16_t vbeg[kMaxNP];        // first index into sorted of block v
+    int16_t vcnt[kMaxNP];        // pairs in block v (1..16)
+};
+
+// One step of an inclusive wavefront scan: add the value of lane
+// (lane - shift) in the same 16-lane row (row_shr), or the last lane of the
+// previous row(s) (row_bcast); lanes without a source add 0.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int scan_step(int v)
+{
+    return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROWMASK, 0xF, false);
+}
+
+// Two steps, so that other prologue loads can be issued in between:
+// groups_set_pairs records this thread's pair (idx = topk_idx[threadIdx.x],
+// loaded by the caller) and clears the histogram, groups_finish builds the
+// buckets (it starts with a barrier). The first kGroupThreads threads do the
+// work; further whole wavefronts (workgroups of 512) only join the barriers.
+__device__ inline void groups_set_pairs(int idx, int NP, int E, Groups &g)
+{
+    const int p = threadIdx.x;
+    if (p >= kGroupThreads)
+        return;
+    if (p < NP)
+        g.e[p] = (int16_t)((idx >= 0 && idx < E) ? idx : -1);
+#pragma unroll
+    for (int i = 0; i < kBinsPerThread; ++i)
+        g.bins[i * kGroupThreads + p] = 0;
+}
+
+__device__ inline void groups_finish(int NP, Groups &g)
+{
+    const int p = threadIdx.x;
+    const int lane = p & (kWave - 1), wave = p / kWave;
+    const bool gp = p < kGroupThreads;           // uniform per wavefront
+    lds_barrier();
+    // histogram: each valid pair takes the next position in its bucket
+    const int ep = p < NP ? g.e[p] : -1;
+    if (ep >= 0)
+        g.slot[p] = (int16_t)atomicAdd(&g.bins[ep], 1);
+    lds_barrier();
+    // packed per-expert fields, summed by one exclusive scan over experts:
+    // bits 0-9 pairs (bucket offset), 10-19 non-empty buckets (bucket
+    // index), 20-29 column blocks (first block); every total is <= 256
+    int cnt[kBinsPerThread], pk[kBinsPerThread];
+    int tsum = 0, incl = 0;
+    if (gp) {
+#pragma unroll
+        for (int i = 0; i < kBinsPerThread; ++i) {
+            cnt[i] = g.bins[p * kBinsPerThread + i];
+            pk[i] = cnt[i] | ((cnt[i] > 0) << 10) | (((cnt[i] + 15) >> 4) << 20);
+            tsum += pk[i];
+        }
+        incl = tsum;
+        incl = scan_step<0x111, 0xF>(incl);          // row_shr:1
+        incl = scan_step<0x112, 0xF>(incl);          // row_shr:2
+        incl = scan_step<0x114, 0xF>(incl);          // row_shr:4
+        incl = scan_step<0x118, 0xF>(incl);          // row_shr:8
+        incl = scan_step<0x142, 0xA>(incl);          // row_bcast:15
+        incl = scan_step<0x143, 0xC>(incl);          // row_bcast:31
+        if (lane == kWave - 1)
+            g.wsum[wave] = incl;
+    }
+    lds_barrier();
+    if (gp) {
+        int run = incl - tsum;
+        for (int w = 0; w < wave; ++w)
+            run += g.wsum[w];
+        if (p == kGroupThreads - 1) {
+            const int tot = run + tsum;
+            g.D = (tot >> 10) & 1023;
+            g.DV = tot >> 20;
+        }
+#pragma unroll
+        for (int i = 0; i < kBinsPerThread; ++i) {
+            const int off = run & 1023, v0 = run >> 20;
+            const int expert = p * kBinsPerThread + i;
+            g.bins[expert] = off;                     // bucket offset for the scatter
+            for (int o = 0; o < cnt[i]; o += 16) {
+                const int v = v0 + o / 16;
+                g.vexp[v] = (int16_t)expert;
+                g.vbeg[v] = (int16_t)(off + o);
+                g.vcnt[v] = (int16_t)(cnt[i] - o < 16 ? cnt[i] - o : 16);
+            }
+            run += pk[i];
+        }
+    }
+    lds_barrier();
+    if (ep >= 0)
+        g.sorted[g.bins[ep] + g.slot[p]] = (int16_t)p;
+    lds_barrier();
+}
+
+__device__ inline void build_groups(const int *__restrict__ topk_idx, int NP, int E, Groups &g)
+{
+    const int idx = (int)threadIdx.x < NP ? topk_idx[threadIdx.x] : -1;
+    groups_set_pairs(idx, NP, E, g);
+    groups_finish(NP, g);
+}
+
+static_assert(sizeof(Groups) + 64 <= 8 * 1024, "static LDS margin");
+static_assert(kXThreads >= kGroupThreads, "grouping needs a thread per histogram slice");
 
 // Pairs: p < NP = M*k are routed (token p / k, slot p % k); with a shared
 // expert (ns = 1) p = NP + t is token t's pair with it, expert id E.
@@ -99,10 +222,14 @@ __global__ __launch_bounds__(kXThreads) void expert_down_kernel(
     unsigned char *ring = smem + wave * NB * kBlk;
     float *y_s = (float *)(smem + kXWaves * NB * kBlk);  // [NPT][R]
     const int NP = M * k, NPT = NP + ns * M;
+    float *s_tw = y_s + NPT * R;                         // [NP] routing weights
 
     {
         const int id = pair_expert(topk_idx, threadIdx.x, NP, NPT, E);
+        const float pw = (int)threadIdx.x < NP ? topk_w[threadIdx.x] : 0.0f;
         groups_set_pairs(id, NPT, E + ns, g);
+        if ((int)threadIdx.x < NP)
+            s_tw[threadIdx.x] = pw;
         groups_finish(NPT, g);
     }
 
@@ -187,7 +314,7 @@ __global__ __launch_bounds__(kXThreads) void expert_down_kernel(
         for (int jj = 0; jj < k; ++jj) {
             const int p = t * k + jj;
             if (g.e[p] >= 0)
-                sum = fmaf(topk_w[p], y_s[p * R + rr], sum);
+                sum = fmaf(s_tw[p], y_s[p * R + rr], sum);
         }
         if (ns)                                          // the shared expert, weight 1
             sum += y_s[(NP + t) * R + rr];
@@ -209,6 +336,10 @@ __global__ __launch_bounds__(kXThreads) void expert_down_kernel(
 // in order in the combine. Workgroup b owns rows r0 .. r0+R-1 of every
 // expert; its wavefronts split the column blocks (v = wave, wave+4, ...).
 constexpr int kDnKB = 512;                       // K elements per block
+// four wavefronts, each with the whole ring of its column blocks (eight, two
+// per SIMD, were measured slower: fewer blocks per wavefront, M=1 +6 us)
+constexpr int kDnWaves = 4;
+constexpr int kDnThreads = kDnWaves * kWave;
 constexpr int kDnCh = kDnKB / 8;                 // 16-byte chunks per row per block
 
 // Sum over the wavefront in a fixed order, returned uniform: the 16-lane row
@@ -244,8 +375,9 @@ __host__ __device__ inline size_t down_gemv_act_bytes(int NP, int I, bool w8)
 }
 __host__ __device__ inline size_t down_gemv_lds_bytes(int R, int NP, int I, bool w8)
 {
+    // activations, then the block sums [NP][nkb][R], then NP routing weights
     return down_gemv_act_bytes(NP, I, w8) +
-           (size_t)NP * down_gemv_nkb(I, w8) * R * sizeof(float);
+           (size_t)NP * (down_gemv_nkb(I, w8) * R + 1) * sizeof(float);
 }
 
 // W8: fp8 W_down (E4M3 codes, an fp32 scale per row in sd): a block is
@@ -253,7 +385,7 @@ __host__ __device__ inline size_t down_gemv_lds_bytes(int R, int NP, int I, bool
 // activation chunks; the row's scale is one more per-lane load of the block
 // and multiplies the reduced sum.
 template <int R, int NB, bool W8>
-__global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
+__global__ __launch_bounds__(kDnThreads) void expert_down_gemv_kernel(
     const u32x4 *__restrict__ act, const int *__restrict__ topk_idx,
     const float *__restrict__ topk_w, const u32x4 *__restrict__ wd,
     const u32x4 *__restrict__ wds, const float *__restrict__ sd, int M, int H, int I,
@@ -273,12 +405,17 @@ __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
     const int nr = min(R, H - r0);
     u32x4 *s_act = (u32x4 *)smem;                        // [NPT][xs]
     float *s_y = (float *)(smem + down_gemv_act_bytes(NPT, I, W8));  // [NPT][nkb][R]
+    float *s_tw = s_y + NPT * nkb * R;                   // [NP] routing weights
 
-    // prologue: pair ids and buckets; then the ring's first weight blocks
-    // and every pair's activation row into LDS (direct-to-LDS), so the
-    // weights lead the memory queue
+    // prologue: pair ids, routing weights (for the combine at the end) and
+    // buckets; then the ring's first weight blocks and every pair's
+    // activation row into LDS (direct-to-LDS), so the weights lead the
+    // memory queue
+    const float pw = (int)threadIdx.x < NP ? topk_w[threadIdx.x] : 0.0f;
     groups_set_pairs(pair_expert(topk_idx, threadIdx.x, NP, NPT, E), NPT, E + ns, g);
-    wait_vmcnt<0>();                                     // only the pair id is in flight
+    wait_vmcnt<0>();                                     // only the pair id and weight are in flight
+    if ((int)threadIdx.x < NP)
+        s_tw[threadIdx.x] = pw;
     for (int i = threadIdx.x; i < NPT * (xs - nch); i += blockDim.x) {
         const int p = i / (xs - nch), c = nch + i % (xs - nch);
         s_act[p * xs + c] = u32x4{0, 0, 0, 0};           // K padding reads as zero
@@ -286,7 +423,7 @@ __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
     groups_finish(NPT, g);
 
     const int DV = uniform(g.DV);
-    const int nv = DV > wave ? (DV - wave + kXWaves - 1) / kXWaves : 0;
+    const int nv = DV > wave ? (DV - wave + kDnWaves - 1) / kDnWaves : 0;
     const int nblk = nv * nkb;                           // this wavefront's blocks
 
     // Block X = (column block v, K block kb): lane i loads chunk i of the
@@ -296,7 +433,7 @@ __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
     auto issue = [&](int X, u32x4 (&dst)[R], float &sdv) {
         const bool real = X < nblk;
         const int Xr = real ? X : 0;
-        const int v = wave + kXWaves * (Xr / nkb), kb = Xr % nkb;
+        const int v = wave + kDnWaves * (Xr / nkb), kb = Xr % nkb;
         const int ev = uniform(g.vexp[min(v, kMaxNP - 1)]);
         const bool sh = real && ev >= E;                 // the shared expert's slab
         const size_t ebase = real && !sh ? (size_t)ev * H : 0;   // first row of the slab
@@ -321,7 +458,7 @@ __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
         }
     };
     auto consume = [&](int X, u32x4 (&wr)[R], float sdv) {
-        const int v = wave + kXWaves * (X / nkb), kb = X % nkb;
+        const int v = wave + kDnWaves * (X / nkb), kb = X % nkb;
         const int npair = uniform(g.vcnt[v]);
         const int pb = uniform(g.vbeg[v]);
         if (kb * kDnCh + kDnCh > nwc) {                  // uniform: the K tail block
@@ -387,7 +524,7 @@ __global__ __launch_bounds__(kXThreads) void expert_down_gemv_kernel(
                 float y = 0.0f;
                 for (int kb = 0; kb < nkb; ++kb)
                     y += s_y[(p * nkb + kb) * R + rr];
-                sum = fmaf(topk_w[p], y, sum);
+                sum = fmaf(s_tw[p], y, sum);
             }
         }
         if (ns) {                                        // the shared expert, weight 1
@@ -652,7 +789,8 @@ static bool down_gemv_fits(int R, int NPT, int I, bool w8)
 }
 static size_t down_lds_bytes(int R, int NB, int NPT)
 {
-    return (size_t)kXWaves * NB * R * kXRowPitch + (size_t)NPT * R * sizeof(float);
+    // the weight rings, the pairs' sums [NPT][R], the routing weights [NPT]
+    return (size_t)kXWaves * NB * R * kXRowPitch + (size_t)NPT * (R + 1) * sizeof(float);
 }
 static int down_nb(int R, int NPT)
 {
@@ -724,12 +862,12 @@ static void launch_down_gemv(const uint16_t *act, const int *idx, const float *t
     const size_t lds = down_gemv_lds_bytes(R, M * k + ex.ns * M, I, ex.w8);
     if (ex.w8)
         hipLaunchKernelGGL((expert_down_gemv_kernel<R, down_gemv_nb(R), true>), dim3(grid),
-                           dim3(kXThreads), lds, st, (const u32x4 *)act, idx, tw,
+                           dim3(kDnThreads), lds, st, (const u32x4 *)act, idx, tw,
                            (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, ex.sd, M, H, I, E, k,
                            ex.ns, out);
     else
         hipLaunchKernelGGL((expert_down_gemv_kernel<R, down_gemv_nb(R), false>), dim3(grid),
-                           dim3(kXThreads), lds, st, (const u32x4 *)act, idx, tw,
+                           dim3(kDnThreads), lds, st, (const u32x4 *)act, idx, tw,
                            (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, nullptr, M, H, I, E, k,
                            ex.ns, out);
 }
