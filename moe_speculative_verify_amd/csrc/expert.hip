@@ -50,6 +50,7 @@ constexpr int kXKB = 512;                           // K elements per block
 constexpr int kXRowPitch = kXKB * 2 + 16;           // LDS bytes per row (padded)
 constexpr int kXSteps = kXKB / 32;                  // MFMA steps per block
 constexpr int kXGrid = 256;                         // one workgroup per CU
+constexpr int kUpPend = kWave;                      // queued up-projection outputs per wavefront
 constexpr int kXLdsDynMax = 160 * 1024 - 8 * 1024;  // static LDS stays below 8 KB
 
 
@@ -539,6 +540,14 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_gemv_kernel(
 }
 
 // ------------------------------------------------------------ up (GEMV)
+// LDS bytes of the up GEMV's x copy: M rows of whole K blocks
+__host__ __device__ inline size_t up_gemv_x_bytes(int M, int H, int KC, bool w8)
+{
+    const int nwc = w8 ? H / 16 : H / 8;
+    const int nbu = (nwc + KC * kWave - 1) / (KC * kWave);
+    return align_up((size_t)M * nbu * KC * kWave * (w8 ? 2 : 1) * 16, 256);
+}
+
 // The up projection at verify widths is a set of matrix-vector products as
 // well: a selected expert serves about one pair. Units are (column block v,
 // row i of I): the unit's gate row and up row, KC chunks of 16 bytes per
@@ -572,6 +581,20 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
     const int xs = nbu * KC * kWave * (W8 ? 2 : 1);      // LDS x row, chunks
     const int NP = M * k, NPT = NP + ns * M;
     u32x4 *s_x = (u32x4 *)smem;                          // [M][xs]
+    // finished (gate, up) sums waiting for the SwiGLU epilogue: up to
+    // kUpPend per wavefront, turned into activations 64 lanes at a time
+    float2 *s_gu = (float2 *)(smem + up_gemv_x_bytes(M, H, KC, W8)) + wave * kUpPend;
+    int *s_ai = (int *)((float2 *)(smem + up_gemv_x_bytes(M, H, KC, W8)) + kXWaves * kUpPend) +
+                wave * kUpPend;
+    int pend = 0;                                        // uniform
+    auto flush = [&]() {
+        // SwiGLU in fp32, one rounding to bf16, one output per lane
+        if (lane < pend) {
+            const float2 v = s_gu[lane];
+            act[s_ai[lane]] = (uint16_t)f32_to_bf16_rne(v.x / (1.0f + expf(-v.x)) * v.y);
+        }
+        pend = 0;
+    };
 
     groups_set_pairs(pair_expert(topk_idx, threadIdx.x, NP, NPT, E), NPT, E + ns, g);
     wait_vmcnt<0>();                                     // only the pair id is in flight
@@ -675,9 +698,13 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
                 gt *= sgv;
                 ut *= suv;
             }
-            // SwiGLU in fp32, one rounding to bf16
-            if (lane == 0)
-                act[(size_t)p * I + i] = (uint16_t)f32_to_bf16_rne(gt / (1.0f + expf(-gt)) * ut);
+            // queued for the epilogue (lane 0 writes, the wavefront reads)
+            if (lane == 0) {
+                s_gu[pend] = make_float2(gt, ut);
+                s_ai[pend] = p * I + i;
+            }
+            if (++pend == kUpPend)
+                flush();
         }
     };
 
@@ -700,13 +727,13 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
         }
     }
     wait_vmcnt<0>();                                     // dummy loads have landed
+    flush();
 }
 
+// x of the M tokens, then each wavefront's queue of finished sums
 __host__ __device__ inline size_t up_gemv_lds_bytes(int M, int H, int KC, bool w8)
 {
-    const int nwc = w8 ? H / 16 : H / 8;
-    const int nbu = (nwc + KC * kWave - 1) / (KC * kWave);
-    return align_up((size_t)M * nbu * KC * kWave * (w8 ? 2 : 1) * 16, 256);
+    return up_gemv_x_bytes(M, H, KC, w8) + (size_t)kXWaves * kUpPend * (sizeof(float2) + 4);
 }
 
 // ------------------------------------------------------------------ host
