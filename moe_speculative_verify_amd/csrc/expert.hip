@@ -562,8 +562,8 @@ __host__ __device__ inline size_t up_gemv_x_bytes(int M, int H, int KC, bool w8)
 // W8: fp8 weights (E4M3 codes, 16 per 16-byte chunk, an fp32 scale per
 // row in sg / su); each chunk is widened to two bf16 chunks that meet two x
 // chunks, and the row scales multiply the reduced sums before the SwiGLU.
-template <int KC, int NB, bool W8>
-__global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
+template <int KC, int NB, bool W8, int WV>
+__global__ __launch_bounds__(WV * kWave) void expert_up_gemv_kernel(
     const u32x4 *__restrict__ x, const int *__restrict__ topk_idx,
     const u32x4 *__restrict__ wg, const u32x4 *__restrict__ wu,
     const u32x4 *__restrict__ wgs, const u32x4 *__restrict__ wus,
@@ -572,7 +572,6 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ Groups g;
-    __shared__ float s_acc[kXWaves][16][2];      // per-pair running sums
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     const int nch = H / 8;                               // 16-byte x chunks per row
@@ -584,8 +583,11 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
     // finished (gate, up) sums waiting for the SwiGLU epilogue: up to
     // kUpPend per wavefront, turned into activations 64 lanes at a time
     float2 *s_gu = (float2 *)(smem + up_gemv_x_bytes(M, H, KC, W8)) + wave * kUpPend;
-    int *s_ai = (int *)((float2 *)(smem + up_gemv_x_bytes(M, H, KC, W8)) + kXWaves * kUpPend) +
+    int *s_ai = (int *)((float2 *)(smem + up_gemv_x_bytes(M, H, KC, W8)) + WV * kUpPend) +
                 wave * kUpPend;
+    // per-pair running sums over the K blocks of a unit (up to 16 pairs)
+    float2 *s_acc = (float2 *)((int *)((float2 *)(smem + up_gemv_x_bytes(M, H, KC, W8)) +
+                                       WV * kUpPend) + WV * kUpPend) + wave * 16;
     int pend = 0;                                        // uniform
     auto flush = [&]() {
         // SwiGLU in fp32, one rounding to bf16, one output per lane
@@ -604,13 +606,13 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
     }
     groups_finish(NPT, g);
 
-    // ---- unit u runs on wavefront u mod (4 * gridDim.x), so every
+    // ---- unit u runs on wavefront u mod (WV * gridDim.x), so every
     // wavefront sees every column block and a heavily shared expert's cost
     // spreads evenly; block X of this wavefront carries the tag
     // unit * 16 + kb, or -1 past its last block
     const int nunits = uniform(g.DV) * I;
-    const int GW = gridDim.x * kXWaves;
-    const int gw = blockIdx.x * kXWaves + wave;
+    const int GW = gridDim.x * WV;
+    const int gw = blockIdx.x * WV + wave;
     const int nmine = nunits > gw ? (nunits - 1 - gw) / GW + 1 : 0;
     const int nblk = nmine * nbu;
     auto tag_of = [&](int X) {
@@ -683,14 +685,13 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
             float gt = wave_total(ga), ut = wave_total(ua);
             if (nbu > 1) {                               // uniform
                 if (kb > 0) {
-                    gt = s_acc[wave][jj][0] + gt;
-                    ut = s_acc[wave][jj][1] + ut;
+                    const float2 a = s_acc[jj];
+                    gt = a.x + gt;
+                    ut = a.y + ut;
                 }
                 if (kb < nbu - 1) {
-                    if (lane == 0) {
-                        s_acc[wave][jj][0] = gt;
-                        s_acc[wave][jj][1] = ut;
-                    }
+                    if (lane == 0)
+                        s_acc[jj] = make_float2(gt, ut);
                     continue;
                 }
             }
@@ -730,10 +731,12 @@ __global__ __launch_bounds__(kXThreads) void expert_up_gemv_kernel(
     flush();
 }
 
-// x of the M tokens, then each wavefront's queue of finished sums
-__host__ __device__ inline size_t up_gemv_lds_bytes(int M, int H, int KC, bool w8)
+// x of the M tokens, then, for each of the wv wavefronts, its queue of
+// finished sums and its 16 running sums
+__host__ __device__ inline size_t up_gemv_lds_bytes(int M, int H, int KC, bool w8, int wv)
 {
-    return up_gemv_x_bytes(M, H, KC, w8) + (size_t)kXWaves * kUpPend * (sizeof(float2) + 4);
+    return up_gemv_x_bytes(M, H, KC, w8) +
+           (size_t)wv * (kUpPend * (sizeof(float2) + 4) + 16 * sizeof(float2));
 }
 
 // ------------------------------------------------------------------ host
@@ -741,8 +744,9 @@ __host__ __device__ inline size_t up_gemv_lds_bytes(int M, int H, int KC, bool w
 // GEMV up kernel: KC 16-byte chunks per lane per row and block (a unit is
 // one block when a row has at most 5 * 64 chunks), a 4-deep register ring
 constexpr int kUpGemvNB = 4;
-// fp8 rows are half the bytes: a deeper ring keeps as many bytes in flight
-constexpr int up_gemv_nb(bool w8) { return w8 ? 6 : kUpGemvNB; }
+// fp8 rows are half the bytes: a deeper ring keeps as many bytes in flight,
+// except with eight wavefronts, whose 256-register budget it would exceed
+constexpr int up_gemv_nb(bool w8, int wv) { return w8 && wv == 4 ? 6 : kUpGemvNB; }
 static int up_gemv_kc(int H, bool w8)
 {
     const int need = ((w8 ? H / 16 : H / 8) + kWave - 1) / kWave;
@@ -750,7 +754,7 @@ static int up_gemv_kc(int H, bool w8)
 }
 static bool up_gemv_fits(int M, int H, bool w8)
 {
-    return up_gemv_lds_bytes(M, H, up_gemv_kc(H, w8), w8) <= (size_t)kXLdsDynMax;
+    return up_gemv_lds_bytes(M, H, up_gemv_kc(H, w8), w8, 8) <= (size_t)kXLdsDynMax;
 }
 
 // The experts of one call: routed weights and, when ns = 1, the shared
@@ -764,24 +768,33 @@ struct Experts {
     const float *sg, *su, *sd;
 };
 
-// Two workgroups per CU when their LDS allows (x of M tokens plus the
-// grouping): eight wavefronts per CU hide each other's per-unit latency
-// (the group lookups, the reductions, the epilogue).
-static int up_gemv_grid(size_t lds, int M)
+// Eight wavefronts per CU when there is more than one token: they hide each
+// other's per-unit latency (the group lookups, the reductions, the
+// epilogue) and keep the loads of one flowing while another computes. Two
+// four-wavefront workgroups per CU when their LDS allows (x of M tokens,
+// the queues, the grouping), else one workgroup of eight.
+// (a single token has only k units per 1024 rows: four per CU are enough)
+template <int KC, int NB, bool W8, int WV>
+static void launch_up_gemv_wv(int grid, size_t lds, const uint16_t *x, const int *idx,
+                              const Experts &ex, int M, int H, int I, int E, int k,
+                              uint16_t *act, hipStream_t st)
 {
-    // (a single token has only k units per 1024 rows: one per CU is enough)
-    return M > 1 && lds + 10 * 1024 <= 80 * 1024 ? 2 * kXGrid : kXGrid;
+    hipLaunchKernelGGL((expert_up_gemv_kernel<KC, NB, W8, WV>), dim3(grid), dim3(WV * kWave), lds,
+                       st, (const u32x4 *)x, idx, (const u32x4 *)ex.wg, (const u32x4 *)ex.wu,
+                       (const u32x4 *)ex.wgs, (const u32x4 *)ex.wus, ex.sg, ex.su, M, H, I, E,
+                       k, ex.ns, act);
 }
-
 template <int KC, bool W8>
 static void launch_up_gemv(const uint16_t *x, const int *idx, const Experts &ex, int M, int H,
                            int I, int E, int k, uint16_t *act, hipStream_t st)
 {
-    const size_t lds = up_gemv_lds_bytes(M, H, KC, W8);
-    hipLaunchKernelGGL((expert_up_gemv_kernel<KC, up_gemv_nb(W8), W8>), dim3(up_gemv_grid(lds, M)),
-                       dim3(kXThreads), lds, st, (const u32x4 *)x,
-                       idx, (const u32x4 *)ex.wg, (const u32x4 *)ex.wu, (const u32x4 *)ex.wgs,
-                       (const u32x4 *)ex.wus, ex.sg, ex.su, M, H, I, E, k, ex.ns, act);
+    const size_t lds4 = up_gemv_lds_bytes(M, H, KC, W8, 4);
+    if (M == 1 || lds4 + 10 * 1024 <= 80 * 1024)
+        launch_up_gemv_wv<KC, up_gemv_nb(W8, 4), W8, 4>(M == 1 ? kXGrid : 2 * kXGrid, lds4, x,
+                                                        idx, ex, M, H, I, E, k, act, st);
+    else
+        launch_up_gemv_wv<KC, up_gemv_nb(W8, 8), W8, 8>(kXGrid, up_gemv_lds_bytes(M, H, KC, W8, 8),
+                                                        x, idx, ex, M, H, I, E, k, act, st);
 }
 template <bool W8>
 static void launch_up_gemv_kc(const uint16_t *x, const int *idx, const Experts &ex, int M,
@@ -868,8 +881,10 @@ static hipError_t set_lds_attributes()
 {
     hipError_t e = hipSuccess;
     auto chk = [&](hipError_t r) { if (r != hipSuccess) e = r; };
-#define MV_UP_ATTR(KC) chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(false), false>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(true), true>));
+#define MV_UP_ATTR(KC) chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(false, 4), false, 4>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(true, 4), true, 4>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(false, 8), false, 8>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(true, 8), true, 8>));
     MV_UP_ATTR(1) MV_UP_ATTR(2) MV_UP_ATTR(3) MV_UP_ATTR(4) MV_UP_ATTR(5)
 #undef MV_UP_ATTR
 #define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, 2>)); chk(allow_lds(expert_down_kernel<R, 3>)); \
