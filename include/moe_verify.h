@@ -35,10 +35,11 @@
  *     1 <= V < 2^31.
  *   - Workspaces: size from the matching *_workspace_bytes query,
  *     16-byte aligned, ZERO-FILLED before their first use (one
- *     moe_workspace_clear call, or any zero fill). The first 256 bytes of
- *     every workspace are a header whose counters (an arrival ticket) sit
- *     at fixed offsets; every call leaves them at zero again, so one
- *     workspace is reused by every entry point and shape without clearing.
+ *     moe_workspace_clear call, or any zero fill). The first 4096 bytes of
+ *     every workspace are a header whose counters (arrival tickets, one per
+ *     128-byte line) sit at fixed offsets; every call leaves them at zero
+ *     again, so one workspace is reused by every entry point and shape
+ *     without clearing.
  *     Two calls that may run concurrently must not share a workspace.
  *   - Results are deterministic: no floating-point atomics; rerunning a
  *     call on the same inputs gives bitwise-equal outputs, and a token's

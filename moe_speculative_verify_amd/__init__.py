@@ -157,7 +157,7 @@ class Workspace:
         key = (kind, torch.device(device).index, stream_handle)
         ws = cls._pool.get(key)
         if ws is None or ws.numel() < nbytes:
-            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+            ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
             cls._pool[key] = ws
         return ws
 

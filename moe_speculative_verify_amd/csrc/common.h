@@ -194,11 +194,16 @@ __device__ inline void stage_rows_lds(const u32x4 *__restrict__ src, int nrows, 
 
 // -------------------------------------------------------------------- host
 
-// Every workspace layout starts with the same 256-byte header whose first
-// word is the arrival ticket of the last-workgroup pattern; the ticket is zero
-// when a call starts and when it ends, and it sits at the same offset for
-// every entry point and shape, so one workspace serves them all in turn.
-constexpr size_t kWsHeader = 256;
+// Every workspace layout starts with the same 4 KB header of arrival
+// counters, one per 128-byte line (device-scope atomics on one line are
+// serialised, so counters that many workgroups hit sit on lines of their
+// own): word 0 is the arrival ticket of the last-workgroup pattern, word 32 g
+// (g = 1 .. 31) the ticket of arrival group g. Every counter is zero when a
+// call starts and when it ends, at the same offset for every entry point and
+// shape, so one workspace serves them all in turn.
+constexpr size_t kWsHeader = 4096;
+constexpr int kWsLineWords = 32;              // words per 128-byte line
+constexpr int kWsGroups = 31;                 // arrival groups the header holds
 
 // Dynamic LDS a kernel may request: 160 KB per CU on gfx950, less a margin
 // for the kernels' small static arrays.

@@ -38,8 +38,9 @@
 
 namespace mv {
 
-constexpr int kRouteWaves = 8;              // wavefronts per workgroup
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+// workgroups per arrival group of the two-level ticket
+constexpr int kRouteGroup = 32;
 
 // ---- per-lane sorted lists of 64-bit selection keys (order code of the
 // logit << 32 | ~id: a larger key is a larger logit, or an equal logit with
@@ -116,23 +117,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     v = max_u32_dpp<0x143, 0xC>(v);
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
-// largest 64-bit key over the wavefront, uniform: the largest high word,
-// then the largest low word among the lanes holding it (branch-free)
+// largest 64-bit key over the wavefront, uniform: the largest high word;
+// when a single lane holds it (equal logits are rare) the low word is read
+// from that lane, else it is the largest low word among the lanes holding it
 __device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
 {
     const uint32_t hi = (uint32_t)(v >> 32);
     const uint32_t whi = wave_max_u32(hi);
-    const uint32_t wlo = wave_max_u32(hi == whi ? (uint32_t)v : 0u);
+    const unsigned long long at = __ballot(hi == whi);
+    uint32_t wlo;
+    if (__popcll(at) == 1)                       // uniform
+        wlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, __builtin_ctzll(at));
+    else
+        wlo = wave_max_u32(hi == whi ? (uint32_t)v : 0u);
     return ((uint64_t)whi << 32) | wlo;
 }
 
-// S: MFMA steps per wavefront; KJ: logits per lane in the selection (a
-// power of two, KJ * 64 >= E); RT: router rows per workgroup; P: column
-// blocks per MFMA. With P = 2 (RT = 8 rows, at most 8 tokens) one MFMA takes
-// two 32-column blocks at once, block-diagonally: tile rows 0-7 and tokens
-// 0-7 carry block X, tile rows 8-15 and tokens 8-15 carry block Y (the same
-// router rows and tokens), so D[r][t] + D[8+r][8+t] is the dot product over
-// 64 columns and every lane loads distinct data.
 // bf16(x * gain * inv) for eight elements: x * gain is exact in fp32 (two
 // 8-bit significands), then one product and one rounding to bf16
 // (v_cvt_pk_bf16_f32: nearest, ties to even, in the default mode)
@@ -151,19 +151,32 @@ __device__ __forceinline__ u32x4 rmsnorm8_bf16(u32x4 v, u32x4 g, float inv)
     return r;
 }
 
-template <int S, int KJ, int RT, int P, bool NORM>
-__global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
+// S: MFMA steps per wavefront; KJ: logits per lane in the selection (a
+// power of two, KJ * 64 >= E); RT: router rows per workgroup; P: column
+// blocks per MFMA. With P = 2 (RT = 8 rows, at most 8 tokens) one MFMA takes
+// two 32-column blocks at once, block-diagonally: tile rows 0-7 and tokens
+// 0-7 carry block X, tile rows 8-15 and tokens 8-15 carry block Y (the same
+// router rows and tokens), so D[r][t] + D[8+r][8+t] is the dot product over
+// 64 columns and every lane loads distinct data.
+// W: wavefronts per workgroup; in the selecting workgroup each takes one
+// token at a time. KS: workgroups per group of router rows, each taking
+// 1/KS of the hidden dimension (slice q = its index mod KS; inside it the
+// W wavefronts split the columns again), so that the cold read is spread
+// over KS times more CUs; their partial logits plog[q][t][e] are added in
+// slice order, then the bias, by the selecting workgroup.
+template <int S, int KJ, int RT, int P, bool NORM, int W, int KS>
+__global__ __launch_bounds__(W * kWave) void route_kernel(
     const u32x4 *__restrict__ x, const u32x4 *__restrict__ wr,
     const float *__restrict__ bias, int M, int H, int E, int k,
-    float *__restrict__ logits, int *__restrict__ topk_idx,
+    float *__restrict__ plog, float *__restrict__ logits, int *__restrict__ topk_idx,
     float *__restrict__ topk_w, unsigned *__restrict__ ticket,
     const u32x4 *__restrict__ gamma, float eps, u32x4 *__restrict__ xn_out)
 {
     static_assert(RT == 8 || RT == 16, "tile rows");
     static_assert(P == 1 || (P == 2 && RT == 8), "block-diagonal packing needs 8-row tiles");
     static_assert(!NORM || S <= 16, "the norm needs every hidden-state chunk in registers at once");
-    __shared__ f32x4 s_part[kRouteWaves][kWave];
-    __shared__ float s_ss[NORM ? kRouteWaves : 1][kWave];
+    __shared__ f32x4 s_part[W][kWave];
+    __shared__ float s_ss[NORM ? W : 1][kWave];
     __shared__ int s_last;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
@@ -171,7 +184,8 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     const int j = lane & 15;                     // A row in the tile / B column
     const int g = lane >> 4;                     // chunk within a 32-column block
     const int blk = P == 2 ? j >> 3 : 0;         // column block of this lane
-    const int e0 = blockIdx.x * RT;
+    const int ks = KS > 1 ? (int)(blockIdx.x % KS) : 0;   // this workgroup's slice
+    const int e0 = (int)(blockIdx.x / KS) * RT;
 
     // ---- every load first, unpredicated: rows past E, tokens past M and
     // chunks past the row end read valid memory (zeroed or unused below)
@@ -181,13 +195,9 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     tok = tok < M ? tok : M - 1;
     const u32x4 *ap = wr + (size_t)arow * nch;
     const u32x4 *bp = x + (size_t)tok * nch;
-    const int cbase = wave * (4 * P * S) + 4 * blk + g;
-    float bv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int e = e0 + 4 * g + r;
-        bv[r] = bias ? bias[e < E ? e : E - 1] : 0.0f;
-    }
+    // first chunk of this lane in slice q (then every 4P chunks, S steps)
+    auto chunk0 = [&](int q) { return (q * W + wave) * (4 * P * S) + 4 * blk + g; };
+    const int cbase = chunk0(ks);
     // at most 16 steps of operands in registers at a time
     constexpr int SPH = S < 16 ? S : 16;
     static_assert(S % SPH == 0, "steps per phase");
@@ -208,24 +218,49 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
             if constexpr (NORM)
                 gm[s] = gamma[c < nch ? c : nch - 1];
         }
+        // with the norm, the same lane's chunks of the other slices too
+        // (slices in order, this workgroup's own left out): the squares
+        // cover the whole row in every workgroup
+        u32x4 xo[NORM && KS > 1 ? KS - 1 : 1][NORM ? SPH : 1];
+        if constexpr (NORM && KS > 1) {
+#pragma unroll
+            for (int q = 0; q < KS - 1; ++q) {
+                const int qa = q < ks ? q : q + 1;
+#pragma unroll
+                for (int s = 0; s < SPH; ++s) {
+                    const int c = chunk0(qa) + 4 * P * s;
+                    xo[q][s] = bp[c < nch ? c : nch - 1];
+                }
+            }
+        }
         wait_vmcnt<0>();
         if constexpr (NORM) {
-            // this lane's squares in step order; then, in every wavefront,
-            // each lane adds the eight wavefronts' values of its own lane
-            // slot, and an xor butterfly over the lanes that hold the same
-            // token (j = t and, packed, t + 8; every g) completes the row:
-            // one fixed order, the same in every lane and workgroup
+            // this lane's squares, slices in order, steps in order; then, in
+            // every wavefront, each lane adds the W wavefronts' values of its
+            // own lane slot, and an xor butterfly over the lanes that hold
+            // the same token (j = t and, packed, t + 8; every g) completes
+            // the row: one fixed order, the same in every lane and workgroup
             float ss = 0.0f;
 #pragma unroll
-            for (int s = 0; s < SPH; ++s) {
-                const float q = dot8_bf16(b[s], b[s], 0.0f);   // v_dot2_f32_bf16
-                ss += cbase + 4 * P * (ph + s) < nch ? q : 0.0f;
+            for (int qa = 0; qa < KS; ++qa) {
+#pragma unroll
+                for (int s = 0; s < SPH; ++s) {
+                    u32x4 v = b[s];
+                    if constexpr (KS > 1) {
+                        // slice qa is xo[qa] below this workgroup's, xo[qa - 1] above
+                        const u32x4 lo = xo[qa < KS - 1 ? qa : KS - 2][s];
+                        const u32x4 hi = xo[qa > 0 ? qa - 1 : 0][s];
+                        v = qa < ks ? lo : (qa > ks ? hi : v);
+                    }
+                    const float q = dot8_bf16(v, v, 0.0f);     // v_dot2_f32_bf16
+                    ss += chunk0(qa) + 4 * P * s < nch ? q : 0.0f;
+                }
             }
             s_ss[wave][lane] = ss;
             __syncthreads();
             float tot = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kRouteWaves; ++w)
+            for (int w = 0; w < W; ++w)
                 tot += s_ss[w][lane];
             if (P == 2)
                 tot += __shfl_xor(tot, 8);
@@ -254,13 +289,13 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     if (wave == 0) {
         f32x4 sum = s_part[0][lane];
 #pragma unroll
-        for (int w = 1; w < kRouteWaves; ++w)
+        for (int w = 1; w < W; ++w)
             sum += s_part[w][lane];
         if (P == 2) {
             const int ly = (lane + 40) & (kWave - 1);
             f32x4 sy = s_part[0][ly];
 #pragma unroll
-            for (int w = 1; w < kRouteWaves; ++w)
+            for (int w = 1; w < W; ++w)
                 sy += s_part[w][ly];
             sum += sy;
         }
@@ -268,23 +303,38 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
         for (int r = 0; r < 4; ++r) {
             const int row = 4 * g + r, e = e0 + row;
             if (row < RT && e < E && j < M && (P == 1 || j < 8))
-                __hip_atomic_store(logits + (size_t)j * E + e, sum[r] + bv[r],
+                __hip_atomic_store(plog + ((size_t)ks * M + j) * E + e, sum[r],
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 
     // ---- the last workgroup to arrive selects
-    __builtin_amdgcn_s_waitcnt(0);               // this thread's logits are out
+    __builtin_amdgcn_s_waitcnt(0);               // this thread's partial logits are out
     __syncthreads();
-    if (threadIdx.x == 0)
-        s_last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+    if (threadIdx.x == 0) {
+        // two-level arrival: workgroup b counts in at group b / kRouteGroup
+        // (its counter on a line of its own); the group's last arrival
+        // resets it and counts in at the ticket, whose last arrival selects
+        const int grp = blockIdx.x / kRouteGroup;
+        const int ng = (gridDim.x + kRouteGroup - 1) / kRouteGroup;
+        const unsigned gsz = (unsigned)min(kRouteGroup, (int)gridDim.x - grp * kRouteGroup);
+        unsigned *gc = ticket + kWsLineWords * (1 + grp);
+        bool last = false;
+        if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            gsz - 1) {
+            __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == (unsigned)ng - 1;
+        }
+        s_last = last;
+    }
     __syncthreads();
     if constexpr (NORM) {
-        // workgroup 0 writes the normalised rows for the expert kernels only
-        // now: they must land by the end of the kernel, not before the
-        // ticket, so their latency overlaps the selection
-        if (blockIdx.x == 0 && (P == 2 ? (j & 7) : j) < M) {
+        // the workgroups of row group 0 (one per slice) write the
+        // normalised rows for the expert kernels only now: they must land by
+        // the end of the kernel, not before the ticket, so their latency
+        // overlaps the selection
+        if (e0 == 0 && (P == 2 ? (j & 7) : j) < M) {
 #pragma unroll
             for (int s = 0; s < SPH; ++s) {
                 const int c = cbase + 4 * P * s;
@@ -298,20 +348,31 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
     if (threadIdx.x == 0)
         __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    for (int t = wave; t < M; t += kRouteWaves) {
+    for (int t = wave; t < M; t += W) {
         // this lane's logits e = lane + 64*q as (order code, id); ids past E
         // get code 0, below every number (k <= E keeps them unselected)
         uint64_t key[KJ];
-        float lv[KJ];
+        float lv[KJ], pv[KS][KJ], bq[KJ];
 #pragma unroll
         for (int q = 0; q < KJ; ++q) {           // all loads in flight together
-            const int e = lane + kWave * q;
-            lv[q] = __hip_atomic_load(logits + (size_t)t * E + (e < E ? e : E - 1),
-                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int e = lane + kWave * q, ec = e < E ? e : E - 1;
+#pragma unroll
+            for (int sl = 0; sl < KS; ++sl)
+                pv[sl][q] = __hip_atomic_load(plog + ((size_t)sl * M + t) * E + ec,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            bq[q] = bias ? bias[ec] : 0.0f;
         }
 #pragma unroll
         for (int q = 0; q < KJ; ++q) {
             const int e = lane + kWave * q;
+            // the slices' partial sums in slice order, then the bias
+            float l = pv[0][q];
+#pragma unroll
+            for (int sl = 1; sl < KS; ++sl)
+                l += pv[sl][q];
+            lv[q] = l + bq[q];
+            if (logits && e < E)
+                logits[(size_t)t * E + e] = lv[q];
             // NaN never outranks a number; -0 and +0 share a code
             uint32_t u = __float_as_uint(lv[q] != lv[q] ? -INFINITY : lv[q]);
             u = u == 0x80000000u ? 0u : u;
@@ -321,9 +382,9 @@ __global__ __launch_bounds__(kRouteWaves * kWave) void route_kernel(
         sel_sort<KJ>(key);
         uint64_t sel = 0;                        // lane s keeps selection s
         for (int s = 0; s < k; ++s) {
-            const uint64_t W = wave_max_key(key[0]);
-            sel = lane == s ? W : sel;
-            sel_pop<KJ>(key, key[0] == W);       // the winner's next logit moves up
+            const uint64_t win = wave_max_key(key[0]);
+            sel = lane == s ? win : sel;
+            sel_pop<KJ>(key, key[0] == win);     // the winner's next logit moves up
         }
         const int sel_i = (int)~(uint32_t)sel;
         const uint32_t sel_h = (uint32_t)(sel >> 32);
@@ -346,76 +407,108 @@ struct RouteNorm {
     uint16_t *xn;
 };
 
-template <int S, int KJ, int P>
-static moe_status_t launch_route3(const uint16_t *x, const uint16_t *w, const float *bias,
-                                  int M, int H, int E, int k, float *logits, int *idx,
-                                  float *tw, unsigned *ticket, const RouteNorm &nm,
+// RT router rows per workgroup, W wavefronts, KS workgroups per row group
+template <int S, int KJ, int RT, int P, int W, int KS>
+static moe_status_t launch_route4(const uint16_t *x, const uint16_t *w, const float *bias,
+                                  int M, int H, int E, int k, float *plog, float *logits,
+                                  int *idx, float *tw, unsigned *ticket, const RouteNorm &nm,
                                   hipStream_t st)
 {
-    constexpr int RT = 8;
-    const int grid = (E + RT - 1) / RT;
+    const int grid = (E + RT - 1) / RT * KS;
+    if ((grid + kRouteGroup - 1) / kRouteGroup > kWsGroups)
+        return MOE_ERR_UNSUPPORTED;                      // (E <= 1024 stays within)
     if (nm.gamma) {
-        if constexpr (S <= 16)
-            hipLaunchKernelGGL((route_kernel<S, KJ, RT, P, true>), dim3(grid),
-                               dim3(kRouteWaves * kWave), 0, st, (const u32x4 *)x,
-                               (const u32x4 *)w, bias, M, H, E, k, logits, idx, tw, ticket,
+        if constexpr (S <= 128 / W)
+            hipLaunchKernelGGL((route_kernel<S, KJ, RT, P, true, W, KS>), dim3(grid),
+                               dim3(W * kWave), 0, st, (const u32x4 *)x, (const u32x4 *)w, bias,
+                               M, H, E, k, plog, logits, idx, tw, ticket,
                                (const u32x4 *)nm.gamma, nm.eps, (u32x4 *)nm.xn);
         else
             return MOE_ERR_UNSUPPORTED;
     } else {
-        hipLaunchKernelGGL((route_kernel<S, KJ, RT, P, false>), dim3(grid),
-                           dim3(kRouteWaves * kWave), 0, st, (const u32x4 *)x,
-                           (const u32x4 *)w, bias, M, H, E, k, logits, idx, tw, ticket,
-                           nullptr, 0.0f, nullptr);
+        hipLaunchKernelGGL((route_kernel<S, KJ, RT, P, false, W, KS>), dim3(grid),
+                           dim3(W * kWave), 0, st, (const u32x4 *)x, (const u32x4 *)w, bias, M,
+                           H, E, k, plog, logits, idx, tw, ticket, nullptr, 0.0f, nullptr);
     }
     return check_launch();
 }
 
-// S counts MFMA steps of 32 columns; packed, each step takes 64
-template <int S, int KJ>
-static moe_status_t launch_route2(const uint16_t *x, const uint16_t *w, const float *bias,
-                                  int M, int H, int E, int k, float *logits, int *idx,
-                                  float *tw, unsigned *ticket, const RouteNorm &nm,
+// Rows whose columns take at least four steps of every wavefront are
+// split over kRouteSlices workgroups when the grid stays within two
+// workgroups per CU: the 2.6 MB gate of 512 x 2560 then streams through
+// 256 CUs instead of 64.
+constexpr int kRouteSlices = 4;
+template <int S, int KJ, int RT, int P, int W>
+static moe_status_t launch_route3(const uint16_t *x, const uint16_t *w, const float *bias,
+                                  int M, int H, int E, int k, float *plog, float *logits,
+                                  int *idx, float *tw, unsigned *ticket, const RouteNorm &nm,
                                   hipStream_t st)
 {
+    if constexpr (S >= kRouteSlices) {
+        if ((E + RT - 1) / RT * kRouteSlices <= 2 * 256)   // (at most 16 arrival groups)
+            return launch_route4<(S + kRouteSlices - 1) / kRouteSlices, KJ, RT, P, W,
+                                 kRouteSlices>(x, w, bias, M, H, E, k, plog, logits, idx, tw,
+                                               ticket, nm, st);
+    }
+    return launch_route4<S, KJ, RT, P, W, 1>(x, w, bias, M, H, E, k, plog, logits, idx, tw,
+                                             ticket, nm, st);
+}
+
+// S counts the 32-column MFMA steps of eight wavefronts. Up to 8 tokens:
+// 8-row tiles, two blocks packed per step, eight wavefronts. More tokens
+// fill a 16-row tile with 16 distinct rows and 16 token columns; sixteen
+// wavefronts (up to 512 experts) then halve the steps of each and select
+// one token each.
+template <int S, int KJ>
+static moe_status_t launch_route2(const uint16_t *x, const uint16_t *w, const float *bias,
+                                  int M, int H, int E, int k, float *plog, float *logits,
+                                  int *idx, float *tw, unsigned *ticket, const RouteNorm &nm,
+                                  hipStream_t st)
+{
+    // (the selection's keys and partial sums of more than 512 experts need
+    // the register budget of eight wavefronts)
+    constexpr int W = KJ <= 8 ? 16 : 8;
     if (M <= 8)
-        return launch_route3<(S + 1) / 2, KJ, 2>(x, w, bias, M, H, E, k, logits, idx, tw,
-                                                 ticket, nm, st);
-    return launch_route3<S, KJ, 1>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, nm, st);
+        return launch_route3<(S + 1) / 2, KJ, 8, 2, 8>(x, w, bias, M, H, E, k, plog, logits,
+                                                       idx, tw, ticket, nm, st);
+    return launch_route3<(S * 8 + W - 1) / W, KJ, 16, 1, W>(x, w, bias, M, H, E, k, plog,
+                                                            logits, idx, tw, ticket, nm, st);
 }
 
 template <int S>
 static moe_status_t launch_route(const uint16_t *x, const uint16_t *w, const float *bias,
-                                 int M, int H, int E, int k, float *logits, int *idx,
-                                 float *tw, unsigned *ticket, const RouteNorm &nm,
+                                 int M, int H, int E, int k, float *plog, float *logits,
+                                 int *idx, float *tw, unsigned *ticket, const RouteNorm &nm,
                                  hipStream_t st)
 {
     if (E <= 128)
-        return launch_route2<S, 2>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, nm, st);
+        return launch_route2<S, 2>(x, w, bias, M, H, E, k, plog, logits, idx, tw, ticket, nm, st);
     if (E <= 256)
-        return launch_route2<S, 4>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, nm, st);
+        return launch_route2<S, 4>(x, w, bias, M, H, E, k, plog, logits, idx, tw, ticket, nm, st);
     if (E <= 512)
-        return launch_route2<S, 8>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, nm, st);
-    return launch_route2<S, 16>(x, w, bias, M, H, E, k, logits, idx, tw, ticket, nm, st);
+        return launch_route2<S, 8>(x, w, bias, M, H, E, k, plog, logits, idx, tw, ticket, nm, st);
+    return launch_route2<S, 16>(x, w, bias, M, H, E, k, plog, logits, idx, tw, ticket, nm, st);
 }
 
-// Workspace: the header (ticket), then [M,E] fp32 logits scratch.
+// Workspace: the header (ticket), then the partial logits [KS][M][E] fp32
+// of up to kRouteSlices slices.
 static size_t route_ws_logits(int32_t M, int32_t E)
 {
-    return align_up((size_t)M * (size_t)E * sizeof(float), 256);
+    return align_up((size_t)kRouteSlices * M * (size_t)E * sizeof(float), 256);
 }
 
-// MFMA steps per wavefront: eight wavefronts of 32-column steps
+// 32-column MFMA steps of each of eight wavefronts
 static int route_need(int H)
 {
-    return (H / 8 + 4 * kRouteWaves - 1) / (4 * kRouteWaves);
+    return (H / 8 + 4 * 8 - 1) / (4 * 8);
 }
 
 // the norm needs every chunk of a lane in registers at once: at most 16
-// MFMA steps per lane (always true when two blocks pack, M <= 8)
+// MFMA steps per lane with eight wavefronts (M <= 8, any H up to 8192), at
+// most 8 with sixteen, whose register budget is half (H <= 4096)
 bool route_norm_supported(int32_t M, int32_t H)
 {
-    return M <= 8 || route_need(H) <= 16;
+    return (route_need(H) + 1) / 2 <= (M <= 8 ? 16 : 8);
 }
 
 moe_status_t route_enqueue(const uint16_t *x, const uint16_t *w_router,
@@ -425,18 +518,21 @@ moe_status_t route_enqueue(const uint16_t *x, const uint16_t *w_router,
                            const uint16_t *gamma, float eps, uint16_t *x_norm)
 {
     unsigned *ticket = (unsigned *)ws;
-    float *lg = logits ? logits : (float *)((char *)ws + kWsHeader);
+    float *plog = (float *)((char *)ws + kWsHeader);
     const RouteNorm nm{gamma, eps, x_norm};
     const int need = route_need(H);
+#define MV_ROUTE(S) launch_route<S>(x, w_router, bias, M, H, E, k, plog, logits, topk_idx, \
+                                    topk_w, ticket, nm, st)
     if (need <= 2)
-        return launch_route<2>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, nm, st);
+        return MV_ROUTE(2);
     if (need <= 4)
-        return launch_route<4>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, nm, st);
+        return MV_ROUTE(4);
     if (need <= 10)
-        return launch_route<10>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, nm, st);
+        return MV_ROUTE(10);
     if (need <= 16)
-        return launch_route<16>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, nm, st);
-    return launch_route<32>(x, w_router, bias, M, H, E, k, lg, topk_idx, topk_w, ticket, nm, st);
+        return MV_ROUTE(16);
+    return MV_ROUTE(32);
+#undef MV_ROUTE
 }
 
 moe_status_t norm_check(const uint16_t *gamma, float eps, const uint16_t *x_norm,

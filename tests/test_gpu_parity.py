@@ -61,6 +61,8 @@ ROUTE_CASES = [
     (5, 4096, 1024, 16, 0.5),    # largest E and k
     (8, 8192, 256, 8, None),     # widest hidden state staged in LDS
     (16, 8192, 1024, 16, 0.5),   # hidden states too large for LDS: read from the caches
+    (9, 2560, 512, 8, None),     # one token past the packed launch shape
+    (12, 520, 100, 6, 1.0),      # ragged: 65 chunks per row, 100 experts
 ]
 
 
@@ -98,24 +100,26 @@ def test_route_zero_input_and_planted_ties():
     assert np.array_equal(gi_a, gi_b) and np.array_equal(gl_b, 2 * gl_a)
 
 
-@pytest.mark.parametrize("E,k", [(512, 8), (1024, 16), (200, 8)])
-def test_route_planted_ties_full_width(E, k):
+@pytest.mark.parametrize("E,k,M", [(512, 8, 1), (1024, 16, 1), (200, 8, 1), (512, 8, 12)])
+def test_route_planted_ties_full_width(E, k, M):
     """Zero hidden states make the logits equal to the bias exactly; a bias
     with few distinct values plants ties inside a lane (ids e and e + 64) and
-    across lanes. Order is value descending, then id ascending."""
-    say("route planted ties", E, k)
-    M, H = 3, 2560
+    across lanes. Order is value descending, then id ascending. M = 12 runs
+    the launch shape for more than eight tokens, every row the same."""
+    say("route planted ties", E, k, M)
+    H = 2560
     wr = synth.normal_bf16((E, H), 0.02, 9, E)
     bias = np.stack([((np.arange(E) * (31 + 6 * t)) % (5 + t)).astype(np.float32)
-                     for t in range(M)])
-    for t in range(M):
-        gi, gw, gl = run_route(np.zeros((1, H), np.uint16), wr, bias[t].copy(), k)
+                     for t in range(3)])
+    for t in range(3):
+        gi, gw, gl = run_route(np.zeros((M, H), np.uint16), wr, bias[t].copy(), k)
         order = np.lexsort((np.arange(E), -bias[t].astype(np.float64)))[:k]
-        assert np.array_equal(gi[0], order), (t, gi[0], order)
-        assert np.array_equal(gl[0], bias[t])
         ref = oracle.route(np.zeros((1, H), np.uint16), wr, bias[t].copy(), k)
-        assert np.array_equal(gi[0], ref["idx"][0])
-        assert_close(gw[0], ref["w"][0], "topk_w")
+        assert np.array_equal(ref["idx"][0], order)
+        for r in range(M):
+            assert np.array_equal(gi[r], order), (t, r, gi[r], order)
+            assert np.array_equal(gl[r], bias[t])
+            assert_close(gw[r], ref["w"][0], "topk_w")
 
 
 # ----------------------------------------------------------- expert FFN
@@ -425,7 +429,7 @@ def test_workspace_reuse_across_shapes():
 def test_layer_workspace_shared_across_M(full_layer):
     """One workspace serves moe_layer at M = 6, 1, 16, 6 in turn, with
     moe_expert_ffn calls in between: every result equals the same call on a
-    fresh zero-filled workspace, and the 256-byte header of counters is
+    fresh zero-filled workspace, and the 4 KB header of counters is
     zero after every call (the header sits at fixed offsets for every
     shape)."""
     say("workspace shared across M")
@@ -441,9 +445,9 @@ def test_layer_workspace_shared_across_M(full_layer):
         torch.cuda.synchronize()
         for ta, tb in zip(a, b):
             assert torch.equal(ta, tb), (M, "layer")
-        assert int(shared[:256].count_nonzero()) == 0, (M, "header after moe_layer")
+        assert int(shared[:4096].count_nonzero()) == 0, (M, "header after moe_layer")
         # the FFN alone on the same workspace, routed by the layer's ids
         c = mv.moe_expert_ffn(x, a[0], a[1], fw["gate"], fw["up"], fw["down"], workspace=shared)
         torch.cuda.synchronize()
         assert torch.equal(c, a[2]), (M, "ffn")
-        assert int(shared[:256].count_nonzero()) == 0, (M, "header after moe_expert_ffn")
+        assert int(shared[:4096].count_nonzero()) == 0, (M, "header after moe_expert_ffn")
