@@ -7,8 +7,10 @@
 // single-request step", Fig. 3).
 //
 // Design (gfx950):
-//   - The vocabulary is cut into 16-row tiles; workgroup b owns a contiguous
-//     run of tiles and its four wavefronts take every fourth tile.
+//   - The vocabulary is cut into 16-row tiles, dealt round-robin: wavefront w
+//     of workgroup b (of G) takes tiles b + G (w + 4 i), i = 0, 1, ..., so
+//     at any moment the whole chip streams one window of neighbouring tiles
+//     (measured faster than each workgroup walking a contiguous run).
 //   - A wavefront streams its tile K-block by K-block (KB elements of each of
 //     the 16 rows) straight from HBM into its own LDS double buffer with
 //     non-temporal 128-bit direct-to-LDS loads: every load instruction reads
@@ -66,7 +68,7 @@ template <bool W8>
 __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     const u32x4 *__restrict__ h, const u32x4 *__restrict__ wl,
     const float *__restrict__ wscale, int M, int H,
-    int V, int tiles_per_wg, unsigned long long *__restrict__ keys,
+    int V, unsigned long long *__restrict__ keys,
     unsigned *__restrict__ ticket, int *__restrict__ argmax,
     float *__restrict__ max_logit, const int *__restrict__ tokens,
     int *__restrict__ accept)
@@ -107,12 +109,10 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
                       g * (W8 ? 8 : 16);
 
     const int ntiles = (V + 15) / 16;
-    const int t0 = blockIdx.x * tiles_per_wg;
-    const int t1 = min(ntiles, t0 + tiles_per_wg);
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 
-    for (int tile = t0 + wave; tile < t1; tile += kLmWaves) {
+    for (int tile = blockIdx.x + gridDim.x * wave; tile < ntiles; tile += gridDim.x * kLmWaves) {
         const u32x4 *rp[kLmLoads];
 #pragma unroll
         for (int q = 0; q < kLmLoads; ++q) {
@@ -289,8 +289,7 @@ static moe_status_t lmhead_enqueue(const uint16_t *h, const void *w_lm, const fl
     unsigned *ticket = (unsigned *)workspace;
     unsigned long long *keys = (unsigned long long *)((char *)workspace + kWsHeader);
     const int ntiles = (V + 15) / 16;
-    const int tpw = (ntiles + kLmGridTarget - 1) / kLmGridTarget;
-    const int grid = (ntiles + tpw - 1) / tpw;
+    const int grid = min(ntiles, kLmGridTarget);
     const size_t lds = lm_lds_bytes(M, H, w8);
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
@@ -306,11 +305,11 @@ static moe_status_t lmhead_enqueue(const uint16_t *h, const void *w_lm, const fl
     if (w8)
         hipLaunchKernelGGL(lmhead_kernel<true>, dim3(grid), dim3(kLmWaves * kWave), lds,
                            (hipStream_t)stream, (const u32x4 *)h, (const u32x4 *)w_lm, w_scale,
-                           M, H, V, tpw, keys, ticket, argmax, max_logit, tokens, accept);
+                           M, H, V, keys, ticket, argmax, max_logit, tokens, accept);
     else
         hipLaunchKernelGGL(lmhead_kernel<false>, dim3(grid), dim3(kLmWaves * kWave), lds,
                            (hipStream_t)stream, (const u32x4 *)h, (const u32x4 *)w_lm, nullptr,
-                           M, H, V, tpw, keys, ticket, argmax, max_logit, tokens, accept);
+                           M, H, V, keys, ticket, argmax, max_logit, tokens, accept);
     return check_launch();
 }
 
