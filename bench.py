@@ -286,15 +286,31 @@ def main():
         pl8 = [(h.data_ptr(), q.data_ptr(), sc.data_ptr(), chain.data_ptr(), M, H, V,
                 am.data_ptr(), None, acc.data_ptr(), ws_lm.data_ptr(), ws_lm.numel(), stream)
                for q, sc in lms8]
+        # the routing of every expert call is kept, so the expert kernels'
+        # counters can be set against their algorithmic bytes
+        ids, ids8 = [], []
         for s in range(args.profile_steps):
             step(s)
+            ids.append(idx.clone())
             check("moe_route", L.moe_route(*route_args[s % len(route_args)]))
             check("moe_route_rmsnorm", L.moe_route_rmsnorm(*rn_args[s % len(rn_args)]))
             if p8 and M <= 9:
                 check("moe_layer_fp8", L.moe_layer_fp8(*p8[s % len(p8)]))
+                ids8.append(idx.clone())
             if pl8:
                 check("lmhead_greedy_verify_fp8", L.lmhead_greedy_verify_fp8(*pl8[s % len(pl8)]))
         torch.cuda.synchronize()
+        for name, lst, up_b, dn_b in (
+                ("bf16", ids, 2 * I * H * 2, H * I * 2),
+                ("fp8", ids8, 2 * I * (H + 4), H * (I + 4))):
+            if not lst:
+                continue
+            D = [len(np.unique(t.cpu().numpy())) for t in lst]
+            wd = sum(D) / len(D)
+            # reads: weights + x (or the activations) + routing; writes: act, out
+            log(f"profile {name} expert calls: distinct experts {D}; algorithmic bytes per call, "
+                f"mean: up read {wd * up_b + M * H * 2 + M * k * 4:.0f} write {M * k * I * 2}, "
+                f"down read {wd * dn_b + M * k * I * 2 + M * k * 8:.0f} write {M * H * 4}")
         log(f"profile run: {args.profile_steps} steps done")
         return
 
