@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--lm-copies", type=int, default=2)
     ap.add_argument("--fp8-layers", type=int, default=8,
                     help="distinct fp8 expert layers rotated for the fp8 lines (0 skips them)")
-    ap.add_argument("--router-copies", type=int, default=128,
+    ap.add_argument("--router-copies", type=int, default=512,
                     help="distinct router gates rotated in the gate-only timing")
     ap.add_argument("--zipf-alpha", type=float, default=None,
                     help="add a Zipf(1.1)-shaped router bias of this strength")
@@ -372,7 +372,7 @@ def main():
     # gate coldness: the same calls cycling over fewer distinct copies (the
     # time rises to a plateau once the copies no longer fit the caches)
     gate_sweep = {}
-    for n in (8, 32, R):
+    for n in sorted({min(c, R) for c in (8, 32, 128, R)}):
         for s in range(n):
             check("moe_route", L.moe_route(*route_args[s]))
         torch.cuda.synchronize()
@@ -384,6 +384,26 @@ def main():
         g1.record()
         torch.cuda.synchronize()
         gate_sweep[str(n)] = round(g0.elapsed_time(g1) * 1e3 / (2 * R), 2)
+
+    # the measured HBM read ceiling: a plain streaming read (grid-stride
+    # non-temporal 16-byte loads) over 4 rotating 1 GiB buffers
+    probe_bufs = [torch.empty(2**30, dtype=torch.uint8, device=dev) for _ in range(4)]
+    for b_ in probe_bufs:
+        b_.fill_(1)
+    sums = torch.empty(mv.HBM_PROBE_GROUPS, dtype=torch.int32, device=dev)
+    for b_ in probe_bufs[:2]:
+        mv.moe_hbm_read_probe(b_, sums)
+    torch.cuda.synchronize()
+    p0 = torch.cuda.Event(enable_timing=True)
+    p1 = torch.cuda.Event(enable_timing=True)
+    p0.record()
+    for s in range(16):
+        mv.moe_hbm_read_probe(probe_bufs[s % 4], sums)
+    p1.record()
+    torch.cuda.synchronize()
+    probe_gbps = 16 * 2**30 / (p0.elapsed_time(p1) * 1e-3) / 1e9
+    del probe_bufs
+    log(f"streaming-read probe: {probe_gbps:.0f} GB/s")
 
     for s in range(min(R, 16)):
         check("moe_route_rmsnorm", L.moe_route_rmsnorm(*rn_args[s]))
@@ -566,6 +586,11 @@ def main():
                       "bytes": int(layer_bytes_mean), "distinct_experts_mean": sum(D) / len(D)},
         "lm_head": {"us": round(lm_us_mean, 2), "GBps": round(lm_gbps, 1),
                     "frac": round(lm_gbps / HBM_PEAK_GBPS, 4), "bytes": lm_bytes},
+        "hbm_read_probe": {"GBps": round(probe_gbps, 1),
+                           "frac": round(probe_gbps / HBM_PEAK_GBPS, 4),
+                           "kernel": "moe_hbm_read_probe: grid-stride non-temporal 16-byte loads, "
+                                     "256 x 256 threads, 8 in flight per thread",
+                           "bytes_per_call": 2**30, "buffers_rotated": 4, "calls": 16},
         "router_gate_cold": {"us": round(route_us, 2),
                              "GBps": round(route_bytes / (route_us * 1e-6) / 1e9, 1),
                              "copies": R, "us_by_distinct_copies": gate_sweep},

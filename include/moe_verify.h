@@ -78,6 +78,26 @@ const char *moe_status_str(moe_status_t status);
 moe_status_t moe_workspace_clear(void *workspace, size_t bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * moe_hbm_read_probe -- a plain streaming read of `bytes` of device memory,
+ * the measured HBM read ceiling against which the kernels' rates are set
+ * (cold-weight bandwidth is the bound of every step of the path).
+ * MOE_HBM_PROBE_GROUPS workgroups of 256 threads read 16-byte chunks in
+ * grid-stride order (chunk c by thread c mod 65536) with non-temporal
+ * loads, eight in flight per thread, and fold every 32-bit word into an
+ * XOR.
+ *
+ *   src        device memory, 16-byte aligned, bytes a positive multiple
+ *              of 16; only read
+ *   checksums  [MOE_HBM_PROBE_GROUPS] u32 out: the XOR of the words each
+ *              workgroup read (their XOR is the XOR of all words of src)
+ *
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (bytes), MOE_ERR_ALIGN.
+ * ---------------------------------------------------------------------- */
+#define MOE_HBM_PROBE_GROUPS 256
+moe_status_t moe_hbm_read_probe(const void *src, size_t bytes, uint32_t *checksums,
+                                void *stream);
+
+/* ------------------------------------------------------------------------
  * moe_route -- router gate GEMV, softmax top-k, renormalised weights.
  * (router chain: gate matvec -> top-k; section "PDL: the latency floor of
  *  stacked small kernels", Fig. 7; bf16 gate, section "bf16 router gate

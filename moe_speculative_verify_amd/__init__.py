@@ -23,7 +23,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_UNSUPP
           4: "MOE_ERR_ALIGN", 5: "MOE_ERR_WORKSPACE", 6: "MOE_ERR_LAUNCH"}
 
 #: every symbol the header declares
-EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_clear",
+EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_clear", "moe_hbm_read_probe",
            "moe_route_workspace_bytes", "moe_route", "moe_route_rmsnorm",
            "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_expert_ffn_shared",
            "moe_expert_ffn_fp8", "moe_layer_fp8",
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.moe_status_str.argtypes = [ctypes.c_int32]
         L.moe_workspace_clear.restype = ctypes.c_int32
         L.moe_workspace_clear.argtypes = [_P, _S, _P]
+        L.moe_hbm_read_probe.restype = ctypes.c_int32
+        L.moe_hbm_read_probe.argtypes = [_P, _S, _P, _P]
         L.moe_route_workspace_bytes.restype = _S
         L.moe_route_workspace_bytes.argtypes = [_I, _I]
         L.moe_route.restype = ctypes.c_int32
@@ -166,6 +168,22 @@ def moe_workspace_clear(ws: torch.Tensor, stream=None) -> None:
     _check("moe_workspace_clear",
            lib().moe_workspace_clear(_ptr(ws, "workspace"), ws.numel() * ws.element_size(),
                                      _stream(stream)))
+
+
+#: workgroups of moe_hbm_read_probe, one checksum each
+HBM_PROBE_GROUPS = 256
+
+
+def moe_hbm_read_probe(buf: torch.Tensor, checksums: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """Plain streaming read of buf (the measured HBM read ceiling). Returns
+    the per-workgroup XOR checksums [HBM_PROBE_GROUPS] (int32 view of u32)."""
+    if checksums is None:
+        checksums = torch.empty(HBM_PROBE_GROUPS, dtype=torch.int32, device=buf.device)
+    _check("moe_hbm_read_probe",
+           lib().moe_hbm_read_probe(_ptr(buf, "buf"), buf.numel() * buf.element_size(),
+                                    _ptr(checksums, "checksums"), _stream(stream)))
+    return checksums
 
 
 def moe_route_workspace_bytes(M: int, E: int) -> int:

@@ -152,6 +152,15 @@ def test_workspace_clear_checks(L):
     assert L.moe_workspace_clear(A, 0, None) == OK
 
 
+def test_hbm_read_probe_checks(L):
+    assert L.moe_hbm_read_probe(None, 256, A, None) == NULL
+    assert L.moe_hbm_read_probe(A, 256, None, None) == NULL
+    assert L.moe_hbm_read_probe(A, 0, A, None) == SHAPE
+    assert L.moe_hbm_read_probe(A, 250, A, None) == SHAPE
+    assert L.moe_hbm_read_probe(MIS, 256, A, None) == ALIGN
+    assert L.moe_hbm_read_probe(A, 256, A + 2, None) == ALIGN
+
+
 def test_binding_refuses_host_tensors(L):
     import torch
     x = torch.zeros((1, 256), dtype=torch.bfloat16)

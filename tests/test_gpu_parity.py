@@ -226,6 +226,32 @@ def test_expert_ffn_single_expert_scaling():
     assert_close(a, ref, "out")
 
 
+def test_layer_expert_relabeling():
+    """Renaming the experts (router rows, weight slabs and bias entries moved
+    by one permutation) renames the selected ids and leaves the weights and
+    the output bitwise unchanged: no result depends on an expert's id or
+    position beyond the lowest-id tie rule."""
+    say("layer expert relabeling")
+    M, H, I, E, k = 6, 512, 256, 64, 4
+    x, w, bias = host_case(M, H, E, I, seed=71, bias_alpha=1.0)
+    perm = synth.rng(72).permutation(E)      # expert e is renamed perm[e]
+    wp, bp = {}, np.empty_like(bias)
+    for key, v in w.items():
+        wp[key] = np.empty_like(v)
+        wp[key][perm] = v
+    bp[perm] = bias
+    gi, gw, go = _layer_gpu(x, {key: to_dev(v) for key, v in w.items()}, bias, k)
+    pi, pw, po = _layer_gpu(x, {key: to_dev(v) for key, v in wp.items()}, bp, k)
+    ref = oracle.route(x, w["router"], bias, k)
+    tied = [t for t in range(M) if ref["gap_sel"][t] < TIE_BAND or ref["gap_order"][t] < TIE_BAND]
+    for t in range(M):
+        if t in tied:           # the lowest-id rule may order a tie differently
+            continue
+        assert np.array_equal(pi[t], perm[gi[t]]), (t, pi[t], perm[gi[t]])
+        assert np.array_equal(pw[t], gw[t])
+        assert np.array_equal(po[t], go[t])
+
+
 # ------------------------------------------------------------- full layer
 
 def _layer_gpu(x, w, bias, k):
@@ -451,3 +477,17 @@ def test_layer_workspace_shared_across_M(full_layer):
         torch.cuda.synchronize()
         assert torch.equal(c, a[2]), (M, "ffn")
         assert int(shared[:4096].count_nonzero()) == 0, (M, "header after moe_expert_ffn")
+
+
+def test_hbm_read_probe_checksum():
+    """The streaming-read probe reads every word once: the XOR of its
+    per-workgroup checksums equals the XOR of the buffer's 32-bit words, with
+    a ragged tail past the last full grid-stride sweep."""
+    nbytes = 64 * 2**20 + 48
+    say("hbm read probe", nbytes)
+    words = synth.rng(90).integers(0, 2**32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    cs = mv.moe_hbm_read_probe(buf)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(cs.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(words)
