@@ -173,6 +173,29 @@ def test_expert_ffn_full_size(full_layer, M, skew):
     assert_close(got, ref, "out")
 
 
+LIMIT_CASES = [
+    # M, H, I, E, k, routing skew
+    (5, 4096, 2048, 8, 4, 0.0),      # widest H of the down GEMV (16 rows per workgroup); 2 K blocks up
+    (16, 512, 256, 1024, 16, 0.0),   # most experts and slots: 256 pairs over 1024 experts
+    (2, 256, 8192, 8, 2, 0.0),       # largest I: 16 K blocks of every down row
+    (16, 1024, 512, 64, 8, 1.0),     # skewed routing: hot experts with up to 16 pairs
+]
+
+
+@pytest.mark.parametrize("M,H,I,E,k,skew", LIMIT_CASES)
+def test_expert_ffn_limits(M, H, I, E, k, skew):
+    say("expert_ffn limits", M, H, I, E, k, skew)
+    dw = device_layer(H, E, I, seed=synth.WEIGHT_SEED + H + I)
+    x = synth.activations(M, H, seed=500 + M + I)
+    idx, tw = synth.random_routing(M, E, k, 500 + E, skew)
+    out = mv.moe_expert_ffn(to_dev(x), torch.from_numpy(idx).cuda(), torch.from_numpy(tw).cuda(),
+                            dw["gate"], dw["up"], dw["down"])
+    got = out.cpu().numpy()
+    ref = oracle_ffn_from_device(x, idx, tw.astype(np.float64), dw)
+    assert_close(got, ref, "out")
+    del dw
+
+
 def test_expert_ffn_identical_tokens_share_experts(full_layer):
     """M identical tokens route identically: every row equals the M=1 row."""
     say("expert_ffn identical tokens")
