@@ -150,6 +150,43 @@ __device__ __forceinline__ float f32_unorder(uint32_t u)
     return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
+// one fused DPP step of a wave-wide uint32 maximum; rows a broadcast leaves
+// out receive 0, the identity, so the move folds into v_max_u32_dpp
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint32_t max_u32_dpp(uint32_t v)
+{
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWMASK, 0xF, false);
+    return o > v ? o : v;
+}
+// maximum over the wavefront, uniform: DPP steps inside each 16-lane row,
+// the rows combined with row_bcast:15 (into rows 1 and 3) and row_bcast:31
+// (into rows 2 and 3), then lane 63, which has seen every lane
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max_u32_dpp<0xB1, 0xF>(v);
+    v = max_u32_dpp<0x4E, 0xF>(v);
+    v = max_u32_dpp<0x141, 0xF>(v);
+    v = max_u32_dpp<0x140, 0xF>(v);
+    v = max_u32_dpp<0x142, 0xA>(v);
+    v = max_u32_dpp<0x143, 0xC>(v);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+// largest 64-bit key over the wavefront, uniform: the largest high word;
+// when a single lane holds it (equal logits are rare) the low word is read
+// from that lane, else it is the largest low word among the lanes holding it
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
+{
+    const uint32_t hi = (uint32_t)(v >> 32);
+    const uint32_t whi = wave_max_u32(hi);
+    const unsigned long long at = __ballot(hi == whi);
+    uint32_t wlo;
+    if (__popcll(at) == 1)                       // uniform
+        wlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, __builtin_ctzll(at));
+    else
+        wlo = wave_max_u32(hi == whi ? (uint32_t)v : 0u);
+    return ((uint64_t)whi << 32) | wlo;
+}
+
 // fp32 -> bf16 bits, round to nearest, ties to even (NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
 {
@@ -204,6 +241,27 @@ __device__ inline void stage_rows_lds(const u32x4 *__restrict__ src, int nrows, 
 constexpr size_t kWsHeader = 4096;
 constexpr int kWsLineWords = 32;              // words per 128-byte line
 constexpr int kWsGroups = 31;                 // arrival groups the header holds
+
+// Two-level arrival of the last-workgroup pattern, called by one thread per
+// workgroup once its results are out (stored at device scope and waited
+// for): workgroup b counts in at the counter of group b / kArrivalGroup (a
+// line of its own), the group's last arrival resets that counter and counts
+// in at the ticket (word 0), and the ticket's last arrival gets true and
+// resets nothing: the caller resets the ticket. Grids of up to kArrivalGroup
+// * kWsGroups workgroups.
+constexpr int kArrivalGroup = 32;
+__device__ inline bool arrive_last(unsigned *ticket)
+{
+    const int grp = blockIdx.x / kArrivalGroup;
+    const int ng = (gridDim.x + kArrivalGroup - 1) / kArrivalGroup;
+    const unsigned gsz = (unsigned)min(kArrivalGroup, (int)gridDim.x - grp * kArrivalGroup);
+    unsigned *gc = ticket + kWsLineWords * (1 + grp);
+    if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gsz - 1)
+        return false;
+    __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (unsigned)ng - 1;
+}
 
 // Dynamic LDS a kernel may request: 160 KB per CU on gfx950, less a margin
 // for the kernels' small static arrays.

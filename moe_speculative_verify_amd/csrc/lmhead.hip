@@ -22,11 +22,13 @@
 //     (staged once per workgroup in LDS, zero columns beyond M). One MFMA
 //     covers 1 KB of weights; no cross-lane reductions are needed.
 //   - Each lane keeps a running (max, first index) for its token; the
-//     workgroup's best per token is folded into a 64-bit key
-//     (order-preserving value bits << 32 | ~index) with a device-scope
-//     atomic max, so the largest value and then the lowest index win
-//     whatever the order. The last workgroup to take a ticket (device-scope
-//     atomic, no spinning, no cache flush) decodes the keys and resets them.
+//     workgroup's best per token becomes a 64-bit key (order-preserving
+//     value bits << 32 | ~index, so the largest value and then the lowest
+//     index win) stored in the workgroup's own slot of the workspace. The
+//     last workgroup to arrive (two-level ticket: device-scope atomics, no
+//     spinning, no cache flush) takes each token's maximum over the slots
+//     and decodes it. Every slot is written before it is read, so nothing
+//     past the header needs to be zero.
 //   - fp8 weights (lmhead_argmax_fp8, lmhead_greedy_verify_fp8): OCP E4M3
 //     codes with one fp32 scale per vocabulary row. A block is still 512
 //     bytes of each of the 16 rows (now 512 columns), staged the same way;
@@ -44,6 +46,9 @@
 namespace mv {
 
 constexpr int kLmWaves = 4;
+// one workgroup per CU: the LDS footprint allows no more
+constexpr int kLmGridTarget = 256;
+static_assert(kMaxM % kLmWaves == 0 && kLmGridTarget % kWave == 0, "key slots per lane");
 constexpr int kLmRowBytes = 512;                  // bytes of a row per block
 constexpr int kLmRowsPerLd = 1024 / kLmRowBytes;  // rows per load instruction
 constexpr int kLmLoads = 16 / kLmRowsPerLd;       // load instructions per block
@@ -208,29 +213,49 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
             }
         const unsigned long long key =
             ((unsigned long long)f32_order(best) << 32) | (uint32_t)(~(uint32_t)besti);
-        // returning form: the max has been performed when the value is back
-        const unsigned long long old = __hip_atomic_fetch_max(
-            keys + t, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == ~0ull)                                // never true: keeps old live
-            s_i[0][t] = 0;
+        __hip_atomic_store(keys + (size_t)blockIdx.x * M + t, key, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(0);                       // this workgroup's keys are out
     __syncthreads();
     if (threadIdx.x == 0)
-        s_last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+        s_last = arrive_last(ticket);
     __syncthreads();
     if (!s_last)
         return;
-    if (threadIdx.x < M) {
-        const int t = threadIdx.x;
-        const unsigned long long key = __hip_atomic_exchange(
-            keys + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int tok = (int)(~(uint32_t)key);
-        argmax[t] = tok;
-        s_tok[t] = tok;
-        if (max_logit)
-            max_logit[t] = f32_unorder((uint32_t)(key >> 32));
+    // wavefront w takes tokens w, w + 4, ...: lane l reads slots l, l + 64,
+    // ... of each (every load in flight at once, clamped addresses), keeps
+    // the largest, and the largest key over the wavefront decodes the token
+    constexpr int kTpw = kMaxM / kLmWaves;                // tokens per wavefront
+    constexpr int kSpl = kLmGridTarget / kWave;           // slots per lane
+    unsigned long long kv[kTpw][kSpl];
+#pragma unroll
+    for (int q = 0; q < kTpw; ++q) {
+        const int t = min(wave + kLmWaves * q, M - 1);
+#pragma unroll
+        for (int sl = 0; sl < kSpl; ++sl) {
+            const int b = min(lane + kWave * sl, (int)gridDim.x - 1);
+            kv[q][sl] = __hip_atomic_load(keys + (size_t)b * M + t, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < kTpw; ++q) {
+        const int t = wave + kLmWaves * q;
+        if (t >= M)                                      // uniform
+            break;
+        unsigned long long best = 0;
+#pragma unroll
+        for (int sl = 0; sl < kSpl; ++sl)
+            best = kv[q][sl] > best ? kv[q][sl] : best;  // (clamped reads repeat a slot)
+        const unsigned long long key = wave_max_key(best);
+        if (lane == 0) {
+            const int tok = (int)(~(uint32_t)key);
+            argmax[t] = tok;
+            s_tok[t] = tok;
+            if (max_logit)
+                max_logit[t] = f32_unorder((uint32_t)(key >> 32));
+        }
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -249,19 +274,17 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     }
 }
 
-// one workgroup per CU: the LDS footprint allows no more
-constexpr int kLmGridTarget = 256;
 
 } // namespace mv
 
 using namespace mv;
 
-// Workspace: the header (ticket), then M 64-bit keys.
+// Workspace: the header (tickets), then each workgroup's M 64-bit keys.
 extern "C" size_t lmhead_argmax_workspace_bytes(int32_t M, int32_t V)
 {
     if (M < 1 || M > kMaxM || V < 1)
         return 0;
-    return kWsHeader + align_up((size_t)M * 8, 256);
+    return kWsHeader + align_up((size_t)kLmGridTarget * M * 8, 256);
 }
 
 // w_lm: bf16 rows, or fp8 codes when w_scale is given (one scale per row)

@@ -39,8 +39,6 @@
 namespace mv {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-// workgroups per arrival group of the two-level ticket
-constexpr int kRouteGroup = 32;
 
 // ---- per-lane sorted lists of 64-bit selection keys (order code of the
 // logit << 32 | ~id: a larger key is a larger logit, or an equal logit with
@@ -96,42 +94,6 @@ __device__ __forceinline__ void sel_pop(uint64_t (&key)[KJ], bool adv)
     }
 }
 
-// one fused DPP step of a wave-wide uint32 maximum; rows a broadcast leaves
-// out receive 0, the identity, so the move folds into v_max_u32_dpp
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ uint32_t max_u32_dpp(uint32_t v)
-{
-    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWMASK, 0xF, false);
-    return o > v ? o : v;
-}
-// maximum over the wavefront, uniform: DPP steps inside each 16-lane row,
-// the rows combined with row_bcast:15 (into rows 1 and 3) and row_bcast:31
-// (into rows 2 and 3), then lane 63, which has seen every lane
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
-{
-    v = max_u32_dpp<0xB1, 0xF>(v);
-    v = max_u32_dpp<0x4E, 0xF>(v);
-    v = max_u32_dpp<0x141, 0xF>(v);
-    v = max_u32_dpp<0x140, 0xF>(v);
-    v = max_u32_dpp<0x142, 0xA>(v);
-    v = max_u32_dpp<0x143, 0xC>(v);
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-// largest 64-bit key over the wavefront, uniform: the largest high word;
-// when a single lane holds it (equal logits are rare) the low word is read
-// from that lane, else it is the largest low word among the lanes holding it
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
-{
-    const uint32_t hi = (uint32_t)(v >> 32);
-    const uint32_t whi = wave_max_u32(hi);
-    const unsigned long long at = __ballot(hi == whi);
-    uint32_t wlo;
-    if (__popcll(at) == 1)                       // uniform
-        wlo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, __builtin_ctzll(at));
-    else
-        wlo = wave_max_u32(hi == whi ? (uint32_t)v : 0u);
-    return ((uint64_t)whi << 32) | wlo;
-}
 
 // bf16(x * gain * inv) for eight elements: x * gain is exact in fp32 (two
 // 8-bit significands), then one product and one rounding to bf16
@@ -311,23 +273,8 @@ __global__ __launch_bounds__(W * kWave) void route_kernel(
     // ---- the last workgroup to arrive selects
     __builtin_amdgcn_s_waitcnt(0);               // this thread's partial logits are out
     __syncthreads();
-    if (threadIdx.x == 0) {
-        // two-level arrival: workgroup b counts in at group b / kRouteGroup
-        // (its counter on a line of its own); the group's last arrival
-        // resets it and counts in at the ticket, whose last arrival selects
-        const int grp = blockIdx.x / kRouteGroup;
-        const int ng = (gridDim.x + kRouteGroup - 1) / kRouteGroup;
-        const unsigned gsz = (unsigned)min(kRouteGroup, (int)gridDim.x - grp * kRouteGroup);
-        unsigned *gc = ticket + kWsLineWords * (1 + grp);
-        bool last = false;
-        if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            gsz - 1) {
-            __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            last = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT) == (unsigned)ng - 1;
-        }
-        s_last = last;
-    }
+    if (threadIdx.x == 0)
+        s_last = arrive_last(ticket);                    // two-level arrival
     __syncthreads();
     if constexpr (NORM) {
         // the workgroups of row group 0 (one per slice) write the
@@ -415,7 +362,7 @@ static moe_status_t launch_route4(const uint16_t *x, const uint16_t *w, const fl
                                   hipStream_t st)
 {
     const int grid = (E + RT - 1) / RT * KS;
-    if ((grid + kRouteGroup - 1) / kRouteGroup > kWsGroups)
+    if ((grid + kArrivalGroup - 1) / kArrivalGroup > kWsGroups)
         return MOE_ERR_UNSUPPORTED;                      // (E <= 1024 stays within)
     if (nm.gamma) {
         if constexpr (S <= 128 / W)

@@ -461,6 +461,47 @@ def test_determinism_and_batch_invariance(full_layer):
         assert am1[0] == am[t] and ml1[0] == ml[t]
 
 
+def test_workspace_shared_by_every_entry_point(full_layer):
+    """One workspace serves moe_layer, lmhead_argmax, moe_route and
+    lmhead_greedy_verify in turn with no clearing in between (whatever one
+    call leaves past the header must not change the next call's results):
+    every result equals the same call on a fresh zero-filled workspace, and
+    the header is zero after every call."""
+    say("workspace shared by every entry point")
+    k, H, E, I = 8, 2560, 512, 1024
+    M, V = 6, 20000
+    nbytes = max(mv.moe_layer_workspace_bytes(16, H, I, E, k),
+                 mv.lmhead_argmax_workspace_bytes(16, V), mv.moe_route_workspace_bytes(16, E))
+    shared = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    fw = full_layer
+    x = to_dev(synth.activations(M, H, seed=1200))
+    h = to_dev(synth.activations(M, H, seed=1201))
+    # small lm_head logits (|z| ~ 0.03): a key left over from another call
+    # (route logits ~ N(0, 1)) would win any argmax that read it
+    wl = to_dev(synth.normal_bf16((V, H), 0.0005, 1202, 0))
+
+    def fresh():
+        return torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+
+    chain = torch.zeros(M, dtype=torch.int32, device="cuda")
+    calls = [
+        lambda ws: mv.moe_layer(x, fw["router"], fw["gate"], fw["up"], fw["down"], k,
+                                workspace=ws),
+        lambda ws: mv.lmhead_argmax(h, wl, want_max=True, workspace=ws),
+        lambda ws: mv.moe_route(x, fw["router"], k, want_logits=True, workspace=ws),
+        lambda ws: mv.lmhead_greedy_verify(h, wl, chain, workspace=ws),
+        lambda ws: mv.moe_layer(x, fw["router"], fw["gate"], fw["up"], fw["down"], k,
+                                workspace=ws),
+    ]
+    for i, call in enumerate(calls):
+        a = call(fresh())
+        b = call(shared)
+        torch.cuda.synchronize()
+        for ta, tb in zip(a, b):
+            assert torch.equal(ta, tb), (i, "result")
+        assert int(shared[:4096].count_nonzero()) == 0, (i, "header")
+
+
 def test_workspace_reuse_across_shapes():
     """Counters left at zero: calls of different shapes reuse one workspace."""
     say("workspace reuse")
