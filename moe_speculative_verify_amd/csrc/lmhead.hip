@@ -10,7 +10,7 @@
 //   - The vocabulary is cut into 16-row tiles, dealt round-robin: wavefront w
 //     of workgroup b (of G) takes tiles b + G (w + 4 i), i = 0, 1, ..., so
 //     at any moment the whole chip streams one window of neighbouring tiles
-//     (measured faster than each workgroup walking a contiguous run).
+//     (the access order of the fastest plain read measured on this part).
 //   - A wavefront streams its tile K-block by K-block (KB elements of each of
 //     the 16 rows) straight from HBM into its own LDS double buffer with
 //     non-temporal 128-bit direct-to-LDS loads: every load instruction reads

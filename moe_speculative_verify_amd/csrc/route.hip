@@ -8,30 +8,33 @@
 // The post hides the gate's 2.6 MB cold read behind its producer with a
 // programmatic dependent launch. Here the chain is one launch whose latency
 // is a single HBM round trip plus the selection:
-//   - a workgroup owns RT router rows (one MFMA tile of 16 rows, or 8 rows
-//     with the upper half of the tile repeating the lower) and its eight
-//     wavefronts split the hidden dimension. Every wavefront issues all of
-//     its weight loads and hidden-state loads (the latter hit in L2) at
-//     once, so the whole gate matrix is in flight across the grid, then runs
-//     one v_mfma_f32_16x16x32_bf16 per 32 columns. The eight partial tiles
-//     are added in LDS in a fixed order, the bias added, and the logits
-//     published with device-scope stores;
-//   - the last workgroup to take a ticket (device-scope atomic; no spinning,
-//     no cache flush) selects, one wavefront per token: every lane sorts its
-//     logits by (value descending, id ascending) once; then each of the k
-//     rounds takes the wave-wide maximum of the lane heads (DPP on the
-//     32-bit order code), breaks an equal-value tie by the lowest id, and
-//     advances the winning lane's list. All loads are unpredicated and every
-//     step is branch-free apart from uniform tie checks. The softmax of the
-//     selected logits is taken in fp32.
+//   - a group of RT router rows (8 rows with two column blocks packed per
+//     v_mfma_f32_16x16x32_bf16 up to 8 tokens, else 16 rows) is split along
+//     the hidden dimension over KS workgroups (4 when every wavefront would
+//     otherwise take at least four steps), so the cold read is spread over
+//     all CUs; each workgroup's wavefronts split its slice again. Every
+//     wavefront issues all of its weight loads and hidden-state loads (the
+//     latter hit in L2) at once, then runs one MFMA per 32 (or 64) columns.
+//     The partial tiles are added in LDS in a fixed order and each slice's
+//     partial logits published with device-scope stores;
+//   - the last workgroup to arrive (two-level ticket of device-scope
+//     atomics; no spinning, no cache flush) adds each logit's slice partials
+//     in slice order and the bias, then selects, one wavefront per token:
+//     every lane sorts its logits by (value descending, id ascending) once;
+//     then each of the k rounds takes the wave-wide maximum of the lane heads
+//     (DPP on the 32-bit order code), breaks an equal-value tie by the
+//     lowest id, and advances the winning lane's list. All loads are
+//     unpredicated and every step is branch-free apart from uniform tie
+//     checks. The softmax of the selected logits is taken in fp32.
 //   - moe_route_rmsnorm puts the chain's norm in front (Fig. 7: norm -> gate
-//     matvec -> top-k), read as RMSNorm with a per-column gain: every
-//     workgroup already holds each (token, column) of the hidden states in
-//     exactly one lane, so the sum of squares is taken from those registers
-//     (per lane in step order, then over the lanes of a token in a fixed
-//     order through LDS), each lane scales its chunks and rounds them once to
-//     bf16 before the MFMAs, and workgroup 0 writes the normalised rows for
-//     the expert kernels. Every workgroup computes the same bits.
+//     matvec -> top-k), read as RMSNorm with a per-column gain: every lane
+//     already holds its chunks of the hidden states and loads the same
+//     lane's chunks of the other slices, so the sum of squares is taken
+//     from registers (per lane in slice and step order, then over the lanes
+//     of a token in a fixed order through LDS), each lane scales its chunks
+//     and rounds them once to bf16 before the MFMAs, and the workgroups of
+//     row group 0 write the normalised rows for the expert kernels. Every
+//     workgroup computes the same bits.
 #include "common.h"
 
 #include <utility>
