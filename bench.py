@@ -66,11 +66,37 @@ def parse():
     return ap.parse_args()
 
 
+def code_text(src: str) -> str:
+    """C++ source without comments and blank-line or trailing-space
+    differences: what the compiler sees of it."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        if src.startswith("//", i):
+            i = src.find("\n", i)
+            i = n if i < 0 else i
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif src[i] == '"':                     # string literals are kept whole
+            j = i + 1
+            while j < n and src[j] != '"':
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(src[i])
+            i += 1
+    lines = [ln.rstrip() for ln in "".join(out).splitlines()]
+    return "\n".join(ln for ln in lines if ln)
+
+
 def src_digest(*names: str) -> str:
+    """Digest of the code (not the comments) of the named sources: the
+    counters stay valid while it matches."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "moe_speculative_verify_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "moe_speculative_verify_amd", "csrc", n)) as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 
