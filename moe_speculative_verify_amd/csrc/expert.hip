@@ -789,7 +789,12 @@ static void launch_up_gemv(const uint16_t *x, const int *idx, const Experts &ex,
                            int I, int E, int k, uint16_t *act, hipStream_t st)
 {
     const size_t lds4 = up_gemv_lds_bytes(M, H, KC, W8, 4);
-    if (M == 1 || lds4 + 10 * 1024 <= 80 * 1024)
+    if (W8 && M > 1 && 3 * (lds4 + 10 * 1024) <= 160 * 1024)
+        // fp8: three workgroups per CU with a 4-deep ring (three wavefronts
+        // per SIMD fit its registers)
+        launch_up_gemv_wv<KC, kUpGemvNB, W8, 4>(3 * kXGrid, lds4, x, idx, ex, M, H, I, E, k, act,
+                                                st);
+    else if (M == 1 || lds4 + 10 * 1024 <= 80 * 1024)
         launch_up_gemv_wv<KC, up_gemv_nb(W8, 4), W8, 4>(M == 1 ? kXGrid : 2 * kXGrid, lds4, x,
                                                         idx, ex, M, H, I, E, k, act, st);
     else
@@ -883,6 +888,7 @@ static hipError_t set_lds_attributes()
     auto chk = [&](hipError_t r) { if (r != hipSuccess) e = r; };
 #define MV_UP_ATTR(KC) chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(false, 4), false, 4>)); \
     chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(true, 4), true, 4>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, true, 4>)); \
     chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(false, 8), false, 8>)); \
     chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(true, 8), true, 8>));
     MV_UP_ATTR(1) MV_UP_ATTR(2) MV_UP_ATTR(3) MV_UP_ATTR(4) MV_UP_ATTR(5)
