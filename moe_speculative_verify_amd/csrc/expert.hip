@@ -11,8 +11,8 @@
 // At verify widths (M <= 16 tokens, top-k of 512 experts) a selected expert
 // serves about one (token, slot) pair, so both projections are streamed as
 // matrix-vector products: the weights go straight from HBM into registers
-// (128-bit non-temporal loads, 1 KB contiguous per instruction, a register
-// ring of several blocks in flight per wavefront), the tokens' vectors sit
+// (128-bit non-temporal loads, 1 KB contiguous per instruction, one block
+// in flight per wavefront while it consumes the one before), the tokens' vectors sit
 // in LDS, and every lane forms eight-element dot products
 // (v_dot2_f32_bf16) that fixed DPP trees sum over the wavefront. No
 // floating-point atomics: results are bitwise reproducible and every pair's
@@ -742,11 +742,17 @@ __host__ __device__ inline size_t up_gemv_lds_bytes(int M, int H, int KC, bool w
 // ------------------------------------------------------------------ host
 
 // GEMV up kernel: KC 16-byte chunks per lane per row and block (a unit is
-// one block when a row has at most 5 * 64 chunks), a 4-deep register ring
-constexpr int kUpGemvNB = 4;
-// fp8 rows are half the bytes: a deeper ring keeps as many bytes in flight,
-// except with eight wavefronts, whose 256-register budget it would exceed
-constexpr int up_gemv_nb(bool w8, int wv) { return w8 && wv == 4 ? 6 : kUpGemvNB; }
+// one block when a row has at most 5 * 64 chunks), a 2-deep register ring:
+// one block in flight while the wavefront consumes the one before. Deeper
+// rings were measured slower at every width (M=6: 3 blocks ahead 77.7 us,
+// 1 ahead 75.6; fp8 M=1: 5 ahead 18.2 us, 1 ahead 14.3): with eight
+// wavefronts per CU the extra loads in flight only lengthen every load's
+// wait, and the CUs finish further apart.
+constexpr int kUpGemvNB = 2;
+// three fp8 workgroups per CU (twelve wavefronts) issue enough on their own:
+// no block ahead (M=6: 42.8 us, against 44.7 one ahead; M=1: 12.3 against
+// 12.7 with two workgroups per CU one ahead)
+constexpr int kUpGemvNB3 = 1;
 static int up_gemv_kc(int H, bool w8)
 {
     const int need = ((w8 ? H / 16 : H / 8) + kWave - 1) / kWave;
@@ -768,12 +774,11 @@ struct Experts {
     const float *sg, *su, *sd;
 };
 
-// Eight wavefronts per CU when there is more than one token: they hide each
-// other's per-unit latency (the group lookups, the reductions, the
-// epilogue) and keep the loads of one flowing while another computes. Two
-// four-wavefront workgroups per CU when their LDS allows (x of M tokens,
-// the queues, the grouping), else one workgroup of eight.
-// (a single token has only k units per 1024 rows: four per CU are enough)
+// Eight wavefronts per CU: they hide each other's per-unit latency (the
+// group lookups, the reductions, the epilogue) and keep the loads of one
+// flowing while another computes. Two four-wavefront workgroups per CU when
+// their LDS allows (x of M tokens, the queues, the grouping), else one
+// workgroup of eight; fp8 workgroups three per CU when their LDS allows.
 template <int KC, int NB, bool W8, int WV>
 static void launch_up_gemv_wv(int grid, size_t lds, const uint16_t *x, const int *idx,
                               const Experts &ex, int M, int H, int I, int E, int k,
@@ -789,17 +794,16 @@ static void launch_up_gemv(const uint16_t *x, const int *idx, const Experts &ex,
                            int I, int E, int k, uint16_t *act, hipStream_t st)
 {
     const size_t lds4 = up_gemv_lds_bytes(M, H, KC, W8, 4);
-    if (W8 && M > 1 && 3 * (lds4 + 10 * 1024) <= 160 * 1024)
-        // fp8: three workgroups per CU with a 4-deep ring (three wavefronts
-        // per SIMD fit its registers)
-        launch_up_gemv_wv<KC, kUpGemvNB, W8, 4>(3 * kXGrid, lds4, x, idx, ex, M, H, I, E, k, act,
+    if (W8 && 3 * (lds4 + 10 * 1024) <= 160 * 1024)
+        // fp8: three workgroups per CU, no block ahead
+        launch_up_gemv_wv<KC, kUpGemvNB3, W8, 4>(3 * kXGrid, lds4, x, idx, ex, M, H, I, E, k, act,
+                                                 st);
+    else if (lds4 + 10 * 1024 <= 80 * 1024)
+        launch_up_gemv_wv<KC, kUpGemvNB, W8, 4>(2 * kXGrid, lds4, x, idx, ex, M, H, I, E, k, act,
                                                 st);
-    else if (M == 1 || lds4 + 10 * 1024 <= 80 * 1024)
-        launch_up_gemv_wv<KC, up_gemv_nb(W8, 4), W8, 4>(M == 1 ? kXGrid : 2 * kXGrid, lds4, x,
-                                                        idx, ex, M, H, I, E, k, act, st);
     else
-        launch_up_gemv_wv<KC, up_gemv_nb(W8, 8), W8, 8>(kXGrid, up_gemv_lds_bytes(M, H, KC, W8, 8),
-                                                        x, idx, ex, M, H, I, E, k, act, st);
+        launch_up_gemv_wv<KC, kUpGemvNB, W8, 8>(kXGrid, up_gemv_lds_bytes(M, H, KC, W8, 8), x, idx,
+                                                ex, M, H, I, E, k, act, st);
 }
 template <bool W8>
 static void launch_up_gemv_kc(const uint16_t *x, const int *idx, const Experts &ex, int M,
@@ -824,8 +828,10 @@ static int down_rows(int H)
             return r;
     return 0;
 }
-// register ring depth of the GEMV down kernel: R * NB 16-byte loads per lane
-constexpr int down_gemv_nb(int R) { return R <= 10 ? 4 : (R <= 12 ? 3 : 2); }
+// register ring depth of the GEMV down kernel: one block (R 16-byte loads
+// per lane) in flight while the wavefront consumes the one before (three
+// ahead: M=6 45.9 us, M=1 15.7; one ahead: 44.3 and 13.6)
+constexpr int kDnGemvNB = 2;
 // the GEMV down kernel runs when every pair's activation row fits in LDS
 // (NPT pairs: M*k routed, plus M with a shared expert)
 static bool down_gemv_fits(int R, int NPT, int I, bool w8)
@@ -837,12 +843,12 @@ static size_t down_lds_bytes(int R, int NB, int NPT)
     // the weight rings, the pairs' sums [NPT][R], the routing weights [NPT]
     return (size_t)kXWaves * NB * R * kXRowPitch + (size_t)NPT * (R + 1) * sizeof(float);
 }
-static int down_nb(int R, int NPT)
+// LDS ring of the MFMA down kernel: one block in flight while the one before
+// is consumed (a third slot measured no faster: M=16 107.0 against 105.9 us)
+constexpr int kDnMfmaNB = 2;
+static bool down_mfma_fits(int R, int NPT)
 {
-    for (int nb = 3; nb >= 2; --nb)
-        if (down_lds_bytes(R, nb, NPT) <= (size_t)kXLdsDynMax)
-            return nb;
-    return 0;
+    return down_lds_bytes(R, kDnMfmaNB, NPT) <= (size_t)kXLdsDynMax;
 }
 
 // Workspace: the header, then the bf16 activations of M*(k+1) pairs (room
@@ -866,7 +872,7 @@ static moe_status_t ffn_check(const uint16_t *x, const int32_t *topk_idx,
     if (I < 1)
         return MOE_ERR_SHAPE;
     if (I % 8 != 0 || I > kMaxDim || !up_gemv_fits(M, H, false) || down_rows(H) == 0 ||
-        down_nb(down_rows(H), M * k) == 0)
+        !down_mfma_fits(down_rows(H), M * k))
         return MOE_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) ||
         !aligned16(w_down) || !aligned4(topk_idx) || !aligned4(topk_w) ||
@@ -886,16 +892,16 @@ static hipError_t set_lds_attributes()
 {
     hipError_t e = hipSuccess;
     auto chk = [&](hipError_t r) { if (r != hipSuccess) e = r; };
-#define MV_UP_ATTR(KC) chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(false, 4), false, 4>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(true, 4), true, 4>)); \
+#define MV_UP_ATTR(KC) chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false, 4>)); \
     chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, true, 4>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(false, 8), false, 8>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, up_gemv_nb(true, 8), true, 8>));
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB3, true, 4>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false, 8>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, true, 8>));
     MV_UP_ATTR(1) MV_UP_ATTR(2) MV_UP_ATTR(3) MV_UP_ATTR(4) MV_UP_ATTR(5)
 #undef MV_UP_ATTR
-#define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, 2>)); chk(allow_lds(expert_down_kernel<R, 3>)); \
-    chk(allow_lds(expert_down_gemv_kernel<R, down_gemv_nb(R), false>)); \
-    chk(allow_lds(expert_down_gemv_kernel<R, down_gemv_nb(R), true>));
+#define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, kDnMfmaNB>)); \
+    chk(allow_lds(expert_down_gemv_kernel<R, kDnGemvNB, false>)); \
+    chk(allow_lds(expert_down_gemv_kernel<R, kDnGemvNB, true>));
     MV_DOWN_ATTR(4) MV_DOWN_ATTR(8) MV_DOWN_ATTR(10) MV_DOWN_ATTR(12) MV_DOWN_ATTR(16)
 #undef MV_DOWN_ATTR
     return e;
@@ -909,32 +915,27 @@ static void launch_down_gemv(const uint16_t *act, const int *idx, const float *t
     const int grid = (H + R - 1) / R;
     const size_t lds = down_gemv_lds_bytes(R, M * k + ex.ns * M, I, ex.w8);
     if (ex.w8)
-        hipLaunchKernelGGL((expert_down_gemv_kernel<R, down_gemv_nb(R), true>), dim3(grid),
+        hipLaunchKernelGGL((expert_down_gemv_kernel<R, kDnGemvNB, true>), dim3(grid),
                            dim3(kDnThreads), lds, st, (const u32x4 *)act, idx, tw,
                            (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, ex.sd, M, H, I, E, k,
                            ex.ns, out);
     else
-        hipLaunchKernelGGL((expert_down_gemv_kernel<R, down_gemv_nb(R), false>), dim3(grid),
+        hipLaunchKernelGGL((expert_down_gemv_kernel<R, kDnGemvNB, false>), dim3(grid),
                            dim3(kDnThreads), lds, st, (const u32x4 *)act, idx, tw,
                            (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, nullptr, M, H, I, E, k,
                            ex.ns, out);
 }
 
 template <int R>
-static void launch_down_r(int nb, const uint16_t *act, const int *idx, const float *tw,
+static void launch_down_r(const uint16_t *act, const int *idx, const float *tw,
                           const Experts &ex, int M, int H, int I, int E, int k, float *out,
                           hipStream_t st)
 {
     const int grid = (H + R - 1) / R;
-    const size_t lds = down_lds_bytes(R, nb, M * k + ex.ns * M);
-    if (nb == 3)
-        hipLaunchKernelGGL((expert_down_kernel<R, 3>), dim3(grid), dim3(kXThreads), lds, st,
-                           (const u32x4 *)act, idx, tw, (const u32x4 *)ex.wd,
-                           (const u32x4 *)ex.wds, M, H, I, E, k, ex.ns, out);
-    else
-        hipLaunchKernelGGL((expert_down_kernel<R, 2>), dim3(grid), dim3(kXThreads), lds, st,
-                           (const u32x4 *)act, idx, tw, (const u32x4 *)ex.wd,
-                           (const u32x4 *)ex.wds, M, H, I, E, k, ex.ns, out);
+    const size_t lds = down_lds_bytes(R, kDnMfmaNB, M * k + ex.ns * M);
+    hipLaunchKernelGGL((expert_down_kernel<R, kDnMfmaNB>), dim3(grid), dim3(kXThreads), lds, st,
+                       (const u32x4 *)act, idx, tw, (const u32x4 *)ex.wd,
+                       (const u32x4 *)ex.wds, M, H, I, E, k, ex.ns, out);
 }
 
 static moe_status_t ffn_enqueue(const uint16_t *x, const int32_t *topk_idx,
@@ -973,13 +974,12 @@ static moe_status_t ffn_enqueue(const uint16_t *x, const int32_t *topk_idx,
     }
     if (ex.w8)                       // fp8 runs the GEMV down kernel only (checked)
         return MOE_ERR_UNSUPPORTED;
-    const int nbd = down_nb(R, NPT);
     switch (R) {
-    case 4: launch_down_r<4>(nbd, act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
-    case 8: launch_down_r<8>(nbd, act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
-    case 10: launch_down_r<10>(nbd, act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
-    case 12: launch_down_r<12>(nbd, act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
-    default: launch_down_r<16>(nbd, act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
+    case 4: launch_down_r<4>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
+    case 8: launch_down_r<8>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
+    case 10: launch_down_r<10>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
+    case 12: launch_down_r<12>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
+    default: launch_down_r<16>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
     }
     return check_launch();
 }
@@ -992,7 +992,7 @@ static moe_status_t shared_check(const uint16_t *wgs, const uint16_t *wus, const
     if (!wgs || !wus || !wds)
         return MOE_ERR_NULL;
     if (M * (k + 1) > kMaxNP || E + 1 > kMaxE ||
-        down_nb(down_rows(H), M * (k + 1)) == 0 || I > kMaxDim)
+        !down_mfma_fits(down_rows(H), M * (k + 1)) || I > kMaxDim)
         return MOE_ERR_UNSUPPORTED;
     if (!aligned16(wgs) || !aligned16(wus) || !aligned16(wds))
         return MOE_ERR_ALIGN;
