@@ -562,7 +562,7 @@ __host__ __device__ inline size_t up_gemv_x_bytes(int M, int H, int KC, bool w8)
 // W8: fp8 weights (E4M3 codes, 16 per 16-byte chunk, an fp32 scale per
 // row in sg / su); each chunk is widened to two bf16 chunks that meet two x
 // chunks, and the row scales multiply the reduced sums before the SwiGLU.
-template <int KC, int NB, bool W8, int WV>
+template <int KC, int NB, bool W8, int WV, bool CLAIM>
 __global__ __launch_bounds__(WV * kWave) void expert_up_gemv_kernel(
     const u32x4 *__restrict__ x, const int *__restrict__ topk_idx,
     const u32x4 *__restrict__ wg, const u32x4 *__restrict__ wu,
@@ -598,25 +598,52 @@ __global__ __launch_bounds__(WV * kWave) void expert_up_gemv_kernel(
         pend = 0;
     };
 
+    __shared__ int s_next;                               // the workgroup's next unit to claim
     groups_set_pairs(pair_expert(topk_idx, threadIdx.x, NP, NPT, E), NPT, E + ns, g);
+    if (threadIdx.x == 0)
+        s_next = 0;
     wait_vmcnt<0>();                                     // only the pair id is in flight
     for (int i = threadIdx.x; i < M * (xs - nch); i += blockDim.x) {
         const int t = i / (xs - nch), c = nch + i % (xs - nch);
         s_x[t * xs + c] = u32x4{0, 0, 0, 0};             // K padding reads as zero
     }
-    groups_finish(NPT, g);
+    groups_finish(NPT, g);                               // (its barriers also publish s_next)
 
-    // ---- unit u runs on wavefront u mod (WV * gridDim.x), so every
-    // wavefront sees every column block and a heavily shared expert's cost
-    // spreads evenly; block X of this wavefront carries the tag
-    // unit * 16 + kb, or -1 past its last block
+    // ---- Units in order (column block v, row i): the chip streams one moving
+    // window of the weights. Tag of a block: unit * 16 + kb, or -1 past the
+    // end. A unit's K blocks stay on one wavefront.
+    // CLAIM: the workgroup's units are b, b + grid, b + 2 grid, ...; its
+    // wavefronts claim them one at a time from an LDS counter, so a wavefront
+    // that its SIMD's arbitration serves less often (the younger of the
+    // SIMD's wavefronts) simply takes fewer units.
+    // Static: unit u runs on wavefront u mod (WV * grid).
     const int nunits = uniform(g.DV) * I;
+    const int nwg = nunits > (int)blockIdx.x ? (nunits - 1 - (int)blockIdx.x) / gridDim.x + 1 : 0;
+    auto claim = [&]() {                                 // uniform: a unit, or -1
+        int j = 0;
+        if (lane == 0)
+            j = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        j = uniform(__builtin_amdgcn_readlane(j, 0));
+        return j < nwg ? (int)blockIdx.x + (int)gridDim.x * j : -1;
+    };
     const int GW = gridDim.x * WV;
     const int gw = blockIdx.x * WV + wave;
-    const int nmine = nunits > gw ? (nunits - 1 - gw) / GW + 1 : 0;
-    const int nblk = nmine * nbu;
-    auto tag_of = [&](int X) {
-        return X < nblk ? (gw + GW * (X / nbu)) * 16 + X % nbu : -1;
+    const int nblk = nunits > gw ? ((nunits - 1 - gw) / GW + 1) * nbu : 0;   // static: this wavefront's blocks
+    int X = 0;                                           // static: the next block
+    int cur_u = CLAIM ? claim() : -1, cur_kb = 0;        // claims: the next block to issue
+    auto next_tag = [&]() {
+        int t = -1;
+        if constexpr (!CLAIM) {
+            t = X < nblk ? (gw + GW * (X / nbu)) * 16 + X % nbu : -1;
+            ++X;
+        } else if (cur_u >= 0) {
+            t = cur_u * 16 + cur_kb;
+            if (++cur_kb == nbu) {
+                cur_kb = 0;
+                cur_u = claim();
+            }
+        }
+        return t;
     };
 
     // Block of a tag: KC loads of the gate row, KC of the up row. A -1 tag
@@ -711,20 +738,27 @@ __global__ __launch_bounds__(WV * kWave) void expert_up_gemv_kernel(
 
     u32x4 wgr[NB][KC], wur[NB][KC];
     float sgr[NB] = {}, sur[NB] = {};                    // fp8 row scales (unused for bf16)
+    int tg[NB];                                          // tags of the ring's blocks
 #pragma unroll
-    for (int q = 0; q < NB - 1; ++q)
-        issue(tag_of(q), wgr[q], wur[q], sgr[q], sur[q]);
+    for (int q = 0; q < NB - 1; ++q) {
+        tg[q] = next_tag();
+        issue(tg[q], wgr[q], wur[q], sgr[q], sur[q]);
+    }
     stage_rows_lds(x, M, nch, s_x, xs);
     wait_vmcnt<0>();                                     // this wave's share of x has landed
     lds_barrier();                                       // ... and every other wave's
-    for (int X0 = 0; X0 < nblk; X0 += NB) {
+    for (bool live = true; live;) {
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
             const int nq = (q + NB - 1) % NB;
-            issue(tag_of(X0 + q + NB - 1), wgr[nq], wur[nq], sgr[nq], sur[nq]);
-            wait_vmcnt<(NB - 1) * 2 * KC>();             // block X0 + q has landed
-            if (X0 + q < nblk)
-                consume(tag_of(X0 + q), wgr[q], wur[q], sgr[q], sur[q]);
+            tg[nq] = next_tag();
+            issue(tg[nq], wgr[nq], wur[nq], sgr[nq], sur[nq]);
+            wait_vmcnt<(NB - 1) * 2 * KC>();             // block q has landed
+            if (tg[q] < 0) {                             // uniform: nothing left
+                live = false;
+                break;
+            }
+            consume(tg[q], wgr[q], wur[q], sgr[q], sur[q]);
         }
     }
     wait_vmcnt<0>();                                     // dummy loads have landed
@@ -742,17 +776,24 @@ __host__ __device__ inline size_t up_gemv_lds_bytes(int M, int H, int KC, bool w
 // ------------------------------------------------------------------ host
 
 // GEMV up kernel: KC 16-byte chunks per lane per row and block (a unit is
-// one block when a row has at most 5 * 64 chunks), a 2-deep register ring:
-// one block in flight while the wavefront consumes the one before. Deeper
-// rings were measured slower at every width (M=6: 3 blocks ahead 77.7 us,
-// 1 ahead 75.6; fp8 M=1: 5 ahead 18.2 us, 1 ahead 14.3): with eight
-// wavefronts per CU the extra loads in flight only lengthen every load's
-// wait, and the CUs finish further apart.
+// one block when a row has at most 5 * 64 chunks), streamed through a
+// register ring of NB blocks (NB - 1 in flight while one is consumed).
+// Shallow rings measured faster at every width (static split, M=6: 3 blocks
+// ahead 77.7 us, 1 ahead 75.6; fp8 M=1: 5 ahead 18.2 us, 1 ahead 14.3): with
+// eight or more wavefronts per CU extra loads in flight only lengthen every
+// load's wait.
+// The default: one workgroup of twelve wavefronts per CU (three per SIMD)
+// that claim units from an LDS counter, no block ahead. A SIMD serves its
+// older wavefront first (with a static split the younger wavefronts of a CU
+// ended 15 us after the older ones at M=6, 40 us at M=16); with claims they
+// all end within about one unit. Against the static split on eight
+// wavefronts: M=6 75.9 against 76.8 us, M=16 181.0 against 187.8, fp8 M=6
+// 41.0 against 43.5, fp8 M=1 12.5 against 13.3.
+constexpr int kUpClaimWaves = 12;
+constexpr int kUpClaimNB = 1;
+// bf16 at M = 1: two four-wavefront workgroups per CU with the static split
+// and one block ahead (17.8 us, against 18.6 with claims)
 constexpr int kUpGemvNB = 2;
-// three fp8 workgroups per CU (twelve wavefronts) issue enough on their own:
-// no block ahead (M=6: 42.8 us, against 44.7 one ahead; M=1: 12.3 against
-// 12.7 with two workgroups per CU one ahead)
-constexpr int kUpGemvNB3 = 1;
 static int up_gemv_kc(int H, bool w8)
 {
     const int need = ((w8 ? H / 16 : H / 8) + kWave - 1) / kWave;
@@ -774,36 +815,34 @@ struct Experts {
     const float *sg, *su, *sd;
 };
 
-// Eight wavefronts per CU: they hide each other's per-unit latency (the
-// group lookups, the reductions, the epilogue) and keep the loads of one
-// flowing while another computes. Two four-wavefront workgroups per CU when
-// their LDS allows (x of M tokens, the queues, the grouping), else one
-// workgroup of eight; fp8 workgroups three per CU when their LDS allows.
-template <int KC, int NB, bool W8, int WV>
+// Several wavefronts per SIMD hide each other's per-unit latency (the group
+// lookups, the reductions, the epilogue) and keep the loads of one flowing
+// while another computes.
+template <int KC, int NB, bool W8, int WV, bool CLAIM>
 static void launch_up_gemv_wv(int grid, size_t lds, const uint16_t *x, const int *idx,
                               const Experts &ex, int M, int H, int I, int E, int k,
                               uint16_t *act, hipStream_t st)
 {
-    hipLaunchKernelGGL((expert_up_gemv_kernel<KC, NB, W8, WV>), dim3(grid), dim3(WV * kWave), lds,
-                       st, (const u32x4 *)x, idx, (const u32x4 *)ex.wg, (const u32x4 *)ex.wu,
-                       (const u32x4 *)ex.wgs, (const u32x4 *)ex.wus, ex.sg, ex.su, M, H, I, E,
-                       k, ex.ns, act);
+    hipLaunchKernelGGL((expert_up_gemv_kernel<KC, NB, W8, WV, CLAIM>), dim3(grid),
+                       dim3(WV * kWave), lds, st, (const u32x4 *)x, idx, (const u32x4 *)ex.wg,
+                       (const u32x4 *)ex.wu, (const u32x4 *)ex.wgs, (const u32x4 *)ex.wus, ex.sg,
+                       ex.su, M, H, I, E, k, ex.ns, act);
 }
 template <int KC, bool W8>
 static void launch_up_gemv(const uint16_t *x, const int *idx, const Experts &ex, int M, int H,
                            int I, int E, int k, uint16_t *act, hipStream_t st)
 {
     const size_t lds4 = up_gemv_lds_bytes(M, H, KC, W8, 4);
-    if (W8 && 3 * (lds4 + 10 * 1024) <= 160 * 1024)
-        // fp8: three workgroups per CU, no block ahead
-        launch_up_gemv_wv<KC, kUpGemvNB3, W8, 4>(3 * kXGrid, lds4, x, idx, ex, M, H, I, E, k, act,
-                                                 st);
-    else if (lds4 + 10 * 1024 <= 80 * 1024)
-        launch_up_gemv_wv<KC, kUpGemvNB, W8, 4>(2 * kXGrid, lds4, x, idx, ex, M, H, I, E, k, act,
-                                                st);
-    else
-        launch_up_gemv_wv<KC, kUpGemvNB, W8, 8>(kXGrid, up_gemv_lds_bytes(M, H, KC, W8, 8), x, idx,
-                                                ex, M, H, I, E, k, act, st);
+    const size_t lds12 = up_gemv_lds_bytes(M, H, KC, W8, kUpClaimWaves);
+    if (!W8 && M == 1 && lds4 + 10 * 1024 <= 80 * 1024)
+        launch_up_gemv_wv<KC, kUpGemvNB, false, 4, false>(2 * kXGrid, lds4, x, idx, ex, M, H, I,
+                                                          E, k, act, st);
+    else if (lds12 <= (size_t)kXLdsDynMax)
+        launch_up_gemv_wv<KC, kUpClaimNB, W8, kUpClaimWaves, true>(kXGrid, lds12, x, idx, ex, M,
+                                                                   H, I, E, k, act, st);
+    else                                                 // eight claiming wavefronts
+        launch_up_gemv_wv<KC, kUpGemvNB, W8, 8, true>(kXGrid, up_gemv_lds_bytes(M, H, KC, W8, 8),
+                                                      x, idx, ex, M, H, I, E, k, act, st);
 }
 template <bool W8>
 static void launch_up_gemv_kc(const uint16_t *x, const int *idx, const Experts &ex, int M,
@@ -892,11 +931,11 @@ static hipError_t set_lds_attributes()
 {
     hipError_t e = hipSuccess;
     auto chk = [&](hipError_t r) { if (r != hipSuccess) e = r; };
-#define MV_UP_ATTR(KC) chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false, 4>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, true, 4>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB3, true, 4>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false, 8>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, true, 8>));
+#define MV_UP_ATTR(KC) chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false, 4, false>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, false, kUpClaimWaves, true>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, true, kUpClaimWaves, true>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false, 8, true>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, true, 8, true>));
     MV_UP_ATTR(1) MV_UP_ATTR(2) MV_UP_ATTR(3) MV_UP_ATTR(4) MV_UP_ATTR(5)
 #undef MV_UP_ATTR
 #define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, kDnMfmaNB>)); \
