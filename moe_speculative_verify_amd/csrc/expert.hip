@@ -328,19 +328,16 @@ __global__ __launch_bounds__(kXThreads) void expert_down_kernel(
 // with distinct experts per token a column block holds about one pair. The
 // weights therefore stream straight into registers -- one 1 KB load per row
 // per K block (lane i takes 16-byte chunk i), an NB-deep register ring, so
-// (NB - 1) blocks of every wavefront are in flight while one is consumed --
+// NB - 1 blocks of every wavefront are in flight while one is consumed --
 // and every pair's activation row sits in LDS, staged once per workgroup with
 // direct-to-LDS loads. Nothing but the weights is read inside the loop, so
 // the loop waits on one constant count. Per (pair, K block) every lane forms
 // R eight-element dot products (v_dot2_f32_bf16) and each row is summed over
 // the wavefront in a fixed DPP tree; the block sums are added over K blocks
 // in order in the combine. Workgroup b owns rows r0 .. r0+R-1 of every
-// expert; its wavefronts split the column blocks (v = wave, wave+4, ...).
+// expert; its wavefronts claim the (column block, K block) blocks one at a
+// time from an LDS counter.
 constexpr int kDnKB = 512;                       // K elements per block
-// four wavefronts, each with the whole ring of its column blocks (eight, two
-// per SIMD, were measured slower: fewer blocks per wavefront, M=1 +6 us)
-constexpr int kDnWaves = 4;
-constexpr int kDnThreads = kDnWaves * kWave;
 constexpr int kDnCh = kDnKB / 8;                 // 16-byte chunks per row per block
 
 // Sum over the wavefront in a fixed order, returned uniform: the 16-lane row
@@ -385,8 +382,8 @@ __host__ __device__ inline size_t down_gemv_lds_bytes(int R, int NP, int I, bool
 // 1024 columns, each chunk widened to two bf16 chunks that meet two
 // activation chunks; the row's scale is one more per-lane load of the block
 // and multiplies the reduced sum.
-template <int R, int NB, bool W8>
-__global__ __launch_bounds__(kDnThreads) void expert_down_gemv_kernel(
+template <int R, int NB, bool W8, int WV>
+__global__ __launch_bounds__(WV * kWave) void expert_down_gemv_kernel(
     const u32x4 *__restrict__ act, const int *__restrict__ topk_idx,
     const float *__restrict__ topk_w, const u32x4 *__restrict__ wd,
     const u32x4 *__restrict__ wds, const float *__restrict__ sd, int M, int H, int I,
@@ -396,7 +393,6 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_gemv_kernel(
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ Groups g;
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = uniform(threadIdx.x / kWave);
     const int nch = I / 8;                               // bf16 activation chunks (K = I)
     const int nwc = W8 ? I / 16 : nch;                   // weight chunks per row
     const int nkb = down_gemv_nkb(I, W8);
@@ -412,8 +408,11 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_gemv_kernel(
     // buckets; then the ring's first weight blocks and every pair's
     // activation row into LDS (direct-to-LDS), so the weights lead the
     // memory queue
+    __shared__ int s_next;                               // the workgroup's next block to claim
     const float pw = (int)threadIdx.x < NP ? topk_w[threadIdx.x] : 0.0f;
     groups_set_pairs(pair_expert(topk_idx, threadIdx.x, NP, NPT, E), NPT, E + ns, g);
+    if (threadIdx.x == 0)
+        s_next = 0;
     wait_vmcnt<0>();                                     // only the pair id and weight are in flight
     if ((int)threadIdx.x < NP)
         s_tw[threadIdx.x] = pw;
@@ -423,18 +422,27 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_gemv_kernel(
     }
     groups_finish(NPT, g);
 
-    const int DV = uniform(g.DV);
-    const int nv = DV > wave ? (DV - wave + kDnWaves - 1) / kDnWaves : 0;
-    const int nblk = nv * nkb;                           // this wavefront's blocks
+    // Blocks B = v * nkb + kb (column block v, K block kb), claimed one at a
+    // time by the workgroup's wavefronts from an LDS counter (a SIMD serves
+    // its older wavefront first; the claims let that one take more blocks);
+    // -1 past the last.
+    const int nblk = uniform(g.DV) * nkb;
+    auto next_block = [&]() {                            // uniform
+        int j = 0;
+        if (lane == 0)
+            j = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        j = uniform(__builtin_amdgcn_readlane(j, 0));
+        return j < nblk ? j : -1;
+    };
 
-    // Block X = (column block v, K block kb): lane i loads chunk i of the
-    // block for each of the R rows. Past the end of the sequence the same
-    // number of loads rereads the first kilobyte of W_down (cached), so every
-    // wait is one constant; the choice is an index select, one base pointer.
-    auto issue = [&](int X, u32x4 (&dst)[R], float &sdv) {
-        const bool real = X < nblk;
-        const int Xr = real ? X : 0;
-        const int v = wave + kDnWaves * (Xr / nkb), kb = Xr % nkb;
+    // Block B: lane i loads chunk i of the block for each of the R rows. A -1
+    // block rereads the first kilobyte of W_down (cached) with the same
+    // number of loads, so every wait is one constant; the choice is an index
+    // select, one base pointer.
+    auto issue = [&](int B, u32x4 (&dst)[R], float &sdv) {
+        const bool real = B >= 0;
+        const int Br = real ? B : 0;
+        const int v = Br / nkb, kb = Br % nkb;
         const int ev = uniform(g.vexp[min(v, kMaxNP - 1)]);
         const bool sh = real && ev >= E;                 // the shared expert's slab
         const size_t ebase = real && !sh ? (size_t)ev * H : 0;   // first row of the slab
@@ -458,8 +466,8 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_gemv_kernel(
             sdv = sd[ebase + si];
         }
     };
-    auto consume = [&](int X, u32x4 (&wr)[R], float sdv) {
-        const int v = wave + kDnWaves * (X / nkb), kb = X % nkb;
+    auto consume = [&](int B, u32x4 (&wr)[R], float sdv) {
+        const int v = B / nkb, kb = B % nkb;
         const int npair = uniform(g.vcnt[v]);
         const int pb = uniform(g.vbeg[v]);
         if (kb * kDnCh + kDnCh > nwc) {                  // uniform: the K tail block
@@ -497,19 +505,27 @@ __global__ __launch_bounds__(kDnThreads) void expert_down_gemv_kernel(
 
     u32x4 w[NB][R];
     float sdr[NB] = {};                                  // fp8 row scales (unused for bf16)
+    int tb[NB];                                          // blocks of the ring
 #pragma unroll
-    for (int q = 0; q < NB - 1; ++q)
-        issue(q, w[q], sdr[q]);
+    for (int q = 0; q < NB - 1; ++q) {
+        tb[q] = next_block();
+        issue(tb[q], w[q], sdr[q]);
+    }
     stage_rows_lds(act, NPT, nch, s_act, xs);
     wait_vmcnt<0>();                                     // this wave's staging has landed
     lds_barrier();                                       // ... and every other wave's staging
-    for (int X0 = 0; X0 < nblk; X0 += NB) {
+    for (bool live = true; live;) {
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
-            issue(X0 + q + NB - 1, w[(q + NB - 1) % NB], sdr[(q + NB - 1) % NB]);
-            wait_vmcnt<(NB - 1) * kLoads>();             // block X0 + q has landed
-            if (X0 + q < nblk)
-                consume(X0 + q, w[q], sdr[q]);
+            const int nq = (q + NB - 1) % NB;
+            tb[nq] = next_block();
+            issue(tb[nq], w[nq], sdr[nq]);
+            wait_vmcnt<(NB - 1) * kLoads>();             // block q has landed
+            if (tb[q] < 0) {                             // uniform: nothing left
+                live = false;
+                break;
+            }
+            consume(tb[q], w[q], sdr[q]);
         }
     }
     wait_vmcnt<0>();                                     // dummy loads have landed
@@ -867,10 +883,16 @@ static int down_rows(int H)
             return r;
     return 0;
 }
-// register ring depth of the GEMV down kernel: one block (R 16-byte loads
-// per lane) in flight while the wavefront consumes the one before (three
-// ahead: M=6 45.9 us, M=1 15.7; one ahead: 44.3 and 13.6)
-constexpr int kDnGemvNB = 2;
+// GEMV down kernel: eight claiming wavefronts per CU (twelve for fp8), each
+// waiting for the block it just issued (no block ahead: more wavefronts keep
+// the CU's loads flowing, and during the activation staging eight or twelve
+// blocks per CU are in flight instead of four). Against four wavefronts one
+// block ahead: M=6 42.6 against 44.8 us, M=1 13.0 against 15.2, fp8 M=6 26.0
+// against 28.9, fp8 M=1 10.3 against 11.9 (three blocks ahead on four
+// wavefronts: M=6 45.9, M=1 15.7).
+constexpr int kDnGemvNB = 1;
+constexpr int kDnGemvWaves = 8;
+constexpr int kDnGemvWaves8 = 12;
 // the GEMV down kernel runs when every pair's activation row fits in LDS
 // (NPT pairs: M*k routed, plus M with a shared expert)
 static bool down_gemv_fits(int R, int NPT, int I, bool w8)
@@ -939,8 +961,8 @@ static hipError_t set_lds_attributes()
     MV_UP_ATTR(1) MV_UP_ATTR(2) MV_UP_ATTR(3) MV_UP_ATTR(4) MV_UP_ATTR(5)
 #undef MV_UP_ATTR
 #define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, kDnMfmaNB>)); \
-    chk(allow_lds(expert_down_gemv_kernel<R, kDnGemvNB, false>)); \
-    chk(allow_lds(expert_down_gemv_kernel<R, kDnGemvNB, true>));
+    chk(allow_lds(expert_down_gemv_kernel<R, kDnGemvNB, false, kDnGemvWaves>)); \
+    chk(allow_lds(expert_down_gemv_kernel<R, kDnGemvNB, true, kDnGemvWaves8>));
     MV_DOWN_ATTR(4) MV_DOWN_ATTR(8) MV_DOWN_ATTR(10) MV_DOWN_ATTR(12) MV_DOWN_ATTR(16)
 #undef MV_DOWN_ATTR
     return e;
@@ -954,15 +976,15 @@ static void launch_down_gemv(const uint16_t *act, const int *idx, const float *t
     const int grid = (H + R - 1) / R;
     const size_t lds = down_gemv_lds_bytes(R, M * k + ex.ns * M, I, ex.w8);
     if (ex.w8)
-        hipLaunchKernelGGL((expert_down_gemv_kernel<R, kDnGemvNB, true>), dim3(grid),
-                           dim3(kDnThreads), lds, st, (const u32x4 *)act, idx, tw,
-                           (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, ex.sd, M, H, I, E, k,
-                           ex.ns, out);
+        hipLaunchKernelGGL((expert_down_gemv_kernel<R, kDnGemvNB, true, kDnGemvWaves8>),
+                           dim3(grid), dim3(kDnGemvWaves8 * kWave), lds, st, (const u32x4 *)act,
+                           idx, tw, (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, ex.sd, M, H, I,
+                           E, k, ex.ns, out);
     else
-        hipLaunchKernelGGL((expert_down_gemv_kernel<R, kDnGemvNB, false>), dim3(grid),
-                           dim3(kDnThreads), lds, st, (const u32x4 *)act, idx, tw,
-                           (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, nullptr, M, H, I, E, k,
-                           ex.ns, out);
+        hipLaunchKernelGGL((expert_down_gemv_kernel<R, kDnGemvNB, false, kDnGemvWaves>),
+                           dim3(grid), dim3(kDnGemvWaves * kWave), lds, st, (const u32x4 *)act,
+                           idx, tw, (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, nullptr, M, H, I,
+                           E, k, ex.ns, out);
 }
 
 template <int R>
