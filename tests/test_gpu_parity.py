@@ -331,8 +331,12 @@ def _compare_lm(am, ml, h, wl_bits, ref):
     assert_close(ml, ref["zmax"], "max_logit")
 
 
+# (6, 2560, 30272): 1892 tiles, so 156 workgroups hold 3 leftover tiles whose
+# 30 K blocks are split across their four wavefronts, ranges spanning two
+# tiles; (4, 1024, 22560): 1410 tiles, 2 or 1 leftover tiles of 4 K blocks
 @pytest.mark.parametrize("M,H,V", [(1, 256, 1000), (3, 264, 777), (16, 256, 4099),
-                                   (6, 2560, 65), (2, 8, 1)])
+                                   (6, 2560, 65), (2, 8, 1), (6, 2560, 30272),
+                                   (4, 1024, 22560)])
 def test_lmhead_matches_oracle(M, H, V):
     say("lmhead", M, H, V)
     h = synth.activations(M, H, seed=500 + V)
