@@ -331,9 +331,9 @@ def _compare_lm(am, ml, h, wl_bits, ref):
     assert_close(ml, ref["zmax"], "max_logit")
 
 
-# (6, 2560, 30272): 1892 tiles, so 156 workgroups hold 3 leftover tiles whose
-# 30 K blocks are split across their four wavefronts, ranges spanning two
-# tiles; (4, 1024, 22560): 1410 tiles, 2 or 1 leftover tiles of 4 K blocks
+# (6, 2560, 30272): 1892 tiles of 16 rows over 256 workgroups, 8 or 7 per
+# workgroup (wavefronts with 2 or 1 tiles); (4, 1024, 22560): 1410 tiles, 6
+# or 5 per workgroup
 @pytest.mark.parametrize("M,H,V", [(1, 256, 1000), (3, 264, 777), (16, 256, 4099),
                                    (6, 2560, 65), (2, 8, 1), (6, 2560, 30272),
                                    (4, 1024, 22560)])
