@@ -197,15 +197,16 @@ __device__ __forceinline__ int pair_expert(const int *__restrict__ topk_idx, int
 
 
 // ----------------------------------------------------------------- down
-// Workgroup b owns R output rows r0 .. r0+R-1 for every expert; its
-// wavefronts split the column blocks (v = wave, wave+4, ...) and stream
-// the R rows of W_down[e] (1 KB per row per block, NB-deep ring). The B
-// fragments (the pairs' activations, L2-resident) are loaded at the start
-// of their block, ahead of the next weight block. Per-pair results y land in LDS and the
-// workgroup finishes with the weighted combine over slots in order, so no
-// other kernel and no cross-workgroup traffic is needed.
-template <int R, int NB>
-__global__ __launch_bounds__(kXThreads) void expert_down_kernel(
+// Workgroup b owns R output rows r0 .. r0+R-1 for every expert; its WV
+// wavefronts claim the column blocks one at a time from an LDS counter and
+// stream the R rows of W_down[e] of each (1 KB per row per K block) through
+// an NB-slot direct-to-LDS ring. The B fragments (the pairs' activations,
+// L2-resident) are loaded at the start of their block, ahead of the next
+// weight block. Per-pair results y land in LDS and the workgroup finishes
+// with the weighted combine over slots in order, so no other kernel and no
+// cross-workgroup traffic is needed.
+template <int R, int NB, int WV>
+__global__ __launch_bounds__(WV * kWave) void expert_down_kernel(
     const u32x4 *__restrict__ act, const int *__restrict__ topk_idx,
     const float *__restrict__ topk_w, const u32x4 *__restrict__ wd,
     const u32x4 *__restrict__ wds, int M, int H, int I, int E, int k, int ns,
@@ -214,6 +215,7 @@ __global__ __launch_bounds__(kXThreads) void expert_down_kernel(
     constexpr int kBlk = R * kXRowPitch;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ Groups g;
+    __shared__ int s_next;                               // the workgroup's next column block
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     const int nch = I / 8;                               // K = I here
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(kXThreads) void expert_down_kernel(
     const int r0 = blockIdx.x * R;
     const int nr = min(R, H - r0);
     unsigned char *ring = smem + wave * NB * kBlk;
-    float *y_s = (float *)(smem + kXWaves * NB * kBlk);  // [NPT][R]
+    float *y_s = (float *)(smem + WV * NB * kBlk);       // [NPT][R]
     const int NP = M * k, NPT = NP + ns * M;
     float *s_tw = y_s + NPT * R;                         // [NP] routing weights
 
@@ -231,26 +233,43 @@ __global__ __launch_bounds__(kXThreads) void expert_down_kernel(
         groups_set_pairs(id, NPT, E + ns, g);
         if ((int)threadIdx.x < NP)
             s_tw[threadIdx.x] = pw;
-        groups_finish(NPT, g);
+        if (threadIdx.x == 0)
+            s_next = 0;
+        groups_finish(NPT, g);                           // (its barriers also publish s_next)
     }
 
     const int DV = uniform(g.DV);
-    const int nv = DV > wave ? (DV - wave + kXWaves - 1) / kXWaves : 0;
-    const int nblk = nv * nkb;                           // this wavefront's blocks
     const int j = lane & 15, gq = lane >> 4;
     const bool row_ok = j < nr;
+    // Tag of a block: column block v * 16 + K block kb, or -1 past the end;
+    // a column block's K blocks stay on the wavefront that claimed it
+    auto claim = [&]() {                                 // uniform: a column block, or -1
+        int c = 0;
+        if (lane == 0)
+            c = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        c = uniform(__builtin_amdgcn_readlane(c, 0));
+        return c < DV ? c : -1;
+    };
+    int cur_v = claim(), cur_kb = 0;                     // the next block to issue
+    auto next_tag = [&]() {
+        int t = -1;
+        if (cur_v >= 0) {
+            t = cur_v * 16 + cur_kb;
+            if (++cur_kb == nkb) {
+                cur_kb = 0;
+                cur_v = claim();
+            }
+        }
+        return t;
+    };
 
-    // Block X = (column block v, K block kb): R rows of W_down[e], 1 KB per
-    // row, into ring slot X % NB, issued NB-1 blocks ahead. Past the end of
-    // the sequence the same number of loads reads a cached dummy (act,
-    // clamped) into a slot nobody reads: every iteration then has the same
-    // loads in flight and waits on one constant count.
+    // Block of a tag: R rows of W_down[e], 1 KB per row, into a ring slot. A
+    // -1 tag loads a cached dummy (act, clamped) with the same number of
+    // loads, so every wait is one constant count.
     const u32x4 *dummy = act + min(lane, NPT * nch - 1);
-    auto issue = [&](int X) {
-        const bool real = X < nblk;
-        const int Xr = real ? X : 0;
-        const int v = wave + kXWaves * (Xr / nkb), kb = Xr % nkb;
-        unsigned char *slot = ring + (X % NB) * kBlk;
+    auto issue = [&](int tag, unsigned char *slot) {
+        const bool real = tag >= 0;
+        const int v = real ? tag >> 4 : 0, kb = real ? tag & 15 : 0;
         const int ev = uniform(g.vexp[min(v, kMaxNP - 1)]);
         const u32x4 *base = ev >= E ? wds : wd + (size_t)ev * H * nch;
         int c = kb * (kXKB / 8) + lane;
@@ -262,47 +281,71 @@ __global__ __launch_bounds__(kXThreads) void expert_down_kernel(
         }
     };
 
+    // tg[q]: the tag of ring slot q. With NB > 1 the block NB - 1 ahead is
+    // issued before the current one is consumed; with NB = 1 each block is
+    // issued right behind its B fragments and waited for at once.
+    int tg[NB];
 #pragma unroll
-    for (int q = 0; q < NB - 1; ++q)
-        issue(q);
+    for (int q = 0; q < NB - 1; ++q) {
+        tg[q] = next_tag();
+        issue(tg[q], ring + q * kBlk);
+    }
+    if constexpr (NB == 1)
+        tg[0] = next_tag();
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int X = 0; X < nblk; ++X) {
-        const int v = wave + kXWaves * (X / nkb), kb = X % nkb;
-        const int npair = uniform(g.vcnt[v]);
-        const bool col_ok = j < npair;
-        // B fragments of block X (pair j's activation chunks for K group
-        // gq, L2-resident), issued before the next weight block so that one
-        // wait covers both them and block X's weights (loads retire in order)
-        const int p = g.sorted[uniform(g.vbeg[v]) + (col_ok ? j : 0)];
-        u32x4 bf[kXSteps];
+    for (bool live = true; live;) {
 #pragma unroll
-        for (int s = 0; s < kXSteps; ++s) {
-            const int c = min(kb * (kXKB / 8) + 4 * s + gq, nch - 1);
-            bf[s] = act[(size_t)p * nch + c];
-        }
-        issue(X + NB - 1);
-        // block X's B loads (and everything older, block X's weights among
-        // them) have landed; the newest weight block stays in flight
-        wait_vmcnt<R>();
-        const unsigned char *slot = ring + (X % NB) * kBlk + (row_ok ? j : 0) * kXRowPitch + gq * 16;
-#pragma unroll
-        for (int s = 0; s < kXSteps; ++s) {
-            u32x4 a = *(const MV_LDS u32x4 *)(slot + s * 64);
-            if (!row_ok)
-                a = u32x4{0, 0, 0, 0};
-            u32x4 bv = bf[s];
-            if (!col_ok || kb * (kXKB / 8) + 4 * s + gq >= nch)
-                bv = u32x4{0, 0, 0, 0};
-            acc = mfma_bf16(a, bv, acc);
-        }
-        if (kb == nkb - 1) {
-            if (col_ok) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (4 * gq + r < nr)
-                        y_s[p * R + 4 * gq + r] = acc[r];
+        for (int q = 0; q < NB; ++q) {
+            if (tg[q] < 0) {                             // uniform: nothing left
+                live = false;
+                break;
             }
-            acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const int v = tg[q] >> 4, kb = tg[q] & 15;
+            const int npair = uniform(g.vcnt[v]);
+            const bool col_ok = j < npair;
+            // B fragments of this block (pair j's activation chunks for K
+            // group gq, L2-resident), issued before the next weight block so
+            // that one wait covers both them and this block's weights (loads
+            // retire in order)
+            const int p = g.sorted[uniform(g.vbeg[v]) + (col_ok ? j : 0)];
+            u32x4 bf[kXSteps];
+#pragma unroll
+            for (int s = 0; s < kXSteps; ++s) {
+                const int c = min(kb * (kXKB / 8) + 4 * s + gq, nch - 1);
+                bf[s] = act[(size_t)p * nch + c];
+            }
+            const int nq = (q + NB - 1) % NB;
+            if constexpr (NB > 1) {
+                tg[nq] = next_tag();
+                issue(tg[nq], ring + nq * kBlk);
+            } else {
+                issue(tg[0], ring);
+            }
+            // this block's B loads and weights (and everything older) have
+            // landed; the newest weight block stays in flight
+            wait_vmcnt<(NB - 1) * R>();
+            const unsigned char *slot = ring + q * kBlk + (row_ok ? j : 0) * kXRowPitch + gq * 16;
+#pragma unroll
+            for (int s = 0; s < kXSteps; ++s) {
+                u32x4 a = *(const MV_LDS u32x4 *)(slot + s * 64);
+                if (!row_ok)
+                    a = u32x4{0, 0, 0, 0};
+                u32x4 bv = bf[s];
+                if (!col_ok || kb * (kXKB / 8) + 4 * s + gq >= nch)
+                    bv = u32x4{0, 0, 0, 0};
+                acc = mfma_bf16(a, bv, acc);
+            }
+            if (kb == nkb - 1) {
+                if (col_ok) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * gq + r < nr)
+                            y_s[p * R + 4 * gq + r] = acc[r];
+                }
+                acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+            if constexpr (NB == 1)
+                tg[0] = next_tag();
         }
     }
     wait_vmcnt<0>();                                     // dummy loads have landed
@@ -817,7 +860,7 @@ static int up_gemv_kc(int H, bool w8)
 }
 static bool up_gemv_fits(int M, int H, bool w8)
 {
-    return up_gemv_lds_bytes(M, H, up_gemv_kc(H, w8), w8, 8) <= (size_t)kXLdsDynMax;
+    return up_gemv_lds_bytes(M, H, up_gemv_kc(H, w8), w8, kUpClaimWaves) <= (size_t)kXLdsDynMax;
 }
 
 // The experts of one call: routed weights and, when ns = 1, the shared
@@ -848,17 +891,15 @@ template <int KC, bool W8>
 static void launch_up_gemv(const uint16_t *x, const int *idx, const Experts &ex, int M, int H,
                            int I, int E, int k, uint16_t *act, hipStream_t st)
 {
-    const size_t lds4 = up_gemv_lds_bytes(M, H, KC, W8, 4);
-    const size_t lds12 = up_gemv_lds_bytes(M, H, KC, W8, kUpClaimWaves);
-    if (!W8 && M == 1 && lds4 + 10 * 1024 <= 80 * 1024)
-        launch_up_gemv_wv<KC, kUpGemvNB, false, 4, false>(2 * kXGrid, lds4, x, idx, ex, M, H, I,
-                                                          E, k, act, st);
-    else if (lds12 <= (size_t)kXLdsDynMax)
-        launch_up_gemv_wv<KC, kUpClaimNB, W8, kUpClaimWaves, true>(kXGrid, lds12, x, idx, ex, M,
-                                                                   H, I, E, k, act, st);
-    else                                                 // eight claiming wavefronts
-        launch_up_gemv_wv<KC, kUpGemvNB, W8, 8, true>(kXGrid, up_gemv_lds_bytes(M, H, KC, W8, 8),
-                                                      x, idx, ex, M, H, I, E, k, act, st);
+    // (the supported shapes always fit: up_gemv_fits; one token's two
+    // workgroups per CU hold less than the twelve-wavefront one)
+    if (!W8 && M == 1)
+        launch_up_gemv_wv<KC, kUpGemvNB, false, 4, false>(
+            2 * kXGrid, up_gemv_lds_bytes(M, H, KC, W8, 4), x, idx, ex, M, H, I, E, k, act, st);
+    else
+        launch_up_gemv_wv<KC, kUpClaimNB, W8, kUpClaimWaves, true>(
+            kXGrid, up_gemv_lds_bytes(M, H, KC, W8, kUpClaimWaves), x, idx, ex, M, H, I, E, k,
+            act, st);
 }
 template <bool W8>
 static void launch_up_gemv_kc(const uint16_t *x, const int *idx, const Experts &ex, int M,
@@ -899,17 +940,21 @@ static bool down_gemv_fits(int R, int NPT, int I, bool w8)
 {
     return down_gemv_lds_bytes(R, NPT, I, w8) <= (size_t)kXLdsDynMax;
 }
-static size_t down_lds_bytes(int R, int NB, int NPT)
+static size_t down_lds_bytes(int R, int NB, int WV, int NPT)
 {
     // the weight rings, the pairs' sums [NPT][R], the routing weights [NPT]
-    return (size_t)kXWaves * NB * R * kXRowPitch + (size_t)NPT * (R + 1) * sizeof(float);
+    return (size_t)WV * NB * R * kXRowPitch + (size_t)NPT * (R + 1) * sizeof(float);
 }
-// LDS ring of the MFMA down kernel: one block in flight while the one before
-// is consumed (a third slot measured no faster: M=16 107.0 against 105.9 us)
-constexpr int kDnMfmaNB = 2;
+// MFMA down kernel: eight claiming wavefronts, each issuing its block right
+// behind the block's B fragments and waiting for both (one LDS slot each).
+// Against four wavefronts with two slots: M=16 98.8 against 118.7 us, with
+// Zipf-skewed routing 70.7 against 83.6 (twelve wavefronts: 98.1 and 69.5,
+// but their slots do not fit at R = 16).
+constexpr int kDnMfmaNB = 1;
+constexpr int kDnMfmaWaves = 8;
 static bool down_mfma_fits(int R, int NPT)
 {
-    return down_lds_bytes(R, kDnMfmaNB, NPT) <= (size_t)kXLdsDynMax;
+    return down_lds_bytes(R, kDnMfmaNB, kDnMfmaWaves, NPT) <= (size_t)kXLdsDynMax;
 }
 
 // Workspace: the header, then the bf16 activations of M*(k+1) pairs (room
@@ -955,12 +1000,10 @@ static hipError_t set_lds_attributes()
     auto chk = [&](hipError_t r) { if (r != hipSuccess) e = r; };
 #define MV_UP_ATTR(KC) chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false, 4, false>)); \
     chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, false, kUpClaimWaves, true>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, true, kUpClaimWaves, true>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false, 8, true>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, true, 8, true>));
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, true, kUpClaimWaves, true>));
     MV_UP_ATTR(1) MV_UP_ATTR(2) MV_UP_ATTR(3) MV_UP_ATTR(4) MV_UP_ATTR(5)
 #undef MV_UP_ATTR
-#define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, kDnMfmaNB>)); \
+#define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, kDnMfmaNB, kDnMfmaWaves>)); \
     chk(allow_lds(expert_down_gemv_kernel<R, kDnGemvNB, false, kDnGemvWaves>)); \
     chk(allow_lds(expert_down_gemv_kernel<R, kDnGemvNB, true, kDnGemvWaves8>));
     MV_DOWN_ATTR(4) MV_DOWN_ATTR(8) MV_DOWN_ATTR(10) MV_DOWN_ATTR(12) MV_DOWN_ATTR(16)
@@ -993,8 +1036,9 @@ static void launch_down_r(const uint16_t *act, const int *idx, const float *tw,
                           hipStream_t st)
 {
     const int grid = (H + R - 1) / R;
-    const size_t lds = down_lds_bytes(R, kDnMfmaNB, M * k + ex.ns * M);
-    hipLaunchKernelGGL((expert_down_kernel<R, kDnMfmaNB>), dim3(grid), dim3(kXThreads), lds, st,
+    const size_t lds = down_lds_bytes(R, kDnMfmaNB, kDnMfmaWaves, M * k + ex.ns * M);
+    hipLaunchKernelGGL((expert_down_kernel<R, kDnMfmaNB, kDnMfmaWaves>), dim3(grid),
+                       dim3(kDnMfmaWaves * kWave), lds, st,
                        (const u32x4 *)act, idx, tw, (const u32x4 *)ex.wd,
                        (const u32x4 *)ex.wds, M, H, I, E, k, ex.ns, out);
 }
