@@ -404,54 +404,50 @@ __device__ __forceinline__ float wave_total(float v)
 }
 
 // K blocks of a W_down row: kDnCh 16-byte chunks, 512 bf16 or 1024 fp8
-// columns; the activations sit in LDS as bf16 rows padded to whole blocks
+// columns
 __host__ __device__ inline int down_gemv_nkb(int I, bool w8)
 {
     const int nwc = w8 ? I / 16 : I / 8;
     return (nwc + kDnCh - 1) / kDnCh;
 }
-__host__ __device__ inline size_t down_gemv_act_bytes(int NP, int I, bool w8)
+// LDS: the block sums [NPT][nkb][R], then the NP routing weights
+__host__ __device__ inline size_t down_gemv_lds_bytes(int R, int NPT, int I, bool w8)
 {
-    return align_up((size_t)NP * down_gemv_nkb(I, w8) * kDnCh * (w8 ? 2 : 1) * 16, 256);
+    return (size_t)NPT * (down_gemv_nkb(I, w8) * R + 1) * sizeof(float);
 }
-__host__ __device__ inline size_t down_gemv_lds_bytes(int R, int NP, int I, bool w8)
-{
-    // activations, then the block sums [NP][nkb][R], then NP routing weights
-    return down_gemv_act_bytes(NP, I, w8) +
-           (size_t)NP * (down_gemv_nkb(I, w8) * R + 1) * sizeof(float);
-}
+// activation chunks of the first kDnPre pairs of a column block are loaded
+// together with the block's weights; further pairs (rare at these widths)
+// are loaded when they are reached
+constexpr int kDnPre = 2;
+static_assert(kDnPre == 2, "the pair select in the GEMV down kernel takes two");
 
 // W8: fp8 W_down (E4M3 codes, an fp32 scale per row in sd): a block is
 // 1024 columns, each chunk widened to two bf16 chunks that meet two
 // activation chunks; the row's scale is one more per-lane load of the block
 // and multiplies the reduced sum.
-template <int R, int NB, bool W8, int WV>
+template <int R, bool W8, int WV>
 __global__ __launch_bounds__(WV * kWave) void expert_down_gemv_kernel(
     const u32x4 *__restrict__ act, const int *__restrict__ topk_idx,
     const float *__restrict__ topk_w, const u32x4 *__restrict__ wd,
     const u32x4 *__restrict__ wds, const float *__restrict__ sd, int M, int H, int I,
     int E, int k, int ns, float *__restrict__ out)
 {
-    constexpr int kLoads = R + (W8 ? 1 : 0);             // loads per block
+    constexpr int kAc = W8 ? 2 : 1;                      // activation chunks per lane per pair
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ Groups g;
+    __shared__ int s_next;                               // the workgroup's next block to claim
     const int lane = threadIdx.x & (kWave - 1);
     const int nch = I / 8;                               // bf16 activation chunks (K = I)
     const int nwc = W8 ? I / 16 : nch;                   // weight chunks per row
     const int nkb = down_gemv_nkb(I, W8);
-    const int xs = nkb * kDnCh * (W8 ? 2 : 1);           // LDS activation row, chunks
     const int NP = M * k, NPT = NP + ns * M;
     const int r0 = blockIdx.x * R;
     const int nr = min(R, H - r0);
-    u32x4 *s_act = (u32x4 *)smem;                        // [NPT][xs]
-    float *s_y = (float *)(smem + down_gemv_act_bytes(NPT, I, W8));  // [NPT][nkb][R]
+    float *s_y = (float *)smem;                          // [NPT][nkb][R]
     float *s_tw = s_y + NPT * nkb * R;                   // [NP] routing weights
 
     // prologue: pair ids, routing weights (for the combine at the end) and
-    // buckets; then the ring's first weight blocks and every pair's
-    // activation row into LDS (direct-to-LDS), so the weights lead the
-    // memory queue
-    __shared__ int s_next;                               // the workgroup's next block to claim
+    // buckets
     const float pw = (int)threadIdx.x < NP ? topk_w[threadIdx.x] : 0.0f;
     groups_set_pairs(pair_expert(topk_idx, threadIdx.x, NP, NPT, E), NPT, E + ns, g);
     if (threadIdx.x == 0)
@@ -459,11 +455,7 @@ __global__ __launch_bounds__(WV * kWave) void expert_down_gemv_kernel(
     wait_vmcnt<0>();                                     // only the pair id and weight are in flight
     if ((int)threadIdx.x < NP)
         s_tw[threadIdx.x] = pw;
-    for (int i = threadIdx.x; i < NPT * (xs - nch); i += blockDim.x) {
-        const int p = i / (xs - nch), c = nch + i % (xs - nch);
-        s_act[p * xs + c] = u32x4{0, 0, 0, 0};           // K padding reads as zero
-    }
-    groups_finish(NPT, g);
+    groups_finish(NPT, g);                               // (its barriers also publish s_next)
 
     // Blocks B = v * nkb + kb (column block v, K block kb), claimed one at a
     // time by the workgroup's wavefronts from an LDS counter (a SIMD serves
@@ -477,101 +469,86 @@ __global__ __launch_bounds__(WV * kWave) void expert_down_gemv_kernel(
         j = uniform(__builtin_amdgcn_readlane(j, 0));
         return j < nblk ? j : -1;
     };
-
-    // Block B: lane i loads chunk i of the block for each of the R rows. A -1
-    // block rereads the first kilobyte of W_down (cached) with the same
-    // number of loads, so every wait is one constant; the choice is an index
-    // select, one base pointer.
-    auto issue = [&](int B, u32x4 (&dst)[R], float &sdv) {
-        const bool real = B >= 0;
-        const int Br = real ? B : 0;
-        const int v = Br / nkb, kb = Br % nkb;
-        const int ev = uniform(g.vexp[min(v, kMaxNP - 1)]);
-        const bool sh = real && ev >= E;                 // the shared expert's slab
-        const size_t ebase = real && !sh ? (size_t)ev * H : 0;   // first row of the slab
-        // the shared slab's rows are reached through off below; dummy blocks
-        // read wd itself (this form of the select also keeps the captured
-        // pointers out of scratch)
-        const u32x4 *bp = sh ? wds : wd + ebase * nwc;
-        int c = kb * kDnCh + lane;
-        c = c < nwc ? c : nwc - 1;                       // K tail: zeroed before use
-        const int cd = min(lane, nwc - 1);
+    // this lane's activation chunks of pair p in K block kb (clamped in the
+    // K tail, zeroed before use)
+    auto load_act = [&](int p, int kb, u32x4 (&a)[kAc]) {
+        const int c = min(kAc * (kb * kDnCh + lane), nch - kAc);
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int row = min(r0 + r, H - 1);          // rows past H: unused
-            int off = real ? row * nwc + c : cd;
-            asm volatile("" : "+v"(off));                // one load on one path: no branch
-            dst[r] = load_stream(bp + off);
-        }
-        if constexpr (W8) {                              // lane r < R: row r's scale
-            int si = real ? (int)min(r0 + min(lane, R - 1), H - 1) : 0;
-            asm volatile("" : "+v"(si));
-            sdv = sd[ebase + si];
-        }
+        for (int i = 0; i < kAc; ++i)
+            a[i] = act[(size_t)p * nch + c + i];
     };
-    auto consume = [&](int B, u32x4 (&wr)[R], float sdv) {
+
+    // Each block: lane i loads chunk i of the block for each of the R rows,
+    // and the activation chunks of the column block's first pairs (the
+    // pairs' rows sit in L2: every workgroup reads all of them), then waits
+    // for all of it and consumes the block.
+    for (;;) {
+        const int B = next_block();
+        if (B < 0)                                       // uniform
+            break;
         const int v = B / nkb, kb = B % nkb;
         const int npair = uniform(g.vcnt[v]);
         const int pb = uniform(g.vbeg[v]);
-        if (kb * kDnCh + kDnCh > nwc) {                  // uniform: the K tail block
-            const bool ok = kb * kDnCh + lane < nwc;
+        const int ev = uniform(g.vexp[v]);
+        const bool sh = ev >= E;                         // the shared expert's slab
+        const size_t ebase = sh ? 0 : (size_t)ev * H;    // first row of the slab
+        const u32x4 *bp = sh ? wds : wd + ebase * nwc;
+        int c = kb * kDnCh + lane;
+        c = c < nwc ? c : nwc - 1;                       // K tail: zeroed before use
+        u32x4 w[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = min(r0 + r, H - 1);          // rows past H: unused
+            w[r] = load_stream(bp + (size_t)row * nwc + c);
+        }
+        float sdv = 1.0f;
+        if constexpr (W8)                                // lane r < R: row r's scale
+            sdv = sd[ebase + min(r0 + min(lane, R - 1), H - 1)];
+        u32x4 ap[kDnPre][kAc];
+#pragma unroll
+        for (int q = 0; q < kDnPre; ++q)
+            load_act(uniform(g.sorted[pb + min(q, npair - 1)]), kb, ap[q]);
+        wait_vmcnt<0>();
+        const bool ok = kb * kDnCh + lane < nwc;         // the K tail
+        if (kb * kDnCh + kDnCh > nwc) {                  // uniform
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                wr[r] = ok ? wr[r] : u32x4{0, 0, 0, 0};
+                w[r] = ok ? w[r] : u32x4{0, 0, 0, 0};
         }
         for (int jj = 0; jj < npair; ++jj) {
             const int p = uniform(g.sorted[pb + jj]);
+            u32x4 a[kAc];
+            if (jj < kDnPre) {                           // uniform
+#pragma unroll
+                for (int i = 0; i < kAc; ++i)
+                    a[i] = jj == 0 ? ap[0][i] : ap[kDnPre - 1][i];
+            } else {
+                load_act(p, kb, a);
+            }
+#pragma unroll
+            for (int i = 0; i < kAc; ++i)
+                a[i] = ok ? a[i] : u32x4{0, 0, 0, 0};
             float yv = 0.0f;
             if constexpr (W8) {
-                const u32x4 *ar = s_act + p * xs + 2 * (kb * kDnCh + lane);
-                const u32x4 a0 = ar[0], a1 = ar[1];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    float d = dot8_bf16(e4m3x8_to_bf16(wr[r].x, wr[r].y), a0, 0.0f);
-                    d = dot8_bf16(e4m3x8_to_bf16(wr[r].z, wr[r].w), a1, d);
+                    float d = dot8_bf16(e4m3x8_to_bf16(w[r].x, w[r].y), a[0], 0.0f);
+                    d = dot8_bf16(e4m3x8_to_bf16(w[r].z, w[r].w), a[1], d);
                     const float t = wave_total(d);
                     yv = lane == r ? t : yv;
                 }
                 yv *= sdv;                               // lane r: row r's scale
             } else {
-                const u32x4 a = s_act[p * xs + kb * kDnCh + lane];
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const float t = wave_total(dot8_bf16(wr[r], a, 0.0f));
+                    const float t = wave_total(dot8_bf16(w[r], a[0], 0.0f));
                     yv = lane == r ? t : yv;
                 }
             }
             if (lane < nr)
                 s_y[(p * nkb + kb) * R + lane] = yv;
         }
-    };
-
-    u32x4 w[NB][R];
-    float sdr[NB] = {};                                  // fp8 row scales (unused for bf16)
-    int tb[NB];                                          // blocks of the ring
-#pragma unroll
-    for (int q = 0; q < NB - 1; ++q) {
-        tb[q] = next_block();
-        issue(tb[q], w[q], sdr[q]);
     }
-    stage_rows_lds(act, NPT, nch, s_act, xs);
-    wait_vmcnt<0>();                                     // this wave's staging has landed
-    lds_barrier();                                       // ... and every other wave's staging
-    for (bool live = true; live;) {
-#pragma unroll
-        for (int q = 0; q < NB; ++q) {
-            const int nq = (q + NB - 1) % NB;
-            tb[nq] = next_block();
-            issue(tb[nq], w[nq], sdr[nq]);
-            wait_vmcnt<(NB - 1) * kLoads>();             // block q has landed
-            if (tb[q] < 0) {                             // uniform: nothing left
-                live = false;
-                break;
-            }
-            consume(tb[q], w[q], sdr[q]);
-        }
-    }
-    wait_vmcnt<0>();                                     // dummy loads have landed
     __syncthreads();
 
     // weighted combine, slots in order, fp32; each pair's K blocks in order
@@ -926,19 +903,21 @@ static int down_rows(int H)
 }
 // GEMV down kernel: eight claiming wavefronts per CU (twelve for fp8), each
 // waiting for the block it just issued (no block ahead: more wavefronts keep
-// the CU's loads flowing, and during the activation staging eight or twelve
-// blocks per CU are in flight instead of four). Against four wavefronts one
-// block ahead: M=6 42.6 against 44.8 us, M=1 13.0 against 15.2, fp8 M=6 26.0
-// against 28.9, fp8 M=1 10.3 against 11.9 (three blocks ahead on four
-// wavefronts: M=6 45.9, M=1 15.7).
-constexpr int kDnGemvNB = 1;
+// the CU's loads flowing). Against four wavefronts one block ahead: M=6 42.6
+// against 44.8 us, M=1 13.0 against 15.2, fp8 M=6 26.0 against 28.9, fp8 M=1
+// 10.3 against 11.9 (three blocks ahead on four wavefronts: M=6 45.9, M=1
+// 15.7).
 constexpr int kDnGemvWaves = 8;
 constexpr int kDnGemvWaves8 = 12;
-// the GEMV down kernel runs when every pair's activation row fits in LDS
-// (NPT pairs: M*k routed, plus M with a shared expert)
+// The GEMV down kernel serves the widths whose pairs' activation rows would
+// fit in LDS (NPT pairs: M*k routed, plus M with a shared expert; M <= 9 at
+// I = 1024, k = 8), where a column block holds about one pair; wider bf16
+// calls take the MFMA kernel.
 static bool down_gemv_fits(int R, int NPT, int I, bool w8)
 {
-    return down_gemv_lds_bytes(R, NPT, I, w8) <= (size_t)kXLdsDynMax;
+    const size_t rows =
+        align_up((size_t)NPT * down_gemv_nkb(I, w8) * kDnCh * (w8 ? 2 : 1) * 16, 256);
+    return rows + down_gemv_lds_bytes(R, NPT, I, w8) <= (size_t)kXLdsDynMax;
 }
 static size_t down_lds_bytes(int R, int NB, int WV, int NPT)
 {
@@ -1004,8 +983,8 @@ static hipError_t set_lds_attributes()
     MV_UP_ATTR(1) MV_UP_ATTR(2) MV_UP_ATTR(3) MV_UP_ATTR(4) MV_UP_ATTR(5)
 #undef MV_UP_ATTR
 #define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, kDnMfmaNB, kDnMfmaWaves>)); \
-    chk(allow_lds(expert_down_gemv_kernel<R, kDnGemvNB, false, kDnGemvWaves>)); \
-    chk(allow_lds(expert_down_gemv_kernel<R, kDnGemvNB, true, kDnGemvWaves8>));
+    chk(allow_lds(expert_down_gemv_kernel<R, false, kDnGemvWaves>)); \
+    chk(allow_lds(expert_down_gemv_kernel<R, true, kDnGemvWaves8>));
     MV_DOWN_ATTR(4) MV_DOWN_ATTR(8) MV_DOWN_ATTR(10) MV_DOWN_ATTR(12) MV_DOWN_ATTR(16)
 #undef MV_DOWN_ATTR
     return e;
@@ -1019,12 +998,12 @@ static void launch_down_gemv(const uint16_t *act, const int *idx, const float *t
     const int grid = (H + R - 1) / R;
     const size_t lds = down_gemv_lds_bytes(R, M * k + ex.ns * M, I, ex.w8);
     if (ex.w8)
-        hipLaunchKernelGGL((expert_down_gemv_kernel<R, kDnGemvNB, true, kDnGemvWaves8>),
+        hipLaunchKernelGGL((expert_down_gemv_kernel<R, true, kDnGemvWaves8>),
                            dim3(grid), dim3(kDnGemvWaves8 * kWave), lds, st, (const u32x4 *)act,
                            idx, tw, (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, ex.sd, M, H, I,
                            E, k, ex.ns, out);
     else
-        hipLaunchKernelGGL((expert_down_gemv_kernel<R, kDnGemvNB, false, kDnGemvWaves>),
+        hipLaunchKernelGGL((expert_down_gemv_kernel<R, false, kDnGemvWaves>),
                            dim3(grid), dim3(kDnGemvWaves * kWave), lds, st, (const u32x4 *)act,
                            idx, tw, (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, nullptr, M, H, I,
                            E, k, ex.ns, out);
