@@ -82,7 +82,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     constexpr int kLmSteps = KB / 32;                    // MFMA steps per block
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int nch = H / 8;                               // bf16 chunks of an h row
     const int nwch = W8 ? H / 16 : nch;                  // 16-byte chunks of a weight row
     const int nkb = (H + KB - 1) / KB;
@@ -117,35 +117,60 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 
-    for (int tile = blockIdx.x + gridDim.x * wave; tile < ntiles; tile += gridDim.x * kLmWaves) {
-        const u32x4 *rp[kLmLoads];
+    // The double buffer runs across tiles: while a tile's last block is
+    // consumed, the next tile's first block is already in flight, so every
+    // wavefront keeps one block in flight from its first tile to its last.
+    // Block n of the wavefront (counted over its tiles) sits in buffer n & 1.
+    auto tile_rows = [&](int tile, const u32x4 *(&rp)[kLmLoads]) {
 #pragma unroll
         for (int q = 0; q < kLmLoads; ++q) {
             int row = tile * 16 + q * kLmRowsPerLd + lrow;
             row = row < V ? row : V - 1;                 // tail rows: valid memory, ignored
             rp[q] = wl + (size_t)row * nwch;
         }
-        // fp8: the scales of this lane's four tile rows, used after the K loop
+    };
+    auto issue = [&](const u32x4 *(&rp)[kLmLoads], int kb, int buf) {
+        int c = kb * kLmRowCh + lcol;
+        c = c < nwch ? c : nwch - 1;                     // K tail: valid memory, x is zero there
+#pragma unroll
+        for (int q = 0; q < kLmLoads; ++q)
+            load_lds16(rp[q] + c, wbuf + buf * kLmBuf + q * kLmLdStride);
+    };
+    const int tstride = gridDim.x * kLmWaves;
+    int tile = blockIdx.x + gridDim.x * wave;
+    const u32x4 *rp[kLmLoads], *rpn[kLmLoads];
+    int nblk = 0;                                        // blocks of this wavefront so far
+    if (tile < ntiles) {
+        tile_rows(tile, rp);
+        issue(rp, 0, 0);
+    }
+    for (; tile < ntiles; tile += tstride) {
+        const bool more = tile + tstride < ntiles;
+        if (more)
+            tile_rows(tile + tstride, rpn);
+        // fp8: the scales of this lane's four tile rows, used after the K loop;
+        // the tile's 16 scales are read with scalar loads (the tile index is
+        // uniform), which the vector-memory waits of the ring do not count,
+        // so using them never waits for the next tile's block in flight
         float rs[4] = {1.0f, 1.0f, 1.0f, 1.0f};
         if constexpr (W8) {
+            float sc[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                sc[i] = wscale[min(tile * 16 + i, V - 1)];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                rs[r] = wscale[min(tile * 16 + 4 * g + r, V - 1)];
+                rs[r] = g == 0 ? sc[r] : g == 1 ? sc[4 + r] : g == 2 ? sc[8 + r] : sc[12 + r];
         }
-        auto issue = [&](int kb, int b) {
-            int c = kb * kLmRowCh + lcol;
-            c = c < nwch ? c : nwch - 1;                 // K tail: valid memory, x is zero there
-#pragma unroll
-            for (int q = 0; q < kLmLoads; ++q)
-                load_lds16(rp[q] + c, wbuf + b * kLmBuf + q * kLmLdStride);
-        };
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        issue(0, 0);
         for (int kb = 0; kb < nkb; ++kb) {
-            const int b = kb & 1;
+            const int b = (nblk + kb) & 1;
             if (kb + 1 < nkb) {
-                issue(kb + 1, b ^ 1);
+                issue(rp, kb + 1, b ^ 1);
                 wait_vmcnt<kLmLoads>();                  // block kb has landed
+            } else if (more) {
+                issue(rpn, 0, b ^ 1);                    // the next tile's first block
+                wait_vmcnt<kLmLoads>();
             } else {
                 wait_vmcnt<0>();
             }
@@ -165,6 +190,12 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
                     x = u32x4{0, 0, 0, 0};
                 acc = mfma_bf16(a, x, acc);
             }
+        }
+        nblk += nkb;
+        if (more) {
+#pragma unroll
+            for (int q = 0; q < kLmLoads; ++q)
+                rp[q] = rpn[q];
         }
         if constexpr (W8) {
 #pragma unroll
