@@ -11,10 +11,11 @@
 // At verify widths (M <= 16 tokens, top-k of 512 experts) a selected expert
 // serves about one (token, slot) pair, so both projections are streamed as
 // matrix-vector products: the weights go straight from HBM into registers
-// (128-bit non-temporal loads, 1 KB contiguous per instruction, one block
-// in flight per wavefront while it consumes the one before), the tokens' vectors sit
-// in LDS, and every lane forms eight-element dot products
-// (v_dot2_f32_bf16) that fixed DPP trees sum over the wavefront. No
+// (128-bit non-temporal loads, 1 KB contiguous per instruction), many
+// wavefronts per CU claim their blocks from an LDS counter and each waits
+// for the block it issued, the tokens' vectors sit in LDS (up) or come from
+// L2 with each block (down), and every lane forms eight-element dot
+// products (v_dot2_f32_bf16) that fixed DPP trees sum over the wavefront. No
 // floating-point atomics: results are bitwise reproducible and every pair's
 // result depends only on its own token.
 //
@@ -24,9 +25,9 @@
 //            block sums y[pair, rows] in LDS.
 //   combine  out[t, r] = sum_j w[t,j] * y[(t,j), r], slots in order, fp32,
 //            at the end of the down kernel.
-// When the pairs' activations do not fit in LDS (M*k*I*2 bytes beyond about
-// 150 KB, i.e. M >= 10 at I = 1024, k = 8) the down projection runs as the
-// MFMA kernel below instead: v_mfma_f32_16x16x32_bf16 with A = 16 rows of
+// Beyond the widths whose pairs' activations would fit in LDS (M*k*I*2 bytes
+// beyond about 150 KB, i.e. M >= 10 at I = 1024, k = 8; a column block then
+// holds several pairs) the down projection runs as the MFMA kernel below: v_mfma_f32_16x16x32_bf16 with A = 16 rows of
 // W_down from a direct-to-LDS ring and B = the pairs' activations read from
 // L2; its summation order differs, so batch invariance holds within each of
 // the two regimes. Every workgroup rebuilds the pair grouping in LDS from
@@ -44,8 +45,6 @@
 
 namespace mv {
 
-constexpr int kXWaves = 4;
-constexpr int kXThreads = kXWaves * kWave;
 constexpr int kXKB = 512;                           // K elements per block
 constexpr int kXRowPitch = kXKB * 2 + 16;           // LDS bytes per row (padded)
 constexpr int kXSteps = kXKB / 32;                  // MFMA steps per block
@@ -181,7 +180,8 @@ __device__ inline void build_groups(const int *__restrict__ topk_idx, int NP, in
 }
 
 static_assert(sizeof(Groups) + 64 <= 8 * 1024, "static LDS margin");
-static_assert(kXThreads >= kGroupThreads, "grouping needs a thread per histogram slice");
+// (every expert kernel's workgroups have at least kGroupThreads threads:
+// checked where their sizes are set)
 
 // Pairs: p < NP = M*k are routed (token p / k, slot p % k); with a shared
 // expert (ns = 1) p = NP + t is token t's pair with it, expert id E.
@@ -370,11 +370,10 @@ __global__ __launch_bounds__(WV * kWave) void expert_down_kernel(
 // The down projection at verify widths is a set of matrix-vector products:
 // with distinct experts per token a column block holds about one pair. The
 // weights therefore stream straight into registers -- one 1 KB load per row
-// per K block (lane i takes 16-byte chunk i), an NB-deep register ring, so
-// NB - 1 blocks of every wavefront are in flight while one is consumed --
-// and every pair's activation row sits in LDS, staged once per workgroup with
-// direct-to-LDS loads. Nothing but the weights is read inside the loop, so
-// the loop waits on one constant count. Per (pair, K block) every lane forms
+// per K block (lane i takes 16-byte chunk i) -- together with the
+// activation chunks of the column block's pairs (from L2), and each
+// wavefront waits for the block it issued before it consumes it; the other
+// wavefronts of the CU keep the loads flowing. Per (pair, K block) every lane forms
 // R eight-element dot products (v_dot2_f32_bf16) and each row is summed over
 // the wavefront in a fixed DPP tree; the block sums are added over K blocks
 // in order in the combine. Workgroup b owns rows r0 .. r0+R-1 of every
@@ -931,6 +930,10 @@ static size_t down_lds_bytes(int R, int NB, int WV, int NPT)
 // but their slots do not fit at R = 16).
 constexpr int kDnMfmaNB = 1;
 constexpr int kDnMfmaWaves = 8;
+static_assert(4 * kWave >= kGroupThreads && kUpClaimWaves * kWave >= kGroupThreads &&
+                  kDnGemvWaves * kWave >= kGroupThreads &&
+                  kDnGemvWaves8 * kWave >= kGroupThreads && kDnMfmaWaves * kWave >= kGroupThreads,
+              "the grouping needs a thread per histogram slice");
 static bool down_mfma_fits(int R, int NPT)
 {
     return down_lds_bytes(R, kDnMfmaNB, kDnMfmaWaves, NPT) <= (size_t)kXLdsDynMax;
@@ -1275,7 +1278,8 @@ extern "C" moe_status_t moe_layer_rmsnorm(const uint16_t *h, const uint16_t *gam
 }
 
 // fp8 experts: E4M3 codes [E,I,H] / [E,H,I] with fp32 scales per row; H and
-// I multiples of 16; the down projection's activations must fit in LDS
+// I multiples of 16; the widths of the GEMV down kernel (M <= 9 at I = 1024,
+// k = 8: the MFMA down kernel is bf16 only)
 static moe_status_t ffn8_check(const uint16_t *x, const int32_t *topk_idx,
                                const float *topk_w, const uint8_t *w_gate, const float *s_gate,
                                const uint8_t *w_up, const float *s_up, const uint8_t *w_down,
