@@ -597,7 +597,10 @@ __host__ __device__ inline size_t up_gemv_x_bytes(int M, int H, int KC, bool w8)
 // W8: fp8 weights (E4M3 codes, 16 per 16-byte chunk, an fp32 scale per
 // row in sg / su); each chunk is widened to two bf16 chunks that meet two x
 // chunks, and the row scales multiply the reduced sums before the SwiGLU.
-template <int KC, int NB, bool W8, int WV, bool CLAIM>
+// XR (one token, one K block per unit): the lane's x chunks are the same
+// for every unit, so they are loaded once into registers at the start (no
+// LDS staging, no wait on it before the first weights go out).
+template <int KC, int NB, bool W8, int WV, bool CLAIM, bool XR>
 __global__ __launch_bounds__(WV * kWave) void expert_up_gemv_kernel(
     const u32x4 *__restrict__ x, const int *__restrict__ topk_idx,
     const u32x4 *__restrict__ wg, const u32x4 *__restrict__ wu,
@@ -634,13 +637,38 @@ __global__ __launch_bounds__(WV * kWave) void expert_up_gemv_kernel(
     };
 
     __shared__ int s_next;                               // the workgroup's next unit to claim
+    constexpr int kXr = XR ? KC * (W8 ? 2 : 1) : 1;
+    u32x4 xreg[kXr];                                     // XR: this lane's x chunks
+    if constexpr (XR) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            const int cp = c * kWave + lane;             // the lane's weight chunk c
+            if constexpr (W8) {
+                const int xc = min(2 * cp, nch - 2);     // clamped; zeroed below
+                xreg[2 * c] = x[xc];
+                xreg[2 * c + 1] = x[xc + 1];
+            } else {
+                xreg[c] = x[min(cp, nch - 1)];
+            }
+        }
+    }
     groups_set_pairs(pair_expert(topk_idx, threadIdx.x, NP, NPT, E), NPT, E + ns, g);
     if (threadIdx.x == 0)
         s_next = 0;
-    wait_vmcnt<0>();                                     // only the pair id is in flight
-    for (int i = threadIdx.x; i < M * (xs - nch); i += blockDim.x) {
-        const int t = i / (xs - nch), c = nch + i % (xs - nch);
-        s_x[t * xs + c] = u32x4{0, 0, 0, 0};             // K padding reads as zero
+    wait_vmcnt<0>();                                     // the pair id (and XR: x) is in
+    if constexpr (XR) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c)                     // the K tail of x reads as zero
+            if (c * kWave + lane >= nwc) {
+#pragma unroll
+                for (int i = 0; i < (W8 ? 2 : 1); ++i)
+                    xreg[c * (W8 ? 2 : 1) + i] = u32x4{0, 0, 0, 0};
+            }
+    } else {
+        for (int i = threadIdx.x; i < M * (xs - nch); i += blockDim.x) {
+            const int t = i / (xs - nch), c = nch + i % (xs - nch);
+            s_x[t * xs + c] = u32x4{0, 0, 0, 0};         // K padding reads as zero
+        }
     }
     groups_finish(NPT, g);                               // (its barriers also publish s_next)
 
@@ -729,7 +757,8 @@ __global__ __launch_bounds__(WV * kWave) void expert_up_gemv_kernel(
                 const u32x4 *xr = s_x + pair_token(p, NP, k) * xs + 2 * (kb * KC * kWave + lane);
 #pragma unroll
                 for (int c = 0; c < KC; ++c) {
-                    const u32x4 x0 = xr[2 * c * kWave], x1 = xr[2 * c * kWave + 1];
+                    const u32x4 x0 = XR ? xreg[2 * c % kXr] : xr[2 * c * kWave];
+                    const u32x4 x1 = XR ? xreg[(2 * c + 1) % kXr] : xr[2 * c * kWave + 1];
                     ga = dot8_bf16(e4m3x8_to_bf16(dg[c].x, dg[c].y), x0, ga);
                     ga = dot8_bf16(e4m3x8_to_bf16(dg[c].z, dg[c].w), x1, ga);
                     ua = dot8_bf16(e4m3x8_to_bf16(du[c].x, du[c].y), x0, ua);
@@ -739,7 +768,7 @@ __global__ __launch_bounds__(WV * kWave) void expert_up_gemv_kernel(
                 const u32x4 *xr = s_x + pair_token(p, NP, k) * xs + kb * KC * kWave + lane;
 #pragma unroll
                 for (int c = 0; c < KC; ++c) {
-                    const u32x4 xv = xr[c * kWave];
+                    const u32x4 xv = XR ? xreg[c % kXr] : xr[c * kWave];
                     ga = dot8_bf16(dg[c], xv, ga);
                     ua = dot8_bf16(du[c], xv, ua);
                 }
@@ -779,9 +808,11 @@ __global__ __launch_bounds__(WV * kWave) void expert_up_gemv_kernel(
         tg[q] = next_tag();
         issue(tg[q], wgr[q], wur[q], sgr[q], sur[q]);
     }
-    stage_rows_lds(x, M, nch, s_x, xs);
-    wait_vmcnt<0>();                                     // this wave's share of x has landed
-    lds_barrier();                                       // ... and every other wave's
+    if constexpr (!XR) {
+        stage_rows_lds(x, M, nch, s_x, xs);
+        wait_vmcnt<0>();                                 // this wave's share of x has landed
+        lds_barrier();                                   // ... and every other wave's
+    }
     for (bool live = true; live;) {
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
@@ -853,12 +884,12 @@ struct Experts {
 // Several wavefronts per SIMD hide each other's per-unit latency (the group
 // lookups, the reductions, the epilogue) and keep the loads of one flowing
 // while another computes.
-template <int KC, int NB, bool W8, int WV, bool CLAIM>
+template <int KC, int NB, bool W8, int WV, bool CLAIM, bool XR>
 static void launch_up_gemv_wv(int grid, size_t lds, const uint16_t *x, const int *idx,
                               const Experts &ex, int M, int H, int I, int E, int k,
                               uint16_t *act, hipStream_t st)
 {
-    hipLaunchKernelGGL((expert_up_gemv_kernel<KC, NB, W8, WV, CLAIM>), dim3(grid),
+    hipLaunchKernelGGL((expert_up_gemv_kernel<KC, NB, W8, WV, CLAIM, XR>), dim3(grid),
                        dim3(WV * kWave), lds, st, (const u32x4 *)x, idx, (const u32x4 *)ex.wg,
                        (const u32x4 *)ex.wu, (const u32x4 *)ex.wgs, (const u32x4 *)ex.wus, ex.sg,
                        ex.su, M, H, I, E, k, ex.ns, act);
@@ -869,13 +900,22 @@ static void launch_up_gemv(const uint16_t *x, const int *idx, const Experts &ex,
 {
     // (the supported shapes always fit: up_gemv_fits; one token's two
     // workgroups per CU hold less than the twelve-wavefront one)
-    if (!W8 && M == 1)
-        launch_up_gemv_wv<KC, kUpGemvNB, false, 4, false>(
-            2 * kXGrid, up_gemv_lds_bytes(M, H, KC, W8, 4), x, idx, ex, M, H, I, E, k, act, st);
+    const size_t lds4 = up_gemv_lds_bytes(M, H, KC, W8, 4);
+    const size_t lds12 = up_gemv_lds_bytes(M, H, KC, W8, kUpClaimWaves);
+    // one token and one K block per unit: x in registers
+    const bool xr = M == 1 && (W8 ? H / 16 : H / 8) <= KC * kWave;
+    if (!W8 && M == 1 && xr)
+        launch_up_gemv_wv<KC, kUpGemvNB, false, 4, false, true>(2 * kXGrid, lds4, x, idx, ex, M,
+                                                                H, I, E, k, act, st);
+    else if (!W8 && M == 1)
+        launch_up_gemv_wv<KC, kUpGemvNB, false, 4, false, false>(2 * kXGrid, lds4, x, idx, ex, M,
+                                                                 H, I, E, k, act, st);
+    else if (xr)
+        launch_up_gemv_wv<KC, kUpClaimNB, W8, kUpClaimWaves, true, true>(
+            kXGrid, lds12, x, idx, ex, M, H, I, E, k, act, st);
     else
-        launch_up_gemv_wv<KC, kUpClaimNB, W8, kUpClaimWaves, true>(
-            kXGrid, up_gemv_lds_bytes(M, H, KC, W8, kUpClaimWaves), x, idx, ex, M, H, I, E, k,
-            act, st);
+        launch_up_gemv_wv<KC, kUpClaimNB, W8, kUpClaimWaves, true, false>(
+            kXGrid, lds12, x, idx, ex, M, H, I, E, k, act, st);
 }
 template <bool W8>
 static void launch_up_gemv_kc(const uint16_t *x, const int *idx, const Experts &ex, int M,
@@ -980,9 +1020,12 @@ static hipError_t set_lds_attributes()
 {
     hipError_t e = hipSuccess;
     auto chk = [&](hipError_t r) { if (r != hipSuccess) e = r; };
-#define MV_UP_ATTR(KC) chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false, 4, false>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, false, kUpClaimWaves, true>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, true, kUpClaimWaves, true>));
+#define MV_UP_ATTR(KC) chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false, 4, false, false>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false, 4, false, true>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, false, kUpClaimWaves, true, false>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, false, kUpClaimWaves, true, true>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, true, kUpClaimWaves, true, false>)); \
+    chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, true, kUpClaimWaves, true, true>));
     MV_UP_ATTR(1) MV_UP_ATTR(2) MV_UP_ATTR(3) MV_UP_ATTR(4) MV_UP_ATTR(5)
 #undef MV_UP_ATTR
 #define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, kDnMfmaNB, kDnMfmaWaves>)); \
