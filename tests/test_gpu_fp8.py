@@ -118,6 +118,7 @@ FP8_CASES = [
     (9, 512, 1024, 64, 8),
     (2, 16, 16, 3, 2),
     (6, 2560, 1024, 32, 8),
+    (1, 1040, 256, 12, 3),       # one token, x in registers, a partial last chunk column
 ]
 
 

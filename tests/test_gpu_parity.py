@@ -138,6 +138,8 @@ FFN_CASES = [
     (16, 256, 128, 16, 16),      # every token uses every expert
     (2, 8, 8, 3, 2),             # smallest shape
     (7, 512, 1032, 40, 3),       # I not a multiple of the 512-element lane stride
+    (1, 1032, 256, 12, 3),       # one token, x in registers, a partial last chunk column
+    (1, 3072, 256, 16, 4),       # one token, two K blocks per unit: x staged in LDS
 ]
 
 
