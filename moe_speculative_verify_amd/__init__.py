@@ -139,27 +139,37 @@ def _ptr(t: torch.Tensor | None, name: str, dtypes=None, shape=None) -> int | No
     return t.data_ptr()
 
 
+def _stream_obj(stream):
+    return torch.cuda.current_stream() if stream is None else stream
+
+
 def _stream(stream) -> int:
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream
+    return _stream_obj(stream).cuda_stream
 
 
 class Workspace:
-    """A zero-filled device workspace, grown on demand, one per key.
+    """A zero-filled device workspace, grown on demand, one per (kind,
+    device, stream).
 
     The library leaves every counter it uses at zero, so a workspace is
-    reused across calls on the same stream without clearing.
+    reused across calls on the same stream without clearing. A new one is
+    allocated and zero-filled on the stream the library will run on, so the
+    fill is ordered before the kernels that rely on it, and the caching
+    allocator ties its block to that stream: a buffer it replaces is only
+    handed out again to later work on the same stream, after the kernels
+    already enqueued there.
     """
 
     _pool: dict = {}
 
     @classmethod
-    def get(cls, kind: str, nbytes: int, device, stream_handle: int) -> torch.Tensor:
-        key = (kind, torch.device(device).index, stream_handle)
+    def get(cls, kind: str, nbytes: int, device, stream) -> torch.Tensor:
+        stream = _stream_obj(stream)
+        key = (kind, torch.device(device).index, stream.cuda_stream)
         ws = cls._pool.get(key)
         if ws is None or ws.numel() < nbytes:
-            ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
+            with torch.cuda.stream(stream):
+                ws = torch.zeros(max(nbytes, 4096), dtype=torch.uint8, device=device)
             cls._pool[key] = ws
         return ws
 
@@ -217,7 +227,7 @@ def moe_route(x, w_router, k: int, bias=None, *, want_logits=False, out=None,
         logits = torch.empty((M, E), dtype=torch.float32, device=dev)
     st = _stream(stream)
     nbytes = moe_route_workspace_bytes(M, E)
-    ws = workspace if workspace is not None else Workspace.get("route", nbytes, dev, st)
+    ws = workspace if workspace is not None else Workspace.get("route", nbytes, dev, stream)
     _check("moe_route", lib().moe_route(
         _ptr(x, "x", _BF16), _ptr(w_router, "w_router", _BF16, (E, H)),
         _ptr(bias, "bias", (torch.float32,), (E,)), M, H, E, k,
@@ -239,7 +249,7 @@ def moe_expert_ffn(x, topk_idx, topk_w, w_gate, w_up, w_down, *, out=None,
         out = torch.empty((M, H), dtype=torch.float32, device=dev)
     st = _stream(stream)
     nbytes = moe_expert_ffn_workspace_bytes(M, H, I, E, k)
-    ws = workspace if workspace is not None else Workspace.get("ffn", nbytes, dev, st)
+    ws = workspace if workspace is not None else Workspace.get("ffn", nbytes, dev, stream)
     _check("moe_expert_ffn", lib().moe_expert_ffn(
         _ptr(x, "x", _BF16), _ptr(topk_idx, "topk_idx", (torch.int32,), (M, k)),
         _ptr(topk_w, "topk_w", (torch.float32,), (M, k)),
@@ -264,7 +274,7 @@ def moe_layer(x, w_router, w_gate, w_up, w_down, k: int, bias=None, *, out=None,
         o = torch.empty((M, H), dtype=torch.float32, device=dev)
     st = _stream(stream)
     nbytes = moe_layer_workspace_bytes(M, H, I, E, k)
-    ws = workspace if workspace is not None else Workspace.get("layer", nbytes, dev, st)
+    ws = workspace if workspace is not None else Workspace.get("layer", nbytes, dev, stream)
     _check("moe_layer", lib().moe_layer(
         _ptr(x, "x", _BF16), _ptr(w_router, "w_router", _BF16, (E, H)),
         _ptr(bias, "bias", (torch.float32,), (E,)),
@@ -288,7 +298,7 @@ def lmhead_argmax(h, w_lm, *, want_max=False, out=None, workspace=None, stream=N
         ml = torch.empty(M, dtype=torch.float32, device=dev)
     st = _stream(stream)
     nbytes = lmhead_argmax_workspace_bytes(M, V)
-    ws = workspace if workspace is not None else Workspace.get("lmhead", nbytes, dev, st)
+    ws = workspace if workspace is not None else Workspace.get("lmhead", nbytes, dev, stream)
     _check("lmhead_argmax", lib().lmhead_argmax(
         _ptr(h, "h", _BF16), _ptr(w_lm, "w_lm", _BF16, (V, H)), M, H, V,
         _ptr(am, "argmax", (torch.int32,), (M,)),
@@ -314,7 +324,7 @@ def lmhead_greedy_verify(h, w_lm, tokens, *, want_max=False, out=None, workspace
         ml = torch.empty(M, dtype=torch.float32, device=dev)
     st = _stream(stream)
     nbytes = lmhead_argmax_workspace_bytes(M, V)
-    ws = workspace if workspace is not None else Workspace.get("lmhead", nbytes, dev, st)
+    ws = workspace if workspace is not None else Workspace.get("lmhead", nbytes, dev, stream)
     _check("lmhead_greedy_verify", lib().lmhead_greedy_verify(
         _ptr(h, "h", _BF16), _ptr(w_lm, "w_lm", _BF16, (V, H)),
         _ptr(tokens, "tokens", (torch.int32,), (M,)), M, H, V,
@@ -343,7 +353,7 @@ def moe_route_rmsnorm(h, gamma, eps: float, w_router, k: int, bias=None, *, want
         logits = torch.empty((M, E), dtype=torch.float32, device=dev)
     st = _stream(stream)
     nbytes = moe_route_workspace_bytes(M, E)
-    ws = workspace if workspace is not None else Workspace.get("route", nbytes, dev, st)
+    ws = workspace if workspace is not None else Workspace.get("route", nbytes, dev, stream)
     _check("moe_route_rmsnorm", lib().moe_route_rmsnorm(
         _ptr(h, "h", _BF16), _ptr(gamma, "gamma", _BF16, (H,)), float(eps),
         _ptr(w_router, "w_router", _BF16, (E, H)),
@@ -374,7 +384,7 @@ def moe_layer_rmsnorm(h, gamma, eps: float, w_router, w_gate, w_up, w_down, k: i
         o = torch.empty((M, H), dtype=torch.float32, device=dev)
     st = _stream(stream)
     nbytes = moe_layer_workspace_bytes(M, H, I, E, k)
-    ws = workspace if workspace is not None else Workspace.get("layer", nbytes, dev, st)
+    ws = workspace if workspace is not None else Workspace.get("layer", nbytes, dev, stream)
     _check("moe_layer_rmsnorm", lib().moe_layer_rmsnorm(
         _ptr(h, "h", _BF16), _ptr(gamma, "gamma", _BF16, (H,)), float(eps),
         _ptr(w_router, "w_router", _BF16, (E, H)),
@@ -399,7 +409,7 @@ def moe_expert_ffn_shared(x, topk_idx, topk_w, w_gate, w_up, w_down, w_gate_shar
     o = out if out is not None else torch.empty((M, H), dtype=torch.float32, device=dev)
     st = _stream(stream)
     nbytes = moe_expert_ffn_workspace_bytes(M, H, I, E, k)
-    ws = workspace if workspace is not None else Workspace.get("ffn", nbytes, dev, st)
+    ws = workspace if workspace is not None else Workspace.get("ffn", nbytes, dev, stream)
     _check("moe_expert_ffn_shared", lib().moe_expert_ffn_shared(
         _ptr(x, "x", _BF16), _ptr(topk_idx, "topk_idx", (torch.int32,), (M, k)),
         _ptr(topk_w, "topk_w", (torch.float32,), (M, k)),
@@ -427,7 +437,7 @@ def moe_layer_shared(x, w_router, w_gate, w_up, w_down, w_gate_shared, w_up_shar
         o = torch.empty((M, H), dtype=torch.float32, device=dev)
     st = _stream(stream)
     nbytes = moe_layer_workspace_bytes(M, H, I, E, k)
-    ws = workspace if workspace is not None else Workspace.get("layer", nbytes, dev, st)
+    ws = workspace if workspace is not None else Workspace.get("layer", nbytes, dev, stream)
     _check("moe_layer_shared", lib().moe_layer_shared(
         _ptr(x, "x", _BF16), _ptr(w_router, "w_router", _BF16, (E, H)),
         _ptr(bias, "bias", (torch.float32,), (E,)),
@@ -459,7 +469,7 @@ def lmhead_argmax_fp8(h, w_lm, w_scale, *, want_max=False, out=None, workspace=N
         ml = torch.empty(M, dtype=torch.float32, device=dev)
     st = _stream(stream)
     nbytes = lmhead_argmax_workspace_bytes(M, V)
-    ws = workspace if workspace is not None else Workspace.get("lmhead", nbytes, dev, st)
+    ws = workspace if workspace is not None else Workspace.get("lmhead", nbytes, dev, stream)
     _check("lmhead_argmax_fp8", lib().lmhead_argmax_fp8(
         _ptr(h, "h", _BF16), _ptr(w_lm, "w_lm", _U8, (V, H)),
         _ptr(w_scale, "w_scale", (torch.float32,), (V,)), M, H, V,
@@ -485,7 +495,7 @@ def lmhead_greedy_verify_fp8(h, w_lm, w_scale, tokens, *, want_max=False, out=No
         ml = torch.empty(M, dtype=torch.float32, device=dev)
     st = _stream(stream)
     nbytes = lmhead_argmax_workspace_bytes(M, V)
-    ws = workspace if workspace is not None else Workspace.get("lmhead", nbytes, dev, st)
+    ws = workspace if workspace is not None else Workspace.get("lmhead", nbytes, dev, stream)
     _check("lmhead_greedy_verify_fp8", lib().lmhead_greedy_verify_fp8(
         _ptr(h, "h", _BF16), _ptr(w_lm, "w_lm", _U8, (V, H)),
         _ptr(w_scale, "w_scale", (torch.float32,), (V,)),
@@ -514,7 +524,7 @@ def moe_expert_ffn_fp8(x, topk_idx, topk_w, w_gate, s_gate, w_up, s_up, w_down, 
     o = out if out is not None else torch.empty((M, H), dtype=torch.float32, device=dev)
     st = _stream(stream)
     nbytes = moe_expert_ffn_workspace_bytes(M, H, I, E, k)
-    ws = workspace if workspace is not None else Workspace.get("ffn", nbytes, dev, st)
+    ws = workspace if workspace is not None else Workspace.get("ffn", nbytes, dev, stream)
     _check("moe_expert_ffn_fp8", lib().moe_expert_ffn_fp8(
         _ptr(x, "x", _BF16), _ptr(topk_idx, "topk_idx", (torch.int32,), (M, k)),
         _ptr(topk_w, "topk_w", (torch.float32,), (M, k)),
@@ -539,7 +549,7 @@ def moe_layer_fp8(x, w_router, w_gate, s_gate, w_up, s_up, w_down, s_down, k: in
         o = torch.empty((M, H), dtype=torch.float32, device=dev)
     st = _stream(stream)
     nbytes = moe_layer_workspace_bytes(M, H, I, E, k)
-    ws = workspace if workspace is not None else Workspace.get("layer", nbytes, dev, st)
+    ws = workspace if workspace is not None else Workspace.get("layer", nbytes, dev, stream)
     _check("moe_layer_fp8", lib().moe_layer_fp8(
         _ptr(x, "x", _BF16), _ptr(w_router, "w_router", _BF16, (E, H)),
         _ptr(bias, "bias", (torch.float32,), (E,)),

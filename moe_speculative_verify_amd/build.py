@@ -1,8 +1,14 @@
-"""Build the gfx950 shared library libmoeverify.so in the package directory."""
+"""Build the gfx950 shared library libmoeverify.so in the package directory.
+
+Each source is compiled to its own object in parallel (no device code crosses
+files), then the objects are linked into the shared library.
+"""
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import subprocess
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -12,22 +18,32 @@ SOURCES = ["capi.hip", "route.hip", "expert.hip", "lmhead.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 instructions stay off: hipcc would otherwise form them
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
 ]
 
 
-def build(out: str = LIB, verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + r.stdout + r.stderr)
+
+
+def build(out: str = LIB, verbose: bool = False) -> str:
+    inc = ["-I", os.path.join(ROOT, "include")]
+    with tempfile.TemporaryDirectory(prefix="mvbuild") as tmpd:
+        objs = [os.path.join(tmpd, s.replace(".hip", ".o")) for s in SOURCES]
+        cmds = [[HIPCC, *FLAGS, *inc, "-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        with concurrent.futures.ThreadPoolExecutor(len(cmds)) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = out + ".tmp"
+        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
     return out
 

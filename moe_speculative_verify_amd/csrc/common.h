@@ -138,16 +138,53 @@ __device__ __forceinline__ void wait_vmcnt()
 
 // Order-preserving map of fp32 to uint32 (-0 and +0 both map to +0's code;
 // larger floats give larger codes) and its inverse.
-__device__ __forceinline__ uint32_t f32_order(float f)
+__host__ __device__ inline uint32_t f32_order(float f)
 {
-    uint32_t u = __float_as_uint(f);
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
     if (u == 0x80000000u)
         u = 0;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float f32_unorder(uint32_t u)
+__host__ __device__ inline float f32_unorder(uint32_t u)
 {
-    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+    return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// Running first-index argmax over rows visited in ascending order: a NaN
+// counts as -inf (as in the router's selection), the first row visited is
+// always taken, and a later row only when strictly larger, so the result is
+// the lowest row holding the maximum -- row 0 of a run whose values are all
+// -inf or NaN. kNoRow marks a lane that has visited no row yet; it loses
+// every tie against a real row in the cross-lane reductions.
+constexpr int kNoRow = 0x7FFFFFFF;
+__host__ __device__ inline void argmax_take(float &bv, int &bi, float v, int row)
+{
+    v = v != v ? -INFINITY : v;
+    if (v > bv || bi == kNoRow) {
+        bv = v;
+        bi = row;
+    }
+}
+
+// Merge of two running argmaxes over disjoint rows: the larger value, then
+// the lower row (kNoRow, the largest int, loses every tie).
+__host__ __device__ inline void argmax_merge(float &bv, int &bi, float ov, int oi)
+{
+    if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+    }
+}
+// 64-bit key of a (value, row): order code of the value above the inverted
+// row, so a larger key is a larger value or an equal value at a lower row;
+// and its row.
+__host__ __device__ inline unsigned long long argmax_key(float v, int row)
+{
+    return ((unsigned long long)f32_order(v) << 32) | (uint32_t)(~(uint32_t)row);
+}
+__host__ __device__ inline int argmax_key_row(unsigned long long key)
+{
+    return (int)(~(uint32_t)key);
 }
 
 // one fused DPP step of a wave-wide uint32 maximum; rows a broadcast leaves
@@ -231,24 +268,35 @@ __device__ inline void stage_rows_lds(const u32x4 *__restrict__ src, int nrows, 
 
 // -------------------------------------------------------------------- host
 
-// Every workspace layout starts with the same 4 KB header of arrival
-// counters, one per 128-byte line (device-scope atomics on one line are
-// serialised, so counters that many workgroups hit sit on lines of their
-// own): word 0 is the arrival ticket of the last-workgroup pattern, word 32 g
-// (g = 1 .. 31) the ticket of arrival group g. Every counter is zero when a
-// call starts and when it ends, at the same offset for every entry point and
-// shape, so one workspace serves them all in turn.
+// Every workspace layout starts with the same 4 KB header of counters, one
+// per 128-byte line (device-scope atomics on one line are serialised, so
+// counters that many workgroups hit sit on lines of their own), at the same
+// offsets for every entry point and shape:
+//   line 0         the ticket of the last-workgroup pattern
+//   lines 1 .. 20  the tickets of arrival groups 1 .. 20 (arrive_last)
+// Every counter is zero when a call starts and when it ends, so one
+// workspace serves every entry point and shape in turn.
 constexpr size_t kWsHeader = 4096;
 constexpr int kWsLineWords = 32;              // words per 128-byte line
-constexpr int kWsGroups = 31;                 // arrival groups the header holds
+constexpr int kWsGroups = 20;                 // arrival groups the header holds
 
 // Two-level arrival of the last-workgroup pattern, called by one thread per
-// workgroup once its results are out (stored at device scope and waited
-// for): workgroup b counts in at the counter of group b / kArrivalGroup (a
-// line of its own), the group's last arrival resets that counter and counts
-// in at the ticket (word 0), and the ticket's last arrival gets true and
-// resets nothing: the caller resets the ticket. Grids of up to kArrivalGroup
-// * kWsGroups workgroups.
+// workgroup once its results are out (every thread of the workgroup has
+// stored its part and passed a workgroup barrier, so those stores happen
+// before this call): workgroup b counts in at the counter of group
+// b / kArrivalGroup (a line of its own), the group's last arrival resets that
+// counter and counts in at the ticket (word 0), and the ticket's last arrival
+// gets true and resets nothing: the caller resets the ticket.
+// Ordering (device / agent scope): every count is a release, so it publishes
+// the results that happen before it; the last arrival of a group follows its
+// count with an acquire fence, which synchronises with every release its
+// count read (the counts form one read-modify-write chain), before it counts
+// in at the ticket; the ticket's last arrival acquires in the same way. So
+// the selecting workgroup's later loads see every workgroup's results, and
+// only the two arrivals on the chain pay for an acquire (an agent-scope
+// release writes back this XCD's L2, an acquire invalidates it: about 1.3 and
+// 1.0 us each, measured with 256 workgroups).
+// Grids of up to kArrivalGroup * kWsGroups workgroups.
 constexpr int kArrivalGroup = 32;
 __device__ inline bool arrive_last(unsigned *ticket)
 {
@@ -256,11 +304,15 @@ __device__ inline bool arrive_last(unsigned *ticket)
     const int ng = (gridDim.x + kArrivalGroup - 1) / kArrivalGroup;
     const unsigned gsz = (unsigned)min(kArrivalGroup, (int)gridDim.x - grp * kArrivalGroup);
     unsigned *gc = ticket + kWsLineWords * (1 + grp);
-    if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gsz - 1)
+    if (__hip_atomic_fetch_add(gc, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) != gsz - 1)
         return false;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     __hip_atomic_store(gc, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-           (unsigned)ng - 1;
+    if (__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) !=
+        (unsigned)ng - 1)
+        return false;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return true;
 }
 
 // Dynamic LDS a kernel may request: 160 KB per CU on gfx950, less a margin

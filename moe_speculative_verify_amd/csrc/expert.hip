@@ -40,6 +40,7 @@
 // same up and down launches stream it with the routed experts (the post's
 // "513-expert" MoE decode, section "Two fusions and a retune").
 #include "common.h"
+#include "select.h"
 
 #include <mutex>
 
@@ -366,20 +367,16 @@ __global__ __launch_bounds__(WV * kWave) void expert_down_kernel(
     }
 }
 
-// ---------------------------------------------------------- down (GEMV)
-// The down projection at verify widths is a set of matrix-vector products:
-// with distinct experts per token a column block holds about one pair. The
-// weights therefore stream straight into registers -- one 1 KB load per row
-// per K block (lane i takes 16-byte chunk i) -- together with the
-// activation chunks of the column block's pairs (from L2), and each
-// wavefront waits for the block it issued before it consumes it; the other
-// wavefronts of the CU keep the loads flowing. Per (pair, K block) every lane forms
-// R eight-element dot products (v_dot2_f32_bf16) and each row is summed over
-// the wavefront in a fixed DPP tree; the block sums are added over K blocks
-// in order in the combine. Workgroup b owns rows r0 .. r0+R-1 of every
-// expert; its wavefronts claim the (column block, K block) blocks one at a
-// time from an LDS counter.
-constexpr int kDnKB = 512;                       // K elements per block
+// ---------------------------------------------------------------- GEMVs
+// At verify widths a selected expert serves about one (token, slot) pair, so
+// both projections are streamed as matrix-vector products: the weights go
+// straight from HBM into registers (1 KB contiguous per load instruction:
+// lane i takes 16-byte chunk i), each wavefront waits for the block it
+// issued before it consumes it while the CU's other wavefronts keep the
+// loads flowing, and every lane forms eight-element dot products
+// (v_dot2_f32_bf16) that fixed DPP trees sum over the wavefront.
+
+constexpr int kDnKB = 512;                       // down: K elements per block (bf16)
 constexpr int kDnCh = kDnKB / 8;                 // 16-byte chunks per row per block
 
 // Sum over the wavefront in a fixed order, returned uniform: the 16-lane row
@@ -402,6 +399,323 @@ __device__ __forceinline__ float wave_total(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// ------------------------------------------------------------ up (GEMV)
+// Units are (column block v, row i of I), in order, so the chip streams one
+// moving window of the weights; a block is the unit's gate row and up row,
+// KC loads of 1 KB each per matrix per K block, streamed into registers.
+// Workgroup b (one per CU) owns units b, b + G, b + 2G, ..., and its kUpWaves
+// wavefronts claim them one at a time from an LDS counter, each waiting for
+// the block it just issued: a SIMD serves its older wavefront first, and the
+// claims let that one take more units instead of the younger ones ending
+// last. For every pair of the column block each lane forms its gate and up
+// partial dots and two DPP trees reduce them; lane 0 queues the sums, and
+// every 64 queued outputs the 64 lanes take a = bf16(silu(g) * u) (fp32,
+// one rounding), one output each. With more than KC * 64 chunks per row a
+// unit spans several K blocks, whose sums are added in LDS in block order.
+constexpr int kUpWaves = 12;                     // wavefronts per workgroup
+
+__host__ __device__ inline size_t up_x_bytes(int M, int H, int KC, bool w8, bool xr)
+{
+    if (xr)
+        return 0;
+    const int nwc = w8 ? H / 16 : H / 8;
+    const int nbu = (nwc + KC * kWave - 1) / (KC * kWave);
+    return align_up((size_t)M * nbu * KC * kWave * (w8 ? 2 : 1) * 16, 256);
+}
+// x of the M tokens in whole K blocks (none when x sits in registers), then
+// each streaming wavefront's queue of finished sums and its 16 running sums
+__host__ __device__ inline size_t up_lds_bytes(int M, int H, int KC, bool w8, bool xr)
+{
+    return up_x_bytes(M, H, KC, w8, xr) +
+           (size_t)kUpWaves * (kUpPend * (sizeof(float2) + 4) + 16 * sizeof(float2));
+}
+
+// The router's selection when it runs in the up kernel (moe_layer): the
+// partial logits [nks][M][E] of the router kernel (slices of the hidden
+// dimension), the optional bias, and where workgroup 0 writes the selection.
+struct UpSelect {
+    const float *plog;
+    int nks;
+    const float *bias;
+    int *topk_idx;
+    float *topk_w;
+};
+constexpr int kSelKJ = 8;                        // logits per lane: E <= 512
+
+// KC: 16-byte chunks per lane per row and K block (a unit is one block when
+// a row has at most KC * 64 chunks); W8: fp8 weights (E4M3 codes, 16 per
+// chunk, an fp32 scale per row in sg / su); XR: one token and one K block
+// per unit, so the lane's x chunks are the same for every unit and are
+// loaded once into registers instead of staged in LDS. SEL: the expert ids
+// are not given: every workgroup takes the router's softmax top-k itself from
+// the partial logits (the same function and the same order as the router
+// kernel, so the same bits in every workgroup), which saves the router
+// kernel its cross-workgroup arrival and selection, and the expert kernels a
+// reload of the ids; workgroup 0 writes the selection out.
+template <int KC, bool W8, bool XR, bool SEL>
+__global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
+    const u32x4 *__restrict__ x, const int *__restrict__ topk_idx,
+    const u32x4 *__restrict__ wg, const u32x4 *__restrict__ wu,
+    const u32x4 *__restrict__ wgs, const u32x4 *__restrict__ wus,
+    const float *__restrict__ sg, const float *__restrict__ su, int M, int H, int I, int E,
+    int k, int ns, uint16_t *__restrict__ act, UpSelect sel)
+{
+    constexpr int WV = kUpWaves;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ Groups g;
+    __shared__ int s_next;                               // the next unit of this workgroup
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
+    const int nch = H / 8;                               // 16-byte x chunks per row
+    const int nwc = W8 ? H / 16 : nch;                   // 16-byte weight chunks per row
+    const int nbu = (nwc + KC * kWave - 1) / (KC * kWave);   // K blocks per unit
+    const int xs = nbu * KC * kWave * (W8 ? 2 : 1);      // LDS x row, chunks
+    const int NP = M * k, NPT = NP + ns * M;
+    const size_t xbytes = up_x_bytes(M, H, KC, W8, XR);
+    u32x4 *s_x = (u32x4 *)smem;                          // [M][xs]
+    // finished (gate, up) sums waiting for the SwiGLU epilogue: up to
+    // kUpPend per wavefront, turned into activations 64 lanes at a time
+    float2 *s_gu = (float2 *)(smem + xbytes) + wave * kUpPend;
+    int *s_ai = (int *)((float2 *)(smem + xbytes) + WV * kUpPend) + wave * kUpPend;
+    // per-pair running sums over the K blocks of a unit (up to 16 pairs)
+    float2 *s_acc = (float2 *)((int *)((float2 *)(smem + xbytes) + WV * kUpPend) +
+                               WV * kUpPend) + wave * 16;
+
+    // ---- prologue: x (XR), pair ids, then the buckets
+    constexpr int kXr = XR ? KC * (W8 ? 2 : 1) : 1;
+    u32x4 xreg[kXr];                                     // XR: this lane's x chunks
+    if constexpr (XR) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            const int cp = c * kWave + lane;             // the lane's weight chunk c
+            if constexpr (W8) {
+                const int xc = min(2 * cp, nch - 2);     // clamped; zeroed below
+                xreg[2 * c] = x[xc];
+                xreg[2 * c + 1] = x[xc + 1];
+            } else {
+                xreg[c] = x[min(cp, nch - 1)];
+            }
+        }
+    }
+    int pid;                                             // this thread's pair's expert
+    if constexpr (SEL) {
+        // one wavefront per token: the slices' partial sums in slice order,
+        // then the bias, then the top-k and its softmax. The selection waits
+        // in the epilogue queues' LDS, unused until the units start.
+        int *s_sel = (int *)(smem + xbytes);
+        static_assert(kUpWaves * kUpPend * sizeof(float2) >= kMaxNP * sizeof(int), "room");
+        for (int t = wave; t < M; t += WV) {
+            float pv[kRouteSlicesMax][kSelKJ], bq[kSelKJ], lv[kSelKJ];
+#pragma unroll
+            for (int q = 0; q < kSelKJ; ++q) {           // all loads in flight together
+                const int e = lane + kWave * q, ec = e < E ? e : E - 1;
+#pragma unroll
+                for (int sl = 0; sl < kRouteSlicesMax; ++sl)
+                    if (sl < sel.nks)
+                        pv[sl][q] = sel.plog[((size_t)sl * M + t) * E + ec];
+                bq[q] = sel.bias ? sel.bias[ec] : 0.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < kSelKJ; ++q) {
+                float l = pv[0][q];
+#pragma unroll
+                for (int sl = 1; sl < kRouteSlicesMax; ++sl)
+                    if (sl < sel.nks)
+                        l += pv[sl][q];
+                lv[q] = l + bq[q];
+            }
+            int si;
+            float sw;
+            topk_select<kSelKJ>(lv, E, k, lane, si, sw);
+            if (lane < k) {
+                s_sel[t * k + lane] = si;
+                if (blockIdx.x == 0) {
+                    sel.topk_idx[(size_t)t * k + lane] = si;
+                    sel.topk_w[(size_t)t * k + lane] = sw;
+                }
+            }
+        }
+        lds_barrier();
+        const int p = threadIdx.x;
+        pid = p < NP ? s_sel[p] : (p < NPT ? E : -1);
+    } else {
+        pid = pair_expert(topk_idx, threadIdx.x, NP, NPT, E);
+    }
+    groups_set_pairs(pid, NPT, E + ns, g);
+    if (threadIdx.x == 0)
+        s_next = 0;
+    wait_vmcnt<0>();                                     // the pair id (and XR: x) is in
+    if constexpr (XR) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c)                     // the K tail of x reads as zero
+            if (c * kWave + lane >= nwc) {
+#pragma unroll
+                for (int i = 0; i < (W8 ? 2 : 1); ++i)
+                    xreg[c * (W8 ? 2 : 1) + i] = u32x4{0, 0, 0, 0};
+            }
+    } else {
+        for (int i = threadIdx.x; i < M * (xs - nch); i += blockDim.x) {
+            const int t = i / (xs - nch), c = nch + i % (xs - nch);
+            s_x[t * xs + c] = u32x4{0, 0, 0, 0};         // K padding reads as zero
+        }
+    }
+    groups_finish(NPT, g);                               // (its barriers also publish s_next)
+    if constexpr (!XR) {
+        stage_rows_lds(x, M, nch, s_x, xs);
+        wait_vmcnt<0>();                                 // this wave's share of x has landed
+        lds_barrier();                                   // ... and every other wave's
+    }
+
+    const int nunits = uniform(g.DV) * I;
+    const int nwg = nunits > (int)blockIdx.x ? (nunits - 1 - (int)blockIdx.x) / gridDim.x + 1 : 0;
+
+    int pend = 0;                                        // uniform
+    auto flush = [&]() {
+        if (lane < pend) {
+            const float2 v = s_gu[lane];
+            act[s_ai[lane]] = (uint16_t)f32_to_bf16_rne(v.x / (1.0f + expf(-v.x)) * v.y);
+        }
+        pend = 0;
+    };
+    auto claim = [&]() {                                 // uniform: a unit, or -1
+        int j = 0;
+        if (lane == 0)
+            j = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        j = uniform(__builtin_amdgcn_readlane(j, 0));
+        return j < nwg ? (int)blockIdx.x + (int)gridDim.x * j : -1;
+    };
+    // Tag of a block: unit * 16 + kb, or -1 past the end; a unit's K blocks
+    // stay on one wavefront
+    int cur_u = claim(), cur_kb = 0;
+    auto next_tag = [&]() {
+        int t = -1;
+        if (cur_u >= 0) {
+            t = cur_u * 16 + cur_kb;
+            if (++cur_kb == nbu) {
+                cur_kb = 0;
+                cur_u = claim();
+            }
+        }
+        return t;
+    };
+
+    // Block of a tag: KC loads of the gate row, KC of the up row. A -1 tag
+    // rereads the first kilobyte of W_gate instead, so every wait is one
+    // constant.
+    auto issue = [&](int tag, u32x4 (&dg)[KC], u32x4 (&du)[KC], float &sgv, float &suv) {
+        const bool real = tag >= 0;
+        const int u = real ? tag >> 4 : 0, kb = real ? tag & 15 : 0;
+        const int v = min(u / I, kMaxNP - 1), i = u % I;
+        const int ev = uniform(g.vexp[v]);
+        const bool sh = real && ev >= E;                 // the shared expert's slabs
+        const size_t row = real ? (size_t)(sh ? 0 : ev) * I + i : 0;   // row in its tensor
+        const size_t roff = row * nwc;
+        const u32x4 *bg = sh ? wgs + roff : wg + roff;   // uniform
+        const u32x4 *bu = sh ? wus + roff : wu + roff;
+        if constexpr (W8) {                              // the rows' scales (uniform)
+            sgv = sg[row];
+            suv = su[row];
+        }
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            int ch = (kb * KC + c) * kWave + lane;
+            ch = ch < nwc ? ch : nwc - 1;                // K tail: zeroed before use
+            int off = real ? ch : min(lane, nwc - 1);
+            asm volatile("" : "+v"(off));                // one load on one path: no branch
+            dg[c] = load_stream(bg + off);
+            du[c] = load_stream(bu + off);
+        }
+    };
+    auto consume = [&](int tag, u32x4 (&dg)[KC], u32x4 (&du)[KC], float sgv, float suv) {
+        const int u = tag >> 4, kb = tag & 15;
+        const int v = u / I, i = u % I;
+        const int npair = uniform(g.vcnt[v]);
+        const int pb = uniform(g.vbeg[v]);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            if ((kb * KC + c) * kWave + kWave > nwc) {   // uniform: the K tail
+                const bool ok = (kb * KC + c) * kWave + lane < nwc;
+                dg[c] = ok ? dg[c] : u32x4{0, 0, 0, 0};
+                du[c] = ok ? du[c] : u32x4{0, 0, 0, 0};
+            }
+        }
+        for (int jj = 0; jj < npair; ++jj) {
+            const int p = uniform(g.sorted[pb + jj]);
+            float ga = 0.0f, ua = 0.0f;
+            if constexpr (W8) {
+                // chunk c holds columns 16 ch .. 16 ch + 15: x chunks 2 ch, 2 ch + 1
+                const u32x4 *xr = s_x + pair_token(p, NP, k) * xs + 2 * (kb * KC * kWave + lane);
+#pragma unroll
+                for (int c = 0; c < KC; ++c) {
+                    const u32x4 x0 = XR ? xreg[2 * c % kXr] : xr[2 * c * kWave];
+                    const u32x4 x1 = XR ? xreg[(2 * c + 1) % kXr] : xr[2 * c * kWave + 1];
+                    ga = dot8_bf16(e4m3x8_to_bf16(dg[c].x, dg[c].y), x0, ga);
+                    ga = dot8_bf16(e4m3x8_to_bf16(dg[c].z, dg[c].w), x1, ga);
+                    ua = dot8_bf16(e4m3x8_to_bf16(du[c].x, du[c].y), x0, ua);
+                    ua = dot8_bf16(e4m3x8_to_bf16(du[c].z, du[c].w), x1, ua);
+                }
+            } else {
+                const u32x4 *xr = s_x + pair_token(p, NP, k) * xs + kb * KC * kWave + lane;
+#pragma unroll
+                for (int c = 0; c < KC; ++c) {
+                    const u32x4 xv = XR ? xreg[c % kXr] : xr[c * kWave];
+                    ga = dot8_bf16(dg[c], xv, ga);
+                    ua = dot8_bf16(du[c], xv, ua);
+                }
+            }
+            float gt = wave_total(ga), ut = wave_total(ua);
+            if (nbu > 1) {                               // uniform
+                if (kb > 0) {
+                    const float2 a = s_acc[jj];
+                    gt = a.x + gt;
+                    ut = a.y + ut;
+                }
+                if (kb < nbu - 1) {
+                    if (lane == 0)
+                        s_acc[jj] = make_float2(gt, ut);
+                    continue;
+                }
+            }
+            if constexpr (W8) {                          // the rows' scales
+                gt *= sgv;
+                ut *= suv;
+            }
+            // queued for the epilogue (lane 0 writes, the wavefront reads)
+            if (lane == 0) {
+                s_gu[pend] = make_float2(gt, ut);
+                s_ai[pend] = p * I + i;
+            }
+            if (++pend == kUpPend)
+                flush();
+        }
+    };
+
+    u32x4 wgr[KC], wur[KC];
+    float sgr = 0.0f, sur = 0.0f;                        // fp8 row scales (unused for bf16)
+    for (;;) {
+        const int tg = next_tag();
+        issue(tg, wgr, wur, sgr, sur);
+        wait_vmcnt<0>();                                 // the block has landed
+        if (tg < 0)                                      // uniform: nothing left
+            break;
+        consume(tg, wgr, wur, sgr, sur);
+    }
+    flush();                                             // the last queued outputs
+}
+
+// ---------------------------------------------------------- down (GEMV)
+// The down projection at verify widths: with distinct experts per token a
+// column block holds about one pair. The weights stream straight into
+// registers -- one 1 KB load per row per K block (lane i takes 16-byte chunk
+// i) -- together with the activation chunks of the column block's first
+// pairs (from L2), and each wavefront waits for the block it issued before
+// it consumes it; the other wavefronts of the CU keep the loads flowing.
+// Per (pair, K block) every lane forms R eight-element dot products
+// (v_dot2_f32_bf16) and each row is summed over the wavefront in a fixed DPP
+// tree; the block sums are added over K blocks in order in the combine.
+// Workgroup b owns rows r0 .. r0+R-1 of every expert; its wavefronts claim
+// the (column block, K block) blocks one at a time from an LDS counter.
+
 // K blocks of a W_down row: kDnCh 16-byte chunks, 512 bf16 or 1024 fp8
 // columns
 __host__ __device__ inline int down_gemv_nkb(int I, bool w8)
@@ -415,8 +729,8 @@ __host__ __device__ inline size_t down_gemv_lds_bytes(int R, int NPT, int I, boo
     return (size_t)NPT * (down_gemv_nkb(I, w8) * R + 1) * sizeof(float);
 }
 // activation chunks of the first kDnPre pairs of a column block are loaded
-// together with the block's weights; further pairs (rare at these widths)
-// are loaded when they are reached
+// together with the block's weights; further pairs are loaded when they are
+// reached
 constexpr int kDnPre = 2;
 static_assert(kDnPre == 2, "the pair select in the GEMV down kernel takes two");
 
@@ -574,371 +888,26 @@ __global__ __launch_bounds__(WV * kWave) void expert_down_gemv_kernel(
     }
 }
 
-// ------------------------------------------------------------ up (GEMV)
-// LDS bytes of the up GEMV's x copy: M rows of whole K blocks
-__host__ __device__ inline size_t up_gemv_x_bytes(int M, int H, int KC, bool w8)
-{
-    const int nwc = w8 ? H / 16 : H / 8;
-    const int nbu = (nwc + KC * kWave - 1) / (KC * kWave);
-    return align_up((size_t)M * nbu * KC * kWave * (w8 ? 2 : 1) * 16, 256);
-}
-
-// The up projection at verify widths is a set of matrix-vector products as
-// well: a selected expert serves about one pair. Units are (column block v,
-// row i of I): the unit's gate row and up row, KC chunks of 16 bytes per
-// lane each (lane l takes chunks l, l+64, ...: 1 KB contiguous per load),
-// stream straight into registers through an NB-deep register ring; x sits in
-// LDS, staged once per workgroup. For every pair of the column block each
-// lane forms its gate and up partial dot products (v_dot2_f32_bf16), two
-// fixed DPP trees sum them over the wavefront, and the SwiGLU product is
-// taken in fp32 and rounded once to bf16. With more than KC * 64 chunks per
-// row a unit spans several K blocks; the per-block sums of each pair are
-// added in LDS in block order.
-// W8: fp8 weights (E4M3 codes, 16 per 16-byte chunk, an fp32 scale per
-// row in sg / su); each chunk is widened to two bf16 chunks that meet two x
-// chunks, and the row scales multiply the reduced sums before the SwiGLU.
-// XR (one token, one K block per unit): the lane's x chunks are the same
-// for every unit, so they are loaded once into registers at the start (no
-// LDS staging, no wait on it before the first weights go out).
-template <int KC, int NB, bool W8, int WV, bool CLAIM, bool XR>
-__global__ __launch_bounds__(WV * kWave) void expert_up_gemv_kernel(
-    const u32x4 *__restrict__ x, const int *__restrict__ topk_idx,
-    const u32x4 *__restrict__ wg, const u32x4 *__restrict__ wu,
-    const u32x4 *__restrict__ wgs, const u32x4 *__restrict__ wus,
-    const float *__restrict__ sg, const float *__restrict__ su, int M, int H,
-    int I, int E, int k, int ns, uint16_t *__restrict__ act)
-{
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    __shared__ Groups g;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = uniform(threadIdx.x / kWave);
-    const int nch = H / 8;                               // 16-byte x chunks per row
-    const int nwc = W8 ? H / 16 : nch;                   // 16-byte weight chunks per row
-    const int nbu = (nwc + KC * kWave - 1) / (KC * kWave);   // K blocks per unit
-    const int xs = nbu * KC * kWave * (W8 ? 2 : 1);      // LDS x row, chunks
-    const int NP = M * k, NPT = NP + ns * M;
-    u32x4 *s_x = (u32x4 *)smem;                          // [M][xs]
-    // finished (gate, up) sums waiting for the SwiGLU epilogue: up to
-    // kUpPend per wavefront, turned into activations 64 lanes at a time
-    float2 *s_gu = (float2 *)(smem + up_gemv_x_bytes(M, H, KC, W8)) + wave * kUpPend;
-    int *s_ai = (int *)((float2 *)(smem + up_gemv_x_bytes(M, H, KC, W8)) + WV * kUpPend) +
-                wave * kUpPend;
-    // per-pair running sums over the K blocks of a unit (up to 16 pairs)
-    float2 *s_acc = (float2 *)((int *)((float2 *)(smem + up_gemv_x_bytes(M, H, KC, W8)) +
-                                       WV * kUpPend) + WV * kUpPend) + wave * 16;
-    int pend = 0;                                        // uniform
-    auto flush = [&]() {
-        // SwiGLU in fp32, one rounding to bf16, one output per lane
-        if (lane < pend) {
-            const float2 v = s_gu[lane];
-            act[s_ai[lane]] = (uint16_t)f32_to_bf16_rne(v.x / (1.0f + expf(-v.x)) * v.y);
-        }
-        pend = 0;
-    };
-
-    __shared__ int s_next;                               // the workgroup's next unit to claim
-    constexpr int kXr = XR ? KC * (W8 ? 2 : 1) : 1;
-    u32x4 xreg[kXr];                                     // XR: this lane's x chunks
-    if constexpr (XR) {
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            const int cp = c * kWave + lane;             // the lane's weight chunk c
-            if constexpr (W8) {
-                const int xc = min(2 * cp, nch - 2);     // clamped; zeroed below
-                xreg[2 * c] = x[xc];
-                xreg[2 * c + 1] = x[xc + 1];
-            } else {
-                xreg[c] = x[min(cp, nch - 1)];
-            }
-        }
-    }
-    groups_set_pairs(pair_expert(topk_idx, threadIdx.x, NP, NPT, E), NPT, E + ns, g);
-    if (threadIdx.x == 0)
-        s_next = 0;
-    wait_vmcnt<0>();                                     // the pair id (and XR: x) is in
-    if constexpr (XR) {
-#pragma unroll
-        for (int c = 0; c < KC; ++c)                     // the K tail of x reads as zero
-            if (c * kWave + lane >= nwc) {
-#pragma unroll
-                for (int i = 0; i < (W8 ? 2 : 1); ++i)
-                    xreg[c * (W8 ? 2 : 1) + i] = u32x4{0, 0, 0, 0};
-            }
-    } else {
-        for (int i = threadIdx.x; i < M * (xs - nch); i += blockDim.x) {
-            const int t = i / (xs - nch), c = nch + i % (xs - nch);
-            s_x[t * xs + c] = u32x4{0, 0, 0, 0};         // K padding reads as zero
-        }
-    }
-    groups_finish(NPT, g);                               // (its barriers also publish s_next)
-
-    // ---- Units in order (column block v, row i): the chip streams one moving
-    // window of the weights. Tag of a block: unit * 16 + kb, or -1 past the
-    // end. A unit's K blocks stay on one wavefront.
-    // CLAIM: the workgroup's units are b, b + grid, b + 2 grid, ...; its
-    // wavefronts claim them one at a time from an LDS counter, so a wavefront
-    // that its SIMD's arbitration serves less often (the younger of the
-    // SIMD's wavefronts) simply takes fewer units.
-    // Static: unit u runs on wavefront u mod (WV * grid).
-    const int nunits = uniform(g.DV) * I;
-    const int nwg = nunits > (int)blockIdx.x ? (nunits - 1 - (int)blockIdx.x) / gridDim.x + 1 : 0;
-    auto claim = [&]() {                                 // uniform: a unit, or -1
-        int j = 0;
-        if (lane == 0)
-            j = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        j = uniform(__builtin_amdgcn_readlane(j, 0));
-        return j < nwg ? (int)blockIdx.x + (int)gridDim.x * j : -1;
-    };
-    const int GW = gridDim.x * WV;
-    const int gw = blockIdx.x * WV + wave;
-    const int nblk = nunits > gw ? ((nunits - 1 - gw) / GW + 1) * nbu : 0;   // static: this wavefront's blocks
-    int X = 0;                                           // static: the next block
-    int cur_u = CLAIM ? claim() : -1, cur_kb = 0;        // claims: the next block to issue
-    auto next_tag = [&]() {
-        int t = -1;
-        if constexpr (!CLAIM) {
-            t = X < nblk ? (gw + GW * (X / nbu)) * 16 + X % nbu : -1;
-            ++X;
-        } else if (cur_u >= 0) {
-            t = cur_u * 16 + cur_kb;
-            if (++cur_kb == nbu) {
-                cur_kb = 0;
-                cur_u = claim();
-            }
-        }
-        return t;
-    };
-
-    // Block of a tag: KC loads of the gate row, KC of the up row. A -1 tag
-    // rereads the first kilobyte of W_gate instead, so every wait is one
-    // constant.
-    auto issue = [&](int tag, u32x4 (&dg)[KC], u32x4 (&du)[KC], float &sgv, float &suv) {
-        const bool real = tag >= 0;
-        const int u = real ? tag >> 4 : 0, kb = real ? tag & 15 : 0;
-        const int v = min(u / I, kMaxNP - 1), i = u % I;
-        const int ev = uniform(g.vexp[v]);
-        const bool sh = real && ev >= E;                 // the shared expert's slabs
-        const size_t row = real ? (size_t)(sh ? 0 : ev) * I + i : 0;   // row in its tensor
-        const size_t roff = row * nwc;
-        const u32x4 *bg = sh ? wgs + roff : wg + roff;   // uniform
-        const u32x4 *bu = sh ? wus + roff : wu + roff;
-        if constexpr (W8) {                              // the rows' scales (uniform)
-            sgv = sg[row];
-            suv = su[row];
-        }
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            int ch = (kb * KC + c) * kWave + lane;
-            ch = ch < nwc ? ch : nwc - 1;                // K tail: zeroed before use
-            int off = real ? ch : min(lane, nwc - 1);
-            asm volatile("" : "+v"(off));                // one load on one path: no branch
-            dg[c] = load_stream(bg + off);
-            du[c] = load_stream(bu + off);
-        }
-    };
-    auto consume = [&](int tag, u32x4 (&dg)[KC], u32x4 (&du)[KC], float sgv, float suv) {
-        const int u = tag >> 4, kb = tag & 15;
-        const int v = u / I, i = u % I;
-        const int npair = uniform(g.vcnt[v]);
-        const int pb = uniform(g.vbeg[v]);
-#pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            if ((kb * KC + c) * kWave + kWave > nwc) {   // uniform: the K tail
-                const bool ok = (kb * KC + c) * kWave + lane < nwc;
-                dg[c] = ok ? dg[c] : u32x4{0, 0, 0, 0};
-                du[c] = ok ? du[c] : u32x4{0, 0, 0, 0};
-            }
-        }
-        for (int jj = 0; jj < npair; ++jj) {
-            const int p = uniform(g.sorted[pb + jj]);
-            float ga = 0.0f, ua = 0.0f;
-            if constexpr (W8) {
-                // chunk c holds columns 16 ch .. 16 ch + 15: x chunks 2 ch, 2 ch + 1
-                const u32x4 *xr = s_x + pair_token(p, NP, k) * xs + 2 * (kb * KC * kWave + lane);
-#pragma unroll
-                for (int c = 0; c < KC; ++c) {
-                    const u32x4 x0 = XR ? xreg[2 * c % kXr] : xr[2 * c * kWave];
-                    const u32x4 x1 = XR ? xreg[(2 * c + 1) % kXr] : xr[2 * c * kWave + 1];
-                    ga = dot8_bf16(e4m3x8_to_bf16(dg[c].x, dg[c].y), x0, ga);
-                    ga = dot8_bf16(e4m3x8_to_bf16(dg[c].z, dg[c].w), x1, ga);
-                    ua = dot8_bf16(e4m3x8_to_bf16(du[c].x, du[c].y), x0, ua);
-                    ua = dot8_bf16(e4m3x8_to_bf16(du[c].z, du[c].w), x1, ua);
-                }
-            } else {
-                const u32x4 *xr = s_x + pair_token(p, NP, k) * xs + kb * KC * kWave + lane;
-#pragma unroll
-                for (int c = 0; c < KC; ++c) {
-                    const u32x4 xv = XR ? xreg[c % kXr] : xr[c * kWave];
-                    ga = dot8_bf16(dg[c], xv, ga);
-                    ua = dot8_bf16(du[c], xv, ua);
-                }
-            }
-            float gt = wave_total(ga), ut = wave_total(ua);
-            if (nbu > 1) {                               // uniform
-                if (kb > 0) {
-                    const float2 a = s_acc[jj];
-                    gt = a.x + gt;
-                    ut = a.y + ut;
-                }
-                if (kb < nbu - 1) {
-                    if (lane == 0)
-                        s_acc[jj] = make_float2(gt, ut);
-                    continue;
-                }
-            }
-            if constexpr (W8) {                          // the rows' scales
-                gt *= sgv;
-                ut *= suv;
-            }
-            // queued for the epilogue (lane 0 writes, the wavefront reads)
-            if (lane == 0) {
-                s_gu[pend] = make_float2(gt, ut);
-                s_ai[pend] = p * I + i;
-            }
-            if (++pend == kUpPend)
-                flush();
-        }
-    };
-
-    u32x4 wgr[NB][KC], wur[NB][KC];
-    float sgr[NB] = {}, sur[NB] = {};                    // fp8 row scales (unused for bf16)
-    int tg[NB];                                          // tags of the ring's blocks
-#pragma unroll
-    for (int q = 0; q < NB - 1; ++q) {
-        tg[q] = next_tag();
-        issue(tg[q], wgr[q], wur[q], sgr[q], sur[q]);
-    }
-    if constexpr (!XR) {
-        stage_rows_lds(x, M, nch, s_x, xs);
-        wait_vmcnt<0>();                                 // this wave's share of x has landed
-        lds_barrier();                                   // ... and every other wave's
-    }
-    for (bool live = true; live;) {
-#pragma unroll
-        for (int q = 0; q < NB; ++q) {
-            const int nq = (q + NB - 1) % NB;
-            tg[nq] = next_tag();
-            issue(tg[nq], wgr[nq], wur[nq], sgr[nq], sur[nq]);
-            wait_vmcnt<(NB - 1) * 2 * KC>();             // block q has landed
-            if (tg[q] < 0) {                             // uniform: nothing left
-                live = false;
-                break;
-            }
-            consume(tg[q], wgr[q], wur[q], sgr[q], sur[q]);
-        }
-    }
-    wait_vmcnt<0>();                                     // dummy loads have landed
-    flush();
-}
-
-// x of the M tokens, then, for each of the wv wavefronts, its queue of
-// finished sums and its 16 running sums
-__host__ __device__ inline size_t up_gemv_lds_bytes(int M, int H, int KC, bool w8, int wv)
-{
-    return up_gemv_x_bytes(M, H, KC, w8) +
-           (size_t)wv * (kUpPend * (sizeof(float2) + 4) + 16 * sizeof(float2));
-}
-
 // ------------------------------------------------------------------ host
 
-// GEMV up kernel: KC 16-byte chunks per lane per row and block (a unit is
-// one block when a row has at most 5 * 64 chunks), streamed through a
-// register ring of NB blocks (NB - 1 in flight while one is consumed).
-// Shallow rings measured faster at every width (static split, M=6: 3 blocks
-// ahead 77.7 us, 1 ahead 75.6; fp8 M=1: 5 ahead 18.2 us, 1 ahead 14.3): with
-// eight or more wavefronts per CU extra loads in flight only lengthen every
-// load's wait.
-// The default: one workgroup of twelve wavefronts per CU (three per SIMD)
-// that claim units from an LDS counter, no block ahead. A SIMD serves its
-// older wavefront first (with a static split the younger wavefronts of a CU
-// ended 15 us after the older ones at M=6, 40 us at M=16); with claims they
-// all end within about one unit. Against the static split on eight
-// wavefronts: M=6 75.9 against 76.8 us, M=16 181.0 against 187.8, fp8 M=6
-// 41.0 against 43.5, fp8 M=1 12.5 against 13.3.
-constexpr int kUpClaimWaves = 12;
-constexpr int kUpClaimNB = 1;
-// bf16 at M = 1: two four-wavefront workgroups per CU with the static split
-// and one block ahead (17.8 us, against 18.6 with claims)
-constexpr int kUpGemvNB = 2;
+// up: KC 16-byte chunks per lane per row and block (a unit is one block when
+// a row has at most 5 * 64 chunks)
 static int up_gemv_kc(int H, bool w8)
 {
     const int need = ((w8 ? H / 16 : H / 8) + kWave - 1) / kWave;
     return need <= 5 ? need : 4;
 }
-static bool up_gemv_fits(int M, int H, bool w8)
+// one token and one K block per unit: x in registers
+static bool up_xr(int M, int H, bool w8)
 {
-    return up_gemv_lds_bytes(M, H, up_gemv_kc(H, w8), w8, kUpClaimWaves) <= (size_t)kXLdsDynMax;
+    return M == 1 && (w8 ? H / 16 : H / 8) <= up_gemv_kc(H, w8) * kWave;
 }
-
-// The experts of one call: routed weights and, when ns = 1, the shared
-// expert's (gate [I,H], up [I,H], down [H,I]).
-// With w8 the routed tensors are fp8 codes with per-row scales sg, su, sd.
-struct Experts {
-    const void *wg, *wu, *wd;
-    const uint16_t *wgs, *wus, *wds;
-    int ns;
-    bool w8;
-    const float *sg, *su, *sd;
-};
-
-// Several wavefronts per SIMD hide each other's per-unit latency (the group
-// lookups, the reductions, the epilogue) and keep the loads of one flowing
-// while another computes.
-template <int KC, int NB, bool W8, int WV, bool CLAIM, bool XR>
-static void launch_up_gemv_wv(int grid, size_t lds, const uint16_t *x, const int *idx,
-                              const Experts &ex, int M, int H, int I, int E, int k,
-                              uint16_t *act, hipStream_t st)
+// rows of W_down per down workgroup: 256 workgroups at H = 2560; fp8 keeps
+// 10 (16 rows of widened codes do not fit the registers of twelve
+// wavefronts)
+static int down_rows(int H, bool w8)
 {
-    hipLaunchKernelGGL((expert_up_gemv_kernel<KC, NB, W8, WV, CLAIM, XR>), dim3(grid),
-                       dim3(WV * kWave), lds, st, (const u32x4 *)x, idx, (const u32x4 *)ex.wg,
-                       (const u32x4 *)ex.wu, (const u32x4 *)ex.wgs, (const u32x4 *)ex.wus, ex.sg,
-                       ex.su, M, H, I, E, k, ex.ns, act);
-}
-template <int KC, bool W8>
-static void launch_up_gemv(const uint16_t *x, const int *idx, const Experts &ex, int M, int H,
-                           int I, int E, int k, uint16_t *act, hipStream_t st)
-{
-    // (the supported shapes always fit: up_gemv_fits; one token's two
-    // workgroups per CU hold less than the twelve-wavefront one)
-    const size_t lds4 = up_gemv_lds_bytes(M, H, KC, W8, 4);
-    const size_t lds12 = up_gemv_lds_bytes(M, H, KC, W8, kUpClaimWaves);
-    // one token and one K block per unit: x in registers
-    const bool xr = M == 1 && (W8 ? H / 16 : H / 8) <= KC * kWave;
-    if (!W8 && M == 1 && xr)
-        launch_up_gemv_wv<KC, kUpGemvNB, false, 4, false, true>(2 * kXGrid, lds4, x, idx, ex, M,
-                                                                H, I, E, k, act, st);
-    else if (!W8 && M == 1)
-        launch_up_gemv_wv<KC, kUpGemvNB, false, 4, false, false>(2 * kXGrid, lds4, x, idx, ex, M,
-                                                                 H, I, E, k, act, st);
-    else if (xr)
-        launch_up_gemv_wv<KC, kUpClaimNB, W8, kUpClaimWaves, true, true>(
-            kXGrid, lds12, x, idx, ex, M, H, I, E, k, act, st);
-    else
-        launch_up_gemv_wv<KC, kUpClaimNB, W8, kUpClaimWaves, true, false>(
-            kXGrid, lds12, x, idx, ex, M, H, I, E, k, act, st);
-}
-template <bool W8>
-static void launch_up_gemv_kc(const uint16_t *x, const int *idx, const Experts &ex, int M,
-                              int H, int I, int E, int k, uint16_t *act, hipStream_t st)
-{
-    switch (up_gemv_kc(H, W8)) {
-    case 1: launch_up_gemv<1, W8>(x, idx, ex, M, H, I, E, k, act, st); break;
-    case 2: launch_up_gemv<2, W8>(x, idx, ex, M, H, I, E, k, act, st); break;
-    case 3: launch_up_gemv<3, W8>(x, idx, ex, M, H, I, E, k, act, st); break;
-    case 4: launch_up_gemv<4, W8>(x, idx, ex, M, H, I, E, k, act, st); break;
-    default: launch_up_gemv<5, W8>(x, idx, ex, M, H, I, E, k, act, st); break;
-    }
-}
-
-// rows per down workgroup: at least ceil(H / 256), from the instantiated set
-static int down_rows(int H)
-{
-    const int need = (H + kXGrid - 1) / kXGrid;
-    const int opts[] = {4, 8, 10, 12, 16};
-    for (int r : opts)
-        if (r >= need)
-            return r;
-    return 0;
+    return H <= 2560 || w8 ? 10 : 16;
 }
 // GEMV down kernel: eight claiming wavefronts per CU (twelve for fp8), each
 // waiting for the block it just issued (no block ahead: more wavefronts keep
@@ -948,15 +917,14 @@ static int down_rows(int H)
 // 15.7).
 constexpr int kDnGemvWaves = 8;
 constexpr int kDnGemvWaves8 = 12;
-// The GEMV down kernel serves the widths whose pairs' activation rows would
-// fit in LDS (NPT pairs: M*k routed, plus M with a shared expert; M <= 9 at
-// I = 1024, k = 8), where a column block holds about one pair; wider bf16
-// calls take the MFMA kernel.
-static bool down_gemv_fits(int R, int NPT, int I, bool w8)
+// The GEMV down kernel serves every fp8 call and the bf16 calls whose pairs'
+// activations stay below kGemvActMax bytes (M <= 9 at I = 1024, k = 8):
+// there a column block holds about one pair. Wider bf16 calls take the MFMA
+// kernel (several pairs per column block: a contraction).
+constexpr size_t kGemvActMax = 150 * 1024;
+static bool use_down_gemv(int NPT, int I, bool w8)
 {
-    const size_t rows =
-        align_up((size_t)NPT * down_gemv_nkb(I, w8) * kDnCh * (w8 ? 2 : 1) * 16, 256);
-    return rows + down_gemv_lds_bytes(R, NPT, I, w8) <= (size_t)kXLdsDynMax;
+    return w8 || (size_t)NPT * I * 2 <= kGemvActMax;
 }
 static size_t down_lds_bytes(int R, int NB, int WV, int NPT)
 {
@@ -970,12 +938,18 @@ static size_t down_lds_bytes(int R, int NB, int WV, int NPT)
 // but their slots do not fit at R = 16).
 constexpr int kDnMfmaNB = 1;
 constexpr int kDnMfmaWaves = 8;
-static_assert(4 * kWave >= kGroupThreads && kUpClaimWaves * kWave >= kGroupThreads &&
-                  kDnGemvWaves * kWave >= kGroupThreads &&
+static_assert(kUpWaves * kWave >= kGroupThreads && kDnGemvWaves * kWave >= kGroupThreads &&
                   kDnGemvWaves8 * kWave >= kGroupThreads && kDnMfmaWaves * kWave >= kGroupThreads,
               "the grouping needs a thread per histogram slice");
-static bool down_mfma_fits(int R, int NPT)
+// Whether a call's shapes fit the LDS of the kernels that would serve it.
+static bool ffn_supported(int M, int H, int I, int NPT, bool w8)
 {
+    const int KC = up_gemv_kc(H, w8);
+    if (up_lds_bytes(M, H, KC, w8, up_xr(M, H, w8)) > (size_t)kXLdsDynMax)
+        return false;
+    const int R = down_rows(H, w8);
+    if (use_down_gemv(NPT, I, w8))
+        return down_gemv_lds_bytes(R, NPT, I, w8) <= (size_t)kXLdsDynMax;
     return down_lds_bytes(R, kDnMfmaNB, kDnMfmaWaves, NPT) <= (size_t)kXLdsDynMax;
 }
 
@@ -999,8 +973,7 @@ static moe_status_t ffn_check(const uint16_t *x, const int32_t *topk_idx,
         return s;
     if (I < 1)
         return MOE_ERR_SHAPE;
-    if (I % 8 != 0 || I > kMaxDim || !up_gemv_fits(M, H, false) || down_rows(H) == 0 ||
-        !down_mfma_fits(down_rows(H), M * k))
+    if (I % 8 != 0 || I > kMaxDim || !ffn_supported(M, H, I, M * k, false))
         return MOE_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) ||
         !aligned16(w_down) || !aligned4(topk_idx) || !aligned4(topk_w) ||
@@ -1016,24 +989,89 @@ static hipError_t allow_lds(K kernel)
                                hipFuncAttributeMaxDynamicSharedMemorySize, kXLdsDynMax);
 }
 
+template <int KC>
+static void up_attr(hipError_t &e)
+{
+    for (hipError_t r : {allow_lds(expert_up_kernel<KC, false, false, false>),
+                         allow_lds(expert_up_kernel<KC, false, true, false>),
+                         allow_lds(expert_up_kernel<KC, true, false, false>),
+                         allow_lds(expert_up_kernel<KC, true, true, false>),
+                         allow_lds(expert_up_kernel<KC, false, false, true>),
+                         allow_lds(expert_up_kernel<KC, false, true, true>),
+                         allow_lds(expert_up_kernel<KC, true, false, true>),
+                         allow_lds(expert_up_kernel<KC, true, true, true>)})
+        if (r != hipSuccess)
+            e = r;
+}
 static hipError_t set_lds_attributes()
 {
     hipError_t e = hipSuccess;
-    auto chk = [&](hipError_t r) { if (r != hipSuccess) e = r; };
-#define MV_UP_ATTR(KC) chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false, 4, false, false>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpGemvNB, false, 4, false, true>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, false, kUpClaimWaves, true, false>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, false, kUpClaimWaves, true, true>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, true, kUpClaimWaves, true, false>)); \
-    chk(allow_lds(expert_up_gemv_kernel<KC, kUpClaimNB, true, kUpClaimWaves, true, true>));
-    MV_UP_ATTR(1) MV_UP_ATTR(2) MV_UP_ATTR(3) MV_UP_ATTR(4) MV_UP_ATTR(5)
-#undef MV_UP_ATTR
-#define MV_DOWN_ATTR(R) chk(allow_lds(expert_down_kernel<R, kDnMfmaNB, kDnMfmaWaves>)); \
-    chk(allow_lds(expert_down_gemv_kernel<R, false, kDnGemvWaves>)); \
-    chk(allow_lds(expert_down_gemv_kernel<R, true, kDnGemvWaves8>));
-    MV_DOWN_ATTR(4) MV_DOWN_ATTR(8) MV_DOWN_ATTR(10) MV_DOWN_ATTR(12) MV_DOWN_ATTR(16)
-#undef MV_DOWN_ATTR
+    up_attr<1>(e);
+    up_attr<2>(e);
+    up_attr<3>(e);
+    up_attr<4>(e);
+    up_attr<5>(e);
+    for (hipError_t r : {allow_lds(expert_down_kernel<10, kDnMfmaNB, kDnMfmaWaves>),
+                         allow_lds(expert_down_kernel<16, kDnMfmaNB, kDnMfmaWaves>),
+                         allow_lds(expert_down_gemv_kernel<10, false, kDnGemvWaves>),
+                         allow_lds(expert_down_gemv_kernel<16, false, kDnGemvWaves>),
+                         allow_lds(expert_down_gemv_kernel<10, true, kDnGemvWaves8>)})
+        if (r != hipSuccess)
+            e = r;
     return e;
+}
+
+// The experts of one call: routed weights and, when ns = 1, the shared
+// expert's (gate [I,H], up [I,H], down [H,I]).
+// With w8 the routed tensors are fp8 codes with per-row scales sg, su, sd.
+struct Experts {
+    const void *wg, *wu, *wd;
+    const uint16_t *wgs, *wus, *wds;
+    int ns;
+    bool w8;
+    const float *sg, *su, *sd;
+};
+
+// Workgroups of the up kernel: one per CU, 256 on an MI355X; each asks for
+// more than half of a CU's LDS, so that no CU takes two while another
+// takes none.
+constexpr int kUpGrid = 256;
+constexpr size_t kOneWgLds = 81 * 1024;
+
+template <int KC, bool W8, bool XR>
+static void launch_up3(size_t lds, const uint16_t *x, const int *idx, const Experts &ex, int M,
+                       int H, int I, int E, int k, uint16_t *act, const UpSelect *sel,
+                       hipStream_t st)
+{
+    if (sel)
+        hipLaunchKernelGGL((expert_up_kernel<KC, W8, XR, true>), dim3(kUpGrid),
+                           dim3(kUpWaves * kWave), lds, st, (const u32x4 *)x, idx,
+                           (const u32x4 *)ex.wg, (const u32x4 *)ex.wu, (const u32x4 *)ex.wgs,
+                           (const u32x4 *)ex.wus, ex.sg, ex.su, M, H, I, E, k, ex.ns, act, *sel);
+    else
+        hipLaunchKernelGGL((expert_up_kernel<KC, W8, XR, false>), dim3(kUpGrid),
+                           dim3(kUpWaves * kWave), lds, st, (const u32x4 *)x, idx,
+                           (const u32x4 *)ex.wg, (const u32x4 *)ex.wu, (const u32x4 *)ex.wgs,
+                           (const u32x4 *)ex.wus, ex.sg, ex.su, M, H, I, E, k, ex.ns, act,
+                           UpSelect{});
+}
+template <bool W8>
+static void launch_up(const uint16_t *x, const int *idx, const Experts &ex, int M, int H, int I,
+                      int E, int k, uint16_t *act, const UpSelect *sel, hipStream_t st)
+{
+    const int KC = up_gemv_kc(H, W8);
+    const bool xr = up_xr(M, H, W8);
+    const size_t lds = max(up_lds_bytes(M, H, KC, W8, xr), kOneWgLds);
+#define MV_UP(KC_) (xr ? launch_up3<KC_, W8, true>(lds, x, idx, ex, M, H, I, E, k, act, sel, st) \
+                       : launch_up3<KC_, W8, false>(lds, x, idx, ex, M, H, I, E, k, act, sel, st))
+    switch (KC) {
+    case 1: MV_UP(1); break;
+    case 2: MV_UP(2); break;
+    case 3: MV_UP(3); break;
+    case 4: MV_UP(4); break;
+    default: MV_UP(5); break;
+    }
+#undef MV_UP
 }
 
 template <int R>
@@ -1043,16 +1081,19 @@ static void launch_down_gemv(const uint16_t *act, const int *idx, const float *t
 {
     const int grid = (H + R - 1) / R;
     const size_t lds = down_gemv_lds_bytes(R, M * k + ex.ns * M, I, ex.w8);
-    if (ex.w8)
-        hipLaunchKernelGGL((expert_down_gemv_kernel<R, true, kDnGemvWaves8>),
-                           dim3(grid), dim3(kDnGemvWaves8 * kWave), lds, st, (const u32x4 *)act,
-                           idx, tw, (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, ex.sd, M, H, I,
-                           E, k, ex.ns, out);
-    else
-        hipLaunchKernelGGL((expert_down_gemv_kernel<R, false, kDnGemvWaves>),
-                           dim3(grid), dim3(kDnGemvWaves * kWave), lds, st, (const u32x4 *)act,
-                           idx, tw, (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, nullptr, M, H, I,
-                           E, k, ex.ns, out);
+    if constexpr (R == 10) {
+        if (ex.w8) {
+            hipLaunchKernelGGL((expert_down_gemv_kernel<R, true, kDnGemvWaves8>), dim3(grid),
+                               dim3(kDnGemvWaves8 * kWave), lds, st, (const u32x4 *)act, idx,
+                               tw, (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, ex.sd, M, H, I,
+                               E, k, ex.ns, out);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((expert_down_gemv_kernel<R, false, kDnGemvWaves>), dim3(grid),
+                       dim3(kDnGemvWaves * kWave), lds, st, (const u32x4 *)act, idx, tw,
+                       (const u32x4 *)ex.wd, (const u32x4 *)ex.wds, nullptr, M, H, I, E, k,
+                       ex.ns, out);
 }
 
 template <int R>
@@ -1068,48 +1109,42 @@ static void launch_down_r(const uint16_t *act, const int *idx, const float *tw,
                        (const u32x4 *)ex.wds, M, H, I, E, k, ex.ns, out);
 }
 
+// ws: the workspace (its header of counters at the start); data: where the
+// caller's layout puts the activations
+// sel: the router's selection runs in the up kernel (then topk_idx and
+// topk_w are written there, by its workgroup 0, and read by the down
+// kernel)
 static moe_status_t ffn_enqueue(const uint16_t *x, const int32_t *topk_idx,
                                 const float *topk_w, const Experts &ex,
                                 int32_t M, int32_t H, int32_t I, int32_t E,
-                                int32_t k, float *out, void *data, hipStream_t st)
+                                int32_t k, float *out, void *ws, void *data, hipStream_t st,
+                                const UpSelect *sel = nullptr)
 {
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] { attr = set_lds_attributes(); });
     if (attr != hipSuccess)
         return MOE_ERR_LAUNCH;
-    // the activations live in the data part, wherever the caller's layout
-    // puts it
     uint16_t *act = (uint16_t *)data;
-
+    (void)ws;
     if (ex.w8)
-        launch_up_gemv_kc<true>(x, topk_idx, ex, M, H, I, E, k, act, st);
+        launch_up<true>(x, topk_idx, ex, M, H, I, E, k, act, sel, st);
     else
-        launch_up_gemv_kc<false>(x, topk_idx, ex, M, H, I, E, k, act, st);
+        launch_up<false>(x, topk_idx, ex, M, H, I, E, k, act, sel, st);
     moe_status_t s = check_launch();
     if (s != MOE_OK)
         return s;
-
-    const int R = down_rows(H);
-    const int NPT = M * k + ex.ns * M;
-    if (down_gemv_fits(R, NPT, I, ex.w8)) {
-        switch (R) {
-        case 4: launch_down_gemv<4>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
-        case 8: launch_down_gemv<8>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
-        case 10: launch_down_gemv<10>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
-        case 12: launch_down_gemv<12>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
-        default: launch_down_gemv<16>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
-        }
-        return check_launch();
-    }
-    if (ex.w8)                       // fp8 runs the GEMV down kernel only (checked)
-        return MOE_ERR_UNSUPPORTED;
-    switch (R) {
-    case 4: launch_down_r<4>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
-    case 8: launch_down_r<8>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
-    case 10: launch_down_r<10>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
-    case 12: launch_down_r<12>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
-    default: launch_down_r<16>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st); break;
+    const int R = down_rows(H, ex.w8);
+    if (use_down_gemv(M * k + ex.ns * M, I, ex.w8)) {
+        if (R == 10)
+            launch_down_gemv<10>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st);
+        else
+            launch_down_gemv<16>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st);
+    } else {
+        if (R == 10)
+            launch_down_r<10>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st);
+        else
+            launch_down_r<16>(act, topk_idx, topk_w, ex, M, H, I, E, k, out, st);
     }
     return check_launch();
 }
@@ -1121,8 +1156,8 @@ static moe_status_t shared_check(const uint16_t *wgs, const uint16_t *wus, const
 {
     if (!wgs || !wus || !wds)
         return MOE_ERR_NULL;
-    if (M * (k + 1) > kMaxNP || E + 1 > kMaxE ||
-        !down_mfma_fits(down_rows(H), M * (k + 1)) || I > kMaxDim)
+    if (M * (k + 1) > kMaxNP || E + 1 > kMaxE || I > kMaxDim ||
+        !ffn_supported(M, H, I, M * (k + 1), false))
         return MOE_ERR_UNSUPPORTED;
     if (!aligned16(wgs) || !aligned16(wus) || !aligned16(wds))
         return MOE_ERR_ALIGN;
@@ -1138,7 +1173,32 @@ moe_status_t route_enqueue(const uint16_t *x, const uint16_t *w_router,
                            const float *bias, int32_t M, int32_t H, int32_t E,
                            int32_t k, int32_t *topk_idx, float *topk_w,
                            float *logits, void *ws, hipStream_t st,
-                           const uint16_t *gamma, float eps, uint16_t *x_norm);
+                           const uint16_t *gamma, float eps, uint16_t *x_norm,
+                           bool select, int *ks);
+
+// One MoE layer step: the router, then the expert FFN on x (x_norm with the
+// norm). With at most kSelKJ * 64 experts the router kernel stops at its
+// partial logits and the up kernel selects (no cross-workgroup arrival, no
+// reload of the ids); with more, the router kernel selects.
+static moe_status_t layer_enqueue(const uint16_t *x, const uint16_t *w_router, const float *bias,
+                                  const Experts &ex, int32_t M, int32_t H, int32_t I, int32_t E,
+                                  int32_t k, int32_t *topk_idx, float *topk_w, float *out,
+                                  void *workspace, hipStream_t st, const uint16_t *gamma = nullptr,
+                                  float eps = 0.0f, uint16_t *x_norm = nullptr)
+{
+    const size_t r = moe_route_workspace_bytes(M, E);
+    const bool fused_sel = E <= kSelKJ * kWave;
+    int ks = 1;
+    moe_status_t s = route_enqueue(x, w_router, bias, M, H, E, k, topk_idx, topk_w, nullptr,
+                                   workspace, st, gamma, eps, x_norm, !fused_sel, &ks);
+    if (s != MOE_OK)
+        return s;
+    const uint16_t *xe = gamma ? x_norm : x;             // the rows the experts read
+    const UpSelect sel{(const float *)((const char *)workspace + kWsHeader), ks, bias, topk_idx,
+                       topk_w};
+    return ffn_enqueue(xe, topk_idx, topk_w, ex, M, H, I, E, k, out, workspace,
+                       (char *)workspace + r, st, fused_sel ? &sel : nullptr);
+}
 moe_status_t norm_check(const uint16_t *gamma, float eps, const uint16_t *x_norm,
                         int32_t M, int32_t H);
 
@@ -1172,8 +1232,8 @@ extern "C" moe_status_t moe_expert_ffn(const uint16_t *x, const int32_t *topk_id
     if (workspace_bytes < moe_expert_ffn_workspace_bytes(M, H, I, E, k))
         return MOE_ERR_WORKSPACE;
     const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0, false, nullptr, nullptr, nullptr};
-    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k,
-                       out, (char *)workspace + kWsHeader, (hipStream_t)stream);
+    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k, out, workspace,
+                       (char *)workspace + kWsHeader, (hipStream_t)stream);
 }
 
 extern "C" moe_status_t moe_expert_ffn_shared(
@@ -1198,8 +1258,8 @@ extern "C" moe_status_t moe_expert_ffn_shared(
         return MOE_ERR_WORKSPACE;
     const Experts ex{w_gate, w_up, w_down, w_gate_shared, w_up_shared, w_down_shared, 1, false,
                       nullptr, nullptr, nullptr};
-    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k,
-                       out, (char *)workspace + kWsHeader, (hipStream_t)stream);
+    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k, out, workspace,
+                       (char *)workspace + kWsHeader, (hipStream_t)stream);
 }
 
 extern "C" size_t moe_layer_workspace_bytes(int32_t M, int32_t H, int32_t I,
@@ -1236,15 +1296,9 @@ extern "C" moe_status_t moe_layer(const uint16_t *x, const uint16_t *w_router,
         return MOE_ERR_WORKSPACE;
     // the FFN's data part starts where the route's ends; both share the
     // header at the start of the workspace
-    const size_t r = moe_route_workspace_bytes(M, E);
-    hipStream_t st = (hipStream_t)stream;
-    s = route_enqueue(x, w_router, bias, M, H, E, k, topk_idx, topk_w, nullptr,
-                      workspace, st, nullptr, 0.0f, nullptr);
-    if (s != MOE_OK)
-        return s;
     const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0, false, nullptr, nullptr, nullptr};
-    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k,
-                       out, (char *)workspace + r, st);
+    return layer_enqueue(x, w_router, bias, ex, M, H, I, E, k, topk_idx, topk_w, out, workspace,
+                         (hipStream_t)stream);
 }
 
 extern "C" moe_status_t moe_layer_shared(
@@ -1270,16 +1324,10 @@ extern "C" moe_status_t moe_layer_shared(
         return MOE_ERR_ALIGN;
     if (workspace_bytes < moe_layer_workspace_bytes(M, H, I, E, k))
         return MOE_ERR_WORKSPACE;
-    const size_t r = moe_route_workspace_bytes(M, E);
-    hipStream_t st = (hipStream_t)stream;
-    s = route_enqueue(x, w_router, bias, M, H, E, k, topk_idx, topk_w, nullptr,
-                      workspace, st, nullptr, 0.0f, nullptr);
-    if (s != MOE_OK)
-        return s;
     const Experts ex{w_gate, w_up, w_down, w_gate_shared, w_up_shared, w_down_shared, 1, false,
                       nullptr, nullptr, nullptr};
-    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k,
-                       out, (char *)workspace + r, st);
+    return layer_enqueue(x, w_router, bias, ex, M, H, I, E, k, topk_idx, topk_w, out, workspace,
+                         (hipStream_t)stream);
 }
 
 extern "C" moe_status_t moe_layer_rmsnorm(const uint16_t *h, const uint16_t *gamma,
@@ -1309,15 +1357,9 @@ extern "C" moe_status_t moe_layer_rmsnorm(const uint16_t *h, const uint16_t *gam
         return MOE_ERR_WORKSPACE;
     // the route kernel writes the normalised rows; the expert kernels read
     // them after the kernel boundary
-    const size_t r = moe_route_workspace_bytes(M, E);
-    hipStream_t st = (hipStream_t)stream;
-    s = route_enqueue(h, w_router, bias, M, H, E, k, topk_idx, topk_w, nullptr,
-                      workspace, st, gamma, eps, x_norm);
-    if (s != MOE_OK)
-        return s;
     const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0, false, nullptr, nullptr, nullptr};
-    return ffn_enqueue(x_norm, topk_idx, topk_w, ex, M, H, I, E, k,
-                       out, (char *)workspace + r, st);
+    return layer_enqueue(h, w_router, bias, ex, M, H, I, E, k, topk_idx, topk_w, out, workspace,
+                         (hipStream_t)stream, gamma, eps, x_norm);
 }
 
 // fp8 experts: E4M3 codes [E,I,H] / [E,H,I] with fp32 scales per row; H and
@@ -1337,8 +1379,7 @@ static moe_status_t ffn8_check(const uint16_t *x, const int32_t *topk_idx,
         return s;
     if (I < 1)
         return MOE_ERR_SHAPE;
-    if (H % 16 != 0 || I % 16 != 0 || I > kMaxDim || !up_gemv_fits(M, H, true) ||
-        down_rows(H) == 0 || !down_gemv_fits(down_rows(H), M * k, I, true))
+    if (H % 16 != 0 || I % 16 != 0 || I > kMaxDim || !ffn_supported(M, H, I, M * k, true))
         return MOE_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) ||
         !aligned4(s_gate) || !aligned4(s_up) || !aligned4(s_down) || !aligned4(topk_idx) ||
@@ -1365,7 +1406,7 @@ extern "C" moe_status_t moe_expert_ffn_fp8(
         return MOE_ERR_WORKSPACE;
     const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0, true,
                      s_gate, s_up, s_down};
-    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k, out,
+    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k, out, workspace,
                        (char *)workspace + kWsHeader, (hipStream_t)stream);
 }
 
@@ -1389,13 +1430,8 @@ extern "C" moe_status_t moe_layer_fp8(
         return MOE_ERR_ALIGN;
     if (workspace_bytes < moe_layer_workspace_bytes(M, H, I, E, k))
         return MOE_ERR_WORKSPACE;
-    const size_t r = moe_route_workspace_bytes(M, E);
-    hipStream_t st = (hipStream_t)stream;
-    s = route_enqueue(x, w_router, bias, M, H, E, k, topk_idx, topk_w, nullptr, workspace, st,
-                      nullptr, 0.0f, nullptr);
-    if (s != MOE_OK)
-        return s;
     const Experts ex{w_gate, w_up, w_down, nullptr, nullptr, nullptr, 0, true,
                      s_gate, s_up, s_down};
-    return ffn_enqueue(x, topk_idx, topk_w, ex, M, H, I, E, k, out, (char *)workspace + r, st);
+    return layer_enqueue(x, w_router, bias, ex, M, H, I, E, k, topk_idx, topk_w, out, workspace,
+                         (hipStream_t)stream);
 }

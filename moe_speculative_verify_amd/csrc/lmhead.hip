@@ -114,8 +114,9 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
                       g * (W8 ? 8 : 16);
 
     const int ntiles = (V + 15) / 16;
+    // running (max, first row) of this lane; kNoRow until its first row
     float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    int bi = kNoRow;
 
     // The double buffer runs across tiles: while a tile's last block is
     // consumed, the next tile's first block is already in flight, so every
@@ -202,15 +203,12 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
             for (int r = 0; r < 4; ++r)
                 acc[r] *= rs[r];
         }
-        // rows 4g..4g+3 of the tile for token j; ascending rows, so a strict
-        // comparison keeps the first of equal values
+        // rows 4g..4g+3 of the tile for token j, in ascending order
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = tile * 16 + 4 * g + r;
-            if (row < V && acc[r] > bv) {
-                bv = acc[r];
-                bi = row;
-            }
+            if (row < V)
+                argmax_take(bv, bi, acc[r], row);
         }
     }
 
@@ -219,10 +217,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     for (int m = 16; m <= 32; m <<= 1) {
         const float ov = __shfl_xor(bv, m);
         const int oi = __shfl_xor(bi, m);
-        if (ov > bv || (ov == bv && oi < bi)) {
-            bv = ov;
-            bi = oi;
-        }
+        argmax_merge(bv, bi, ov, oi);
     }
     __shared__ float s_v[kLmWaves][16];
     __shared__ int s_i[kLmWaves][16];
@@ -238,16 +233,13 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
         float best = s_v[0][t];
         int besti = s_i[0][t];
         for (int w = 1; w < kLmWaves; ++w)
-            if (s_v[w][t] > best || (s_v[w][t] == best && s_i[w][t] < besti)) {
-                best = s_v[w][t];
-                besti = s_i[w][t];
-            }
-        const unsigned long long key =
-            ((unsigned long long)f32_order(best) << 32) | (uint32_t)(~(uint32_t)besti);
+            argmax_merge(best, besti, s_v[w][t], s_i[w][t]);
+        const unsigned long long key = argmax_key(best, besti);
         __hip_atomic_store(keys + (size_t)blockIdx.x * M + t, key, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
-    __builtin_amdgcn_s_waitcnt(0);                       // this workgroup's keys are out
+    // wave 0 stored this workgroup's keys; thread 0 (of wave 0) releases
+    // them with its arrival, and the last arrival acquires every slot
     __syncthreads();
     if (threadIdx.x == 0)
         s_last = arrive_last(ticket);
@@ -281,7 +273,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
             best = kv[q][sl] > best ? kv[q][sl] : best;  // (clamped reads repeat a slot)
         const unsigned long long key = wave_max_key(best);
         if (lane == 0) {
-            const int tok = (int)(~(uint32_t)key);
+            const int tok = argmax_key_row(key);
             argmax[t] = tok;
             s_tok[t] = tok;
             if (max_logit)

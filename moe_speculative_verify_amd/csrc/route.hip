@@ -36,67 +36,13 @@
 //     row group 0 write the normalised rows for the expert kernels. Every
 //     workgroup computes the same bits.
 #include "common.h"
+#include "select.h"
 
 #include <utility>
 
 namespace mv {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// ---- per-lane sorted lists of 64-bit selection keys (order code of the
-// logit << 32 | ~id: a larger key is a larger logit, or an equal logit with
-// a smaller id; keys of distinct ids never tie). Written with compile-time
-// indices only, so every element stays in its own registers.
-
-template <int KJ, int A, int B, bool DESC>
-__device__ __forceinline__ void sel_cex(uint64_t (&key)[KJ])
-{
-    const uint64_t ka = key[A], kb = key[B];
-    const bool sw = DESC ? ka < kb : ka > kb;
-    key[A] = sw ? kb : ka;
-    key[B] = sw ? ka : kb;
-}
-
-// one bitonic stage: compare-exchange every pair (a, a ^ STRIDE)
-template <int KJ, int SIZE, int STRIDE, int A>
-__device__ __forceinline__ void sel_stage(uint64_t (&key)[KJ])
-{
-    if constexpr (A < KJ) {
-        constexpr int B = A ^ STRIDE;
-        if constexpr (B > A)
-            sel_cex<KJ, A, B, (A & SIZE) == 0>(key);
-        sel_stage<KJ, SIZE, STRIDE, A + 1>(key);
-    }
-}
-template <int KJ, int SIZE, int STRIDE>
-__device__ __forceinline__ void sel_merge(uint64_t (&key)[KJ])
-{
-    if constexpr (STRIDE > 0) {
-        sel_stage<KJ, SIZE, STRIDE, 0>(key);
-        sel_merge<KJ, SIZE, STRIDE / 2>(key);
-    }
-}
-// bitonic sort, largest key first (KJ a power of two)
-template <int KJ, int SIZE = 2>
-__device__ __forceinline__ void sel_sort(uint64_t (&key)[KJ])
-{
-    if constexpr (SIZE <= KJ) {
-        sel_merge<KJ, SIZE, SIZE / 2>(key);
-        sel_sort<KJ, SIZE * 2>(key);
-    }
-}
-// drop the head of the list where adv is set (key 0 enters at the end)
-template <int KJ, int J = 0>
-__device__ __forceinline__ void sel_pop(uint64_t (&key)[KJ], bool adv)
-{
-    if constexpr (J + 1 < KJ) {
-        key[J] = adv ? key[J + 1] : key[J];
-        sel_pop<KJ, J + 1>(key, adv);
-    } else {
-        key[J] = adv ? 0ull : key[J];
-    }
-}
-
 
 // bf16(x * gain * inv) for eight elements: x * gain is exact in fp32 (two
 // 8-bit significands), then one product and one rounding to bf16
@@ -117,7 +63,8 @@ __device__ __forceinline__ u32x4 rmsnorm8_bf16(u32x4 v, u32x4 g, float inv)
 }
 
 // S: MFMA steps per wavefront; KJ: logits per lane in the selection (a
-// power of two, KJ * 64 >= E); RT: router rows per workgroup; P: column
+// power of two, KJ * 64 >= E; 0: no arrival and no selection, the kernel
+// ends once its partial logits are out); RT: router rows per workgroup; P: column
 // blocks per MFMA. With P = 2 (RT = 8 rows, at most 8 tokens) one MFMA takes
 // two 32-column blocks at once, block-diagonally: tile rows 0-7 and tokens
 // 0-7 carry block X, tile rows 8-15 and tokens 8-15 carry block Y (the same
@@ -273,79 +220,80 @@ __global__ __launch_bounds__(W * kWave) void route_kernel(
         }
     }
 
-    // ---- the last workgroup to arrive selects
-    __builtin_amdgcn_s_waitcnt(0);               // this thread's partial logits are out
-    __syncthreads();
-    if (threadIdx.x == 0)
-        s_last = arrive_last(ticket);                    // two-level arrival
-    __syncthreads();
-    if constexpr (NORM) {
-        // the workgroups of row group 0 (one per slice) write the
-        // normalised rows for the expert kernels only now: they must land by
-        // the end of the kernel, not before the ticket, so their latency
-        // overlaps the selection
-        if (e0 == 0 && (P == 2 ? (j & 7) : j) < M) {
+    // ---- KJ = 0: the partial logits are the result (moe_layer: the up
+    // projection's prologue selects); with the norm, row group 0's
+    // workgroups also write the normalised rows
+    if constexpr (KJ == 0) {
+        if constexpr (NORM) {
+            if (e0 == 0 && (P == 2 ? (j & 7) : j) < M) {
 #pragma unroll
-            for (int s = 0; s < SPH; ++s) {
-                const int c = cbase + 4 * P * s;
-                if (c < nch)
-                    xn_out[(size_t)tok * nch + c] = xn_keep[s];
+                for (int s = 0; s < SPH; ++s) {
+                    const int c = cbase + 4 * P * s;
+                    if (c < nch)
+                        xn_out[(size_t)tok * nch + c] = xn_keep[s];
+                }
             }
         }
-    }
-    if (!s_last)
         return;
-    if (threadIdx.x == 0)
-        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        // ---- the last workgroup to arrive selects. Wave 0 stored this
+        // workgroup's partial logits; thread 0 (of wave 0) releases them with its
+        // arrival and the last arrival acquires them (two-level arrival)
+        __syncthreads();
+        if (threadIdx.x == 0)
+            s_last = arrive_last(ticket);
+        __syncthreads();
+        if constexpr (NORM) {
+            // the workgroups of row group 0 (one per slice) write the
+            // normalised rows for the expert kernels only now: they must land by
+            // the end of the kernel, not before the ticket, so their latency
+            // overlaps the selection
+            if (e0 == 0 && (P == 2 ? (j & 7) : j) < M) {
+#pragma unroll
+                for (int s = 0; s < SPH; ++s) {
+                    const int c = cbase + 4 * P * s;
+                    if (c < nch)
+                        xn_out[(size_t)tok * nch + c] = xn_keep[s];
+                }
+            }
+        }
+        if (!s_last)
+            return;
+        if (threadIdx.x == 0)
+            __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    for (int t = wave; t < M; t += W) {
-        // this lane's logits e = lane + 64*q as (order code, id); ids past E
-        // get code 0, below every number (k <= E keeps them unselected)
-        uint64_t key[KJ];
-        float lv[KJ], pv[KS][KJ], bq[KJ];
+        for (int t = wave; t < M; t += W) {
+            // this lane's logits e = lane + 64*q as (order code, id); ids past E
+            // get code 0, below every number (k <= E keeps them unselected)
+            float lv[KJ], pv[KS][KJ], bq[KJ];
 #pragma unroll
-        for (int q = 0; q < KJ; ++q) {           // all loads in flight together
-            const int e = lane + kWave * q, ec = e < E ? e : E - 1;
+            for (int q = 0; q < KJ; ++q) {           // all loads in flight together
+                const int e = lane + kWave * q, ec = e < E ? e : E - 1;
 #pragma unroll
-            for (int sl = 0; sl < KS; ++sl)
-                pv[sl][q] = __hip_atomic_load(plog + ((size_t)sl * M + t) * E + ec,
-                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            bq[q] = bias ? bias[ec] : 0.0f;
-        }
+                for (int sl = 0; sl < KS; ++sl)
+                    pv[sl][q] = __hip_atomic_load(plog + ((size_t)sl * M + t) * E + ec,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                bq[q] = bias ? bias[ec] : 0.0f;
+            }
 #pragma unroll
-        for (int q = 0; q < KJ; ++q) {
-            const int e = lane + kWave * q;
-            // the slices' partial sums in slice order, then the bias
-            float l = pv[0][q];
+            for (int q = 0; q < KJ; ++q) {
+                const int e = lane + kWave * q;
+                // the slices' partial sums in slice order, then the bias
+                float l = pv[0][q];
 #pragma unroll
-            for (int sl = 1; sl < KS; ++sl)
-                l += pv[sl][q];
-            lv[q] = l + bq[q];
-            if (logits && e < E)
-                logits[(size_t)t * E + e] = lv[q];
-            // NaN never outranks a number; -0 and +0 share a code
-            uint32_t u = __float_as_uint(lv[q] != lv[q] ? -INFINITY : lv[q]);
-            u = u == 0x80000000u ? 0u : u;
-            const uint32_t code = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-            key[q] = e < E ? ((uint64_t)code << 32) | (uint32_t)~(uint32_t)e : 0ull;
-        }
-        sel_sort<KJ>(key);
-        uint64_t sel = 0;                        // lane s keeps selection s
-        for (int s = 0; s < k; ++s) {
-            const uint64_t win = wave_max_key(key[0]);
-            sel = lane == s ? win : sel;
-            sel_pop<KJ>(key, key[0] == win);     // the winner's next logit moves up
-        }
-        const int sel_i = (int)~(uint32_t)sel;
-        const uint32_t sel_h = (uint32_t)(sel >> 32);
-        // softmax over the selected logits, shifted by the largest
-        const float my_v = f32_unorder(sel_h);
-        const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
-        const float ex = (lane < k) ? expf(my_v - top) : 0.0f;
-        const float den = wave_sum(ex);
-        if (lane < k) {
-            topk_idx[(size_t)t * k + lane] = sel_i;
-            topk_w[(size_t)t * k + lane] = ex / den;
+                for (int sl = 1; sl < KS; ++sl)
+                    l += pv[sl][q];
+                lv[q] = l + bq[q];
+                if (logits && e < E)
+                    logits[(size_t)t * E + e] = lv[q];
+            }
+            int sel_i;
+            float sel_w;
+            topk_select<KJ>(lv, E, k, lane, sel_i, sel_w);
+            if (lane < k) {
+                topk_idx[(size_t)t * k + lane] = sel_i;
+                topk_w[(size_t)t * k + lane] = sel_w;
+            }
         }
     }
 }
@@ -355,6 +303,7 @@ struct RouteNorm {
     const uint16_t *gamma;
     float eps;
     uint16_t *xn;
+    int *ks_out;                 // the launch's number of slices of the hidden dimension
 };
 
 // RT router rows per workgroup, W wavefronts, KS workgroups per row group
@@ -364,6 +313,7 @@ static moe_status_t launch_route4(const uint16_t *x, const uint16_t *w, const fl
                                   int *idx, float *tw, unsigned *ticket, const RouteNorm &nm,
                                   hipStream_t st)
 {
+    nm.ks_out[0] = KS;
     const int grid = (E + RT - 1) / RT * KS;
     if ((grid + kArrivalGroup - 1) / kArrivalGroup > kWsGroups)
         return MOE_ERR_UNSUPPORTED;                      // (E <= 1024 stays within)
@@ -387,7 +337,7 @@ static moe_status_t launch_route4(const uint16_t *x, const uint16_t *w, const fl
 // split over kRouteSlices workgroups when the grid stays within two
 // workgroups per CU: the 2.6 MB gate of 512 x 2560 then streams through
 // 256 CUs instead of 64.
-constexpr int kRouteSlices = 4;
+constexpr int kRouteSlices = kRouteSlicesMax;
 template <int S, int KJ, int RT, int P, int W>
 static moe_status_t launch_route3(const uint16_t *x, const uint16_t *w, const float *bias,
                                   int M, int H, int E, int k, float *plog, float *logits,
@@ -429,8 +379,10 @@ template <int S>
 static moe_status_t launch_route(const uint16_t *x, const uint16_t *w, const float *bias,
                                  int M, int H, int E, int k, float *plog, float *logits,
                                  int *idx, float *tw, unsigned *ticket, const RouteNorm &nm,
-                                 hipStream_t st)
+                                 bool select, hipStream_t st)
 {
+    if (!select)                 // partial logits only
+        return launch_route2<S, 0>(x, w, bias, M, H, E, k, plog, logits, idx, tw, ticket, nm, st);
     if (E <= 128)
         return launch_route2<S, 2>(x, w, bias, M, H, E, k, plog, logits, idx, tw, ticket, nm, st);
     if (E <= 256)
@@ -461,18 +413,23 @@ bool route_norm_supported(int32_t M, int32_t H)
     return (route_need(H) + 1) / 2 <= (M <= 8 ? 16 : 8);
 }
 
+// select = false: the kernel stops at the partial logits (plog in the
+// workspace, *ks slices of the hidden dimension), which the caller's next
+// kernel selects from.
 moe_status_t route_enqueue(const uint16_t *x, const uint16_t *w_router,
                            const float *bias, int32_t M, int32_t H, int32_t E,
                            int32_t k, int32_t *topk_idx, float *topk_w,
                            float *logits, void *ws, hipStream_t st,
-                           const uint16_t *gamma, float eps, uint16_t *x_norm)
+                           const uint16_t *gamma, float eps, uint16_t *x_norm,
+                           bool select, int *ks)
 {
     unsigned *ticket = (unsigned *)ws;
     float *plog = (float *)((char *)ws + kWsHeader);
-    const RouteNorm nm{gamma, eps, x_norm};
+    int ks_local = 1;
+    const RouteNorm nm{gamma, eps, x_norm, ks ? ks : &ks_local};
     const int need = route_need(H);
 #define MV_ROUTE(S) launch_route<S>(x, w_router, bias, M, H, E, k, plog, logits, topk_idx, \
-                                    topk_w, ticket, nm, st)
+                                    topk_w, ticket, nm, select, st)
     if (need <= 2)
         return MV_ROUTE(2);
     if (need <= 4)
@@ -543,7 +500,7 @@ extern "C" moe_status_t moe_route(const uint16_t *x, const uint16_t *w_router,
     if (workspace_bytes < moe_route_workspace_bytes(M, E))
         return MOE_ERR_WORKSPACE;
     return route_enqueue(x, w_router, bias, M, H, E, k, topk_idx, topk_w, logits,
-                         workspace, (hipStream_t)stream, nullptr, 0.0f, nullptr);
+                         workspace, (hipStream_t)stream, nullptr, 0.0f, nullptr, true, nullptr);
 }
 
 extern "C" moe_status_t moe_route_rmsnorm(const uint16_t *h, const uint16_t *gamma,
@@ -567,5 +524,5 @@ extern "C" moe_status_t moe_route_rmsnorm(const uint16_t *h, const uint16_t *gam
     if (workspace_bytes < moe_route_workspace_bytes(M, E))
         return MOE_ERR_WORKSPACE;
     return route_enqueue(h, w_router, bias, M, H, E, k, topk_idx, topk_w, logits,
-                         workspace, (hipStream_t)stream, gamma, eps, x_norm);
+                         workspace, (hipStream_t)stream, gamma, eps, x_norm, true, nullptr);
 }

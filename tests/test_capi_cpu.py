@@ -225,7 +225,7 @@ def test_fp8_checks(L):
     assert ef(sd=None) == NULL
     assert ef(H=2568) == UNSUP             # H a multiple of 16
     assert ef(I=1032) == UNSUP             # I a multiple of 16
-    assert ef(M=16) == UNSUP               # 128 activation rows beyond LDS
+    assert ef(M=16, H=8192) == UNSUP       # x of 16 tokens at H = 8192 beyond LDS
     assert ef(wg=A + 8) == ALIGN
     assert ef(sg=A + 2) == ALIGN
     assert ef(wsb=16) == WS

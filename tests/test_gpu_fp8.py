@@ -119,6 +119,11 @@ FP8_CASES = [
     (2, 16, 16, 3, 2),
     (6, 2560, 1024, 32, 8),
     (1, 1040, 256, 12, 3),       # one token, x in registers, a partial last chunk column
+    (1, 4096, 128, 8, 2),        # one token, x in registers, 4 chunk columns per lane
+    (1, 5120, 128, 8, 2),        # one token, x in registers, 5 chunk columns per lane
+    (2, 6144, 128, 8, 2),        # two K blocks per unit: running sums across blocks
+    (10, 512, 1024, 64, 8),      # the block-16 verify widths: 80 and 128 pairs
+    (16, 256, 1024, 16, 8),      # 128 pairs over 16 experts: 8 pairs per column block
 ]
 
 
@@ -138,17 +143,33 @@ def test_expert_ffn_fp8_matches_oracle(M, H, I, E, k):
     assert_close(out.cpu().numpy(), ref, "out")
 
 
-def test_expert_ffn_fp8_limits():
-    """Beyond the LDS limit of the activations (M*k*I*2 bytes) the call is
-    refused on the host, with nothing launched."""
-    say("expert_ffn fp8 limits")
-    M, H, I, E, k = 16, 256, 1024, 16, 8
+def test_expert_ffn_fp8_skewed_and_limits():
+    """Skewed routing at M = 16 (hot experts with up to 16 pairs in one
+    column block, pairs past the first two loaded as they are reached), and
+    the refusal beyond LDS: x of 16 tokens at H = 8192 is refused on the
+    host, with nothing launched."""
+    say("expert_ffn fp8 skewed, limits")
+    M, H, I, E, k = 16, 1024, 512, 64, 8
     x = synth.activations(M, H, seed=5500)
-    w = dev8(fp8_experts_host(H, I, E, 5501))
-    idx, tw = synth.random_routing(M, E, k, 5502, 0.0)
+    w = fp8_experts_host(H, I, E, 5501)
+    idx, tw = synth.random_routing(M, E, k, 5502, 1.0)
+    d = dev8(w)
+    out = mv.moe_expert_ffn_fp8(to_dev(x), torch.from_numpy(idx).cuda(),
+                                torch.from_numpy(tw).cuda(), d["gate"], d["s_gate"], d["up"],
+                                d["s_up"], d["down"], d["s_down"])
+    torch.cuda.synchronize()
+    ref = oracle.expert_ffn_fp8(x, idx, tw, w["gate"], w["s_gate"], w["up"], w["s_up"],
+                                w["down"], w["s_down"])
+    assert_close(out.cpu().numpy(), ref, "out")
+    H = 8192
+    xb = torch.zeros((M, H), dtype=torch.bfloat16, device="cuda")
+    qg = torch.zeros((E, I, H), dtype=torch.uint8, device="cuda")
+    qd = torch.zeros((E, H, I), dtype=torch.uint8, device="cuda")
+    sg = torch.ones((E, I), dtype=torch.float32, device="cuda")
+    sd = torch.ones((E, H), dtype=torch.float32, device="cuda")
     with pytest.raises(mv.MoeError) as ei:
-        mv.moe_expert_ffn_fp8(to_dev(x), torch.from_numpy(idx).cuda(), torch.from_numpy(tw).cuda(),
-                              w["gate"], w["s_gate"], w["up"], w["s_up"], w["down"], w["s_down"])
+        mv.moe_expert_ffn_fp8(xb, torch.from_numpy(idx).cuda(), torch.from_numpy(tw).cuda(),
+                              qg, sg, qg, sg, qd, sd)
     assert ei.value.status == 3
 
 
@@ -164,17 +185,20 @@ def full_layer8():
     return dict(router=router, gate=qg, s_gate=sg, up=qu, s_up=su, down=qd, s_down=sd)
 
 
-@pytest.mark.parametrize("M", [1, 6, 9])
-def test_layer_fp8_full_size(full_layer8, M):
-    say("layer fp8 full size", M)
+@pytest.mark.parametrize("M,alpha", [(1, None), (6, None), (9, None), (10, None), (16, None),
+                                     (16, 1.0)])
+def test_layer_fp8_full_size(full_layer8, M, alpha):
+    say("layer fp8 full size", M, alpha)
     k = 8
     L = full_layer8
     x = synth.activations(M, 2560, seed=5600 + M)
+    bias = None if alpha is None else synth.zipf_bias(512, alpha)
     gi, gw, go = mv.moe_layer_fp8(to_dev(x), L["router"], L["gate"], L["s_gate"], L["up"],
-                                  L["s_up"], L["down"], L["s_down"], k)
+                                  L["s_up"], L["down"], L["s_down"], k,
+                                  None if bias is None else torch.from_numpy(bias).cuda())
     torch.cuda.synchronize()
     gi, gw, go = gi.cpu().numpy(), gw.cpu().numpy(), go.cpu().numpy()
-    ref = oracle.route(x, to_host_bits(L["router"]), None, k)
+    ref = oracle.route(x, to_host_bits(L["router"]), bias, k)
     same = compare_route(gi, gw, None, ref, k)
     assert len(same) >= M - 1, "more than one near-tie in a handful of tokens"
     uniq, inv = np.unique(ref["idx"], return_inverse=True)

@@ -313,6 +313,42 @@ def test_layer_full_size(full_layer, M, alpha):
     assert_close(go[same], out[same], "out")
 
 
+@pytest.mark.parametrize("M,H,E,I,k,alpha", [
+    (1, 2560, 512, 1024, 8, None),   # four slices of the hidden dimension, one token
+    (6, 2560, 512, 1024, 8, 1.0),    # the verify width, with the router bias
+    (16, 2560, 512, 1024, 8, None),  # 16 tokens: two tokens per selecting wavefront
+    (3, 264, 20, 136, 4, 1.0),       # one slice, ragged E (keys past E absent)
+    (12, 520, 100, 64, 6, None),     # one slice, 12 tokens
+    (9, 1024, 384, 256, 16, 0.5),    # k = 16
+])
+def test_layer_selection_in_up_kernel_equals_route_then_ffn(M, H, E, I, k, alpha):
+    """With at most 512 experts moe_layer selects inside the up kernel from
+    the router kernel's partial logits; its ids, weights and output equal
+    moe_route followed by moe_expert_ffn bit for bit."""
+    say("layer selection in the up kernel", M, H, E, I, k, alpha)
+    dw = device_layer(H, E, I, seed=synth.WEIGHT_SEED + 7 * H + E)
+    x = to_dev(synth.activations(M, H, seed=1700 + M))
+    b = None if alpha is None else torch.from_numpy(synth.zipf_bias(E, alpha)).cuda()
+    li, lw, lo = mv.moe_layer(x, dw["router"], dw["gate"], dw["up"], dw["down"], k, b)
+    ri, rw = mv.moe_route(x, dw["router"], k, b)
+    ro = mv.moe_expert_ffn(x, ri, rw, dw["gate"], dw["up"], dw["down"])
+    torch.cuda.synchronize()
+    assert torch.equal(li, ri) and torch.equal(lw, rw) and torch.equal(lo, ro)
+
+
+def test_layer_more_than_512_experts():
+    """Above 512 experts the router kernel selects (the up kernel's prologue
+    holds 8 logits per lane): moe_layer against the oracle at E = 1024."""
+    M, H, E, I, k = 5, 256, 1024, 128, 16
+    say("layer E=1024", M, H, E, I, k)
+    x, w, bias = host_case(M, H, E, I, seed=1800, bias_alpha=0.5)
+    gi, gw, go = _layer_gpu(x, {key: to_dev(v) for key, v in w.items()}, bias, k)
+    ref = oracle.route(x, w["router"], bias, k)
+    same = compare_route(gi, gw, None, ref, k)
+    out = oracle.expert_ffn(x, ref["idx"], ref["w"], w["gate"], w["up"], w["down"])
+    assert_close(go[same], out[same], "out")
+
+
 # ---------------------------------------------------------------- lm_head
 
 def _lm_gpu(h, wl):
@@ -371,6 +407,51 @@ def test_lmhead_zero_hidden():
     wl = synth.normal_bf16((300, 64), 0.02, 3, 3)
     am, ml = _lm_gpu(np.zeros((2, 64), np.uint16), wl)
     assert am.tolist() == [0, 0] and np.all(ml == 0.0)
+
+
+def test_lmhead_all_minus_inf():
+    """Every logit overflows to -inf in fp32 (finite bf16 inputs whose
+    products exceed the fp32 range): the argmax is row 0, as the oracle's
+    first-index rule on its fp32-rounded logits gives, and a row whose logit
+    is finite wins over the -inf rows."""
+    say("lmhead all -inf")
+    M, H, V = 3, 256, 4099
+    big = synth.bf16_bits(np.float32([2.0 ** 100]))[0]
+    h = np.zeros((M, H), np.uint16)
+    h[:, 0] = big
+    wl = np.zeros((V, H), np.uint16)
+    wl[:, 0] = synth.bf16_bits(np.float32([-(2.0 ** 100)]))[0]
+    am, ml = _lm_gpu(h, wl)
+    ref = oracle.lmhead(h, wl)
+    assert am.tolist() == [0] * M == ref["tok"].tolist()
+    assert np.all(np.isneginf(ml))
+    wl[2500, 0] = synth.bf16_bits(np.float32([2.0 ** -10]))[0]
+    am, ml = _lm_gpu(h, wl)
+    assert am.tolist() == [2500] * M == oracle.lmhead(h, wl)["tok"].tolist()
+    assert np.all(ml == np.float32(2.0 ** 90))
+
+
+def test_side_stream_matches_default_stream(full_layer):
+    """moe_layer and lmhead_greedy_verify enqueued on a side stream (their
+    pooled workspaces allocated and zero-filled on that stream) give the
+    default stream's results bit for bit."""
+    say("side stream")
+    k, M, V = 8, 6, 20000
+    fw = full_layer
+    x = to_dev(synth.activations(M, 2560, seed=1300))
+    h = to_dev(synth.activations(M, 2560, seed=1301))
+    wl = to_dev(synth.normal_bf16((V, 2560), synth.WEIGHT_STD, 1302, 0))
+    chain = torch.zeros(M, dtype=torch.int32, device="cuda")
+    a = mv.moe_layer(x, fw["router"], fw["gate"], fw["up"], fw["down"], k)
+    la = mv.lmhead_greedy_verify(h, wl, chain)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        b = mv.moe_layer(x, fw["router"], fw["gate"], fw["up"], fw["down"], k, stream=side)
+        lb = mv.lmhead_greedy_verify(h, wl, chain, stream=side)
+    torch.cuda.synchronize()
+    for ta, tb in zip(a + la, b + lb):
+        assert torch.equal(ta, tb)
 
 
 # --------------------------------------------------- greedy verify verdict
