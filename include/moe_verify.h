@@ -252,6 +252,36 @@ moe_status_t moe_layer(const uint16_t *x, const uint16_t *w_router,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * moe_layer_noalloc -- moe_layer without a caller workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). The same kernels run with
+ * their scratch (arrival counters, partial router logits, the pairs'
+ * activations) in a library-owned array of MOE_NOALLOC_SCRATCH_BYTES that
+ * every GPU the library runs on holds, one copy per device, until the
+ * process ends. The call itself allocates nothing: at its first call on a
+ * device it looks the array's device address up and clears its counter
+ * header with a fill kernel on `stream`; every call leaves the counters at
+ * zero again, as with a workspace.
+ *
+ *   Arguments and results: as moe_layer, without workspace/workspace_bytes.
+ *
+ * Every call on one GPU shares that GPU's array and it keeps the last call's
+ * contents: calls that may overlap on one GPU (two streams, two host
+ * threads) race and must be serialised by the caller. Errors: as moe_layer;
+ * MOE_ERR_WORKSPACE when moe_layer_workspace_bytes(M,H,I,E,k) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (never for the shapes moe_layer admits: the
+ * largest needs 4,722,688 bytes), MOE_ERR_LAUNCH when the array's address
+ * cannot be found on the current device.
+ * ---------------------------------------------------------------------- */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)5 << 20)
+moe_status_t moe_layer_noalloc(const uint16_t *x, const uint16_t *w_router,
+                               const float *bias, const uint16_t *w_gate,
+                               const uint16_t *w_up, const uint16_t *w_down,
+                               int32_t M, int32_t H, int32_t I, int32_t E,
+                               int32_t k, int32_t *topk_idx, float *topk_w,
+                               float *out, void *stream);
+
+/* ------------------------------------------------------------------------
  * moe_layer_shared -- moe_route then moe_expert_ffn_shared on one stream.
  *   Arguments as moe_layer, plus the shared expert's three tensors as in
  *   moe_expert_ffn_shared. Workspace: moe_layer_workspace_bytes.

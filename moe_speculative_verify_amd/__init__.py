@@ -27,7 +27,7 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_clear", "moe_hbm_
            "moe_route_workspace_bytes", "moe_route", "moe_route_rmsnorm",
            "moe_expert_ffn_workspace_bytes", "moe_expert_ffn", "moe_expert_ffn_shared",
            "moe_expert_ffn_fp8", "moe_layer_fp8",
-           "moe_layer_workspace_bytes", "moe_layer", "moe_layer_rmsnorm",
+           "moe_layer_workspace_bytes", "moe_layer", "moe_layer_noalloc", "moe_layer_rmsnorm",
            "moe_layer_shared",
            "lmhead_argmax_workspace_bytes", "lmhead_argmax", "lmhead_greedy_verify",
            "lmhead_argmax_fp8", "lmhead_greedy_verify_fp8")
@@ -85,6 +85,9 @@ def lib() -> ctypes.CDLL:
         L.moe_expert_ffn.restype = ctypes.c_int32
         L.moe_expert_ffn.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                      _P, _P, _S, _P]
+        L.moe_layer_noalloc.restype = ctypes.c_int32
+        L.moe_layer_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                        _P, _P, _P, _P]
         L.moe_layer_workspace_bytes.restype = _S
         L.moe_layer_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
         L.moe_layer.restype = ctypes.c_int32
@@ -283,6 +286,31 @@ def moe_layer(x, w_router, w_gate, w_up, w_down, k: int, bias=None, *, out=None,
         _ptr(idx, "topk_idx", (torch.int32,), (M, k)),
         _ptr(w, "topk_w", (torch.float32,), (M, k)),
         _ptr(o, "out", (torch.float32,), (M, H)), _ptr(ws, "workspace"), ws.numel(), st))
+    return idx, w, o
+
+
+def moe_layer_noalloc(x, w_router, w_gate, w_up, w_down, k: int, bias=None, *, out=None,
+                      stream=None):
+    """moe_layer with its scratch in the library's own per-GPU array (no
+    workspace). Returns (topk_idx, topk_w, out)."""
+    M, H = x.shape
+    E, I, _ = w_gate.shape
+    dev = x.device
+    idx, w, o = out if out is not None else (None, None, None)
+    if idx is None:
+        idx = torch.empty((M, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((M, k), dtype=torch.float32, device=dev)
+    if o is None:
+        o = torch.empty((M, H), dtype=torch.float32, device=dev)
+    _check("moe_layer_noalloc", lib().moe_layer_noalloc(
+        _ptr(x, "x", _BF16), _ptr(w_router, "w_router", _BF16, (E, H)),
+        _ptr(bias, "bias", (torch.float32,), (E,)),
+        _ptr(w_gate, "w_gate", _BF16, (E, I, H)), _ptr(w_up, "w_up", _BF16, (E, I, H)),
+        _ptr(w_down, "w_down", _BF16, (E, H, I)), M, H, I, E, k,
+        _ptr(idx, "topk_idx", (torch.int32,), (M, k)),
+        _ptr(w, "topk_w", (torch.float32,), (M, k)),
+        _ptr(o, "out", (torch.float32,), (M, H)), _stream(stream)))
     return idx, w, o
 
 

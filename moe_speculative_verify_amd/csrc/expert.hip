@@ -1301,6 +1301,61 @@ extern "C" moe_status_t moe_layer(const uint16_t *x, const uint16_t *w_router,
                          (hipStream_t)stream);
 }
 
+// ---------------------------------------------------- moe_layer_noalloc
+// The scratch of moe_layer_noalloc: one array per GPU, for the life of the
+// process. In host code `scratch` only names the symbol; its device address
+// (a different one on each GPU) comes from hipGetSymbolAddress and is what
+// the kernels are given.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+static_assert(kWsHeader + 4 * 16 * 1024 * 4 + 16 * 17 * 8192 * 2 <= MOE_NOALLOC_SCRATCH_BYTES,
+              "the scratch holds the workspace of the largest moe_layer shape");
+constexpr int kScratchDevices = 64;
+
+// The scratch's address on the current device, looked up (and its counter
+// header cleared on `st`) at the first call there; nullptr if the lookup fails.
+static void *scratch_on_device(hipStream_t st)
+{
+    static std::mutex mu;
+    static void *ptr[kScratchDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices)
+        return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return nullptr;
+        // the counters must start at zero (the kernels leave them so)
+        if (moe_workspace_clear(p, kWsHeader, st) != MOE_OK)
+            return nullptr;
+        ptr[dev] = p;
+    }
+    return ptr[dev];
+}
+
+extern "C" moe_status_t moe_layer_noalloc(const uint16_t *x, const uint16_t *w_router,
+                                          const float *bias, const uint16_t *w_gate,
+                                          const uint16_t *w_up, const uint16_t *w_down,
+                                          int32_t M, int32_t H, int32_t I, int32_t E,
+                                          int32_t k, int32_t *topk_idx, float *topk_w,
+                                          float *out, void *stream)
+{
+    moe_status_t s = route_check(x, w_router, bias, M, H, E, k, topk_idx, topk_w, nullptr);
+    if (s != MOE_OK)
+        return s;
+    s = ffn_check(x, topk_idx, topk_w, w_gate, w_up, w_down, M, H, I, E, k, out);
+    if (s != MOE_OK)
+        return s;
+    const size_t need = moe_layer_workspace_bytes(M, H, I, E, k);
+    if (need > MOE_NOALLOC_SCRATCH_BYTES)
+        return MOE_ERR_WORKSPACE;
+    void *ws = scratch_on_device((hipStream_t)stream);
+    if (!ws)
+        return MOE_ERR_LAUNCH;
+    return moe_layer(x, w_router, bias, w_gate, w_up, w_down, M, H, I, E, k, topk_idx, topk_w,
+                     out, ws, need, stream);
+}
+
 extern "C" moe_status_t moe_layer_shared(
     const uint16_t *x, const uint16_t *w_router, const float *bias, const uint16_t *w_gate,
     const uint16_t *w_up, const uint16_t *w_down, const uint16_t *w_gate_shared,
