@@ -497,6 +497,8 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
             }
         }
     }
+    if constexpr (!XR)                                   // x into LDS while the ids are found
+        stage_rows_lds(x, M, nch, s_x, xs);
     int pid;                                             // this thread's pair's expert
     if constexpr (SEL) {
         // one wavefront per token: the slices' partial sums in slice order,
@@ -505,15 +507,25 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
         int *s_sel = (int *)(smem + xbytes);
         static_assert(kUpWaves * kUpPend * sizeof(float2) >= kMaxNP * sizeof(int), "room");
         for (int t = wave; t < M; t += WV) {
+            // every load unpredicated and in flight together: slices past
+            // nks reread the last one (the workspace holds kRouteSlicesMax)
+            // and are left out of the sum
             float pv[kRouteSlicesMax][kSelKJ], bq[kSelKJ], lv[kSelKJ];
 #pragma unroll
-            for (int q = 0; q < kSelKJ; ++q) {           // all loads in flight together
+            for (int q = 0; q < kSelKJ; ++q) {
                 const int e = lane + kWave * q, ec = e < E ? e : E - 1;
 #pragma unroll
                 for (int sl = 0; sl < kRouteSlicesMax; ++sl)
-                    if (sl < sel.nks)
-                        pv[sl][q] = sel.plog[((size_t)sl * M + t) * E + ec];
-                bq[q] = sel.bias ? sel.bias[ec] : 0.0f;
+                    pv[sl][q] = sel.plog[((size_t)min(sl, sel.nks - 1) * M + t) * E + ec];
+            }
+            if (sel.bias) {                              // uniform
+#pragma unroll
+                for (int q = 0; q < kSelKJ; ++q)
+                    bq[q] = sel.bias[min(lane + kWave * q, E - 1)];
+            } else {
+#pragma unroll
+                for (int q = 0; q < kSelKJ; ++q)
+                    bq[q] = 0.0f;
             }
 #pragma unroll
             for (int q = 0; q < kSelKJ; ++q) {
@@ -544,7 +556,7 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
     groups_set_pairs(pid, NPT, E + ns, g);
     if (threadIdx.x == 0)
         s_next = 0;
-    wait_vmcnt<0>();                                     // the pair id (and XR: x) is in
+    wait_vmcnt<0>();                                     // the pair id and x are in
     if constexpr (XR) {
 #pragma unroll
         for (int c = 0; c < KC; ++c)                     // the K tail of x reads as zero
@@ -561,7 +573,6 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
     }
     groups_finish(NPT, g);                               // (its barriers also publish s_next)
     if constexpr (!XR) {
-        stage_rows_lds(x, M, nch, s_x, xs);
         wait_vmcnt<0>();                                 // this wave's share of x has landed
         lds_barrier();                                   // ... and every other wave's
     }
