@@ -33,6 +33,34 @@
  *     loads). Shape limits: 1 <= M <= 16, 1 <= k <= min(E, 16),
  *     1 <= E <= 1024, H and I multiples of 8 and at most 8192,
  *     1 <= V < 2^31.
+ *   - Wider rows: the kernels keep every token's row of the hidden
+ *     dimension on chip (the expert up kernel and the lm_head stage the M
+ *     rows of x or h in LDS, 160 KB per CU; the norm holds each lane's
+ *     share in registers), so above some H a call is refused with
+ *     MOE_ERR_UNSUPPORTED before anything is launched. The largest H
+ *     accepted, by M (every smaller multiple of 8, or of 16 for fp8
+ *     weights, is accepted; the limit depends on M and H only, not on I,
+ *     E, k or V):
+ *
+ *        M   experts bf16   experts fp8   lm_head bf16   lm_head fp8   norm
+ *       1-5      8192           8192          8192           8192       8192
+ *        6       8192           8192          7936           7680       8192
+ *        7       8192           8192          6656           6656       8192
+ *        8       8192           8192          5888           5632       8192
+ *        9       6144           5120          5120           5120       4096
+ *       10       6144           5120          4608           4608       4096
+ *       11       6144           5120          4352           4096       4096
+ *       12       4096           5120          3840           3584       4096
+ *       13       4096           5120          3584           3584       4096
+ *       14       4096           5120          3328           3072       4096
+ *       15       4096           4096          3072           3072       4096
+ *       16       4096           4096          2816           2560       4096
+ *
+ *     "experts" covers moe_expert_ffn, moe_expert_ffn_shared and the
+ *     moe_layer entry points (with their fp8 variants), "lm_head" the
+ *     lmhead_* entry points, "norm" moe_route_rmsnorm and
+ *     moe_layer_rmsnorm (which also takes the experts' limit). The model's
+ *     width, H = 2560, is accepted everywhere at every M.
  *   - Workspaces: size from the matching *_workspace_bytes query,
  *     16-byte aligned, ZERO-FILLED before their first use (one
  *     moe_workspace_clear call, or any zero fill). The first 4096 bytes of
@@ -112,7 +140,17 @@ moe_status_t moe_hbm_read_probe(const void *src, size_t bytes, uint32_t *checksu
  *   topk_w    [M,k] fp32   out: softmax of the selected logits (equal to a
  *                          softmax over all E renormalised over the set)
  *   logits    [M,E] fp32   optional out (NULL skips): l = x.w_router^T + bias
- *   workspace              moe_route_workspace_bytes(M, E) bytes
+ *   workspace              moe_route_workspace_bytes(M, E) bytes: the
+ *                          counter header and the partial logits
+ *                          [slices][M][E] fp32 of the workgroups that split
+ *                          the hidden dimension (up to four slices, so a
+ *                          2.6 MB gate spreads over every CU); the last
+ *                          workgroup to arrive sums them in slice order and
+ *                          selects. Its size depends on M and E only.
+ *
+ * Errors: MOE_ERR_NULL (x, w_router, topk_idx, topk_w or workspace NULL),
+ * MOE_ERR_SHAPE (M, H, E or k below 1), MOE_ERR_UNSUPPORTED (the shape
+ * limits above), MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH.
  * ---------------------------------------------------------------------- */
 size_t moe_route_workspace_bytes(int32_t M, int32_t E);
 moe_status_t moe_route(const uint16_t *x, const uint16_t *w_router,
@@ -141,7 +179,8 @@ moe_status_t moe_route(const uint16_t *x, const uint16_t *w_router,
  * Errors: as moe_route; MOE_ERR_NULL for a NULL gamma or x_norm,
  * MOE_ERR_SHAPE for a negative, NaN or infinite eps, MOE_ERR_ALIGN unless
  * gamma and x_norm are 16-byte aligned, MOE_ERR_UNSUPPORTED when M > 8 and
- * H > 4096 (every hidden-state chunk of a lane must fit in registers).
+ * H > 4096 (every hidden-state chunk of a lane must fit in registers; the
+ * "norm" column of the limits table).
  * ---------------------------------------------------------------------- */
 moe_status_t moe_route_rmsnorm(const uint16_t *h, const uint16_t *gamma, float eps,
                                const uint16_t *w_router, const float *bias,
@@ -172,6 +211,11 @@ moe_status_t moe_route_rmsnorm(const uint16_t *h, const uint16_t *gamma, float e
  *
  * Every distinct selected expert's weights are read from HBM exactly once
  * per call, however many tokens chose it.
+ *
+ * Errors: MOE_ERR_NULL (any tensor or the workspace NULL), MOE_ERR_SHAPE
+ * (M, H, I, E or k below 1), MOE_ERR_UNSUPPORTED (I not a multiple of 8 or
+ * above 8192, or the "experts bf16" limit of the table above),
+ * MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH.
  * ---------------------------------------------------------------------- */
 size_t moe_expert_ffn_workspace_bytes(int32_t M, int32_t H, int32_t I,
                                       int32_t E, int32_t k);
@@ -223,9 +267,9 @@ moe_status_t moe_expert_ffn_shared(const uint16_t *x, const int32_t *topk_idx,
  *   w_down       [E,H,I] uint8   E4M3 codes
  *   s_down       [E,H]   fp32    row scales of W_down
  *   the rest:                    as moe_expert_ffn (same workspace size)
- * H and I must be multiples of 16. The activations of the M*k pairs must
- * fit in LDS (M*k*I*2 bytes up to about 150 KB: M <= 9 at I = 1024, k = 8),
- * else MOE_ERR_UNSUPPORTED. NaN codes are the caller's to avoid.
+ * H and I must be multiples of 16 (else MOE_ERR_UNSUPPORTED), and H within
+ * the "experts fp8" column of the limits table above. NaN codes are the
+ * caller's to avoid.
  * ---------------------------------------------------------------------- */
 moe_status_t moe_expert_ffn_fp8(const uint16_t *x, const int32_t *topk_idx,
                                 const float *topk_w, const uint8_t *w_gate,
@@ -339,9 +383,21 @@ moe_status_t moe_layer_rmsnorm(const uint16_t *h, const uint16_t *gamma, float e
  *   argmax     [M]   int32  out: first v with the largest fp32 logit
  *                           z[t,v] = h[t,:].w_lm[v,:] (lowest id on ties)
  *   max_logit  [M]   fp32   optional out (NULL skips): z[t, argmax[t]]
- *   workspace               lmhead_argmax_workspace_bytes(M, V) bytes
+ *   workspace               lmhead_argmax_workspace_bytes(M, V) bytes: the
+ *                           counter header and one M-key slot per workgroup
+ *                           (each workgroup's per-token winner, merged by
+ *                           the last to arrive). V is an argument because
+ *                           the workgroup count is min(ceil(V/16), 256):
+ *                           the query returns 0 for an invalid M or V, and
+ *                           today's size is that of 256 workgroups.
  *
- * The [M,V] logits are never written to memory.
+ * The [M,V] logits are never written to memory. A NaN logit counts as
+ * -inf; when every logit of a row is -inf (or NaN) the row's argmax is 0.
+ *
+ * Errors: MOE_ERR_NULL (h, w_lm, argmax or workspace NULL), MOE_ERR_SHAPE
+ * (M, H or V below 1), MOE_ERR_UNSUPPORTED (M above 16, H not a multiple of
+ * 8 or above the "lm_head bf16" limit of the table above), MOE_ERR_ALIGN,
+ * MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH.
  * ---------------------------------------------------------------------- */
 size_t lmhead_argmax_workspace_bytes(int32_t M, int32_t V);
 moe_status_t lmhead_argmax(const uint16_t *h, const uint16_t *w_lm,

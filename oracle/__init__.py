@@ -65,8 +65,20 @@ class Oracle:
         lib.oracle_rmsnorm.restype = ctypes.c_int
         lib.oracle_greedy_verdict.argtypes = [_P, _P, _I, _P]
         lib.oracle_greedy_verdict.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [_I]
+        lib.oracle_set_threads.restype = None
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int32
         self.lib = lib
         self.path = path
+
+    def set_threads(self, n: int) -> int:
+        """Use n OpenMP threads from now on; returns the count in effect."""
+        self.lib.oracle_set_threads(int(n))
+        return int(self.lib.oracle_threads())
+
+    def threads(self) -> int:
+        return int(self.lib.oracle_threads())
 
     @staticmethod
     def _check(rc: int, what: str) -> None:
@@ -219,6 +231,14 @@ def load() -> Oracle:
             build()
         _default = Oracle(_LIB)
     return _default
+
+
+def set_threads(n):
+    return load().set_threads(n)
+
+
+def threads():
+    return load().threads()
 
 
 def route(x, wg, bias, k):

@@ -32,8 +32,23 @@
 #include "oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Threads the OpenMP loops below use from now on (n >= 1), and how many
+ * they use: set once for a single-threaded timing, once for all cores.
+ * Thread counts never change a result, only which thread computes it. */
+void oracle_set_threads(int32_t n)
+{
+    if (n >= 1)
+        omp_set_num_threads(n);
+}
+
+int32_t oracle_threads(void)
+{
+    return (int32_t)omp_get_max_threads();
+}
 
 double oracle_bf16_value(uint16_t bits)
 {

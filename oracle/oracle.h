@@ -151,6 +151,10 @@ int oracle_lmhead_fp8(const uint16_t *h, const uint8_t *qlm, const float *slm,
 int oracle_greedy_verdict(const int32_t *tokens, const int32_t *tok, int32_t M,
                           int32_t *accept);
 
+/* Thread count of the OpenMP loops (n >= 1), and the current count. */
+void oracle_set_threads(int32_t n);
+int32_t oracle_threads(void);
+
 #ifdef __cplusplus
 }
 #endif

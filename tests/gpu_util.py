@@ -92,3 +92,22 @@ def device_layer(H, E, I, layer=0, seed=synth.WEIGHT_SEED):
         up=synth.device_normal_bf16((E, I, H), synth.WEIGHT_STD, seed, layer, K["up"]),
         down=synth.device_normal_bf16((E, H, I), synth.WEIGHT_STD, seed, layer, K["down"]),
     )
+
+
+def check_tie_rows(x_bits, gi, gw, go, ref, ffn):
+    """Rows where the GPU took another valid top-k at an oracle-flagged
+    near-tie (compare_route already checked the set): the GPU's routing
+    weights must be the softmax of the oracle's logits over the GPU's own
+    set, and the GPU's output the oracle FFN on the GPU's own ids and
+    weights. ffn(x_rows, idx, w) is the oracle FFN of the layer's experts.
+    Returns the rows checked."""
+    rows = [t for t in range(gi.shape[0]) if not np.array_equal(gi[t], ref["idx"][t])]
+    if not rows:
+        return rows
+    for t in rows:
+        lt = ref["logits"][t][gi[t]]
+        wt = np.exp(lt - lt.max())
+        assert_close(gw[t], wt / wt.sum(), f"topk_w of near-tie token {t}")
+    out = ffn(x_bits[rows], gi[rows], gw[rows].astype(np.float64))
+    assert_close(go[rows], out, "out of the near-tie tokens")
+    return rows

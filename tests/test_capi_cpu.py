@@ -238,3 +238,104 @@ def test_fp8_checks(L):
     assert lf(wsb=16) == WS
     assert L.lmhead_greedy_verify_fp8(A, A, A, None, 6, 2560, 157184, A, None, A, B, 1 << 20,
                                       None) == NULL
+
+
+# ---------------------------------------------- the header's H limits by M
+# Each call below passes every check but the workspace size (0 bytes), so an
+# accepted shape returns MOE_ERR_WORKSPACE and nothing is launched; a refused
+# one returns MOE_ERR_UNSUPPORTED.
+
+def header_limits():
+    """The table of largest accepted H by M in include/moe_verify.h:
+    {column: {M: H}}."""
+    cols = ("experts_bf16", "experts_fp8", "lm_bf16", "lm_fp8", "norm")
+    out = {c: {} for c in cols}
+    for line in open(HEADER):
+        m = re.match(r"\s*\*\s+(\d+)(?:-(\d+))?((?:\s+\d+){5})\s*$", line)
+        if not m:
+            continue
+        lo = int(m.group(1))
+        hi = int(m.group(2) or lo)
+        vals = [int(v) for v in m.group(3).split()]
+        for M in range(lo, hi + 1):
+            for c, v in zip(cols, vals):
+                out[c][M] = v
+    assert all(sorted(t) == list(range(1, 17)) for t in out.values()), out
+    return out
+
+
+def _limit_calls(L):
+    f = ctypes.c_float(1e-6)
+    return {
+        "experts_bf16": (8, [
+            lambda M, H: L.moe_expert_ffn(A, A, A, A, A, A, M, H, 1024, 512, 8, A, B, 0, None),
+            lambda M, H: L.moe_expert_ffn_shared(A, A, A, A, A, A, A, A, A, M, H, 1024, 512, 8,
+                                                 A, B, 0, None),
+            lambda M, H: L.moe_layer(A, A, None, A, A, A, M, H, 1024, 512, 8, A, A, A, B, 0,
+                                     None),
+            lambda M, H: L.moe_layer_shared(A, A, None, A, A, A, A, A, A, M, H, 1024, 512, 8,
+                                            A, A, A, B, 0, None)]),
+        "experts_fp8": (16, [
+            lambda M, H: L.moe_expert_ffn_fp8(A, A, A, A, A, A, A, A, A, M, H, 1024, 512, 8, A,
+                                              B, 0, None),
+            lambda M, H: L.moe_layer_fp8(A, A, None, A, A, A, A, A, A, M, H, 1024, 512, 8, A, A,
+                                         A, B, 0, None)]),
+        "lm_bf16": (8, [
+            lambda M, H: L.lmhead_argmax(A, A, M, H, 157184, A, None, B, 0, None),
+            lambda M, H: L.lmhead_greedy_verify(A, A, A, M, H, 157184, A, None, A, B, 0, None)]),
+        "lm_fp8": (16, [
+            lambda M, H: L.lmhead_argmax_fp8(A, A, A, M, H, 157184, A, None, B, 0, None),
+            lambda M, H: L.lmhead_greedy_verify_fp8(A, A, A, A, M, H, 157184, A, None, A, B, 0,
+                                                    None)]),
+        "norm": (8, [
+            lambda M, H: L.moe_route_rmsnorm(A, A, f, A, None, M, H, 512, 8, A, A, A, None, B, 0,
+                                             None)]),
+    }
+
+
+def test_header_h_limits_table_matches_the_library(L):
+    lim = header_limits()
+    for col, (step, calls) in _limit_calls(L).items():
+        for M in range(1, 17):
+            hmax = lim[col][M]
+            for fn in calls:
+                # every width up to the limit is accepted, the next one refused
+                for H in range(step, hmax + 1, step):
+                    assert fn(M, H) == WS, (col, M, H)
+                if hmax < 8192:
+                    assert fn(M, hmax + step) == UNSUP, (col, M, hmax + step)
+
+
+def test_rmsnorm_layer_takes_both_limits(L):
+    lim = header_limits()
+    f = ctypes.c_float(1e-6)
+    for M in range(1, 17):
+        hmax = min(lim["norm"][M], lim["experts_bf16"][M])
+        call = lambda H: L.moe_layer_rmsnorm(A, A, f, A, None, A, A, A, M, H, 1024, 512, 8, A, A,
+                                             A, A, B, 0, None)
+        assert call(hmax) == WS
+        if hmax < 8192:
+            assert call(hmax + 8) == UNSUP
+
+
+def test_h_limits_do_not_depend_on_i_e_k(L):
+    # at the widest accepted H of each M, every I, E and k the ABI admits is
+    # accepted too (the down kernels' LDS never binds first)
+    lim = header_limits()
+    for M in (1, 6, 9, 12, 16):
+        for I in (16, 1024, 4096, 8192):
+            for E, k in ((16, 16), (512, 8), (1024, 1), (1024, 16)):
+                h = lim["experts_bf16"][M]
+                assert L.moe_expert_ffn(A, A, A, A, A, A, M, h, I, E, k, A, B, 0, None) == WS
+                h8 = lim["experts_fp8"][M]
+                assert L.moe_expert_ffn_fp8(A, A, A, A, A, A, A, A, A, M, h8, I, E, k, A, B, 0,
+                                            None) == WS
+    for M in (1, 6, 16):
+        for V in (1, 16, 157184, 2**31 - 1):
+            assert L.lmhead_argmax(A, A, M, lim["lm_bf16"][M], V, A, None, B, 0, None) == WS
+
+
+def test_model_width_accepted_everywhere(L):
+    lim = header_limits()
+    for col in lim:
+        assert all(v >= 2560 for v in lim[col].values()), col

@@ -12,7 +12,7 @@ import torch
 import moe_speculative_verify_amd as mv
 import oracle
 import synth
-from gpu_util import TIE_BAND, assert_close, compare_route, to_dev, to_host_bits
+from gpu_util import TIE_BAND, assert_close, check_tie_rows, compare_route, to_dev, to_host_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -201,11 +201,17 @@ def test_layer_fp8_full_size(full_layer8, M, alpha):
     ref = oracle.route(x, to_host_bits(L["router"]), bias, k)
     same = compare_route(gi, gw, None, ref, k)
     assert len(same) >= M - 1, "more than one near-tie in a handful of tokens"
-    uniq, inv = np.unique(ref["idx"], return_inverse=True)
-    sel = torch.as_tensor(uniq, dtype=torch.long, device="cuda")
-    sub = {key: L[key].index_select(0, sel).cpu().numpy()
-           for key in ("gate", "s_gate", "up", "s_up", "down", "s_down")}
-    out = oracle.expert_ffn_fp8(x, inv.reshape(ref["idx"].shape).astype(np.int32), ref["w"],
-                                sub["gate"], sub["s_gate"], sub["up"], sub["s_up"],
-                                sub["down"], sub["s_down"])
+
+    def ffn8(xr, ids, w):
+        # the oracle on the experts listed in ids, reading back just those
+        uniq, inv = np.unique(ids, return_inverse=True)
+        sel = torch.as_tensor(uniq, dtype=torch.long, device="cuda")
+        sub = {key: L[key].index_select(0, sel).cpu().numpy()
+               for key in ("gate", "s_gate", "up", "s_up", "down", "s_down")}
+        return oracle.expert_ffn_fp8(xr, inv.reshape(ids.shape).astype(np.int32), w,
+                                     sub["gate"], sub["s_gate"], sub["up"], sub["s_up"],
+                                     sub["down"], sub["s_down"])
+
+    out = ffn8(x, ref["idx"], ref["w"])
     assert_close(go[same], out[same], "out")
+    check_tie_rows(x, gi, gw, go, ref, ffn8)

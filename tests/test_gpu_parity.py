@@ -12,8 +12,8 @@ import torch
 import moe_speculative_verify_amd as mv
 import oracle
 import synth
-from gpu_util import (REL_TOL, TIE_BAND, assert_close, check_selection, compare_route,
-                      device_layer, oracle_ffn_from_device, to_dev, to_host_bits)
+from gpu_util import (REL_TOL, TIE_BAND, assert_close, check_selection, check_tie_rows,
+                      compare_route, device_layer, oracle_ffn_from_device, to_dev, to_host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -296,9 +296,12 @@ def test_layer_tiny():
     same = compare_route(gi, gw, None, ref, cfg["k"])
     out = oracle.expert_ffn(x, ref["idx"], ref["w"], w["gate"], w["up"], w["down"])
     assert_close(go[same], out[same], "out")
+    check_tie_rows(x, gi, gw, go, ref, lambda xr, ids, tw: oracle.expert_ffn(
+        xr, ids, tw, w["gate"], w["up"], w["down"]))
 
 
-@pytest.mark.parametrize("M,alpha", [(1, None), (6, None), (6, 1.0), (16, 1.0), (16, 0.0)])
+@pytest.mark.parametrize("M,alpha", [(1, None), (1, 1.0), (6, None), (6, 1.0), (16, 1.0),
+                                     (16, 0.0)])
 def test_layer_full_size(full_layer, M, alpha):
     say("layer full size", M, alpha)
     k = 8
@@ -311,6 +314,8 @@ def test_layer_full_size(full_layer, M, alpha):
     assert len(same) >= M - 1, "more than one near-tie in a handful of tokens"
     out = oracle_ffn_from_device(x, ref["idx"], ref["w"], full_layer)
     assert_close(go[same], out[same], "out")
+    check_tie_rows(x, gi, gw, go, ref,
+                   lambda xr, ids, w: oracle_ffn_from_device(xr, ids, w, full_layer))
 
 
 @pytest.mark.parametrize("M,H,E,I,k,alpha", [
@@ -347,6 +352,8 @@ def test_layer_more_than_512_experts():
     same = compare_route(gi, gw, None, ref, k)
     out = oracle.expert_ffn(x, ref["idx"], ref["w"], w["gate"], w["up"], w["down"])
     assert_close(go[same], out[same], "out")
+    check_tie_rows(x, gi, gw, go, ref, lambda xr, ids, tw: oracle.expert_ffn(
+        xr, ids, tw, w["gate"], w["up"], w["down"]))
 
 
 # ---------------------------------------------------------------- lm_head

@@ -17,8 +17,8 @@ import torch
 import moe_speculative_verify_amd as mv
 import oracle
 import synth
-from gpu_util import (assert_close, compare_route, device_layer, oracle_ffn_from_device,
-                      to_dev, to_host_bits)
+from gpu_util import (assert_close, check_tie_rows, compare_route, device_layer,
+                      oracle_ffn_from_device, to_dev, to_host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -130,6 +130,8 @@ def test_layer_rmsnorm_full_size(full_layer, M, alpha):
     assert len(same) >= M - 1, "more than one near-tie in a handful of tokens"
     out = oracle_ffn_from_device(rxn, ref["idx"], ref["w"], full_layer)
     assert_close(go[same], out[same], "out")
+    check_tie_rows(rxn, gi, gw, go, ref,
+                   lambda xr, ids, w: oracle_ffn_from_device(xr, ids, w, full_layer))
     # bit for bit the plain layer on the rows the kernel wrote
     pi, pw, po = mv.moe_layer(to_dev(gxn), full_layer["router"], full_layer["gate"],
                               full_layer["up"], full_layer["down"], k, b)

@@ -14,7 +14,8 @@ import torch
 import moe_speculative_verify_amd as mv
 import oracle
 import synth
-from gpu_util import assert_close, compare_route, device_layer, gather_experts, to_dev, to_host_bits
+from gpu_util import (assert_close, check_tie_rows, compare_route, device_layer, gather_experts,
+                      to_dev, to_host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -131,8 +132,13 @@ def test_layer_shared_full_size(full_layer, M, alpha):
     ref = oracle.route(x, to_host_bits(full_layer["router"]), bias, k)
     same = compare_route(gi, gw, None, ref, k)
     assert len(same) >= M - 1, "more than one near-tie in a handful of tokens"
-    uniq, inv = np.unique(ref["idx"], return_inverse=True)
-    sub = gather_experts(full_layer, uniq)
     sw = {key: to_host_bits(S[key]) for key in ("gate", "up", "down")}
-    out = oracle_with_shared(x, inv.reshape(ref["idx"].shape).astype(np.int32), ref["w"], sub, sw)
+
+    def ffn_shared(xr, ids, w):
+        uniq, inv = np.unique(ids, return_inverse=True)
+        sub = gather_experts(full_layer, uniq)
+        return oracle_with_shared(xr, inv.reshape(ids.shape).astype(np.int32), w, sub, sw)
+
+    out = ffn_shared(x, ref["idx"], ref["w"])
     assert_close(go[same], out[same], "out")
+    check_tie_rows(x, gi, gw, go, ref, ffn_shared)
