@@ -63,17 +63,19 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // section "PDL: the latency floor of stacked small kernels"): a histogram of
 // the pairs over the experts (LDS atomics), one packed prefix scan over the
 // experts that yields each bucket's offset, index and first column block
-// at once, and a scatter of the pair ids. Buckets are ordered by expert id;
-// the order of pairs inside a bucket is whatever the atomics produced,
-// which no result depends on (every pair's arithmetic is its own). A bucket
-// is cut into column blocks of at most 16 pairs (one MFMA B operand); with
-// distinct experts per token a bucket never exceeds M <= 16 pairs.
+// at once, and a scatter of the pair ids. Buckets are ordered by expert id
+// (by pair on the direct path below); the order of pairs inside a bucket is
+// whatever the atomics produced, which no result depends on (every pair's
+// arithmetic is its own). A bucket is cut into column blocks of at most 16
+// pairs (one MFMA B operand); with distinct experts per token a bucket never
+// exceeds M <= 16 pairs.
 constexpr int kGroupThreads = 256;               // threads that build it (the first 256)
 constexpr int kBinsPerThread = kMaxE / kGroupThreads;
 
 struct Groups {
     int D;                       // distinct valid experts
     int DV;                      // column blocks
+    int direct;                  // built by the few-distinct-pairs path
     int wsum[kGroupThreads / kWave];   // per-wavefront totals of the scan
     int bins[kMaxE];             // pairs per expert, then bucket offsets
     int16_t e[kMaxNP];           // expert of pair p, -1 if out of range
@@ -110,12 +112,51 @@ __device__ inline void groups_set_pairs(int idx, int NP, int E, Groups &g)
         g.bins[i * kGroupThreads + p] = 0;
 }
 
+// Few pairs, all in distinct experts (one verify token: the router never
+// picks an expert twice for a token): every valid pair is a bucket of its
+// own and its own column block, in pair order, found by wavefront 0 without
+// the histogram -- the blocks the histogram would build, in another order,
+// which no result depends on. Pairs that share an expert take the histogram.
+constexpr int kDirectNP = 16;
+
 __device__ inline void groups_finish(int NP, Groups &g)
 {
     const int p = threadIdx.x;
     const int lane = p & (kWave - 1), wave = p / kWave;
     const bool gp = p < kGroupThreads;           // uniform per wavefront
     lds_barrier();
+    if (NP <= kDirectNP) {                       // uniform
+        if (wave == 0) {
+            const int ep = p < NP ? g.e[p] : -1;
+            bool dup = false;
+            for (int q = 0; q < NP; ++q) {
+                const int eq = __builtin_amdgcn_readlane(ep, q);
+                dup = dup || (q < p && ep >= 0 && eq == ep);
+            }
+            const bool direct = __ballot(dup) == 0;
+            if (direct) {
+                const unsigned long long val = __ballot(ep >= 0);
+                // valid pairs before this one: its block index
+                const int v = __builtin_amdgcn_mbcnt_hi(
+                    (uint32_t)(val >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)val, 0u));
+                if (ep >= 0) {
+                    g.vexp[v] = (int16_t)ep;
+                    g.vbeg[v] = (int16_t)v;
+                    g.vcnt[v] = 1;
+                    g.sorted[v] = (int16_t)p;
+                }
+                if (lane == 0) {
+                    g.D = __popcll(val);
+                    g.DV = __popcll(val);
+                }
+            }
+            if (lane == 0)
+                g.direct = direct;
+        }
+        lds_barrier();
+        if (uniform(g.direct))
+            return;
+    }
     // histogram: each valid pair takes the next position in its bucket
     const int ep = p < NP ? g.e[p] : -1;
     if (ep >= 0)
@@ -650,9 +691,25 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
                 du[c] = ok ? du[c] : u32x4{0, 0, 0, 0};
             }
         }
-        for (int jj = 0; jj < npair; ++jj) {
-            const int p = uniform(g.sorted[pb + jj]);
-            float ga = 0.0f, ua = 0.0f;
+        // fp8: the codes widened to bf16 once, for every pair of the unit
+        constexpr int kWc = W8 ? 2 * KC : KC;            // bf16 weight chunks per lane
+        u32x4 bg[kWc], bu[kWc];
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            if constexpr (W8) {
+                bg[2 * c] = e4m3x8_to_bf16(dg[c].x, dg[c].y);
+                bg[2 * c + 1] = e4m3x8_to_bf16(dg[c].z, dg[c].w);
+                bu[2 * c] = e4m3x8_to_bf16(du[c].x, du[c].y);
+                bu[2 * c + 1] = e4m3x8_to_bf16(du[c].z, du[c].w);
+            } else {
+                bg[c] = dg[c];
+                bu[c] = du[c];
+            }
+        }
+        // the lane's gate and up partial dots of pair p, chunks in order
+        auto dots = [&](int p, float &ga, float &ua) {
+            ga = 0.0f;
+            ua = 0.0f;
             if constexpr (W8) {
                 // chunk c holds columns 16 ch .. 16 ch + 15: x chunks 2 ch, 2 ch + 1
                 const u32x4 *xr = s_x + pair_token(p, NP, k) * xs + 2 * (kb * KC * kWave + lane);
@@ -660,21 +717,24 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
                 for (int c = 0; c < KC; ++c) {
                     const u32x4 x0 = XR ? xreg[2 * c % kXr] : xr[2 * c * kWave];
                     const u32x4 x1 = XR ? xreg[(2 * c + 1) % kXr] : xr[2 * c * kWave + 1];
-                    ga = dot8_bf16(e4m3x8_to_bf16(dg[c].x, dg[c].y), x0, ga);
-                    ga = dot8_bf16(e4m3x8_to_bf16(dg[c].z, dg[c].w), x1, ga);
-                    ua = dot8_bf16(e4m3x8_to_bf16(du[c].x, du[c].y), x0, ua);
-                    ua = dot8_bf16(e4m3x8_to_bf16(du[c].z, du[c].w), x1, ua);
+                    ga = dot8_bf16(bg[2 * c], x0, ga);
+                    ga = dot8_bf16(bg[2 * c + 1], x1, ga);
+                    ua = dot8_bf16(bu[2 * c], x0, ua);
+                    ua = dot8_bf16(bu[2 * c + 1], x1, ua);
                 }
             } else {
                 const u32x4 *xr = s_x + pair_token(p, NP, k) * xs + kb * KC * kWave + lane;
 #pragma unroll
                 for (int c = 0; c < KC; ++c) {
                     const u32x4 xv = XR ? xreg[c % kXr] : xr[c * kWave];
-                    ga = dot8_bf16(dg[c], xv, ga);
-                    ua = dot8_bf16(du[c], xv, ua);
+                    ga = dot8_bf16(bg[c], xv, ga);
+                    ua = dot8_bf16(bu[c], xv, ua);
                 }
             }
-            float gt = wave_total(ga), ut = wave_total(ua);
+        };
+        // the unit's reduced sums of its jj-th pair: added over K blocks,
+        // then queued for the epilogue
+        auto finish = [&](int jj, int p, float gt, float ut) {
             if (nbu > 1) {                               // uniform
                 if (kb > 0) {
                     const float2 a = s_acc[jj];
@@ -684,7 +744,7 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
                 if (kb < nbu - 1) {
                     if (lane == 0)
                         s_acc[jj] = make_float2(gt, ut);
-                    continue;
+                    return;
                 }
             }
             if constexpr (W8) {                          // the rows' scales
@@ -698,6 +758,12 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
             }
             if (++pend == kUpPend)
                 flush();
+        };
+        for (int jj = 0; jj < npair; ++jj) {
+            const int p = uniform(g.sorted[pb + jj]);
+            float ga, ua;
+            dots(p, ga, ua);
+            finish(jj, p, wave_total(ga), wave_total(ua));
         }
     };
 

@@ -68,31 +68,48 @@ __device__ __forceinline__ void sel_pop(uint64_t (&key)[KJ], bool adv)
 }
 
 
+// Selection key of logit v of expert e: order code << 32 | ~id, so a larger
+// key is a larger logit or an equal logit with a smaller id (keys of
+// distinct ids never tie); ids from E on get key 0, below every number
+// (k <= E keeps them unselected); NaN never outranks a number; -0 and +0
+// share a code.
+__device__ __forceinline__ uint64_t sel_key(float v, int e, int E)
+{
+    uint32_t u = __float_as_uint(v != v ? -INFINITY : v);
+    u = u == 0x80000000u ? 0u : u;
+    const uint32_t code = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+    return e < E ? ((uint64_t)code << 32) | (uint32_t)~(uint32_t)e : 0ull;
+}
+
+// Lane s < k holds the s-th selected key (descending): its expert id and
+// the softmax weight of the selected logits, taken in fp32, shifted by the
+// largest, summed over the wavefront in a fixed order.
+__device__ __forceinline__ void sel_softmax(uint64_t sel, int k, int lane, int &sel_idx,
+                                            float &sel_w)
+{
+    sel_idx = (int)~(uint32_t)sel;
+    const float my_v = f32_unorder((uint32_t)(sel >> 32));
+    const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
+    const float ex = (lane < k) ? expf(my_v - top) : 0.0f;
+    const float den = wave_sum(ex);
+    sel_w = ex / den;
+}
+
 // The k largest of this wavefront's logits lv[q] (id e = lane + 64 q, ids
 // from E on absent) and their softmax weights: lane s < k gets the s-th
 // selection (descending logit, ties to the lower id) and its weight. Every
 // lane sorts its logits by (value descending, id ascending) once; then each
 // of the k rounds takes the wave-wide maximum of the lane heads (DPP on the
 // 32-bit order code), breaks an equal-value tie by the lowest id, and
-// advances the winning lane's list. The softmax of the selected logits is
-// taken in fp32, shifted by the largest, summed over the wavefront in a
-// fixed order.
+// advances the winning lane's list.
 template <int KJ>
 __device__ __forceinline__ void topk_select(const float (&lv)[KJ], int E, int k, int lane,
                                             int &sel_idx, float &sel_w)
 {
-    // keys: order code << 32 | ~id; ids past E get key 0, below every number
-    // (k <= E keeps them unselected); NaN never outranks a number; -0 and +0
-    // share a code
     uint64_t key[KJ];
 #pragma unroll
-    for (int q = 0; q < KJ; ++q) {
-        const int e = lane + kWave * q;
-        uint32_t u = __float_as_uint(lv[q] != lv[q] ? -INFINITY : lv[q]);
-        u = u == 0x80000000u ? 0u : u;
-        const uint32_t code = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-        key[q] = e < E ? ((uint64_t)code << 32) | (uint32_t)~(uint32_t)e : 0ull;
-    }
+    for (int q = 0; q < KJ; ++q)
+        key[q] = sel_key(lv[q], lane + kWave * q, E);
     sel_sort<KJ>(key);
     uint64_t sel = 0;                            // lane s keeps selection s
     for (int s = 0; s < k; ++s) {
@@ -100,12 +117,7 @@ __device__ __forceinline__ void topk_select(const float (&lv)[KJ], int E, int k,
         sel = lane == s ? win : sel;
         sel_pop<KJ>(key, key[0] == win);         // the winner's next logit moves up
     }
-    sel_idx = (int)~(uint32_t)sel;
-    const float my_v = f32_unorder((uint32_t)(sel >> 32));
-    const float top = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_v), 0));
-    const float ex = (lane < k) ? expf(my_v - top) : 0.0f;
-    const float den = wave_sum(ex);
-    sel_w = ex / den;
+    sel_softmax(sel, k, lane, sel_idx, sel_w);
 }
 
 } // namespace mv

@@ -124,6 +124,8 @@ FP8_CASES = [
     (2, 6144, 128, 8, 2),        # two K blocks per unit: running sums across blocks
     (10, 512, 1024, 64, 8),      # the block-16 verify widths: 80 and 128 pairs
     (16, 256, 1024, 16, 8),      # 128 pairs over 16 experts: 8 pairs per column block
+    (12, 528, 1040, 40, 8),      # 96 pairs: a 16-element K tail, 8 rows in the last workgroup
+    (16, 256, 2064, 32, 16),     # 256 pairs, three K blocks of codes per down row
 ]
 
 
