@@ -212,7 +212,9 @@ def write_counters(args) -> None:
               f"--algo <algo json> --out {os.path.basename(args.out)}",
               f"# source digest (code of {', '.join(ALL_SOURCES)}): {src_digest(*ALL_SOURCES)}",
               "", f"Workload: {algo['workload']}.",
-              f"Distinct experts per expert call: {algo.get('distinct_experts')}.",
+              "Distinct experts per expert call (mean): " + (", ".join(
+                  f"{kd} {sum(v) / len(v):.2f} over {len(v)} calls"
+                  for kd, v in algo.get("distinct_experts", {}).items()) or "none") + ".",
               f"Counter to bytes: FETCH_SIZE x 1024 / {f_fac:.4f}, WRITE_SIZE x 1024 / "
               f"{w_fac:.4f} (the factors the calibration kernel, torch int32 bitwise_not over "
               f"{args.calib_mib} MiB in and out, reads in the same runs).",
@@ -272,7 +274,9 @@ def write_stats(args) -> None:
               f"--out {os.path.basename(args.out)}",
               f"# source digest (code of {', '.join(ALL_SOURCES)}): {src_digest(*ALL_SOURCES)}",
               "", f"Workload: {algo['workload']}.",
-              f"Distinct experts per expert call: {algo.get('distinct_experts')}.",
+              "Distinct experts per expert call (mean): " + (", ".join(
+                  f"{kd} {sum(v) / len(v):.2f} over {len(v)} calls"
+                  for kd, v in algo.get("distinct_experts", {}).items()) or "none") + ".",
               "Algorithmic bytes per call (mean): " + algo["definition"], "",
               "| kernel | calls | avg us | min us | max us | algorithmic MB | TB/s | % of 8 TB/s |",
               "|---|---|---|---|---|---|---|---|"]
