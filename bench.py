@@ -251,10 +251,13 @@ def write_stats(args) -> None:
     """Average duration of every kernel of a profile run (rocprofv3 --stats
     kernel_stats.csv), with the algorithmic bytes the run logged and the
     rate they imply."""
-    if not (args.algo and args.out):
-        raise SystemExit("--write-stats needs --algo and --out")
-    with open(args.algo) as f:
-        algo = json.load(f)
+    if not args.out:
+        raise SystemExit("--write-stats needs --out")
+    algo = {"workload": args.title or "see the command", "classes": {},
+            "definition": "not given for this run (see the bench line for the step's bytes)"}
+    if args.algo:
+        with open(args.algo) as f:
+            algo = json.load(f)
     rows = []
     with open(args.write_stats, newline="") as f:
         for row in csv.DictReader(f):
@@ -270,8 +273,8 @@ def write_stats(args) -> None:
     lines = [f"# {args.title}" if args.title else "# rocprofv3 kernel stats",
              "# commands (repository root on the GPU box, TMPDIR=/tmp):"]
     lines += [f"#   {c}" for c in args.cmd]
-    lines += [f"# summary: python3 bench.py --write-stats <kernel_stats.csv> --algo <algo json> "
-              f"--out {os.path.basename(args.out)}",
+    lines += [f"# summary: python3 bench.py --write-stats <kernel_stats.csv> "
+              f"{'--algo <algo json> ' if args.algo else ''}--out {os.path.basename(args.out)}",
               f"# source digest (code of {', '.join(ALL_SOURCES)}): {src_digest(*ALL_SOURCES)}",
               "", f"Workload: {algo['workload']}.",
               "Distinct experts per expert call (mean): " + (", ".join(

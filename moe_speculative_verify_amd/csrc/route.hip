@@ -17,9 +17,10 @@
 //     latter hit in L2) at once, then runs one MFMA per 32 (or 64) columns.
 //     The partial tiles are added in LDS in a fixed order and each slice's
 //     partial logits published with device-scope stores;
-//   - the last workgroup to arrive (two-level ticket of device-scope
-//     atomics; no spinning, no cache flush) adds each logit's slice partials
-//     in slice order and the bias, then selects, one wavefront per token:
+//   - the last workgroup to arrive (two-level ticket counted with
+//     agent-scope releases and acquired on the chain; no spinning) adds each
+//     logit's slice partials in slice order and the bias, then selects, one
+//     wavefront per token:
 //     every lane sorts its logits by (value descending, id ascending) once;
 //     then each of the k rounds takes the wave-wide maximum of the lane heads
 //     (DPP on the 32-bit order code), breaks an equal-value tie by the
