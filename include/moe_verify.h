@@ -70,8 +70,13 @@
  *     without clearing.
  *     Two calls that may run concurrently must not share a workspace.
  *   - Results are deterministic: no floating-point atomics; rerunning a
- *     call on the same inputs gives bitwise-equal outputs, and a token's
- *     results do not depend on the other tokens in the call.
+ *     call on the same inputs gives bitwise-equal outputs. A token's results
+ *     do not depend on the other tokens in the call as long as M stays on
+ *     the same side of two regime limits: the router sums a logit over
+ *     8-row tiles for M <= 8 and 16-row tiles above, and the down
+ *     projection takes its matrix-core kernel once the pairs' activations
+ *     (M*k*I*2 bytes) pass 150 KB. Across them the sums run in another
+ *     order and agree within rounding.
  */
 #ifndef MOE_VERIFY_H
 #define MOE_VERIFY_H

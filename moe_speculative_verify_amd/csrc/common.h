@@ -82,6 +82,57 @@ __device__ __forceinline__ int dpp_i32(int v)
 {
     return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
+// The value v of lane (lane ^ S) of the wavefront (S a power of two below
+// 64; every lane active): DPP inside a quad (S = 1, 2) or a row (S = 8:
+// rotate by 8), ds_swizzle inside 32 lanes (S = 4, 16: bitmask mode, xor S),
+// ds_bpermute across the halves (S = 32).
+template <int S>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v)
+{
+    const int iv = (int)v;
+    if constexpr (S == 1)
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false);
+    else if constexpr (S == 2)
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false);
+    else if constexpr (S == 8)
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, iv, 0x128, 0xF, 0xF, false);
+    else if constexpr (S == 4 || S == 16)
+        return (uint32_t)__builtin_amdgcn_ds_swizzle(iv, 0x1F | (S << 10));
+    else {
+        static_assert(S == 32, "lane_xor: S in 1, 2, 4, 8, 16, 32");
+        return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((threadIdx.x & 63u) ^ 32u) << 2), iv);
+    }
+}
+
+// One compare-exchange step of a bitonic sort across the wavefront: lane i
+// meets lane i ^ STRIDE; in blocks of SIZE lanes that ascend ((i & SIZE) ==
+// 0) the lower lane keeps the smaller key, in descending blocks the larger.
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ uint32_t wave_sort_step(uint32_t v, int lane)
+{
+    const uint32_t p = lane_xor<STRIDE>(v);
+    const bool up = (lane & SIZE) == 0, low = (lane & STRIDE) == 0;
+    return up == low ? min(v, p) : max(v, p);
+}
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ uint32_t wave_sort_merge(uint32_t v, int lane)
+{
+    v = wave_sort_step<SIZE, STRIDE>(v, lane);
+    if constexpr (STRIDE > 1)
+        v = wave_sort_merge<SIZE, STRIDE / 2>(v, lane);
+    return v;
+}
+// Ascending bitonic sort of one 32-bit key per lane over the 64 lanes (21
+// compare-exchange steps): lane i ends with the i-th smallest key.
+template <int SIZE = 2>
+__device__ __forceinline__ uint32_t wave_sort_asc(uint32_t v, int lane)
+{
+    v = wave_sort_merge<SIZE, SIZE / 2>(v, lane);
+    if constexpr (SIZE < 64)
+        v = wave_sort_asc<SIZE * 2>(v, lane);
+    return v;
+}
+
 constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- 7-i within 8

@@ -75,7 +75,6 @@ constexpr int kBinsPerThread = kMaxE / kGroupThreads;
 struct Groups {
     int D;                       // distinct valid experts
     int DV;                      // column blocks
-    int direct;                  // built by the few-distinct-pairs path
     int wsum[kGroupThreads / kWave];   // per-wavefront totals of the scan
     int bins[kMaxE];             // pairs per expert, then bucket offsets
     int16_t e[kMaxNP];           // expert of pair p, -1 if out of range
@@ -112,11 +111,16 @@ __device__ inline void groups_set_pairs(int idx, int NP, int E, Groups &g)
         g.bins[i * kGroupThreads + p] = 0;
 }
 
-// Few pairs, all in distinct experts (one verify token: the router never
-// picks an expert twice for a token): every valid pair is a bucket of its
-// own and its own column block, in pair order, found by wavefront 0 without
-// the histogram -- the blocks the histogram would build, in another order,
-// which no result depends on. Pairs that share an expert take the histogram.
+// At most 64 pairs (M <= 8 at k = 8): wavefront 0 builds the buckets alone,
+// behind one barrier. With at most 16 pairs whose valid experts are all
+// distinct (one verify token: the router never picks an expert twice for a
+// token) every valid pair is a bucket and a column block of its own, in
+// pair order, read off the ids with readlane compares and a ballot.
+// Otherwise the pairs' (expert, pair) keys are sorted across the wavefront
+// (bitonic), the lanes where the expert changes start the buckets, and each
+// bucket is cut into column blocks of 16 from its first lane. Either way the
+// blocks hold what the histogram would build, in another order, which no
+// result depends on. Above 64 pairs the histogram below runs.
 constexpr int kDirectNP = 16;
 
 __device__ inline void groups_finish(int NP, Groups &g)
@@ -125,16 +129,15 @@ __device__ inline void groups_finish(int NP, Groups &g)
     const int lane = p & (kWave - 1), wave = p / kWave;
     const bool gp = p < kGroupThreads;           // uniform per wavefront
     lds_barrier();
-    if (NP <= kDirectNP) {                       // uniform
+    if (NP <= kWave) {                           // uniform
         if (wave == 0) {
             const int ep = p < NP ? g.e[p] : -1;
-            bool dup = false;
-            for (int q = 0; q < NP; ++q) {
+            bool dup = NP > kDirectNP;
+            for (int q = 0; q < NP && NP <= kDirectNP; ++q) {
                 const int eq = __builtin_amdgcn_readlane(ep, q);
                 dup = dup || (q < p && ep >= 0 && eq == ep);
             }
-            const bool direct = __ballot(dup) == 0;
-            if (direct) {
+            if (__ballot(dup) == 0) {
                 const unsigned long long val = __ballot(ep >= 0);
                 // valid pairs before this one: its block index
                 const int v = __builtin_amdgcn_mbcnt_hi(
@@ -149,13 +152,38 @@ __device__ inline void groups_finish(int NP, Groups &g)
                     g.D = __popcll(val);
                     g.DV = __popcll(val);
                 }
+            } else {
+                // key expert << 8 | pair, invalid pairs (and lanes past NP) last
+                uint32_t key = ep >= 0 ? ((uint32_t)ep << 8) | (uint32_t)p : 0xFFFFFFFFu;
+                key = wave_sort_asc(key, lane);
+                const bool valid = key != 0xFFFFFFFFu;
+                const int e = (int)(key >> 8), pr = (int)(key & 0xFFu);
+                const int nvalid = __popcll(__ballot(valid));      // lanes 0 .. nvalid - 1
+                const int eprev = __builtin_amdgcn_ds_bpermute((int)(((unsigned)lane + 63u) & 63u) << 2, e);
+                const bool bstart = valid && (lane == 0 || e != eprev);
+                const unsigned long long smask = __ballot(bstart);
+                const unsigned long long upto = (2ull << lane) - 1ull;     // lanes 0 .. lane
+                const unsigned long long above = smask & ~upto;
+                const int bfirst = 63 - __clzll(smask & upto);   // this bucket's first lane
+                const int bend = above ? __ffsll(above) - 1 : nvalid;
+                const bool vstart = valid && (lane - bfirst) % 16 == 0;
+                const unsigned long long cmask = __ballot(vstart);
+                const int v = __popcll(cmask & upto) - 1;
+                if (valid)
+                    g.sorted[lane] = (int16_t)pr;
+                if (vstart) {
+                    g.vexp[v] = (int16_t)e;
+                    g.vbeg[v] = (int16_t)lane;
+                    g.vcnt[v] = (int16_t)min(16, bend - lane);
+                }
+                if (lane == 0) {
+                    g.D = __popcll(smask);
+                    g.DV = __popcll(cmask);
+                }
             }
-            if (lane == 0)
-                g.direct = direct;
         }
         lds_barrier();
-        if (uniform(g.direct))
-            return;
+        return;
     }
     // histogram: each valid pair takes the next position in its bucket
     const int ep = p < NP ? g.e[p] : -1;
