@@ -25,9 +25,9 @@
 //     workgroup's best per token becomes a 64-bit key (order-preserving
 //     value bits << 32 | ~index, so the largest value and then the lowest
 //     index win) stored in the workgroup's own slot of the workspace. The
-//     last workgroup to arrive (two-level ticket counted with agent-scope
-//     releases and acquired on the chain; no spinning) takes each token's
-//     maximum over the slots and decodes it. Every slot is written before it is read, so nothing
+//     last workgroup to arrive (one ticket counted with agent-scope
+//     releases, acquired by the last arrival; no spinning) takes each
+//     token's maximum over the slots and decodes it. Every slot is written before it is read, so nothing
 //     past the header needs to be zero.
 //   - fp8 weights (lmhead_argmax_fp8, lmhead_greedy_verify_fp8): OCP E4M3
 //     codes with one fp32 scale per vocabulary row. A block is still 512
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     // them with its arrival, and the last arrival acquires every slot
     __syncthreads();
     if (threadIdx.x == 0)
-        s_last = arrive_last(ticket);
+        s_last = arrive_last_flat(ticket);
     __syncthreads();
     if (!s_last)
         return;
