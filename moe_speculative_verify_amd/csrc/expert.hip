@@ -512,6 +512,47 @@ __host__ __device__ inline int up_row(int u, int I)
     return (u % I + u / I) % I;
 }
 
+// The units of workgroup b. Workgroup b runs on XCD b % 8 (workgroups are
+// dealt to the XCDs in turn), and under a full-chip read the odd-numbered
+// XCDs stream several percent slower than the even ones (a plain streaming
+// probe with no arithmetic shows it for every row pattern, as do the up
+// kernel's per-XCD end times). So the units come in periods of R rounds of G
+// (one unit per workgroup, dealt in turn: a moving window, every column block
+// spread over every workgroup) plus one unit for each even-numbered
+// workgroup: those take R + 1 units per period, the odd ones R. A partial
+// last period deals its rounds first. R = 0: plain rounds. Every unit is
+// taken exactly once whatever the placement; only the balance depends on it.
+// Paired A/B of the layer (both builds in one process, calls alternated on
+// cold layers): bf16 with R = 10, 1.4 us less at M = 6 and 3.5 us less at
+// M = 16, no change at M = 1 and on Zipf-routed M = 16; the fp8 kernel, which
+// streams below the chip's read rate, got slower with any R (10, 20, 30), so
+// it keeps plain rounds.
+__host__ __device__ inline int up_count(int N, int b, int G, int R)
+{
+    if (R == 0)
+        return N > b ? (N - 1 - b) / G + 1 : 0;
+    const int ge = (G + 1) / 2, P = R * G + ge;          // units per period
+    const int F = N / P, rem = N - F * P;
+    const bool even = (b & 1) == 0;
+    const int ord = min(rem, R * G);                     // the partial period's rounds
+    int n = F * (R + (even ? 1 : 0)) + (ord > b ? (ord - 1 - b) / G + 1 : 0);
+    if (even && rem - R * G > b / 2)
+        ++n;
+    return n;
+}
+__host__ __device__ inline int up_unit(int j, int N, int b, int G, int R)
+{
+    if (R == 0)
+        return b + G * j;
+    const int ge = (G + 1) / 2, P = R * G + ge;
+    const int S = R + ((b & 1) == 0 ? 1 : 0);            // slots per full period
+    const int F = N / P;
+    const int f = j < F * S ? j / S : F, s = j < F * S ? j % S : j - F * S;
+    return f * P + (s < R ? s * G + b : R * G + b / 2);
+}
+constexpr int kUpRounds = 10;                    // bf16: even XCDs take 11 units to 10
+constexpr int kUpRounds8 = 0;                    // fp8: plain rounds
+
 // The router's selection when it runs in the up kernel (moe_layer): the
 // partial logits [nks][M][E] of the router kernel (slices of the hidden
 // dimension), the optional bias, and where workgroup 0 writes the selection.
@@ -660,7 +701,8 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
     }
 
     const int nunits = uniform(g.DV) * I;
-    const int nwg = nunits > (int)blockIdx.x ? (nunits - 1 - (int)blockIdx.x) / gridDim.x + 1 : 0;
+    constexpr int kR = W8 ? kUpRounds8 : kUpRounds;
+    const int nwg = up_count(nunits, (int)blockIdx.x, (int)gridDim.x, kR);
 
     int pend = 0;                                        // uniform
     auto flush = [&]() {
@@ -675,7 +717,7 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
         if (lane == 0)
             j = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         j = uniform(__builtin_amdgcn_readlane(j, 0));
-        return j < nwg ? (int)blockIdx.x + (int)gridDim.x * j : -1;
+        return j < nwg ? up_unit(j, nunits, (int)blockIdx.x, (int)gridDim.x, kR) : -1;
     };
     // Tag of a block: unit * 16 + kb, or -1 past the end; a unit's K blocks
     // stay on one wavefront

@@ -140,6 +140,11 @@ FFN_CASES = [
     (7, 512, 1032, 40, 3),       # I not a multiple of the 512-element lane stride
     (1, 1032, 256, 12, 3),       # one token, x in registers, a partial last chunk column
     (1, 3072, 256, 16, 4),       # one token, two K blocks per unit: x staged in LDS
+    # the up kernel deals its units in periods of 10 rounds of 256 plus 128
+    # units for the even-numbered workgroups (2688); a partial last period
+    # deals its rounds first, then the rest to the even ones:
+    (1, 256, 1304, 8, 2),        # 2608 units: 48 past the partial period's rounds
+    (1, 3072, 3992, 8, 2),       # 7984 = 2 periods + 2608, two K blocks per unit
 ]
 
 
