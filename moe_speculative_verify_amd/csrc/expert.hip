@@ -121,9 +121,13 @@ __device__ inline void groups_set_pairs(int idx, int NP, int E, Groups &g)
 // bucket is cut into column blocks of 16 from its first lane. Either way the
 // blocks hold what the histogram would build, in another order, which no
 // result depends on. Above 64 pairs the histogram below runs.
+// first_e (the shared expert, or -1): its blocks come first, the others
+// keep expert order. Its bucket holds every token, so its blocks cost the
+// most arithmetic; taken last they would leave a tail of it after the
+// streaming has ended.
 constexpr int kDirectNP = 16;
 
-__device__ inline void groups_finish(int NP, Groups &g)
+__device__ inline void groups_finish(int NP, Groups &g, int first_e = -1)
 {
     const int p = threadIdx.x;
     const int lane = p & (kWave - 1), wave = p / kWave;
@@ -153,11 +157,14 @@ __device__ inline void groups_finish(int NP, Groups &g)
                     g.DV = __popcll(val);
                 }
             } else {
-                // key expert << 8 | pair, invalid pairs (and lanes past NP) last
-                uint32_t key = ep >= 0 ? ((uint32_t)ep << 8) | (uint32_t)p : 0xFFFFFFFFu;
+                // key (expert + 1, or 0 for first_e) << 8 | pair, invalid
+                // pairs (and lanes past NP) last
+                const uint32_t eord = ep == first_e ? 0u : (uint32_t)ep + 1u;
+                uint32_t key = ep >= 0 ? (eord << 8) | (uint32_t)p : 0xFFFFFFFFu;
                 key = wave_sort_asc(key, lane);
                 const bool valid = key != 0xFFFFFFFFu;
-                const int e = (int)(key >> 8), pr = (int)(key & 0xFFu);
+                const int e = (key >> 8) == 0 ? first_e : (int)(key >> 8) - 1;
+                const int pr = (int)(key & 0xFFu);
                 const int nvalid = __popcll(__ballot(valid));      // lanes 0 .. nvalid - 1
                 const int eprev = __builtin_amdgcn_ds_bpermute((int)(((unsigned)lane + 63u) & 63u) << 2, e);
                 const bool bstart = valid && (lane == 0 || e != eprev);
@@ -195,6 +202,8 @@ __device__ inline void groups_finish(int NP, Groups &g)
     // index), 20-29 column blocks (first block); every total is <= 256
     int cnt[kBinsPerThread], pk[kBinsPerThread];
     int tsum = 0, incl = 0;
+    // first_e's column blocks, which move to the front
+    const int nbf = first_e >= 0 ? (g.bins[first_e] + 15) >> 4 : 0;
     if (gp) {
 #pragma unroll
         for (int i = 0; i < kBinsPerThread; ++i) {
@@ -228,7 +237,8 @@ __device__ inline void groups_finish(int NP, Groups &g)
             const int expert = p * kBinsPerThread + i;
             g.bins[expert] = off;                     // bucket offset for the scatter
             for (int o = 0; o < cnt[i]; o += 16) {
-                const int v = v0 + o / 16;
+                const int v = expert == first_e ? o / 16
+                                                : v0 + o / 16 + (expert < first_e ? nbf : 0);
                 g.vexp[v] = (int16_t)expert;
                 g.vbeg[v] = (int16_t)(off + o);
                 g.vcnt[v] = (int16_t)(cnt[i] - o < 16 ? cnt[i] - o : 16);
@@ -305,7 +315,7 @@ __global__ __launch_bounds__(WV * kWave) void expert_down_kernel(
             s_tw[threadIdx.x] = pw;
         if (threadIdx.x == 0)
             s_next = 0;
-        groups_finish(NPT, g);                           // (its barriers also publish s_next)
+        groups_finish(NPT, g, ns ? E : -1);              // (its barriers also publish s_next)
     }
 
     const int DV = uniform(g.DV);
@@ -694,7 +704,7 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
             s_x[t * xs + c] = u32x4{0, 0, 0, 0};         // K padding reads as zero
         }
     }
-    groups_finish(NPT, g);                               // (its barriers also publish s_next)
+    groups_finish(NPT, g, ns ? E : -1);                  // (its barriers also publish s_next)
     if constexpr (!XR) {
         wait_vmcnt<0>();                                 // this wave's share of x has landed
         lds_barrier();                                   // ... and every other wave's
@@ -928,7 +938,7 @@ __global__ __launch_bounds__(WV * kWave) void expert_down_gemv_kernel(
     wait_vmcnt<0>();                                     // only the pair id and weight are in flight
     if ((int)threadIdx.x < NP)
         s_tw[threadIdx.x] = pw;
-    groups_finish(NPT, g);                               // (its barriers also publish s_next)
+    groups_finish(NPT, g, ns ? E : -1);                  // (its barriers also publish s_next)
 
     // Blocks B = v * nkb + kb (column block v, K block kb), claimed one at a
     // time by the workgroup's wavefronts from an LDS counter (a SIMD serves
