@@ -482,11 +482,11 @@ __device__ __forceinline__ float wave_total(float v)
 // Units are (column block v, row i of I), in order, so the chip streams one
 // moving window of the weights; a block is the unit's gate row and up row,
 // KC loads of 1 KB each per matrix per K block, streamed into registers.
-// Workgroup b (one per CU) owns units b, b + G, b + 2G, ..., and its kUpWaves
-// wavefronts claim them one at a time from an LDS counter, each waiting for
-// the block it just issued: a SIMD serves its older wavefront first, and the
-// claims let that one take more units instead of the younger ones ending
-// last. For every pair of the column block each lane forms its gate and up
+// The units are dealt to the workgroups (one per CU) in rounds (up_count,
+// up_unit below), and a workgroup's kUpWaves wavefronts claim its units one
+// at a time from an LDS counter, each waiting for the block it just issued:
+// a SIMD serves its older wavefront first, and the claims let that one take
+// more units instead of the younger ones ending last. For every pair of the column block each lane forms its gate and up
 // partial dots and two DPP trees reduce them; lane 0 queues the sums, and
 // every 64 queued outputs the 64 lanes take a = bf16(silu(g) * u) (fp32,
 // one rounding), one output each. With more than KC * 64 chunks per row a
