@@ -390,9 +390,9 @@ __global__ __launch_bounds__(WV * kWave) void expert_down_kernel(
             const int p = g.sorted[uniform(g.vbeg[v]) + (col_ok ? j : 0)];
             u32x4 bf[kXSteps];
 #pragma unroll
-            for (int s = 0; s < kXSteps; ++s) {
+            for (int s = 0; s < kXSteps; ++s) {              // (no load where no pair)
                 const int c = min(kb * (kXKB / 8) + 4 * s + gq, nch - 1);
-                bf[s] = act[(size_t)p * nch + c];
+                bf[s] = col_ok ? act[(size_t)p * nch + c] : u32x4{0, 0, 0, 0};
             }
             const int nq = (q + NB - 1) % NB;
             if constexpr (NB > 1) {
