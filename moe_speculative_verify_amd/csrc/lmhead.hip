@@ -64,9 +64,9 @@ __host__ __device__ static size_t lm_x_bytes(int M, int H, bool w8)
     const int nkb = (H + KB - 1) / KB;
     return align_up((size_t)M * (nkb * (KB / 8) + 1) * 16, 256);
 }
-static size_t lm_lds_bytes(int M, int H, bool w8)
+static size_t lm_lds_bytes(int M, int H, bool w8, int nslot = 2)
 {
-    return lm_x_bytes(M, H, w8) + (size_t)kLmWaves * 2 * kLmBuf;
+    return lm_x_bytes(M, H, w8) + (size_t)kLmWaves * nslot * kLmBuf;
 }
 
 template <bool W8>
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     int V, unsigned long long *__restrict__ keys,
     unsigned *__restrict__ ticket, int *__restrict__ argmax,
     float *__restrict__ max_logit, const int *__restrict__ tokens,
-    int *__restrict__ accept)
+    int *__restrict__ accept, int nslot)
 {
     constexpr int KB = lm_kb(W8);
     constexpr int kLmSteps = KB / 32;                    // MFMA steps per block
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     const int nkb = (H + KB - 1) / KB;
     const int xs = nkb * (KB / 8) + 1;                   // padded x row, chunks
     u32x4 *s_x = (u32x4 *)smem;
-    unsigned char *wbuf = smem + lm_x_bytes(M, H, W8) + wave * 2 * kLmBuf;
+    unsigned char *wbuf = smem + lm_x_bytes(M, H, W8) + wave * nslot * kLmBuf;
 
     // hidden states into LDS with direct-to-LDS loads (all in flight at
     // once), K padding zeroed
@@ -118,10 +118,15 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     float bv = -INFINITY;
     int bi = kNoRow;
 
-    // The double buffer runs across tiles: while a tile's last block is
-    // consumed, the next tile's first block is already in flight, so every
-    // wavefront keeps one block in flight from its first tile to its last.
-    // Block n of the wavefront (counted over its tiles) sits in buffer n & 1.
+    // The ring runs across tiles: while a tile's last block is consumed, the
+    // next tile's first block is already in flight, so every wavefront keeps
+    // one block in flight from its first tile to its last. Where the LDS
+    // holds a third slot per wavefront (nslot = 3), the last tile keeps two
+    // blocks in flight: by then most wavefronts have finished and the HBM
+    // has room, and a wavefront's single block in flight would set the pace
+    // (paired: 0.9 us less per call at M = 6, 0.8 at M = 1; two blocks ahead
+    // in every tile measured slower). Block n of the wavefront (counted over
+    // its tiles) sits in slot n % nslot.
     auto tile_rows = [&](int tile, const u32x4 *(&rp)[kLmLoads]) {
 #pragma unroll
         for (int q = 0; q < kLmLoads; ++q) {
@@ -164,13 +169,25 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
                 rs[r] = g == 0 ? sc[r] : g == 1 ? sc[4 + r] : g == 2 ? sc[8 + r] : sc[12 + r];
         }
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        const bool deep = !more && nslot == 3;           // the last tile: two blocks ahead
         for (int kb = 0; kb < nkb; ++kb) {
-            const int b = (nblk + kb) & 1;
-            if (kb + 1 < nkb) {
-                issue(rp, kb + 1, b ^ 1);
+            const int b = (nblk + kb) % nslot;
+            if (deep) {
+                if (kb == 0 && kb + 1 < nkb)
+                    issue(rp, kb + 1, (b + 1) % 3);
+                if (kb + 2 < nkb)
+                    issue(rp, kb + 2, (b + 2) % 3);
+                if (kb + 2 < nkb)
+                    wait_vmcnt<2 * kLmLoads>();          // block kb has landed
+                else if (kb + 1 < nkb)
+                    wait_vmcnt<kLmLoads>();
+                else
+                    wait_vmcnt<0>();
+            } else if (kb + 1 < nkb) {
+                issue(rp, kb + 1, (b + 1) % nslot);
                 wait_vmcnt<kLmLoads>();                  // block kb has landed
             } else if (more) {
-                issue(rpn, 0, b ^ 1);                    // the next tile's first block
+                issue(rpn, 0, (b + 1) % nslot);          // the next tile's first block
                 wait_vmcnt<kLmLoads>();
             } else {
                 wait_vmcnt<0>();
@@ -336,7 +353,8 @@ static moe_status_t lmhead_enqueue(const uint16_t *h, const void *w_lm, const fl
     unsigned long long *keys = (unsigned long long *)((char *)workspace + kWsHeader);
     const int ntiles = (V + 15) / 16;
     const int grid = min(ntiles, kLmGridTarget);
-    const size_t lds = lm_lds_bytes(M, H, w8);
+    const int nslot = lm_lds_bytes(M, H, w8, 3) <= (size_t)kLdsDynMax ? 3 : 2;
+    const size_t lds = lm_lds_bytes(M, H, w8, nslot);
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
@@ -351,11 +369,11 @@ static moe_status_t lmhead_enqueue(const uint16_t *h, const void *w_lm, const fl
     if (w8)
         hipLaunchKernelGGL(lmhead_kernel<true>, dim3(grid), dim3(kLmWaves * kWave), lds,
                            (hipStream_t)stream, (const u32x4 *)h, (const u32x4 *)w_lm, w_scale,
-                           M, H, V, keys, ticket, argmax, max_logit, tokens, accept);
+                           M, H, V, keys, ticket, argmax, max_logit, tokens, accept, nslot);
     else
         hipLaunchKernelGGL(lmhead_kernel<false>, dim3(grid), dim3(kLmWaves * kWave), lds,
                            (hipStream_t)stream, (const u32x4 *)h, (const u32x4 *)w_lm, nullptr,
-                           M, H, V, keys, ticket, argmax, max_logit, tokens, accept);
+                           M, H, V, keys, ticket, argmax, max_logit, tokens, accept, nslot);
     return check_launch();
 }
 
