@@ -6,8 +6,10 @@ meet in combinations no hand-picked case covers: unit counts that end
 anywhere in the up kernel's dealing periods, column blocks of one to sixteen
 pairs in every grouping path (with and without the shared expert, whose
 blocks go first), K tails of every length, both down kernels, and lm_head
-tile counts and K blocks that leave partial tiles and partial rings. The
-draws come from one fixed seed; the case list is the same on every run.
+tile counts and K blocks that leave partial tiles and partial rings, and
+whole layers whose selection runs in the up kernel (ragged E, one to four
+slices of H). The draws come from one fixed seed; the case list is the same
+on every run.
 
 Acceptance as in every parity test: expert-FFN outputs within
 1e-2 * max|ref|; argmax exact except at oracle-flagged near-ties, where the
@@ -21,7 +23,7 @@ import torch
 import moe_speculative_verify_amd as mv
 import oracle
 import synth
-from gpu_util import TIE_BAND, assert_close, to_dev
+from gpu_util import TIE_BAND, assert_close, check_tie_rows, compare_route, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -151,3 +153,42 @@ def test_random_lmhead_verdict(c, w8, M, H, V):
     assert_close(ml, ref["zmax"], "max_logit")
     n, bonus = oracle.greedy_verdict(tokens, am)
     assert (acc[0], acc[1]) == (n, bonus)
+
+
+def _layer_cases(n):
+    rng = np.random.default_rng(SEED + 2)
+    cases = []
+    for c in range(n):
+        M = int(rng.integers(1, 17))
+        E = int(rng.integers(2, 513))                # E <= 512: the up kernel selects
+        k = int(rng.integers(1, min(E, 16) + 1))
+        H = _mult(rng, 8, 1024, 8)
+        I = _mult(rng, 8, 1024, 8)
+        while E * H * I > 40_000_000:               # keep the host weights small
+            E = max(k, E // 2)
+        alpha = [None, 0.5, 1.0][c % 3]
+        cases.append((c, M, H, I, E, k, alpha))
+    return cases
+
+
+@pytest.mark.parametrize("c,M,H,I,E,k,alpha", _layer_cases(12))
+def test_random_layer(c, M, H, I, E, k, alpha):
+    """moe_layer (selection inside the up kernel from the router kernel's
+    partial logits) against the oracle's route and FFN: ids and weights
+    exact away from near-ties, outputs within tolerance; a near-tie row's
+    output checked against the oracle FFN on the GPU's own selection."""
+    say("random layer", c, M, H, I, E, k, alpha)
+    x = synth.activations(M, H, seed=7700 + c)
+    w = synth.layer_weights(H, E, I, seed=synth.WEIGHT_SEED + 7800 + c)
+    bias = None if alpha is None else synth.zipf_bias(E, alpha)
+    b = None if bias is None else torch.from_numpy(bias).cuda()
+    gi, gw, go = mv.moe_layer(to_dev(x), to_dev(w["router"]), to_dev(w["gate"]), to_dev(w["up"]),
+                              to_dev(w["down"]), k, b)
+    torch.cuda.synchronize()
+    gi, gw, go = gi.cpu().numpy(), gw.cpu().numpy(), go.cpu().numpy()
+    ref = oracle.route(x, w["router"], bias, k)
+    same = compare_route(gi, gw, None, ref, k)
+    out = oracle.expert_ffn(x, ref["idx"], ref["w"], w["gate"], w["up"], w["down"])
+    assert_close(go[same], out[same], "out")
+    check_tie_rows(x, gi, gw, go, ref, lambda xr, ids, tw: oracle.expert_ffn(
+        xr, ids, tw, w["gate"], w["up"], w["down"]))
