@@ -12,11 +12,12 @@
 //     at any moment the whole chip streams one window of neighbouring tiles
 //     (the access order of the fastest plain read measured on this part).
 //   - A wavefront streams its tile K-block by K-block (KB elements of each of
-//     the 16 rows) straight from HBM into its own LDS double buffer with
-//     non-temporal 128-bit direct-to-LDS loads: every load instruction reads
-//     1 KB made of two 512-byte row runs, the access pattern that reaches the
-//     HBM roofline, and the next block is in flight while the current one is
-//     consumed.
+//     the 16 rows) straight from HBM into its own LDS ring (two slots, a
+//     third where the LDS has room) with non-temporal 128-bit direct-to-LDS
+//     loads: every load instruction reads 1 KB made of two 512-byte row
+//     runs, the access pattern that reaches the HBM roofline, and the next
+//     block is in flight while the current one is consumed (the next two in
+//     the wavefront's last tile, when it has a third slot).
 //   - The dot products run on the matrix cores: v_mfma_f32_16x16x32_bf16
 //     with A = 16 weight rows (from LDS) and B = the M <= 16 hidden states
 //     (staged once per workgroup in LDS, zero columns beyond M). One MFMA
