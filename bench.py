@@ -619,6 +619,32 @@ def main():
         torch.cuda.synchronize()
         gate_sweep[str(n)] = round(re0.elapsed_time(re1) * 1e3 / (2 * R), 2)
 
+    # the gate as a steady stream: 128 back-to-back calls on distinct cold
+    # copies captured in one HIP graph, replayed, timed by events / 128
+    gate_graph = None
+    if args.graph_steps > 0:
+        GN = min(128, R)
+        capg = torch.cuda.Stream()
+        g_gate = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_gate, stream=capg):
+            for s in range(GN):
+                check("moe_route", L.moe_route(*(route_args[s][:-1] + (capg.cuda_stream,))))
+        g_gate.replay()
+        torch.cuda.synchronize()
+        reps = 4
+        ge = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ge[0].record()
+        for r in range(reps):
+            g_gate.replay()
+            ge[r + 1].record()
+        torch.cuda.synchronize()
+        gate_graph_us = sum(ge[r].elapsed_time(ge[r + 1]) for r in range(reps)) * 1e3 / (reps * GN)
+        gate_graph = {"calls_per_graph": GN, "replays": reps, "us": round(gate_graph_us, 2),
+                      "GBps": round(route_bytes / (gate_graph_us * 1e-6) / 1e9, 1)}
+        del g_gate
+        log(f"gate graph: {GN} back-to-back calls, {gate_graph_us:.2f} us per call "
+            f"({gate_graph['GBps']} GB/s)")
+
     for s in range(min(R, 16)):
         check("moe_route_rmsnorm", L.moe_route_rmsnorm(*rn_args[s]))
     torch.cuda.synchronize()
@@ -751,7 +777,8 @@ def main():
                            "bytes_per_call": 2**30, "buffers_rotated": 4, "calls": 16},
         "router_gate_cold": {"us": round(route_us, 2),
                              "GBps": round(route_bytes / (route_us * 1e-6) / 1e9, 1),
-                             "copies": R, "us_by_distinct_copies": gate_sweep},
+                             "copies": R, "us_by_distinct_copies": gate_sweep,
+                             "graph_of_back_to_back_calls": gate_graph},
         "router_chain_rmsnorm": {"gate_us": round(route_norm_us, 2),
                                  "moe_layer_rmsnorm": layer_norm},
         "moe_layer_shared_expert": layer_shared,
