@@ -784,7 +784,8 @@ def main():
         "moe_layer_shared_expert": layer_shared,
         "fp8_weights": fp8,
         "roofline": {"kernel": f"lmhead_kernel<false> (lmhead_greedy_verify, {V}x{H} bf16, M={M}),"
-                               " the step's longest kernel",
+                               " the step's longest kernel; timed as the whole call, which also"
+                               " holds the one-workgroup lmhead_merge_kernel behind it",
                      "bound": "hbm", "achieved": round(lm_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(lm_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": traffic},

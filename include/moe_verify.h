@@ -391,7 +391,9 @@ moe_status_t moe_layer_rmsnorm(const uint16_t *h, const uint16_t *gamma, float e
  *   workspace               lmhead_argmax_workspace_bytes(M, V) bytes: the
  *                           counter header and one M-key slot per workgroup
  *                           (each workgroup's per-token winner, merged by
- *                           the last to arrive). V is an argument because
+ *                           a second one-workgroup kernel that the call
+ *                           enqueues behind the first on `stream`). V is
+ *                           an argument because
  *                           the workgroup count is min(ceil(V/16), 256):
  *                           the query returns 0 for an invalid M or V, and
  *                           today's size is that of 256 workgroups.
@@ -411,7 +413,7 @@ moe_status_t lmhead_argmax(const uint16_t *h, const uint16_t *w_lm,
                            size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
- * lmhead_greedy_verify -- lmhead_argmax and, in the same launch, the greedy
+ * lmhead_greedy_verify -- lmhead_argmax and, in the same call, the greedy
  * verdict of the verify chain. (Section "The shape of a single-request
  * step": the target scores the drafted chain in one forward and the verdict
  * is taken inside the verify step, on the device; greedy decoding.)

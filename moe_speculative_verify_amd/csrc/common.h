@@ -366,23 +366,6 @@ __device__ inline bool arrive_last(unsigned *ticket)
     return true;
 }
 
-// One-level arrival, for grids whose workgroups end spread out in time (the
-// lm_head's tiles): every workgroup counts in at the ticket (word 0) with a
-// release, and the last arrival acquires, which synchronises with every
-// count (the counts form one read-modify-write chain). The critical path
-// holds one release and one acquire instead of two of each, and arrivals
-// spread over microseconds do not contend on the one line (paired A/B on the
-// lm_head, 32 pairs: 1.6 us less at M = 1 and 6, equal at M = 16). The
-// caller resets the ticket.
-__device__ inline bool arrive_last_flat(unsigned *ticket)
-{
-    if (__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT) !=
-        gridDim.x - 1)
-        return false;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    return true;
-}
-
 // Dynamic LDS a kernel may request: 160 KB per CU on gfx950, less a margin
 // for the kernels' small static arrays.
 constexpr int kLdsDynMax = 159 * 1024;

@@ -25,21 +25,27 @@
 //   - Each lane keeps a running (max, first index) for its token; the
 //     workgroup's best per token becomes a 64-bit key (order-preserving
 //     value bits << 32 | ~index, so the largest value and then the lowest
-//     index win) stored in the workgroup's own slot of the workspace. The
-//     last workgroup to arrive (one ticket counted with agent-scope
-//     releases, acquired by the last arrival; no spinning) takes each
-//     token's maximum over the slots and decodes it. Every slot is written before it is read, so nothing
-//     past the header needs to be zero.
+//     index win) stored in the workgroup's own slot of the workspace. A
+//     second kernel of one workgroup, launched behind it on the same
+//     stream, takes each token's maximum over the slots and decodes it:
+//     the kernel boundary orders every slot's store before the merge's
+//     loads, so no workgroup pays for a device-scope release or acquire
+//     (a last-workgroup hand-off inside the kernel, counted with
+//     agent-scope releases and acquired by the last arrival, measured
+//     6-7 us slower per call: each release writes back an XCD's L2 while
+//     the other workgroups there still stream). Every slot is written
+//     before it is read, so nothing past the header needs to be zero, and
+//     the header's counters are not used.
 //   - fp8 weights (lmhead_argmax_fp8, lmhead_greedy_verify_fp8): OCP E4M3
 //     codes with one fp32 scale per vocabulary row. A block is still 512
 //     bytes of each of the 16 rows (now 512 columns), staged the same way;
 //     each MFMA step reads the lane's eight codes from LDS, widens them to
 //     bf16 (exact), and the row scales multiply the fp32 tile before the
 //     argmax.
-//   - lmhead_greedy_verify: the same launch, and the same last workgroup
-//     then takes the greedy verdict of the verify chain from the decoded
-//     tokens (section "The shape of a single-request step": the verdict is
-//     part of the verify step and stays on the device).
+//   - lmhead_greedy_verify: the same two kernels; the merge then takes the
+//     greedy verdict of the verify chain from the decoded tokens (section
+//     "The shape of a single-request step": the verdict is part of the
+//     verify step and stays on the device).
 #include "common.h"
 
 #include <mutex>
@@ -74,10 +80,7 @@ template <bool W8>
 __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     const u32x4 *__restrict__ h, const u32x4 *__restrict__ wl,
     const float *__restrict__ wscale, int M, int H,
-    int V, unsigned long long *__restrict__ keys,
-    unsigned *__restrict__ ticket, int *__restrict__ argmax,
-    float *__restrict__ max_logit, const int *__restrict__ tokens,
-    int *__restrict__ accept, int nslot)
+    int V, unsigned long long *__restrict__ keys, int nslot)
 {
     constexpr int KB = lm_kb(W8);
     constexpr int kLmSteps = KB / 32;                    // MFMA steps per block
@@ -239,8 +242,6 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     }
     __shared__ float s_v[kLmWaves][16];
     __shared__ int s_i[kLmWaves][16];
-    __shared__ int s_last;
-    __shared__ int s_tok[kMaxM];
     if (g == 0) {
         s_v[wave][j] = bv;
         s_i[wave][j] = bi;
@@ -252,21 +253,22 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
         int besti = s_i[0][t];
         for (int w = 1; w < kLmWaves; ++w)
             argmax_merge(best, besti, s_v[w][t], s_i[w][t]);
-        const unsigned long long key = argmax_key(best, besti);
-        __hip_atomic_store(keys + (size_t)blockIdx.x * M + t, key, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        keys[(size_t)blockIdx.x * M + t] = argmax_key(best, besti);
     }
-    // wave 0 stored this workgroup's keys; thread 0 (of wave 0) releases
-    // them with its arrival, and the last arrival acquires every slot
-    __syncthreads();
-    if (threadIdx.x == 0)
-        s_last = arrive_last_flat(ticket);
-    __syncthreads();
-    if (!s_last)
-        return;
-    // wavefront w takes tokens w, w + 4, ...: lane l reads slots l, l + 64,
-    // ... of each (every load in flight at once, clamped addresses), keeps
-    // the largest, and the largest key over the wavefront decodes the token
+}
+
+// The merge of the G workgroups' keys, one workgroup of kLmWaves
+// wavefronts: wavefront w takes tokens w, w + 4, ...; lane l reads slots
+// l, l + 64, ... of each (every load in flight at once, clamped addresses),
+// keeps the largest, and the largest key over the wavefront decodes the
+// token. With tokens given, thread 0 then takes the greedy verdict.
+__global__ __launch_bounds__(kLmWaves * kWave) void lmhead_merge_kernel(
+    const unsigned long long *__restrict__ keys, int G, int M, int *__restrict__ argmax,
+    float *__restrict__ max_logit, const int *__restrict__ tokens, int *__restrict__ accept)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    __shared__ int s_tok[kMaxM];
     constexpr int kTpw = kMaxM / kLmWaves;                // tokens per wavefront
     constexpr int kSpl = kLmGridTarget / kWave;           // slots per lane
     unsigned long long kv[kTpw][kSpl];
@@ -274,11 +276,8 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
     for (int q = 0; q < kTpw; ++q) {
         const int t = min(wave + kLmWaves * q, M - 1);
 #pragma unroll
-        for (int sl = 0; sl < kSpl; ++sl) {
-            const int b = min(lane + kWave * sl, (int)gridDim.x - 1);
-            kv[q][sl] = __hip_atomic_load(keys + (size_t)b * M + t, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-        }
+        for (int sl = 0; sl < kSpl; ++sl)
+            kv[q][sl] = keys[(size_t)min(lane + kWave * sl, G - 1) * M + t];
     }
 #pragma unroll
     for (int q = 0; q < kTpw; ++q) {
@@ -298,8 +297,6 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
                 max_logit[t] = f32_unorder((uint32_t)(key >> 32));
         }
     }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (tokens == nullptr)                               // uniform
         return;
     // Greedy verdict: drafted candidate i (chain position i >= 1) is
@@ -320,7 +317,7 @@ __global__ __launch_bounds__(kLmWaves * kWave) void lmhead_kernel(
 
 using namespace mv;
 
-// Workspace: the header (tickets), then each workgroup's M 64-bit keys.
+// Workspace: the header (not used here), then each workgroup's M 64-bit keys.
 extern "C" size_t lmhead_argmax_workspace_bytes(int32_t M, int32_t V)
 {
     if (M < 1 || M > kMaxM || V < 1)
@@ -350,7 +347,6 @@ static moe_status_t lmhead_enqueue(const uint16_t *h, const void *w_lm, const fl
         return MOE_ERR_ALIGN;
     if (workspace_bytes < lmhead_argmax_workspace_bytes(M, V))
         return MOE_ERR_WORKSPACE;
-    unsigned *ticket = (unsigned *)workspace;
     unsigned long long *keys = (unsigned long long *)((char *)workspace + kWsHeader);
     const int ntiles = (V + 15) / 16;
     const int grid = min(ntiles, kLmGridTarget);
@@ -370,11 +366,15 @@ static moe_status_t lmhead_enqueue(const uint16_t *h, const void *w_lm, const fl
     if (w8)
         hipLaunchKernelGGL(lmhead_kernel<true>, dim3(grid), dim3(kLmWaves * kWave), lds,
                            (hipStream_t)stream, (const u32x4 *)h, (const u32x4 *)w_lm, w_scale,
-                           M, H, V, keys, ticket, argmax, max_logit, tokens, accept, nslot);
+                           M, H, V, keys, nslot);
     else
         hipLaunchKernelGGL(lmhead_kernel<false>, dim3(grid), dim3(kLmWaves * kWave), lds,
                            (hipStream_t)stream, (const u32x4 *)h, (const u32x4 *)w_lm, nullptr,
-                           M, H, V, keys, ticket, argmax, max_logit, tokens, accept, nslot);
+                           M, H, V, keys, nslot);
+    if (check_launch() != MOE_OK)
+        return MOE_ERR_LAUNCH;
+    hipLaunchKernelGGL(lmhead_merge_kernel, dim3(1), dim3(kLmWaves * kWave), 0,
+                       (hipStream_t)stream, keys, grid, M, argmax, max_logit, tokens, accept);
     return check_launch();
 }
 
