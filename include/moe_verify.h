@@ -75,8 +75,10 @@
  *     the same side of two regime limits: the router sums a logit over
  *     8-row tiles for M <= 8 and 16-row tiles above, and the down
  *     projection takes its matrix-core kernel once the pairs' activations
- *     (M*k*I*2 bytes) pass 150 KB. Across them the sums run in another
- *     order and agree within rounding.
+ *     (M*k*I*2 bytes) pass 150 KB. With fp8 weights a third: an expert that
+ *     serves at least 4 of the call's (token, slot) pairs runs its up
+ *     projection on the matrix cores. Across a limit the sums run in
+ *     another order and agree within rounding.
  */
 #ifndef MOE_VERIFY_H
 #define MOE_VERIFY_H

@@ -20,7 +20,10 @@
 // result depends only on its own token.
 //
 //   up       unit = (expert, row i of I): gate row and up row of the unit;
-//            epilogue a = bf16(silu(g) * u) in fp32, one rounding.
+//            epilogue a = bf16(silu(g) * u) in fp32, one rounding. With fp8
+//            weights an expert that serves at least kHotPairs pairs (tokens
+//            that share it) is taken 8 rows at a time on the matrix cores,
+//            so its codes are widened once for all of its pairs.
 //   down     workgroup b owns R rows of W_down of every selected expert;
 //            block sums y[pair, rows] in LDS.
 //   combine  out[t, r] = sum_j w[t,j] * y[(t,j), r], slots in order, fp32,
@@ -70,6 +73,10 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // pairs (one MFMA B operand); with distinct experts per token a bucket never
 // exceeds M <= 16 pairs.
 constexpr int kGroupThreads = 256;               // threads that build it (the first 256)
+// With fp8 weights, column blocks of at least this many pairs run the up
+// projection on the matrix cores: 8 gate and 8 up rows per unit against the
+// block's pairs.
+constexpr int kHotPairs = 4;
 constexpr int kBinsPerThread = kMaxE / kGroupThreads;
 
 struct Groups {
@@ -124,10 +131,11 @@ __device__ inline void groups_set_pairs(int idx, int NP, int E, Groups &g)
 // first_e (the shared expert, or -1): its blocks come first, the others
 // keep expert order. Its bucket holds every token, so its blocks cost the
 // most arithmetic; taken last they would leave a tail of it after the
-// streaming has ended.
+// streaming has ended. nhot (LDS, zero on entry, or null): incremented by the
+// number of column blocks of at least kHotPairs pairs.
 constexpr int kDirectNP = 16;
 
-__device__ inline void groups_finish(int NP, Groups &g, int first_e = -1)
+__device__ inline void groups_finish(int NP, Groups &g, int first_e = -1, int *nhot = nullptr)
 {
     const int p = threadIdx.x;
     const int lane = p & (kWave - 1), wave = p / kWave;
@@ -183,9 +191,12 @@ __device__ inline void groups_finish(int NP, Groups &g, int first_e = -1)
                     g.vbeg[v] = (int16_t)lane;
                     g.vcnt[v] = (int16_t)min(16, bend - lane);
                 }
+                const int nh = __popcll(__ballot(vstart && bend - lane >= kHotPairs));
                 if (lane == 0) {
                     g.D = __popcll(smask);
                     g.DV = __popcll(cmask);
+                    if (nhot)
+                        *nhot = nh;
                 }
             }
         }
@@ -244,6 +255,14 @@ __device__ inline void groups_finish(int NP, Groups &g, int first_e = -1)
                 g.vcnt[v] = (int16_t)(cnt[i] - o < 16 ? cnt[i] - o : 16);
             }
             run += pk[i];
+        }
+        if (nhot) {
+            int nh = 0;                                  // this thread's hot blocks
+#pragma unroll
+            for (int i = 0; i < kBinsPerThread; ++i)
+                nh += cnt[i] / 16 + (cnt[i] % 16 >= kHotPairs ? 1 : 0);
+            if (nh)
+                atomicAdd(nhot, nh);
         }
     }
     lds_barrier();
@@ -493,13 +512,18 @@ __device__ __forceinline__ float wave_total(float v)
 // unit spans several K blocks, whose sums are added in LDS in block order.
 constexpr int kUpWaves = 12;                     // wavefronts per workgroup
 
+// LDS row of x, in 16-byte chunks: the unit's K blocks
+__host__ __device__ inline int up_x_pitch(int H, int KC, bool w8)
+{
+    const int nwc = w8 ? H / 16 : H / 8;
+    const int nbu = (nwc + KC * kWave - 1) / (KC * kWave);
+    return nbu * KC * kWave * (w8 ? 2 : 1);
+}
 __host__ __device__ inline size_t up_x_bytes(int M, int H, int KC, bool w8, bool xr)
 {
     if (xr)
         return 0;
-    const int nwc = w8 ? H / 16 : H / 8;
-    const int nbu = (nwc + KC * kWave - 1) / (KC * kWave);
-    return align_up((size_t)M * nbu * KC * kWave * (w8 ? 2 : 1) * 16, 256);
+    return align_up((size_t)M * up_x_pitch(H, KC, w8) * 16, 256);
 }
 // x of the M tokens in whole K blocks (none when x sits in registers), then
 // each streaming wavefront's queue of finished sums and its 16 running sums
@@ -563,6 +587,49 @@ __host__ __device__ inline int up_unit(int j, int N, int b, int G, int R)
 constexpr int kUpRounds = 10;                    // bf16: even XCDs take 11 units to 10
 constexpr int kUpRounds8 = 0;                    // fp8: plain rounds
 
+// Wavefront 0 of an up workgroup, with s_nhot = the number of hot blocks
+// (from the grouping): the column block list rewritten as the blocks of at
+// least kHotPairs pairs, then the others, each part in its previous order
+// (blocks are independent, so no result depends on the order); s_nhot then
+// rounded down to even. The caller synchronises.
+__device__ inline void hot_blocks_first(Groups &g, int lane, int &s_nhot)
+{
+    const int nh = uniform(s_nhot);
+    if (lane == 0)
+        s_nhot = nh & ~1;
+    if (nh < 2)                                          // uniform: nothing moves
+        return;
+    constexpr int kC = kMaxNP / kWave;                   // blocks per lane
+    const int DV = uniform(g.DV);
+    int ve[kC], vb[kC], vc[kC];
+    bool ok[kC], hot[kC];
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+        const int v = c * kWave + lane;
+        ok[c] = v < DV;
+        ve[c] = ok[c] ? g.vexp[v] : 0;
+        vb[c] = ok[c] ? g.vbeg[v] : 0;
+        vc[c] = ok[c] ? g.vcnt[v] : 0;
+        hot[c] = ok[c] && vc[c] >= kHotPairs;
+    }
+    int hb = 0, cb = nh;                                 // next hot / other position
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+        const unsigned long long mh = __ballot(hot[c]), mc = __ballot(ok[c] && !hot[c]);
+        const unsigned long long m = hot[c] ? mh : mc;
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        const int pos = (hot[c] ? hb : cb) + below;
+        if (ok[c]) {
+            g.vexp[pos] = (int16_t)ve[c];
+            g.vbeg[pos] = (int16_t)vb[c];
+            g.vcnt[pos] = (int16_t)vc[c];
+        }
+        hb += __popcll(mh);
+        cb += __popcll(mc);
+    }
+}
+
 // The router's selection when it runs in the up kernel (moe_layer): the
 // partial logits [nks][M][E] of the router kernel (slices of the hidden
 // dimension), the optional bias, and where workgroup 0 writes the selection.
@@ -597,12 +664,13 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ Groups g;
     __shared__ int s_next;                               // the next unit of this workgroup
+    __shared__ int s_nhot;                               // hot column blocks
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = uniform(threadIdx.x / kWave);
     const int nch = H / 8;                               // 16-byte x chunks per row
     const int nwc = W8 ? H / 16 : nch;                   // 16-byte weight chunks per row
     const int nbu = (nwc + KC * kWave - 1) / (KC * kWave);   // K blocks per unit
-    const int xs = nbu * KC * kWave * (W8 ? 2 : 1);      // LDS x row, chunks
+    const int xs = up_x_pitch(H, KC, W8);                // LDS x row, chunks
     const int NP = M * k, NPT = NP + ns * M;
     const size_t xbytes = up_x_bytes(M, H, KC, W8, XR);
     u32x4 *s_x = (u32x4 *)smem;                          // [M][xs]
@@ -687,8 +755,10 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
         pid = pair_expert(topk_idx, threadIdx.x, NP, NPT, E);
     }
     groups_set_pairs(pid, NPT, E + ns, g);
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
         s_next = 0;
+        s_nhot = 0;
+    }
     wait_vmcnt<0>();                                     // the pair id and x are in
     if constexpr (XR) {
 #pragma unroll
@@ -704,13 +774,27 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
             s_x[t * xs + c] = u32x4{0, 0, 0, 0};         // K padding reads as zero
         }
     }
-    groups_finish(NPT, g, ns ? E : -1);                  // (its barriers also publish s_next)
+    constexpr bool HOT = W8 && !XR;
+    groups_finish(NPT, g, ns ? E : -1, HOT ? &s_nhot : nullptr);  // (its barriers also publish s_next)
+    // fp8: column blocks of at least kHotPairs pairs go to the matrix cores
+    // (hot units below) and move to the front: wavefront 0 rewrites the
+    // block list as [hot blocks][the rest], each part in its previous order,
+    // published by the barrier after x. Only an even number of them, nhot,
+    // run as hot units (with I / 8 units per block every workgroup then gets
+    // the same number of them); an odd one out stays first among the GEMV
+    // blocks.
+    if constexpr (HOT) {
+        if (M >= kHotPairs && wave == 0)                 // uniform
+            hot_blocks_first(g, lane, s_nhot);
+    }
     if constexpr (!XR) {
         wait_vmcnt<0>();                                 // this wave's share of x has landed
         lds_barrier();                                   // ... and every other wave's
     }
-
-    const int nunits = uniform(g.DV) * I;
+    const int nhot = HOT && M >= kHotPairs ? uniform(s_nhot) : 0;
+    const int nhu = nhot * (I / 8);                      // hot units: 8 rows of a hot block
+    const int nhw = up_count(nhu, (int)blockIdx.x, (int)gridDim.x, 0);   // this workgroup's
+    const int nunits = (uniform(g.DV) - nhot) * I;       // GEMV units, after the hot blocks
     constexpr int kR = W8 ? kUpRounds8 : kUpRounds;
     const int nwg = up_count(nunits, (int)blockIdx.x, (int)gridDim.x, kR);
 
@@ -722,15 +806,23 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
         }
         pend = 0;
     };
-    auto claim = [&]() {                                 // uniform: a unit, or -1
+    // uniform: a GEMV unit (blocks from nhot on), -2 - h for hot unit h, or
+    // -1 past the end. The workgroup's hot units come first.
+    auto claim = [&]() {
         int j = 0;
         if (lane == 0)
             j = __hip_atomic_fetch_add(&s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         j = uniform(__builtin_amdgcn_readlane(j, 0));
-        return j < nwg ? up_unit(j, nunits, (int)blockIdx.x, (int)gridDim.x, kR) : -1;
+        if constexpr (HOT) {
+            if (j < nhw)
+                return -2 - ((int)blockIdx.x + (int)gridDim.x * j);
+            j -= nhw;
+        }
+        return j < nwg ? nhot * I + up_unit(j, nunits, (int)blockIdx.x, (int)gridDim.x, kR) : -1;
     };
     // Tag of a block: unit * 16 + kb, or -1 past the end; a unit's K blocks
-    // stay on one wavefront
+    // stay on one wavefront. The workgroup's hot units are claimed first and
+    // taken whole, below, before the first GEMV unit.
     int cur_u = claim(), cur_kb = 0;
     auto next_tag = [&]() {
         int t = -1;
@@ -859,6 +951,79 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
             finish(jj, p, wave_total(ga), wave_total(ua));
         }
     };
+
+    // fp8 hot unit h: rows i0 .. i0 + 7 of a hot block's gate and up
+    // matrices against its (up to 16) pairs on v_mfma_f32_16x16x32_bf16.
+    // A = the 16 weight rows (lane l: row l % 16, gate rows first), streamed
+    // into registers one K block of 32 chunks per row at a time (each load:
+    // 64 contiguous bytes of each of the 16 rows), a chunk of 16 codes widened
+    // to two bf16 steps; B = the pairs' x rows from LDS (lane l: pair l % 16,
+    // x chunks 2c and 2c + 1 against code chunk c). Lane l receives rows
+    // 4 (l / 16) .. + 3 of pair l % 16: gate sums in lanes 0-31, up sums in
+    // 32-63, each times its row's scale; lanes 0-31 take the up sums of lane
+    // l + 32 and write the activations of their 4 rows. (The fp8 entry points
+    // have no shared expert.)
+    if constexpr (HOT) {
+        while (cur_u <= -2) {                            // uniform: a hot unit, whole
+            const int h = -2 - cur_u;
+            const int v = h / (I / 8), i0 = 8 * (h % (I / 8));
+            const int ev = uniform(g.vexp[v]);
+            const int npair = uniform(g.vcnt[v]);
+            const int r = lane & 15, gq = lane >> 4;
+            const size_t row = (size_t)ev * I + i0 + (r & 7);
+            const u32x4 *wr = (r < 8 ? wg : wu) + row * nwc;
+            const bool col_ok = r < npair;
+            const int p = g.sorted[uniform(g.vbeg[v]) + (col_ok ? r : 0)];
+            const u32x4 *xr = s_x + pair_token(p, NP, k) * xs;
+            constexpr int kHq = 8;                       // loads per lane per K block
+            const int nkh = (nwc + 4 * kHq - 1) / (4 * kHq);   // K blocks of 4 kHq chunks
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int kb = 0; kb < nkh; ++kb) {
+                // past the K tail the loads are clamped to the row's last
+                // chunk (finite weights) and meet x's zero padding
+                u32x4 a[kHq];
+#pragma unroll
+                for (int q = 0; q < kHq; ++q)
+                    a[q] = load_stream(wr + min(kb * 4 * kHq + 4 * q + gq, nwc - 1));
+                wait_vmcnt<0>();
+#pragma unroll
+                for (int q = 0; q < kHq; ++q) {
+                    // this lane supplies row r of A and column r of B (zero
+                    // past the block's pairs)
+                    const int c = kb * 4 * kHq + 4 * q + gq;
+                    const u32x4 a0 = e4m3x8_to_bf16(a[q].x, a[q].y);
+                    const u32x4 a1 = e4m3x8_to_bf16(a[q].z, a[q].w);
+                    u32x4 b0 = *(const MV_LDS u32x4 *)(xr + 2 * c);
+                    u32x4 b1 = *(const MV_LDS u32x4 *)(xr + 2 * c + 1);
+                    if (!col_ok) {
+                        b0 = u32x4{0, 0, 0, 0};
+                        b1 = u32x4{0, 0, 0, 0};
+                    }
+                    acc = mfma_bf16(a0, b0, acc);
+                    acc = mfma_bf16(a1, b1, acc);
+                }
+            }
+            const float *sc = (gq < 2 ? sg : su) + row - (r & 7) + 4 * (gq & 1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)                  // the rows' scales
+                acc[j] *= sc[j];
+            float upv[4];                                // lane l + 32's sums: the up rows
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                upv[j] = __shfl_xor(acc[j], 32);
+            if (gq < 2 && col_ok) {
+                uint32_t o[2];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float g0 = acc[2 * j], g1 = acc[2 * j + 1];
+                    o[j] = f32_to_bf16_rne(g0 / (1.0f + expf(-g0)) * upv[2 * j]) |
+                           (f32_to_bf16_rne(g1 / (1.0f + expf(-g1)) * upv[2 * j + 1]) << 16);
+                }
+                *(uint2 *)(act + (size_t)p * I + i0 + 4 * gq) = uint2{o[0], o[1]};
+            }
+            cur_u = claim();
+        }
+    }
 
     u32x4 wgr[KC], wur[KC];
     float sgr = 0.0f, sur = 0.0f;                        // fp8 row scales (unused for bf16)

@@ -203,12 +203,14 @@ def test_expert_ffn_limits(M, H, I, E, k, skew):
     del dw
 
 
-def test_expert_ffn_identical_tokens_share_experts(full_layer):
-    """M identical tokens route identically: every row equals the M=1 row."""
-    say("expert_ffn identical tokens")
+@pytest.mark.parametrize("M", [3, 6])
+def test_expert_ffn_identical_tokens_share_experts(full_layer, M):
+    """M identical tokens route identically: every row equals the M=1 row,
+    bit for bit (with bf16 weights every column block runs on the GEMV
+    path however many pairs it holds)."""
+    say("expert_ffn identical tokens", M)
     x1 = synth.activations(1, 2560, seed=41)
     idx1, tw1 = synth.random_routing(1, 512, 8, 41)
-    M = 6
     x = np.repeat(x1, M, axis=0)
     idx = np.repeat(idx1, M, axis=0)
     tw = np.repeat(tw1, M, axis=0)
