@@ -587,18 +587,12 @@ __host__ __device__ inline int up_unit(int j, int N, int b, int G, int R)
 constexpr int kUpRounds = 10;                    // bf16: even XCDs take 11 units to 10
 constexpr int kUpRounds8 = 0;                    // fp8: plain rounds
 
-// Wavefront 0 of an up workgroup, with s_nhot = the number of hot blocks
-// (from the grouping): the column block list rewritten as the blocks of at
-// least kHotPairs pairs, then the others, each part in its previous order
-// (blocks are independent, so no result depends on the order); s_nhot then
-// rounded down to even. The caller synchronises.
-__device__ inline void hot_blocks_first(Groups &g, int lane, int &s_nhot)
+// One wavefront, given nh = the number of column blocks of at least
+// kHotPairs pairs (counted by the grouping): the block list rewritten as
+// those blocks, then the others, each part in its previous order (blocks are
+// independent, so no result depends on the order). The caller synchronises.
+__device__ inline void hot_blocks_first(Groups &g, int lane, int nh)
 {
-    const int nh = uniform(s_nhot);
-    if (lane == 0)
-        s_nhot = nh & ~1;
-    if (nh < 2)                                          // uniform: nothing moves
-        return;
     constexpr int kC = kMaxNP / kWave;                   // blocks per lane
     const int DV = uniform(g.DV);
     int ve[kC], vb[kC], vc[kC];
@@ -784,8 +778,13 @@ __global__ __launch_bounds__(kUpWaves * kWave) void expert_up_kernel(
     // the same number of them); an odd one out stays first among the GEMV
     // blocks.
     if constexpr (HOT) {
-        if (M >= kHotPairs && wave == 0)                 // uniform
-            hot_blocks_first(g, lane, s_nhot);
+        if (M >= kHotPairs && wave == 0) {               // uniform
+            const int nh = uniform(s_nhot);
+            if (nh >= 2)
+                hot_blocks_first(g, lane, nh);
+            if (lane == 0)
+                s_nhot = nh & ~1;
+        }
     }
     if constexpr (!XR) {
         wait_vmcnt<0>();                                 // this wave's share of x has landed
@@ -1084,7 +1083,9 @@ __global__ __launch_bounds__(WV * kWave) void expert_down_gemv_kernel(
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ Groups g;
     __shared__ int s_next;                               // the workgroup's next block to claim
+    __shared__ int s_nhot;                               // (fp8) hot column blocks
     const int lane = threadIdx.x & (kWave - 1);
+    const int wave = uniform(threadIdx.x / kWave);
     const int nch = I / 8;                               // bf16 activation chunks (K = I)
     const int nwc = W8 ? I / 16 : nch;                   // weight chunks per row
     const int nkb = down_gemv_nkb(I, W8);
@@ -1098,12 +1099,25 @@ __global__ __launch_bounds__(WV * kWave) void expert_down_gemv_kernel(
     // buckets
     const float pw = (int)threadIdx.x < NP ? topk_w[threadIdx.x] : 0.0f;
     groups_set_pairs(pair_expert(topk_idx, threadIdx.x, NP, NPT, E), NPT, E + ns, g);
-    if (threadIdx.x == 0)
+    if (threadIdx.x == 0) {
         s_next = 0;
+        s_nhot = 0;
+    }
     wait_vmcnt<0>();                                     // only the pair id and weight are in flight
     if ((int)threadIdx.x < NP)
         s_tw[threadIdx.x] = pw;
-    groups_finish(NPT, g, ns ? E : -1);                  // (its barriers also publish s_next)
+    groups_finish(NPT, g, ns ? E : -1, W8 ? &s_nhot : nullptr);   // (its barriers also publish s_next)
+    // fp8: the column blocks of at least kHotPairs pairs move to the front
+    // and run on the matrix cores (below)
+    int nhot = 0;                                        // uniform
+    if constexpr (W8) {
+        nhot = uniform(s_nhot);
+        if (nhot > 0) {
+            if (wave == 0)
+                hot_blocks_first(g, lane, nhot);
+            lds_barrier();
+        }
+    }
 
     // Blocks B = v * nkb + kb (column block v, K block kb), claimed one at a
     // time by the workgroup's wavefronts from an LDS counter (a SIMD serves
@@ -1126,12 +1140,75 @@ __global__ __launch_bounds__(WV * kWave) void expert_down_gemv_kernel(
             a[i] = act[(size_t)p * nch + c + i];
     };
 
+    // fp8 hot block B (column block v < nhot, K block kb of 64 code chunks
+    // per row): the R rows against the block's (up to 16) pairs on
+    // v_mfma_f32_16x16x32_bf16. Lane l supplies row l % 16 of A (the row's
+    // codes, widened; zero past R) and column l % 16 of B (that pair's
+    // activations from L2; zero past the block's pairs and the K tail):
+    // chunk c of 16 codes meets activation chunks 2c and 2c + 1. Lane l
+    // receives rows 4 (l / 16) .. + 3 of pair l % 16, times each row's
+    // scale, into the block sums. The workgroup's hot blocks are claimed
+    // first. (The fp8 entry points have no shared expert.)
+    int B = next_block();
+    if constexpr (W8) {
+        const int r = lane & 15, gq = lane >> 4;
+        while (B >= 0 && B < nhot * nkb) {               // uniform
+            const int v = B / nkb, kb = B % nkb;
+            const int ev = uniform(g.vexp[v]);
+            const int npair = uniform(g.vcnt[v]);
+            const bool row_ok = r < nr, col_ok = r < npair;
+            const u32x4 *wp = wd + ((size_t)ev * H + r0 + (row_ok ? r : 0)) * nwc;
+            const int p = g.sorted[uniform(g.vbeg[v]) + (col_ok ? r : 0)];
+            const u32x4 *ap = act + (size_t)p * nch;
+            u32x4 a[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q)                 // clamped in the K tail
+                a[q] = load_stream(wp + min(kb * kDnCh + 4 * q + gq, nwc - 1));
+            float scl[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                scl[j] = sd[(size_t)ev * H + min(r0 + 4 * gq + j, H - 1)];
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int qr = 0; qr < 16; qr += 8) {
+                u32x4 b[16];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int c = min(kb * kDnCh + 4 * (qr + q) + gq, nwc - 1);
+                    b[2 * q] = ap[2 * c];
+                    b[2 * q + 1] = ap[2 * c + 1];
+                }
+                wait_vmcnt<0>();
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const bool bok = col_ok && kb * kDnCh + 4 * (qr + q) + gq < nwc;
+                    u32x4 a0 = e4m3x8_to_bf16(a[qr + q].x, a[qr + q].y);
+                    u32x4 a1 = e4m3x8_to_bf16(a[qr + q].z, a[qr + q].w);
+                    if (!row_ok) {
+                        a0 = u32x4{0, 0, 0, 0};
+                        a1 = u32x4{0, 0, 0, 0};
+                    }
+                    const u32x4 b0 = bok ? b[2 * q] : u32x4{0, 0, 0, 0};
+                    const u32x4 b1 = bok ? b[2 * q + 1] : u32x4{0, 0, 0, 0};
+                    acc = mfma_bf16(a0, b0, acc);
+                    acc = mfma_bf16(a1, b1, acc);
+                }
+            }
+            if (col_ok) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (4 * gq + j < nr)
+                        s_y[(p * nkb + kb) * R + 4 * gq + j] = acc[j] * scl[j];
+            }
+            B = next_block();
+        }
+    }
+
     // Each block: lane i loads chunk i of the block for each of the R rows,
     // and the activation chunks of the column block's first pairs (the
     // pairs' rows sit in L2: every workgroup reads all of them), then waits
     // for all of it and consumes the block.
-    for (;;) {
-        const int B = next_block();
+    for (;; B = next_block()) {
         if (B < 0)                                       // uniform
             break;
         const int v = B / nkb, kb = B % nkb;

@@ -1,8 +1,10 @@
 """GPU parity of experts that several verify tokens share. With fp8
 weights a column block of at least 4 pairs runs the up projection on the
 matrix cores (8-row units: 8 gate and 8 up rows against the block's pairs)
-instead of one-row GEMV units; with bf16 weights every block stays on the
-GEMV path, each pair paying its own dot products. The routing is planted so
+instead of one-row GEMV units, and the down projection's blocks of it on the
+matrix cores too (a workgroup's rows against the block's pairs); with bf16
+weights every block stays on the GEMV paths, each pair paying its own dot
+products. The routing is planted so
 that the number of pairs per expert is known: blocks of exactly 4 (the
 threshold) and 3 (below it), 16 (a full block), an odd number of hot blocks
 (the last one stays on the GEMV path), ragged K tails, I not a multiple of
@@ -93,9 +95,9 @@ def _fp8_host(H, I, E, seed):
 
 FP8_HOT_CASES = [
     # M, H, I, E, k, pairs per planted expert
-    (16, 528, 48, 48, 3, (16, 9, 4, 3)),       # 3 hot blocks: 2 on the MFMA, one stays GEMV; 33 code chunks per row
+    (16, 528, 48, 48, 3, (16, 9, 4, 3)),       # up: 2 hot blocks on the MFMA, one stays GEMV (down: all 3); 8 rows in the last down workgroup
     (12, 2560, 64, 40, 4, (12, 12, 7, 4)),     # the model's width: 3 K blocks of codes, the last partial
-    (16, 1040, 1040, 24, 2, (16, 5, 5)),       # 1040 columns: a 16-code tail chunk; odd hot count
+    (16, 1040, 1040, 24, 2, (16, 5, 5)),       # 1040 columns: a 16-code tail chunk in both projections; odd hot count
     (8, 256, 64, 40, 4, (8, 8, 4, 4, 3)),      # 4 hot blocks, two exactly at the threshold
     (16, 2560, 128, 64, 6, (16, 16, 12, 5)),   # 96 pairs (histogram grouping), 4 hot blocks
 ]
