@@ -450,14 +450,24 @@ __global__ __launch_bounds__(WV * kWave) void expert_down_kernel(
     wait_vmcnt<0>();                                     // dummy loads have landed
     __syncthreads();
 
-    // weighted combine, slots in order, fp32
+    // weighted combine, slots in order, fp32 (eight slots' values read at a
+    // time)
     for (int i = threadIdx.x; i < M * nr; i += blockDim.x) {
         const int t = i / nr, rr = i % nr;
         float sum = 0.0f;
-        for (int jj = 0; jj < k; ++jj) {
-            const int p = t * k + jj;
-            if (g.e[p] >= 0)
-                sum = fmaf(s_tw[p], y_s[p * R + rr], sum);
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            float tw[8], y[8];
+            int e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int p = t * k + min(j0 + q, k - 1);
+                e[q] = j0 + q < k ? g.e[p] : -1;
+                tw[q] = s_tw[p];
+                y[q] = y_s[p * R + rr];
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                sum = e[q] >= 0 ? fmaf(tw[q], y[q], sum) : sum;
         }
         if (ns)                                          // the shared expert, weight 1
             sum += y_s[(NP + t) * R + rr];
@@ -1277,17 +1287,28 @@ __global__ __launch_bounds__(WV * kWave) void expert_down_gemv_kernel(
     __syncthreads();
 
     // weighted combine, slots in order, fp32; each pair's K blocks in order
+    // (eight slots' values read at a time)
     for (int i = threadIdx.x; i < M * nr; i += blockDim.x) {
         const int t = i / nr, rr = i % nr;
         float sum = 0.0f;
-        for (int jj = 0; jj < k; ++jj) {
-            const int p = t * k + jj;
-            if (g.e[p] >= 0) {
-                float y = 0.0f;
-                for (int kb = 0; kb < nkb; ++kb)
-                    y += s_y[(p * nkb + kb) * R + rr];
-                sum = fmaf(s_tw[p], y, sum);
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            float tw[8], y[8];
+            int e[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int p = t * k + min(j0 + q, k - 1);
+                e[q] = j0 + q < k ? g.e[p] : -1;
+                tw[q] = s_tw[p];
+                y[q] = 0.0f;
             }
+            for (int kb = 0; kb < nkb; ++kb) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    y[q] += s_y[((t * k + min(j0 + q, k - 1)) * nkb + kb) * R + rr];
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                sum = e[q] >= 0 ? fmaf(tw[q], y[q], sum) : sum;
         }
         if (ns) {                                        // the shared expert, weight 1
             const int p = NP + t;
