@@ -468,6 +468,42 @@ moe_status_t lmhead_greedy_verify_fp8(const uint16_t *h, const uint8_t *w_lm,
                                       int32_t *accept, void *workspace,
                                       size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * lmhead_partial_keys, lmhead_partial_keys_fp8, lmhead_merge_keys -- the two
+ * phases that lmhead_argmax and lmhead_greedy_verify (and their fp8
+ * variants) enqueue, as separate calls, for callers that time the
+ * lm_head's GEMV alone or put other work between the phases. (Same
+ * sections as lmhead_argmax.)
+ *
+ * lmhead_partial_keys(_fp8): the GEMV. Arguments as lmhead_argmax(_fp8)
+ *   without the outputs; every workgroup writes its per-token winner (a
+ *   64-bit key: the logit's order code, then the row) into the workspace.
+ * lmhead_merge_keys: the merge of those keys, then the verdict when tokens
+ *   is given. argmax, max_logit (optional), tokens and accept as in
+ *   lmhead_greedy_verify; tokens and accept both NULL for lmhead_argmax's
+ *   outputs alone. workspace: the one the partial-keys call wrote, with the
+ *   same M and V, on the same stream after it (nothing may write the
+ *   workspace in between).
+ *
+ * partial keys then merge keys gives bitwise the outputs of the combined
+ * call. Errors: those of lmhead_argmax(_fp8) for their arguments;
+ * lmhead_merge_keys: MOE_ERR_NULL (argmax or workspace NULL, or only one
+ * of tokens and accept given), MOE_ERR_SHAPE (M or V below 1),
+ * MOE_ERR_UNSUPPORTED (M above 16), MOE_ERR_ALIGN, MOE_ERR_WORKSPACE,
+ * MOE_ERR_LAUNCH.
+ * ---------------------------------------------------------------------- */
+moe_status_t lmhead_partial_keys(const uint16_t *h, const uint16_t *w_lm, int32_t M,
+                                 int32_t H, int32_t V, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+moe_status_t lmhead_partial_keys_fp8(const uint16_t *h, const uint8_t *w_lm,
+                                     const float *w_scale, int32_t M, int32_t H,
+                                     int32_t V, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+moe_status_t lmhead_merge_keys(int32_t M, int32_t V, int32_t *argmax, float *max_logit,
+                               const int32_t *tokens, int32_t *accept,
+                               const void *workspace, size_t workspace_bytes,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,8 @@ EXPORTS = ("moe_abi_version", "moe_status_str", "moe_workspace_clear", "moe_hbm_
            "moe_layer_workspace_bytes", "moe_layer", "moe_layer_noalloc", "moe_layer_rmsnorm",
            "moe_layer_shared",
            "lmhead_argmax_workspace_bytes", "lmhead_argmax", "lmhead_greedy_verify",
-           "lmhead_argmax_fp8", "lmhead_greedy_verify_fp8")
+           "lmhead_argmax_fp8", "lmhead_greedy_verify_fp8",
+           "lmhead_partial_keys", "lmhead_partial_keys_fp8", "lmhead_merge_keys")
 
 
 class MoeError(RuntimeError):
@@ -101,6 +102,12 @@ def lib() -> ctypes.CDLL:
         L.lmhead_argmax_fp8.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _S, _P]
         L.lmhead_greedy_verify_fp8.restype = ctypes.c_int32
         L.lmhead_greedy_verify_fp8.argtypes = [_P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _S, _P]
+        L.lmhead_partial_keys.restype = ctypes.c_int32
+        L.lmhead_partial_keys.argtypes = [_P, _P, _I, _I, _I, _P, _S, _P]
+        L.lmhead_partial_keys_fp8.restype = ctypes.c_int32
+        L.lmhead_partial_keys_fp8.argtypes = [_P, _P, _P, _I, _I, _I, _P, _S, _P]
+        L.lmhead_merge_keys.restype = ctypes.c_int32
+        L.lmhead_merge_keys.argtypes = [_I, _I, _P, _P, _P, _P, _P, _S, _P]
         L.lmhead_greedy_verify.restype = ctypes.c_int32
         L.lmhead_greedy_verify.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _S, _P]
         _lib = L
@@ -533,6 +540,46 @@ def lmhead_greedy_verify_fp8(h, w_lm, w_scale, tokens, *, want_max=False, out=No
         _ptr(acc, "accept", (torch.int32,), (2,)),
         _ptr(ws, "workspace"), ws.numel(), st))
     return (am, acc, ml) if want_max else (am, acc)
+
+
+def lmhead_partial_keys(h, w_lm, workspace, *, w_scale=None, stream=None):
+    """The lm_head's GEMV phase: each workgroup's per-token winner as a key in
+    `workspace` (lmhead_argmax_workspace_bytes(M, V) bytes). With w_scale the
+    rows are fp8 codes."""
+    M, H = h.shape
+    V = w_lm.shape[0]
+    st = _stream(stream)
+    if w_scale is None:
+        _check("lmhead_partial_keys", lib().lmhead_partial_keys(
+            _ptr(h, "h", _BF16), _ptr(w_lm, "w_lm", _BF16, (V, H)), M, H, V,
+            _ptr(workspace, "workspace"), workspace.numel(), st))
+    else:
+        _check("lmhead_partial_keys_fp8", lib().lmhead_partial_keys_fp8(
+            _ptr(h, "h", _BF16), _ptr(w_lm, "w_lm", _U8, (V, H)),
+            _ptr(w_scale, "w_scale", (torch.float32,), (V,)), M, H, V,
+            _ptr(workspace, "workspace"), workspace.numel(), st))
+
+
+def lmhead_merge_keys(M: int, V: int, workspace, *, tokens=None, want_max=False, out=None,
+                      stream=None):
+    """The lm_head's merge phase over the keys lmhead_partial_keys wrote.
+    Returns argmax (, accept with tokens) (, max_logit)."""
+    dev = workspace.device
+    am, acc, ml = out if out is not None else (None, None, None)
+    if am is None:
+        am = torch.empty(M, dtype=torch.int32, device=dev)
+    if tokens is not None and acc is None:
+        acc = torch.empty(2, dtype=torch.int32, device=dev)
+    if want_max and ml is None:
+        ml = torch.empty(M, dtype=torch.float32, device=dev)
+    _check("lmhead_merge_keys", lib().lmhead_merge_keys(
+        M, V, _ptr(am, "argmax", (torch.int32,), (M,)),
+        _ptr(ml, "max_logit", (torch.float32,), (M,)) if want_max else None,
+        _ptr(tokens, "tokens", (torch.int32,), (M,)) if tokens is not None else None,
+        _ptr(acc, "accept", (torch.int32,), (2,)) if tokens is not None else None,
+        _ptr(workspace, "workspace"), workspace.numel(), _stream(stream)))
+    res = (am,) + ((acc,) if tokens is not None else ()) + ((ml,) if want_max else ())
+    return res[0] if len(res) == 1 else res
 
 
 def _fp8_expert_ptrs(E, I, H, w_gate, s_gate, w_up, s_up, w_down, s_down):

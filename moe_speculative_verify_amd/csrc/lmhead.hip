@@ -325,14 +325,19 @@ extern "C" size_t lmhead_argmax_workspace_bytes(int32_t M, int32_t V)
     return kWsHeader + align_up((size_t)kLmGridTarget * M * 8, 256);
 }
 
-// w_lm: bf16 rows, or fp8 codes when w_scale is given (one scale per row)
-static moe_status_t lmhead_enqueue(const uint16_t *h, const void *w_lm, const float *w_scale,
-                                   bool w8, int32_t M, int32_t H, int32_t V, int32_t *argmax,
-                                   float *max_logit, const int32_t *tokens,
-                                   int32_t *accept, void *workspace,
-                                   size_t workspace_bytes, void *stream)
+// The workgroups of the GEMV: one key slot each in the workspace.
+static int lm_grid(int V)
 {
-    if (!h || !w_lm || !argmax || !workspace || (w8 && !w_scale))
+    return min((V + 15) / 16, kLmGridTarget);
+}
+
+// Checks of the GEMV phase: w_lm bf16 rows, or fp8 codes when w8 (one
+// scale per row); workspace: the keys, one M-key slot per workgroup.
+static moe_status_t lm_check_keys(const uint16_t *h, const void *w_lm, const float *w_scale,
+                                  bool w8, int32_t M, int32_t H, int32_t V,
+                                  const void *workspace, size_t workspace_bytes)
+{
+    if (!h || !w_lm || !workspace || (w8 && !w_scale))
         return MOE_ERR_NULL;
     if (M < 1 || H < 1 || V < 1)
         return MOE_ERR_SHAPE;
@@ -341,15 +346,41 @@ static moe_status_t lmhead_enqueue(const uint16_t *h, const void *w_lm, const fl
         return MOE_ERR_UNSUPPORTED;
     if (w8 && !aligned4(w_scale))
         return MOE_ERR_ALIGN;
-    if (!aligned16(h) || !aligned16(w_lm) || !aligned4(argmax) ||
-        (max_logit && !aligned4(max_logit)) || !aligned16(workspace) ||
+    if (!aligned16(h) || !aligned16(w_lm) || !aligned16(workspace))
+        return MOE_ERR_ALIGN;
+    if (workspace_bytes < lmhead_argmax_workspace_bytes(M, V))
+        return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+// Checks of the merge phase (tokens and accept both given or both NULL).
+static moe_status_t lm_check_merge(int32_t M, int32_t V, const int32_t *argmax,
+                                   const float *max_logit, const int32_t *tokens,
+                                   const int32_t *accept, const void *workspace,
+                                   size_t workspace_bytes)
+{
+    if (!argmax || !workspace || (!tokens) != (!accept))
+        return MOE_ERR_NULL;
+    if (M < 1 || V < 1)
+        return MOE_ERR_SHAPE;
+    if (M > kMaxM)
+        return MOE_ERR_UNSUPPORTED;
+    if (!aligned4(argmax) || (max_logit && !aligned4(max_logit)) || !aligned16(workspace) ||
         (tokens && (!aligned4(tokens) || !aligned4(accept))))
         return MOE_ERR_ALIGN;
     if (workspace_bytes < lmhead_argmax_workspace_bytes(M, V))
         return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+// The GEMV phase: every workgroup's per-token winner as a 64-bit key in the
+// workspace (arguments checked).
+static moe_status_t lm_launch_keys(const uint16_t *h, const void *w_lm, const float *w_scale,
+                                   bool w8, int32_t M, int32_t H, int32_t V, void *workspace,
+                                   void *stream)
+{
     unsigned long long *keys = (unsigned long long *)((char *)workspace + kWsHeader);
-    const int ntiles = (V + 15) / 16;
-    const int grid = min(ntiles, kLmGridTarget);
+    const int grid = lm_grid(V);
     const int nslot = lm_lds_bytes(M, H, w8, 3) <= (size_t)kLdsDynMax ? 3 : 2;
     const size_t lds = lm_lds_bytes(M, H, w8, nslot);
     static std::once_flag once;
@@ -371,11 +402,81 @@ static moe_status_t lmhead_enqueue(const uint16_t *h, const void *w_lm, const fl
         hipLaunchKernelGGL(lmhead_kernel<false>, dim3(grid), dim3(kLmWaves * kWave), lds,
                            (hipStream_t)stream, (const u32x4 *)h, (const u32x4 *)w_lm, nullptr,
                            M, H, V, keys, nslot);
-    if (check_launch() != MOE_OK)
-        return MOE_ERR_LAUNCH;
-    hipLaunchKernelGGL(lmhead_merge_kernel, dim3(1), dim3(kLmWaves * kWave), 0,
-                       (hipStream_t)stream, keys, grid, M, argmax, max_logit, tokens, accept);
     return check_launch();
+}
+
+// The merge phase: the keys of the GEMV's workgroups, then the verdict when
+// tokens are given (arguments checked).
+static moe_status_t lm_launch_merge(int32_t M, int32_t V, int32_t *argmax, float *max_logit,
+                                    const int32_t *tokens, int32_t *accept,
+                                    const void *workspace, void *stream)
+{
+    const unsigned long long *keys =
+        (const unsigned long long *)((const char *)workspace + kWsHeader);
+    hipLaunchKernelGGL(lmhead_merge_kernel, dim3(1), dim3(kLmWaves * kWave), 0,
+                       (hipStream_t)stream, keys, lm_grid(V), M, argmax, max_logit, tokens,
+                       accept);
+    return check_launch();
+}
+
+// Both phases on one stream; every argument is checked before anything is
+// launched.
+static moe_status_t lmhead_enqueue(const uint16_t *h, const void *w_lm, const float *w_scale,
+                                   bool w8, int32_t M, int32_t H, int32_t V, int32_t *argmax,
+                                   float *max_logit, const int32_t *tokens,
+                                   int32_t *accept, void *workspace,
+                                   size_t workspace_bytes, void *stream)
+{
+    if (!h || !w_lm || !argmax || !workspace || (w8 && !w_scale))
+        return MOE_ERR_NULL;
+    if (M < 1 || H < 1 || V < 1)
+        return MOE_ERR_SHAPE;
+    if (M > kMaxM || H % (w8 ? 16 : 8) != 0 || H > kMaxDim ||
+        lm_lds_bytes(M, H, w8) > (size_t)kLdsDynMax)
+        return MOE_ERR_UNSUPPORTED;
+    if (w8 && !aligned4(w_scale))
+        return MOE_ERR_ALIGN;
+    if (!aligned16(h) || !aligned16(w_lm) || !aligned4(argmax) ||
+        (max_logit && !aligned4(max_logit)) || !aligned16(workspace) ||
+        (tokens && (!aligned4(tokens) || !aligned4(accept))))
+        return MOE_ERR_ALIGN;
+    if (workspace_bytes < lmhead_argmax_workspace_bytes(M, V))
+        return MOE_ERR_WORKSPACE;
+    const moe_status_t st = lm_launch_keys(h, w_lm, w_scale, w8, M, H, V, workspace, stream);
+    if (st != MOE_OK)
+        return st;
+    return lm_launch_merge(M, V, argmax, max_logit, tokens, accept, workspace, stream);
+}
+
+extern "C" moe_status_t lmhead_partial_keys(const uint16_t *h, const uint16_t *w_lm, int32_t M,
+                                            int32_t H, int32_t V, void *workspace,
+                                            size_t workspace_bytes, void *stream)
+{
+    const moe_status_t st =
+        lm_check_keys(h, w_lm, nullptr, false, M, H, V, workspace, workspace_bytes);
+    return st != MOE_OK ? st : lm_launch_keys(h, w_lm, nullptr, false, M, H, V, workspace, stream);
+}
+
+extern "C" moe_status_t lmhead_partial_keys_fp8(const uint16_t *h, const uint8_t *w_lm,
+                                                const float *w_scale, int32_t M, int32_t H,
+                                                int32_t V, void *workspace,
+                                                size_t workspace_bytes, void *stream)
+{
+    const moe_status_t st =
+        lm_check_keys(h, w_lm, w_scale, true, M, H, V, workspace, workspace_bytes);
+    return st != MOE_OK ? st : lm_launch_keys(h, w_lm, w_scale, true, M, H, V, workspace, stream);
+}
+
+extern "C" moe_status_t lmhead_merge_keys(int32_t M, int32_t V, int32_t *argmax,
+                                          float *max_logit, const int32_t *tokens,
+                                          int32_t *accept, const void *workspace,
+                                          size_t workspace_bytes, void *stream)
+{
+    const moe_status_t st =
+        lm_check_merge(M, V, argmax, max_logit, tokens, accept, workspace, workspace_bytes);
+    return st != MOE_OK ? st
+                        : lm_launch_merge(M, V, argmax, max_logit, tokens, accept, workspace,
+                                          stream);
 }
 
 extern "C" moe_status_t lmhead_argmax(const uint16_t *h, const uint16_t *w_lm,

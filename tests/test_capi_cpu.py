@@ -132,6 +132,39 @@ def test_lmhead_checks(L):
     assert lm(wsb=16) == WS
 
 
+def test_lmhead_phase_checks(L):
+    """The two phases of the lm_head call check their own arguments."""
+    def pk(h=A, w=A, M=6, H=2560, V=157184, ws=B, wsb=1 << 20):
+        return L.lmhead_partial_keys(h, w, M, H, V, ws, wsb, None)
+    assert pk(h=None) == NULL
+    assert pk(ws=None) == NULL
+    assert pk(V=0) == SHAPE
+    assert pk(M=17) == UNSUP
+    assert pk(H=12) == UNSUP
+    assert pk(w=MIS) == ALIGN
+    assert pk(wsb=16) == WS
+
+    def pk8(h=A, w=A, sc=A, M=6, H=2560, V=157184, ws=B, wsb=1 << 20):
+        return L.lmhead_partial_keys_fp8(h, w, sc, M, H, V, ws, wsb, None)
+    assert pk8(sc=None) == NULL
+    assert pk8(H=2568) == UNSUP
+    assert pk8(sc=A + 2) == ALIGN
+    assert pk8(wsb=16) == WS
+
+    def mk(M=6, V=157184, am=A, ml=None, tok=None, acc=None, ws=B, wsb=1 << 20):
+        return L.lmhead_merge_keys(M, V, am, ml, tok, acc, ws, wsb, None)
+    assert mk(am=None) == NULL
+    assert mk(ws=None) == NULL
+    assert mk(tok=A) == NULL                 # tokens without accept
+    assert mk(acc=B) == NULL                 # accept without tokens
+    assert mk(M=0) == SHAPE
+    assert mk(V=0) == SHAPE
+    assert mk(M=17) == UNSUP
+    assert mk(am=A + 2) == ALIGN
+    assert mk(tok=A, acc=B + 1) == ALIGN
+    assert mk(wsb=16) == WS
+
+
 def test_greedy_verify_checks(L):
     def gv(h=A, w=A, tok=A, M=6, H=2560, V=157184, am=A, ml=None, acc=B, ws=B, wsb=1 << 20):
         return L.lmhead_greedy_verify(h, w, tok, M, H, V, am, ml, acc, ws, wsb, None)

@@ -416,6 +416,32 @@ def test_lmhead_full_size():
     _compare_lm(am, ml, h, wl_bits, oracle.lmhead(h, wl_bits))
 
 
+@pytest.mark.parametrize("M,H,V,fp8", [(6, 2560, 5000, False), (16, 256, 4099, False),
+                                        (1, 264, 100, False), (6, 1040, 3001, True)])
+def test_lmhead_phases_equal_the_combined_call(M, H, V, fp8):
+    """lmhead_partial_keys then lmhead_merge_keys gives bitwise what
+    lmhead_greedy_verify (and lmhead_argmax, without tokens) gives."""
+    say("lmhead phases", M, H, V, fp8)
+    h = to_dev(synth.activations(M, H, seed=800 + M))
+    if fp8:
+        q, sc = synth.fp8_rows((V, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 801, V)
+        w, sc = torch.from_numpy(q).cuda(), torch.from_numpy(sc).cuda()
+    else:
+        w, sc = to_dev(synth.normal_bf16((V, H), 0.02, 802, V)), None
+    chain = torch.from_numpy(np.random.default_rng(803).integers(0, V, size=M).astype(np.int32)).cuda()
+    if fp8:
+        am0, acc0, ml0 = mv.lmhead_greedy_verify_fp8(h, w, sc, chain, want_max=True)
+    else:
+        am0, acc0, ml0 = mv.lmhead_greedy_verify(h, w, chain, want_max=True)
+    ws = torch.zeros(mv.lmhead_argmax_workspace_bytes(M, V), dtype=torch.uint8, device="cuda")
+    mv.lmhead_partial_keys(h, w, ws, w_scale=sc)
+    am1, acc1, ml1 = mv.lmhead_merge_keys(M, V, ws, tokens=chain, want_max=True)
+    am2 = mv.lmhead_merge_keys(M, V, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(am0, am1) and torch.equal(acc0, acc1) and torch.equal(ml0, ml1)
+    assert torch.equal(am0, am2)
+
+
 def test_lmhead_zero_hidden():
     say("lmhead zero hidden")
     wl = synth.normal_bf16((300, 64), 0.02, 3, 3)
