@@ -515,11 +515,14 @@ __device__ __forceinline__ float wave_total(float v)
 // up_unit below), and a workgroup's kUpWaves wavefronts claim its units one
 // at a time from an LDS counter, each waiting for the block it just issued:
 // a SIMD serves its older wavefront first, and the claims let that one take
-// more units instead of the younger ones ending last. For every pair of the column block each lane forms its gate and up
-// partial dots and two DPP trees reduce them; lane 0 queues the sums, and
-// every 64 queued outputs the 64 lanes take a = bf16(silu(g) * u) (fp32,
-// one rounding), one output each. With more than KC * 64 chunks per row a
-// unit spans several K blocks, whose sums are added in LDS in block order.
+// more units instead of the younger ones ending last. For every pair of the
+// column block each lane forms its gate and up partial dots and two DPP
+// trees reduce them; lane 0 queues the sums, and every 64 queued outputs the
+// 64 lanes take a = bf16(silu(g) * u) (fp32, one rounding), one output each.
+// With more than KC * 64 chunks per row a unit spans several K blocks, whose
+// sums are added in LDS in block order. With fp8 weights the column blocks
+// of at least kHotPairs pairs are taken first, 8 rows per unit on the matrix
+// cores (below).
 constexpr int kUpWaves = 12;                     // wavefronts per workgroup
 
 // LDS row of x, in 16-byte chunks: the unit's K blocks
