@@ -8,7 +8,8 @@ pairs in every grouping path (with and without the shared expert, whose
 blocks go first), K tails of every length, both down kernels, and lm_head
 tile counts and K blocks that leave partial tiles and partial rings, and
 whole layers whose selection runs in the up kernel (ragged E, one to four
-slices of H). The draws come from one fixed seed; the case list is the same
+slices of H; bf16, and fp8 with experts that four or more pairs share on
+the matrix cores). The draws come from one fixed seed; the case list is the same
 on every run.
 
 Acceptance as in every parity test: expert-FFN outputs within
@@ -192,3 +193,49 @@ def test_random_layer(c, M, H, I, E, k, alpha):
     assert_close(go[same], out[same], "out")
     check_tie_rows(x, gi, gw, go, ref, lambda xr, ids, tw: oracle.expert_ffn(
         xr, ids, tw, w["gate"], w["up"], w["down"]))
+
+
+def _layer8_cases(n):
+    rng = np.random.default_rng(SEED + 3)
+    cases = []
+    for c in range(n):
+        M = int(rng.integers(4, 17))                 # four or more pairs can share a block
+        E = int(rng.integers(2, 129))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        H = _mult(rng, 16, 1024, 16)
+        I = _mult(rng, 16, 1024, 16)
+        while E * H * I > 40_000_000:
+            E = max(k, E // 2)
+        alpha = [1.0, 0.5, None][c % 3]
+        cases.append((c, M, H, I, E, k, alpha))
+    return cases
+
+
+@pytest.mark.parametrize("c,M,H,I,E,k,alpha", _layer8_cases(9))
+def test_random_layer_fp8(c, M, H, I, E, k, alpha):
+    """moe_layer_fp8: the selection inside the fp8 up kernel, then both
+    projections with the experts that four or more of the call's pairs share
+    on the matrix cores and the rest on the GEMV paths (the skewed draws
+    make such experts common), against the oracle's route and fp8 FFN."""
+    say("random layer fp8", c, M, H, I, E, k, alpha)
+    x = synth.activations(M, H, seed=7900 + c)
+    router = synth.normal_bf16((E, H), synth.WEIGHT_STD, synth.WEIGHT_SEED + 7950 + c, 0)
+    w = {}
+    for j, name in enumerate(("gate", "up", "down")):
+        shape = (E, H, I) if name == "down" else (E, I, H)
+        w[name], w["s_" + name] = synth.fp8_rows(shape, synth.WEIGHT_STD, 8000 + c, j + 1)
+    bias = None if alpha is None else synth.zipf_bias(E, alpha)
+    b = None if bias is None else torch.from_numpy(bias).cuda()
+    gi, gw, go = mv.moe_layer_fp8(to_dev(x), to_dev(router), _u8(w["gate"]), _f32(w["s_gate"]),
+                                  _u8(w["up"]), _f32(w["s_up"]), _u8(w["down"]),
+                                  _f32(w["s_down"]), k, b)
+    torch.cuda.synchronize()
+    gi, gw, go = gi.cpu().numpy(), gw.cpu().numpy(), go.cpu().numpy()
+    ref = oracle.route(x, router, bias, k)
+    same = compare_route(gi, gw, None, ref, k)
+
+    def ffn8(xr, ids, tw):
+        return oracle.expert_ffn_fp8(xr, ids, tw, w["gate"], w["s_gate"], w["up"], w["s_up"],
+                                     w["down"], w["s_down"])
+    assert_close(go[same], ffn8(x, ref["idx"], ref["w"])[same], "out")
+    check_tie_rows(x, gi, gw, go, ref, ffn8)
