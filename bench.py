@@ -206,7 +206,7 @@ def write_counters(args) -> None:
                          write_kib=w_kib, write_b=w_kib * 1024 / w_fac,
                          algo_write_b=a.get("write")))
     lines = [f"# {args.title}" if args.title else "# rocprofv3 HBM counters",
-             "# commands (repository root on the GPU box, TMPDIR=/tmp), one counter pass each:"]
+             "# commands (repository root on the machine with the GPU, TMPDIR=/tmp), one counter pass each:"]
     lines += [f"#   {c}" for c in args.cmd]
     lines += [f"# summary: python3 bench.py --write-counters <fetch csv> <write csv> "
               f"--algo <algo json> --out {os.path.basename(args.out)}",
@@ -271,7 +271,7 @@ def write_stats(args) -> None:
             rows.append((name, int(row["Calls"]), avg_us, float(row["MinNs"]) / 1e3,
                          float(row["MaxNs"]) / 1e3, byts))
     lines = [f"# {args.title}" if args.title else "# rocprofv3 kernel stats",
-             "# commands (repository root on the GPU box, TMPDIR=/tmp):"]
+             "# commands (repository root on the machine with the GPU, TMPDIR=/tmp):"]
     lines += [f"#   {c}" for c in args.cmd]
     lines += [f"# summary: python3 bench.py --write-stats <kernel_stats.csv> "
               f"{'--algo <algo json> ' if args.algo else ''}--out {os.path.basename(args.out)}",
