@@ -34,9 +34,19 @@ class Step:
     """Inputs, outputs and raw argument tuples of one verify step: one MoE
     layer (moe_layer, or moe_layer_noalloc) and the lm_head verdict."""
 
-    def __init__(self, L, M, H, I, E, k, V, layer, ws_layer, ws_lm, noalloc=False, zipf=None):
+    def __init__(self, L, M, H, I, E, k, V, layer, ws_layer, ws_lm, noalloc=False, zipf=None,
+                 fp8=False):
         self.L, self.M, self.H, self.I, self.E, self.k, self.V = L, M, H, I, E, k, V
         self.w = small_layer(H, E, I, layer)
+        self.fp8 = fp8
+        if fp8:                                      # E4M3 codes, fp32 row scales
+            for j, name in enumerate(("gate", "up", "down")):
+                shape = (E, H, I) if name == "down" else (E, I, H)
+                q, sc = synth.fp8_rows(shape, synth.WEIGHT_STD, 60 + layer, j + 1)
+                self.w[name] = torch.from_numpy(q).cuda()
+                self.w["s_" + name] = torch.from_numpy(sc).cuda()
+            q, sc = synth.fp8_rows((V, H), synth.WEIGHT_STD, 65 + layer, 4)
+            self.wlm8, self.slm8 = torch.from_numpy(q).cuda(), torch.from_numpy(sc).cuda()
         self.x = to_dev(synth.activations(M, H, seed=70 + layer))
         self.h = to_dev(synth.activations(M, H, seed=80 + layer))
         self.wlm = to_dev(synth.normal_bf16((V, H), synth.WEIGHT_STD, synth.WEIGHT_SEED, 90 + layer,
@@ -61,6 +71,22 @@ class Step:
     def enqueue(self, stream):
         L, M, H, I, E, k = self.L, self.M, self.H, self.I, self.E, self.k
         b = None if self.bias is None else self.bias.data_ptr()
+        if self.fp8:
+            w = self.w
+            rc = L.moe_layer_fp8(self.x.data_ptr(), w["router"].data_ptr(), b,
+                                 w["gate"].data_ptr(), w["s_gate"].data_ptr(), w["up"].data_ptr(),
+                                 w["s_up"].data_ptr(), w["down"].data_ptr(),
+                                 w["s_down"].data_ptr(), M, H, I, E, k, self.idx.data_ptr(),
+                                 self.tw.data_ptr(), self.out.data_ptr(), self.ws_layer.data_ptr(),
+                                 ctypes.c_size_t(self.ws_layer.numel()), stream)
+            assert rc == 0, mv.status_str(rc)
+            rc = L.lmhead_greedy_verify_fp8(self.h.data_ptr(), self.wlm8.data_ptr(),
+                                            self.slm8.data_ptr(), self.chain.data_ptr(), M, H,
+                                            self.V, self.am.data_ptr(), None, self.acc.data_ptr(),
+                                            self.ws_lm.data_ptr(),
+                                            ctypes.c_size_t(self.ws_lm.numel()), stream)
+            assert rc == 0, mv.status_str(rc)
+            return
         a = [self.x.data_ptr(), self.w["router"].data_ptr(), b, self.w["gate"].data_ptr(),
              self.w["up"].data_ptr(), self.w["down"].data_ptr(), M, H, I, E, k,
              self.idx.data_ptr(), self.tw.data_ptr(), self.out.data_ptr()]
@@ -77,13 +103,13 @@ class Step:
         assert rc == 0, mv.status_str(rc)
 
 
-def run_graph_case(M, H, I, E, k, V, nsteps, noalloc_step=None, zipf=None):
+def run_graph_case(M, H, I, E, k, V, nsteps, noalloc_step=None, zipf=None, fp8=False):
     L = mv.lib()
     ws_layer = torch.zeros(L.moe_layer_workspace_bytes(M, H, I, E, k), dtype=torch.uint8,
                            device="cuda")
     ws_lm = torch.zeros(L.lmhead_argmax_workspace_bytes(M, V), dtype=torch.uint8, device="cuda")
     steps = [Step(L, M, H, I, E, k, V, layer=s, ws_layer=ws_layer, ws_lm=ws_lm,
-                  noalloc=(s == noalloc_step), zipf=zipf) for s in range(nsteps)]
+                  noalloc=(s == noalloc_step), zipf=zipf, fp8=fp8) for s in range(nsteps)]
     cur = torch.cuda.current_stream().cuda_stream
     # eager reference (also the warm-up: attributes and the static scratch
     # address are set up outside the capture)
@@ -136,3 +162,10 @@ def test_graph_replay_equals_eager_mfma_regime():
 
 def test_graph_replay_equals_eager_one_token():
     run_graph_case(1, 256, 128, 16, 2, 1000, nsteps=3, noalloc_step=2)
+
+
+def test_graph_replay_equals_eager_fp8_shared_experts():
+    # fp8 layer and fp8 lm_head verdict at M = 16 with Zipf-skewed routing:
+    # experts that four or more pairs share run both projections on the
+    # matrix cores inside the captured graph
+    run_graph_case(16, 512, 256, 24, 8, 2048, nsteps=2, zipf=1.0, fp8=True)
