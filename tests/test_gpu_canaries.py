@@ -80,6 +80,47 @@ def test_layer_and_ffn_stay_in_bounds(M, H, I, E, k):
     assert torch.equal(out, out2)
 
 
+
+@pytest.mark.parametrize("M,H,I,E,k", [(16, 528, 48, 10, 5), (5, 272, 1040, 6, 4),
+                                       (1, 1040, 256, 12, 3), (12, 256, 2064, 40, 8)])
+def test_layer_fp8_stays_in_bounds(M, H, I, E, k):
+    """moe_layer_fp8 then the fp8 lm_head verdict at ragged shapes, with few
+    experts for many pairs (the matrix-core units of shared experts, with
+    K tails and a ragged last down workgroup), canaries after every output
+    and workspace."""
+    say("canaries layer fp8", M, H, I, E, k)
+    router = to_dev(synth.normal_bf16((E, H), synth.WEIGHT_STD, 3500 + H, 0))
+    d = {}
+    for j, name in enumerate(("gate", "up", "down")):
+        shape = (E, H, I) if name == "down" else (E, I, H)
+        q, sc = synth.fp8_rows(shape, synth.WEIGHT_STD, 3501 + I, j + 1)
+        d[name], d["s_" + name] = torch.from_numpy(q).cuda(), torch.from_numpy(sc).cuda()
+    x = to_dev(synth.activations(M, H, seed=3502 + M))
+    idx, ib = padded((M, k), torch.int32)
+    tw, wb = padded((M, k), torch.float32)
+    out, ob = padded((M, H), torch.float32)
+    nb = mv.moe_layer_workspace_bytes(M, H, I, E, k)
+    ws = workspace(nb)
+    mv.moe_layer_fp8(x, router, d["gate"], d["s_gate"], d["up"], d["s_up"], d["down"],
+                     d["s_down"], k, out=(idx, tw, out), workspace=ws[:nb])
+    torch.cuda.synchronize()
+    assert canary_intact(ib, M * k) and canary_intact(wb, M * k) and canary_intact(ob, M * H)
+    assert ws_ok(ws, nb)
+    V = 3 * 16 + 5                                    # a partial last tile
+    q, sc = synth.fp8_rows((V, H), synth.WEIGHT_STD, 3503, V)
+    am, ab = padded((M,), torch.int32)
+    ml, mb = padded((M,), torch.float32)
+    acc, cb = padded((2,), torch.int32)
+    nl = mv.lmhead_argmax_workspace_bytes(M, V)
+    wl = workspace(nl)
+    chain = torch.zeros(M, dtype=torch.int32, device="cuda")
+    mv.lmhead_greedy_verify_fp8(to_dev(synth.activations(M, H, seed=3504)),
+                                torch.from_numpy(q).cuda(), torch.from_numpy(sc).cuda(), chain,
+                                want_max=True, out=(am, acc, ml), workspace=wl[:nl])
+    torch.cuda.synchronize()
+    assert canary_intact(ab, M) and canary_intact(mb, M) and canary_intact(cb, 2)
+    assert ws_ok(wl, nl)
+
 @pytest.mark.parametrize("M,H,V", [(3, 264, 777), (16, 256, 4099), (1, 2560, 65)])
 def test_lmhead_stays_in_bounds(M, H, V):
     say("canaries lm_head", M, H, V)
