@@ -5,7 +5,8 @@ every workspace at ragged shapes: no call may write beyond what it owns.
 One workspace reused by calls of shrinking shapes must give the results of
 fresh ones (whatever a larger call left past the header -- its activations,
 partial logits or keys -- must never be read as a counter or as data by a
-smaller one), with the header's counters back at zero after every call.
+smaller one), with the header's counters back at zero after every call. The workspace
+clear zeroes exactly its bytes, also replayed from a graph.
 """
 import numpy as np
 import pytest
@@ -175,3 +176,28 @@ def test_ffn_workspace_reused_by_shrinking_shapes():
             b8 = mv.moe_expert_ffn_fp8(x, idx, tw, *d8, workspace=shared)
             torch.cuda.synchronize()
             assert torch.equal(a8, b8) and int(shared[:HEADER].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 4096 + 48, 3 * 1024 * 1024 + 16])
+def test_workspace_clear_fills_exactly_its_bytes(nbytes):
+    """moe_workspace_clear zeroes exactly `bytes` (ragged against its fill
+    kernel's 16-byte stores and grid), eagerly and as a captured graph
+    replayed several times, each replay after an eager re-poisoning."""
+    say("workspace clear", nbytes)
+    ws = workspace(nbytes)
+    ws[:nbytes] = 0xA7
+    mv.moe_workspace_clear(ws[:nbytes])
+    torch.cuda.synchronize()
+    assert int(ws[:nbytes].count_nonzero()) == 0
+    assert bool((ws[nbytes:] == CANARY_U8).all())
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=cap):
+        mv.moe_workspace_clear(ws[:nbytes], stream=cap)
+    for rep in range(3):
+        ws[:nbytes] = 0x5C + rep
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(ws[:nbytes].count_nonzero()) == 0, f"replay {rep}"
+        assert bool((ws[nbytes:] == CANARY_U8).all()), f"replay {rep}"
